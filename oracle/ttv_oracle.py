@@ -1,0 +1,326 @@
+"""Oracle implementation (test infrastructure only; see the package header).
+
+Sources, cited by page title and section:
+  [I1204] mlxcel issue #1204, "perf(speculative): draft a tree instead of a
+          chain ..." -- sections "What this needs", "Increment 1 landed on a
+          branch: topology, mask, walk", "The rollback constraint, which
+          decides feasibility", "Redirection ...", "Increment 3: the mask is
+          now the shape a forward actually takes".
+  [PR1212] mlxcel PR #1212, "feat(speculative): draft and verify a token
+          tree, behind a flag, default off" -- its commit messages: the
+          topology/mask/walk commit, the gather_positions commit, the commit
+          widening the gather to every sequence-axis buffer, the history-mask
+          commit, the Gemma 4 tree-verify commit, the verify_finalize_tree
+          commit, the gather_within_tail commit, the rollback-to-path commit.
+  [S728]  splash issue #728, "Experiment: qualify shared-prefix tree
+          verification and conservative admission" -- "What it does",
+          "Results", "Earlier controlled experiments".
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "decode_bf16",
+    "decode_fp16",
+    "decode_kv",
+    "validate_parent",
+    "ancestor_sets",
+    "ancestor_bits",
+    "node_depths",
+    "additive_mask_with_history",
+    "visible_keys",
+    "attention_rows",
+    "tree_verify_attention",
+    "tree_verify_attention_dense",
+    "vocab_argmax",
+    "tree_accept_walk",
+    "rollback_selection",
+    "gather_positions",
+    "gather_layer",
+    "verify_round",
+]
+
+MASKED = -1e9  # blocking value of the additive mask ([PR1212] Gemma 4 tree-verify commit)
+
+
+# ----------------------------------------------------------------------------
+# Storage decoding (plain format definitions).
+# ----------------------------------------------------------------------------
+
+def decode_bf16(bits) -> np.ndarray:
+    """bf16 bit pattern -> float64: the pattern is the top half of an fp32."""
+    b = np.asarray(bits).view(np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def decode_fp16(x) -> np.ndarray:
+    """IEEE binary16 -> float64 (exact)."""
+    return np.asarray(x).view(np.float16).astype(np.float64)
+
+
+def decode_kv(buf, dtype: str, scale=None) -> np.ndarray:
+    """Cache values as float64. int8 codes are dequantised with their per-token
+    fp16 scale: value = code * scale ([PR1212] gather_positions commit: Int8
+    keeps a per-token scale sidecar on the sequence axis)."""
+    if dtype == "f32":
+        return np.asarray(buf, dtype=np.float64)
+    if dtype == "bf16":
+        return decode_bf16(buf)
+    if dtype == "i8":
+        return np.asarray(buf, dtype=np.int8).astype(np.float64) * decode_fp16(scale)[..., None]
+    raise ValueError(dtype)
+
+
+# ----------------------------------------------------------------------------
+# Step 1: ancestor mask.
+# ----------------------------------------------------------------------------
+
+def validate_parent(parent) -> None:
+    """A draft tree lists its nodes in topological order: node 0 is the root
+    (parent -1) and every other node's parent precedes it ([I1204] "Increment
+    1": DraftTree keeps parents[i] < i)."""
+    for i, p in enumerate(parent):
+        p = int(p)
+        if i == 0 and p != -1:
+            raise ValueError("node 0 must be the root (parent -1)")
+        if i > 0 and not (0 <= p < i):
+            raise ValueError(f"parent[{i}] = {p} is not an earlier node")
+
+
+def ancestor_sets(parent) -> list:
+    """anc(i) = {i} plus every node on the parent chain from i up to the root,
+    found by following the chain explicitly."""
+    validate_parent(parent)
+    out = []
+    for i in range(len(parent)):
+        s = set()
+        j = i
+        while j != -1:
+            s.add(j)
+            j = int(parent[j])
+        out.append(frozenset(s))
+    return out
+
+
+def ancestor_bits(parent) -> np.ndarray:
+    """uint64 per node: bit j set iff block node j is in anc(i) (T <= 64)."""
+    if len(parent) > 64:
+        raise ValueError("more than 64 nodes")
+    out = np.zeros(len(parent), dtype=np.uint64)
+    for i, s in enumerate(ancestor_sets(parent)):
+        w = 0
+        for j in s:
+            w |= 1 << j
+        out[i] = np.uint64(w)
+    return out
+
+
+def node_depths(parent) -> np.ndarray:
+    """Number of proper ancestors of each node (root depth 0)."""
+    return np.asarray([len(s) - 1 for s in ancestor_sets(parent)], dtype=np.int32)
+
+
+def additive_mask_with_history(parent, offset: int, masked: float = MASKED) -> np.ndarray:
+    """[T, offset + T] float32 additive mask ([I1204] "Increment 3"; [PR1212]
+    history-mask commit): query row q sits at logical position q + offset; the
+    first ``offset`` columns are the cached history every node attends in
+    full; block column offset + j is open (0) iff j is an ancestor of q or q
+    itself, and carries ``masked`` otherwise (so siblings never see each
+    other). The blocking value is -1e9 rather than -inf ([PR1212] Gemma 4
+    tree-verify commit)."""
+    T = len(parent)
+    m = np.full((T, offset + T), np.float32(masked), dtype=np.float32)
+    m[:, :offset] = 0.0
+    for q, s in enumerate(ancestor_sets(parent)):
+        for j in s:
+            m[q, offset + j] = 0.0
+    return m
+
+
+# ----------------------------------------------------------------------------
+# Step 2: tree-masked GQA verify attention.
+# ----------------------------------------------------------------------------
+
+def visible_keys(P: int, anc) -> np.ndarray:
+    """Cache rows a node attends: the whole prefix [0, P) and the block rows
+    P + a for a in anc(i). Block node i's K/V row sits at P + i because the
+    verify block is appended in topological order ([PR1212] rollback-to-path
+    commit)."""
+    return np.concatenate([np.arange(P), P + np.asarray(sorted(anc), dtype=np.int64)]).astype(np.int64)
+
+
+def attention_rows(qrows, K, V, keys, softmax_scale: float) -> np.ndarray:
+    """softmax(scale * q . K[keys]) @ V[keys] for each query row, in float64.
+    qrows [n, D]; K, V [S, D] already decoded."""
+    q = np.asarray(qrows, dtype=np.float64)
+    Kk = K[keys]
+    Vk = V[keys]
+    s = softmax_scale * (q @ Kk.T)               # [n, |keys|]
+    s = s - s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    p /= p.sum(axis=1, keepdims=True)
+    return p @ Vk
+
+
+def tree_verify_attention(q, layer: dict, node_off, hist_len, parents, softmax_scale: float,
+                          q_dtype: str, kv_dtype: str) -> np.ndarray:
+    """Explicit key-set form, batched over sequences ([I1204] "Redirection":
+    the nodes are flattened into one sequence and the tree mask hides
+    siblings; [PR1212] history-mask commit: full history plus ancestors).
+
+    q: [n_nodes, Hq, D] (float32 or bf16 bits); layer: {'k','v'[, 'k_scale',
+    'v_scale']} with [B, Hkv, cap, D] caches; parents: per-sequence parent
+    arrays, or None for the causal (linear) reading. GQA: query head h reads
+    KV head h // (Hq / Hkv). Returns float64 [n_nodes, Hq, D]."""
+    qf = np.asarray(q, dtype=np.float64) if q_dtype == "f32" else decode_bf16(q)
+    n, Hq, D = qf.shape
+    Hkv = layer["k"].shape[1]
+    G = Hq // Hkv
+    out = np.zeros((n, Hq, D), dtype=np.float64)
+    B = len(hist_len)
+    for b in range(B):
+        P = int(hist_len[b])
+        o0, o1 = int(node_off[b]), int(node_off[b + 1])
+        T = o1 - o0
+        if T == 0:
+            continue
+        par = np.arange(-1, T - 1) if parents is None else parents[b]
+        sets = ancestor_sets(par)
+        for g in range(Hkv):
+            K = decode_kv(layer["k"][b, g, : P + T], kv_dtype, None if kv_dtype != "i8" else layer["k_scale"][b, g, : P + T])
+            V = decode_kv(layer["v"][b, g, : P + T], kv_dtype, None if kv_dtype != "i8" else layer["v_scale"][b, g, : P + T])
+            for i in range(T):
+                keys = visible_keys(P, sets[i])
+                out[o0 + i, g * G:(g + 1) * G] = attention_rows(qf[o0 + i, g * G:(g + 1) * G], K, V, keys, softmax_scale)
+    return out
+
+
+def tree_verify_attention_dense(qf, K, V, mask_add, softmax_scale: float, G: int) -> np.ndarray:
+    """Dense form for one sequence: scores over all P + T cache rows plus the
+    additive mask, then softmax and V. qf [T, Hq, D] float64; K, V [Hkv, P+T, D]
+    float64; mask_add [T, P+T]."""
+    T, Hq, D = qf.shape
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    for h in range(Hq):
+        g = h // G
+        s = softmax_scale * (qf[:, h, :] @ K[g].T) + np.asarray(mask_add, dtype=np.float64)
+        s = s - s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        p /= p.sum(axis=1, keepdims=True)
+        out[:, h, :] = p @ V[g]
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Step 3: per-node argmax over the vocabulary.
+# ----------------------------------------------------------------------------
+
+def vocab_argmax(logits) -> np.ndarray:
+    """The target's greedy selection at every node: the index of the row
+    maximum, compared in the logits' own fp32 ([I1204] "Increment 1": the
+    target emits one argmax per position; [S728] "Results": raw F32 argmax).
+    Ties go to the lowest index; -0.0 equals +0.0; a NaN outranks every number
+    and the first NaN wins (numpy.argmax semantics)."""
+    return np.argmax(np.asarray(logits, dtype=np.float32), axis=-1).astype(np.int32)
+
+
+# ----------------------------------------------------------------------------
+# Step 4: tree accept walk.
+# ----------------------------------------------------------------------------
+
+def tree_accept_walk(parent, token, target_argmax):
+    """Start at the root (node 0, the committed token, never compared). At the
+    current node, descend to the child whose draft token equals the target's
+    selection at the current node; when two children carry that token take
+    the lower label and do not fan out ([I1204] "Increment 1"; [S728] "What it
+    does"). Stop when no child matches.
+
+    Returns (path, emitted): path lists node ids from 0; accepted = len(path)
+    - 1; emitted[k] = target_argmax[path[k]], i.e. accepted + 1 tokens (the
+    accepted drafts plus the target's token after the last one)."""
+    validate_parent(parent)
+    T = len(parent)
+    kids = [[] for _ in range(T)]
+    for i in range(1, T):
+        kids[int(parent[i])].append(i)
+    path = [0]
+    cur = 0
+    while True:
+        nxt = None
+        for c in kids[cur]:
+            if int(token[c]) == int(target_argmax[cur]):
+                nxt = c
+                break
+        if nxt is None:
+            break
+        path.append(nxt)
+        cur = nxt
+    emitted = [int(target_argmax[n]) for n in path]
+    return path, emitted
+
+
+# ----------------------------------------------------------------------------
+# Step 5: rollback by gather along the sequence axis.
+# ----------------------------------------------------------------------------
+
+def rollback_selection(P: int, path) -> np.ndarray:
+    """Survivors of a tree round: the whole history [0, P) and the accepted
+    path's block rows P + path[k] ([PR1212] rollback-to-path commit: the cache
+    gather is handed the accepted nodes as block offsets)."""
+    return np.concatenate([np.arange(P, dtype=np.int64), P + np.asarray(path, dtype=np.int64)])
+
+
+def gather_positions(buf, sel, axis: int) -> np.ndarray:
+    """Select and compact a scattered set of positions along the sequence axis
+    ([I1204] "Redirection"; [PR1212] gather_positions commit)."""
+    return np.take(buf, np.asarray(sel, dtype=np.int64), axis=axis)
+
+
+def gather_layer(layer: dict, sels, base: dict | None = None) -> dict:
+    """Apply per-sequence selections to one layer's cache [B, Hkv, cap, D] and,
+    for int8, its scales [B, Hkv, cap] -- every sequence-axis buffer moves
+    with its tokens ([PR1212] gather_positions commit and the commit widening
+    it). Rows [0, len(sel_b)) of the result hold the survivors; rows beyond
+    keep ``base``'s contents (the source itself for an in-place rollback, the
+    destination's prior contents for an out-of-place take)."""
+    base = layer if base is None else base
+    out = {name: np.array(base[name], copy=True) for name in layer}
+    for b, sel in enumerate(sels):
+        n = len(sel)
+        for name in layer:
+            if name.endswith("_scale"):
+                out[name][b, :, :n] = gather_positions(layer[name][b], sel, axis=1)
+            else:
+                out[name][b, :, :n, :] = gather_positions(layer[name][b], sel, axis=1)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# One round.
+# ----------------------------------------------------------------------------
+
+def verify_round(spec, tensors: dict, softmax_scale: float | None = None) -> dict:
+    """mask -> attention (every layer) -> argmax -> walk -> rollback
+    selection -> gather, for a workloads.RoundSpec and its host tensors."""
+    scale = 1.0 / np.sqrt(spec.D) if softmax_scale is None else softmax_scale
+    node_off = spec.node_off
+    anc = np.concatenate([ancestor_bits(p) for p in spec.parents]) if spec.B else np.zeros(0, np.uint64)
+    depth = np.concatenate([node_depths(p) for p in spec.parents]) if spec.B else np.zeros(0, np.int32)
+    outs = [tree_verify_attention(L["q"], L, node_off, spec.hist_len, spec.parents, scale,
+                                  spec.q_dtype, spec.kv_dtype) for L in tensors["layers"]]
+    am = vocab_argmax(tensors["logits"])
+    paths, emitted, sels = [], [], []
+    for b in range(spec.B):
+        o0, o1 = int(node_off[b]), int(node_off[b + 1])
+        path, em = tree_accept_walk(spec.parents[b], spec.tokens[b], am[o0:o1])
+        paths.append(path)
+        emitted.append(em)
+        sels.append(rollback_selection(int(spec.hist_len[b]), path))
+    caches = []
+    for L in tensors["layers"]:
+        kv = {k: v for k, v in L.items() if k != "q"}
+        caches.append(gather_layer(kv, sels))
+    return {"anc": anc, "depth": depth, "attn": outs, "argmax": am, "paths": paths,
+            "emitted": emitted, "sels": sels, "caches": caches}

@@ -1,0 +1,542 @@
+"""Pins of the CPU oracle against things other than itself: the pages'
+equivalences and worked examples, closed forms, brute force on tiny inputs,
+and library routines (torch SDPA in float64, Python's max/index)."""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from workloads import (binary_tree_7, chain_tree, config1_round, config2_round, config3_round,
+                       confidence_tree, plant_walk, planted_logits, quantize_int8_per_token,
+                       random_descent, random_tree, rng_for, sary_tree, to_bf16_bits,
+                       unique_fp16_scales)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+MASKED = np.float32(-1e9)
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------
+# independent references
+# ---------------------------------------------------------------------------
+
+def closure_ancestors(parent):
+    """Reflexive-transitive closure of the child->parent relation by repeated
+    boolean matrix products (a different algorithm from chain walking)."""
+    T = len(parent)
+    A = np.zeros((T, T), dtype=bool)
+    for i in range(1, T):
+        A[i, parent[i]] = True
+    R = np.eye(T, dtype=bool)
+    while True:
+        R2 = R | ((R.astype(np.int64) @ A.astype(np.int64)) > 0)
+        if (R2 == R).all():
+            return R
+        R = R2
+
+
+def causal_mask(T, offset):
+    """Textbook causal mask with history: row q (position q + offset) sees
+    columns c <= q + offset."""
+    m = np.full((T, offset + T), MASKED, dtype=np.float32)
+    for q in range(T):
+        m[q, : q + offset + 1] = 0.0
+    return m
+
+
+def speculative_walk(drafts, target):
+    """Chain acceptance: the longest prefix of the drafts where draft k (node
+    k, k >= 1) equals the target's token at node k-1; emitted are the target's
+    tokens at nodes 0..accepted."""
+    a = 0
+    while a + 1 < len(drafts) and drafts[a + 1] == target[a]:
+        a += 1
+    return a, [int(t) for t in target[: a + 1]]
+
+
+def sdpa_reference(qf, K, V, P, open_mask, G, scale):
+    """torch SDPA (float64) for one sequence: qf [T, Hq, D], K, V [Hkv, P+T, D],
+    open_mask [T, T] boolean over block columns (history always open)."""
+    T, Hq, D = qf.shape
+    Hkv = K.shape[0]
+    q = torch.from_numpy(qf).permute(1, 0, 2)[None]                      # [1, Hq, T, D]
+    k = torch.from_numpy(K).repeat_interleave(G, dim=0)[None]              # [1, Hq, S, D]
+    v = torch.from_numpy(V).repeat_interleave(G, dim=0)[None]
+    allow = torch.ones(T, P + T, dtype=torch.bool)
+    allow[:, P:] = torch.from_numpy(open_mask)
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=allow, scale=scale)
+    return o[0].permute(1, 0, 2).numpy()
+
+
+# ---------------------------------------------------------------------------
+# Step 1: mask
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T", range(0, 6))
+def test_linear_tree_masks_as_causal_offset0(T):
+    np.testing.assert_array_equal(O.additive_mask_with_history(chain_tree(T), 0), causal_mask(T, 0))
+
+
+@pytest.mark.parametrize("T,offset", itertools.product(range(0, 6), [1, 3, 64]))
+def test_linear_tree_history_mask_equals_causal(T, offset):
+    np.testing.assert_array_equal(O.additive_mask_with_history(chain_tree(T), offset), causal_mask(T, offset))
+
+
+def test_mask_golden_binary7():
+    g = _golden("mask_binary7_p2.json")
+    rows = g["rows_open_o_masked_x"]
+    want = np.array([[0.0 if ch == "o" else MASKED for ch in rows[2 * i] + rows[2 * i + 1]]
+                     for i in range(len(g["parent"]))], dtype=np.float32)
+    np.testing.assert_array_equal(O.additive_mask_with_history(g["parent"], g["offset"]), want)
+    np.testing.assert_array_equal(O.node_depths(g["parent"]), g["depth"])
+
+
+def _trees():
+    out = [chain_tree(1), chain_tree(64), sary_tree(3, 3), sary_tree(2, 5)]
+    for s in range(6):
+        out.append(binary_tree_7(rng_for(900, s)))
+        out.append(random_tree(rng_for(901, s), int(rng_for(902, s).integers(2, 65))))
+        out.append(confidence_tree(rng_for(903, s), 16, 8, 1000, 4)[0])
+    return out
+
+
+@pytest.mark.parametrize("idx", range(22))
+def test_ancestors_brute_force(idx):
+    parent = _trees()[idx]
+    R = closure_ancestors(parent)
+    sets = O.ancestor_sets(parent)
+    for i in range(len(parent)):
+        assert sets[i] == frozenset(np.nonzero(R[i])[0].tolist())
+    bits = O.ancestor_bits(parent)
+    for i in range(len(parent)):
+        assert int(bits[i]) == sum(1 << int(j) for j in np.nonzero(R[i])[0])
+    np.testing.assert_array_equal(O.node_depths(parent), R.sum(axis=1) - 1)
+
+
+@pytest.mark.parametrize("idx", range(22))
+def test_mask_invariants(idx):
+    parent = _trees()[idx]
+    T = len(parent)
+    for P in (0, 5):
+        m = O.additive_mask_with_history(parent, P)
+        assert (m[:, :P] == 0).all()                         # history open to every node
+        for i in range(T):
+            assert m[i, P + i] == 0                          # self
+            assert (m[i] == 0).any()                         # no fully masked row
+        for i, j in itertools.combinations(range(1, T), 2):
+            if parent[i] == parent[j]:                       # siblings never see each other
+                assert m[i, P + j] == MASKED and m[j, P + i] == MASKED
+        assert set(np.unique(m)) <= {0.0, MASKED}
+        np.testing.assert_array_equal((m[:, P:] == 0).sum(axis=1), O.node_depths(parent) + 1)
+
+
+def test_invalid_parent_rejected():
+    for bad in ([0, 0], [-1, 1], [-1, 0, 2], [-1, -1]):
+        with pytest.raises(ValueError):
+            O.ancestor_sets(bad)
+
+
+# ---------------------------------------------------------------------------
+# Step 4: walk
+# ---------------------------------------------------------------------------
+
+def test_walk_golden_cases():
+    for c in _golden("walk_cases.json")["cases"]:
+        path, em = O.tree_accept_walk(c["parent"], c["token"], c["argmax"])
+        assert path == c["path"], c["name"]
+        assert em == c["emitted"], c["name"]
+
+
+@pytest.mark.parametrize("T", range(1, 9))
+def test_linear_tree_walks_as_speculative_walk(T):
+    # every accept length, with planted tokens
+    for acc in range(T):
+        tok, tgt, _ = plant_walk(chain_tree(T), list(range(acc + 1)), rng_for(910, T, acc), 50)
+        path, em = O.tree_accept_walk(chain_tree(T), tok, tgt)
+        a, em2 = speculative_walk(list(tok), list(tgt))
+        assert a == acc and len(path) - 1 == a and em == em2 and path == list(range(a + 1))
+    # and on unplanted tokens over a 2-token vocabulary (many chance matches)
+    r = rng_for(911, T)
+    for _ in range(50):
+        tok = r.integers(0, 2, size=T)
+        tgt = r.integers(0, 2, size=T)
+        path, em = O.tree_accept_walk(chain_tree(T), tok, tgt)
+        a, em2 = speculative_walk(list(tok), list(tgt))
+        assert len(path) - 1 == a and em == em2
+
+
+def brute_force_walk(parent, token, target):
+    """All root paths whose every step matches (token[child] == target[parent]);
+    of the maximal ones, the lexicographically smallest label sequence."""
+    T = len(parent)
+    kids = [[c for c in range(1, T) if parent[c] == u] for u in range(T)]
+    paths = []
+
+    def dfs(p):
+        ext = [c for c in kids[p[-1]] if token[c] == target[p[-1]]]
+        if not ext:
+            paths.append(p)
+        for c in ext:
+            dfs(p + [c])
+
+    dfs([0])
+    return min(paths)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_walk_brute_force(seed):
+    r = rng_for(920, seed)
+    T = int(r.integers(1, 40))
+    parent = random_tree(r, T)
+    token = r.integers(0, 3, size=T)
+    target = r.integers(0, 3, size=T)
+    path, em = O.tree_accept_walk(parent, token, target)
+    assert path == brute_force_walk(parent, token, target)
+    for k in range(1, len(path)):
+        assert parent[path[k]] == path[k - 1]
+        assert token[path[k]] == target[path[k - 1]]
+    assert em == [int(target[n]) for n in path] and len(em) == len(path)
+
+
+def test_equal_token_siblings_single_path():
+    for s in range(20):
+        spec = config1_round(accepted=2, equal_sibling=True, seed=1000 + s)
+        n, sib = spec.extra["dup"]
+        path, _ = O.tree_accept_walk(spec.parents[0], spec.tokens[0], spec.targets[0])
+        assert spec.tokens[0][n] == spec.tokens[0][sib] and n < sib
+        assert n in path and sib not in path
+        assert path == spec.paths[0]
+
+
+@pytest.mark.parametrize("make", ["c1", "c2", "c3", "rand"])
+def test_walk_follows_planted_path(make):
+    for s in range(10):
+        if make == "c1":
+            spec = config1_round(seed=2000 + s)
+        elif make == "c2":
+            spec = config2_round(8, s % 8, seed=2000 + s)
+        elif make == "c3":
+            spec = config3_round(seed=2000 + s, P=8, L=1)
+        else:
+            parent = random_tree(rng_for(930, s), 30)
+            path = random_descent(parent, rng_for(931, s))
+            tok, tgt, _ = plant_walk(parent, path, rng_for(932, s), 5)
+            assert O.tree_accept_walk(parent, tok, tgt)[0] == path
+            continue
+        assert O.tree_accept_walk(spec.parents[0], spec.tokens[0], spec.targets[0])[0] == spec.paths[0]
+
+
+def test_pages_round_arithmetic():
+    """emitted = accepted + 1 per round reproduces the pages' printed 2.4359
+    emitted per verify from 56 accepted over 39 rounds."""
+    g = _golden("round_stats_pages.json")
+    assert round((g["accepted"] + g["rounds"]) / g["rounds"], 4) == g["emitted_per_verify"]
+    assert g["zero"] + g["partial"] + g["full"] == g["rounds"]
+
+
+# ---------------------------------------------------------------------------
+# Step 3: argmax
+# ---------------------------------------------------------------------------
+
+def first_max_index(row):
+    row = [float(x) for x in row]
+    for i, x in enumerate(row):
+        if x != x:
+            return i
+    return row.index(max(row))
+
+
+def test_argmax_ties_zero_nan_against_python():
+    r = rng_for(940)
+    rows = []
+    V = 1031
+    for k in range(40):
+        x = r.integers(-3, 4, size=V).astype(np.float32)      # many exact ties
+        rows.append(x)
+    z = np.zeros(V, np.float32); z[5] = -0.0; z[:] = -1; z[7] = -0.0; z[9] = 0.0; rows.append(z)
+    z = np.full(V, -1, np.float32); z[11] = 0.0; z[3] = -0.0; rows.append(z)
+    z = r.standard_normal(V).astype(np.float32); z[600] = np.nan; z[900] = np.nan; rows.append(z)
+    z = r.standard_normal(V).astype(np.float32); z[V - 1] = 50; z[V - 2] = 50; rows.append(z)
+    z = np.full(V, -np.inf, np.float32); rows.append(z)
+    z = r.standard_normal(V).astype(np.float32); z[17] = np.inf; z[400] = np.inf; rows.append(z)
+    X = np.stack(rows)
+    got = O.vocab_argmax(X)
+    assert got.dtype == np.int32
+    for i, row in enumerate(X):
+        assert got[i] == first_max_index(row), i
+
+
+def test_argmax_planted_rows():
+    tg = rng_for(941).integers(0, 248320, size=6)
+    X = planted_logits(rng_for(942), tg, 248320, 2.0)
+    np.testing.assert_array_equal(O.vocab_argmax(X), tg)
+    # ties planted across the row, including the last element of the 248,320 tail
+    X[0, [3, 70000, 248319]] = X[0].max()
+    X[1, [248319, 248318]] = X[1].max() + 5
+    got = O.vocab_argmax(X)
+    assert got[0] == min(3, tg[0]) and got[1] == 248318
+    for i in range(len(X)):
+        assert got[i] == first_max_index(X[i])
+
+
+# ---------------------------------------------------------------------------
+# Step 2: attention
+# ---------------------------------------------------------------------------
+
+def _small_case(seed, kv_dtype, T=None, P=None, Hq=4, Hkv=2, D=16, tree="random"):
+    r = rng_for(950, seed)
+    T = int(r.integers(1, 12)) if T is None else T
+    P = int(r.integers(0, 20)) if P is None else P
+    parent = random_tree(r, T) if tree == "random" else chain_tree(T)
+    from workloads import make_kv_cache, make_queries
+    kv = make_kv_cache(951, seed, 1, Hkv, P + T, D, kv_dtype)
+    q = make_queries(952, seed, T, Hq, D, "f32" if kv_dtype == "f32" else "bf16")
+    return parent, kv, q, P, T
+
+
+def _decode_with_torch(kv, q, kv_dtype):
+    """Library decoding for the reference side: torch's bfloat16 / float16."""
+    if kv_dtype == "bf16":
+        K = torch.from_numpy(kv["k"][0].view(np.int16)).view(torch.bfloat16).double().numpy()
+        V = torch.from_numpy(kv["v"][0].view(np.int16)).view(torch.bfloat16).double().numpy()
+    elif kv_dtype == "i8":
+        ks = torch.from_numpy(kv["k_scale"][0]).double()[..., None]
+        vs = torch.from_numpy(kv["v_scale"][0]).double()[..., None]
+        K = (torch.from_numpy(kv["k"][0]).double() * ks).numpy()
+        V = (torch.from_numpy(kv["v"][0]).double() * vs).numpy()
+    else:
+        K, V = kv["k"][0].astype(np.float64), kv["v"][0].astype(np.float64)
+    if q.dtype == np.uint16:
+        qf = torch.from_numpy(q.view(np.int16)).view(torch.bfloat16).double().numpy()
+    else:
+        qf = q.astype(np.float64)
+    return qf, K, V
+
+
+@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("kv_dtype", ["f32", "bf16", "i8"])
+def test_attention_matches_sdpa_with_closure_mask(seed, kv_dtype):
+    parent, kv, q, P, T = _small_case(seed, kv_dtype)
+    scale = 1 / math.sqrt(16)
+    node_off = np.array([0, T])
+    got = O.tree_verify_attention(q, kv, node_off, [P], [parent], scale,
+                                  "f32" if kv_dtype == "f32" else "bf16", kv_dtype)
+    qf, K, V = _decode_with_torch(kv, q, kv_dtype)
+    want = sdpa_reference(qf, K, V, P, closure_ancestors(parent), 2, scale)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_attention_dense_form_agrees(seed):
+    parent, kv, q, P, T = _small_case(seed, "bf16")
+    scale = 0.25
+    got = O.tree_verify_attention(q, kv, [0, T], [P], [parent], scale, "bf16", "bf16")
+    qf = O.decode_bf16(q)
+    dense = O.tree_verify_attention_dense(qf, O.decode_bf16(kv["k"][0]), O.decode_bf16(kv["v"][0]),
+                                          O.additive_mask_with_history(parent, P), scale, 2)
+    np.testing.assert_allclose(got, dense, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_attention_zero_query_is_mean_over_visible_set(seed):
+    """q = 0 makes every visible key equally likely, so the output is the
+    plain mean of V over exactly the visible rows; one-hot V rows expose the
+    set itself."""
+    r = rng_for(960, seed)
+    T, P = int(r.integers(1, 10)), int(r.integers(0, 8))
+    parent = random_tree(r, T)
+    S = P + T
+    D = S
+    k = r.standard_normal((1, 1, S, D)).astype(np.float32)
+    v = np.eye(S, D, dtype=np.float32)[None, None]
+    q = np.zeros((T, 1, D), np.float32)
+    got = O.tree_verify_attention(q, {"k": k, "v": v}, [0, T], [P], [parent], 0.3, "f32", "f32")
+    R = closure_ancestors(parent)
+    for i in range(T):
+        want = np.zeros(D)
+        vis = list(range(P)) + [P + j for j in range(T) if R[i, j]]
+        want[vis] = 1.0 / len(vis)
+        np.testing.assert_allclose(got[i, 0], want, atol=1e-15)
+
+
+def test_attention_T1_is_single_query_decode():
+    parent, kv, q, P, T = _small_case(3, "f32", T=1, P=13)
+    got = O.tree_verify_attention(q, kv, [0, 1], [P], [parent], 0.2, "f32", "f32")
+    qf, K, V = _decode_with_torch(kv, q, "f32")
+    for h in range(4):
+        g = h // 2
+        qt = torch.from_numpy(qf[0, h])[None, None, None]
+        o = torch.nn.functional.scaled_dot_product_attention(
+            qt, torch.from_numpy(K[g, : P + 1])[None, None], torch.from_numpy(V[g, : P + 1])[None, None], scale=0.2)
+        np.testing.assert_allclose(got[0, h], o[0, 0, 0].numpy(), atol=1e-13)
+
+
+@pytest.mark.parametrize("kv_dtype", ["f32", "bf16", "i8"])
+def test_linear_tree_attention_is_causal(kv_dtype):
+    parent, kv, q, P, T = _small_case(7, kv_dtype, T=9, P=11, tree="chain")
+    qd = "f32" if kv_dtype == "f32" else "bf16"
+    tree = O.tree_verify_attention(q, kv, [0, T], [P], [parent], 0.25, qd, kv_dtype)
+    causal = O.tree_verify_attention(q, kv, [0, T], [P], None, 0.25, qd, kv_dtype)
+    np.testing.assert_array_equal(tree, causal)
+    qf, K, V = _decode_with_torch(kv, q, kv_dtype)
+    tril = np.tril(np.ones((T, T), dtype=bool))
+    np.testing.assert_allclose(tree, sdpa_reference(qf, K, V, P, tril, 2, 0.25), atol=1e-12)
+
+
+def test_gqa_head_map():
+    """Query head h reads KV head h // G: with q = 0 and V constant per KV
+    head the output of head h is that head's constant."""
+    Hq, Hkv, D, P, T = 6, 3, 4, 5, 3
+    k = rng_for(970).standard_normal((1, Hkv, P + T, D)).astype(np.float32)
+    v = np.zeros((1, Hkv, P + T, D), np.float32)
+    for g in range(Hkv):
+        v[0, g] = g + 1
+    q = np.zeros((T, Hq, D), np.float32)
+    got = O.tree_verify_attention(q, {"k": k, "v": v}, [0, T], [P], [chain_tree(T)], 1.0, "f32", "f32")
+    for h in range(Hq):
+        np.testing.assert_allclose(got[:, h], h // 2 + 1, atol=1e-15)
+
+
+def test_int8_quantiser_and_dequant():
+    x = rng_for(980).standard_normal((64, 128)).astype(np.float32)
+    code, scale = quantize_int8_per_token(x)
+    deq = O.decode_kv(code, "i8", scale)
+    s = scale.astype(np.float64)[:, None]
+    assert (np.abs(deq - x) <= s / 2 + 1e-12).all()
+    assert (np.abs(code) <= 127).all() and (np.abs(code).max(axis=1) >= 126).all()
+    # a single-valued token maps every element to the same code (pages, gather_positions commit)
+    c, sc = quantize_int8_per_token(np.full((3, 128), 0.37, np.float32))
+    assert (c == c[:, :1]).all() and (c == 127).all()
+    # the zero token gives a zero scale and zero codes
+    c, sc = quantize_int8_per_token(np.zeros((1, 8), np.float32))
+    assert sc[0] == 0 and (c == 0).all()
+
+
+def test_bf16_decode_and_rounding():
+    x = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, -2.5, 3e-30, 65504.0], np.float32)
+    bits = to_bf16_bits(x)
+    t = torch.from_numpy(x).to(torch.bfloat16)
+    np.testing.assert_array_equal(bits.view(np.int16), t.view(torch.int16).numpy())
+    np.testing.assert_array_equal(O.decode_bf16(bits), t.double().numpy())
+
+
+# ---------------------------------------------------------------------------
+# Step 5: gather
+# ---------------------------------------------------------------------------
+
+def _cache(seed, dtype="i8", B=2, H=3, cap=40, D=8, unique=True):
+    from workloads import make_kv_cache
+    return make_kv_cache(990, seed, B, H, cap, D, dtype, unique_scales=unique)
+
+
+def test_prefix_selection_equals_trim_to():
+    c = _cache(0)
+    for n in (0, 1, 17, 40):
+        got = O.gather_layer(c, [np.arange(n)] * 2)
+        for name in c:
+            trimmed = c[name][:, :, :n]                  # trim_to(n): keep the first n rows
+            np.testing.assert_array_equal(got[name][:, :, :n], trimmed)
+            np.testing.assert_array_equal(got[name][:, :, n:], c[name][:, :, n:])
+
+
+def test_identity_selection_is_noop():
+    c = _cache(1)
+    got = O.gather_layer(c, [np.arange(40), np.arange(40)])
+    for name in c:
+        np.testing.assert_array_equal(got[name], c[name])
+
+
+def test_absolute_selection_equals_tail_form():
+    """gather_within_tail(tail_len, kept) keeps [0, tail_start) and writes the
+    kept block offsets to [tail_start, tail_start + len(kept)); the same
+    selection in absolute positions must give the same cache."""
+    c = _cache(2)
+    tail_start, kept = 30, np.array([0, 2, 3, 7, 9])
+    tail = {n: c[n].copy() for n in c}
+    for n in c:
+        tail[n][:, :, tail_start: tail_start + len(kept)] = c[n][:, :, tail_start + kept]
+    absolute = np.concatenate([np.arange(tail_start), tail_start + kept])
+    got = O.gather_layer(c, [absolute, absolute])
+    for n in c:
+        np.testing.assert_array_equal(got[n], tail[n])
+
+
+@pytest.mark.parametrize("T", [1, 4, 8, 16])
+def test_linear_tree_path_selection_equals_trim(T):
+    P = 20
+    c = _cache(3, cap=P + T)
+    for acc in range(T):
+        tok, tgt, _ = plant_walk(chain_tree(T), list(range(acc + 1)), rng_for(991, T, acc), 9)
+        path, _ = O.tree_accept_walk(chain_tree(T), tok, tgt)
+        sel = O.rollback_selection(P, path)
+        got = O.gather_layer(c, [sel, sel])
+        n = acc + 1                                    # chain rollback keeps P + n rows
+        trim = T - n
+        live = P + T - trim
+        for name in c:
+            np.testing.assert_array_equal(got[name][:, :, :live], c[name][:, :, :live])
+
+
+def test_scales_move_with_tokens():
+    c = _cache(4, unique=True)
+    sel = np.array([0, 1, 2, 5, 9, 10, 23, 39])
+    got = O.gather_layer(c, [sel, sel[:5]])
+    for b, s in enumerate([sel, sel[:5]]):
+        for h in range(3):
+            for j, src in enumerate(s):
+                assert got["k_scale"][b, h, j] == c["k_scale"][b, h, src]
+                assert (got["k"][b, h, j] == c["k"][b, h, src]).all()
+                assert got["v_scale"][b, h, j] == c["v_scale"][b, h, src]
+    # the scales are distinct per token, so leaving them behind is visible
+    assert (got["k_scale"][0, :, 3:8] != c["k_scale"][0, :, 3:8]).all()
+    assert len(np.unique(c["k_scale"][0, 0])) == 40
+
+
+def test_take_matches_row_loop():
+    c = _cache(5, dtype="bf16", unique=False)
+    sel = np.array([1, 4, 5, 6, 30])
+    got = O.gather_positions(c["k"][1], sel, axis=1)
+    for h in range(3):
+        for j, s in enumerate(sel):
+            np.testing.assert_array_equal(got[h, j], c["k"][1, h, s])
+
+
+def test_unique_scales_are_distinct():
+    s = unique_fp16_scales(rng_for(1), (2, 3, 500))
+    for row in s.reshape(-1, 500):
+        assert len(np.unique(row.view(np.uint16))) == 500 and np.isfinite(row).all() and (row > 0).all()
+
+
+# ---------------------------------------------------------------------------
+# Round: a linear tree behaves as the chain round
+# ---------------------------------------------------------------------------
+
+def test_linear_tree_round_equals_chain_round():
+    T, P, Hq, Hkv, D = 6, 12, 4, 2, 8
+    script = [T - 1, 2, 0, T - 1, 4, 0, 1]            # full, partial, zero accepts
+    kinds = set()
+    c = _cache(6, dtype="i8", B=1, H=Hkv, cap=P + T, D=D)
+    for r, acc in enumerate(script):
+        tok, tgt, _ = plant_walk(chain_tree(T), list(range(acc + 1)), rng_for(995, r), 40)
+        logits = planted_logits(rng_for(996, r), tgt, 40, 1.0)
+        am = O.vocab_argmax(logits)
+        path, emitted = O.tree_accept_walk(chain_tree(T), tok, am)
+        a, em_chain = speculative_walk(list(tok), list(am))
+        assert emitted == em_chain and len(path) - 1 == a == acc
+        kinds.add("full" if a == T - 1 else "zero" if a == 0 else "partial")
+        tree_cache = O.gather_layer(c, [O.rollback_selection(P, path)])
+        n = a + 1
+        live = P + T - (T - n)                         # kv.trim(block_size - n)
+        for name in c:
+            np.testing.assert_array_equal(tree_cache[name][:, :, :live], c[name][:, :, :live])
+    assert kinds == {"full", "partial", "zero"}
