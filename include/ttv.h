@@ -1,0 +1,233 @@
+/*
+ * ttv.h -- token-tree verification hot path on AMD Instinct MI355X (gfx950).
+ *
+ * One speculative verify round over a batch of draft trees:
+ *   tree_build_mask      ancestor bitsets from a per-round parent[] topology
+ *   tree_verify_attention tree-masked GQA attention over the KV prefix plus
+ *                        each node's ancestors
+ *   vocab_argmax         per-node argmax over the target's vocabulary logits
+ *   tree_accept_walk     descend the one child matching the target's argmax
+ *   kv_gather_positions  compact the accepted path's K/V (and int8 scales)
+ *                        along the sequence axis
+ *
+ * Sources are cited by page title and section:
+ *   [I1204]  mlxcel issue #1204 "perf(speculative): draft a tree instead of a
+ *            chain, so an MTP round emits more than 2.33 tokens"
+ *   [PR1212] mlxcel PR #1212 "feat(speculative): draft and verify a token
+ *            tree, behind a flag, default off" (its commit messages)
+ *   [S728]   splash issue #728 "Experiment: qualify shared-prefix tree
+ *            verification and conservative admission"
+ *
+ * Conventions for every call
+ *  - Pointers marked (device) are device memory; (host) are host memory.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL is the default
+ *    stream). The library never synchronises, never allocates and holds no
+ *    state apart from a thread-local error string. The caller owns every
+ *    buffer, including workspaces sized by the *_ws queries.
+ *  - Return value: TTV_OK, or an error code with a reason in ttv_last_error().
+ *    TTV_ERR_INVALID and TTV_ERR_UNSUPPORTED are decided on the host before
+ *    anything is launched, so nothing has been written when they return.
+ *  - Kernel-side validation (of data only the device sees) reports through a
+ *    caller-provided `dev_status` int32 (device): kernels only ever store a
+ *    nonzero TTV_DEV_* code into it, so the caller zeroes it beforehand and
+ *    reads it at its next synchronisation point.
+ *  - Limits: B <= TTV_MAX_BATCH sequences, T_b <= 64 nodes per tree.
+ */
+#ifndef TTV_H
+#define TTV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TTV_MAX_BATCH 128
+#define TTV_MAX_NODES 64
+
+typedef enum ttv_status {
+  TTV_OK = 0,
+  TTV_ERR_INVALID = 1,     /* malformed shapes/metadata; nothing launched */
+  TTV_ERR_UNSUPPORTED = 2, /* a named refusal: the caller must decline the tree round */
+  TTV_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the *_ws query */
+  TTV_ERR_HIP = 4          /* a HIP launch error */
+} ttv_status;
+
+/* Device-side status codes (stored into dev_status). */
+#define TTV_DEV_OK 0
+#define TTV_DEV_BAD_PARENT 1    /* parent[0] != -1 or parent[i] not in [0, i) */
+#define TTV_DEV_BAD_SELECTION 2 /* selection not strictly increasing / out of range / too long */
+
+typedef enum ttv_dtype {
+  TTV_F32 = 0,  /* float32 */
+  TTV_BF16 = 1, /* bfloat16 */
+  TTV_I8 = 2    /* int8 codes with fp16 per-token scale sidecars (KV only) */
+} ttv_dtype;
+
+/*
+ * A batch of draft trees. Sequence b owns block nodes
+ * [node_off[b], node_off[b+1]) of every node-indexed array, listed in
+ * topological order (parent precedes child; node 0 of each tree is its root,
+ * the last committed token) [I1204] "Increment 1". hist_len[b] is the live
+ * cache length before the verify block (P_b): the block's K/V rows are
+ * already appended at [P_b, P_b + T_b) in node order [PR1212] rollback-to-path
+ * commit. The host and device copies must hold the same values.
+ */
+typedef struct ttv_batch {
+  int32_t B;
+  const int32_t* node_off_h; /* (host)   [B+1], node_off[0] == 0, non-decreasing */
+  const int32_t* hist_len_h; /* (host)   [B] */
+  const int32_t* node_off_d; /* (device) [B+1] */
+  const int32_t* hist_len_d; /* (device) [B] */
+} ttv_batch;
+
+/*
+ * One layer's KV cache: k and v are [B][Hkv][cap][D] contiguous, the sequence
+ * axis third ([PR1212] commit widening the gather: every per-token buffer sits
+ * on axis 2). For TTV_I8, k_scale and v_scale are fp16 bit patterns
+ * [B][Hkv][cap], one scale per (token, KV head): value = code * scale.
+ */
+typedef struct ttv_kv_layer {
+  void* k;            /* (device) */
+  void* v;            /* (device) */
+  uint16_t* k_scale;  /* (device) fp16, required iff dtype == TTV_I8, else NULL */
+  uint16_t* v_scale;  /* (device) fp16, required iff dtype == TTV_I8, else NULL */
+  int32_t dtype;      /* ttv_dtype */
+  int32_t Hkv;
+  int32_t D;
+  int32_t cap;        /* allocated rows per (b, head) */
+} ttv_kv_layer;
+
+/*
+ * Step 1 -- ancestor mask [I1204] "What this needs" (1), "Increment 3";
+ * [PR1212] history-mask commit.
+ * For every node i: anc[i] bit j = 1 iff block node j is i or an ancestor of
+ * i; depth[i] = number of proper ancestors. Row i of the pages' additive mask
+ * [T, P+T] is open (0) on all P history columns and on block column j exactly
+ * when anc[i] bit j is set; the mask is rebuilt every round because the
+ * topology changes.
+ *   parent  (device) int32 [sum T_b], tree-local labels, parent[root] = -1
+ *   anc     (device) uint64 [sum T_b]   out
+ *   depth   (device) int32 [sum T_b]    out (may be NULL)
+ * A tree with an invalid parent[] stores TTV_DEV_BAD_PARENT and writes no
+ * anc/depth entry of that tree. Empty trees (T_b = 0) are allowed.
+ */
+ttv_status tree_build_mask(const ttv_batch* batch, const int32_t* parent, uint64_t* anc,
+                           int32_t* depth, int32_t* dev_status, void* stream);
+
+/*
+ * Interop/test form of step 1: expand sequence b's bitsets into the pages'
+ * dense additive mask out[T_b][P_b + T_b] (float32, row-major, device):
+ * 0 where open, `masked` (the pages use -1e9, [PR1212] Gemma 4 tree-verify
+ * commit) where blocked.
+ */
+ttv_status tree_mask_expand_additive(const ttv_batch* batch, int32_t b, const uint64_t* anc,
+                                     float masked, float* out, void* stream);
+
+/*
+ * Step 2 -- tree-masked GQA verify attention [I1204] "Redirection" (flatten the
+ * nodes into one sequence; the tree mask hides siblings); [PR1212] history-mask
+ * commit. For node i of sequence b and query head h (KV head g = h / (Hq/Hkv)):
+ *   out[i][h] = sum_j softmax_j(scale * q[i][h] . k[b][g][j]) * v[b][g][j]
+ * over j in [0, P_b) and j = P_b + a for every a with anc[i] bit a set.
+ *   q       (device) [sum T_b][Hq][D], q_dtype TTV_F32 or TTV_BF16
+ *   layer   (host)   descriptor; dtype TTV_F32, TTV_BF16 or TTV_I8
+ *   anc     (device) uint64 [sum T_b] from tree_build_mask, or NULL for the
+ *                    causal (linear) block mask: node i sees block rows 0..i.
+ *                    A linear tree's anc gives bit-identical output to NULL.
+ *   out     (device) float32 [sum T_b][Hq][D]
+ *   ws      (device) >= tree_verify_attention_ws(...) bytes. Its first bytes
+ *                    are split counters that must be zero before the first
+ *                    use; every completed call leaves them zero again.
+ * Supported: D in {64, 128}; F32 q requires F32 KV and vice versa (fp32 VALU
+ * path); BF16 q with BF16 or I8 KV (MFMA path when T_b * Hq/Hkv >= 16,
+ * otherwise VALU). Requires Hq % Hkv == 0, cap >= P_b + T_b.
+ * Concurrent calls on one GPU must not share a workspace.
+ */
+size_t tree_verify_attention_ws(const ttv_batch* batch, int32_t Hq, const ttv_kv_layer* layer,
+                                int32_t q_dtype);
+ttv_status tree_verify_attention(const ttv_batch* batch, const void* q, int32_t q_dtype, int32_t Hq,
+                                 const ttv_kv_layer* layer, const uint64_t* anc, float softmax_scale,
+                                 float* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Step 3 -- per-node argmax [I1204] "Increment 1" (the target emits one argmax
+ * per position); [S728] "Results" (raw F32 argmax).
+ *   logits  (device) float32, row r at logits + r * row_stride, vocab entries
+ *   out_idx (device) int32 [n_rows]: the lowest index of the row maximum.
+ * -0.0 and +0.0 compare equal; a NaN outranks every number and the first NaN
+ * wins. ws: >= vocab_argmax_ws(n_rows, vocab) bytes (may be 0).
+ */
+size_t vocab_argmax_ws(int64_t n_rows, int64_t vocab);
+ttv_status vocab_argmax(const float* logits, int64_t n_rows, int64_t vocab, int64_t row_stride,
+                        int32_t* out_idx, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Step 4 -- accept walk [I1204] "What this needs" (2), "Increment 1"; [S728]
+ * "What it does". Per tree: cur = 0, path = [0]; repeat: the child of cur
+ * with the lowest label whose token equals target_argmax[cur] is appended and
+ * becomes cur; stop when none matches. accepted = path_len - 1 and
+ * emitted[k] = target_argmax[path[k]] (accepted + 1 tokens).
+ *   parent, token, target_argmax (device) int32 [sum T_b] (tree-local labels)
+ *   path     (device) int32 [B][64]  out (entries beyond path_len untouched)
+ *   path_len (device) int32 [B]      out
+ *   emitted  (device) int32 [B][64]  out
+ *   sel      (device) int32 [B][sel_stride] out or NULL: the rollback
+ *            selection [0, P_b) ++ (P_b + path[k]) ([PR1212] rollback-to-path
+ *            commit), ready for kv_gather_positions with sel_len = path_len +
+ *            P_b (written into sel_len_out when not NULL).
+ *   sel_len_out (device) int32 [B] out or NULL
+ * sel_stride must be >= max_b(P_b + T_b) when sel is given. An invalid
+ * parent[] stores TTV_DEV_BAD_PARENT and writes nothing for that tree.
+ */
+ttv_status tree_accept_walk(const ttv_batch* batch, const int32_t* parent, const int32_t* token,
+                            const int32_t* target_argmax, int32_t* path, int32_t* path_len,
+                            int32_t* emitted, int32_t* sel, int32_t sel_stride, int32_t* sel_len_out,
+                            int32_t* dev_status, void* stream);
+
+/*
+ * Step 5 -- rollback by gather along the sequence axis [I1204] "The rollback
+ * constraint"; [PR1212] gather_positions commit, the commit widening it,
+ * gather_within_tail commit. For every layer l, sequence b, head h and
+ * j < sel_len[b]:
+ *   dst.k[b][h][j] = src.k[b][h][sel[b][j]], likewise v and, for I8, the
+ *   k_scale/v_scale sidecars (scales always move with their tokens).
+ *   src, dst (host) arrays of n_layers descriptors. dst == NULL or every
+ *            dst[l] describing the same buffers as src[l] means in place;
+ *            otherwise dst must not overlap src. Shapes/dtypes must match.
+ *   sel      (device) int32 [B][sel_stride], strictly increasing, each entry
+ *            in [0, live_len_h[b]).
+ *   sel_len  (device) int32 [B], 0 <= sel_len[b] <= live_len_h[b].
+ *   live_len_h (host) int32 [B] current live rows per sequence.
+ * All-or-nothing: a device-side check runs first; if any sequence's selection
+ * is malformed, TTV_DEV_BAD_SELECTION is stored and no buffer is written.
+ * In place, rows before the first j with sel[j] != j stay where they are, so an
+ * identity or prefix selection (trim_to) moves 0 bytes and a tree rollback
+ * moves only the accepted path's rows. Out of place, every survivor is written
+ * (the pages' take). Rows at and beyond sel_len are not touched; the new live
+ * length is sel_len[b].
+ * ws: >= kv_gather_positions_ws(B) bytes.
+ */
+size_t kv_gather_positions_ws(int32_t B);
+ttv_status kv_gather_positions(const ttv_kv_layer* src, const ttv_kv_layer* dst, int32_t n_layers,
+                               int32_t B, const int32_t* sel, int32_t sel_stride,
+                               const int32_t* sel_len, const int32_t* live_len_h,
+                               int32_t* dev_status, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Capability question asked before a tree is drafted [PR1212] the
+ * tree_round_is_available and verify_finalize_tree commits: once the block is
+ * on the cache a refusal has no recovery. Returns TTV_OK when every layer can
+ * be verified as a tree and rolled back by kv_gather_positions, else
+ * TTV_ERR_UNSUPPORTED (or TTV_ERR_INVALID) with the reason in ttv_last_error().
+ */
+ttv_status kv_can_gather(const ttv_kv_layer* layers, int32_t n_layers);
+
+/* Reason for the last non-OK status returned on this thread ("" if none). */
+const char* ttv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TTV_H */

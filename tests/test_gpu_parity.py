@@ -1,0 +1,446 @@
+"""GPU parity: every step of the HIP path against the CPU oracle on the same
+seeded inputs. Integer/index/byte outputs must match bit for bit; attention
+within max-abs 2e-3 (bf16 or int8 KV, fp32 accumulation) or 1e-5 (fp32)."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from workloads import (binary_tree_7, chain_tree, config1_round, config2_round, config3_round, config4_round,
+                       confidence_tree, host_tensors, make_kv_cache, make_queries, plant_walk, planted_logits,
+                       random_descent, random_tree, rng_for, sary_tree)
+
+from gpu_util import (layer_to_dev, layer_to_host, log, run_argmax, run_attention, run_mask, run_walk, spec_batch,
+                      status, to_dev, to_host, zeros_ws)
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 2e-3
+TOL_F32 = 1e-5
+
+
+@pytest.fixture(scope="module")
+def ttv():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from gpu_util import binding
+    return binding()
+
+
+def _batch_of(ttv, parents, hist):
+    node_off = np.zeros(len(parents) + 1, np.int32)
+    node_off[1:] = np.cumsum([len(p) for p in parents])
+    return ttv.Batch(node_off, hist), node_off
+
+
+def _trees(n=40):
+    out = [chain_tree(1), chain_tree(2), chain_tree(64), sary_tree(3, 3), sary_tree(2, 5), np.zeros(0, np.int32)]
+    for s in range(n):
+        out.append(binary_tree_7(rng_for(1100, s)))
+        out.append(random_tree(rng_for(1101, s), int(rng_for(1102, s).integers(1, 65))))
+        out.append(confidence_tree(rng_for(1103, s), 16, 8, 1000, 4)[0])
+    return out
+
+
+# ---------------------------------------------------------------- mask ----
+
+def test_mask_matches_oracle(ttv):
+    trees = _trees()
+    batch, off = _batch_of(ttv, trees, [0] * len(trees))
+    log(f"mask: {len(trees)} trees, {off[-1]} nodes")
+    par = to_dev(np.concatenate(trees).astype(np.int32))
+    anc, depth, st = run_mask(ttv, batch, par)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    got_a = to_host(anc).view(np.uint64)
+    got_d = to_host(depth)
+    for b, p in enumerate(trees):
+        if len(p) == 0:
+            continue
+        np.testing.assert_array_equal(got_a[off[b]:off[b + 1]], O.ancestor_bits(p))
+        np.testing.assert_array_equal(got_d[off[b]:off[b + 1]], O.node_depths(p))
+
+
+def test_mask_invalid_parent_writes_nothing_for_that_tree(ttv):
+    good = binary_tree_7(rng_for(1110))
+    bad = np.array([-1, 0, 2, 1], np.int32)       # parent[2] = 2 is not an earlier node
+    trees = [good, bad, chain_tree(5)]
+    batch, off = _batch_of(ttv, trees, [3, 3, 3])
+    anc, depth, st = run_mask(ttv, batch, to_dev(np.concatenate(trees)))
+    torch.cuda.synchronize()
+    assert int(st.item()) == ttv.TTV_DEV_BAD_PARENT
+    a = to_host(anc)
+    assert (a[off[1]:off[2]] == -1).all()
+    np.testing.assert_array_equal(a.view(np.uint64)[off[2]:off[3]], O.ancestor_bits(chain_tree(5)))
+    np.testing.assert_array_equal(a.view(np.uint64)[:off[1]], O.ancestor_bits(good))
+
+
+def test_mask_expand_additive_matches_oracle(ttv):
+    for s in range(6):
+        parent = random_tree(rng_for(1120, s), int(rng_for(1121, s).integers(1, 65)))
+        P = [0, 1, 7, 64, 200, 1000][s]
+        batch, off = _batch_of(ttv, [chain_tree(3), parent], [5, P])
+        anc, depth, st = run_mask(ttv, batch, to_dev(np.concatenate([chain_tree(3), parent])))
+        out = torch.zeros(len(parent), P + len(parent), dtype=torch.float32, device="cuda")
+        ttv.tree_mask_expand_additive(batch, 1, anc, -1e9, out)
+        np.testing.assert_array_equal(to_host(out), O.additive_mask_with_history(parent, P))
+
+
+# ---------------------------------------------------------------- walk ----
+
+def _walk_cases():
+    cases = []
+    for acc in range(3):
+        cases.append(config1_round(accepted=acc))
+    cases.append(config1_round(accepted=2, equal_sibling=True))
+    cases.append(config1_round(accepted=1, equal_sibling=True))
+    for T in (3, 4, 8):
+        for acc in range(T):
+            cases.append(config2_round(T, acc))
+    cases.append(config3_round(P=8, L=1))
+    cases.append(config3_round(P=8, L=1, worst_case=True, stream=3))
+    trees, toks, tgts, hist = [], [], [], []
+    for c in cases:
+        trees.append(c.parents[0])
+        toks.append(c.tokens[0])
+        tgts.append(c.targets[0])
+        hist.append(int(c.hist_len[0]))
+    spec4 = config4_round(B=32, pmin=1, pmax=300)
+    trees += spec4.parents
+    toks += spec4.tokens
+    tgts += spec4.targets
+    hist += [int(h) for h in spec4.hist_len]
+    for s in range(30):   # unplanted tokens over a 3-token vocabulary: many equal-token siblings
+        r = rng_for(1130, s)
+        T = int(r.integers(1, 65))
+        trees.append(random_tree(r, T))
+        toks.append(r.integers(0, 3, size=T))
+        tgts.append(r.integers(0, 3, size=T))
+        hist.append(int(r.integers(0, 50)))
+    return trees, toks, tgts, hist
+
+
+def test_walk_matches_oracle(ttv):
+    trees, toks, tgts, hist = _walk_cases()
+    trees, toks, tgts, hist = trees[:128], toks[:128], tgts[:128], hist[:128]
+    batch, off = _batch_of(ttv, trees, hist)
+    log(f"walk: {len(trees)} trees")
+    path, plen, em, sel, sel_len, st = run_walk(
+        ttv, batch, to_dev(np.concatenate(trees).astype(np.int32)), to_dev(np.concatenate(toks).astype(np.int32)),
+        to_dev(np.concatenate(tgts).astype(np.int32)))
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    path, plen, em, sel, sel_len = map(to_host, (path, plen, em, sel, sel_len))
+    n_partial = n_zero = n_full = 0
+    for b in range(len(trees)):
+        want_path, want_em = O.tree_accept_walk(trees[b], toks[b], tgts[b])
+        L = len(want_path)
+        assert plen[b] == L, b
+        assert list(path[b, :L]) == want_path, b
+        assert list(em[b, :L]) == want_em, b
+        assert (path[b, L:] == -3).all() and (em[b, L:] == -3).all()
+        want_sel = O.rollback_selection(hist[b], want_path)
+        assert sel_len[b] == len(want_sel)
+        np.testing.assert_array_equal(sel[b, :len(want_sel)], want_sel)
+        n_zero += L == 1
+        n_partial += 1 < L < len(trees[b])
+    assert n_zero > 0 and n_partial > 0
+
+
+def test_walk_invalid_parent(ttv):
+    trees = [chain_tree(4), np.array([0, 0, 1], np.int32)]   # second tree has no root
+    batch, off = _batch_of(ttv, trees, [2, 2])
+    flat = np.concatenate(trees)
+    path, plen, em, sel, sel_len, st = run_walk(ttv, batch, to_dev(flat), to_dev(np.zeros(len(flat), np.int32)),
+                                                 to_dev(np.zeros(len(flat), np.int32)))
+    torch.cuda.synchronize()
+    assert int(st.item()) == ttv.TTV_DEV_BAD_PARENT
+    assert to_host(plen)[1] == -3 and to_host(plen)[0] == 4
+
+
+# -------------------------------------------------------------- argmax ----
+
+def _check_argmax(ttv, X, label):
+    log(f"argmax: {label} {X.shape}")
+    got = to_host(run_argmax(ttv, to_dev(X)))
+    np.testing.assert_array_equal(got, O.vocab_argmax(X))
+
+
+def test_argmax_config_shapes(ttv):
+    c1 = config1_round()
+    _check_argmax(ttv, host_tensors(c1)["logits"], "config 1")
+    c2 = config2_round(8, 3)
+    X = planted_logits(rng_for(1140), c2.flat_targets, 248320, 2.0)
+    _check_argmax(ttv, X, "config 2")
+    c3 = config3_round(P=8, L=1)
+    _check_argmax(ttv, planted_logits(rng_for(1141), c3.flat_targets, 248320, 2.0), "config 3")
+
+
+def test_argmax_ties_zero_nan_and_tails(ttv):
+    V = 248320
+    r = rng_for(1150)
+    X = (r.standard_normal((24, V)).astype(np.float32) * 2)
+    m = float(X.max()) + 3
+    for i in range(8):              # ties across many candidate chunk boundaries and the tail
+        pos = np.unique(np.concatenate([r.integers(0, V, 3), [V - 1, V - 2, 2047, 2048, 4095, 4096,
+                                                             15519, 15520, 124159, 124160]]))
+        X[i, pos[i % len(pos):]] = m
+    X[8, :] = -np.inf
+    X[9, :] = -np.inf; X[9, V - 1] = -1
+    X[10, 100] = np.nan; X[10, 50000] = np.nan
+    X[11, :] = 0.0; X[11, :1000] = -0.0; X[11, 0] = -0.0
+    X[12, :] = -1.0; X[12, 70001] = -0.0; X[12, 70000] = 0.0; X[12, 9] = -0.0
+    X[13, 200000] = np.inf; X[13, 7] = np.inf
+    X[14, :] = 5.0
+    X[15, ::2] = np.nan
+    X[16] = -X[16]; X[16, V - 1] = m
+    _check_argmax(ttv, X, "ties/zero/nan")
+    # unaligned row stride forces the scalar path
+    Y = np.ascontiguousarray(X[:, :V - 3])
+    Yd = to_dev(np.ascontiguousarray(np.pad(Y, ((0, 0), (0, 1)))))
+    out = torch.full((24,), -7, dtype=torch.int32, device="cuda")
+    ttv.vocab_argmax(Yd, out, zeros_ws(ttv.vocab_argmax_ws(24, V - 3)), vocab=V - 3)
+    np.testing.assert_array_equal(to_host(out), O.vocab_argmax(Y))
+
+
+def test_argmax_many_rows_and_small_vocab(ttv):
+    r = rng_for(1160)
+    _check_argmax(ttv, r.integers(-2, 3, size=(1500, 257)).astype(np.float32), "1500 x 257 ints")
+    _check_argmax(ttv, r.standard_normal((3, 5)).astype(np.float32), "3 x 5")
+    X = r.standard_normal((1150, 248320)).astype(np.float32)
+    _check_argmax(ttv, X, "config 4 rows")
+
+
+# -------------------------------------------------------------- gather ----
+
+def _gather_case(ttv, dtype, in_place, sels, B=3, L=2, H=2, D=64, cap=700, seed=0):
+    host = [make_kv_cache(1170 + seed, l, B, H, cap, D, dtype, unique_scales=(dtype == "i8")) for l in range(L)]
+    devs, layers = zip(*[layer_to_dev(ttv, h) for h in host])
+    live = np.array([cap - 3 * b for b in range(B)], np.int32)
+    stride = cap + 5
+    sel = np.full((B, stride), -1, np.int32)
+    for b, s in enumerate(sels):
+        sel[b, :len(s)] = s
+    sel_len = np.array([len(s) for s in sels], np.int32)
+    if in_place:
+        dst_layers, dst_devs = None, devs
+        base = host
+    else:
+        dst_host = [{n: np.zeros_like(a) for n, a in h.items()} for h in host]
+        for h in dst_host:          # poison
+            for n, a in h.items():
+                a.view(np.uint8)[...] = 0xA5
+        dst_devs, dst_layers = zip(*[layer_to_dev(ttv, h) for h in dst_host])
+        base = dst_host
+    st = status()
+    ttv.kv_gather_positions(list(layers), None if in_place else list(dst_layers), to_dev(sel), to_dev(sel_len),
+                            live, st, zeros_ws(ttv.kv_gather_positions_ws(B)))
+    torch.cuda.synchronize()
+    got = [layer_to_host(d) for d in dst_devs]
+    return host, base, got, int(st.item()), live
+
+
+def _selections(rng, live, kind):
+    out = []
+    for b, n in enumerate(live):
+        if kind == "rollback":
+            P = int(n) - 16
+            path = [0] + sorted(rng.choice(np.arange(1, 16), size=int(rng.integers(0, 8)), replace=False).tolist())
+            out.append(O.rollback_selection(P, path))
+        elif kind == "prefix":
+            out.append(np.arange(int(rng.integers(0, n + 1))))
+        elif kind == "identity":
+            out.append(np.arange(n))
+        elif kind == "scatter":
+            out.append(np.sort(rng.choice(n, size=n // 2, replace=False)))
+        elif kind == "wide":  # long in-place span: moved rows exceed one chunk
+            keep = np.ones(n, bool)
+            keep[5:n:3] = False
+            out.append(np.nonzero(keep)[0])
+        elif kind == "empty":
+            out.append(np.zeros(0, np.int64))
+    return out
+
+
+@pytest.mark.parametrize("dtype,D", [("i8", 64), ("i8", 128), ("bf16", 128), ("f32", 64)])
+@pytest.mark.parametrize("in_place", [True, False])
+@pytest.mark.parametrize("kind", ["rollback", "prefix", "identity", "scatter", "wide", "empty"])
+def test_gather_matches_oracle(ttv, dtype, D, in_place, kind):
+    rng = rng_for(1180, hash((dtype, D, in_place, kind)) % 1000)
+    B, cap = 3, 700
+    live = np.array([cap - 3 * b for b in range(B)])
+    sels = _selections(rng, live, kind)
+    log(f"gather: {dtype} D={D} in_place={in_place} {kind}")
+    host, base, got, st, live = _gather_case(ttv, dtype, in_place, sels, B=B, D=D, cap=cap)
+    assert st == 0
+    for l in range(len(host)):
+        kv = {n: a for n, a in host[l].items()}
+        want = O.gather_layer(kv, sels, base=base[l])
+        for n in want:
+            np.testing.assert_array_equal(got[l][n], want[n], err_msg=f"layer {l} {n}")
+
+
+@pytest.mark.parametrize("in_place", [True, False])
+def test_gather_bad_selection_writes_nothing(ttv, in_place):
+    rng = rng_for(1190)
+    live = np.array([700, 697, 694])
+    sels = _selections(rng, live, "rollback")
+    sels[1] = sels[1].copy()
+    sels[1][-1], sels[1][-2] = sels[1][-2], sels[1][-1]      # not increasing
+    host, base, got, st, _ = _gather_case(ttv, "i8", in_place, sels)
+    assert st == ttv.TTV_DEV_BAD_SELECTION
+    for l in range(len(host)):
+        for n in host[l]:
+            np.testing.assert_array_equal(got[l][n], base[l][n])
+    sels = _selections(rng, live, "prefix")
+    sels[2] = np.array([0, 5, 694])                            # out of range (live 694)
+    host, base, got, st, _ = _gather_case(ttv, "bf16", in_place, sels, D=128)
+    assert st == ttv.TTV_DEV_BAD_SELECTION
+    for l in range(len(host)):
+        for n in host[l]:
+            np.testing.assert_array_equal(got[l][n], base[l][n])
+
+
+# ----------------------------------------------------------- attention ----
+
+def _attn_check(ttv, spec, tensors, tol, layers=None, anc_mode="tree", label=""):
+    batch = spec_batch(ttv, spec)
+    scale = 1.0 / math.sqrt(spec.D)
+    par = to_dev(spec.flat("parents"))
+    anc, _, st = run_mask(ttv, batch, par)
+    worst = 0.0
+    for li in (range(spec.L) if layers is None else layers):
+        host = tensors["layers"][li]
+        dev, kvl = layer_to_dev(ttv, host)
+        q = to_dev(host["q"], "bf16" if spec.q_dtype == "bf16" else None)
+        out, ws = run_attention(ttv, batch, q, kvl, None if anc_mode == "causal" else anc, scale)
+        torch.cuda.synchronize()
+        parents = None if anc_mode == "causal" else spec.parents
+        want = O.tree_verify_attention(host["q"], {k: v for k, v in host.items() if k != "q"}, spec.node_off,
+                                       spec.hist_len, parents, scale, spec.q_dtype, spec.kv_dtype)
+        g = to_host(out)
+        assert np.isfinite(g).all()
+        err = float(np.abs(g - want).max()) if g.size else 0.0
+        worst = max(worst, err)
+        log(f"attention {label} layer {li}: max|err| {err:.3e}")
+        assert err <= tol, (label, li, err)
+    assert int(st.item()) == 0
+    return worst
+
+
+def test_attention_config1_fp32(ttv):
+    for acc in range(3):
+        spec = config1_round(accepted=acc)
+        _attn_check(ttv, spec, host_tensors(spec), TOL_F32, label=f"config1 acc={acc}")
+
+
+@pytest.mark.parametrize("T", [3, 4, 8])
+def test_attention_config2_chain_equals_causal(ttv, T):
+    spec = config2_round(T, T // 2)
+    tensors = host_tensors(spec)
+    _attn_check(ttv, spec, tensors, TOL_BF16, label=f"config2 T={T} tree")
+    _attn_check(ttv, spec, tensors, TOL_BF16, anc_mode="causal", label=f"config2 T={T} causal")
+    # the linear tree's bitsets and anc = NULL give bit-identical outputs
+    batch = spec_batch(ttv, spec)
+    host = tensors["layers"][0]
+    dev, kvl = layer_to_dev(ttv, host)
+    q = to_dev(host["q"], "bf16")
+    anc, _, _ = run_mask(ttv, batch, to_dev(spec.flat("parents")))
+    o1, _ = run_attention(ttv, batch, q, kvl, anc, 1 / math.sqrt(128))
+    o2, _ = run_attention(ttv, batch, q, kvl, None, 1 / math.sqrt(128))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+def test_attention_config3_int8_16_layers(ttv):
+    spec = config3_round()
+    _attn_check(ttv, spec, host_tensors(spec), TOL_BF16, label="config3")
+
+
+GRID = [
+    # (kv dtype, T, P, tree kind, Hq, Hkv)
+    ("bf16", 1, 0, "chain", 40, 8), ("bf16", 1, 1, "chain", 40, 8), ("bf16", 2, 31, "random", 40, 8),
+    ("bf16", 16, 32, "random", 40, 8), ("bf16", 33, 33, "random", 40, 8), ("bf16", 64, 100, "random", 40, 8),
+    ("bf16", 64, 5000, "random", 40, 8), ("bf16", 40, 3000, "sary", 40, 8), ("bf16", 13, 777, "random", 16, 16),
+    ("i8", 1, 0, "chain", 40, 8), ("i8", 3, 65, "random", 40, 8), ("i8", 16, 4095, "conf", 40, 8),
+    ("i8", 64, 2000, "random", 40, 8), ("i8", 7, 9000, "random", 32, 4),
+    ("f32", 7, 64, "binary", 4, 2), ("f32", 64, 300, "random", 8, 2), ("f32", 1, 0, "chain", 4, 2),
+]
+
+
+@pytest.mark.parametrize("case", range(len(GRID)))
+def test_attention_grid(ttv, case):
+    kv, T, P, kind, Hq, Hkv = GRID[case]
+    r = rng_for(1200, case)
+    parent = {"chain": chain_tree(T), "random": random_tree(r, T), "sary": sary_tree(3, 3)[:T],
+              "conf": confidence_tree(r, T, 8, 1000, 4)[0], "binary": binary_tree_7(r)[:T]}[kind]
+    D = 64 if kv == "f32" else 128
+    qd = "f32" if kv == "f32" else "bf16"
+    from workloads.configs import _spec
+    spec = _spec(1200 + case, 1, 1, Hq, Hkv, D, 16, 1.0, kv, qd, [P], [parent], [np.zeros(T, np.int64)],
+                 [np.zeros(T, np.int64)], [[0]])
+    tensors = {"layers": [dict(make_kv_cache(1201, case, 1, Hkv, P + T + 3, D, kv),
+                               q=make_queries(1202, case, T, Hq, D, qd))]}
+    _attn_check(ttv, spec, tensors, TOL_F32 if kv == "f32" else TOL_BF16, label=f"grid {GRID[case]}")
+
+
+def test_attention_ragged_batch(ttv):
+    spec = config4_round(B=12, pmin=0, pmax=2500)
+    spec.parents[3] = np.zeros(0, np.int32)        # an empty tree in the middle of the batch
+    spec.tokens[3] = np.zeros(0, np.int64)
+    spec.targets[3] = np.zeros(0, np.int64)
+    _attn_check(ttv, spec, host_tensors(spec), TOL_BF16, label="ragged B=12")
+    _attn_check(ttv, spec, host_tensors(spec), TOL_BF16, anc_mode="causal", label="ragged causal")
+
+
+def test_attention_workspace_reuse_across_shapes(ttv):
+    """Split counters return to zero after every call, so one workspace serves
+    calls of different shapes back to back."""
+    big = config3_round(P=6000, L=1)
+    small = config2_round(8, 2)
+    tb, ts = host_tensors(big), host_tensors(small)
+    ws = zeros_ws(64 << 20)
+    for spec, tens in ((big, tb), (small, ts), (big, tb)):
+        batch = spec_batch(ttv, spec)
+        anc, _, _ = run_mask(ttv, batch, to_dev(spec.flat("parents")))
+        host = tens["layers"][0]
+        dev, kvl = layer_to_dev(ttv, host)
+        out, _ = run_attention(ttv, batch, to_dev(host["q"], "bf16"), kvl, anc, 1 / math.sqrt(128), ws=ws)
+        torch.cuda.synchronize()
+        want = O.tree_verify_attention(host["q"], {k: v for k, v in host.items() if k != "q"}, spec.node_off,
+                                       spec.hist_len, spec.parents, 1 / math.sqrt(128), "bf16", spec.kv_dtype)
+        assert float(np.abs(to_host(out) - want).max()) <= TOL_BF16
+    assert int(ws[:4096].view(torch.int32).abs().sum().item()) == 0
+
+
+# --------------------------------------------------------------- round ----
+
+@pytest.mark.parametrize("acc,dup", [(0, False), (1, False), (2, False), (2, True)])
+def test_round_config1_end_to_end(ttv, acc, dup):
+    spec = config1_round(accepted=acc, equal_sibling=dup)
+    tens = host_tensors(spec)
+    want = O.verify_round(spec, tens)
+    batch = spec_batch(ttv, spec)
+    par = to_dev(spec.flat("parents"))
+    anc, depth, st = run_mask(ttv, batch, par)
+    host = tens["layers"][0]
+    dev, kvl = layer_to_dev(ttv, host)
+    out, _ = run_attention(ttv, batch, to_dev(host["q"]), kvl, anc, 1 / math.sqrt(spec.D))
+    am = run_argmax(ttv, to_dev(tens["logits"]))
+    path, plen, em, sel, sel_len, st2 = run_walk(ttv, batch, par, to_dev(spec.flat("tokens").astype(np.int32)), am)
+    st3 = status()
+    ttv.kv_gather_positions([kvl], None, sel, sel_len, spec.hist_len + np.diff(spec.node_off), st3,
+                            zeros_ws(ttv.kv_gather_positions_ws(1)))
+    torch.cuda.synchronize()
+    assert int(st.item()) == int(st2.item()) == int(st3.item()) == 0
+    np.testing.assert_array_equal(to_host(anc).view(np.uint64), want["anc"])
+    assert float(np.abs(to_host(out) - want["attn"][0]).max()) <= TOL_F32
+    np.testing.assert_array_equal(to_host(am), want["argmax"])
+    L = int(to_host(plen)[0])
+    assert list(to_host(path)[0, :L]) == want["paths"][0] == spec.paths[0]
+    assert list(to_host(em)[0, :L]) == want["emitted"][0]
+    got = layer_to_host(dev)
+    for n in want["caches"][0]:
+        np.testing.assert_array_equal(got[n], want["caches"][0][n])

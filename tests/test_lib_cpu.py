@@ -1,0 +1,159 @@
+"""CPU-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and its host-side validation refuses malformed calls before
+anything is launched (no call here reaches a kernel launch)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ttv.h")
+
+ttv = pytest.importorskip("token_tree_verification_build_amd",
+                          reason="libttv.so not built (run __graft_entry__.build())")
+C = ttv._c
+FAKE = 0x10000  # never dereferenced: every call below fails validation on the host
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:ttv_status|size_t|const char\*)\s+(\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = header_functions()
+    assert len(names) >= 11
+    lib = ctypes.CDLL(ttv.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(ttv.EXPORTED)
+
+
+def batch(node_off, hist, dev=True):
+    no = np.ascontiguousarray(node_off, dtype=np.int32)
+    hl = np.ascontiguousarray(hist, dtype=np.int32)
+    b = ttv.TtvBatch(len(hl), no.ctypes.data, hl.ctypes.data, FAKE if dev else None, FAKE if dev else None)
+    return b, (no, hl)
+
+
+def layer(dtype=ttv.TTV_BF16, Hkv=8, D=128, cap=4096, scales=False):
+    s = FAKE if scales else None
+    return ttv.TtvKvLayer(FAKE, FAKE, s, s, dtype, Hkv, D, cap)
+
+
+def test_last_error_empty_after_ok_query():
+    b, keep = batch([0, 4], [10])
+    assert C["tree_verify_attention_ws"](ctypes.byref(b), 40, ctypes.byref(layer()), ttv.TTV_BF16) > 0
+    st, msg = ttv.kv_can_gather_raw([layer()])
+    assert st == ttv.TTV_OK and msg == ""
+
+
+def test_mask_rejects_oversized_tree():
+    b, keep = batch([0, 65], [0])
+    st = C["tree_build_mask"](ctypes.byref(b), FAKE, FAKE, FAKE, FAKE, None)
+    assert st == ttv.TTV_ERR_INVALID and "65 nodes" in ttv.last_error()
+
+
+def test_mask_rejects_bad_offsets_and_batch():
+    b, keep = batch([1, 3], [0])
+    assert C["tree_build_mask"](ctypes.byref(b), FAKE, FAKE, FAKE, FAKE, None) == ttv.TTV_ERR_INVALID
+    b, keep = batch([0, 5, 3], [0, 0])
+    assert C["tree_build_mask"](ctypes.byref(b), FAKE, FAKE, FAKE, FAKE, None) == ttv.TTV_ERR_INVALID
+    no = np.zeros(ttv.MAX_BATCH + 2, np.int32)
+    hl = np.zeros(ttv.MAX_BATCH + 1, np.int32)
+    b = ttv.TtvBatch(ttv.MAX_BATCH + 1, no.ctypes.data, hl.ctypes.data, FAKE, FAKE)
+    assert C["tree_build_mask"](ctypes.byref(b), FAKE, FAKE, FAKE, FAKE, None) == ttv.TTV_ERR_INVALID
+    b, keep = batch([0, 3], [-1])
+    assert C["tree_build_mask"](ctypes.byref(b), FAKE, FAKE, FAKE, FAKE, None) == ttv.TTV_ERR_INVALID
+
+
+def test_mask_null_pointers():
+    b, keep = batch([0, 3], [0])
+    assert C["tree_build_mask"](ctypes.byref(b), None, FAKE, FAKE, FAKE, None) == ttv.TTV_ERR_INVALID
+
+
+def _attn(b, Hq, L, q_dtype=ttv.TTV_BF16, ws_bytes=1 << 40):
+    return C["tree_verify_attention"](ctypes.byref(b), FAKE, q_dtype, Hq, ctypes.byref(L), None, 0.1, FAKE,
+                                      FAKE, ws_bytes, None)
+
+
+def test_attention_validation():
+    b, keep = batch([0, 16], [4096])
+    assert _attn(b, 42, layer()) == ttv.TTV_ERR_INVALID            # Hq % Hkv
+    assert "multiple" in ttv.last_error()
+    assert _attn(b, 40, layer(D=96)) == ttv.TTV_ERR_INVALID        # head dim
+    assert _attn(b, 40, layer(cap=4100)) == ttv.TTV_ERR_INVALID    # cap < P + T
+    assert "cache holds" in ttv.last_error()
+    assert _attn(b, 40, layer(dtype=ttv.TTV_I8, cap=8192)) == ttv.TTV_ERR_UNSUPPORTED   # no scale sidecars
+    assert _attn(b, 40, layer(dtype=ttv.TTV_F32, cap=8192)) == ttv.TTV_ERR_UNSUPPORTED  # bf16 q with f32 KV
+    assert _attn(b, 40, layer(cap=8192), q_dtype=ttv.TTV_F32) == ttv.TTV_ERR_UNSUPPORTED
+    assert _attn(b, 40, layer(cap=8192), ws_bytes=16) == ttv.TTV_ERR_WORKSPACE
+
+
+def test_attention_ws_sizes():
+    L = layer(dtype=ttv.TTV_I8, scales=True, cap=140000)
+    b, keep = batch(np.arange(9) * 16, [131072] * 8)
+    n = C["tree_verify_attention_ws"](ctypes.byref(b), 40, ctypes.byref(L), ttv.TTV_BF16)
+    assert 0 < n < 512 << 20
+    bad, keep2 = batch([0, 16], [4096])
+    assert C["tree_verify_attention_ws"](ctypes.byref(bad), 41, ctypes.byref(L), ttv.TTV_BF16) == 0
+
+
+def test_argmax_validation():
+    f = C["vocab_argmax"]
+    assert f(FAKE, 4, 100, 99, FAKE, None, 0, None) == ttv.TTV_ERR_INVALID       # stride < vocab
+    assert f(FAKE, 4, 0, 0, FAKE, None, 0, None) == ttv.TTV_ERR_INVALID          # empty vocab
+    assert f(FAKE, 0, 10, 10, FAKE, None, 0, None) == ttv.TTV_OK                 # no rows: nothing to do
+    need = C["vocab_argmax_ws"](3, 248320)
+    assert need > 0
+    assert f(FAKE, 3, 248320, 248320, FAKE, FAKE, need - 8, None) == ttv.TTV_ERR_WORKSPACE
+    assert C["vocab_argmax_ws"](4096, 1024) == 0
+
+
+def test_walk_validation():
+    b, keep = batch([0, 0], [5])
+    f = C["tree_accept_walk"]
+    assert f(ctypes.byref(b), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None, FAKE, None) == ttv.TTV_ERR_INVALID
+    b, keep = batch([0, 4], [5])
+    assert f(ctypes.byref(b), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, None, FAKE, None) == ttv.TTV_ERR_INVALID
+    assert "sel_stride" in ttv.last_error()
+
+
+def test_can_gather_refusals():
+    st, msg = ttv.kv_can_gather_raw([layer(dtype=ttv.TTV_I8)])
+    assert st == ttv.TTV_ERR_UNSUPPORTED and "scale" in msg
+    st, msg = ttv.kv_can_gather_raw([layer(), ttv.TtvKvLayer(None, FAKE, None, None, ttv.TTV_BF16, 8, 128, 64)])
+    assert st == ttv.TTV_ERR_UNSUPPORTED and "layer 1" in msg
+    st, msg = ttv.kv_can_gather_raw([layer(dtype=7)])
+    assert st == ttv.TTV_ERR_UNSUPPORTED
+    st, msg = ttv.kv_can_gather_raw([layer(dtype=ttv.TTV_I8, D=8, scales=True)])
+    assert st == ttv.TTV_ERR_UNSUPPORTED
+    assert ttv.kv_can_gather_raw([layer(dtype=ttv.TTV_I8, scales=True), layer(dtype=ttv.TTV_F32, D=64)])[0] == 0
+
+
+def _gather(src, dst, B=2, live=(100, 100), ws=64, sel_stride=128):
+    live = np.asarray(live, np.int32)
+    return C["kv_gather_positions"]((ttv.TtvKvLayer * len(src))(*src),
+                                    None if dst is None else (ttv.TtvKvLayer * len(dst))(*dst), len(src), B, FAKE,
+                                    sel_stride, FAKE, live.ctypes.data, FAKE, FAKE, ws, None)
+
+
+def test_gather_validation():
+    base = 1 << 30
+    mk = lambda off, cap=128: ttv.TtvKvLayer(base + off, base + off + (1 << 24), None, None, ttv.TTV_BF16, 2, 64, cap)
+    # partial aliasing: dst starts inside src's K buffer
+    assert _gather([mk(0)], [mk(4096)]) == ttv.TTV_ERR_INVALID
+    assert "overlaps" in ttv.last_error()
+    # live length beyond capacity
+    assert _gather([mk(0)], None, live=(100, 200)) == ttv.TTV_ERR_INVALID
+    # workspace too small
+    assert _gather([mk(0)], None, ws=4) == ttv.TTV_ERR_WORKSPACE
+    # shape mismatch between src and dst
+    assert _gather([mk(0)], [mk(1 << 28, cap=256)]) == ttv.TTV_ERR_INVALID
+    # int8 without sidecars: a named refusal
+    i8 = ttv.TtvKvLayer(base, base + (1 << 24), None, None, ttv.TTV_I8, 2, 64, 128)
+    assert _gather([i8], None) == ttv.TTV_ERR_UNSUPPORTED
+    assert ttv.kv_gather_positions_ws(8) == 64

@@ -1,0 +1,277 @@
+"""Python binding of libttv (token-tree verification on MI355X).
+
+Argument marshalling only: every step runs in the HIP kernels of libttv.so.
+torch tensors supply device memory and the current HIP stream; the functions
+carry the C ABI names (see include/ttv.h) and raise TTVError on a non-OK
+status. There is no CPU fallback: importing this package fails if the library
+has not been built.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libttv.so")
+
+TTV_OK, TTV_ERR_INVALID, TTV_ERR_UNSUPPORTED, TTV_ERR_WORKSPACE, TTV_ERR_HIP = range(5)
+TTV_DEV_OK, TTV_DEV_BAD_PARENT, TTV_DEV_BAD_SELECTION = 0, 1, 2
+TTV_F32, TTV_BF16, TTV_I8 = 0, 1, 2
+MAX_NODES = 64
+MAX_BATCH = 128
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libttv.so not built ({LIB_PATH}); run __graft_entry__.build() or "
+                      "python token_tree_verification_build_amd/build.py")
+_lib = ctypes.CDLL(LIB_PATH)
+
+_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_sz = ctypes.c_size_t
+
+
+class TtvBatch(ctypes.Structure):
+    _fields_ = [("B", _i32), ("node_off_h", _p), ("hist_len_h", _p), ("node_off_d", _p), ("hist_len_d", _p)]
+
+
+class TtvKvLayer(ctypes.Structure):
+    _fields_ = [("k", _p), ("v", _p), ("k_scale", _p), ("v_scale", _p), ("dtype", _i32), ("Hkv", _i32),
+                ("D", _i32), ("cap", _i32)]
+
+
+def _sig(name, res, args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = args
+    return f
+
+
+_BP = ctypes.POINTER(TtvBatch)
+_LP = ctypes.POINTER(TtvKvLayer)
+_c = {
+    "tree_build_mask": _sig("tree_build_mask", _i32, [_BP, _p, _p, _p, _p, _p]),
+    "tree_mask_expand_additive": _sig("tree_mask_expand_additive", _i32, [_BP, _i32, _p, ctypes.c_float, _p, _p]),
+    "tree_verify_attention_ws": _sig("tree_verify_attention_ws", _sz, [_BP, _i32, _LP, _i32]),
+    "tree_verify_attention": _sig("tree_verify_attention", _i32,
+                                  [_BP, _p, _i32, _i32, _LP, _p, ctypes.c_float, _p, _p, _sz, _p]),
+    "vocab_argmax_ws": _sig("vocab_argmax_ws", _sz, [_i64, _i64]),
+    "vocab_argmax": _sig("vocab_argmax", _i32, [_p, _i64, _i64, _i64, _p, _p, _sz, _p]),
+    "tree_accept_walk": _sig("tree_accept_walk", _i32, [_BP, _p, _p, _p, _p, _p, _p, _p, _i32, _p, _p, _p]),
+    "kv_gather_positions_ws": _sig("kv_gather_positions_ws", _sz, [_i32]),
+    "kv_gather_positions": _sig("kv_gather_positions", _i32,
+                                [_LP, _LP, _i32, _i32, _p, _i32, _p, _p, _p, _p, _sz, _p]),
+    "kv_can_gather": _sig("kv_can_gather", _i32, [_LP, _i32]),
+    "ttv_last_error": _sig("ttv_last_error", ctypes.c_char_p, []),
+}
+
+EXPORTED = tuple(_c)
+
+
+class TTVError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _c["ttv_last_error"]().decode()
+        super().__init__(f"{where}: status {status}: {msg}")
+
+
+def _check(status: int, where: str) -> None:
+    if status != TTV_OK:
+        raise TTVError(status, where)
+
+
+def last_error() -> str:
+    return _c["ttv_last_error"]().decode()
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _dev(t, dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+# ---------------------------------------------------------------------------
+# descriptors
+# ---------------------------------------------------------------------------
+
+class Batch:
+    """Host + device copies of node_off [B+1] and hist_len [B]."""
+
+    def __init__(self, node_off, hist_len, device="cuda"):
+        import torch
+        self.node_off_h = np.ascontiguousarray(node_off, dtype=np.int32)
+        self.hist_len_h = np.ascontiguousarray(hist_len, dtype=np.int32)
+        self.B = len(self.hist_len_h)
+        self.node_off_d = torch.from_numpy(self.node_off_h.copy()).to(device)
+        self.hist_len_d = torch.from_numpy(self.hist_len_h.copy()).to(device)
+        self.c = TtvBatch(self.B, self.node_off_h.ctypes.data, self.hist_len_h.ctypes.data,
+                          self.node_off_d.data_ptr(), self.hist_len_d.data_ptr())
+
+    @property
+    def n_nodes(self) -> int:
+        return int(self.node_off_h[-1])
+
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+_DT = {"f32": TTV_F32, "bf16": TTV_BF16, "i8": TTV_I8}
+
+
+class KVLayer:
+    """One layer's cache [B, Hkv, cap, D] (+ fp16 scales [B, Hkv, cap] for int8)."""
+
+    def __init__(self, k, v, k_scale=None, v_scale=None):
+        import torch
+        want = {torch.float32: "f32", torch.bfloat16: "bf16", torch.int8: "i8"}
+        if k.dtype not in want or v.dtype != k.dtype or k.shape != v.shape or k.dim() != 4:
+            raise ValueError("k and v must be [B, Hkv, cap, D] tensors of one of float32/bfloat16/int8")
+        _dev(k, name="k")
+        _dev(v, name="v")
+        self.dtype = want[k.dtype]
+        if self.dtype == "i8":
+            for s, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+                if s is not None:
+                    _dev(s, torch.float16, n)
+                    if tuple(s.shape) != tuple(k.shape[:3]):
+                        raise ValueError(f"{n} must be [B, Hkv, cap]")
+        self.k, self.v, self.k_scale, self.v_scale = k, v, k_scale, v_scale
+        B, Hkv, cap, D = k.shape
+        self.Hkv, self.cap, self.D = Hkv, cap, D
+        self.c = TtvKvLayer(k.data_ptr(), v.data_ptr(), _ptr(k_scale), _ptr(v_scale), _DT[self.dtype], Hkv, D, cap)
+
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def _layers_array(layers):
+    arr = (TtvKvLayer * len(layers))()
+    for i, L in enumerate(layers):
+        arr[i] = L.c
+    return arr
+
+
+# ---------------------------------------------------------------------------
+# the C ABI, one function each
+# ---------------------------------------------------------------------------
+
+def tree_build_mask(batch: Batch, parent, anc, depth, dev_status, stream=None):
+    import torch
+    _dev(parent, torch.int32, "parent")
+    _dev(anc, torch.int64, "anc")
+    _dev(depth, torch.int32, "depth")
+    _dev(dev_status, torch.int32, "dev_status")
+    _check(_c["tree_build_mask"](batch.ref(), _ptr(parent), _ptr(anc), _ptr(depth), _ptr(dev_status),
+                                 _stream(stream)), "tree_build_mask")
+
+
+def tree_mask_expand_additive(batch: Batch, b: int, anc, masked: float, out, stream=None):
+    import torch
+    _dev(anc, torch.int64, "anc")
+    _dev(out, torch.float32, "out")
+    _check(_c["tree_mask_expand_additive"](batch.ref(), b, _ptr(anc), masked, _ptr(out), _stream(stream)),
+           "tree_mask_expand_additive")
+
+
+def tree_verify_attention_ws(batch: Batch, Hq: int, layer: KVLayer, q_dtype: str) -> int:
+    return int(_c["tree_verify_attention_ws"](batch.ref(), Hq, layer.ref(), _DT[q_dtype]))
+
+
+def tree_verify_attention(batch: Batch, q, layer: KVLayer, anc, softmax_scale: float, out, ws, stream=None):
+    """q [n_nodes, Hq, D] float32 or bfloat16; out float32 like q; anc int64 or None (causal);
+    ws: zero-initialised uint8 device tensor of at least tree_verify_attention_ws bytes."""
+    import torch
+    _dev(q, name="q")
+    qd = {torch.float32: "f32", torch.bfloat16: "bf16"}[q.dtype]
+    _dev(out, torch.float32, "out")
+    _dev(anc, torch.int64, "anc")
+    _dev(ws, torch.uint8, "ws")
+    Hq = q.shape[1]
+    _check(_c["tree_verify_attention"](batch.ref(), _ptr(q), _DT[qd], Hq, layer.ref(), _ptr(anc), softmax_scale,
+                                       _ptr(out), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)),
+           "tree_verify_attention")
+
+
+def vocab_argmax_ws(n_rows: int, vocab: int) -> int:
+    return int(_c["vocab_argmax_ws"](n_rows, vocab))
+
+
+def vocab_argmax(logits, out_idx, ws=None, n_rows=None, vocab=None, row_stride=None, stream=None):
+    """logits: float32 device tensor [n_rows, >= vocab] (row stride from the tensor unless given)."""
+    import torch
+    if logits.dtype != torch.float32 or not logits.is_cuda or logits.stride(-1) != 1:
+        raise ValueError("logits must be a float32 device tensor with unit inner stride")
+    n_rows = logits.shape[0] if n_rows is None else n_rows
+    vocab = logits.shape[1] if vocab is None else vocab
+    row_stride = logits.stride(0) if row_stride is None else row_stride
+    _dev(out_idx, torch.int32, "out_idx")
+    _check(_c["vocab_argmax"](_ptr(logits), n_rows, vocab, row_stride, _ptr(out_idx), _ptr(ws),
+                              ws.numel() if ws is not None else 0, _stream(stream)), "vocab_argmax")
+
+
+def tree_accept_walk(batch: Batch, parent, token, target_argmax, path, path_len, emitted, dev_status,
+                     sel=None, sel_len_out=None, stream=None):
+    import torch
+    for t, n in ((parent, "parent"), (token, "token"), (target_argmax, "target_argmax"), (path, "path"),
+                 (path_len, "path_len"), (emitted, "emitted"), (dev_status, "dev_status"), (sel, "sel"),
+                 (sel_len_out, "sel_len_out")):
+        _dev(t, torch.int32, n)
+    stride = sel.shape[1] if sel is not None else 0
+    _check(_c["tree_accept_walk"](batch.ref(), _ptr(parent), _ptr(token), _ptr(target_argmax), _ptr(path),
+                                  _ptr(path_len), _ptr(emitted), _ptr(sel), stride, _ptr(sel_len_out),
+                                  _ptr(dev_status), _stream(stream)), "tree_accept_walk")
+
+
+def kv_gather_positions_ws(B: int) -> int:
+    return int(_c["kv_gather_positions_ws"](B))
+
+
+def kv_gather_positions(src_layers, dst_layers, sel, sel_len, live_len_h, dev_status, ws, stream=None):
+    """src_layers/dst_layers: lists of KVLayer (dst None = in place). sel int32 [B, stride]."""
+    import torch
+    _dev(sel, torch.int32, "sel")
+    _dev(sel_len, torch.int32, "sel_len")
+    _dev(dev_status, torch.int32, "dev_status")
+    _dev(ws, None, "ws")
+    live = np.ascontiguousarray(live_len_h, dtype=np.int32)
+    src = _layers_array(src_layers)
+    dst = _layers_array(dst_layers) if dst_layers is not None else None
+    B = sel.shape[0]
+    _check(_c["kv_gather_positions"](src, dst, len(src_layers), B, _ptr(sel), sel.shape[1], _ptr(sel_len),
+                                     live.ctypes.data, _ptr(dev_status), _ptr(ws), ws.numel() * ws.element_size(),
+                                     _stream(stream)), "kv_gather_positions")
+
+
+def kv_can_gather(layers) -> tuple[int, str]:
+    arr = _layers_array(layers)
+    st = _c["kv_can_gather"](arr, len(layers))
+    return st, last_error()
+
+
+def kv_can_gather_raw(layer_structs) -> tuple[int, str]:
+    """Capability query on raw TtvKvLayer structs (no tensors needed)."""
+    arr = (TtvKvLayer * len(layer_structs))(*layer_structs)
+    st = _c["kv_can_gather"](arr, len(layer_structs))
+    return st, last_error()
