@@ -412,7 +412,7 @@ def test_attention_workspace_reuse_across_shapes(ttv):
         want = O.tree_verify_attention(host["q"], {k: v for k, v in host.items() if k != "q"}, spec.node_off,
                                        spec.hist_len, spec.parents, 1 / math.sqrt(128), "bf16", spec.kv_dtype)
         assert float(np.abs(to_host(out) - want).max()) <= TOL_BF16
-    assert int(ws[:4096].view(torch.int32).abs().sum().item()) == 0
+    assert int(ws[:32].view(torch.int32).abs().sum().item()) == 0     # the 8 units' split counters
 
 
 # --------------------------------------------------------------- round ----

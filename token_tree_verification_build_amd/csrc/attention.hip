@@ -28,13 +28,18 @@
 //   S^T = K Q^T : A = K (16 keys x 32 d), B = Q^T (32 d x 16 rows). The two
 //       16-key blocks of a tile take keys 8(i/4) + 4kb + i%4, so the output
 //       lane (i, g) receives keys 8g .. 8g+7 of query row i.
-//   O^T = V^T P^T : B = P^T is exactly that lane's 8 probabilities (k-slot
-//       group g <-> keys 8g..8g+7). A = V^T with output row m of d-block db
-//       standing for d = 8m + db, so lane (i, g) needs V[8g + e][8i .. 8i+8)
-//       for e = 0..7: eight contiguous 16-byte (bf16) or 8-byte (int8) loads,
-//       regrouped in registers. No transpose through LDS is needed.
-//   int8 KV: codes (|c| <= 127) convert exactly to bf16; the per-token scales
-//       fold into the scores (s = (q . c) * k_scale) and into the
+//   O^T = V^T P^T (v_mfma_f32_16x16x32_f16): B = P^T is exactly that lane's
+//       8 probabilities (k-slot group g <-> keys 8g..8g+7), rounded to fp16.
+//       A = V^T with output row m of d-block db standing for d = 8m + db, so
+//       lane (i, g) needs V[8g + e][8i .. 8i+8) for e = 0..7: eight contiguous
+//       16-byte (bf16) or 8-byte (int8) loads, regrouped in registers. No
+//       transpose through LDS is needed.
+//   Precision: bf16 values and int8 codes convert to fp16 exactly, so the only
+//       rounding in P V is the fp16 probability (2^-12 relative); a bf16
+//       probability (2^-9) would not hold a 2e-3 bound once a short prefix
+//       makes the softmax peaked. bf16 V must therefore lie in fp16 range.
+//   int8 KV: codes (|c| <= 127) convert exactly to bf16/fp16; the per-token
+//       scales fold into the scores (s = (q . c) * k_scale) and into the
 //       probabilities (p' = p * v_scale), so the matrix cores only see codes.
 // VALU path (fp32 everything, or fewer than 16 rows): one key per lane for
 // scores, one d per lane for the output, queries and probabilities in LDS.
@@ -43,6 +48,7 @@
 namespace ttv {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -293,10 +299,11 @@ __global__ void __launch_bounds__(64) attn_mfma_kernel(const AttnParams p) {
 
     // ---- online softmax; lane holds keys 8g + e of row i ----
     // Lazy rescaling: a row's reference max m only moves when the tile max
-    // exceeds it by more than 2^8 (any lane -> the whole wave takes the
-    // rescale branch), so probabilities stay below 256 and the accumulators
-    // are rescaled a handful of times per workgroup instead of every tile.
-    bf16x8 pt[RB];
+    // exceeds it by more than 2^6 (any lane -> the whole wave takes the
+    // rescale branch), so probabilities stay below 64 (p * v_scale stays in
+    // fp16 range for any fp16 scale) and the accumulators are rescaled a
+    // handful of times per workgroup instead of every tile.
+    f16x8 pt[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       float x[8];
@@ -316,7 +323,7 @@ __global__ void __launch_bounds__(64) attn_mfma_kernel(const AttnParams p) {
       for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      if (__ballot(mx > m[rb] + 8.0f) != 0) {
+      if (__ballot(mx > m[rb] + 6.0f) != 0) {
         const float mnew = fmaxf(m[rb], mx);
         const float alpha = mnew == -INFINITY ? 1.0f : exp2f(m[rb] - mnew);
         l[rb] *= alpha;
@@ -326,13 +333,13 @@ __global__ void __launch_bounds__(64) attn_mfma_kernel(const AttnParams p) {
       }
       const float msub = m[rb] == -INFINITY ? 0.f : m[rb];
       float sum = 0.f;
-      bf16x8 pv;
+      f16x8 pv;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float pe = exp2f(x[e] - msub);
         sum += pe;
         if constexpr (I8) pe *= fv[e];
-        pv[e] = static_cast<__bf16>(pe);
+        pv[e] = static_cast<_Float16>(pe);
       }
       l[rb] += sum;
       pt[rb] = pv;
@@ -341,20 +348,20 @@ __global__ void __launch_bounds__(64) attn_mfma_kernel(const AttnParams p) {
     // ---- O^T += V^T P^T ----
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      bf16x8 vf;
-      if constexpr (I8) {
+      f16x8 vf;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          vf[e] = static_cast<__bf16>(static_cast<float>(static_cast<int8_t>(vr8[e][db >> 2] >> (8 * (db & 3)))));
-      } else {
-        const uint32_t sel = (db & 1) ? 0x07060302u : 0x05040100u;
-        u32x4 pk;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) pk[k] = __builtin_amdgcn_perm(vr[2 * k + 1][db >> 1], vr[2 * k][db >> 1], sel);
-        vf = __builtin_bit_cast(bf16x8, pk);
+      for (int e = 0; e < 8; ++e) {
+        float f;
+        if constexpr (I8) {
+          f = static_cast<float>(static_cast<int8_t>(vr8[e][db >> 2] >> (8 * (db & 3))));
+        } else {
+          const uint32_t wv = vr[e][db >> 1];
+          f = __uint_as_float((db & 1) ? (wv & 0xFFFF0000u) : (wv << 16));
+        }
+        vf[e] = static_cast<_Float16>(f);
       }
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) o[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pt[rb], o[db][rb], 0, 0, 0);
+      for (int rb = 0; rb < RB; ++rb) o[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pt[rb], o[db][rb], 0, 0, 0);
     }
   };
 
