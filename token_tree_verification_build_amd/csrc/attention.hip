@@ -45,6 +45,8 @@
 // scores, one d per lane for the output, queries and probabilities in LDS.
 #include "common.hpp"
 
+#include <type_traits>
+
 namespace ttv {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -53,7 +55,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kMfmaMaxRB = 4;   // row blocks of 16 per MFMA workgroup (64 rows)
+constexpr int kMfmaMaxRB = 5;   // row blocks of 16 per MFMA workgroup (80 rows)
 constexpr int kValuRows = 16;   // rows per VALU workgroup
 constexpr int kTargetWG = 1024;
 constexpr int kMaxSplits = 64;
@@ -70,7 +72,7 @@ struct AttnParams {
   float* part_o;
   float* part_ml;
   int32_t* counters;
-  int B, Hq, Hkv, G, D, cap, split_len, rows_chunk, nwg;
+  int B, Hq, Hkv, G, D, cap, split_len, rows_chunk, nwg, split_pad, waves;
   float scale_log2;
   int32_t node_off[TTV_MAX_BATCH + 1];
   int32_t hist_len[TTV_MAX_BATCH];
@@ -95,12 +97,13 @@ __device__ __forceinline__ void decode(const AttnParams& p, int slot, Work& w) {
   w.P = p.hist_len[lo];
   w.rows = w.T * p.G;
   w.rc_n = (w.rows + p.rows_chunk - 1) / p.rows_chunk;
-  w.nsplit = w.P > 0 ? (w.P + p.split_len - 1) / p.split_len : 1;
+  const int ns = w.P > 0 ? (w.P + p.split_len - 1) / p.split_len : 1;
+  w.nsplit = (ns + p.split_pad - 1) / p.split_pad * p.split_pad;  // trailing splits may be empty
   int rem = slot - p.wg_off[lo];
-  w.rc = rem % w.rc_n;
-  rem /= w.rc_n;
   w.split = rem % w.nsplit;
-  w.kvh = rem / w.nsplit;
+  rem /= w.nsplit;
+  w.rc = rem % w.rc_n;
+  w.kvh = rem / w.rc_n;
   w.unit = p.unit_off[lo] + w.kvh * w.rc_n + w.rc;
   w.slot = slot;
   w.row0 = w.rc * p.rows_chunk;
@@ -129,93 +132,170 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// Merge of a unit's split partials by log-sum-exp; run by the last workgroup
-// of the unit. Partials: o [slot][rows_chunk][D], (m, l) [slot][rows_chunk][2].
-__device__ void merge_unit(const AttnParams& p, const Work& w) {
-  const int lane = threadIdx.x;
-  const int slot0 = p.wg_off[w.b] + (w.kvh * w.nsplit) * w.rc_n + w.rc;
-  const int step = w.rc_n;
-  for (int r = 0; r < w.nrows; ++r) {
+// Merge of n partials of one unit by log-sum-exp, by the whole workgroup.
+// Partials: o [slot][rows_chunk][D] and (m, l) [slot][rows_chunk][2] for
+// slots slot0 .. slot0 + n - 1 (m = -inf marks an empty split). wt is LDS
+// scratch for rows_chunk * n weights: per row, w_s = 2^(m_s - M) / L with
+// M = max m_s and L = sum 2^(m_s - M) l_s; then out = sum_s w_s o_s.
+__device__ void merge_partials(const AttnParams& p, const Work& w, int slot0, int n, float* wt) {
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  for (int r = tid; r < w.nrows; r += nthr) {
     float M = -INFINITY;
-    for (int s = 0; s < w.nsplit; ++s) M = fmaxf(M, p.part_ml[((size_t)(slot0 + s * step) * p.rows_chunk + r) * 2]);
+    for (int s = 0; s < n; ++s) M = fmaxf(M, p.part_ml[((size_t)(slot0 + s) * p.rows_chunk + r) * 2]);
     float L = 0.f;
-    float acc0 = 0.f, acc1 = 0.f;
-    for (int s = 0; s < w.nsplit; ++s) {
-      const size_t pr = (size_t)(slot0 + s * step) * p.rows_chunk + r;
+    for (int s = 0; s < n; ++s) {
+      const size_t pr = (size_t)(slot0 + s) * p.rows_chunk + r;
       const float ms = p.part_ml[pr * 2];
-      const float ls = p.part_ml[pr * 2 + 1];
-      const float wt = ms == -INFINITY ? 0.f : exp2f(ms - M);
-      L += wt * ls;
-      const float* po = p.part_o + pr * p.D;
-      acc0 += wt * po[lane];
-      if (p.D == 128) acc1 += wt * po[lane + 64];
+      const float ws = ms == -INFINITY ? 0.f : exp2f(ms - M);
+      wt[r * n + s] = ws;
+      L += ws * p.part_ml[pr * 2 + 1];
     }
+    const float inv = 1.0f / L;
+    for (int s = 0; s < n; ++s) wt[r * n + s] *= inv;
+  }
+  __syncthreads();
+  const int D4 = p.D / 4;
+  for (int idx = tid; idx < w.nrows * D4; idx += nthr) {
+    const int r = idx / D4, d4 = idx - r * D4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < n; ++s)
+      acc += wt[r * n + s] *
+             reinterpret_cast<const f32x4*>(p.part_o + ((size_t)(slot0 + s) * p.rows_chunk + r) * p.D)[d4];
     const int row = w.row0 + r;
     const int node = w.o0 + row / p.G;
     const int qh = w.kvh * p.G + row % p.G;
-    float* o = p.out + ((size_t)node * p.Hq + qh) * p.D;
-    const float inv = 1.0f / L;
-    o[lane] = acc0 * inv;
-    if (p.D == 128) o[lane + 64] = acc1 * inv;
+    reinterpret_cast<f32x4*>(p.out + ((size_t)node * p.Hq + qh) * p.D)[d4] = acc;
   }
 }
 
-// After a split has written its partials: count it; the last one merges.
-__device__ __forceinline__ void finish_split(const AttnParams& p, const Work& w) {
+// After every thread of the workgroup has stored its share of one of the
+// unit's n partials: count the partial (device-scope); the workgroup that
+// completes the count merges all n and resets the counter to zero.
+__device__ void finish_partial(const AttnParams& p, const Work& w, int slot0, int n, float* wt) {
+  __shared__ int s_last;
   __threadfence();
-  int last = 0;
-  if (threadIdx.x == 0) last = atomicAdd(&p.counters[w.unit], 1) == w.nsplit - 1;
-  last = __shfl(last, 0);
-  if (!last) return;
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = atomicAdd(&p.counters[w.unit], 1) == n - 1;
+  __syncthreads();
+  if (!s_last) return;
   __threadfence();
-  merge_unit(p, w);
+  merge_partials(p, w, slot0, n, wt);
   if (threadIdx.x == 0) atomicExch(&p.counters[w.unit], 0);
 }
 
 // ------------------------------------------------------------- MFMA path ----
 
-__device__ __forceinline__ bf16x8 i8x8_to_bf16(uint32_t lo, uint32_t hi) {
-  bf16x8 r;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    r[k] = static_cast<__bf16>(static_cast<float>(static_cast<int8_t>(lo >> (8 * k))));
-    r[4 + k] = static_cast<__bf16>(static_cast<float>(static_cast<int8_t>(hi >> (8 * k))));
-  }
-  return r;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// int8 code -> fp16, exactly: with u = c ^ 0x80 = c + 128 (as an unsigned byte)
+// the fp16 bit pattern 0x64uu is 1024 + u, and 1024 + u - 1152 = c. v_perm
+// places two bytes under the 0x64 exponent bytes, one packed f16 add removes
+// the offset.
+constexpr uint32_t kExp64 = 0x64646464u;
+__device__ __forceinline__ uint32_t f16pair_from_bytes(uint32_t sel_src, uint32_t sel) {
+  const f16x2 off = {static_cast<_Float16>(-1152.0f), static_cast<_Float16>(-1152.0f)};
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(kExp64, sel_src, sel)) + off);
+}
+// 8 int8 codes (two dwords, already xor-ed with 0x80808080) -> 8 fp16
+__device__ __forceinline__ f16x8 i8x8_to_f16(uint32_t lo, uint32_t hi) {
+  u32x4 r;
+  r[0] = f16pair_from_bytes(lo, 0x04010400u);
+  r[1] = f16pair_from_bytes(lo, 0x04030402u);
+  r[2] = f16pair_from_bytes(hi, 0x04010400u);
+  r[3] = f16pair_from_bytes(hi, 0x04030402u);
+  return __builtin_bit_cast(f16x8, r);
 }
 
-template <bool I8, int RB>
-__global__ void __launch_bounds__(64) attn_mfma_kernel(const AttnParams p) {
-  const int slot = xcd_slot(blockIdx.x, p.nwg);
-  if (slot < 0) return;
-  Work w;
-  decode(p, slot, w);
-  const int lane = threadIdx.x;
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+  __asm__ volatile("" ::: "memory");
+}
+
+// LDS layout of a staged K or V tile: 32 rows of RBYTES, 16-byte chunks. The
+// logical chunk c of row r sits at physical chunk c ^ swz(r), chosen so that
+// the 16 rows one fragment read touches (rows 8a + 4kb + b) land in 16
+// different bank groups.
+template <bool I8>
+__device__ __forceinline__ int lds_swz(int r) {
+  if constexpr (I8) return ((r >> 3) & 3) | (((r >> 1) & 1) << 2);  // 8 chunks per 128-byte row
+  else return ((r >> 3) & 3) | ((r & 3) << 2);                      // 16 chunks per 256-byte row
+}
+
+// Direct global -> LDS load of 16 bytes per lane (lane i lands at lds + 16 i;
+// lds must be wave-uniform). Issued as inline asm on purpose: the compiler
+// treats its own LDS-DMA builtin as possibly aliasing every later LDS read and
+// would wait for all outstanding DMAs (vmcnt 0) before each tile, which
+// serialises the ring. Completion is tracked explicitly with wait_vmcnt; the
+// memory clobber keeps every other memory access in program order.
+__device__ __forceinline__ void dma16(const void* g, const void* lds) {
+  const uint32_t a = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(lds))));
+  __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(a) : "memory");
+}
+
+template <bool I8, int RB, int S>
+__global__ void __launch_bounds__(256) attn_mfma_kernel(const AttnParams p) {
+  constexpr int NW = 4;                       // waves = consecutive key splits of one unit
+  constexpr int D = 128;
+  constexpr int RBYTES = I8 ? D : 2 * D;      // bytes of one K (or V) row
+  constexpr int CH = RBYTES / 16;             // 16-byte chunks per row
+  constexpr int KT = 32;                      // keys per tile
+  constexpr int KBYTES = KT * RBYTES;         // one K (or V) tile
+  constexpr int NK = KBYTES / 1024;           // DMA instructions per K (or V) tile
+  constexpr int SC_OFF = 2 * KBYTES;          // int8: 32 k-scales then 32 v-scales
+  constexpr int TILE = 2 * KBYTES + (I8 ? 128 : 0);
+  constexpr int NDMA = 2 * NK + (I8 ? 1 : 0); // DMA instructions per tile, always all issued
+  typedef typename std::conditional<I8, f16x8, bf16x8>::type qk_t;  // QK operand type
+  // per wave: an S-stage ring of K/V tiles; per workgroup: the unit's Q^T
+  // fragments (one conflict-free 16-byte read per use) and ancestor bitsets
+  __shared__ __attribute__((aligned(16))) char ring_all[NW][S][TILE];
+  __shared__ __attribute__((aligned(16))) u32x4 qsh[RB * 4 * 64];
+  __shared__ uint64_t tbits_s[RB * 16];
+
+  const int wgi = xcd_slot(blockIdx.x, p.nwg / NW);
+  if (wgi < 0) return;  // whole workgroup
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   const int li = lane & 15;
   const int lg = lane >> 4;
-  constexpr int D = 128;
+  Work w;
+  decode(p, wgi * NW + wave, w);  // the waves share (b, kv head, row chunk)
+  char (*ring)[TILE] = ring_all[wave];
 
-  // Q^T fragments, staged once in LDS in lane order (one conflict-free 16-byte
-  // read per fragment per tile). k-slot mapping of the QK product (shared by K
-  // and Q): bf16 KV d = 32ks + 8g + e; int8 KV d = 32g + 8ks + e (so a lane's
-  // 32 int8 codes are contiguous).
-  __shared__ u32x4 qs[RB][4][64];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
+  // Q^T fragments into LDS. k-slot mapping of the QK product (shared by K and
+  // Q): bf16 KV d = 32ks + 8g + e (bf16 operands); int8 KV d = 32g + 8ks + e
+  // (fp16 operands, so a lane's 32 int8 codes are contiguous).
+  for (int f = wave; f < RB * 4; f += NW) {
+    const int rb = f >> 2, ks = f & 3;
     const int rloc = rb * 16 + li;
     const bool ok = rloc < w.nrows;
     const int row = w.row0 + (ok ? rloc : 0);
     const int node = w.o0 + row / p.G;
     const int qh = w.kvh * p.G + row % p.G;
     const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + ((size_t)node * p.Hq + qh) * D;
+    const int d0 = I8 ? 32 * lg + 8 * ks : 32 * ks + 8 * lg;
+    u32x4 x = *reinterpret_cast<const u32x4*>(qrow + d0);
+    if (!ok) x = u32x4{0, 0, 0, 0};
+    if constexpr (I8) {
+      f16x8 h;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int d0 = I8 ? 32 * lg + 8 * ks : 32 * ks + 8 * lg;
-      u32x4 x = *reinterpret_cast<const u32x4*>(qrow + d0);
-      if (!ok) x = u32x4{0, 0, 0, 0};
-      qs[rb][ks][lane] = x;
+      for (int e = 0; e < 8; ++e)
+        h[e] = static_cast<_Float16>(__uint_as_float((e & 1) ? (x[e >> 1] & 0xFFFF0000u) : (x[e >> 1] << 16)));
+      x = __builtin_bit_cast(u32x4, h);
     }
+    qsh[f * 64 + lane] = x;
   }
+  // ancestor bitsets of the unit's rows, needed by block tiles only
+  for (int r = threadIdx.x; r < RB * 16; r += 64 * NW)
+    tbits_s[r] = r < w.nrows ? row_bits(p, w, w.row0 + r) : 1ull;
+  // every ordinary load has landed before the DMA ring starts, so the waits in
+  // the loop count ring traffic only
+  wait_vmcnt<0>();
   __syncthreads();
 
   f32x4 o[8][RB];
@@ -229,103 +309,165 @@ __global__ void __launch_bounds__(64) attn_mfma_kernel(const AttnParams p) {
   }
 
   const size_t head = (size_t)w.b * p.Hkv + w.kvh;
-  const char* kbase = static_cast<const char*>(p.k) + head * p.cap * D * (I8 ? 1 : 2);
-  const char* vbase = static_cast<const char*>(p.v) + head * p.cap * D * (I8 ? 1 : 2);
+  const char* kbase = static_cast<const char*>(p.k) + head * p.cap * RBYTES;
+  const char* vbase = static_cast<const char*>(p.v) + head * p.cap * RBYTES;
   const uint16_t* ksb = I8 ? p.ks + head * p.cap : nullptr;
   const uint16_t* vsb = I8 ? p.vs + head * p.cap : nullptr;
-  constexpr int RBYTES = I8 ? D : 2 * D;
 
-  // mode 0: full prefix tile; 1: prefix tile ending at `limit`; 2: block tile
-  // (tbits: ancestor bitsets of the lane's rows, used in mode 2 only)
-  auto tile = [&](int t0, int mode, int limit, const uint64_t* tbits) {
-    // ---- loads (indices clamped to limit - 1 in boundary tiles) ----
-    bf16x8 kf[2][4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      int key = t0 + 8 * (li >> 2) + 4 * kb + (li & 3);
-      if (mode != 0) key = min(key, limit - 1);
-      const char* kr = kbase + (size_t)key * RBYTES;
-      if constexpr (I8) {
-        const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kr + 32 * lg));
-        const u32x4 c = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kr + 32 * lg + 16));
-        kf[kb][0] = i8x8_to_bf16(a[0], a[1]);
-        kf[kb][1] = i8x8_to_bf16(a[2], a[3]);
-        kf[kb][2] = i8x8_to_bf16(c[0], c[1]);
-        kf[kb][3] = i8x8_to_bf16(c[2], c[3]);
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          kf[kb][ks] = __builtin_bit_cast(
-              bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kr + 2 * (32 * ks + 8 * lg))));
-      }
+  // Tile list: prefix tiles over [k_lo, k_hi) (the last may be partial), then
+  // on the last split the block tiles over [P, P + T).
+  const int n_pref = w.k_hi > w.k_lo ? (w.k_hi - w.k_lo + KT - 1) / KT : 0;
+  const int ntile = n_pref + (w.last ? (w.T + KT - 1) / KT : 0);
+  auto geom = [&](int t, int& t0, int& mode, int& limit) {
+    if (t < n_pref) {
+      t0 = w.k_lo + KT * t;
+      limit = w.k_hi;
+      mode = t0 + KT <= w.k_hi ? 0 : 1;
+    } else {
+      t0 = w.P + KT * (t - n_pref);
+      limit = w.P + w.T;
+      mode = 2;
     }
-    u32x4 vr[8];
-    u32x2 vr8[8];
+  };
+
+  // DMA one tile into ring slot t % S: exactly NDMA instructions, every row
+  // index clamped into [0, limit) so boundary tiles stay in bounds.
+  auto issue = [&](int t) {
+    int t0, mode, limit;
+    geom(t, t0, mode, limit);
+    char* dst = ring[t % S];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      int key = t0 + 8 * lg + e;
-      if (mode != 0) key = min(key, limit - 1);
-      const char* vrow = vbase + (size_t)key * RBYTES;
-      if constexpr (I8)
-        vr8[e] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vrow + 8 * li));
-      else
-        vr[e] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vrow + 16 * li));
+    for (int j = 0; j < NK; ++j) {
+      const int pos = 64 * j + lane;
+      const int r = pos / CH;
+      const int c = (pos % CH) ^ lds_swz<I8>(r);
+      const int key = min(t0 + r, limit - 1);
+      dma16(kbase + (size_t)key * RBYTES + 16 * c, dst + 1024 * j);
+      dma16(vbase + (size_t)key * RBYTES + 16 * c, dst + KBYTES + 1024 * j);
     }
-    float fk[8], fv[8];
     if constexpr (I8) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        int key = t0 + 8 * lg + e;
-        if (mode != 0) key = min(key, limit - 1);
-        fk[e] = fp16_to_f32(ksb[key]) * p.scale_log2;
-        fv[e] = fp16_to_f32(vsb[key]);
+      // lanes 0-3: k-scales of keys t0 + 8 lane .. +8; lanes 4-7: v-scales. A
+      // group reaching past cap is clamped to start at cap - 8 (cap >= 32).
+      if (lane < 8) {
+        const int gs = min(t0 + 8 * (lane & 3), p.cap - 8);
+        dma16((lane < 4 ? ksb : vsb) + gs, dst + SC_OFF);
       }
     }
+  };
 
-    // ---- S^T = K Q^T ----
-    f32x4 sacc[2][RB];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < S - 1; ++t)
+    if (t < ntile) issue(t);
+
+#pragma nounroll
+  for (int t = 0; t < ntile; ++t) {
+    if (t + S - 1 < ntile) {
+      issue(t + S - 1);
+      wait_vmcnt<(S - 1) * NDMA>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    int t0, mode, limit;
+    geom(t, t0, mode, limit);
+    const char* sl = ring[t % S];
+
+    // ---- per-key scales (int8): lane holds keys 8g + e, e = 0..7, as fp16 ----
+    u32x4 ksc = {0, 0, 0, 0}, vsc = {0, 0, 0, 0};
+    if constexpr (I8) {
+      // in a tile reaching past cap the lane group's scales were staged from
+      // cap - 8 on, so key t0 + 8g + e sits delta places further on
+      const int delta = max(0, t0 + 8 * lg + 8 - p.cap);
+      if (delta == 0) {
+        ksc = *reinterpret_cast<const u32x4*>(sl + SC_OFF + 16 * lg);
+        vsc = *reinterpret_cast<const u32x4*>(sl + SC_OFF + 64 + 16 * lg);
+      } else {
+        const uint16_t* ksl = reinterpret_cast<const uint16_t*>(sl + SC_OFF + 16 * lg);
+        const uint16_t* vsl = reinterpret_cast<const uint16_t*>(sl + SC_OFF + 64 + 16 * lg);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int at = min(e + delta, 7);
+          ksc[e >> 1] |= static_cast<uint32_t>(ksl[at]) << (16 * (e & 1));
+          vsc[e >> 1] |= static_cast<uint32_t>(vsl[at]) << (16 * (e & 1));
+        }
+      }
+    }
+    const f16x8 fkh = __builtin_bit_cast(f16x8, ksc);
+    const f16x8 fvh = __builtin_bit_cast(f16x8, vsc);
+
+    // ---- S^T = K Q^T: block kb takes tile rows 8(i/4) + 4kb + i%4 ----
+    // k-step outer, so consecutive MFMAs feed independent accumulators
+    f32x4 sacc[2][RB];
+    {
+      u32x4 kraw[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int r = 8 * (li >> 2) + 4 * kb + (li & 3);
+        const char* krow = sl + r * RBYTES;
+        if constexpr (I8) {
+          const int sw = lds_swz<true>(r);
+          kraw[kb][0] = *reinterpret_cast<const u32x4*>(krow + 16 * ((2 * lg) ^ sw)) ^ 0x80808080u;
+          kraw[kb][1] = *reinterpret_cast<const u32x4*>(krow + 16 * ((2 * lg + 1) ^ sw)) ^ 0x80808080u;
+        }
+      }
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 qf = __builtin_bit_cast(bf16x8, qs[rb][ks][lane]);
-        a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][ks], qf, a0, 0, 0, 0);
-        a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][ks], qf, a1, 0, 0, 0);
+        qk_t kf[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          if constexpr (I8) {
+            const u32x4& src = kraw[kb][ks >> 1];
+            kf[kb] = i8x8_to_f16(src[2 * (ks & 1)], src[2 * (ks & 1) + 1]);
+          } else {
+            const int r = 8 * (li >> 2) + 4 * kb + (li & 3);
+            kf[kb] = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4*>(sl + r * RBYTES + 16 * ((4 * ks + lg) ^ lds_swz<false>(r))));
+          }
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const qk_t qv = __builtin_bit_cast(qk_t, qsh[(rb * 4 + ks) * 64 + lane]);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+            const f32x4 acc = ks == 0 ? zero : sacc[kb][rb];
+            if constexpr (I8)
+              sacc[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[kb], qv, acc, 0, 0, 0);
+            else
+              sacc[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb], qv, acc, 0, 0, 0);
+          }
+        }
       }
-      sacc[0][rb] = a0;
-      sacc[1][rb] = a1;
     }
 
     // ---- online softmax; lane holds keys 8g + e of row i ----
-    // Lazy rescaling: a row's reference max m only moves when the tile max
-    // exceeds it by more than 2^6 (any lane -> the whole wave takes the
-    // rescale branch), so probabilities stay below 64 (p * v_scale stays in
-    // fp16 range for any fp16 scale) and the accumulators are rescaled a
-    // handful of times per workgroup instead of every tile.
+    // Lazy rescaling: a row's reference max m only moves when some score
+    // exceeds it by more than 6 (log2 units). The common case is decided
+    // lane-locally (no cross-lane traffic, one wave-uniform branch per row
+    // block); the rare update reduces the row max across the four lane groups
+    // and rescales. Probabilities therefore stay below 64, so p * v_scale
+    // stays in fp16 range for any fp16 scale.
     f16x8 pt[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       float x[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float s = sacc[e >> 2][rb][e & 3];
-        x[e] = I8 ? s * fk[e] : s * p.scale_log2;
-        if (mode == 1) {
-          if (t0 + 8 * lg + e >= limit) x[e] = -INFINITY;
-        } else if (mode == 2) {
-          const int kt = t0 - w.P + 8 * lg + e;
-          if (t0 + 8 * lg + e >= limit || !((tbits[rb] >> kt) & 1ull)) x[e] = -INFINITY;
+      for (int e = 0; e < 8; ++e)
+        x[e] = sacc[e >> 2][rb][e & 3] * (I8 ? static_cast<float>(fkh[e]) * p.scale_log2 : p.scale_log2);
+      if (mode != 0) {  // boundary tiles only: keys past the range, non-ancestors
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int key = t0 + 8 * lg + e;
+          bool keep = key < limit;
+          if (mode == 2) keep = keep && ((tbits_s[rb * 16 + li] >> ((key - w.P) & 63)) & 1ull);
+          x[e] = keep ? x[e] : -INFINITY;
         }
       }
-      float mx = x[0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      if (__ballot(mx > m[rb] + 6.0f) != 0) {
+      const float lm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+      if (__ballot(lm > m[rb] + 6.0f) != 0) {
+        float mx = fmaxf(lm, __shfl_xor(lm, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float mnew = fmaxf(m[rb], mx);
-        const float alpha = mnew == -INFINITY ? 1.0f : exp2f(m[rb] - mnew);
+        const float alpha = mnew == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m[rb] - mnew);
         l[rb] *= alpha;
 #pragma unroll
         for (int db = 0; db < 8; ++db) o[db][rb] *= alpha;
@@ -336,87 +478,130 @@ __global__ void __launch_bounds__(64) attn_mfma_kernel(const AttnParams p) {
       f16x8 pv;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float pe = exp2f(x[e] - msub);
+        float pe = __builtin_amdgcn_exp2f(x[e] - msub);
         sum += pe;
-        if constexpr (I8) pe *= fv[e];
+        if constexpr (I8) pe *= static_cast<float>(fvh[e]);
         pv[e] = static_cast<_Float16>(pe);
       }
       l[rb] += sum;
       pt[rb] = pv;
     }
 
-    // ---- O^T += V^T P^T ----
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      f16x8 vf;
+    // ---- O^T += V^T P^T: lane (i, g) reads V rows 8g + e, d = 8i .. 8i+7 ----
+    if constexpr (I8) {
+      uint32_t a[8][2];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float f;
-        if constexpr (I8) {
-          f = static_cast<float>(static_cast<int8_t>(vr8[e][db >> 2] >> (8 * (db & 3))));
-        } else {
-          const uint32_t wv = vr[e][db >> 1];
-          f = __uint_as_float((db & 1) ? (wv & 0xFFFF0000u) : (wv << 16));
+        const int r = 8 * lg + e;
+        const u32x2 v2 = *reinterpret_cast<const u32x2*>(sl + KBYTES + r * RBYTES +
+                                                         16 * ((li >> 1) ^ lds_swz<true>(r)) + 8 * (li & 1));
+        a[e][0] = v2[0] ^ 0x80808080u;
+        a[e][1] = v2[1] ^ 0x80808080u;
+      }
+      // regroup: d-block db = 4h + j takes byte j of dword h of keys e = 0..7
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint32_t ilo[4], ihi[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          ilo[k] = __builtin_amdgcn_perm(a[2 * k + 1][h], a[2 * k][h], 0x05010400u);  // a0 b0 a1 b1
+          ihi[k] = __builtin_amdgcn_perm(a[2 * k + 1][h], a[2 * k][h], 0x07030602u);  // a2 b2 a3 b3
         }
-        vf[e] = static_cast<_Float16>(f);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          u32x4 vf;
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            vf[k] = f16pair_from_bytes(j < 2 ? ilo[k] : ihi[k], (j & 1) ? 0x04030402u : 0x04010400u);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+            o[4 * h + j][rb] =
+                __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, vf), pt[rb], o[4 * h + j][rb], 0, 0, 0);
+        }
+      }
+    } else {
+      u32x4 vr[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 8 * lg + e;
+        vr[e] = *reinterpret_cast<const u32x4*>(sl + KBYTES + r * RBYTES + 16 * (li ^ lds_swz<false>(r)));
       }
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) o[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pt[rb], o[db][rb], 0, 0, 0);
-    }
-  };
-
-  int t0 = w.k_lo;
-#pragma nounroll
-  for (; t0 + 32 <= w.k_hi; t0 += 32) tile(t0, 0, 0, nullptr);
-  if (t0 < w.k_hi) tile(t0, 1, w.k_hi, nullptr);
-  if (w.last) {
-    uint64_t bits[RB];
+      for (int db = 0; db < 8; ++db) {
+        f16x8 vf;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int rloc = rb * 16 + li;
-      bits[rb] = rloc < w.nrows ? row_bits(p, w, w.row0 + rloc) : 1ull;
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t wv = vr[e][db >> 1];
+          vf[e] = static_cast<_Float16>(__uint_as_float((db & 1) ? (wv & 0xFFFF0000u) : (wv << 16)));
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) o[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pt[rb], o[db][rb], 0, 0, 0);
+      }
     }
-#pragma nounroll
-    for (int tt = 0; tt < w.T; tt += 32) tile(w.P + tt, 2, w.P + w.T, bits);
   }
 
   // ---- epilogue ----
+  // (1) full row sums; (2) the four waves (four consecutive splits) fold their
+  // (m, l, o) into one in LDS, one wave at a time; (3) a unit covered by this
+  // workgroup alone is written out, otherwise one partial per workgroup goes
+  // to the workspace and the unit's last workgroup merges them.
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     l[rb] += __shfl_xor(l[rb], 16);
     l[rb] += __shfl_xor(l[rb], 32);
   }
-  const bool direct = w.nsplit == 1;
+  float* mo = reinterpret_cast<float*>(&ring_all[0][0][0]);  // [RB][8][4][64] lane-major o
+  float* mml = mo + RB * 32 * 64;                              // [RB * 16][2] (m, l)
+  float* wt = mml + RB * 32;                                   // merge weights
+  __syncthreads();  // every ring is drained
+  for (int step = 0; step < NW; ++step) {
+    if (wave == step) {
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int rloc = rb * 16 + li;
+      for (int rb = 0; rb < RB; ++rb) {
+        const int rloc = rb * 16 + li;
+        const float m_old = step ? mml[rloc * 2] : -INFINITY;
+        const float l_old = step ? mml[rloc * 2 + 1] : 0.f;
+        const float mn = fmaxf(m_old, m[rb]);
+        const float a_old = m_old == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_old - mn);
+        const float a_new = m[rb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[rb] - mn);
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int idx = ((rb * 8 + db) * 4 + r) * 64 + lane;
+            mo[idx] = o[db][rb][r] * a_new + (step ? mo[idx] * a_old : 0.f);
+          }
+        if (lg == 0) {
+          mml[rloc * 2] = mn;
+          mml[rloc * 2 + 1] = l[rb] * a_new + l_old * a_old;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  const int nwg_unit = w.nsplit / NW;
+  const int wslot0 = (p.wg_off[w.b] + (w.kvh * w.rc_n + w.rc) * w.nsplit) / NW;
+  for (int idx = threadIdx.x; idx < RB * 32 * 64; idx += 64 * NW) {
+    const int ln = idx & 63, r = (idx >> 6) & 3, db = (idx >> 8) & 7, rb = idx >> 11;
+    const int rloc = rb * 16 + (ln & 15);
     if (rloc >= w.nrows) continue;
-    float* dst;
-    float scl;
-    if (direct) {
+    const int d = 32 * (ln >> 4) + 8 * r + db;
+    if (nwg_unit == 1) {
       const int row = w.row0 + rloc;
       const int node = w.o0 + row / p.G;
       const int qh = w.kvh * p.G + row % p.G;
-      dst = p.out + ((size_t)node * p.Hq + qh) * D;
-      scl = 1.0f / l[rb];
+      p.out[((size_t)node * p.Hq + qh) * D + d] = mo[idx] / mml[rloc * 2 + 1];
     } else {
-      const size_t pr = (size_t)w.slot * p.rows_chunk + rloc;
-      dst = p.part_o + pr * D;
-      scl = 1.0f;
-      if (lg == 0) {
-        p.part_ml[pr * 2] = m[rb];
-        p.part_ml[pr * 2 + 1] = l[rb];
-      }
+      p.part_o[((size_t)wgi * p.rows_chunk + rloc) * D + d] = mo[idx];
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        f32x4 v = {o[4 * h][rb][r], o[4 * h + 1][rb][r], o[4 * h + 2][rb][r], o[4 * h + 3][rb][r]};
-        *reinterpret_cast<f32x4*>(dst + 32 * lg + 8 * r + 4 * h) = v * scl;
-      }
   }
-  if (!direct) finish_split(p, w);
+  if (nwg_unit > 1) {
+    for (int r = threadIdx.x; r < w.nrows; r += 64 * NW) {
+      p.part_ml[((size_t)wgi * p.rows_chunk + r) * 2] = mml[r * 2];
+      p.part_ml[((size_t)wgi * p.rows_chunk + r) * 2 + 1] = mml[r * 2 + 1];
+    }
+    finish_partial(p, w, wslot0, nwg_unit, wt);
+  }
 }
 
 // ------------------------------------------------------------- VALU path ----
@@ -581,7 +766,10 @@ __global__ void __launch_bounds__(64) attn_valu_kernel(const AttnParams p) {
 #pragma unroll
     for (int c = 0; c < C; ++c) dst[lane + 64 * c] = o[r][c] * scl;
   }
-  if (!direct) finish_split(p, w);
+  if (!direct) {
+    __shared__ float wt[kValuRows * kMaxSplits];
+    finish_partial(p, w, p.wg_off[w.b] + (w.kvh * w.rc_n + w.rc) * w.nsplit, w.nsplit, wt);
+  }
 }
 
 // ------------------------------------------------------------- planning ----
@@ -622,10 +810,11 @@ static ttv_status plan_attention(const ttv_batch* batch, int Hq, const ttv_kv_la
     max_rows = T * G > max_rows ? T * G : max_rows;
     maxP = P > maxP ? P : maxP;
   }
-  pl.mfma = bf && L->D == 128 && max_rows >= 16;
+  pl.mfma = bf && L->D == 128 && max_rows >= 16 && L->cap >= 32;
   if (pl.mfma) {
-    // balanced row chunks of at most 64 rows: e.g. 80 rows -> 2 x 48
-    const int nch = (max_rows + 16 * kMfmaMaxRB - 1) / (16 * kMfmaMaxRB);
+    // balanced row chunks of at most 80 (int8) / 64 (bf16) rows
+    const int max_rb = kMfmaMaxRB;
+    const int nch = (max_rows + 16 * max_rb - 1) / (16 * max_rb);
     const int per = (max_rows + nch - 1) / nch;
     pl.rb = (per + 15) / 16;
   } else {
@@ -653,12 +842,17 @@ static ttv_status plan_attention(const ttv_batch* batch, int Hq, const ttv_kv_la
   if (sl < 256) sl = 256;
   sl = (sl + 63) / 64 * 64;
   p.split_len = static_cast<int>(sl);
+  // MFMA workgroups are 4 waves = 4 consecutive key splits of one unit, so a
+  // unit's split count is padded to a multiple of 4 (padding splits are empty)
+  p.split_pad = pl.mfma ? 4 : 1;
+  p.waves = pl.mfma ? 4 : 1;
   int wg = 0, units = 0;
   for (int b = 0; b < B; ++b) {
     const int T = batch->node_off_h[b + 1] - batch->node_off_h[b];
     const int P = batch->hist_len_h[b];
     const int rc = (T * G + p.rows_chunk - 1) / p.rows_chunk;
-    const int ns = P > 0 ? (P + p.split_len - 1) / p.split_len : 1;
+    const int ns0 = P > 0 ? (P + p.split_len - 1) / p.split_len : 1;
+    const int ns = (ns0 + p.split_pad - 1) / p.split_pad * p.split_pad;
     p.node_off[b] = batch->node_off_h[b];
     p.hist_len[b] = P;
     p.wg_off[b] = wg;
@@ -713,15 +907,18 @@ extern "C" ttv_status tree_verify_attention(const ttv_batch* batch, const void* 
   p.part_o = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.off_o);
   p.scale_log2 = softmax_scale * kLog2e;
   const unsigned grid = static_cast<unsigned>((p.nwg + kNumXcd - 1) / kNumXcd * kNumXcd);
+  const unsigned mgrid = static_cast<unsigned>((p.nwg / 4 + kNumXcd - 1) / kNumXcd * kNumXcd);
   hipStream_t st = (hipStream_t)stream;
   const bool i8 = layer->dtype == TTV_I8;
   if (pl.mfma) {
-#define TTV_MFMA(I, R) hipLaunchKernelGGL((attn_mfma_kernel<I, R>), dim3(grid), dim3(64), 0, st, p)
+#define TTV_MFMA(I, R) hipLaunchKernelGGL((attn_mfma_kernel<I, R, (I) ? 4 : 2>), dim3(mgrid), dim3(256), 0, st, p)
     switch (pl.rb) {
       case 1: if (i8) TTV_MFMA(true, 1); else TTV_MFMA(false, 1); break;
       case 2: if (i8) TTV_MFMA(true, 2); else TTV_MFMA(false, 2); break;
       case 3: if (i8) TTV_MFMA(true, 3); else TTV_MFMA(false, 3); break;
-      default: if (i8) TTV_MFMA(true, 4); else TTV_MFMA(false, 4); break;
+      case 4: if (i8) TTV_MFMA(true, 4); else TTV_MFMA(false, 4); break;
+      default: if (i8) TTV_MFMA(true, 5); else TTV_MFMA(false, 5); break;
+
     }
 #undef TTV_MFMA
   } else {
