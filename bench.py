@@ -34,6 +34,13 @@ def parse():
     ap.add_argument("--no-take", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-heads", type=int, default=2, help="KV heads in the CPU oracle sample")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="after the timed region, run one plain device copy of this many MiB (the reference "
+                         "dispatch that scales FETCH_SIZE / WRITE_SIZE counters to bytes)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two rocprofv3 --pmc counter CSVs (FETCH_SIZE run, WRITE_SIZE run) of "
+                         "'bench.py --copy-calib-mib N' into HBM traffic per kernel, then exit")
+    ap.add_argument("--calib-mib", type=int, default=1024, help="the --copy-calib-mib of the summarised runs")
     return ap.parse_args()
 
 
@@ -139,6 +146,77 @@ def cpu_baseline(spec, caches, qs, logits, heads: int):
     }
 
 
+ATTN_SOURCE = os.path.join(ROOT, "token_tree_verification_build_amd", "csrc", "attention.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "tree_verify_attention_i8_131k_traffic.txt")
+TRAFFIC_TAG = "bench-traffic: "
+
+
+def source_digest(path: str) -> str:
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def pmc_rows(csv_path: str, counter: str) -> dict:
+    """Kernel name -> list of per-dispatch counter values (KiB) from a rocprofv3 counter CSV."""
+    import csv
+    out: dict = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def pmc_summary(fetch_csv: str, write_csv: str, calib_mib: int) -> None:
+    """HBM traffic per dispatch. FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are
+    each scaled by the bytes-per-KiB that the same counter reads for the plain
+    copy of calib_mib MiB (which reads and writes exactly that many bytes)."""
+    fetch, write = pmc_rows(fetch_csv, "FETCH_SIZE"), pmc_rows(write_csv, "WRITE_SIZE")
+    nbytes = calib_mib << 20
+
+    def copy_value(rows):
+        cands = [(k, v) for k, v in rows.items() if "copy" in k.lower()]
+        # the calibration copy is the dispatch whose counter reads closest to its size
+        k, v = min(cands, key=lambda kv: abs(max(kv[1]) * 1024 - nbytes))
+        return k, max(v)
+
+    ck, cf = copy_value(fetch)
+    _, cw = copy_value(write)
+    f_scale, w_scale = nbytes / (cf * 1024), nbytes / (cw * 1024)
+    print(f"calibration copy: {ck[:100]}")
+    print(f"  {calib_mib} MiB copied; FETCH_SIZE {cf:.0f} KiB -> {f_scale:.4f} B per counted B; "
+          f"WRITE_SIZE {cw:.0f} KiB -> {w_scale:.4f} B per counted B")
+    print(f"{'kernel':90s} {'n':>4s} {'fetch MB':>10s} {'write MB':>10s} {'scaled MB':>10s}")
+    attn = None
+    for k in sorted(set(fetch) & set(write)):
+        fv, wv = fetch[k], write[k]
+        fm, wm = sum(fv) / len(fv) * 1024, sum(wv) / len(wv) * 1024
+        tot = fm * f_scale + wm * w_scale
+        print(f"{k[:90]:90s} {len(fv):4d} {fm / 1e6:10.2f} {wm / 1e6:10.2f} {tot / 1e6:10.2f}")
+        if "attn_mfma_kernel" in k and (attn is None or tot > attn[1]):
+            attn = (k, tot, fm * f_scale, wm * w_scale)
+    if attn is not None:
+        rec = {"kernel": attn[0], "traffic_bytes": round(attn[1]), "read_bytes": round(attn[2]),
+               "write_bytes": round(attn[3]), "kernel_source_sha256": source_digest(ATTN_SOURCE)}
+        print(TRAFFIC_TAG + json.dumps(rec))
+
+
+def recorded_traffic():
+    """Scaled HBM bytes per attention launch recorded under profiles/, or None
+    when the attention source has changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if line.startswith(TRAFFIC_TAG):
+                    rec = json.loads(line[len(TRAFFIC_TAG):])
+                    if rec.get("kernel_source_sha256") == source_digest(ATTN_SOURCE):
+                        return int(rec["traffic_bytes"])
+    except OSError:
+        pass
+    return None
+
+
 def torch_int16():
     import torch
     return torch.int16
@@ -146,11 +224,14 @@ def torch_int16():
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.calib_mib)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         if int(os.environ.get("RANK", "0")) == 0:
-            print("bench.py measures one GPU: the verify path runs on a single MI355X in this build; "
-                  "--gpus must be 1 (how the path would shard is described in DESIGN.md)", file=sys.stderr)
+            print("bench.py measures one GPU: the verify path runs on a single MI355X, so --gpus must be 1",
+                  file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -262,6 +343,14 @@ def main():
         del dst_caches, dst_layers
     assert int(st.item()) == 0, "device status"
 
+    if args.copy_calib_mib > 0:
+        a = torch.ones(args.copy_calib_mib << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
     cpu = None
     if not args.no_cpu:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
@@ -286,7 +375,8 @@ def main():
                    "Hq": spec.Hq, "Hkv": spec.Hkv, "head_dim": spec.D, "vocab": spec.vocab,
                    "step": "mask + L x attention + argmax + walk + in-place rollback gather"},
         "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic() if args.config == 5 else None,
                      "kernel": "tree_verify_attention"},
         "cpu_baseline": cpu,
         "kernels": kernels,

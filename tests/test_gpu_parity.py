@@ -215,8 +215,10 @@ def test_argmax_many_rows_and_small_vocab(ttv):
 
 # -------------------------------------------------------------- gather ----
 
-def _gather_case(ttv, dtype, in_place, sels, B=3, L=2, H=2, D=64, cap=700, seed=0):
-    host = [make_kv_cache(1170 + seed, l, B, H, cap, D, dtype, unique_scales=(dtype == "i8")) for l in range(L)]
+def _gather_case(ttv, dtype, in_place, sels, B=3, L=2, H=2, D=64, cap=700, seed=0, unique=True):
+    # distinct per-token scales prove that scales move with their tokens (fp16 has ~26k of them)
+    host = [make_kv_cache(1170 + seed, l, B, H, cap, D, dtype, unique_scales=unique and dtype == "i8")
+            for l in range(L)]
     devs, layers = zip(*[layer_to_dev(ttv, h) for h in host])
     live = np.array([cap - 3 * b for b in range(B)], np.int32)
     stride = cap + 5
@@ -301,6 +303,32 @@ def test_gather_bad_selection_writes_nothing(ttv, in_place):
     for l in range(len(host)):
         for n in host[l]:
             np.testing.assert_array_equal(got[l][n], base[l][n])
+
+
+@pytest.mark.parametrize("in_place", [True, False])
+def test_gather_long_selection_many_chunks(ttv, in_place):
+    """Selections of ~140k entries: the validation runs over many workgroups per
+    sequence; a defect in a late chunk (or right at a chunk seam) still stops
+    every write."""
+    rng = rng_for(1195)
+    B, cap = 2, 140000
+    live = np.array([cap - 3 * b for b in range(B)])
+    sels = [O.rollback_selection(int(live[0]) - 16, [0, 3, 9, 14]), np.sort(rng.choice(live[1], 90001, replace=False))]
+    log(f"gather: long selections in_place={in_place}")
+    host, base, got, st, _ = _gather_case(ttv, "i8", in_place, sels, B=B, L=1, H=1, D=64, cap=cap, seed=7,
+                                             unique=False)
+    assert st == 0
+    want = O.gather_layer(dict(host[0]), sels, base=base[0])
+    for n in want:
+        np.testing.assert_array_equal(got[0][n], want[n], err_msg=n)
+    for where in (4096, 2 * 2304, 57 * 2304, len(sels[0]) - 1):   # 2304 entries per chunk at this size
+        bad = [sels[0].copy(), sels[1]]
+        bad[0][where] = bad[0][where - 1]                       # repeated entry: not increasing
+        host, base, got, st, _ = _gather_case(ttv, "i8", in_place, bad, B=B, L=1, H=1, D=64, cap=cap, seed=7,
+                                                 unique=False)
+        assert st == ttv.TTV_DEV_BAD_SELECTION, where
+        for n in host[0]:
+            np.testing.assert_array_equal(got[0][n], base[0][n], err_msg=f"{where} {n}")
 
 
 # ----------------------------------------------------------- attention ----

@@ -134,7 +134,7 @@ def test_can_gather_refusals():
     assert ttv.kv_can_gather_raw([layer(dtype=ttv.TTV_I8, scales=True), layer(dtype=ttv.TTV_F32, D=64)])[0] == 0
 
 
-def _gather(src, dst, B=2, live=(100, 100), ws=64, sel_stride=128):
+def _gather(src, dst, B=2, live=(100, 100), ws=1 << 20, sel_stride=128):
     live = np.asarray(live, np.int32)
     return C["kv_gather_positions"]((ttv.TtvKvLayer * len(src))(*src),
                                     None if dst is None else (ttv.TtvKvLayer * len(dst))(*dst), len(src), B, FAKE,
@@ -156,4 +156,5 @@ def test_gather_validation():
     # int8 without sidecars: a named refusal
     i8 = ttv.TtvKvLayer(base, base + (1 << 24), None, None, ttv.TTV_I8, 2, 64, 128)
     assert _gather([i8], None) == ttv.TTV_ERR_UNSUPPORTED
-    assert ttv.kv_gather_positions_ws(8) == 64
+    # j0 and bad per sequence, plus a partial pair per validation chunk (at most 64)
+    assert ttv.kv_gather_positions_ws(8) == 8 * (2 + 2 * 64) * 4

@@ -11,9 +11,10 @@
 // changes, so the cost follows the block rather than the context).
 //
 // Launch sequence for one call:
-//  1. validate: one workgroup per sequence checks its selection (strictly
-//     increasing, in range, not longer than the live window or the row
-//     stride) and records j0, the first j with sel[j] != j, and a bad flag.
+//  1. validate: workgroups over (chunk, sequence) check the selection
+//     (strictly increasing, in range, not longer than the live window or the
+//     row stride); a one-workgroup pass folds the chunks into j0, the first j
+//     with sel[j] != j, and a bad flag per sequence.
 //  2. copy: every workgroup first checks all sequences' bad flags (one wave
 //     load + ballot) and leaves without writing if any is set, so a malformed
 //     call writes nothing at all.
@@ -32,6 +33,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kGatherThreads = 256;
 constexpr int kLayersPerLaunch = 16;
 constexpr int kTakeRows = 256;  // rows per out-of-place workgroup
+constexpr int kMaxSelChunks = 64;     // validation workgroups per sequence, at most
+constexpr int kMinSelChunk = 2048;    // selection entries per validation workgroup, at least
 
 struct LayerPtrs {
   const char* k[kLayersPerLaunch];
@@ -48,14 +51,16 @@ struct LiveLens {
   int32_t live[TTV_MAX_BATCH];
 };
 
+// One workgroup per (chunk of the selection, sequence): partial j0 and bad flag.
 __global__ void __launch_bounds__(kGatherThreads) sel_validate_kernel(const int32_t* __restrict__ sel,
                                                                       int sel_stride,
                                                                       const int32_t* __restrict__ sel_len,
-                                                                      LiveLens lens, int32_t* __restrict__ j0_out,
-                                                                      int32_t* __restrict__ bad_out,
-                                                                      int32_t* __restrict__ status) {
+                                                                      LiveLens lens, int chunk,
+                                                                      int32_t* __restrict__ part_j0,
+                                                                      int32_t* __restrict__ part_bad) {
   __shared__ int s_j0;
-  const int b = blockIdx.x;
+  const int c = blockIdx.x;
+  const int b = blockIdx.y;
   const int n = sel_len[b];
   const int live = lens.live[b];
   if (threadIdx.x == 0) s_j0 = n;
@@ -63,8 +68,9 @@ __global__ void __launch_bounds__(kGatherThreads) sel_validate_kernel(const int3
   int bad = (n < 0 || n > live || n > sel_stride) ? 1 : 0;
   if (!bad) {
     const int32_t* row = sel + static_cast<int64_t>(b) * sel_stride;
+    const int j1 = (c + 1) * chunk < n ? (c + 1) * chunk : n;
     int j0 = n;
-    for (int j = threadIdx.x; j < n; j += kGatherThreads) {
+    for (int j = c * chunk + threadIdx.x; j < j1; j += kGatherThreads) {
       const int s = row[j];
       if (s < 0 || s >= live) bad = 1;
       if (j + 1 < n && row[j + 1] <= s) bad = 1;
@@ -74,10 +80,28 @@ __global__ void __launch_bounds__(kGatherThreads) sel_validate_kernel(const int3
   }
   bad = __syncthreads_or(bad);
   if (threadIdx.x == 0) {
-    j0_out[b] = s_j0;
-    bad_out[b] = bad;
-    if (bad) *status = TTV_DEV_BAD_SELECTION;
+    part_j0[b * kMaxSelChunks + c] = s_j0;
+    part_bad[b * kMaxSelChunks + c] = bad;
   }
+}
+
+// One thread per sequence folds the chunk partials into j0[b] and bad[b].
+__global__ void __launch_bounds__(TTV_MAX_BATCH) sel_finalize_kernel(const int32_t* __restrict__ part_j0,
+                                                                     const int32_t* __restrict__ part_bad,
+                                                                     int B, int nch, int32_t* __restrict__ j0_out,
+                                                                     int32_t* __restrict__ bad_out,
+                                                                     int32_t* __restrict__ status) {
+  const int b = threadIdx.x;
+  if (b >= B) return;
+  int j0 = 0x7FFFFFFF, bad = 0;
+  for (int c = 0; c < nch; ++c) {
+    const int v = part_j0[b * kMaxSelChunks + c];
+    j0 = v < j0 ? v : j0;
+    bad |= part_bad[b * kMaxSelChunks + c];
+  }
+  j0_out[b] = j0;
+  bad_out[b] = bad;
+  if (bad) *status = TTV_DEV_BAD_SELECTION;
 }
 
 __device__ __forceinline__ bool any_bad(const int32_t* __restrict__ bad, int B) {
@@ -212,7 +236,7 @@ using namespace ttv;
 
 extern "C" size_t kv_gather_positions_ws(int32_t B) {
   if (B <= 0) return 0;
-  return 2 * static_cast<size_t>(B) * sizeof(int32_t);
+  return (2 + 2 * static_cast<size_t>(kMaxSelChunks)) * static_cast<size_t>(B) * sizeof(int32_t);
 }
 
 extern "C" ttv_status kv_gather_positions(const ttv_kv_layer* src, const ttv_kv_layer* dst, int32_t n_layers,
@@ -277,11 +301,20 @@ extern "C" ttv_status kv_gather_positions(const ttv_kv_layer* src, const ttv_kv_
   }
   int32_t* j0s = static_cast<int32_t*>(ws);
   int32_t* bad = j0s + B;
+  int32_t* part_j0 = bad + B;
+  int32_t* part_bad = part_j0 + static_cast<size_t>(B) * kMaxSelChunks;
+  // a valid selection is no longer than the live window or the row stride
+  const int max_n = max_live < sel_stride ? max_live : sel_stride;
+  int chunk = (max_n + kMaxSelChunks - 1) / kMaxSelChunks;
+  chunk = chunk < kMinSelChunk ? kMinSelChunk : (chunk + 255) / 256 * 256;
+  const int nch = max_n == 0 ? 1 : (max_n + chunk - 1) / chunk;
   hipStream_t st = (hipStream_t)stream;
   LiveLens lens{};
   for (int b = 0; b < B; ++b) lens.live[b] = live_len_h[b];
-  hipLaunchKernelGGL(sel_validate_kernel, dim3(B), dim3(kGatherThreads), 0, st, sel, sel_stride, sel_len, lens,
-                     j0s, bad, dev_status);
+  hipLaunchKernelGGL(sel_validate_kernel, dim3(nch, B), dim3(kGatherThreads), 0, st, sel, sel_stride, sel_len,
+                     lens, chunk, part_j0, part_bad);
+  hipLaunchKernelGGL(sel_finalize_kernel, dim3(1), dim3(TTV_MAX_BATCH), 0, st, part_j0, part_bad, B, nch, j0s, bad,
+                     dev_status);
   ttv_status s = check_launch("kv_gather_positions validate");
   if (s != TTV_OK) return s;
   for (int l0 = 0; l0 < n_layers; l0 += kLayersPerLaunch) {
