@@ -226,16 +226,26 @@ __device__ __forceinline__ int lds_swz(int r) {
   else return ((r >> 3) & 3) | ((r & 3) << 2);                      // 16 chunks per 256-byte row
 }
 
-// Direct global -> LDS load of 16 bytes per lane (lane i lands at lds + 16 i;
-// lds must be wave-uniform). Issued as inline asm on purpose: the compiler
+// Direct global -> LDS loads of 16 bytes per lane; lane i lands at lds + 16 i
+// (lds must be wave-uniform). Issued as inline asm on purpose: the compiler
 // treats its own LDS-DMA builtin as possibly aliasing every later LDS read and
 // would wait for all outstanding DMAs (vmcnt 0) before each tile, which
 // serialises the ring. Completion is tracked explicitly with wait_vmcnt; the
 // memory clobber keeps every other memory access in program order.
-__device__ __forceinline__ void dma16(const void* g, const void* lds) {
-  const uint32_t a = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+__device__ __forceinline__ uint32_t lds_u32(const void* lds) {
+  return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(lds))));
-  __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(a) : "memory");
+}
+// scalar base (wave-uniform) + 32-bit per-lane byte offset
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, const void* lds) {
+  __asm__ volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+                   "s"(lds_u32(lds))
+                   : "memory");
+}
+// per-lane 64-bit address
+__device__ __forceinline__ void dma16v(const void* g, const void* lds) {
+  __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_u32(lds))
+                   : "memory");
 }
 
 template <bool I8, int RB, int S>
@@ -259,7 +269,9 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(const AttnParams p) {
 
   const int wgi = xcd_slot(blockIdx.x, p.nwg / NW);
   if (wgi < 0) return;  // whole workgroup
-  const int wave = threadIdx.x >> 6;
+  // The wave index as a uniform value: the wave's whole work item then lives in
+  // scalar registers and every branch on it is a scalar branch.
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
   const int li = lane & 15;
   const int lg = lane >> 4;
@@ -298,21 +310,36 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(const AttnParams p) {
   wait_vmcnt<0>();
   __syncthreads();
 
+  // Accumulators. o: O^T blocks (unnormalised), touched by the matrix cores
+  // only (a VALU rescale of o in the loop would make the register allocator
+  // shuttle all of it between accumulation and vector registers every tile).
+  // l: the lane's partial row sums of exactly the fp16 probabilities that
+  // enter P V. m: the row's reference max (log2 units).
   f32x4 o[8][RB];
   float m[RB], l[RB];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    m[rb] = -INFINITY;
-    l[rb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < 8; ++db) o[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int rb = 0; rb < RB; ++rb) m[rb] = -INFINITY;
 
   const size_t head = (size_t)w.b * p.Hkv + w.kvh;
   const char* kbase = static_cast<const char*>(p.k) + head * p.cap * RBYTES;
   const char* vbase = static_cast<const char*>(p.v) + head * p.cap * RBYTES;
   const uint16_t* ksb = I8 ? p.ks + head * p.cap : nullptr;
   const uint16_t* vsb = I8 ? p.vs + head * p.cap : nullptr;
+
+  // Per-lane DMA geometry: piece j of a K (or V) tile is tile row
+  // r = (64 j + lane) / CH, 16-byte chunk (64 j + lane) % CH of that row
+  // (swizzled), i.e. byte koff[j] of the tile.
+  auto piece_row = [&](int j) { return (64 * j + lane) / CH; };
+  auto piece_col = [&](int j) {
+    return 16u * static_cast<uint32_t>(((64 * j + lane) % CH) ^ lds_swz<I8>(piece_row(j)));
+  };
+  uint32_t koff[NK];
+#pragma unroll
+  for (int j = 0; j < NK; ++j) koff[j] = static_cast<uint32_t>(piece_row(j) * RBYTES) + piece_col(j);
+  // int8 scales: lanes 0-3 stage k-scales of keys t0 + 8 lane .. +8, lanes 4-7
+  // the v-scales
+  const uint16_t* sc_lane = lane < 4 ? ksb : vsb;
+  const int sc_key = 8 * (lane & 3);
 
   // Tile list: prefix tiles over [k_lo, k_hi) (the last may be partial), then
   // on the last split the block tiles over [P, P + T).
@@ -330,57 +357,65 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(const AttnParams p) {
     }
   };
 
-  // DMA one tile into ring slot t % S: exactly NDMA instructions, every row
-  // index clamped into [0, limit) so boundary tiles stay in bounds.
+  // DMA one tile into ring slot t % S: exactly NDMA instructions. Full tiles
+  // use the precomputed offsets; boundary tiles clamp every row into
+  // [t0, limit) so they stay in bounds.
   auto issue = [&](int t) {
     int t0, mode, limit;
     geom(t, t0, mode, limit);
     char* dst = ring[t % S];
+    const char* kt = kbase + (size_t)t0 * RBYTES;
+    const char* vt = vbase + (size_t)t0 * RBYTES;
+    if (mode == 0) {
 #pragma unroll
-    for (int j = 0; j < NK; ++j) {
-      const int pos = 64 * j + lane;
-      const int r = pos / CH;
-      const int c = (pos % CH) ^ lds_swz<I8>(r);
-      const int key = min(t0 + r, limit - 1);
-      dma16(kbase + (size_t)key * RBYTES + 16 * c, dst + 1024 * j);
-      dma16(vbase + (size_t)key * RBYTES + 16 * c, dst + KBYTES + 1024 * j);
+      for (int j = 0; j < NK; ++j) {
+        dma16(kt, koff[j], dst + 1024 * j);
+        dma16(vt, koff[j], dst + KBYTES + 1024 * j);
+      }
+    } else {
+      const int lim = limit - 1 - t0;
+#pragma unroll
+      for (int j = 0; j < NK; ++j) {
+        const uint32_t off = static_cast<uint32_t>(min(piece_row(j), lim) * RBYTES) + piece_col(j);
+        dma16(kt, off, dst + 1024 * j);
+        dma16(vt, off, dst + KBYTES + 1024 * j);
+      }
     }
     if constexpr (I8) {
-      // lanes 0-3: k-scales of keys t0 + 8 lane .. +8; lanes 4-7: v-scales. A
-      // group reaching past cap is clamped to start at cap - 8 (cap >= 32).
-      if (lane < 8) {
-        const int gs = min(t0 + 8 * (lane & 3), p.cap - 8);
-        dma16((lane < 4 ? ksb : vsb) + gs, dst + SC_OFF);
-      }
+      // a group reaching past cap is clamped to start at cap - 8 (cap >= 32)
+      if (lane < 8) dma16v(sc_lane + min(t0 + sc_key, p.cap - 8), dst + SC_OFF);
     }
   };
 
+  // One tile in two halves. front(t): start the DMA of tile t + S - 1, wait
+  // for tile t, form the scores and t = s * kss - m (in place of the scores)
+  // with the boundary masks, and return the lane's largest t. back(): turn t
+  // into fp16 probabilities, add their row sums and P V into the
+  // accumulators.
+  f32x4 sacc[2][RB];
+  u32x4 vsc = {0, 0, 0, 0};
+  const char* sl = nullptr;
+  float negm[RB];  // -m, or 0 while m is -inf
+  float tmax[RB];  // the lane's largest t = s * kss - m of its row so far
 #pragma unroll
-  for (int t = 0; t < S - 1; ++t)
-    if (t < ntile) issue(t);
+  for (int rb = 0; rb < RB; ++rb) negm[rb] = 0.f;
 
-#pragma nounroll
-  for (int t = 0; t < ntile; ++t) {
-    if (t + S - 1 < ntile) {
-      issue(t + S - 1);
-      wait_vmcnt<(S - 1) * NDMA>();
-    } else {
-      wait_vmcnt<0>();
-    }
+  auto scores = [&](int t) {
     int t0, mode, limit;
     geom(t, t0, mode, limit);
-    const char* sl = ring[t % S];
+    sl = ring[t % S];
 
-    // ---- per-key scales (int8): lane holds keys 8g + e, e = 0..7, as fp16 ----
-    u32x4 ksc = {0, 0, 0, 0}, vsc = {0, 0, 0, 0};
+    // per-key scales (int8): lane holds keys 8g + e, e = 0..7, as fp16
+    u32x4 ksc = {0, 0, 0, 0};
+    vsc = u32x4{0, 0, 0, 0};
     if constexpr (I8) {
-      // in a tile reaching past cap the lane group's scales were staged from
-      // cap - 8 on, so key t0 + 8g + e sits delta places further on
-      const int delta = max(0, t0 + 8 * lg + 8 - p.cap);
-      if (delta == 0) {
+      if (t0 + KT <= p.cap) {
         ksc = *reinterpret_cast<const u32x4*>(sl + SC_OFF + 16 * lg);
         vsc = *reinterpret_cast<const u32x4*>(sl + SC_OFF + 64 + 16 * lg);
       } else {
+        // the tile reaches past cap: the lane group's scales were staged from
+        // cap - 8 on, so key t0 + 8g + e sits delta places further on
+        const int delta = max(0, t0 + 8 * lg + 8 - p.cap);
         const uint16_t* ksl = reinterpret_cast<const uint16_t*>(sl + SC_OFF + 16 * lg);
         const uint16_t* vsl = reinterpret_cast<const uint16_t*>(sl + SC_OFF + 64 + 16 * lg);
 #pragma unroll
@@ -391,19 +426,20 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(const AttnParams p) {
         }
       }
     }
-    const f16x8 fkh = __builtin_bit_cast(f16x8, ksc);
-    const f16x8 fvh = __builtin_bit_cast(f16x8, vsc);
+    float kss[8];  // score scale of key 8g + e, log2 units
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      kss[e] = I8 ? static_cast<float>(__builtin_bit_cast(f16x8, ksc)[e]) * p.scale_log2 : p.scale_log2;
 
-    // ---- S^T = K Q^T: block kb takes tile rows 8(i/4) + 4kb + i%4 ----
-    // k-step outer, so consecutive MFMAs feed independent accumulators
-    f32x4 sacc[2][RB];
+    // S^T = K Q^T: block kb takes tile rows 8(i/4) + 4kb + i%4; k-step outer,
+    // so consecutive MFMAs feed independent accumulators
     {
       u32x4 kraw[2][2];
+      if constexpr (I8) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int r = 8 * (li >> 2) + 4 * kb + (li & 3);
-        const char* krow = sl + r * RBYTES;
-        if constexpr (I8) {
+        for (int kb = 0; kb < 2; ++kb) {
+          const int r = 8 * (li >> 2) + 4 * kb + (li & 3);
+          const char* krow = sl + r * RBYTES;
           const int sw = lds_swz<true>(r);
           kraw[kb][0] = *reinterpret_cast<const u32x4*>(krow + 16 * ((2 * lg) ^ sw)) ^ 0x80808080u;
           kraw[kb][1] = *reinterpret_cast<const u32x4*>(krow + 16 * ((2 * lg + 1) ^ sw)) ^ 0x80808080u;
@@ -436,58 +472,59 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(const AttnParams p) {
               sacc[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb], qv, acc, 0, 0, 0);
           }
         }
+        // keep one k-step of Q fragments in flight at a time (register budget)
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-
-    // ---- online softmax; lane holds keys 8g + e of row i ----
-    // Lazy rescaling: a row's reference max m only moves when some score
-    // exceeds it by more than 6 (log2 units). The common case is decided
-    // lane-locally (no cross-lane traffic, one wave-uniform branch per row
-    // block); the rare update reduces the row max across the four lane groups
-    // and rescales. Probabilities therefore stay below 64, so p * v_scale
-    // stays in fp16 range for any fp16 scale.
-    f16x8 pt[RB];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      float x[8];
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        x[e] = sacc[e >> 2][rb][e & 3] * (I8 ? static_cast<float>(fkh[e]) * p.scale_log2 : p.scale_log2);
-      if (mode != 0) {  // boundary tiles only: keys past the range, non-ancestors
+      for (int e = 0; e < 8; ++e) sacc[e >> 2][rb][e & 3] = fmaf(sacc[e >> 2][rb][e & 3], kss[e], negm[rb]);
+    if (mode != 0) {  // boundary tiles only: keys past the range, non-ancestors
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const uint64_t bits = mode == 2 ? tbits_s[rb * 16 + li] : ~0ull;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int key = t0 + 8 * lg + e;
-          bool keep = key < limit;
-          if (mode == 2) keep = keep && ((tbits_s[rb * 16 + li] >> ((key - w.P) & 63)) & 1ull);
-          x[e] = keep ? x[e] : -INFINITY;
+          const bool keep = key < limit && ((bits >> ((key - w.P) & 63)) & 1ull);
+          sacc[e >> 2][rb][e & 3] = keep ? sacc[e >> 2][rb][e & 3] : -INFINITY;
         }
       }
-      const float lm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-      if (__ballot(lm > m[rb] + 6.0f) != 0) {
-        float mx = fmaxf(lm, __shfl_xor(lm, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(m[rb], mx);
-        const float alpha = mnew == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m[rb] - mnew);
-        l[rb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < 8; ++db) o[db][rb] *= alpha;
-        m[rb] = mnew;
-      }
-      const float msub = m[rb] == -INFINITY ? 0.f : m[rb];
-      float sum = 0.f;
-      f16x8 pv;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float pe = __builtin_amdgcn_exp2f(x[e] - msub);
-        sum += pe;
-        if constexpr (I8) pe *= static_cast<float>(fvh[e]);
-        pv[e] = static_cast<_Float16>(pe);
-      }
-      l[rb] += sum;
-      pt[rb] = pv;
     }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        tmax[rb] = fmaxf(fmaxf(tmax[rb], sacc[kb][rb][0]), sacc[kb][rb][1]);
+        tmax[rb] = fmaxf(fmaxf(tmax[rb], sacc[kb][rb][2]), sacc[kb][rb][3]);
+      }
+  };
+  auto front = [&](int t) {
+    if (t + S - 1 < ntile) {
+      issue(t + S - 1);
+      wait_vmcnt<(S - 1) * NDMA>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    scores(t);
+  };
 
-    // ---- O^T += V^T P^T: lane (i, g) reads V rows 8g + e, d = 8i .. 8i+7 ----
+  auto back = [&]() {
+    // P^T fragments (fp16) and their row sums; int8: P' = P * v_scale feeds P V
+    f16x8 pw[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      f16x8 pr;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pr[e] = static_cast<_Float16>(__builtin_amdgcn_exp2f(sacc[e >> 2][rb][e & 3]));
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        l[rb] = __builtin_amdgcn_fdot2(f16x2{pr[2 * k], pr[2 * k + 1]}, f16x2{1, 1}, l[rb], false);
+      if constexpr (I8) pw[rb] = pr * __builtin_bit_cast(f16x8, vsc);
+      else pw[rb] = pr;
+    }
+    // O^T += V^T P^T: lane (i, g) reads V rows 8g + e, d = 8i .. 8i+7
     if constexpr (I8) {
       uint32_t a[8][2];
 #pragma unroll
@@ -516,7 +553,7 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(const AttnParams p) {
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb)
             o[4 * h + j][rb] =
-                __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, vf), pt[rb], o[4 * h + j][rb], 0, 0, 0);
+                __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, vf), pw[rb], o[4 * h + j][rb], 0, 0, 0);
         }
       }
     } else {
@@ -535,16 +572,78 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(const AttnParams p) {
           vf[e] = static_cast<_Float16>(__uint_as_float((db & 1) ? (wv & 0xFFFF0000u) : (wv << 16)));
         }
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) o[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pt[rb], o[db][rb], 0, 0, 0);
+        for (int rb = 0; rb < RB; ++rb) o[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pw[rb], o[db][rb], 0, 0, 0);
       }
     }
+  };
+
+  // References without rescaling. A row's reference m is set before the loop
+  // from the scores of the split's first tile (row max + kMargin). Inside the
+  // loop it is only tracked: probabilities stay below 2^6 while no score
+  // exceeds m + 6, so p * v_scale stays in fp16 range for any fp16 scale. If
+  // a row broke the bound, the split runs again from zero with raised
+  // references, so o is never rescaled and the loop carries no branch. Every
+  // row's first-tile max is finite: a row sees every key of a prefix tile and,
+  // in a block tile, the root.
+  constexpr float kMargin = 2.0f;
+  auto raise_refs = [&](float margin) -> bool {  // from tmax; true if any row moved
+    bool moved = false;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float mx = fmaxf(tmax[rb], __shfl_xor(tmax[rb], 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      if (__ballot(mx > 6.0f) != 0) {
+        moved = true;
+        m[rb] = (m[rb] == -INFINITY ? 0.f : m[rb]) + mx + margin;
+        negm[rb] = -m[rb];
+      }
+    }
+    return moved;
+  };
+#pragma unroll
+  for (int t = 0; t < S - 1; ++t)
+    if (t < ntile) issue(t);
+  if (ntile > 0) {
+    if (ntile > 1) wait_vmcnt<(S - 2) * NDMA>();  // tile 0 has landed (S >= 2)
+    else wait_vmcnt<0>();
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) tmax[rb] = -INFINITY;
+    scores(0);  // with m = -inf (negm = 0): t is the score itself
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float mx = fmaxf(tmax[rb], __shfl_xor(tmax[rb], 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      m[rb] = mx + kMargin;
+      negm[rb] = -m[rb];
+    }
+  }
+  float margin = 2.0f * kMargin;
+  for (;;) {  // attempts: the first, then one per raise of the references
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      l[rb] = 0.f;
+      tmax[rb] = -INFINITY;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) o[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma nounroll
+    for (int t = 0; t < ntile; ++t) {
+      front(t);
+      back();
+    }
+    if (!raise_refs(margin)) break;
+    margin += kMargin;  // a wider margin on every attempt
+#pragma unroll
+    for (int u = 0; u < S - 1; ++u)  // the ring is drained: the last tile waited for all DMAs
+      if (u < ntile) issue(u);
   }
 
   // ---- epilogue ----
-  // (1) full row sums; (2) the four waves (four consecutive splits) fold their
-  // (m, l, o) into one in LDS, one wave at a time; (3) a unit covered by this
-  // workgroup alone is written out, otherwise one partial per workgroup goes
-  // to the workspace and the unit's last workgroup merges them.
+  // (1) full row sums; (2) the
+  // four waves (four consecutive splits) fold their (m, l, o) into one in LDS,
+  // one wave at a time; (3) a unit covered by this workgroup alone is written
+  // out, otherwise one partial per workgroup goes to the workspace and the
+  // unit's last workgroup merges them.
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     l[rb] += __shfl_xor(l[rb], 16);
