@@ -55,7 +55,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kMfmaMaxRB = 5;   // row blocks of 16 per MFMA workgroup (80 rows)
+constexpr int kMfmaMaxRB = 6;   // row blocks of 16 per MFMA row chunk (96 rows, two waves)
 constexpr int kValuRows = 16;   // rows per VALU workgroup
 constexpr int kTargetWG = 1024;
 constexpr int kMaxSplits = 64;
@@ -72,7 +72,7 @@ struct AttnParams {
   float* part_o;
   float* part_ml;
   int32_t* counters;
-  int B, Hq, Hkv, G, D, cap, split_len, rows_chunk, nwg, split_pad, waves;
+  int B, Hq, Hkv, G, D, cap, split_len, rows_chunk, nwg, split_pad;
   float scale_log2;
   int32_t node_off[TTV_MAX_BATCH + 1];
   int32_t hist_len[TTV_MAX_BATCH];
@@ -216,6 +216,15 @@ __device__ __forceinline__ void wait_vmcnt() {
   __asm__ volatile("" ::: "memory");
 }
 
+// Wait until at most `ahead` tiles of ND DMAs each are outstanding (ahead <= 3).
+template <int ND>
+__device__ __forceinline__ void wait_vmcnt_tiles(int ahead) {
+  if (ahead >= 3) wait_vmcnt<3 * ND>();
+  else if (ahead == 2) wait_vmcnt<2 * ND>();
+  else if (ahead == 1) wait_vmcnt<ND>();
+  else wait_vmcnt<0>();
+}
+
 // LDS layout of a staged K or V tile: 32 rows of RBYTES, 16-byte chunks. The
 // logical chunk c of row r sits at physical chunk c ^ swz(r), chosen so that
 // the 16 rows one fragment read touches (rows 8a + 4kb + b) land in 16
@@ -248,9 +257,15 @@ __device__ __forceinline__ void dma16v(const void* g, const void* lds) {
                    : "memory");
 }
 
-template <bool I8, int RB, int S>
-__global__ void __launch_bounds__(256) attn_mfma_kernel(const AttnParams p) {
-  constexpr int NW = 4;                       // waves = consecutive key splits of one unit
+// A workgroup is NP = 4 wave pairs: the pairs take 4 consecutive key splits
+// of one unit, and the two waves of a pair split the unit's row chunk (RB0
+// row blocks of 16 rows, then RB1) and share one LDS ring, each staging half
+// of every tile. 512 threads at 2 waves per SIMD: 256 registers per wave.
+template <bool I8, int RB0, int RB1, int S>
+__global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
+  constexpr int NP = 4;                       // wave pairs = consecutive key splits of one unit
+  constexpr int NW = 2 * NP;                  // waves
+  constexpr int RBU = RB0 + RB1;              // row blocks of the unit's row chunk
   constexpr int D = 128;
   constexpr int RBYTES = I8 ? D : 2 * D;      // bytes of one K (or V) row
   constexpr int CH = RBYTES / 16;             // 16-byte chunks per row
@@ -259,30 +274,34 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(const AttnParams p) {
   constexpr int NK = KBYTES / 1024;           // DMA instructions per K (or V) tile
   constexpr int SC_OFF = 2 * KBYTES;          // int8: 32 k-scales then 32 v-scales
   constexpr int TILE = 2 * KBYTES + (I8 ? 128 : 0);
-  constexpr int NDMA = 2 * NK + (I8 ? 1 : 0); // DMA instructions per tile, always all issued
+  constexpr int NDK = NK + (I8 ? 1 : 0);      // DMA instructions per tile of the K half (h = 0)
+  constexpr int NDV = NK;                     // ... and of the V half (h = 1), always all issued
   typedef typename std::conditional<I8, f16x8, bf16x8>::type qk_t;  // QK operand type
-  // per wave: an S-stage ring of K/V tiles; per workgroup: the unit's Q^T
+  // per pair: an S-stage ring of K/V tiles; per workgroup: the unit's Q^T
   // fragments (one conflict-free 16-byte read per use) and ancestor bitsets
-  __shared__ __attribute__((aligned(16))) char ring_all[NW][S][TILE];
-  __shared__ __attribute__((aligned(16))) u32x4 qsh[RB * 4 * 64];
-  __shared__ uint64_t tbits_s[RB * 16];
+  __shared__ __attribute__((aligned(16))) char ring_all[NP][S][TILE];
+  __shared__ __attribute__((aligned(16))) u32x4 qsh[RBU * 4 * 64];
+  __shared__ uint64_t tbits_s[RBU * 16];
+  __shared__ int s_nt[NP];
 
-  const int wgi = xcd_slot(blockIdx.x, p.nwg / NW);
+  const int wgi = xcd_slot(blockIdx.x, p.nwg / NP);
   if (wgi < 0) return;  // whole workgroup
   // The wave index as a uniform value: the wave's whole work item then lives in
   // scalar registers and every branch on it is a scalar branch.
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int pair = wave & (NP - 1);  // the pair's two waves sit on one SIMD
+  const int h = wave / NP;  // 0: row blocks [0, RB0), stages K; 1: [RB0, RBU), stages V
   const int lane = threadIdx.x & 63;
   const int li = lane & 15;
   const int lg = lane >> 4;
   Work w;
-  decode(p, wgi * NW + wave, w);  // the waves share (b, kv head, row chunk)
-  char (*ring)[TILE] = ring_all[wave];
+  decode(p, wgi * NP + pair, w);  // the pairs share (b, kv head, row chunk)
+  char (*ring)[TILE] = ring_all[pair];
 
   // Q^T fragments into LDS. k-slot mapping of the QK product (shared by K and
   // Q): bf16 KV d = 32ks + 8g + e (bf16 operands); int8 KV d = 32g + 8ks + e
   // (fp16 operands, so a lane's 32 int8 codes are contiguous).
-  for (int f = wave; f < RB * 4; f += NW) {
+  for (int f = wave; f < RBU * 4; f += NW) {
     const int rb = f >> 2, ks = f & 3;
     const int rloc = rb * 16 + li;
     const bool ok = rloc < w.nrows;
@@ -294,31 +313,21 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(const AttnParams p) {
     u32x4 x = *reinterpret_cast<const u32x4*>(qrow + d0);
     if (!ok) x = u32x4{0, 0, 0, 0};
     if constexpr (I8) {
-      f16x8 h;
+      f16x8 hx;
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        h[e] = static_cast<_Float16>(__uint_as_float((e & 1) ? (x[e >> 1] & 0xFFFF0000u) : (x[e >> 1] << 16)));
-      x = __builtin_bit_cast(u32x4, h);
+        hx[e] = static_cast<_Float16>(__uint_as_float((e & 1) ? (x[e >> 1] & 0xFFFF0000u) : (x[e >> 1] << 16)));
+      x = __builtin_bit_cast(u32x4, hx);
     }
     qsh[f * 64 + lane] = x;
   }
   // ancestor bitsets of the unit's rows, needed by block tiles only
-  for (int r = threadIdx.x; r < RB * 16; r += 64 * NW)
+  for (int r = threadIdx.x; r < RBU * 16; r += 64 * NW)
     tbits_s[r] = r < w.nrows ? row_bits(p, w, w.row0 + r) : 1ull;
   // every ordinary load has landed before the DMA ring starts, so the waits in
   // the loop count ring traffic only
   wait_vmcnt<0>();
   __syncthreads();
-
-  // Accumulators. o: O^T blocks (unnormalised), touched by the matrix cores
-  // only (a VALU rescale of o in the loop would make the register allocator
-  // shuttle all of it between accumulation and vector registers every tile).
-  // l: the lane's partial row sums of exactly the fp16 probabilities that
-  // enter P V. m: the row's reference max (log2 units).
-  f32x4 o[8][RB];
-  float m[RB], l[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) m[rb] = -INFINITY;
 
   const size_t head = (size_t)w.b * p.Hkv + w.kvh;
   const char* kbase = static_cast<const char*>(p.k) + head * p.cap * RBYTES;
@@ -357,330 +366,361 @@ __global__ void __launch_bounds__(256) attn_mfma_kernel(const AttnParams p) {
     }
   };
 
-  // DMA one tile into ring slot t % S: exactly NDMA instructions. Full tiles
-  // use the precomputed offsets; boundary tiles clamp every row into
+  // DMA this wave's half of one tile into ring slot t % S: the K half (with
+  // the int8 scales) or the V half, exactly NDK or NDV instructions. Full
+  // tiles use the precomputed offsets; boundary tiles clamp every row into
   // [t0, limit) so they stay in bounds.
+  const char* hbase = h == 0 ? kbase : vbase;
   auto issue = [&](int t) {
     int t0, mode, limit;
     geom(t, t0, mode, limit);
-    char* dst = ring[t % S];
-    const char* kt = kbase + (size_t)t0 * RBYTES;
-    const char* vt = vbase + (size_t)t0 * RBYTES;
+    char* dst = ring[t % S] + (h == 0 ? 0 : KBYTES);
+    const char* src = hbase + (size_t)t0 * RBYTES;
     if (mode == 0) {
 #pragma unroll
-      for (int j = 0; j < NK; ++j) {
-        dma16(kt, koff[j], dst + 1024 * j);
-        dma16(vt, koff[j], dst + KBYTES + 1024 * j);
-      }
+      for (int j = 0; j < NK; ++j) dma16(src, koff[j], dst + 1024 * j);
     } else {
       const int lim = limit - 1 - t0;
 #pragma unroll
-      for (int j = 0; j < NK; ++j) {
-        const uint32_t off = static_cast<uint32_t>(min(piece_row(j), lim) * RBYTES) + piece_col(j);
-        dma16(kt, off, dst + 1024 * j);
-        dma16(vt, off, dst + KBYTES + 1024 * j);
-      }
+      for (int j = 0; j < NK; ++j)
+        dma16(src, static_cast<uint32_t>(min(piece_row(j), lim) * RBYTES) + piece_col(j), dst + 1024 * j);
     }
     if constexpr (I8) {
       // a group reaching past cap is clamped to start at cap - 8 (cap >= 32)
-      if (lane < 8) dma16v(sc_lane + min(t0 + sc_key, p.cap - 8), dst + SC_OFF);
+      if (h == 0 && lane < 8) dma16v(sc_lane + min(t0 + sc_key, p.cap - 8), ring[t % S] + SC_OFF);
     }
   };
-
-  // One tile in two halves. front(t): start the DMA of tile t + S - 1, wait
-  // for tile t, form the scores and t = s * kss - m (in place of the scores)
-  // with the boundary masks, and return the lane's largest t. back(): turn t
-  // into fp16 probabilities, add their row sums and P V into the
-  // accumulators.
-  f32x4 sacc[2][RB];
-  u32x4 vsc = {0, 0, 0, 0};
-  const char* sl = nullptr;
-  float negm[RB];  // -m, or 0 while m is -inf
-  float tmax[RB];  // the lane's largest t = s * kss - m of its row so far
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) negm[rb] = 0.f;
-
-  auto scores = [&](int t) {
-    int t0, mode, limit;
-    geom(t, t0, mode, limit);
-    sl = ring[t % S];
-
-    // per-key scales (int8): lane holds keys 8g + e, e = 0..7, as fp16
-    u32x4 ksc = {0, 0, 0, 0};
-    vsc = u32x4{0, 0, 0, 0};
-    if constexpr (I8) {
-      if (t0 + KT <= p.cap) {
-        ksc = *reinterpret_cast<const u32x4*>(sl + SC_OFF + 16 * lg);
-        vsc = *reinterpret_cast<const u32x4*>(sl + SC_OFF + 64 + 16 * lg);
-      } else {
-        // the tile reaches past cap: the lane group's scales were staged from
-        // cap - 8 on, so key t0 + 8g + e sits delta places further on
-        const int delta = max(0, t0 + 8 * lg + 8 - p.cap);
-        const uint16_t* ksl = reinterpret_cast<const uint16_t*>(sl + SC_OFF + 16 * lg);
-        const uint16_t* vsl = reinterpret_cast<const uint16_t*>(sl + SC_OFF + 64 + 16 * lg);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int at = min(e + delta, 7);
-          ksc[e >> 1] |= static_cast<uint32_t>(ksl[at]) << (16 * (e & 1));
-          vsc[e >> 1] |= static_cast<uint32_t>(vsl[at]) << (16 * (e & 1));
-        }
-      }
-    }
-    float kss[8];  // score scale of key 8g + e, log2 units
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      kss[e] = I8 ? static_cast<float>(__builtin_bit_cast(f16x8, ksc)[e]) * p.scale_log2 : p.scale_log2;
-
-    // S^T = K Q^T: block kb takes tile rows 8(i/4) + 4kb + i%4; k-step outer,
-    // so consecutive MFMAs feed independent accumulators
-    {
-      u32x4 kraw[2][2];
-      if constexpr (I8) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int r = 8 * (li >> 2) + 4 * kb + (li & 3);
-          const char* krow = sl + r * RBYTES;
-          const int sw = lds_swz<true>(r);
-          kraw[kb][0] = *reinterpret_cast<const u32x4*>(krow + 16 * ((2 * lg) ^ sw)) ^ 0x80808080u;
-          kraw[kb][1] = *reinterpret_cast<const u32x4*>(krow + 16 * ((2 * lg + 1) ^ sw)) ^ 0x80808080u;
-        }
-      }
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        qk_t kf[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          if constexpr (I8) {
-            const u32x4& src = kraw[kb][ks >> 1];
-            kf[kb] = i8x8_to_f16(src[2 * (ks & 1)], src[2 * (ks & 1) + 1]);
-          } else {
-            const int r = 8 * (li >> 2) + 4 * kb + (li & 3);
-            kf[kb] = __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const u32x4*>(sl + r * RBYTES + 16 * ((4 * ks + lg) ^ lds_swz<false>(r))));
-          }
-        }
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const qk_t qv = __builtin_bit_cast(qk_t, qsh[(rb * 4 + ks) * 64 + lane]);
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-            const f32x4 acc = ks == 0 ? zero : sacc[kb][rb];
-            if constexpr (I8)
-              sacc[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[kb], qv, acc, 0, 0, 0);
-            else
-              sacc[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb], qv, acc, 0, 0, 0);
-          }
-        }
-        // keep one k-step of Q fragments in flight at a time (register budget)
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sacc[e >> 2][rb][e & 3] = fmaf(sacc[e >> 2][rb][e & 3], kss[e], negm[rb]);
-    if (mode != 0) {  // boundary tiles only: keys past the range, non-ancestors
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const uint64_t bits = mode == 2 ? tbits_s[rb * 16 + li] : ~0ull;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int key = t0 + 8 * lg + e;
-          const bool keep = key < limit && ((bits >> ((key - w.P) & 63)) & 1ull);
-          sacc[e >> 2][rb][e & 3] = keep ? sacc[e >> 2][rb][e & 3] : -INFINITY;
-        }
-      }
-    }
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        tmax[rb] = fmaxf(fmaxf(tmax[rb], sacc[kb][rb][0]), sacc[kb][rb][1]);
-        tmax[rb] = fmaxf(fmaxf(tmax[rb], sacc[kb][rb][2]), sacc[kb][rb][3]);
-      }
-  };
-  auto front = [&](int t) {
-    if (t + S - 1 < ntile) {
-      issue(t + S - 1);
-      wait_vmcnt<(S - 1) * NDMA>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    scores(t);
+  // this wave's half of tile t has landed: at most its halves of the tiles
+  // issued after t are still outstanding
+  auto wait_tile = [&](int t) {
+    const int ahead = min(S - 2, ntile - 1 - t);
+    if (h == 0) wait_vmcnt_tiles<NDK>(ahead);
+    else wait_vmcnt_tiles<NDV>(ahead);
   };
 
-  auto back = [&]() {
-    // P^T fragments (fp16) and their row sums; int8: P' = P * v_scale feeds P V
-    f16x8 pw[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      f16x8 pr;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pr[e] = static_cast<_Float16>(__builtin_amdgcn_exp2f(sacc[e >> 2][rb][e & 3]));
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        l[rb] = __builtin_amdgcn_fdot2(f16x2{pr[2 * k], pr[2 * k + 1]}, f16x2{1, 1}, l[rb], false);
-      if constexpr (I8) pw[rb] = pr * __builtin_bit_cast(f16x8, vsc);
-      else pw[rb] = pr;
-    }
-    // O^T += V^T P^T: lane (i, g) reads V rows 8g + e, d = 8i .. 8i+7
-    if constexpr (I8) {
-      uint32_t a[8][2];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int r = 8 * lg + e;
-        const u32x2 v2 = *reinterpret_cast<const u32x2*>(sl + KBYTES + r * RBYTES +
-                                                         16 * ((li >> 1) ^ lds_swz<true>(r)) + 8 * (li & 1));
-        a[e][0] = v2[0] ^ 0x80808080u;
-        a[e][1] = v2[1] ^ 0x80808080u;
-      }
-      // regroup: d-block db = 4h + j takes byte j of dword h of keys e = 0..7
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        uint32_t ilo[4], ihi[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          ilo[k] = __builtin_amdgcn_perm(a[2 * k + 1][h], a[2 * k][h], 0x05010400u);  // a0 b0 a1 b1
-          ihi[k] = __builtin_amdgcn_perm(a[2 * k + 1][h], a[2 * k][h], 0x07030602u);  // a2 b2 a3 b3
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          u32x4 vf;
-#pragma unroll
-          for (int k = 0; k < 4; ++k)
-            vf[k] = f16pair_from_bytes(j < 2 ? ilo[k] : ihi[k], (j & 1) ? 0x04030402u : 0x04010400u);
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb)
-            o[4 * h + j][rb] =
-                __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, vf), pw[rb], o[4 * h + j][rb], 0, 0, 0);
-        }
-      }
-    } else {
-      u32x4 vr[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int r = 8 * lg + e;
-        vr[e] = *reinterpret_cast<const u32x4*>(sl + KBYTES + r * RBYTES + 16 * (li ^ lds_swz<false>(r)));
-      }
-#pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        f16x8 vf;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t wv = vr[e][db >> 1];
-          vf[e] = static_cast<_Float16>(__uint_as_float((db & 1) ? (wv & 0xFFFF0000u) : (wv << 16)));
-        }
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) o[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pw[rb], o[db][rb], 0, 0, 0);
-      }
-    }
-  };
-
-  // References without rescaling. A row's reference m is set before the loop
-  // from the scores of the split's first tile (row max + kMargin). Inside the
-  // loop it is only tracked: probabilities stay below 2^6 while no score
-  // exceeds m + 6, so p * v_scale stays in fp16 range for any fp16 scale. If
-  // a row broke the bound, the split runs again from zero with raised
-  // references, so o is never rescaled and the loop carries no branch. Every
-  // row's first-tile max is finite: a row sees every key of a prefix tile and,
-  // in a block tile, the root.
-  constexpr float kMargin = 2.0f;
-  auto raise_refs = [&](float margin) -> bool {  // from tmax; true if any row moved
-    bool moved = false;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      float mx = fmaxf(tmax[rb], __shfl_xor(tmax[rb], 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      if (__ballot(mx > 6.0f) != 0) {
-        moved = true;
-        m[rb] = (m[rb] == -INFINITY ? 0.f : m[rb]) + mx + margin;
-        negm[rb] = -m[rb];
-      }
-    }
-    return moved;
-  };
+  // The pair's two waves each stage half of every tile, so a tile is complete
+  // once both halves landed: one workgroup barrier per tile. It also frees the
+  // slot of the previous tile for the next DMA. All waves run the workgroup's
+  // longest tile list (the last split also takes the block tiles).
 #pragma unroll
   for (int t = 0; t < S - 1; ++t)
     if (t < ntile) issue(t);
-  if (ntile > 0) {
-    if (ntile > 1) wait_vmcnt<(S - 2) * NDMA>();  // tile 0 has landed (S >= 2)
-    else wait_vmcnt<0>();
+  if (lane == 0 && h == 0) s_nt[pair] = ntile;
+  if (ntile > 0) wait_tile(0);
+  __syncthreads();
+  int nt_wg = 0;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) tmax[rb] = -INFINITY;
-    scores(0);  // with m = -inf (negm = 0): t is the score itself
+  for (int q = 0; q < NP; ++q) nt_wg = max(nt_wg, s_nt[q]);
+  float* mo = reinterpret_cast<float*>(&ring_all[0][0][0]);  // [RBU][8][4][64] lane-major o
+  float* mml = mo + RBU * 32 * 64;                             // [RBU * 16][2] (m, l)
+  float* wt = mml + RBU * 32;                                  // merge weights
+  // Everything that depends on the wave's row blocks: RB of them from rb0 on.
+  // Both halves run the same sequence of workgroup barriers.
+  auto per_wave = [&](auto rb_count, const int rb0) {
+    constexpr int RB = decltype(rb_count)::value;
+    // Accumulators. o: O^T blocks (unnormalised), touched by the matrix cores
+    // only (a VALU rescale of o in the loop would make the register allocator
+    // shuttle all of it between accumulation and vector registers every tile).
+    // l: the lane's partial row sums of exactly the fp16 probabilities that
+    // enter P V. m: the row's reference max (log2 units).
+    f32x4 o[8][RB];
+    float m[RB], l[RB];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      float mx = fmaxf(tmax[rb], __shfl_xor(tmax[rb], 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      m[rb] = mx + kMargin;
-      negm[rb] = -m[rb];
-    }
-  }
-  float margin = 2.0f * kMargin;
-  for (;;) {  // attempts: the first, then one per raise of the references
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      l[rb] = 0.f;
-      tmax[rb] = -INFINITY;
-#pragma unroll
-      for (int db = 0; db < 8; ++db) o[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma nounroll
-    for (int t = 0; t < ntile; ++t) {
-      front(t);
-      back();
-    }
-    if (!raise_refs(margin)) break;
-    margin += kMargin;  // a wider margin on every attempt
-#pragma unroll
-    for (int u = 0; u < S - 1; ++u)  // the ring is drained: the last tile waited for all DMAs
-      if (u < ntile) issue(u);
-  }
+    for (int rb = 0; rb < RB; ++rb) m[rb] = -INFINITY;
 
-  // ---- epilogue ----
-  // (1) full row sums; (2) the
-  // four waves (four consecutive splits) fold their (m, l, o) into one in LDS,
-  // one wave at a time; (3) a unit covered by this workgroup alone is written
-  // out, otherwise one partial per workgroup goes to the workspace and the
-  // unit's last workgroup merges them.
+    // One tile of this wave's rows in two halves. scores(t): the scores and
+    // t = s * kss - m (in place of the scores) with the boundary masks, and the
+    // running per-row max of t. back(): turn t into fp16 probabilities, add
+    // their row sums and P V into the accumulators.
+    f32x4 sacc[2][RB];
+    u32x4 vsc = {0, 0, 0, 0};
+    const char* sl = nullptr;
+    float negm[RB];  // -m, or 0 while m is -inf
+    float tmax[RB];  // the lane's largest t = s * kss - m of its row so far
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    l[rb] += __shfl_xor(l[rb], 16);
-    l[rb] += __shfl_xor(l[rb], 32);
-  }
-  float* mo = reinterpret_cast<float*>(&ring_all[0][0][0]);  // [RB][8][4][64] lane-major o
-  float* mml = mo + RB * 32 * 64;                              // [RB * 16][2] (m, l)
-  float* wt = mml + RB * 32;                                   // merge weights
-  __syncthreads();  // every ring is drained
-  for (int step = 0; step < NW; ++step) {
-    if (wave == step) {
+    for (int rb = 0; rb < RB; ++rb) negm[rb] = 0.f;
+
+    auto scores = [&](int t) {
+      int t0, mode, limit;
+      geom(t, t0, mode, limit);
+      sl = ring[t % S];
+
+      // per-key scales (int8): lane holds keys 8g + e, e = 0..7, as fp16
+      u32x4 ksc = {0, 0, 0, 0};
+      vsc = u32x4{0, 0, 0, 0};
+      if constexpr (I8) {
+        if (t0 + KT <= p.cap) {
+          ksc = *reinterpret_cast<const u32x4*>(sl + SC_OFF + 16 * lg);
+          vsc = *reinterpret_cast<const u32x4*>(sl + SC_OFF + 64 + 16 * lg);
+        } else {
+          // the tile reaches past cap: the lane group's scales were staged from
+          // cap - 8 on, so key t0 + 8g + e sits delta places further on
+          const int delta = max(0, t0 + 8 * lg + 8 - p.cap);
+          const uint16_t* ksl = reinterpret_cast<const uint16_t*>(sl + SC_OFF + 16 * lg);
+          const uint16_t* vsl = reinterpret_cast<const uint16_t*>(sl + SC_OFF + 64 + 16 * lg);
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const int rloc = rb * 16 + li;
-        const float m_old = step ? mml[rloc * 2] : -INFINITY;
-        const float l_old = step ? mml[rloc * 2 + 1] : 0.f;
-        const float mn = fmaxf(m_old, m[rb]);
-        const float a_old = m_old == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_old - mn);
-        const float a_new = m[rb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[rb] - mn);
-#pragma unroll
-        for (int db = 0; db < 8; ++db)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int idx = ((rb * 8 + db) * 4 + r) * 64 + lane;
-            mo[idx] = o[db][rb][r] * a_new + (step ? mo[idx] * a_old : 0.f);
+          for (int e = 0; e < 8; ++e) {
+            const int at = min(e + delta, 7);
+            ksc[e >> 1] |= static_cast<uint32_t>(ksl[at]) << (16 * (e & 1));
+            vsc[e >> 1] |= static_cast<uint32_t>(vsl[at]) << (16 * (e & 1));
           }
-        if (lg == 0) {
-          mml[rloc * 2] = mn;
-          mml[rloc * 2 + 1] = l[rb] * a_new + l_old * a_old;
         }
       }
+      float kss[8];  // score scale of key 8g + e, log2 units
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        kss[e] = I8 ? static_cast<float>(__builtin_bit_cast(f16x8, ksc)[e]) * p.scale_log2 : p.scale_log2;
+
+      // S^T = K Q^T: block kb takes tile rows 8(i/4) + 4kb + i%4; k-step outer,
+      // so consecutive MFMAs feed independent accumulators
+      {
+        u32x4 kraw[2][2];
+        if constexpr (I8) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            const int r = 8 * (li >> 2) + 4 * kb + (li & 3);
+            const char* krow = sl + r * RBYTES;
+            const int sw = lds_swz<true>(r);
+            kraw[kb][0] = *reinterpret_cast<const u32x4*>(krow + 16 * ((2 * lg) ^ sw)) ^ 0x80808080u;
+            kraw[kb][1] = *reinterpret_cast<const u32x4*>(krow + 16 * ((2 * lg + 1) ^ sw)) ^ 0x80808080u;
+          }
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          qk_t kf[2];
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            if constexpr (I8) {
+              const u32x4& src = kraw[kb][ks >> 1];
+              kf[kb] = i8x8_to_f16(src[2 * (ks & 1)], src[2 * (ks & 1) + 1]);
+            } else {
+              const int r = 8 * (li >> 2) + 4 * kb + (li & 3);
+              kf[kb] = __builtin_bit_cast(
+                  bf16x8, *reinterpret_cast<const u32x4*>(sl + r * RBYTES + 16 * ((4 * ks + lg) ^ lds_swz<false>(r))));
+            }
+          }
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            const qk_t qv = __builtin_bit_cast(qk_t, qsh[((rb0 + rb) * 4 + ks) * 64 + lane]);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+              const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+              const f32x4 acc = ks == 0 ? zero : sacc[kb][rb];
+              if constexpr (I8)
+                sacc[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[kb], qv, acc, 0, 0, 0);
+              else
+                sacc[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb], qv, acc, 0, 0, 0);
+            }
+          }
+          // keep one k-step of Q fragments in flight at a time (register budget)
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sacc[e >> 2][rb][e & 3] = fmaf(sacc[e >> 2][rb][e & 3], kss[e], negm[rb]);
+      }
+      if (mode != 0) {  // boundary tiles only: keys past the range, non-ancestors
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const uint64_t bits = mode == 2 ? tbits_s[(rb0 + rb) * 16 + li] : ~0ull;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int key = t0 + 8 * lg + e;
+            const bool keep = key < limit && ((bits >> ((key - w.P) & 63)) & 1ull);
+            sacc[e >> 2][rb][e & 3] = keep ? sacc[e >> 2][rb][e & 3] : -INFINITY;
+          }
+        }
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          tmax[rb] = fmaxf(fmaxf(tmax[rb], sacc[kb][rb][0]), sacc[kb][rb][1]);
+          tmax[rb] = fmaxf(fmaxf(tmax[rb], sacc[kb][rb][2]), sacc[kb][rb][3]);
+        }
+      }
+    };
+
+    auto back = [&]() {
+      // P^T fragments (fp16) and their row sums; int8: P' = P * v_scale feeds P V
+      f16x8 pw[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        f16x8 pr;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pr[e] = static_cast<_Float16>(__builtin_amdgcn_exp2f(sacc[e >> 2][rb][e & 3]));
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          l[rb] = __builtin_amdgcn_fdot2(f16x2{pr[2 * k], pr[2 * k + 1]}, f16x2{1, 1}, l[rb], false);
+        if constexpr (I8) pw[rb] = pr * __builtin_bit_cast(f16x8, vsc);
+        else pw[rb] = pr;
+      }
+      // O^T += V^T P^T: lane (i, g) reads V rows 8g + e, d = 8i .. 8i+7
+      if constexpr (I8) {
+        uint32_t a[8][2];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * lg + e;
+          const u32x2 v2 = *reinterpret_cast<const u32x2*>(sl + KBYTES + r * RBYTES +
+                                                           16 * ((li >> 1) ^ lds_swz<true>(r)) + 8 * (li & 1));
+          a[e][0] = v2[0] ^ 0x80808080u;
+          a[e][1] = v2[1] ^ 0x80808080u;
+        }
+        // regroup: d-block db = 4hh + j takes byte j of dword hh of keys e = 0..7
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          uint32_t ilo[4], ihi[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            ilo[k] = __builtin_amdgcn_perm(a[2 * k + 1][hh], a[2 * k][hh], 0x05010400u);  // a0 b0 a1 b1
+            ihi[k] = __builtin_amdgcn_perm(a[2 * k + 1][hh], a[2 * k][hh], 0x07030602u);  // a2 b2 a3 b3
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            u32x4 vf;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              vf[k] = f16pair_from_bytes(j < 2 ? ilo[k] : ihi[k], (j & 1) ? 0x04030402u : 0x04010400u);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                o[4 * hh + j][rb] =
+                  __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, vf), pw[rb], o[4 * hh + j][rb], 0, 0, 0);
+            }
+          }
+        }
+      } else {
+        u32x4 vr[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * lg + e;
+          vr[e] = *reinterpret_cast<const u32x4*>(sl + KBYTES + r * RBYTES + 16 * (li ^ lds_swz<false>(r)));
+        }
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          f16x8 vf;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t wv = vr[e][db >> 1];
+            vf[e] = static_cast<_Float16>(__uint_as_float((db & 1) ? (wv & 0xFFFF0000u) : (wv << 16)));
+          }
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            o[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pw[rb], o[db][rb], 0, 0, 0);
+          }
+        }
+      }
+    };
+
+    // References without rescaling. A row's reference m is set before the loop
+    // from the scores of the split's first tile (row max + kMargin). Inside the
+    // loop it is only tracked: probabilities stay below 2^6 while no score
+    // exceeds m + 6, so p * v_scale stays in fp16 range for any fp16 scale. If
+    // a row broke the bound, the split runs again from zero with raised
+    // references, so o is never rescaled and the loop carries no branch. Every
+    // row's first-tile max is finite: a row sees every key of a prefix tile and,
+    // in a block tile, the root.
+    constexpr float kMargin = 2.0f;
+    auto raise_refs = [&](float margin) -> bool {  // from tmax; true if any row moved
+      bool moved = false;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        float mx = fmaxf(tmax[rb], __shfl_xor(tmax[rb], 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        if (__ballot(mx > 6.0f) != 0) {
+          moved = true;
+          m[rb] = (m[rb] == -INFINITY ? 0.f : m[rb]) + mx + margin;
+          negm[rb] = -m[rb];
+        }
+      }
+      return moved;
+    };
+    if (ntile > 0) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) tmax[rb] = -INFINITY;
+      scores(0);  // with m = -inf (negm = 0): t is the score itself
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        float mx = fmaxf(tmax[rb], __shfl_xor(tmax[rb], 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        m[rb] = mx + kMargin;
+        negm[rb] = -m[rb];
+      }
     }
-    __syncthreads();
-  }
-  const int nwg_unit = w.nsplit / NW;
-  const int wslot0 = (p.wg_off[w.b] + (w.kvh * w.rc_n + w.rc) * w.nsplit) / NW;
-  for (int idx = threadIdx.x; idx < RB * 32 * 64; idx += 64 * NW) {
+    float margin = 2.0f * kMargin;
+    for (;;) {  // attempts: the first, then one per raise of the references
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        l[rb] = 0.f;
+        tmax[rb] = -INFINITY;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) o[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma nounroll
+      for (int t = 0; t < nt_wg; ++t) {
+        if (t < ntile) wait_tile(t);
+        __syncthreads();  // tile t is complete in every pair; slot (t - 1) % S is free
+        if (t + S - 1 < ntile) issue(t + S - 1);
+        if (t < ntile) {
+          scores(t);
+          back();
+        }
+      }
+      // every wave has left the loop (its last wait drained its DMAs) before any
+      // ring slot is staged again
+      const bool mine = RB > 0 && raise_refs(margin);
+      if (!__syncthreads_or(mine)) break;
+      margin += kMargin;  // a wider margin on every attempt
+#pragma unroll
+      for (int u = 0; u < S - 1; ++u)
+        if (u < ntile) issue(u);
+    }
+
+    // ---- epilogue ----
+    // (1) full row sums; (2) the four pairs (four consecutive splits) fold
+    // their (m, l, o) into one in LDS, one pair at a time, the two waves of a
+    // pair on disjoint rows; (3) a unit covered by this workgroup alone is written
+    // out, otherwise one partial per workgroup goes to the workspace and the
+    // unit's last workgroup merges them.
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      l[rb] += __shfl_xor(l[rb], 16);
+      l[rb] += __shfl_xor(l[rb], 32);
+    }
+    __syncthreads();  // every ring is drained
+    for (int step = 0; step < NP; ++step) {
+      if (pair == step) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const int rloc = (rb0 + rb) * 16 + li;
+          const float m_old = step ? mml[rloc * 2] : -INFINITY;
+          const float l_old = step ? mml[rloc * 2 + 1] : 0.f;
+          const float mn = fmaxf(m_old, m[rb]);
+          const float a_old = m_old == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_old - mn);
+          const float a_new = m[rb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[rb] - mn);
+#pragma unroll
+          for (int db = 0; db < 8; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int idx = (((rb0 + rb) * 8 + db) * 4 + r) * 64 + lane;
+              mo[idx] = o[db][rb][r] * a_new + (step ? mo[idx] * a_old : 0.f);
+            }
+          if (lg == 0) {
+            mml[rloc * 2] = mn;
+            mml[rloc * 2 + 1] = l[rb] * a_new + l_old * a_old;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  };
+  if (h == 0) per_wave(std::integral_constant<int, RB0>{}, 0);
+  else per_wave(std::integral_constant<int, RB1>{}, RB0);
+
+  const int nwg_unit = w.nsplit / NP;
+  const int wslot0 = (p.wg_off[w.b] + (w.kvh * w.rc_n + w.rc) * w.nsplit) / NP;
+  for (int idx = threadIdx.x; idx < RBU * 32 * 64; idx += 64 * NW) {
     const int ln = idx & 63, r = (idx >> 6) & 3, db = (idx >> 8) & 7, rb = idx >> 11;
     const int rloc = rb * 16 + (ln & 15);
     if (rloc >= w.nrows) continue;
@@ -911,11 +951,13 @@ static ttv_status plan_attention(const ttv_batch* batch, int Hq, const ttv_kv_la
   }
   pl.mfma = bf && L->D == 128 && max_rows >= 16 && L->cap >= 32;
   if (pl.mfma) {
-    // balanced row chunks of at most 80 (int8) / 64 (bf16) rows
-    const int max_rb = kMfmaMaxRB;
-    const int nch = (max_rows + 16 * max_rb - 1) / (16 * max_rb);
+    // balanced row chunks of at most 96 rows: pl.rb row blocks, split
+    // between the two waves of a pair
+    const int max_rows_chunk = 16 * kMfmaMaxRB;
+    const int nch = (max_rows + max_rows_chunk - 1) / max_rows_chunk;
     const int per = (max_rows + nch - 1) / nch;
     pl.rb = (per + 15) / 16;
+    if (pl.rb < 2) pl.rb = 2;  // one block per wave at least
   } else {
     pl.rb = 0;
   }
@@ -941,10 +983,10 @@ static ttv_status plan_attention(const ttv_batch* batch, int Hq, const ttv_kv_la
   if (sl < 256) sl = 256;
   sl = (sl + 63) / 64 * 64;
   p.split_len = static_cast<int>(sl);
-  // MFMA workgroups are 4 waves = 4 consecutive key splits of one unit, so a
-  // unit's split count is padded to a multiple of 4 (padding splits are empty)
+  // MFMA workgroups are 4 wave pairs = 4 consecutive key splits of one unit,
+  // so a unit's split count is padded to a multiple of 4 (padding splits are
+  // empty)
   p.split_pad = pl.mfma ? 4 : 1;
-  p.waves = pl.mfma ? 4 : 1;
   int wg = 0, units = 0;
   for (int b = 0; b < B; ++b) {
     const int T = batch->node_off_h[b + 1] - batch->node_off_h[b];
@@ -1010,15 +1052,18 @@ extern "C" ttv_status tree_verify_attention(const ttv_batch* batch, const void* 
   hipStream_t st = (hipStream_t)stream;
   const bool i8 = layer->dtype == TTV_I8;
   if (pl.mfma) {
-#define TTV_MFMA(I, R) hipLaunchKernelGGL((attn_mfma_kernel<I, R, (I) ? 4 : 2>), dim3(mgrid), dim3(256), 0, st, p)
-    switch (pl.rb) {
-      case 1: if (i8) TTV_MFMA(true, 1); else TTV_MFMA(false, 1); break;
-      case 2: if (i8) TTV_MFMA(true, 2); else TTV_MFMA(false, 2); break;
-      case 3: if (i8) TTV_MFMA(true, 3); else TTV_MFMA(false, 3); break;
-      case 4: if (i8) TTV_MFMA(true, 4); else TTV_MFMA(false, 4); break;
-      default: if (i8) TTV_MFMA(true, 5); else TTV_MFMA(false, 5); break;
-
+#define TTV_MFMA(I, R0, R1) \
+  hipLaunchKernelGGL((attn_mfma_kernel<I, R0, R1, (I) ? 4 : 2>), dim3(mgrid), dim3(512), 0, st, p)
+#define TTV_MFMA_RB(R0, R1) \
+  if (i8) TTV_MFMA(true, R0, R1); else TTV_MFMA(false, R0, R1)
+    switch (pl.rb) {  // row blocks of a chunk, split between the two waves of a pair
+      case 1: case 2: TTV_MFMA_RB(1, 1); break;
+      case 3: TTV_MFMA_RB(2, 1); break;
+      case 4: TTV_MFMA_RB(2, 2); break;
+      case 5: TTV_MFMA_RB(3, 2); break;
+      default: TTV_MFMA_RB(3, 3); break;
     }
+#undef TTV_MFMA_RB
 #undef TTV_MFMA
   } else {
 #define TTV_VALU(Q, K, DD) hipLaunchKernelGGL((attn_valu_kernel<Q, K, DD>), dim3(grid), dim3(64), 0, st, p)
