@@ -137,9 +137,10 @@ ttv_status tree_mask_expand_additive(const ttv_batch* batch, int32_t b, const ui
  *                    causal (linear) block mask: node i sees block rows 0..i.
  *                    A linear tree's anc gives bit-identical output to NULL.
  *   out     (device) float32 [sum T_b][Hq][D]
- *   ws      (device) >= tree_verify_attention_ws(...) bytes. Its first bytes
- *                    are split counters that must be zero before the first
- *                    use; every completed call leaves them zero again.
+ *   ws      (device) >= tree_verify_attention_ws(...) bytes: the (m, l, o)
+ *                    partials of units whose keys are split across
+ *                    workgroups, merged by a second kernel the call enqueues.
+ *                    Any contents on entry (every byte read is written first).
  * Supported: D in {64, 128}; F32 q requires F32 KV and vice versa (fp32 VALU
  * path); BF16 q with BF16 or I8 KV (MFMA path when D == 128 and
  * T_b * Hq/Hkv >= 16, otherwise VALU). The MFMA path forms P.V in fp16, so

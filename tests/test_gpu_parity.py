@@ -424,12 +424,13 @@ def test_attention_ragged_batch(ttv):
 
 
 def test_attention_workspace_reuse_across_shapes(ttv):
-    """Split counters return to zero after every call, so one workspace serves
-    calls of different shapes back to back."""
+    """One workspace, poisoned first, serves calls of different shapes back to
+    back: nothing in it is read before the call writes it."""
     big = config3_round(P=6000, L=1)
     small = config2_round(8, 2)
     tb, ts = host_tensors(big), host_tensors(small)
     ws = zeros_ws(64 << 20)
+    ws.fill_(0xA5)
     for spec, tens in ((big, tb), (small, ts), (big, tb)):
         batch = spec_batch(ttv, spec)
         anc, _, _ = run_mask(ttv, batch, to_dev(spec.flat("parents")))
@@ -440,7 +441,6 @@ def test_attention_workspace_reuse_across_shapes(ttv):
         want = O.tree_verify_attention(host["q"], {k: v for k, v in host.items() if k != "q"}, spec.node_off,
                                        spec.hist_len, spec.parents, 1 / math.sqrt(128), "bf16", spec.kv_dtype)
         assert float(np.abs(to_host(out) - want).max()) <= TOL_BF16
-    assert int(ws[:32].view(torch.int32).abs().sum().item()) == 0     # the 8 units' split counters
 
 
 # --------------------------------------------------------------- round ----

@@ -9,22 +9,24 @@
 // must reproduce the linear path bit for bit -- here the causal case (anc ==
 // NULL) is literally the linear tree's bitset, so both run the same code.
 //
-// Work decomposition (one wavefront per workgroup):
+// Work decomposition:
 //   unit  = (sequence b, KV head g, row chunk rc). The rows of a unit are the
 //           (node, query head) pairs of the G query heads sharing KV head g:
 //           row r = node * G + head-in-group. Every K/V byte of the unit is
 //           read once for all of its rows (GQA sharing).
 //   split = a range of split_len prefix keys; the last split of a unit also
 //           takes the block keys [P, P + T) under the ancestor bitsets.
-//   Each workgroup keeps an online softmax (running max m, sum l, unnormalised
-//   output) over its keys. With one split it writes the output directly;
-//   otherwise it stores (m, l, o) partials and the last workgroup of the unit
-//   to finish (device-scope counter) merges them by log-sum-exp. Workgroups
-//   are laid out XCD-contiguously so a unit's splits share one L2.
+//   Each split keeps an online softmax (reference max m, sum l, unnormalised
+//   output) over its keys. A unit covered by one workgroup is written
+//   directly; otherwise every workgroup stores one (m, l, o) partial and a
+//   second launch merges a unit's partials by log-sum-exp. Workgroups are laid
+//   out XCD-contiguously so a unit's splits share one L2.
 //
-// MFMA path (bf16 queries, bf16 or int8 KV, D = 128, >= 16 rows): 32-key tiles
-// stream straight from HBM into registers -- no LDS. With lane = (i = lane %
-// 16, g = lane / 16) and v_mfma_f32_16x16x32_bf16:
+// MFMA path (bf16 queries, bf16 or int8 KV, D = 128, >= 16 rows): workgroups
+// of 4 wave pairs; a pair takes one split, its two waves split the unit's
+// rows and share one LDS ring of 32-key K/V tiles streamed from HBM by
+// LDS-DMA (each wave stages half of every tile). With lane = (i = lane % 16,
+// g = lane / 16) and v_mfma_f32_16x16x32_{bf16,f16}:
 //   S^T = K Q^T : A = K (16 keys x 32 d), B = Q^T (32 d x 16 rows). The two
 //       16-key blocks of a tile take keys 8(i/4) + 4kb + i%4, so the output
 //       lane (i, g) receives keys 8g .. 8g+7 of query row i.
@@ -32,14 +34,13 @@
 //       8 probabilities (k-slot group g <-> keys 8g..8g+7), rounded to fp16.
 //       A = V^T with output row m of d-block db standing for d = 8m + db, so
 //       lane (i, g) needs V[8g + e][8i .. 8i+8) for e = 0..7: eight contiguous
-//       16-byte (bf16) or 8-byte (int8) loads, regrouped in registers. No
-//       transpose through LDS is needed.
+//       16-byte (bf16) or 8-byte (int8) LDS reads, regrouped in registers.
 //   Precision: bf16 values and int8 codes convert to fp16 exactly, so the only
 //       rounding in P V is the fp16 probability (2^-12 relative); a bf16
 //       probability (2^-9) would not hold a 2e-3 bound once a short prefix
 //       makes the softmax peaked. bf16 V must therefore lie in fp16 range.
-//   int8 KV: codes (|c| <= 127) convert exactly to bf16/fp16; the per-token
-//       scales fold into the scores (s = (q . c) * k_scale) and into the
+//   int8 KV: codes (|c| <= 127) convert exactly to fp16; the per-token scales
+//       fold into the scores (s = (q . c) * k_scale) and into the
 //       probabilities (p' = p * v_scale), so the matrix cores only see codes.
 // VALU path (fp32 everything, or fewer than 16 rows): one key per lane for
 // scores, one d per lane for the output, queries and probabilities in LDS.
@@ -71,7 +72,6 @@ struct AttnParams {
   float* out;
   float* part_o;
   float* part_ml;
-  int32_t* counters;
   int B, Hq, Hkv, G, D, cap, split_len, rows_chunk, nwg, split_pad;
   float scale_log2;
   int32_t node_off[TTV_MAX_BATCH + 1];
@@ -168,19 +168,37 @@ __device__ void merge_partials(const AttnParams& p, const Work& w, int slot0, in
   }
 }
 
-// After every thread of the workgroup has stored its share of one of the
-// unit's n partials: count the partial (device-scope); the workgroup that
-// completes the count merges all n and resets the counter to zero.
-__device__ void finish_partial(const AttnParams& p, const Work& w, int slot0, int n, float* wt) {
-  __shared__ int s_last;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = atomicAdd(&p.counters[w.unit], 1) == n - 1;
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  merge_partials(p, w, slot0, n, wt);
-  if (threadIdx.x == 0) atomicExch(&p.counters[w.unit], 0);
+// Second launch: one workgroup per unit whose keys were split over more than
+// one partial merges them (a kernel boundary orders the partials' stores
+// before these loads; an in-kernel device-scope fence would write back whole
+// L2 caches). per_slot: key splits per stored partial (4 for the MFMA path,
+// whose workgroups fold their 4 splits first; 1 for the VALU path).
+constexpr int kMergeWt = 2048;  // rows_chunk * partials per unit, at most
+__global__ void __launch_bounds__(256) merge_kernel(const AttnParams p, int per_slot) {
+  __shared__ float wt[kMergeWt];
+  const int u = blockIdx.x;
+  int lo = 0, hi = p.B;  // unit_off[lo] <= u < unit_off[lo + 1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (p.unit_off[mid] <= u) lo = mid; else hi = mid;
+  }
+  Work w;
+  w.b = lo;
+  w.o0 = p.node_off[lo];
+  w.T = p.node_off[lo + 1] - w.o0;
+  w.P = p.hist_len[lo];
+  w.rows = w.T * p.G;
+  w.rc_n = (w.rows + p.rows_chunk - 1) / p.rows_chunk;
+  const int ns = w.P > 0 ? (w.P + p.split_len - 1) / p.split_len : 1;
+  w.nsplit = (ns + p.split_pad - 1) / p.split_pad * p.split_pad;
+  const int n = w.nsplit / per_slot;
+  if (u >= p.unit_off[lo + 1] || n <= 1) return;
+  const int rem = u - p.unit_off[lo];
+  w.kvh = rem / w.rc_n;
+  w.rc = rem % w.rc_n;
+  w.row0 = w.rc * p.rows_chunk;
+  w.nrows = min(p.rows_chunk, w.rows - w.row0);
+  merge_partials(p, w, (p.wg_off[lo] + rem * w.nsplit) / per_slot, n, wt);
 }
 
 // ------------------------------------------------------------- MFMA path ----
@@ -413,7 +431,6 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
   for (int q = 0; q < NP; ++q) nt_wg = max(nt_wg, s_nt[q]);
   float* mo = reinterpret_cast<float*>(&ring_all[0][0][0]);  // [RBU][8][4][64] lane-major o
   float* mml = mo + RBU * 32 * 64;                             // [RBU * 16][2] (m, l)
-  float* wt = mml + RBU * 32;                                  // merge weights
   // Everything that depends on the wave's row blocks: RB of them from rb0 on.
   // Both halves run the same sequence of workgroup barriers.
   auto per_wave = [&](auto rb_count, const int rb0) {
@@ -682,7 +699,7 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
     // their (m, l, o) into one in LDS, one pair at a time, the two waves of a
     // pair on disjoint rows; (3) a unit covered by this workgroup alone is written
     // out, otherwise one partial per workgroup goes to the workspace and the
-    // unit's last workgroup merges them.
+    // second launch merges them.
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       l[rb] += __shfl_xor(l[rb], 16);
@@ -719,19 +736,25 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
   else per_wave(std::integral_constant<int, RB1>{}, RB0);
 
   const int nwg_unit = w.nsplit / NP;
-  const int wslot0 = (p.wg_off[w.b] + (w.kvh * w.rc_n + w.rc) * w.nsplit) / NP;
-  for (int idx = threadIdx.x; idx < RBU * 32 * 64; idx += 64 * NW) {
-    const int ln = idx & 63, r = (idx >> 6) & 3, db = (idx >> 8) & 7, rb = idx >> 11;
-    const int rloc = rb * 16 + (ln & 15);
-    if (rloc >= w.nrows) continue;
-    const int d = 32 * (ln >> 4) + 8 * r + db;
+  // Row-major stores, four consecutive d per thread (coalesced); the fold
+  // left o in LDS in the MFMA lane order: row 16 rb + i, d = 32 g + 8 r + db
+  // at ((rb * 8 + db) * 4 + r) * 64 + 16 g + i.
+  for (int flat = 4 * threadIdx.x; flat < w.nrows * D; flat += 4 * 64 * NW) {
+    const int rloc = flat / D, d0 = flat % D;
+    const int rb = rloc >> 4, i = rloc & 15;
+    f32x4 v;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int d = d0 + u;
+      v[u] = mo[((rb * 8 + (d & 7)) * 4 + ((d >> 3) & 3)) * 64 + 16 * (d >> 5) + i];
+    }
     if (nwg_unit == 1) {
       const int row = w.row0 + rloc;
       const int node = w.o0 + row / p.G;
       const int qh = w.kvh * p.G + row % p.G;
-      p.out[((size_t)node * p.Hq + qh) * D + d] = mo[idx] / mml[rloc * 2 + 1];
+      *reinterpret_cast<f32x4*>(p.out + ((size_t)node * p.Hq + qh) * D + d0) = v / mml[rloc * 2 + 1];
     } else {
-      p.part_o[((size_t)wgi * p.rows_chunk + rloc) * D + d] = mo[idx];
+      *reinterpret_cast<f32x4*>(p.part_o + ((size_t)wgi * p.rows_chunk + rloc) * D + d0) = v;
     }
   }
   if (nwg_unit > 1) {
@@ -739,7 +762,6 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
       p.part_ml[((size_t)wgi * p.rows_chunk + r) * 2] = mml[r * 2];
       p.part_ml[((size_t)wgi * p.rows_chunk + r) * 2 + 1] = mml[r * 2 + 1];
     }
-    finish_partial(p, w, wslot0, nwg_unit, wt);
   }
 }
 
@@ -905,10 +927,6 @@ __global__ void __launch_bounds__(64) attn_valu_kernel(const AttnParams p) {
 #pragma unroll
     for (int c = 0; c < C; ++c) dst[lane + 64 * c] = o[r][c] * scl;
   }
-  if (!direct) {
-    __shared__ float wt[kValuRows * kMaxSplits];
-    finish_partial(p, w, p.wg_off[w.b] + (w.kvh * w.rc_n + w.rc) * w.nsplit, w.nsplit, wt);
-  }
 }
 
 // ------------------------------------------------------------- planning ----
@@ -918,6 +936,7 @@ struct AttnPlan {
   int rb;
   AttnParams prm;  // everything except pointers
   int nunits;
+  bool merge;  // some unit has more than one partial
   size_t off_ml, off_o, ws_bytes;
 };
 
@@ -988,6 +1007,7 @@ static ttv_status plan_attention(const ttv_batch* batch, int Hq, const ttv_kv_la
   // empty)
   p.split_pad = pl.mfma ? 4 : 1;
   int wg = 0, units = 0;
+  pl.merge = false;
   for (int b = 0; b < B; ++b) {
     const int T = batch->node_off_h[b + 1] - batch->node_off_h[b];
     const int P = batch->hist_len_h[b];
@@ -1000,14 +1020,14 @@ static ttv_status plan_attention(const ttv_batch* batch, int Hq, const ttv_kv_la
     p.unit_off[b] = units;
     wg += p.Hkv * ns * rc;
     units += p.Hkv * rc;
+    if (rc > 0 && ns / p.split_pad > 1) pl.merge = true;
   }
   p.node_off[B] = batch->node_off_h[B];
   p.wg_off[B] = wg;
   p.unit_off[B] = units;
   p.nwg = wg;
   pl.nunits = units;
-  const size_t counters = ((size_t)units * 4 + 255) / 256 * 256;
-  pl.off_ml = counters;
+  pl.off_ml = 0;
   pl.off_o = pl.off_ml + ((size_t)wg * p.rows_chunk * 2 * 4 + 255) / 256 * 256;
   pl.ws_bytes = pl.off_o + (size_t)wg * p.rows_chunk * p.D * 4;
   return TTV_OK;
@@ -1043,7 +1063,6 @@ extern "C" ttv_status tree_verify_attention(const ttv_batch* batch, const void* 
   p.vs = layer->dtype == TTV_I8 ? layer->v_scale : nullptr;
   p.anc = anc;
   p.out = out;
-  p.counters = static_cast<int32_t*>(ws);
   p.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.off_ml);
   p.part_o = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.off_o);
   p.scale_log2 = softmax_scale * kLog2e;
@@ -1076,5 +1095,8 @@ extern "C" ttv_status tree_verify_attention(const ttv_batch* batch, const void* 
     }
 #undef TTV_VALU
   }
-  return check_launch("tree_verify_attention");
+  s = check_launch("tree_verify_attention");
+  if (s != TTV_OK || !pl.merge) return s;
+  hipLaunchKernelGGL(merge_kernel, dim3(static_cast<unsigned>(pl.nunits)), dim3(256), 0, st, p, pl.mfma ? 4 : 1);
+  return check_launch("tree_verify_attention merge");
 }
