@@ -57,6 +57,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kMfmaMaxRB = 6;   // row blocks of 16 per MFMA row chunk (96 rows, two waves)
+constexpr int kI8MaxRB = 5;     // int8: both waves of a pair hold all row blocks (80 rows)
 constexpr int kValuRows = 16;   // rows per VALU workgroup
 constexpr int kTargetWG = 1024;
 constexpr int kMaxSplits = 64;
@@ -674,16 +675,18 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
 #pragma unroll
         for (int db = 0; db < 8; ++db) o[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
+      // (the work of a step sits in the loop body unconditionally: a
+      // conditional accumulation would stop the compiler from updating the
+      // matrix-core accumulators in place)
 #pragma nounroll
-      for (int t = 0; t < nt_wg; ++t) {
-        if (t < ntile) wait_tile(t);
+      for (int t = 0; t < ntile; ++t) {
+        wait_tile(t);
         __syncthreads();  // tile t is complete in every pair; slot (t - 1) % S is free
         if (t + S - 1 < ntile) issue(t + S - 1);
-        if (t < ntile) {
-          scores(t);
-          back();
-        }
+        scores(t);
+        back();
       }
+      for (int t = ntile; t < nt_wg; ++t) __syncthreads();
       // every wave has left the loop (its last wait drained its DMAs) before any
       // ring slot is staged again
       const bool mine = RB > 0 && raise_refs(margin);
@@ -747,6 +750,436 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
     for (int u = 0; u < 4; ++u) {
       const int d = d0 + u;
       v[u] = mo[((rb * 8 + (d & 7)) * 4 + ((d >> 3) & 3)) * 64 + 16 * (d >> 5) + i];
+    }
+    if (nwg_unit == 1) {
+      const int row = w.row0 + rloc;
+      const int node = w.o0 + row / p.G;
+      const int qh = w.kvh * p.G + row % p.G;
+      *reinterpret_cast<f32x4*>(p.out + ((size_t)node * p.Hq + qh) * D + d0) = v / mml[rloc * 2 + 1];
+    } else {
+      *reinterpret_cast<f32x4*>(p.part_o + ((size_t)wgi * p.rows_chunk + rloc) * D + d0) = v;
+    }
+  }
+  if (nwg_unit > 1) {
+    for (int r = threadIdx.x; r < w.nrows; r += 64 * NW) {
+      p.part_ml[((size_t)wgi * p.rows_chunk + r) * 2] = mml[r * 2];
+      p.part_ml[((size_t)wgi * p.rows_chunk + r) * 2 + 1] = mml[r * 2 + 1];
+    }
+  }
+}
+
+// int8 KV, MFMA path, by phase. A workgroup is NP = 4 wave pairs taking 4
+// consecutive key splits of one unit; all RB row blocks of the unit's chunk
+// belong to both waves of a pair. The score wave (h = 0) stages the K tiles
+// and both scale sidecars, forms S = K Q^T, the fp16 probabilities of tile t,
+// their row sums and the v-scaled P' = P * v_scale, and hands P' to the value
+// wave (h = 1) through a double-buffered LDS block; the value wave stages the
+// V tiles and accumulates O += P' V for tile t - 1 in the same step. So every K and V byte is converted
+// once, the two waves share one SIMD (2 waves per SIMD, 256 registers each),
+// and one workgroup barrier per step orders the hand-over.
+template <int RB>
+__global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) {
+  constexpr int NP = 4;                      // wave pairs = consecutive key splits of one unit
+  constexpr int NW = 2 * NP;                 // waves
+  constexpr int D = 128;
+  constexpr int RBYTES = D;                  // bytes of one K (or V) row of codes
+  constexpr int CH = RBYTES / 16;            // 16-byte chunks per row
+  constexpr int KT = 32;                     // keys per tile
+  constexpr int KBYTES = KT * RBYTES;        // one K (or V) tile of codes
+  constexpr int NK = KBYTES / 1024;          // DMA instructions per K (or V) tile
+  constexpr int KSLOT = KBYTES + 128;        // K codes + 32 k-scales + 32 v-scales (fp16)
+  constexpr int VSLOT = KBYTES;              // V codes
+  constexpr int SK = 3, SV = 4;              // K ring and V ring stages (V is used one step later)
+  constexpr int NDK = NK + 1, NDV = NK;      // DMA instructions per staged tile, always all issued
+  __shared__ __attribute__((aligned(16))) char kring_all[NP][SK][KSLOT];
+  __shared__ __attribute__((aligned(16))) char vring_all[NP][SV][VSLOT];
+  __shared__ __attribute__((aligned(16))) u32x4 pbuf_all[NP][2][RB * 64];  // P^T fragments, lane-major
+  __shared__ uint64_t tbits_s[RB * 16];
+  __shared__ float mref_s[NP][RB * 16];  // the score wave's references and row sums, for the fold
+  __shared__ float lref_s[NP][RB * 16];
+  __shared__ int s_nt[NP];
+
+  const int wgi = xcd_slot(blockIdx.x, p.nwg / NP);
+  if (wgi < 0) return;  // whole workgroup
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int pair = wave & (NP - 1);  // the pair's two waves sit on one SIMD
+  const int h = wave / NP;           // 0: score wave, 1: value wave
+  const int lane = threadIdx.x & 63;
+  const int li = lane & 15;
+  const int lg = lane >> 4;
+  Work w;
+  decode(p, wgi * NP + pair, w);  // the pairs share (b, kv head, row chunk)
+
+  for (int r = threadIdx.x; r < RB * 16; r += 64 * NW)
+    tbits_s[r] = r < w.nrows ? row_bits(p, w, w.row0 + r) : 1ull;
+
+  const size_t head = (size_t)w.b * p.Hkv + w.kvh;
+  const char* cbase = static_cast<const char*>(h == 0 ? p.k : p.v) + head * p.cap * RBYTES;  // this wave's codes
+  // score wave, lanes 0-3: k-scales of keys t0 + 8 lane .. +8; lanes 4-7: v-scales
+  const uint16_t* sbase = (lane < 4 ? p.ks : p.vs) + head * p.cap;
+  u32x4(*pbuf)[RB * 64] = pbuf_all[pair];
+  // the fold of the four pairs' (m, l, o) reuses the K rings' space
+  f32x4* mo = reinterpret_cast<f32x4*>(&kring_all[0][0][0]);  // [RB][8][64] lane-major o blocks
+  float* mml = reinterpret_cast<float*>(mo + RB * 8 * 64);      // [RB * 16][2] (m, l)
+  static_assert(RB * 32 * 64 * 4 + RB * 16 * 8 <= NP * SK * KSLOT, "fold area");
+
+  // Per-lane DMA geometry: piece j of a tile is tile row (64 j + lane) / CH,
+  // 16-byte chunk (64 j + lane) % CH of that row (swizzled).
+  auto piece_row = [&](int j) { return (64 * j + lane) / CH; };
+  auto piece_col = [&](int j) {
+    return 16u * static_cast<uint32_t>(((64 * j + lane) % CH) ^ lds_swz<true>(piece_row(j)));
+  };
+  uint32_t koff[NK];
+#pragma unroll
+  for (int j = 0; j < NK; ++j) koff[j] = static_cast<uint32_t>(piece_row(j) * RBYTES) + piece_col(j);
+
+  // Tile list: prefix tiles over [k_lo, k_hi) (the last may be partial), then
+  // on the last split the block tiles over [P, P + T).
+  const int n_pref = w.k_hi > w.k_lo ? (w.k_hi - w.k_lo + KT - 1) / KT : 0;
+  const int ntile = n_pref + (w.last ? (w.T + KT - 1) / KT : 0);
+  auto geom = [&](int t, int& t0, int& mode, int& limit) {
+    if (t < n_pref) {
+      t0 = w.k_lo + KT * t;
+      limit = w.k_hi;
+      mode = t0 + KT <= w.k_hi ? 0 : 1;
+    } else {
+      t0 = w.P + KT * (t - n_pref);
+      limit = w.P + w.T;
+      mode = 2;
+    }
+  };
+  // This wave's tile t (codes, + scales for the score wave) into its ring
+  // slot: exactly NDK or NDV DMA instructions. Boundary tiles clamp every row
+  // into [t0, limit); a scale group reaching past cap is clamped to start at
+  // cap - 8 (cap >= 32).
+  auto slot_of = [&](int t) -> char* {
+    return h == 0 ? kring_all[pair][t % SK] : vring_all[pair][t % SV];
+  };
+  auto issue = [&](int t) {
+    int t0, mode, limit;
+    geom(t, t0, mode, limit);
+    char* dst = slot_of(t);
+    const char* src = cbase + (size_t)t0 * RBYTES;
+    if (mode == 0) {
+#pragma unroll
+      for (int j = 0; j < NK; ++j) dma16(src, koff[j], dst + 1024 * j);
+    } else {
+      const int lim = limit - 1 - t0;
+#pragma unroll
+      for (int j = 0; j < NK; ++j)
+        dma16(src, static_cast<uint32_t>(min(piece_row(j), lim) * RBYTES) + piece_col(j), dst + 1024 * j);
+    }
+    if (h == 0 && lane < 8) dma16v(sbase + min(t0 + 8 * (lane & 3), p.cap - 8), dst + KBYTES);
+  };
+  // the lane group's 8 scales (keys 8g + e of tile t), as fp16 pairs; off 0:
+  // k-scales, 64: v-scales
+  auto scales = [&](const char* sl, int t0, int off) -> u32x4 {
+    if (t0 + KT <= p.cap) return *reinterpret_cast<const u32x4*>(sl + KBYTES + off + 16 * lg);
+    const int delta = max(0, t0 + 8 * lg + 8 - p.cap);
+    const uint16_t* sp = reinterpret_cast<const uint16_t*>(sl + KBYTES + off + 16 * lg);
+    u32x4 r = {0, 0, 0, 0};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e >> 1] |= static_cast<uint32_t>(sp[min(e + delta, 7)]) << (16 * (e & 1));
+    return r;
+  };
+
+  // the score wave stages K tiles 0 .. SK-2, the value wave V tiles 0 .. SV-3
+  // (V tile t is used one step after K tile t)
+  for (int t = 0; t < (h == 0 ? SK - 1 : SV - 2); ++t)
+    if (t < ntile) issue(t);
+  if (lane == 0 && h == 0) s_nt[pair] = ntile;
+  __syncthreads();
+  int nt_wg = 0;
+#pragma unroll
+  for (int q = 0; q < NP; ++q) nt_wg = max(nt_wg, s_nt[q]);
+
+  // References without rescaling (see the lazy bound below): set from the
+  // scores of the split's first tile (row max + kMargin), only tracked inside
+  // the loop; if a row broke the bound the pass runs again from zero with
+  // raised references. Every row's first-tile max is finite: a row sees every
+  // key of a prefix tile and, in a block tile, the root.
+  constexpr float kMargin = 2.0f;
+  if (h == 0) {
+    // ------------------------------------------------------ score wave ----
+    // Q^T fragments in registers: d = 32g + 8ks + e (fp16; a lane's 32 codes
+    // of a K row are contiguous)
+    f16x8 qf[RB][4];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int rloc = rb * 16 + li;
+      const bool ok = rloc < w.nrows;
+      const int row = w.row0 + (ok ? rloc : 0);
+      const int node = w.o0 + row / p.G;
+      const int qh = w.kvh * p.G + row % p.G;
+      const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + ((size_t)node * p.Hq + qh) * D;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        u32x4 x = *reinterpret_cast<const u32x4*>(qrow + 32 * lg + 8 * ks);
+        if (!ok) x = u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          qf[rb][ks][e] =
+              static_cast<_Float16>(__uint_as_float((e & 1) ? (x[e >> 1] & 0xFFFF0000u) : (x[e >> 1] << 16)));
+      }
+    }
+    float m[RB], negm[RB], tmax[RB], l[RB];
+    f32x4 sacc[2][RB];
+    u32x4 vsc;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      m[rb] = -INFINITY;
+      negm[rb] = 0.f;
+    }
+    // scores of tile t: t = s * kss - m (in place of the scores), boundary
+    // masks, running per-row max of t
+    auto scores = [&](int t) {
+      int t0, mode, limit;
+      geom(t, t0, mode, limit);
+      const char* sl = kring_all[pair][t % SK];
+      const u32x4 ksc = scales(sl, t0, 0);
+      vsc = scales(sl, t0, 64);
+      float kss[8];  // score scale of key 8g + e, log2 units
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kss[e] = static_cast<float>(__builtin_bit_cast(f16x8, ksc)[e]) * p.scale_log2;
+      // S^T = K Q^T: block kb takes tile rows 8(i/4) + 4kb + i%4
+      u32x4 kraw[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int r = 8 * (li >> 2) + 4 * kb + (li & 3);
+        const char* krow = sl + r * RBYTES;
+        const int sw = lds_swz<true>(r);
+        kraw[kb][0] = *reinterpret_cast<const u32x4*>(krow + 16 * ((2 * lg) ^ sw)) ^ 0x80808080u;
+        kraw[kb][1] = *reinterpret_cast<const u32x4*>(krow + 16 * ((2 * lg + 1) ^ sw)) ^ 0x80808080u;
+      }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        f16x8 kf[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const u32x4& src = kraw[kb][ks >> 1];
+          kf[kb] = i8x8_to_f16(src[2 * (ks & 1)], src[2 * (ks & 1) + 1]);
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+            sacc[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[kb], qf[rb][ks], ks == 0 ? zero : sacc[kb][rb],
+                                                                  0, 0, 0);
+          }
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sacc[e >> 2][rb][e & 3] = fmaf(sacc[e >> 2][rb][e & 3], kss[e], negm[rb]);
+      if (mode != 0) {  // boundary tiles only: keys past the range, non-ancestors
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const uint64_t bits = mode == 2 ? tbits_s[rb * 16 + li] : ~0ull;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int key = t0 + 8 * lg + e;
+            const bool keep = key < limit && ((bits >> ((key - w.P) & 63)) & 1ull);
+            sacc[e >> 2][rb][e & 3] = keep ? sacc[e >> 2][rb][e & 3] : -INFINITY;
+          }
+        }
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          tmax[rb] = fmaxf(fmaxf(tmax[rb], sacc[kb][rb][0]), sacc[kb][rb][1]);
+          tmax[rb] = fmaxf(fmaxf(tmax[rb], sacc[kb][rb][2]), sacc[kb][rb][3]);
+        }
+    };
+    // probabilities of the scored tile: p = 2^t in fp16 (t <= 6 while the
+    // references hold, so p <= 64 and p * v_scale fits fp16); the row sums of
+    // exactly these p; P' = P * v_scale into P buffer b
+    auto hand_over = [&](int b) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        f16x8 pr;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pr[e] = static_cast<_Float16>(__builtin_amdgcn_exp2f(sacc[e >> 2][rb][e & 3]));
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          l[rb] = __builtin_amdgcn_fdot2(f16x2{pr[2 * k], pr[2 * k + 1]}, f16x2{1, 1}, l[rb], false);
+        pbuf[b][rb * 64 + lane] = __builtin_bit_cast(u32x4, pr * __builtin_bit_cast(f16x8, vsc));
+      }
+    };
+    auto raise_refs = [&](float margin) -> bool {  // from tmax; true if any row moved
+      bool moved = false;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        float mx = fmaxf(tmax[rb], __shfl_xor(tmax[rb], 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        if (__ballot(mx > 6.0f) != 0) {
+          moved = true;
+          m[rb] = (m[rb] == -INFINITY ? 0.f : m[rb]) + mx + margin;
+          negm[rb] = -m[rb];
+        }
+      }
+      return moved;
+    };
+
+    if (ntile > 0) {
+      wait_vmcnt_tiles<NDK>(min(SK - 2, ntile - 1));
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) tmax[rb] = -INFINITY;
+      scores(0);  // with m = -inf (negm = 0): t is the score itself
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        float mx = fmaxf(tmax[rb], __shfl_xor(tmax[rb], 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        m[rb] = mx + kMargin;
+        negm[rb] = -m[rb];
+      }
+    }
+    float margin = 2.0f * kMargin;
+    for (;;) {  // attempts
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        tmax[rb] = -INFINITY;
+        l[rb] = 0.f;
+      }
+      // (the work of a step sits in the loop body unconditionally: a
+      // conditional accumulation would stop the compiler from updating the
+      // matrix-core accumulators in place)
+#pragma nounroll
+      for (int t = 0; t < ntile; ++t) {
+        wait_vmcnt_tiles<NDK>(min(SK - 2, ntile - 1 - t));
+        __syncthreads();  // K tile t landed; P buffer t % 2 was read a step ago
+        if (t + SK - 1 < ntile) issue(t + SK - 1);
+        scores(t);
+        hand_over(t & 1);
+      }
+      for (int t = ntile; t <= nt_wg; ++t) __syncthreads();
+      const bool redo = __syncthreads_or(raise_refs(margin));
+      if (!redo) break;
+      margin += kMargin;  // a wider margin on every attempt
+      for (int u = 0; u < SK - 1; ++u)
+        if (u < ntile) issue(u);
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      l[rb] += __shfl_xor(l[rb], 16);
+      l[rb] += __shfl_xor(l[rb], 32);
+      if (lg == 0) {
+        mref_s[pair][rb * 16 + li] = m[rb];
+        lref_s[pair][rb * 16 + li] = l[rb];
+      }
+    }
+    __syncthreads();  // references visible, rings idle
+    for (int step = 0; step < NP; ++step) __syncthreads();  // the value waves fold
+  } else {
+    // ------------------------------------------------------ value wave ----
+    f32x4 o[8][RB];
+    // O^T += V^T P'^T for tile t from P buffer b: lane (i, g) reads V rows
+    // 8g + e, d = 8i .. 8i+7
+    auto accumulate = [&](int t, int b) {
+      const char* sl = vring_all[pair][t % SV];
+      uint32_t a[8][2];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 8 * lg + e;
+        const u32x2 v2 = *reinterpret_cast<const u32x2*>(sl + r * RBYTES + 16 * ((li >> 1) ^ lds_swz<true>(r)) +
+                                                         8 * (li & 1));
+        a[e][0] = v2[0] ^ 0x80808080u;
+        a[e][1] = v2[1] ^ 0x80808080u;
+      }
+      // V^T fragments of the 8 d-blocks: d-block db = 4hh + j takes byte j of
+      // dword hh of keys e = 0..7
+      u32x4 vf[8];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        uint32_t ilo[4], ihi[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          ilo[k] = __builtin_amdgcn_perm(a[2 * k + 1][hh], a[2 * k][hh], 0x05010400u);  // a0 b0 a1 b1
+          ihi[k] = __builtin_amdgcn_perm(a[2 * k + 1][hh], a[2 * k][hh], 0x07030602u);  // a2 b2 a3 b3
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            vf[4 * hh + j][k] = f16pair_from_bytes(j < 2 ? ilo[k] : ihi[k], (j & 1) ? 0x04030402u : 0x04010400u);
+      }
+      // one row block's P'^T fragment at a time (register budget: o holds 32 RB)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const f16x8 pw = __builtin_bit_cast(f16x8, pbuf[b][rb * 64 + lane]);
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+          o[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, vf[db]), pw, o[db][rb], 0, 0, 0);
+      }
+    };
+    for (;;) {  // attempts, in step with the score wave
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int db = 0; db < 8; ++db) o[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      __syncthreads();  // step 0
+      if (SV - 2 < ntile) issue(SV - 2);
+#pragma nounroll
+      for (int t = 1; t <= ntile; ++t) {
+        // V tile t - 1 has landed: at most the tiles issued after it remain
+        wait_vmcnt_tiles<NDV>(min(SV - 2, ntile - t));
+        __syncthreads();  // P of tile t - 1 is in buffer (t - 1) % 2
+        if (t + SV - 2 < ntile) issue(t + SV - 2);
+        accumulate(t - 1, (t - 1) & 1);
+      }
+      for (int t = ntile + 1; t <= nt_wg; ++t) __syncthreads();
+      const bool redo = __syncthreads_or(false);
+      if (!redo) break;
+      for (int u = 0; u < SV - 2; ++u)
+        if (u < ntile) issue(u);
+    }
+    __syncthreads();  // references and row sums visible, rings idle
+    // the four pairs (four consecutive splits) fold their (m, l, o) into one,
+    // one pair at a time
+    for (int step = 0; step < NP; ++step) {
+      if (pair == step) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const int rloc = rb * 16 + li;
+          const float m_new = mref_s[pair][rloc];
+          const float l_new = lref_s[pair][rloc];
+          const float m_old = step ? mml[rloc * 2] : -INFINITY;
+          const float l_old = step ? mml[rloc * 2 + 1] : 0.f;
+          const float mn = fmaxf(m_old, m_new);
+          const float a_old = m_old == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_old - mn);
+          const float a_new = m_new == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_new - mn);
+#pragma unroll
+          for (int db = 0; db < 8; ++db) {
+            const int idx = (rb * 8 + db) * 64 + lane;
+            mo[idx] = step ? o[db][rb] * a_new + mo[idx] * a_old : o[db][rb] * a_new;
+          }
+          if (lg == 0) {
+            mml[rloc * 2] = mn;
+            mml[rloc * 2 + 1] = l_new * a_new + l_old * a_old;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue ----
+  // A unit covered by this workgroup alone is written out, otherwise one
+  // partial per workgroup goes to the workspace and a second launch merges
+  // them.
+  const int nwg_unit = w.nsplit / NP;
+  // Row-major stores, four consecutive d per thread (coalesced); o sits in LDS
+  // in the MFMA lane order: row 16 rb + i, d = 32 g + 8 r + db is element r of
+  // block (rb * 8 + db) * 64 + 16 g + i.
+  for (int flat = 4 * threadIdx.x; flat < w.nrows * D; flat += 4 * 64 * NW) {
+    const int rloc = flat / D, d0 = flat % D;
+    const int rb = rloc >> 4, i = rloc & 15;
+    f32x4 v;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int d = d0 + u;
+      v[u] = mo[(rb * 8 + (d & 7)) * 64 + 16 * (d >> 5) + i][(d >> 3) & 3];
     }
     if (nwg_unit == 1) {
       const int row = w.row0 + rloc;
@@ -970,13 +1403,12 @@ static ttv_status plan_attention(const ttv_batch* batch, int Hq, const ttv_kv_la
   }
   pl.mfma = bf && L->D == 128 && max_rows >= 16 && L->cap >= 32;
   if (pl.mfma) {
-    // balanced row chunks of at most 96 rows: pl.rb row blocks, split
-    // between the two waves of a pair
-    const int max_rows_chunk = 16 * kMfmaMaxRB;
+    // balanced row chunks of at most 96 rows (int8: 80): pl.rb row blocks
+    const int max_rows_chunk = 16 * (L->dtype == TTV_I8 ? kI8MaxRB : kMfmaMaxRB);
     const int nch = (max_rows + max_rows_chunk - 1) / max_rows_chunk;
     const int per = (max_rows + nch - 1) / nch;
     pl.rb = (per + 15) / 16;
-    if (pl.rb < 2) pl.rb = 2;  // one block per wave at least
+    if (L->dtype != TTV_I8 && pl.rb < 2) pl.rb = 2;  // one block per wave of a pair at least
   } else {
     pl.rb = 0;
   }
@@ -1073,9 +1505,17 @@ extern "C" ttv_status tree_verify_attention(const ttv_batch* batch, const void* 
   if (pl.mfma) {
 #define TTV_MFMA(I, R0, R1) \
   hipLaunchKernelGGL((attn_mfma_kernel<I, R0, R1, (I) ? 4 : 2>), dim3(mgrid), dim3(512), 0, st, p)
-#define TTV_MFMA_RB(R0, R1) \
-  if (i8) TTV_MFMA(true, R0, R1); else TTV_MFMA(false, R0, R1)
-    switch (pl.rb) {  // row blocks of a chunk, split between the two waves of a pair
+#define TTV_MFMA_RB(R0, R1) TTV_MFMA(false, R0, R1)
+#define TTV_SPLIT(R) hipLaunchKernelGGL((attn_i8_split_kernel<R>), dim3(mgrid), dim3(512), 0, st, p)
+    if (i8) {
+      switch (pl.rb) {
+        case 1: TTV_SPLIT(1); break;
+        case 2: TTV_SPLIT(2); break;
+        case 3: TTV_SPLIT(3); break;
+        case 4: TTV_SPLIT(4); break;
+        default: TTV_SPLIT(5); break;
+      }
+    } else switch (pl.rb) {  // row blocks of a chunk, split between the two waves of a pair
       case 1: case 2: TTV_MFMA_RB(1, 1); break;
       case 3: TTV_MFMA_RB(2, 1); break;
       case 4: TTV_MFMA_RB(2, 2); break;
@@ -1083,6 +1523,7 @@ extern "C" ttv_status tree_verify_attention(const ttv_batch* batch, const void* 
       default: TTV_MFMA_RB(3, 3); break;
     }
 #undef TTV_MFMA_RB
+#undef TTV_SPLIT
 #undef TTV_MFMA
   } else {
 #define TTV_VALU(Q, K, DD) hipLaunchKernelGGL((attn_valu_kernel<Q, K, DD>), dim3(grid), dim3(64), 0, st, p)
