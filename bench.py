@@ -188,14 +188,19 @@ def pmc_summary(fetch_csv: str, write_csv: str, calib_mib: int) -> None:
     print(f"  {calib_mib} MiB copied; FETCH_SIZE {cf:.0f} KiB -> {f_scale:.4f} B per counted B; "
           f"WRITE_SIZE {cw:.0f} KiB -> {w_scale:.4f} B per counted B")
     print(f"{'kernel':90s} {'n':>4s} {'fetch MB':>10s} {'write MB':>10s} {'scaled MB':>10s}")
-    attn = None
+    attn = None   # the attention call = its main kernel + the merge kernel
+    merge = (0.0, 0.0, 0.0)
     for k in sorted(set(fetch) & set(write)):
         fv, wv = fetch[k], write[k]
         fm, wm = sum(fv) / len(fv) * 1024, sum(wv) / len(wv) * 1024
         tot = fm * f_scale + wm * w_scale
         print(f"{k[:90]:90s} {len(fv):4d} {fm / 1e6:10.2f} {wm / 1e6:10.2f} {tot / 1e6:10.2f}")
-        if "attn_mfma_kernel" in k and (attn is None or tot > attn[1]):
+        if ("attn_mfma_kernel" in k or "attn_i8_split_kernel" in k) and (attn is None or tot > attn[1]):
             attn = (k, tot, fm * f_scale, wm * w_scale)
+        if "merge_kernel" in k:
+            merge = (tot, fm * f_scale, wm * w_scale)
+    if attn is not None:
+        attn = (attn[0], attn[1] + merge[0], attn[2] + merge[1], attn[3] + merge[2])
     if attn is not None:
         rec = {"kernel": attn[0], "traffic_bytes": round(attn[1]), "read_bytes": round(attn[2]),
                "write_bytes": round(attn[3]), "kernel_source_sha256": source_digest(ATTN_SOURCE)}

@@ -10,7 +10,7 @@ import torch
 
 import oracle as O
 from workloads import (binary_tree_7, chain_tree, config1_round, config2_round, config3_round, config4_round,
-                       confidence_tree, host_tensors, make_kv_cache, make_queries, plant_walk, planted_logits,
+                       config5_round, config5_schedule, confidence_tree, host_tensors, make_kv_cache, make_queries, plant_walk, planted_logits,
                        random_descent, random_tree, rng_for, sary_tree)
 
 from gpu_util import (layer_to_dev, layer_to_host, log, run_argmax, run_attention, run_mask, run_walk, spec_batch,
@@ -414,6 +414,37 @@ def test_attention_grid(ttv, case):
     _attn_check(ttv, spec, tensors, TOL_F32 if kv == "f32" else TOL_BF16, label=f"grid {GRID[case]}")
 
 
+@pytest.mark.parametrize("kv", ["i8", "bf16"])
+def test_attention_peaked_scores(ttv, kv):
+    """Scores far above a split's first tile: a few planted keys aligned with
+    their query (scaled queries make every row sharper too). The kernels fix
+    each row's reference from the first tile of a split and run the split again
+    with raised references when a later score exceeds it by more than the fp16
+    headroom; the result must still match the float64 oracle."""
+    from workloads.configs import _spec
+    from workloads.gen import bf16_bits_to_f32, quantize_int8_per_token, to_bf16_bits
+    r = rng_for(1250, 0 if kv == "i8" else 1)
+    T, P, Hq, Hkv, D = 16, 3000, 40, 8, 128
+    parent = confidence_tree(r, T, 8, 1000, 4)[0]
+    spec = _spec(1250, 1, 1, Hq, Hkv, D, 16, 1.0, kv, "bf16", [P], [parent], [np.zeros(T, np.int64)],
+                 [np.zeros(T, np.int64)], [[0]])
+    q = bf16_bits_to_f32(make_queries(1251, 0, T, Hq, D, "bf16")) * 3.0
+    cache = make_kv_cache(1252, 0, 1, Hkv, P + T + 3, D, "f32")
+    G = Hq // Hkv
+    for key, node, h in ((1500, 0, 0), (2900, 3, 7), (700, 15, 39), (2047, 9, 12)):
+        cache["k"][0, h // G, key] = 0.5 * q[node, h]            # score ~ 0.5 |q|^2 / sqrt(D): a spike
+    if kv == "i8":
+        layer = {}
+        for n in ("k", "v"):
+            code, scale = quantize_int8_per_token(cache[n])
+            layer[n], layer[n + "_scale"] = code, scale
+    else:
+        layer = {n: to_bf16_bits(cache[n]) for n in ("k", "v")}
+    layer["q"] = to_bf16_bits(q)
+    log(f"attention peaked {kv}")
+    _attn_check(ttv, spec, {"layers": [layer]}, TOL_BF16, label=f"peaked {kv}")
+
+
 def test_attention_ragged_batch(ttv):
     spec = config4_round(B=12, pmin=0, pmax=2500)
     spec.parents[3] = np.zeros(0, np.int32)        # an empty tree in the middle of the batch
@@ -472,3 +503,104 @@ def test_round_config1_end_to_end(ttv, acc, dup):
     got = layer_to_host(dev)
     for n in want["caches"][0]:
         np.testing.assert_array_equal(got[n], want["caches"][0][n])
+
+
+# -------------------------------------------------------- long-context ----
+
+def test_long_context_rounds_cache_tracks_oracle(ttv):
+    """The long-context stress loop at reduced size (B=2, 2 layers, 10/2 heads,
+    4096-token start, 16-node trees): every round appends the block's 16 rows,
+    runs mask -> attention -> argmax -> walk -> in-place rollback on the GPU,
+    and the paths, emitted tokens, attention and the whole cache (codes and
+    scales) must equal the oracle's, round after round. The schedule mixes
+    scattered tree paths, full accepts (identity selection) and partial
+    accepts (prefix selection)."""
+    from workloads.gen import quantize_int8_per_token
+    B, L, T, Hq, Hkv, D, V = 2, 2, 16, 10, 2, 128, 4096
+    rounds = 12
+    sched = config5_schedule(rounds, seed=77)
+    hist = np.array([4096, 4096 - 40], np.int64)
+    cap = int(hist.max()) + T * rounds + 64
+    mirror = [make_kv_cache(1300, l, B, Hkv, cap, D, "i8") for l in range(L)]
+    devs, layers = zip(*[layer_to_dev(ttv, m) for m in mirror])
+    scale = 1.0 / math.sqrt(D)
+    for r, kind in enumerate(sched):
+        spec = config5_round(r, hist.copy(), kind, seed=77, B=B, L=L, T=T, Hq=Hq, Hkv=Hkv, vocab=V)
+        # the block's 16 rows are appended at P_b (both copies)
+        for l in range(L):
+            for b in range(B):
+                P = int(hist[b])
+                for n in ("k", "v"):
+                    x = rng_for(1301, r, l, b, 0 if n == "k" else 1).standard_normal((Hkv, T, D), dtype=np.float32)
+                    code, sc = quantize_int8_per_token(x)
+                    mirror[l][n][b, :, P:P + T] = code
+                    mirror[l][n + "_scale"][b, :, P:P + T] = sc
+                    devs[l][n][b, :, P:P + T] = to_dev(code)
+                    devs[l][n + "_scale"][b, :, P:P + T] = to_dev(sc)
+        qs = [make_queries(1302, r * L + l, spec.n_nodes, Hq, D, "bf16") for l in range(L)]
+        logits = planted_logits(rng_for(1303, r), spec.flat_targets, V, 2.0)
+        want = O.verify_round(spec, {"layers": [dict(mirror[l], q=qs[l]) for l in range(L)], "logits": logits})
+        # GPU round
+        batch = spec_batch(ttv, spec)
+        par = to_dev(spec.flat("parents"))
+        anc, _, st = run_mask(ttv, batch, par)
+        for l in range(L):
+            out, _ = run_attention(ttv, batch, to_dev(qs[l], "bf16"), layers[l], anc, scale)
+            err = float(np.abs(to_host(out) - want["attn"][l]).max())
+            assert err <= TOL_BF16, (r, kind, l, err)
+        am = run_argmax(ttv, to_dev(logits))
+        path, plen, emitted, sel, sel_len, st2 = run_walk(ttv, batch, par, to_dev(spec.flat("tokens").astype(np.int32)), am)
+        live = (spec.hist_len + np.diff(spec.node_off)).astype(np.int32)
+        gst = status()
+        ttv.kv_gather_positions(list(layers), None, sel, sel_len, live, gst, zeros_ws(ttv.kv_gather_positions_ws(B)))
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0 and int(st2.item()) == 0 and int(gst.item()) == 0
+        pl = to_host(plen)
+        for b in range(B):
+            assert list(to_host(path)[b, :pl[b]]) == list(want["paths"][b]), (r, kind, b)
+            assert list(to_host(emitted)[b, :pl[b]]) == list(want["emitted"][b]), (r, kind, b)
+        assert list(to_host(sel_len)) == [len(x) for x in want["sels"]]
+        for l in range(L):
+            got = layer_to_host(devs[l])
+            for n in got:
+                np.testing.assert_array_equal(got[n], want["caches"][l][n], err_msg=f"round {r} {kind} layer {l} {n}")
+            mirror[l] = want["caches"][l]
+        log(f"long-context round {r} {kind}: paths {[len(x) - 1 for x in want['paths']]} ok")
+        hist = np.array([len(x) for x in want["sels"]], np.int64)
+
+
+def test_long_context_full_size_sampled(ttv):
+    """The long-context workload at full size (B=8, 131,072-token prefix,
+    16-node trees, int8 KV, 40/8 heads) in the bench's launch configuration:
+    sampled output rows checked one by one against the oracle."""
+    from workloads.device import dev_kv_cache, dev_queries
+    spec = config5_round(0, [131072] * 8, "tree", L=1)
+    cap = int(max(spec.hist_len + np.diff(spec.node_off)))
+    c = dev_kv_cache(spec.seed, 100, spec.B, spec.Hkv, cap, spec.D, "i8", "cuda")
+    layer = ttv.KVLayer(c["k"], c["v"], c["k_scale"], c["v_scale"])
+    q = dev_queries(spec.seed, 200, spec.n_nodes, spec.Hq, spec.D, "bf16", "cuda")
+    batch = spec_batch(ttv, spec)
+    anc, _, st = run_mask(ttv, batch, to_dev(spec.flat("parents")))
+    out, _ = run_attention(ttv, batch, q, layer, anc, 1 / math.sqrt(spec.D))
+    torch.cuda.synchronize()
+    r = rng_for(1310)
+    worst = 0.0
+    for _ in range(6):
+        b = int(r.integers(0, spec.B))
+        t = int(r.integers(0, 16))
+        g = int(r.integers(0, spec.Hkv))
+        node = int(spec.node_off[b]) + t
+        P = int(spec.hist_len[b])
+        lay = {n: c[n][b:b + 1, g:g + 1, :P + 16].cpu().numpy() for n in ("k", "v", "k_scale", "v_scale")}
+        qh = q[node:node + 1, g * spec.G:(g + 1) * spec.G].view(torch.int16).cpu().numpy().view(np.uint16)
+        par = spec.parents[b]
+        # the whole tree, one KV head: the oracle's row for (node t, each head of the group)
+        qt = np.zeros((16, spec.G, spec.D), np.uint16)
+        qt[t] = qh[0]
+        want = O.tree_verify_attention(qt, lay, np.array([0, 16]), np.array([P]), [par], 1 / math.sqrt(spec.D),
+                                       "bf16", "i8")[t]
+        got = to_host(out[node, g * spec.G:(g + 1) * spec.G])
+        worst = max(worst, float(np.abs(got - want).max()))
+    log(f"full-size sampled rows: max|err| {worst:.3e}")
+    assert worst <= TOL_BF16
+    assert np.isfinite(to_host(out)).all()

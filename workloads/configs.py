@@ -174,24 +174,24 @@ def config5_schedule(n_rounds: int = 100, seed: int = 5) -> list:
 
 
 def config5_round(round_idx: int, hist_len, kind: str, seed: int = 5, B: int = 8, L: int = 8,
-                  T: int = 16) -> RoundSpec:
+                  T: int = 16, Hq: int = 40, Hkv: int = 8, vocab: int = 248320) -> RoundSpec:
     parents, tokens, targets, paths = [], [], [], []
     for b in range(B):
         if kind == "tree":
-            parent, tok0 = confidence_tree(rng_for(seed, 50, round_idx, b), T, 8, 248320, 4)
+            parent, tok0 = confidence_tree(rng_for(seed, 50, round_idx, b), T, 8, vocab, 4)
             d = random_descent(parent, rng_for(seed, 51, round_idx, b), first_child_not=1)
             path = d
-            tok, tgt, _ = plant_walk(parent, path, rng_for(seed, 52, round_idx, b), 248320, tokens=tok0)
+            tok, tgt, _ = plant_walk(parent, path, rng_for(seed, 52, round_idx, b), vocab, tokens=tok0)
         else:
             parent = chain_tree(T)
             acc = T - 1 if kind == "full" else int(rng_for(seed, 53, round_idx, b).integers(0, T - 1))
             path = list(range(acc + 1))
-            tok, tgt, _ = plant_walk(parent, path, rng_for(seed, 54, round_idx, b), 248320)
+            tok, tgt, _ = plant_walk(parent, path, rng_for(seed, 54, round_idx, b), vocab)
         parents.append(parent)
         tokens.append(tok)
         targets.append(tgt)
         paths.append(path)
-    return _spec(seed, B, L, 40, 8, 128, 248320, 2.0, "i8", "bf16", hist_len, parents, tokens,
+    return _spec(seed, B, L, Hq, Hkv, 128, vocab, 2.0, "i8", "bf16", hist_len, parents, tokens,
                  targets, paths, note=f"round {round_idx} {kind}")
 
 
