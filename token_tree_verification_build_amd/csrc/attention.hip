@@ -373,6 +373,7 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
   // on the last split the block tiles over [P, P + T).
   const int n_pref = w.k_hi > w.k_lo ? (w.k_hi - w.k_lo + KT - 1) / KT : 0;
   const int ntile = n_pref + (w.last ? (w.T + KT - 1) / KT : 0);
+  const int n_full = w.k_hi > w.k_lo ? (w.k_hi - w.k_lo) / KT : 0;  // the leading mode-0 tiles
   auto geom = [&](int t, int& t0, int& mode, int& limit) {
     if (t < n_pref) {
       t0 = w.k_lo + KT * t;
@@ -458,7 +459,7 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) negm[rb] = 0.f;
 
-    auto scores = [&](int t) {
+    auto scores = [&](int t, auto masked) {
       int t0, mode, limit;
       geom(t, t0, mode, limit);
       sl = ring[t % S];
@@ -539,7 +540,7 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) sacc[e >> 2][rb][e & 3] = fmaf(sacc[e >> 2][rb][e & 3], kss[e], negm[rb]);
       }
-      if (mode != 0) {  // boundary tiles only: keys past the range, non-ancestors
+      if (decltype(masked)::value && mode != 0) {  // boundary tiles: keys past the range, non-ancestors
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           const uint64_t bits = mode == 2 ? tbits_s[(rb0 + rb) * 16 + li] : ~0ull;
@@ -657,7 +658,7 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
     if (ntile > 0) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) tmax[rb] = -INFINITY;
-      scores(0);  // with m = -inf (negm = 0): t is the score itself
+      scores(0, std::true_type{});  // with m = -inf (negm = 0): t is the score itself
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         float mx = fmaxf(tmax[rb], __shfl_xor(tmax[rb], 16));
@@ -678,14 +679,19 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
       // (the work of a step sits in the loop body unconditionally: a
       // conditional accumulation would stop the compiler from updating the
       // matrix-core accumulators in place)
-#pragma nounroll
-      for (int t = 0; t < ntile; ++t) {
+      // full prefix tiles need no masks and come first; a loop of their own
+      // keeps the mask code (and its register shuffles) off their path
+      auto step = [&](int t, auto masked) {
         wait_tile(t);
         __syncthreads();  // tile t is complete in every pair; slot (t - 1) % S is free
         if (t + S - 1 < ntile) issue(t + S - 1);
-        scores(t);
+        scores(t, masked);
         back();
-      }
+      };
+#pragma nounroll
+      for (int t = 0; t < n_full; ++t) step(t, std::false_type{});
+#pragma nounroll
+      for (int t = n_full; t < ntile; ++t) step(t, std::true_type{});
       for (int t = ntile; t < nt_wg; ++t) __syncthreads();
       // every wave has left the loop (its last wait drained its DMAs) before any
       // ring slot is staged again
@@ -837,6 +843,7 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
   // on the last split the block tiles over [P, P + T).
   const int n_pref = w.k_hi > w.k_lo ? (w.k_hi - w.k_lo + KT - 1) / KT : 0;
   const int ntile = n_pref + (w.last ? (w.T + KT - 1) / KT : 0);
+  const int n_full = w.k_hi > w.k_lo ? (w.k_hi - w.k_lo) / KT : 0;  // the leading mode-0 tiles
   auto geom = [&](int t, int& t0, int& mode, int& limit) {
     if (t < n_pref) {
       t0 = w.k_lo + KT * t;
@@ -932,7 +939,7 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
     }
     // scores of tile t: t = s * kss - m (in place of the scores), boundary
     // masks, running per-row max of t
-    auto scores = [&](int t) {
+    auto scores = [&](int t, auto masked) {
       int t0, mode, limit;
       geom(t, t0, mode, limit);
       const char* sl = kring_all[pair][t % SK];
@@ -972,7 +979,7 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int e = 0; e < 8; ++e) sacc[e >> 2][rb][e & 3] = fmaf(sacc[e >> 2][rb][e & 3], kss[e], negm[rb]);
-      if (mode != 0) {  // boundary tiles only: keys past the range, non-ancestors
+      if (decltype(masked)::value && mode != 0) {  // boundary tiles: keys past the range, non-ancestors
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           const uint64_t bits = mode == 2 ? tbits_s[rb * 16 + li] : ~0ull;
@@ -1026,7 +1033,7 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
       wait_vmcnt_tiles<NDK>(min(SK - 2, ntile - 1));
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) tmax[rb] = -INFINITY;
-      scores(0);  // with m = -inf (negm = 0): t is the score itself
+      scores(0, std::true_type{});  // with m = -inf (negm = 0): t is the score itself
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         float mx = fmaxf(tmax[rb], __shfl_xor(tmax[rb], 16));
@@ -1045,14 +1052,19 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
       // (the work of a step sits in the loop body unconditionally: a
       // conditional accumulation would stop the compiler from updating the
       // matrix-core accumulators in place)
-#pragma nounroll
-      for (int t = 0; t < ntile; ++t) {
+      // full prefix tiles need no masks and come first; a loop of their own
+      // keeps the mask code (and its register shuffles) off their path
+      auto step = [&](int t, auto masked) {
         wait_vmcnt_tiles<NDK>(min(SK - 2, ntile - 1 - t));
         __syncthreads();  // K tile t landed; P buffer t % 2 was read a step ago
         if (t + SK - 1 < ntile) issue(t + SK - 1);
-        scores(t);
+        scores(t, masked);
         hand_over(t & 1);
-      }
+      };
+#pragma nounroll
+      for (int t = 0; t < n_full; ++t) step(t, std::false_type{});
+#pragma nounroll
+      for (int t = n_full; t < ntile; ++t) step(t, std::true_type{});
       for (int t = ntile; t <= nt_wg; ++t) __syncthreads();
       const bool redo = __syncthreads_or(raise_refs(margin));
       if (!redo) break;
