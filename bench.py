@@ -33,7 +33,8 @@ def parse():
     ap.add_argument("--take-reps", type=int, default=3, help="timed reps of the full-window out-of-place gather")
     ap.add_argument("--no-take", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-heads", type=int, default=2, help="KV heads in the CPU oracle sample")
+    ap.add_argument("--cpu-heads", type=int, default=8, help="KV heads per sampled sequence in the CPU oracle sample")
+    ap.add_argument("--cpu-seqs", type=int, default=2, help="sequences in the CPU oracle sample")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after the timed region, run one plain device copy of this many MiB (the reference "
                          "dispatch that scales FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -95,54 +96,58 @@ def attention_flops(spec) -> int:
     return 4 * spec.D * spec.Hq * total
 
 
-def cpu_baseline(spec, caches, qs, logits, heads: int):
+def cpu_baseline(spec, caches, qs, logits, heads: int, seqs: int):
     """The oracle, untuned, on a bounded sample of the same round: layer 0,
-    sequence 0, KV heads [0, heads), that sequence's argmax, walk and a
-    one-layer rollback gather over the same heads; scaled to a full round."""
+    sequences [0, seqs), KV heads [0, heads) of each, each sequence's argmax,
+    walk and a one-layer rollback gather over the same heads; scaled to a
+    full round."""
     import numpy as np
 
     import oracle as O
 
-    b = 0
-    P = int(spec.hist_len[b])
-    o0, o1 = int(spec.node_off[b]), int(spec.node_off[b + 1])
-    T = o1 - o0
     G = spec.G
     c = caches[0]
-    lay = {}
-    for n, t in c.items():
-        sl = t[b:b + 1, :heads, :P + T]
-        lay[n] = sl.view(torch_int16()).cpu().numpy().view(np.uint16) if str(t.dtype) == "torch.bfloat16" \
-            else sl.cpu().numpy()
-    q = qs[0][o0:o1, :heads * G]
-    qh = q.view(torch_int16()).cpu().numpy().view(np.uint16) if spec.q_dtype == "bf16" else q.cpu().numpy()
-    lg = logits[o0:o1].cpu().numpy()
     threads = len(os.sched_getaffinity(0))
-    t0 = time.perf_counter()
-    O.tree_verify_attention(qh, lay, np.array([0, T]), np.array([P]), [spec.parents[b]], 1 / math.sqrt(spec.D),
-                            spec.q_dtype, spec.kv_dtype)
-    t_attn = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    am = O.vocab_argmax(lg)
-    path, _ = O.tree_accept_walk(spec.parents[b], spec.tokens[b], am)
-    t_walk = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    O.gather_layer(lay, [O.rollback_selection(P, path)])
-    t_gather = time.perf_counter() - t0
+    t_attn = t_walk = t_gather = 0.0
+    for b in range(seqs):
+        P = int(spec.hist_len[b])
+        o0, o1 = int(spec.node_off[b]), int(spec.node_off[b + 1])
+        T = o1 - o0
+        lay = {}
+        for n, t in c.items():
+            sl = t[b:b + 1, :heads, :P + T]
+            lay[n] = sl.view(torch_int16()).cpu().numpy().view(np.uint16) if str(t.dtype) == "torch.bfloat16" \
+                else sl.cpu().numpy()
+        q = qs[0][o0:o1, :heads * G]
+        qh = q.view(torch_int16()).cpu().numpy().view(np.uint16) if spec.q_dtype == "bf16" else q.cpu().numpy()
+        lg = logits[o0:o1].cpu().numpy()
+        t0 = time.perf_counter()
+        O.tree_verify_attention(qh, lay, np.array([0, T]), np.array([P]), [spec.parents[b]], 1 / math.sqrt(spec.D),
+                                spec.q_dtype, spec.kv_dtype)
+        t_attn += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        am = O.vocab_argmax(lg)
+        path, _ = O.tree_accept_walk(spec.parents[b], spec.tokens[b], am)
+        t_walk += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        O.gather_layer(lay, [O.rollback_selection(P, path)])
+        t_gather += time.perf_counter() - t0
+        del lay
     scale = spec.Hkv / heads
-    per_seq = spec.L * scale * (t_attn + t_gather) + t_walk
-    round_s = per_seq * spec.B
+    sampled = t_attn + t_walk + t_gather
+    round_s = (spec.L * scale * (t_attn + t_gather) + t_walk) * spec.B / seqs
     nodes = spec.n_nodes
     return {
         "value": nodes / round_s,
         "unit": "nodes/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"float64 NumPy oracle on layer 0, sequence 0, KV heads 0..{heads - 1} ({heads * G} query heads, "
-                   f"{T} nodes, prefix {P}), plus that sequence's argmax/walk and a one-layer rollback gather of "
-                   f"the same heads; {t_attn + t_walk + t_gather:.1f} s measured, scaled x{spec.L * scale * spec.B:.0f}"
-                   f" to the full round"),
-        "sample_seconds": round(t_attn + t_walk + t_gather, 2),
+        "sample": (f"float64 NumPy oracle on layer 0 of sequences 0..{seqs - 1}, KV heads 0..{heads - 1} of each "
+                   f"({heads * G} query heads, prefix {int(spec.hist_len[:seqs].min())}..{int(spec.hist_len[:seqs].max())}), "
+                   f"plus each sequence's argmax/walk and a one-layer rollback gather of the same heads; "
+                   f"{sampled:.1f} s measured, attention and gather scaled x{spec.L * scale * spec.B / seqs:.0f} "
+                   f"and argmax/walk x{spec.B / seqs:.0f} to the full round"),
+        "sample_seconds": round(sampled, 2),
     }
 
 
@@ -359,7 +364,7 @@ def main():
     cpu = None
     if not args.no_cpu:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(spec, caches, qs, logits, args.cpu_heads)
+        cpu = cpu_baseline(spec, caches, qs, logits, min(args.cpu_heads, spec.Hkv), min(args.cpu_seqs, B))
 
     res = {
         "metric": "verified tree nodes/sec + achieved HBM GB/s (verify attn, KV gather) on 1 MI355X",

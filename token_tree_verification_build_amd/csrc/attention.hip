@@ -215,6 +215,18 @@ __device__ __forceinline__ uint32_t f16pair_from_bytes(uint32_t sel_src, uint32_
   const f16x2 off = {static_cast<_Float16>(-1152.0f), static_cast<_Float16>(-1152.0f)};
   return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(kExp64, sel_src, sel)) + off);
 }
+// The same bytes as fp16 of c + 1152, exactly, in one v_perm per pair: the
+// MFMA paths that can take the constant offset back out of their results
+// (a start value of the accumulator, a row sum) skip the packed add.
+constexpr float kCodeBias = 1152.0f;
+__device__ __forceinline__ f16x8 i8x8_to_f16_biased(uint32_t lo, uint32_t hi) {
+  u32x4 r;
+  r[0] = __builtin_amdgcn_perm(kExp64, lo, 0x04010400u);
+  r[1] = __builtin_amdgcn_perm(kExp64, lo, 0x04030402u);
+  r[2] = __builtin_amdgcn_perm(kExp64, hi, 0x04010400u);
+  r[3] = __builtin_amdgcn_perm(kExp64, hi, 0x04030402u);
+  return __builtin_bit_cast(f16x8, r);
+}
 // 8 int8 codes (two dwords, already xor-ed with 0x80808080) -> 8 fp16
 __device__ __forceinline__ f16x8 i8x8_to_f16(uint32_t lo, uint32_t hi) {
   u32x4 r;
@@ -264,17 +276,20 @@ __device__ __forceinline__ uint32_t lds_u32(const void* lds) {
   return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(lds))));
 }
-// scalar base (wave-uniform) + 32-bit per-lane byte offset
-__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, const void* lds) {
-  __asm__ volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
-                   "s"(lds_u32(lds))
+// scalar base (wave-uniform) + 32-bit per-lane byte offset; lds: LDS byte
+// address (wave-uniform)
+__device__ __forceinline__ void dma16_at(const void* sbase, uint32_t voff, uint32_t lds) {
+  __asm__ volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
                    : "memory");
 }
 // per-lane 64-bit address
-__device__ __forceinline__ void dma16v(const void* g, const void* lds) {
-  __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_u32(lds))
-                   : "memory");
+__device__ __forceinline__ void dma16v_at(const void* g, uint32_t lds) {
+  __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory");
 }
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, const void* lds) {
+  dma16_at(sbase, voff, lds_u32(lds));
+}
+__device__ __forceinline__ void dma16v(const void* g, const void* lds) { dma16v_at(g, lds_u32(lds)); }
 
 // A workgroup is NP = 4 wave pairs: the pairs take 4 consecutive key splits
 // of one unit, and the two waves of a pair split the unit's row chunk (RB0
@@ -779,10 +794,18 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
 // belong to both waves of a pair. The score wave (h = 0) stages the K tiles
 // and both scale sidecars, forms S = K Q^T, the fp16 probabilities of tile t,
 // their row sums and the v-scaled P' = P * v_scale, and hands P' to the value
-// wave (h = 1) through a double-buffered LDS block; the value wave stages the
-// V tiles and accumulates O += P' V for tile t - 1 in the same step. So every K and V byte is converted
-// once, the two waves share one SIMD (2 waves per SIMD, 256 registers each),
-// and one workgroup barrier per step orders the hand-over.
+// wave (h = 1) through a double-buffered LDS block; the value wave
+// accumulates O += P' V for tile t - 1 in the same step and issues every
+// staging load of the pair (K tile t + 2 with its scales, V tile t + 1), so
+// the score wave never waits on memory counters. Every K and V byte is
+// converted once, the two waves share one SIMD (2 waves per SIMD, 256
+// registers each), and one workgroup barrier per step orders the hand-over.
+//
+// Codes enter the matrix cores as fp16 of c + 1152 (one v_perm per pair).
+// The offset leaves S through the accumulators' start value, -1152 sum_d q_d
+// per row, and leaves O through the row sums of P' (a matrix-core product
+// with a ones operand, as are the row sums of P): O -= 1152 sum_j P'_j.
+constexpr int kMaxAttempts = 8;  // passes over a split, at most (inputs with infinite scores stop there)
 template <int RB>
 __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) {
   constexpr int NP = 4;                      // wave pairs = consecutive key splits of one unit
@@ -795,7 +818,7 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
   constexpr int NK = KBYTES / 1024;          // DMA instructions per K (or V) tile
   constexpr int KSLOT = KBYTES + 128;        // K codes + 32 k-scales + 32 v-scales (fp16)
   constexpr int VSLOT = KBYTES;              // V codes
-  constexpr int SK = 3, SV = 4;              // K ring and V ring stages (V is used one step later)
+  constexpr int SK = 3, SV = 3;              // K ring and V ring stages
   constexpr int NDK = NK + 1, NDV = NK;      // DMA instructions per staged tile, always all issued
   __shared__ __attribute__((aligned(16))) char kring_all[NP][SK][KSLOT];
   __shared__ __attribute__((aligned(16))) char vring_all[NP][SV][VSLOT];
@@ -804,6 +827,7 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
   __shared__ float mref_s[NP][RB * 16];  // the score wave's references and row sums, for the fold
   __shared__ float lref_s[NP][RB * 16];
   __shared__ int s_nt[NP];
+  __shared__ int s_bad[NP];  // the value wave's row sums of P' overflowed in this pass
 
   const int wgi = xcd_slot(blockIdx.x, p.nwg / NP);
   if (wgi < 0) return;  // whole workgroup
@@ -820,14 +844,18 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
     tbits_s[r] = r < w.nrows ? row_bits(p, w, w.row0 + r) : 1ull;
 
   const size_t head = (size_t)w.b * p.Hkv + w.kvh;
-  const char* cbase = static_cast<const char*>(h == 0 ? p.k : p.v) + head * p.cap * RBYTES;  // this wave's codes
-  // score wave, lanes 0-3: k-scales of keys t0 + 8 lane .. +8; lanes 4-7: v-scales
+  const char* kbase = static_cast<const char*>(p.k) + head * p.cap * RBYTES;
+  const char* vbase = static_cast<const char*>(p.v) + head * p.cap * RBYTES;
+  // value wave, lanes 0-3: k-scales of keys t0 + 8 lane .. +8; lanes 4-7: v-scales
   const uint16_t* sbase = (lane < 4 ? p.ks : p.vs) + head * p.cap;
+  const uint32_t kring_lds = lds_u32(kring_all[pair][0]);
+  const uint32_t vring_lds = lds_u32(vring_all[pair][0]);
   u32x4(*pbuf)[RB * 64] = pbuf_all[pair];
   // the fold of the four pairs' (m, l, o) reuses the K rings' space
   f32x4* mo = reinterpret_cast<f32x4*>(&kring_all[0][0][0]);  // [RB][8][64] lane-major o blocks
   float* mml = reinterpret_cast<float*>(mo + RB * 8 * 64);      // [RB * 16][2] (m, l)
   static_assert(RB * 32 * 64 * 4 + RB * 16 * 8 <= NP * SK * KSLOT, "fold area");
+  const f16x8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
 
   // Per-lane DMA geometry: piece j of a tile is tile row (64 j + lane) / CH,
   // 16-byte chunk (64 j + lane) % CH of that row (swizzled).
@@ -855,28 +883,47 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
       mode = 2;
     }
   };
-  // This wave's tile t (codes, + scales for the score wave) into its ring
-  // slot: exactly NDK or NDV DMA instructions. Boundary tiles clamp every row
-  // into [t0, limit); a scale group reaching past cap is clamped to start at
-  // cap - 8 (cap >= 32).
-  auto slot_of = [&](int t) -> char* {
-    return h == 0 ? kring_all[pair][t % SK] : vring_all[pair][t % SV];
-  };
-  auto issue = [&](int t) {
+  // Staging loads, issued by the value wave: K tile t (codes + both scale
+  // groups: NDK instructions) or V tile t (NDV) into its ring slot. Boundary
+  // tiles clamp every row into [t0, limit); a scale group reaching past cap is
+  // clamped to start at cap - 8 (cap >= 32).
+  auto issue_codes = [&](const char* base, int t, uint32_t dst) {
     int t0, mode, limit;
     geom(t, t0, mode, limit);
-    char* dst = slot_of(t);
-    const char* src = cbase + (size_t)t0 * RBYTES;
+    const char* src = base + (size_t)t0 * RBYTES;
     if (mode == 0) {
 #pragma unroll
-      for (int j = 0; j < NK; ++j) dma16(src, koff[j], dst + 1024 * j);
+      for (int j = 0; j < NK; ++j) dma16_at(src, koff[j], dst + 1024 * j);
     } else {
       const int lim = limit - 1 - t0;
 #pragma unroll
       for (int j = 0; j < NK; ++j)
-        dma16(src, static_cast<uint32_t>(min(piece_row(j), lim) * RBYTES) + piece_col(j), dst + 1024 * j);
+        dma16_at(src, static_cast<uint32_t>(min(piece_row(j), lim) * RBYTES) + piece_col(j), dst + 1024 * j);
     }
-    if (h == 0 && lane < 8) dma16v(sbase + min(t0 + 8 * (lane & 3), p.cap - 8), dst + KBYTES);
+    return t0;
+  };
+  auto issue_k = [&](int t) {
+    const uint32_t dst = kring_lds + static_cast<uint32_t>((t % SK) * KSLOT);
+    const int t0 = issue_codes(kbase, t, dst);
+    if (lane < 8) dma16v_at(sbase + min(t0 + 8 * (lane & 3), p.cap - 8), dst + KBYTES);
+  };
+  auto issue_v = [&](int t) { issue_codes(vbase, t, vring_lds + static_cast<uint32_t>((t % SV) * VSLOT)); };
+  // Issue order: K 0; K 1, V 0; then at step s: K s + 2, V s + 1. Before
+  // barrier s the value wave needs K s and V s - 1 (issued together a step
+  // earlier), so only the loads of step s - 1 may still be in flight.
+  auto stage_head = [&]() {
+    if (0 < ntile) issue_k(0);
+    if (1 < ntile) issue_k(1);
+    if (0 < ntile) issue_v(0);
+  };
+  auto wait_step = [&](int s) {
+    if (s + 1 < ntile) wait_vmcnt<NDK + NDV>();
+    else if (s < ntile) wait_vmcnt<NDV>();
+    else wait_vmcnt<0>();
+  };
+  auto stage_step = [&](int s) {
+    if (s + 2 < ntile) issue_k(s + 2);
+    if (s + 1 < ntile) issue_v(s + 1);
   };
   // the lane group's 8 scales (keys 8g + e of tile t), as fp16 pairs; off 0:
   // k-scales, 64: v-scales
@@ -890,27 +937,30 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
     return r;
   };
 
-  // the score wave stages K tiles 0 .. SK-2, the value wave V tiles 0 .. SV-3
-  // (V tile t is used one step after K tile t)
-  for (int t = 0; t < (h == 0 ? SK - 1 : SV - 2); ++t)
-    if (t < ntile) issue(t);
+  if (h == 1) {
+    stage_head();
+    wait_step(0);  // K tile 0 has landed: the score wave sets its references from it
+  }
   if (lane == 0 && h == 0) s_nt[pair] = ntile;
   __syncthreads();
   int nt_wg = 0;
 #pragma unroll
   for (int q = 0; q < NP; ++q) nt_wg = max(nt_wg, s_nt[q]);
 
-  // References without rescaling (see the lazy bound below): set from the
-  // scores of the split's first tile (row max + kMargin), only tracked inside
-  // the loop; if a row broke the bound the pass runs again from zero with
-  // raised references. Every row's first-tile max is finite: a row sees every
-  // key of a prefix tile and, in a block tile, the root.
+  // References without rescaling: set from the scores of the split's first
+  // tile (row max + kMargin) and fixed for the pass. If a probability (or its
+  // v-scaled copy) overflowed fp16, its row sum is not finite and the split
+  // runs again from zero, tracking how far the scores went past the
+  // references, and then again with references raised past them. Every row's
+  // first-tile max is finite: a row sees every key of a prefix tile and, in a
+  // block tile, the root.
   constexpr float kMargin = 2.0f;
   if (h == 0) {
     // ------------------------------------------------------ score wave ----
     // Q^T fragments in registers: d = 32g + 8ks + e (fp16; a lane's 32 codes
     // of a K row are contiguous)
     f16x8 qf[RB][4];
+    f32x4 kinit[RB];  // -1152 sum_d q_d of the lane's row: the S accumulators' start
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int rloc = rb * 16 + li;
@@ -919,27 +969,31 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
       const int node = w.o0 + row / p.G;
       const int qh = w.kvh * p.G + row % p.G;
       const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + ((size_t)node * p.Hq + qh) * D;
+      float qsum = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         u32x4 x = *reinterpret_cast<const u32x4*>(qrow + 32 * lg + 8 * ks);
         if (!ok) x = u32x4{0, 0, 0, 0};
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
+        for (int e = 0; e < 8; ++e) {
           qf[rb][ks][e] =
               static_cast<_Float16>(__uint_as_float((e & 1) ? (x[e >> 1] & 0xFFFF0000u) : (x[e >> 1] << 16)));
+          qsum += static_cast<float>(qf[rb][ks][e]);
+        }
       }
+      qsum += __shfl_xor(qsum, 16);
+      qsum += __shfl_xor(qsum, 32);
+      const float c = -kCodeBias * qsum;
+      kinit[rb] = f32x4{c, c, c, c};
     }
-    float m[RB], negm[RB], tmax[RB], l[RB];
+    float negm[RB], tmax[RB], l[RB];  // negm: minus the references (0 for the first tile's raw scores)
     f32x4 sacc[2][RB];
     u32x4 vsc;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      m[rb] = -INFINITY;
-      negm[rb] = 0.f;
-    }
+    for (int rb = 0; rb < RB; ++rb) negm[rb] = 0.f;
     // scores of tile t: t = s * kss - m (in place of the scores), boundary
-    // masks, running per-row max of t
-    auto scores = [&](int t, auto masked) {
+    // masks; with tracking, the running per-row max of t
+    auto scores = [&](int t, auto masked, auto track) {
       int t0, mode, limit;
       geom(t, t0, mode, limit);
       const char* sl = kring_all[pair][t % SK];
@@ -964,16 +1018,14 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const u32x4& src = kraw[kb][ks >> 1];
-          kf[kb] = i8x8_to_f16(src[2 * (ks & 1)], src[2 * (ks & 1) + 1]);
+          kf[kb] = i8x8_to_f16_biased(src[2 * (ks & 1)], src[2 * (ks & 1) + 1]);
         }
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-            sacc[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[kb], qf[rb][ks], ks == 0 ? zero : sacc[kb][rb],
-                                                                  0, 0, 0);
-          }
+          for (int kb = 0; kb < 2; ++kb)
+            sacc[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[kb], qf[rb][ks],
+                                                                  ks == 0 ? kinit[rb] : sacc[kb][rb], 0, 0, 0);
       }
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
@@ -991,17 +1043,19 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
           }
         }
       }
+      if constexpr (decltype(track)::value) {
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          tmax[rb] = fmaxf(fmaxf(tmax[rb], sacc[kb][rb][0]), sacc[kb][rb][1]);
-          tmax[rb] = fmaxf(fmaxf(tmax[rb], sacc[kb][rb][2]), sacc[kb][rb][3]);
-        }
+          for (int kb = 0; kb < 2; ++kb) {
+            tmax[rb] = fmaxf(fmaxf(tmax[rb], sacc[kb][rb][0]), sacc[kb][rb][1]);
+            tmax[rb] = fmaxf(fmaxf(tmax[rb], sacc[kb][rb][2]), sacc[kb][rb][3]);
+          }
+      }
     };
-    // probabilities of the scored tile: p = 2^t in fp16 (t <= 6 while the
-    // references hold, so p <= 64 and p * v_scale fits fp16); the row sums of
-    // exactly these p; P' = P * v_scale into P buffer b
+    // probabilities of the scored tile: p = 2^t in fp16; the row sums of
+    // exactly these p (ones x P^T on the matrix cores: every lane gets its
+    // row's sum); P' = P * v_scale into P buffer b
     auto hand_over = [&](int b) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
@@ -1014,36 +1068,32 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
         pbuf[b][rb * 64 + lane] = __builtin_bit_cast(u32x4, pr * __builtin_bit_cast(f16x8, vsc));
       }
     };
-    auto raise_refs = [&](float margin) -> bool {  // from tmax; true if any row moved
-      bool moved = false;
+    // per row block, the furthest any row went past its reference (tracked
+    // passes); true if a row went past the bound
+    auto past_refs = [&](float (&mx)[RB]) -> bool {
+      bool past = false;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        float mx = fmaxf(tmax[rb], __shfl_xor(tmax[rb], 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        if (__ballot(mx > 6.0f) != 0) {
-          moved = true;
-          m[rb] = (m[rb] == -INFINITY ? 0.f : m[rb]) + mx + margin;
-          negm[rb] = -m[rb];
-        }
+        mx[rb] = fmaxf(tmax[rb], __shfl_xor(tmax[rb], 16));
+        mx[rb] = fmaxf(mx[rb], __shfl_xor(mx[rb], 32));
+        past |= __ballot(mx[rb] > 6.0f) != 0;
       }
-      return moved;
+      return past;
     };
 
     if (ntile > 0) {
-      wait_vmcnt_tiles<NDK>(min(SK - 2, ntile - 1));
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) tmax[rb] = -INFINITY;
-      scores(0, std::true_type{});  // with m = -inf (negm = 0): t is the score itself
+      scores(0, std::true_type{}, std::true_type{});  // with negm = 0: t is the score itself
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         float mx = fmaxf(tmax[rb], __shfl_xor(tmax[rb], 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        m[rb] = mx + kMargin;
-        negm[rb] = -m[rb];
+        negm[rb] = -(mx + kMargin);
       }
     }
     float margin = 2.0f * kMargin;
-    for (;;) {  // attempts
+    for (int attempt = 0;; ++attempt) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         tmax[rb] = -INFINITY;
@@ -1052,32 +1102,48 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
       // (the work of a step sits in the loop body unconditionally: a
       // conditional accumulation would stop the compiler from updating the
       // matrix-core accumulators in place)
-      // full prefix tiles need no masks and come first; a loop of their own
-      // keeps the mask code (and its register shuffles) off their path
-      auto step = [&](int t, auto masked) {
-        wait_vmcnt_tiles<NDK>(min(SK - 2, ntile - 1 - t));
+      auto step = [&](int t, auto masked, auto track) {
         __syncthreads();  // K tile t landed; P buffer t % 2 was read a step ago
-        if (t + SK - 1 < ntile) issue(t + SK - 1);
-        scores(t, masked);
+        scores(t, masked, track);
         hand_over(t & 1);
       };
+      if (attempt == 0) {
+        // full prefix tiles need no masks and come first; a loop of their
+        // own keeps the mask code (and its register shuffles) off their path
 #pragma nounroll
-      for (int t = 0; t < n_full; ++t) step(t, std::false_type{});
+        for (int t = 0; t < n_full; ++t) step(t, std::false_type{}, std::false_type{});
 #pragma nounroll
-      for (int t = n_full; t < ntile; ++t) step(t, std::true_type{});
-      for (int t = ntile; t <= nt_wg; ++t) __syncthreads();
-      const bool redo = __syncthreads_or(raise_refs(margin));
+        for (int t = n_full; t < ntile; ++t) step(t, std::true_type{}, std::false_type{});
+      } else {
+#pragma nounroll
+        for (int t = 0; t < ntile; ++t) step(t, std::true_type{}, std::true_type{});
+      }
+      for (int t = ntile; t <= nt_wg; ++t) __syncthreads();  // the value wave's last step, padding
+      bool bad = false;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) bad |= !__builtin_isfinite(l[rb]);
+      float mx[RB];
+      const bool past = attempt > 0 && past_refs(mx);
+      const bool redo = __syncthreads_or(bad || past) && attempt + 1 < kMaxAttempts;
       if (!redo) break;
-      margin += kMargin;  // a wider margin on every attempt
-      for (int u = 0; u < SK - 1; ++u)
-        if (u < ntile) issue(u);
+      if (attempt > 0) {
+        // raise the rows that went past the bound; an overflow with none of
+        // them came from P * v_scale: lower every row of this split
+        const bool lower_all = !past && (__ballot(bad) != 0 || s_bad[pair] != 0);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          if (__ballot(mx[rb] > 6.0f) != 0) negm[rb] -= mx[rb] + margin;
+          else if (lower_all) negm[rb] -= margin;
+        }
+      }
+      margin += kMargin;  // a wider margin on every pass
     }
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       l[rb] += __shfl_xor(l[rb], 16);
       l[rb] += __shfl_xor(l[rb], 32);
       if (lg == 0) {
-        mref_s[pair][rb * 16 + li] = m[rb];
+        mref_s[pair][rb * 16 + li] = ntile > 0 ? -negm[rb] : -INFINITY;  // -inf: an empty split
         lref_s[pair][rb * 16 + li] = l[rb];
       }
     }
@@ -1085,7 +1151,7 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
     for (int step = 0; step < NP; ++step) __syncthreads();  // the value waves fold
   } else {
     // ------------------------------------------------------ value wave ----
-    f32x4 o[8][RB];
+    f32x4 o[8][RB], osum[RB];
     // O^T += V^T P'^T for tile t from P buffer b: lane (i, g) reads V rows
     // 8g + e, d = 8i .. 8i+7
     auto accumulate = [&](int t, int b) {
@@ -1099,11 +1165,12 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
         a[e][0] = v2[0] ^ 0x80808080u;
         a[e][1] = v2[1] ^ 0x80808080u;
       }
-      // V^T fragments of the 8 d-blocks: d-block db = 4hh + j takes byte j of
-      // dword hh of keys e = 0..7
-      u32x4 vf[8];
+      // V^T fragments (codes + 1152) of d-blocks 4hh .. 4hh + 3, half at a
+      // time (register budget: o holds 32 RB): d-block db = 4hh + j takes
+      // byte j of dword hh of keys e = 0..7
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
+        u32x4 vf[4];
         uint32_t ilo[4], ihi[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -1114,38 +1181,52 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
         for (int j = 0; j < 4; ++j)
 #pragma unroll
           for (int k = 0; k < 4; ++k)
-            vf[4 * hh + j][k] = f16pair_from_bytes(j < 2 ? ilo[k] : ihi[k], (j & 1) ? 0x04030402u : 0x04010400u);
-      }
-      // one row block's P'^T fragment at a time (register budget: o holds 32 RB)
+            vf[j][k] = __builtin_amdgcn_perm(kExp64, j < 2 ? ilo[k] : ihi[k], (j & 1) ? 0x04030402u : 0x04010400u);
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const f16x8 pw = __builtin_bit_cast(f16x8, pbuf[b][rb * 64 + lane]);
+        for (int rb = 0; rb < RB; ++rb) {
+          const f16x8 pw = __builtin_bit_cast(f16x8, pbuf[b][rb * 64 + lane]);
+          if (hh == 0) osum[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pw, osum[rb], 0, 0, 0);
 #pragma unroll
-        for (int db = 0; db < 8; ++db)
-          o[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, vf[db]), pw, o[db][rb], 0, 0, 0);
+          for (int j = 0; j < 4; ++j)
+            o[4 * hh + j][rb] =
+                __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, vf[j]), pw, o[4 * hh + j][rb], 0, 0, 0);
+        }
       }
     };
-    for (;;) {  // attempts, in step with the score wave
+    for (int attempt = 0;; ++attempt) {  // passes, in step with the score wave
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
+      for (int rb = 0; rb < RB; ++rb) {
+        osum[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int db = 0; db < 8; ++db) o[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      __syncthreads();  // step 0
-      if (SV - 2 < ntile) issue(SV - 2);
-#pragma nounroll
-      for (int t = 1; t <= ntile; ++t) {
-        // V tile t - 1 has landed: at most the tiles issued after it remain
-        wait_vmcnt_tiles<NDV>(min(SV - 2, ntile - t));
-        __syncthreads();  // P of tile t - 1 is in buffer (t - 1) % 2
-        if (t + SV - 2 < ntile) issue(t + SV - 2);
-        accumulate(t - 1, (t - 1) & 1);
       }
-      for (int t = ntile + 1; t <= nt_wg; ++t) __syncthreads();
-      const bool redo = __syncthreads_or(false);
+      if (attempt > 0) stage_head();
+      wait_step(0);
+      __syncthreads();  // step 0: K tile 0 has landed
+      stage_step(0);
+#pragma nounroll
+      for (int s = 1; s <= ntile; ++s) {
+        wait_step(s);  // K tile s and V tile s - 1 have landed
+        __syncthreads();  // P of tile s - 1 is in buffer (s - 1) % 2
+        stage_step(s);
+        accumulate(s - 1, (s - 1) & 1);
+      }
+      for (int s = ntile + 1; s <= nt_wg; ++s) __syncthreads();
+      bool bad = false;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) bad |= !__builtin_isfinite(osum[rb][0]);
+      const bool bad_w = __ballot(bad) != 0;
+      if (lane == 0) s_bad[pair] = bad_w ? 1 : 0;
+      const bool redo = __syncthreads_or(bad) && attempt + 1 < kMaxAttempts;
       if (!redo) break;
-      for (int u = 0; u < SV - 2; ++u)
-        if (u < ntile) issue(u);
     }
+    // take the code offset back out of O
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[db][rb][j] = fmaf(-kCodeBias, osum[rb][j], o[db][rb][j]);
     __syncthreads();  // references and row sums visible, rings idle
     // the four pairs (four consecutive splits) fold their (m, l, o) into one,
     // one pair at a time
