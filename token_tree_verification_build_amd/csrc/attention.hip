@@ -133,14 +133,15 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// Merge of n partials of one unit by log-sum-exp, by the whole workgroup.
-// Partials: o [slot][rows_chunk][D] and (m, l) [slot][rows_chunk][2] for
-// slots slot0 .. slot0 + n - 1 (m = -inf marks an empty split). wt is LDS
-// scratch for rows_chunk * n weights: per row, w_s = 2^(m_s - M) / L with
-// M = max m_s and L = sum 2^(m_s - M) l_s; then out = sum_s w_s o_s.
-__device__ void merge_partials(const AttnParams& p, const Work& w, int slot0, int n, float* wt) {
+// Merge of n partials of one unit by log-sum-exp, by the whole workgroup,
+// over rows [r0, r1) of the unit's chunk. Partials: o [slot][rows_chunk][D]
+// and (m, l) [slot][rows_chunk][2] for slots slot0 .. slot0 + n - 1 (m = -inf
+// marks an empty split). wt is LDS scratch for rows_chunk * n weights: per
+// row, w_s = 2^(m_s - M) / L with M = max m_s and L = sum 2^(m_s - M) l_s;
+// then out = sum_s w_s o_s.
+__device__ void merge_partials(const AttnParams& p, const Work& w, int slot0, int n, float* wt, int r0, int r1) {
   const int tid = threadIdx.x, nthr = blockDim.x;
-  for (int r = tid; r < w.nrows; r += nthr) {
+  for (int r = r0 + tid; r < r1; r += nthr) {
     float M = -INFINITY;
     for (int s = 0; s < n; ++s) M = fmaxf(M, p.part_ml[((size_t)(slot0 + s) * p.rows_chunk + r) * 2]);
     float L = 0.f;
@@ -156,8 +157,8 @@ __device__ void merge_partials(const AttnParams& p, const Work& w, int slot0, in
   }
   __syncthreads();
   const int D4 = p.D / 4;
-  for (int idx = tid; idx < w.nrows * D4; idx += nthr) {
-    const int r = idx / D4, d4 = idx - r * D4;
+  for (int idx = tid; idx < (r1 - r0) * D4; idx += nthr) {
+    const int r = r0 + idx / D4, d4 = idx % D4;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < n; ++s)
       acc += wt[r * n + s] *
@@ -169,12 +170,13 @@ __device__ void merge_partials(const AttnParams& p, const Work& w, int slot0, in
   }
 }
 
-// Second launch: one workgroup per unit whose keys were split over more than
-// one partial merges them (a kernel boundary orders the partials' stores
+// Second launch: one workgroup per (unit, block of kMergeRows rows) of the
+// units whose keys were split over more than one partial merges them (a kernel boundary orders the partials' stores
 // before these loads; an in-kernel device-scope fence would write back whole
 // L2 caches). per_slot: key splits per stored partial (4 for the MFMA path,
 // whose workgroups fold their 4 splits first; 1 for the VALU path).
-constexpr int kMergeWt = 2048;  // rows_chunk * partials per unit, at most
+constexpr int kMergeWt = 2048;   // rows_chunk * partials per unit, at most
+constexpr int kMergeRows = 16;   // rows per merge workgroup (grid y)
 __global__ void __launch_bounds__(256) merge_kernel(const AttnParams p, int per_slot) {
   __shared__ float wt[kMergeWt];
   const int u = blockIdx.x;
@@ -199,7 +201,9 @@ __global__ void __launch_bounds__(256) merge_kernel(const AttnParams p, int per_
   w.rc = rem % w.rc_n;
   w.row0 = w.rc * p.rows_chunk;
   w.nrows = min(p.rows_chunk, w.rows - w.row0);
-  merge_partials(p, w, (p.wg_off[lo] + rem * w.nsplit) / per_slot, n, wt);
+  const int r0 = blockIdx.y * kMergeRows;
+  if (r0 >= w.nrows) return;
+  merge_partials(p, w, (p.wg_off[lo] + rem * w.nsplit) / per_slot, n, wt, r0, min(w.nrows, r0 + kMergeRows));
 }
 
 // ------------------------------------------------------------- MFMA path ----
@@ -791,20 +795,20 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
 
 // int8 KV, MFMA path, by phase. A workgroup is NP = 4 wave pairs taking 4
 // consecutive key splits of one unit; all RB row blocks of the unit's chunk
-// belong to both waves of a pair. The score wave (h = 0) stages the K tiles
-// and both scale sidecars, forms S = K Q^T, the fp16 probabilities of tile t,
-// their row sums and the v-scaled P' = P * v_scale, and hands P' to the value
-// wave (h = 1) through a double-buffered LDS block; the value wave
-// accumulates O += P' V for tile t - 1 in the same step and issues every
-// staging load of the pair (K tile t + 2 with its scales, V tile t + 1), so
-// the score wave never waits on memory counters. Every K and V byte is
-// converted once, the two waves share one SIMD (2 waves per SIMD, 256
-// registers each), and one workgroup barrier per step orders the hand-over.
+// belong to both waves of a pair. The score wave (h = 0) forms S = K Q^T,
+// the fp16 probabilities of tile t, their row sums and the v-scaled
+// P' = P * v_scale, and hands P' to the value wave (h = 1) through a
+// double-buffered LDS block; the value wave accumulates O += P' V for tile
+// t - 1 in the same step and issues every staging load of the pair (K tile
+// t + 2 with both scale groups, V tile t + 2), so the score wave never waits
+// on memory counters. Every K and V byte is converted once, the two waves
+// share one SIMD (2 waves per SIMD, 256 registers each), and one workgroup
+// barrier per step orders the hand-over.
 //
 // Codes enter the matrix cores as fp16 of c + 1152 (one v_perm per pair).
 // The offset leaves S through the accumulators' start value, -1152 sum_d q_d
 // per row, and leaves O through the row sums of P' (a matrix-core product
-// with a ones operand, as are the row sums of P): O -= 1152 sum_j P'_j.
+// with a ones operand): O -= 1152 sum_j P'_j.
 constexpr int kMaxAttempts = 8;  // passes over a split, at most (inputs with infinite scores stop there)
 template <int RB>
 __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) {
@@ -818,7 +822,7 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
   constexpr int NK = KBYTES / 1024;          // DMA instructions per K (or V) tile
   constexpr int KSLOT = KBYTES + 128;        // K codes + 32 k-scales + 32 v-scales (fp16)
   constexpr int VSLOT = KBYTES;              // V codes
-  constexpr int SK = 3, SV = 3;              // K ring and V ring stages
+  constexpr int SK = 3, SV = 4;              // K ring and V ring stages (V is used a step after K)
   constexpr int NDK = NK + 1, NDV = NK;      // DMA instructions per staged tile, always all issued
   __shared__ __attribute__((aligned(16))) char kring_all[NP][SK][KSLOT];
   __shared__ __attribute__((aligned(16))) char vring_all[NP][SV][VSLOT];
@@ -908,22 +912,27 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
     if (lane < 8) dma16v_at(sbase + min(t0 + 8 * (lane & 3), p.cap - 8), dst + KBYTES);
   };
   auto issue_v = [&](int t) { issue_codes(vbase, t, vring_lds + static_cast<uint32_t>((t % SV) * VSLOT)); };
-  // Issue order: K 0; K 1, V 0; then at step s: K s + 2, V s + 1. Before
-  // barrier s the value wave needs K s and V s - 1 (issued together a step
-  // earlier), so only the loads of step s - 1 may still be in flight.
+  // Issue order: K 0, V 0; K 1, V 1; then at step s: K s + 2, V s + 2.
+  // Before barrier s the value wave needs K s (issued at step s - 2) and
+  // V s - 1 (a step earlier still), so only the loads of step s - 1 may
+  // still be in flight.
   auto stage_head = [&]() {
-    if (0 < ntile) issue_k(0);
-    if (1 < ntile) issue_k(1);
-    if (0 < ntile) issue_v(0);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      if (t < ntile) {
+        issue_k(t);
+        issue_v(t);
+      }
   };
   auto wait_step = [&](int s) {
     if (s + 1 < ntile) wait_vmcnt<NDK + NDV>();
-    else if (s < ntile) wait_vmcnt<NDV>();
     else wait_vmcnt<0>();
   };
   auto stage_step = [&](int s) {
-    if (s + 2 < ntile) issue_k(s + 2);
-    if (s + 1 < ntile) issue_v(s + 1);
+    if (s + 2 < ntile) {
+      issue_k(s + 2);
+      issue_v(s + 2);
+    }
   };
   // the lane group's 8 scales (keys 8g + e of tile t), as fp16 pairs; off 0:
   // k-scales, 64: v-scales
@@ -1631,6 +1640,8 @@ extern "C" ttv_status tree_verify_attention(const ttv_batch* batch, const void* 
   }
   s = check_launch("tree_verify_attention");
   if (s != TTV_OK || !pl.merge) return s;
-  hipLaunchKernelGGL(merge_kernel, dim3(static_cast<unsigned>(pl.nunits)), dim3(256), 0, st, p, pl.mfma ? 4 : 1);
+  hipLaunchKernelGGL(merge_kernel,
+                     dim3(static_cast<unsigned>(pl.nunits), static_cast<unsigned>((p.rows_chunk + kMergeRows - 1) / kMergeRows)),
+                     dim3(128), 0, st, p, pl.mfma ? 4 : 1);
   return check_launch("tree_verify_attention merge");
 }
