@@ -351,6 +351,27 @@ def main():
         print(f"[bench] full-window take {take_ms:.3f} ms ({kernels['kv_gather_positions_take']['GBps']} GB/s)",
               file=sys.stderr, flush=True)
         del dst_caches, dst_layers
+        # the practically reachable ceiling for a read+write stream: a plain
+        # device copy of 4 GiB (torch's copy kernel), bytes read + written
+        a = torch.empty(4 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        b2 = torch.empty_like(a)
+        b2.copy_(a)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(5):
+            b2.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        copy_ms = e0.elapsed_time(e1) / 5
+        kernels["plain_copy_4GiB"] = {
+            "avg_us": round(copy_ms * 1e3, 1), "bytes": 2 * (4 << 30),
+            "GBps": round(2 * (4 << 30) / (copy_ms / 1e3) / 1e9, 1),
+            "frac_hbm": round(2 * (4 << 30) / (copy_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "what": "device-to-device copy of 4 GiB (read + write bytes): the reachable ceiling for the take",
+        }
+        print(f"[bench] plain copy {kernels['plain_copy_4GiB']['GBps']} GB/s", file=sys.stderr, flush=True)
+        del a, b2
     assert int(st.item()) == 0, "device status"
 
     if args.copy_calib_mib > 0:

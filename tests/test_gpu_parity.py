@@ -604,3 +604,42 @@ def test_long_context_full_size_sampled(ttv):
     log(f"full-size sampled rows: max|err| {worst:.3e}")
     assert worst <= TOL_BF16
     assert np.isfinite(to_host(out)).all()
+
+
+def test_ragged_batch_full_size_sampled(ttv):
+    """The batched ragged workload at full size (B=32, bf16, prefixes up to
+    32,768, trees of 8-64 nodes, so up to 320 rows per KV head) in the bench's
+    launch configuration: sampled output rows checked one by one against the
+    oracle."""
+    from workloads.device import dev_kv_cache, dev_queries
+    spec = config4_round()
+    T_b = np.diff(spec.node_off)
+    cap = int(max(spec.hist_len + T_b))
+    c = dev_kv_cache(spec.seed, 100, spec.B, spec.Hkv, cap, spec.D, "bf16", "cuda")
+    layer = ttv.KVLayer(c["k"], c["v"])
+    q = dev_queries(spec.seed, 200, spec.n_nodes, spec.Hq, spec.D, "bf16", "cuda")
+    batch = spec_batch(ttv, spec)
+    anc, _, st = run_mask(ttv, batch, to_dev(spec.flat("parents")))
+    out, _ = run_attention(ttv, batch, q, layer, anc, 1 / math.sqrt(spec.D))
+    torch.cuda.synchronize()
+    r = rng_for(1320)
+    worst = 0.0
+    big = [b for b in range(spec.B) if T_b[b] * spec.G > 96]  # sequences with more than one row chunk
+    for i in range(8):
+        b = int(big[int(r.integers(0, len(big)))]) if i % 2 == 0 else int(r.integers(0, spec.B))
+        T = int(T_b[b])
+        t = int(r.integers(0, T))
+        g = int(r.integers(0, spec.Hkv))
+        node = int(spec.node_off[b]) + t
+        P = int(spec.hist_len[b])
+        lay = {n: c[n][b:b + 1, g:g + 1, :P + T].view(torch.int16).cpu().numpy().view(np.uint16) for n in ("k", "v")}
+        qh = q[node:node + 1, g * spec.G:(g + 1) * spec.G].view(torch.int16).cpu().numpy().view(np.uint16)
+        qt = np.zeros((T, spec.G, spec.D), np.uint16)
+        qt[t] = qh[0]
+        want = O.tree_verify_attention(qt, lay, np.array([0, T]), np.array([P]), [spec.parents[b]],
+                                       1 / math.sqrt(spec.D), "bf16", "bf16")[t]
+        got = to_host(out[node, g * spec.G:(g + 1) * spec.G])
+        worst = max(worst, float(np.abs(got - want).max()))
+    log(f"ragged full-size sampled rows: max|err| {worst:.3e}")
+    assert worst <= TOL_BF16
+    assert np.isfinite(to_host(out)).all()

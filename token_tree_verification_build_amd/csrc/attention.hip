@@ -60,6 +60,8 @@ constexpr int kMfmaMaxRB = 6;   // row blocks of 16 per MFMA row chunk (96 rows,
 constexpr int kI8MaxRB = 5;     // int8: both waves of a pair hold all row blocks (80 rows)
 constexpr int kValuRows = 16;   // rows per VALU workgroup
 constexpr int kTargetWG = 1024;
+constexpr int kWideTargetWG = 1024;
+constexpr int kWideMaxRB = 5;  // bf16 wide layout: row blocks per chunk (LDS holds four chunks' Q)
 constexpr int kMaxSplits = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -74,11 +76,13 @@ struct AttnParams {
   float* part_o;
   float* part_ml;
   int B, Hq, Hkv, G, D, cap, split_len, rows_chunk, nwg, split_pad;
+  int rc_group;  // wide layout: row chunks per (kv head, split) group of slots (a multiple of 4), else 0
   float scale_log2;
   int32_t node_off[TTV_MAX_BATCH + 1];
   int32_t hist_len[TTV_MAX_BATCH];
   int32_t wg_off[TTV_MAX_BATCH + 1];
   int32_t unit_off[TTV_MAX_BATCH + 1];
+  int32_t rchunk[TTV_MAX_BATCH];  // rows per chunk of sequence b (<= rows_chunk, the partials' row stride)
 };
 
 struct Work {
@@ -97,18 +101,26 @@ __device__ __forceinline__ void decode(const AttnParams& p, int slot, Work& w) {
   w.T = p.node_off[lo + 1] - w.o0;
   w.P = p.hist_len[lo];
   w.rows = w.T * p.G;
-  w.rc_n = (w.rows + p.rows_chunk - 1) / p.rows_chunk;
+  const int rch = p.rchunk[lo];
+  w.rc_n = (w.rows + rch - 1) / rch;
   const int ns = w.P > 0 ? (w.P + p.split_len - 1) / p.split_len : 1;
   w.nsplit = (ns + p.split_pad - 1) / p.split_pad * p.split_pad;  // trailing splits may be empty
   int rem = slot - p.wg_off[lo];
-  w.split = rem % w.nsplit;
-  rem /= w.nsplit;
-  w.rc = rem % w.rc_n;
-  w.kvh = rem / w.rc_n;
+  if (p.rc_group > 0) {  // wide: the row chunks of one (kv head, split) are consecutive slots
+    w.rc = rem % p.rc_group;
+    rem /= p.rc_group;
+    w.split = rem % w.nsplit;
+    w.kvh = rem / w.nsplit;
+  } else {
+    w.split = rem % w.nsplit;
+    rem /= w.nsplit;
+    w.rc = rem % w.rc_n;
+    w.kvh = rem / w.rc_n;
+  }
   w.unit = p.unit_off[lo] + w.kvh * w.rc_n + w.rc;
   w.slot = slot;
-  w.row0 = w.rc * p.rows_chunk;
-  w.nrows = min(p.rows_chunk, w.rows - w.row0);
+  w.row0 = w.rc * rch;
+  w.nrows = max(0, min(rch, w.rows - w.row0));  // 0: a padding chunk of the wide layout
   w.k_lo = w.split * p.split_len;
   w.k_hi = min(w.P, w.k_lo + p.split_len);
   w.last = w.split == w.nsplit - 1;
@@ -135,18 +147,19 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 // Merge of n partials of one unit by log-sum-exp, by the whole workgroup,
 // over rows [r0, r1) of the unit's chunk. Partials: o [slot][rows_chunk][D]
-// and (m, l) [slot][rows_chunk][2] for slots slot0 .. slot0 + n - 1 (m = -inf
-// marks an empty split). wt is LDS scratch for rows_chunk * n weights: per
+// and (m, l) [slot][rows_chunk][2] for slots slot0 + s * stride, s < n
+// (m = -inf marks an empty split). wt is LDS scratch for rows_chunk * n weights: per
 // row, w_s = 2^(m_s - M) / L with M = max m_s and L = sum 2^(m_s - M) l_s;
 // then out = sum_s w_s o_s.
-__device__ void merge_partials(const AttnParams& p, const Work& w, int slot0, int n, float* wt, int r0, int r1) {
+__device__ void merge_partials(const AttnParams& p, const Work& w, int slot0, int n, float* wt, int r0, int r1,
+                               int stride) {
   const int tid = threadIdx.x, nthr = blockDim.x;
   for (int r = r0 + tid; r < r1; r += nthr) {
     float M = -INFINITY;
-    for (int s = 0; s < n; ++s) M = fmaxf(M, p.part_ml[((size_t)(slot0 + s) * p.rows_chunk + r) * 2]);
+    for (int s = 0; s < n; ++s) M = fmaxf(M, p.part_ml[((size_t)(slot0 + s * stride) * p.rows_chunk + r) * 2]);
     float L = 0.f;
     for (int s = 0; s < n; ++s) {
-      const size_t pr = (size_t)(slot0 + s) * p.rows_chunk + r;
+      const size_t pr = (size_t)(slot0 + s * stride) * p.rows_chunk + r;
       const float ms = p.part_ml[pr * 2];
       const float ws = ms == -INFINITY ? 0.f : exp2f(ms - M);
       wt[r * n + s] = ws;
@@ -162,7 +175,7 @@ __device__ void merge_partials(const AttnParams& p, const Work& w, int slot0, in
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < n; ++s)
       acc += wt[r * n + s] *
-             reinterpret_cast<const f32x4*>(p.part_o + ((size_t)(slot0 + s) * p.rows_chunk + r) * p.D)[d4];
+             reinterpret_cast<const f32x4*>(p.part_o + ((size_t)(slot0 + s * stride) * p.rows_chunk + r) * p.D)[d4];
     const int row = w.row0 + r;
     const int node = w.o0 + row / p.G;
     const int qh = w.kvh * p.G + row % p.G;
@@ -191,7 +204,8 @@ __global__ void __launch_bounds__(256) merge_kernel(const AttnParams p, int per_
   w.T = p.node_off[lo + 1] - w.o0;
   w.P = p.hist_len[lo];
   w.rows = w.T * p.G;
-  w.rc_n = (w.rows + p.rows_chunk - 1) / p.rows_chunk;
+  const int rch = p.rchunk[lo];
+  w.rc_n = (w.rows + rch - 1) / rch;
   const int ns = w.P > 0 ? (w.P + p.split_len - 1) / p.split_len : 1;
   w.nsplit = (ns + p.split_pad - 1) / p.split_pad * p.split_pad;
   const int n = w.nsplit / per_slot;
@@ -199,11 +213,15 @@ __global__ void __launch_bounds__(256) merge_kernel(const AttnParams p, int per_
   const int rem = u - p.unit_off[lo];
   w.kvh = rem / w.rc_n;
   w.rc = rem % w.rc_n;
-  w.row0 = w.rc * p.rows_chunk;
-  w.nrows = min(p.rows_chunk, w.rows - w.row0);
+  w.row0 = w.rc * rch;
+  w.nrows = min(rch, w.rows - w.row0);
   const int r0 = blockIdx.y * kMergeRows;
   if (r0 >= w.nrows) return;
-  merge_partials(p, w, (p.wg_off[lo] + rem * w.nsplit) / per_slot, n, wt, r0, min(w.nrows, r0 + kMergeRows));
+  if (p.rc_group > 0)  // wide: split s of this chunk is slot group (kvh, s), member rc
+    merge_partials(p, w, p.wg_off[lo] + w.kvh * w.nsplit * p.rc_group + w.rc, n, wt, r0,
+                   min(w.nrows, r0 + kMergeRows), p.rc_group);
+  else
+    merge_partials(p, w, (p.wg_off[lo] + rem * w.nsplit) / per_slot, n, wt, r0, min(w.nrows, r0 + kMergeRows), 1);
 }
 
 // ------------------------------------------------------------- MFMA path ----
@@ -299,9 +317,13 @@ __device__ __forceinline__ void dma16v(const void* g, const void* lds) { dma16v_
 // of one unit, and the two waves of a pair split the unit's row chunk (RB0
 // row blocks of 16 rows, then RB1) and share one LDS ring, each staging half
 // of every tile. 512 threads at 2 waves per SIMD: 256 registers per wave.
-template <bool I8, int RB0, int RB1, int S>
+// WIDE (bf16): the pairs take 4 row chunks of one (kv head, key split)
+// instead and all eight waves share one ring, each staging an eighth of every
+// tile, so a K/V byte is read once for up to 4 * 96 rows.
+template <bool I8, bool WIDE, int RB0, int RB1, int S>
 __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
-  constexpr int NP = 4;                       // wave pairs = consecutive key splits of one unit
+  static_assert(!(I8 && WIDE), "the wide layout is bf16 only");
+  constexpr int NP = 4;                       // wave pairs = consecutive key splits (WIDE: row chunks)
   constexpr int NW = 2 * NP;                  // waves
   constexpr int RBU = RB0 + RB1;              // row blocks of the unit's row chunk
   constexpr int D = 128;
@@ -312,14 +334,19 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
   constexpr int NK = KBYTES / 1024;           // DMA instructions per K (or V) tile
   constexpr int SC_OFF = 2 * KBYTES;          // int8: 32 k-scales then 32 v-scales
   constexpr int TILE = 2 * KBYTES + (I8 ? 128 : 0);
-  constexpr int NDK = NK + (I8 ? 1 : 0);      // DMA instructions per tile of the K half (h = 0)
-  constexpr int NDV = NK;                     // ... and of the V half (h = 1), always all issued
+  constexpr int NDK = WIDE ? NK / 4 : NK + (I8 ? 1 : 0);  // DMA instructions per tile of the K half (h = 0)
+  constexpr int NDV = WIDE ? NK / 4 : NK;     // ... and of the V half (h = 1), always all issued
+  constexpr int NR = WIDE ? 1 : NP;           // rings
+  constexpr int NQ = WIDE ? NP : 1;           // row chunks with their own Q fragments
   typedef typename std::conditional<I8, f16x8, bf16x8>::type qk_t;  // QK operand type
   // per pair: an S-stage ring of K/V tiles; per workgroup: the unit's Q^T
   // fragments (one conflict-free 16-byte read per use) and ancestor bitsets
-  __shared__ __attribute__((aligned(16))) char ring_all[NP][S][TILE];
-  __shared__ __attribute__((aligned(16))) u32x4 qsh[RBU * 4 * 64];
-  __shared__ uint64_t tbits_s[RBU * 16];
+  __shared__ __attribute__((aligned(16))) char ring_all[NR][S][TILE];
+  __shared__ __attribute__((aligned(16))) u32x4 qsh_all[NQ][RBU * 4 * 64];
+  __shared__ uint64_t tbits_all[NQ][RBU * 16];
+  // WIDE: V^T fragments of a tile as fp16, converted once for all waves
+  // (double-buffered: tile t is converted in step t and used in step t + 1)
+  __shared__ __attribute__((aligned(16))) u32x4 vT[WIDE ? 2 : 1][WIDE ? 8 * 64 : 1];
   __shared__ int s_nt[NP];
 
   const int wgi = xcd_slot(blockIdx.x, p.nwg / NP);
@@ -333,17 +360,19 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
   const int li = lane & 15;
   const int lg = lane >> 4;
   Work w;
-  decode(p, wgi * NP + pair, w);  // the pairs share (b, kv head, row chunk)
-  char (*ring)[TILE] = ring_all[pair];
+  decode(p, wgi * NP + pair, w);  // the pairs share (b, kv head, row chunk); WIDE: (b, kv head, split)
+  char (*ring)[TILE] = ring_all[WIDE ? 0 : pair];
+  u32x4* qsh = qsh_all[WIDE ? pair : 0];
+  uint64_t* tbits_s = tbits_all[WIDE ? pair : 0];
 
   // Q^T fragments into LDS. k-slot mapping of the QK product (shared by K and
   // Q): bf16 KV d = 32ks + 8g + e (bf16 operands); int8 KV d = 32g + 8ks + e
   // (fp16 operands, so a lane's 32 int8 codes are contiguous).
-  for (int f = wave; f < RBU * 4; f += NW) {
+  for (int f = WIDE ? h : wave; f < RBU * 4; f += WIDE ? 2 : NW) {  // WIDE: the pair loads its own chunk
     const int rb = f >> 2, ks = f & 3;
     const int rloc = rb * 16 + li;
     const bool ok = rloc < w.nrows;
-    const int row = w.row0 + (ok ? rloc : 0);
+    const int row = ok ? w.row0 + rloc : 0;  // a padding chunk (WIDE) reads row 0
     const int node = w.o0 + row / p.G;
     const int qh = w.kvh * p.G + row % p.G;
     const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + ((size_t)node * p.Hq + qh) * D;
@@ -360,8 +389,11 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
     qsh[f * 64 + lane] = x;
   }
   // ancestor bitsets of the unit's rows, needed by block tiles only
-  for (int r = threadIdx.x; r < RBU * 16; r += 64 * NW)
+  for (int r = WIDE ? h * 64 + lane : static_cast<int>(threadIdx.x); r < RBU * 16; r += WIDE ? 128 : 64 * NW)
     tbits_s[r] = r < w.nrows ? row_bits(p, w, w.row0 + r) : 1ull;
+  if constexpr (WIDE) {  // the "previous tile" of step 0 multiplies zeros
+    vT[1][threadIdx.x] = u32x4{0, 0, 0, 0};
+  }
   // every ordinary load has landed before the DMA ring starts, so the waits in
   // the loop count ring traffic only
   wait_vmcnt<0>();
@@ -380,9 +412,12 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
   auto piece_col = [&](int j) {
     return 16u * static_cast<uint32_t>(((64 * j + lane) % CH) ^ lds_swz<I8>(piece_row(j)));
   };
-  uint32_t koff[NK];
+  // WIDE: wave (h, pair) stages pieces NDK * pair .. of its half of each tile
+  constexpr int NKW = WIDE ? NK / 4 : NK;
+  const int j0 = WIDE ? NKW * pair : 0;
+  uint32_t koff[NKW];
 #pragma unroll
-  for (int j = 0; j < NK; ++j) koff[j] = static_cast<uint32_t>(piece_row(j) * RBYTES) + piece_col(j);
+  for (int j = 0; j < NKW; ++j) koff[j] = static_cast<uint32_t>(piece_row(j0 + j) * RBYTES) + piece_col(j0 + j);
   // int8 scales: lanes 0-3 stage k-scales of keys t0 + 8 lane .. +8, lanes 4-7
   // the v-scales
   const uint16_t* sc_lane = lane < 4 ? ksb : vsb;
@@ -417,12 +452,13 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
     const char* src = hbase + (size_t)t0 * RBYTES;
     if (mode == 0) {
 #pragma unroll
-      for (int j = 0; j < NK; ++j) dma16(src, koff[j], dst + 1024 * j);
+      for (int j = 0; j < NKW; ++j) dma16(src, koff[j], dst + 1024 * (j0 + j));
     } else {
       const int lim = limit - 1 - t0;
 #pragma unroll
-      for (int j = 0; j < NK; ++j)
-        dma16(src, static_cast<uint32_t>(min(piece_row(j), lim) * RBYTES) + piece_col(j), dst + 1024 * j);
+      for (int j = 0; j < NKW; ++j)
+        dma16(src, static_cast<uint32_t>(min(piece_row(j0 + j), lim) * RBYTES) + piece_col(j0 + j),
+              dst + 1024 * (j0 + j));
     }
     if constexpr (I8) {
       // a group reaching past cap is clamped to start at cap - 8 (cap >= 32)
@@ -450,19 +486,53 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
   int nt_wg = 0;
 #pragma unroll
   for (int q = 0; q < NP; ++q) nt_wg = max(nt_wg, s_nt[q]);
-  float* mo = reinterpret_cast<float*>(&ring_all[0][0][0]);  // [RBU][8][4][64] lane-major o
-  float* mml = mo + RBU * 32 * 64;                             // [RBU * 16][2] (m, l)
+  // the fold (WIDE: each pair's output in turn) goes through LDS: the rings,
+  // or for WIDE the Q fragments' space
+  float* mo = WIDE ? reinterpret_cast<float*>(&qsh_all[0][0]) : reinterpret_cast<float*>(&ring_all[0][0][0]);
+  float* mml = mo + RBU * 32 * 64;  // mo: [RBU][8][4][64] lane-major o; mml: [RBU * 16][2] (m, l)
+  static_assert(RBU * 32 * 64 * 4 + RBU * 16 * 8 <= (WIDE ? NQ * RBU * 4 * 64 * 16 : NR * S * TILE), "fold area");
+  // Row-major stores of rows [0, wq.nrows) of a chunk from mo / mml, four
+  // consecutive d per thread (coalesced): the unit's output if one partial
+  // covers it, else partial slot `slot`. LDS holds o in the MFMA lane order:
+  // row 16 rb + i, d = 32 g + 8 r + db at ((rb * 8 + db) * 4 + r) * 64 + 16 g + i.
+  auto store_out = [&](const Work& wq, int slot, bool whole) {
+    for (int flat = 4 * threadIdx.x; flat < wq.nrows * D; flat += 4 * 64 * NW) {
+      const int rloc = flat / D, d0 = flat % D;
+      const int rb = rloc >> 4, i = rloc & 15;
+      f32x4 v;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int d = d0 + u;
+        v[u] = mo[((rb * 8 + (d & 7)) * 4 + ((d >> 3) & 3)) * 64 + 16 * (d >> 5) + i];
+      }
+      if (whole) {
+        const int row = wq.row0 + rloc;
+        const int node = wq.o0 + row / p.G;
+        const int qh = wq.kvh * p.G + row % p.G;
+        *reinterpret_cast<f32x4*>(p.out + ((size_t)node * p.Hq + qh) * D + d0) = v / mml[rloc * 2 + 1];
+      } else {
+        *reinterpret_cast<f32x4*>(p.part_o + ((size_t)slot * p.rows_chunk + rloc) * D + d0) = v;
+      }
+    }
+    if (!whole) {
+      for (int r = threadIdx.x; r < wq.nrows; r += 64 * NW) {
+        p.part_ml[((size_t)slot * p.rows_chunk + r) * 2] = mml[r * 2];
+        p.part_ml[((size_t)slot * p.rows_chunk + r) * 2 + 1] = mml[r * 2 + 1];
+      }
+    }
+  };
   // Everything that depends on the wave's row blocks: RB of them from rb0 on.
   // Both halves run the same sequence of workgroup barriers.
   auto per_wave = [&](auto rb_count, const int rb0) {
     constexpr int RB = decltype(rb_count)::value;
+    constexpr int RBA = RB > 0 ? RB : 1;  // array extents (a wave without rows declares one unused block)
     // Accumulators. o: O^T blocks (unnormalised), touched by the matrix cores
     // only (a VALU rescale of o in the loop would make the register allocator
     // shuttle all of it between accumulation and vector registers every tile).
     // l: the lane's partial row sums of exactly the fp16 probabilities that
     // enter P V. m: the row's reference max (log2 units).
-    f32x4 o[8][RB];
-    float m[RB], l[RB];
+    f32x4 o[8][RBA];
+    float m[RBA], l[RBA];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) m[rb] = -INFINITY;
 
@@ -470,11 +540,11 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
     // t = s * kss - m (in place of the scores) with the boundary masks, and the
     // running per-row max of t. back(): turn t into fp16 probabilities, add
     // their row sums and P V into the accumulators.
-    f32x4 sacc[2][RB];
+    f32x4 sacc[2][RBA];
     u32x4 vsc = {0, 0, 0, 0};
     const char* sl = nullptr;
-    float negm[RB];  // -m, or 0 while m is -inf
-    float tmax[RB];  // the lane's largest t = s * kss - m of its row so far
+    float negm[RBA];  // -m, or 0 while m is -inf
+    float tmax[RBA];  // the lane's largest t = s * kss - m of its row so far
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) negm[rb] = 0.f;
 
@@ -583,7 +653,7 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
 
     auto back = [&]() {
       // P^T fragments (fp16) and their row sums; int8: P' = P * v_scale feeds P V
-      f16x8 pw[RB];
+      f16x8 pw[RBA];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         f16x8 pr;
@@ -651,6 +721,42 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
       }
     };
 
+    // WIDE: P V runs one step behind, from the shared fp16 V^T fragments
+    f16x8 pprev[RBA];
+    auto make_p = [&]() {  // P^T fragments (fp16) of the scored tile and their row sums
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        f16x8 pr;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pr[e] = static_cast<_Float16>(__builtin_amdgcn_exp2f(sacc[e >> 2][rb][e & 3]));
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          l[rb] = __builtin_amdgcn_fdot2(f16x2{pr[2 * k], pr[2 * k + 1]}, f16x2{1, 1}, l[rb], false);
+        pprev[rb] = pr;
+      }
+    };
+    // this wave's key of every lane group of V tile t as fp16 into vT[t & 1]:
+    // fragment (db, lane (i, g)) element e holds V[8g + e][8i + db]; wave w
+    // converts e = w
+    auto convert_v = [&](int t) {
+      const int r = 8 * lg + wave;
+      const u32x4 x = *reinterpret_cast<const u32x4*>(ring[t % S] + KBYTES + r * RBYTES + 16 * (li ^ lds_swz<false>(r)));
+      _Float16* dst = reinterpret_cast<_Float16*>(&vT[t & 1][0]) + wave;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const uint32_t wv = x[db >> 1];
+        dst[(db * 64 + lane) * 8] = static_cast<_Float16>(__uint_as_float((db & 1) ? (wv & 0xFFFF0000u) : (wv << 16)));
+      }
+    };
+    auto pv_wide = [&](int t) {  // O^T += V^T P^T for tile t with the P of that tile
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const f16x8 vf = __builtin_bit_cast(f16x8, vT[t & 1][db * 64 + lane]);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) o[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pprev[rb], o[db][rb], 0, 0, 0);
+      }
+    };
+
     // References without rescaling. A row's reference m is set before the loop
     // from the scores of the split's first tile (row max + kMargin). Inside the
     // loop it is only tracked: probabilities stay below 2^6 while no score
@@ -704,13 +810,28 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
         wait_tile(t);
         __syncthreads();  // tile t is complete in every pair; slot (t - 1) % S is free
         if (t + S - 1 < ntile) issue(t + S - 1);
-        scores(t, masked);
-        back();
+        if constexpr (WIDE) {
+          convert_v(t);
+          scores(t, masked);
+          pv_wide(t - 1);  // (step 0: zero P times the zeroed buffer)
+          make_p();
+        } else {
+          scores(t, masked);
+          back();
+        }
       };
+      if constexpr (WIDE) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) pprev[rb] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      }
 #pragma nounroll
       for (int t = 0; t < n_full; ++t) step(t, std::false_type{});
 #pragma nounroll
       for (int t = n_full; t < ntile; ++t) step(t, std::true_type{});
+      if constexpr (WIDE) {
+        __syncthreads();  // the last tile's fragments are complete
+        pv_wide(ntile - 1);
+      }
       for (int t = ntile; t < nt_wg; ++t) __syncthreads();
       // every wave has left the loop (its last wait drained its DMAs) before any
       // ring slot is staged again
@@ -734,6 +855,32 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
       l[rb] += __shfl_xor(l[rb], 32);
     }
     __syncthreads();  // every ring is drained
+    if constexpr (WIDE) {
+      // the pairs' chunks are disjoint: each is written out (or stored as
+      // a partial of its own) in turn
+      for (int q = 0; q < NP; ++q) {
+        if (pair == q) {
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            const int rloc = (rb0 + rb) * 16 + li;
+#pragma unroll
+            for (int db = 0; db < 8; ++db)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) mo[(((rb0 + rb) * 8 + db) * 4 + r) * 64 + lane] = o[db][rb][r];
+            if (lg == 0) {
+              mml[rloc * 2] = m[rb];
+              mml[rloc * 2 + 1] = l[rb];
+            }
+          }
+        }
+        __syncthreads();
+        Work wq;
+        decode(p, wgi * NP + q, wq);
+        store_out(wq, wgi * NP + q, wq.nsplit == 1);
+        __syncthreads();
+      }
+      return;
+    }
     for (int step = 0; step < NP; ++step) {
       if (pair == step) {
 #pragma unroll
@@ -760,36 +907,24 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
       __syncthreads();
     }
   };
-  if (h == 0) per_wave(std::integral_constant<int, RB0>{}, 0);
-  else per_wave(std::integral_constant<int, RB1>{}, RB0);
-
-  const int nwg_unit = w.nsplit / NP;
-  // Row-major stores, four consecutive d per thread (coalesced); the fold
-  // left o in LDS in the MFMA lane order: row 16 rb + i, d = 32 g + 8 r + db
-  // at ((rb * 8 + db) * 4 + r) * 64 + 16 g + i.
-  for (int flat = 4 * threadIdx.x; flat < w.nrows * D; flat += 4 * 64 * NW) {
-    const int rloc = flat / D, d0 = flat % D;
-    const int rb = rloc >> 4, i = rloc & 15;
-    f32x4 v;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int d = d0 + u;
-      v[u] = mo[((rb * 8 + (d & 7)) * 4 + ((d >> 3) & 3)) * 64 + 16 * (d >> 5) + i];
+  if constexpr (WIDE) {
+    // the pair's row blocks, the first half (rounded up) on wave 0: each wave
+    // runs the variant for its own count, so small trees cost no idle MFMAs
+    const int nrb = (w.nrows + 15) / 16;  // <= RB0 + RB1
+    const int a = (nrb + 1) / 2;
+    const int nrb_w = h == 0 ? a : nrb - a;
+    const int rb0 = h == 0 ? 0 : a;
+    static_assert(RB0 == 3 && RB1 == 2, "wide variants");
+    switch (nrb_w) {
+      case 0: per_wave(std::integral_constant<int, 0>{}, rb0); break;
+      case 1: per_wave(std::integral_constant<int, 1>{}, rb0); break;
+      case 2: per_wave(std::integral_constant<int, 2>{}, rb0); break;
+      default: per_wave(std::integral_constant<int, 3>{}, rb0); break;
     }
-    if (nwg_unit == 1) {
-      const int row = w.row0 + rloc;
-      const int node = w.o0 + row / p.G;
-      const int qh = w.kvh * p.G + row % p.G;
-      *reinterpret_cast<f32x4*>(p.out + ((size_t)node * p.Hq + qh) * D + d0) = v / mml[rloc * 2 + 1];
-    } else {
-      *reinterpret_cast<f32x4*>(p.part_o + ((size_t)wgi * p.rows_chunk + rloc) * D + d0) = v;
-    }
-  }
-  if (nwg_unit > 1) {
-    for (int r = threadIdx.x; r < w.nrows; r += 64 * NW) {
-      p.part_ml[((size_t)wgi * p.rows_chunk + r) * 2] = mml[r * 2];
-      p.part_ml[((size_t)wgi * p.rows_chunk + r) * 2 + 1] = mml[r * 2 + 1];
-    }
+  } else {
+    if (h == 0) per_wave(std::integral_constant<int, RB0>{}, 0);
+    else per_wave(std::integral_constant<int, RB1>{}, RB0);
+    store_out(w, wgi, w.nsplit / NP == 1);  // one partial per workgroup
   }
 }
 
@@ -1468,6 +1603,7 @@ __global__ void __launch_bounds__(64) attn_valu_kernel(const AttnParams p) {
 
 struct AttnPlan {
   bool mfma;
+  bool wide;  // bf16 MFMA with the four pairs of a workgroup on four row chunks of one split
   int rb;
   AttnParams prm;  // everything except pointers
   int nunits;
@@ -1504,7 +1640,15 @@ static ttv_status plan_attention(const ttv_batch* batch, int Hq, const ttv_kv_la
     maxP = P > maxP ? P : maxP;
   }
   pl.mfma = bf && L->D == 128 && max_rows >= 16 && L->cap >= 32;
-  if (pl.mfma) {
+  pl.wide = pl.mfma && L->dtype != TTV_I8 && max_rows > 16 * kMfmaMaxRB;
+  if (pl.wide) {
+    // up to four balanced chunks of at most 80 rows side by side (more rows
+    // take further groups of four)
+    const int ngrp = (max_rows + 4 * 16 * kWideMaxRB - 1) / (4 * 16 * kWideMaxRB);
+    const int per = (max_rows + 4 * ngrp - 1) / (4 * ngrp);
+    pl.rb = (per + 15) / 16;
+    if (pl.rb < 2) pl.rb = 2;
+  } else if (pl.mfma) {
     // balanced row chunks of at most 96 rows (int8: 80): pl.rb row blocks
     const int max_rows_chunk = 16 * (L->dtype == TTV_I8 ? kI8MaxRB : kMfmaMaxRB);
     const int nch = (max_rows + max_rows_chunk - 1) / max_rows_chunk;
@@ -1523,14 +1667,36 @@ static ttv_status plan_attention(const ttv_batch* batch, int Hq, const ttv_kv_la
   p.D = L->D;
   p.cap = L->cap;
   p.rows_chunk = pl.mfma ? 16 * pl.rb : kValuRows;
+  // rows per chunk of each sequence: the launch's chunk, or for the wide
+  // layout the sequence's own row blocks spread over groups of four chunks
+  // (so a small tree keeps its rows on few waves and a large one on all)
+  auto chunk_rows = [&](int rows) -> int {
+    if (!pl.wide || rows == 0) return p.rows_chunk;
+    const int nrb = (rows + 15) / 16;
+    const int ngrp = (nrb + 4 * kWideMaxRB - 1) / (4 * kWideMaxRB);
+    return 16 * ((nrb + 4 * ngrp - 1) / (4 * ngrp));
+  };
+  int max_rc = 0, max_rch = 0;
+  for (int b = 0; b < B; ++b) {
+    const int T = batch->node_off_h[b + 1] - batch->node_off_h[b];
+    p.rchunk[b] = chunk_rows(T * G);
+    const int rc = (T * G + p.rchunk[b] - 1) / p.rchunk[b];
+    max_rc = rc > max_rc ? rc : max_rc;
+    max_rch = p.rchunk[b] > max_rch ? p.rchunk[b] : max_rch;
+  }
+  if (pl.wide) p.rows_chunk = max_rch;  // the partials' row stride
+  // wide: every (kv head, split) takes rc_group slots (4 per workgroup)
+  p.rc_group = pl.wide ? (max_rc + 3) / 4 * 4 : 0;
   int64_t work = 0;
   for (int b = 0; b < B; ++b) {
     const int T = batch->node_off_h[b + 1] - batch->node_off_h[b];
-    const int rc = (T * G + p.rows_chunk - 1) / p.rows_chunk;
+    const int rc = (T * G + p.rchunk[b] - 1) / p.rchunk[b];
     const int P = batch->hist_len_h[b];
-    work += (int64_t)p.Hkv * rc * (P > 0 ? P : 1);
+    work += (int64_t)p.Hkv * (pl.wide ? (rc + 3) / 4 : rc) * (P > 0 ? P : 1);
   }
-  int64_t sl = (work + kTargetWG - 1) / kTargetWG;
+  // a wide workgroup's partial is up to 384 rows of fp32: its split is kept
+  // long (about two workgroups per compute unit)
+  int64_t sl = (work + (pl.wide ? kWideTargetWG : kTargetWG) - 1) / (pl.wide ? kWideTargetWG : kTargetWG);
   const int64_t min_sl = (maxP + kMaxSplits - 1) / kMaxSplits;
   if (sl < min_sl) sl = min_sl;
   if (sl < 256) sl = 256;
@@ -1538,21 +1704,21 @@ static ttv_status plan_attention(const ttv_batch* batch, int Hq, const ttv_kv_la
   p.split_len = static_cast<int>(sl);
   // MFMA workgroups are 4 wave pairs = 4 consecutive key splits of one unit,
   // so a unit's split count is padded to a multiple of 4 (padding splits are
-  // empty)
-  p.split_pad = pl.mfma ? 4 : 1;
+  // empty); wide workgroups take 4 row chunks of one split instead
+  p.split_pad = pl.mfma && !pl.wide ? 4 : 1;
   int wg = 0, units = 0;
   pl.merge = false;
   for (int b = 0; b < B; ++b) {
     const int T = batch->node_off_h[b + 1] - batch->node_off_h[b];
     const int P = batch->hist_len_h[b];
-    const int rc = (T * G + p.rows_chunk - 1) / p.rows_chunk;
+    const int rc = (T * G + p.rchunk[b] - 1) / p.rchunk[b];
     const int ns0 = P > 0 ? (P + p.split_len - 1) / p.split_len : 1;
     const int ns = (ns0 + p.split_pad - 1) / p.split_pad * p.split_pad;
     p.node_off[b] = batch->node_off_h[b];
     p.hist_len[b] = P;
     p.wg_off[b] = wg;
     p.unit_off[b] = units;
-    wg += p.Hkv * ns * rc;
+    wg += p.Hkv * ns * (pl.wide ? (rc > 0 ? p.rc_group : 0) : rc);
     units += p.Hkv * rc;
     if (rc > 0 && ns / p.split_pad > 1) pl.merge = true;
   }
@@ -1606,7 +1772,8 @@ extern "C" ttv_status tree_verify_attention(const ttv_batch* batch, const void* 
   const bool i8 = layer->dtype == TTV_I8;
   if (pl.mfma) {
 #define TTV_MFMA(I, R0, R1) \
-  hipLaunchKernelGGL((attn_mfma_kernel<I, R0, R1, (I) ? 4 : 2>), dim3(mgrid), dim3(512), 0, st, p)
+  hipLaunchKernelGGL((attn_mfma_kernel<I, false, R0, R1, (I) ? 4 : 2>), dim3(mgrid), dim3(512), 0, st, p)
+#define TTV_WIDE(R0, R1) hipLaunchKernelGGL((attn_mfma_kernel<false, true, R0, R1, 3>), dim3(mgrid), dim3(512), 0, st, p)
 #define TTV_MFMA_RB(R0, R1) TTV_MFMA(false, R0, R1)
 #define TTV_SPLIT(R) hipLaunchKernelGGL((attn_i8_split_kernel<R>), dim3(mgrid), dim3(512), 0, st, p)
     if (i8) {
@@ -1617,6 +1784,8 @@ extern "C" ttv_status tree_verify_attention(const ttv_batch* batch, const void* 
         case 4: TTV_SPLIT(4); break;
         default: TTV_SPLIT(5); break;
       }
+    } else if (pl.wide) {
+      TTV_WIDE(3, 2);  // up to 5 row blocks per chunk; each wave runs its own count
     } else switch (pl.rb) {  // row blocks of a chunk, split between the two waves of a pair
       case 1: case 2: TTV_MFMA_RB(1, 1); break;
       case 3: TTV_MFMA_RB(2, 1); break;
@@ -1625,6 +1794,7 @@ extern "C" ttv_status tree_verify_attention(const ttv_batch* batch, const void* 
       default: TTV_MFMA_RB(3, 3); break;
     }
 #undef TTV_MFMA_RB
+#undef TTV_WIDE
 #undef TTV_SPLIT
 #undef TTV_MFMA
   } else {
@@ -1642,6 +1812,6 @@ extern "C" ttv_status tree_verify_attention(const ttv_batch* batch, const void* 
   if (s != TTV_OK || !pl.merge) return s;
   hipLaunchKernelGGL(merge_kernel,
                      dim3(static_cast<unsigned>(pl.nunits), static_cast<unsigned>((p.rows_chunk + kMergeRows - 1) / kMergeRows)),
-                     dim3(128), 0, st, p, pl.mfma ? 4 : 1);
+                     dim3(128), 0, st, p, pl.mfma && !pl.wide ? 4 : 1);
   return check_launch("tree_verify_attention merge");
 }
