@@ -61,7 +61,7 @@ constexpr int kI8MaxRB = 5;     // int8: both waves of a pair hold all row block
 constexpr int kValuRows = 16;   // rows per VALU workgroup
 constexpr int kTargetWG = 1024;
 constexpr int kWideTargetWG = 1024;
-constexpr int kWideMaxRB = 5;  // bf16 wide layout: row blocks per chunk (LDS holds four chunks' Q)
+constexpr int kWideMaxRB = 4;  // bf16 wide layout: row blocks per chunk (two per wave, Q in registers)
 constexpr int kMaxSplits = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -76,7 +76,7 @@ struct AttnParams {
   float* part_o;
   float* part_ml;
   int B, Hq, Hkv, G, D, cap, split_len, rows_chunk, nwg, split_pad;
-  int rc_group;  // wide layout: row chunks per (kv head, split) group of slots (a multiple of 4), else 0
+  int wide;  // wide layout: the row chunks of one (kv head, split) take ceil(rc_n / 4) * 4 consecutive slots
   float scale_log2;
   int32_t node_off[TTV_MAX_BATCH + 1];
   int32_t hist_len[TTV_MAX_BATCH];
@@ -106,9 +106,10 @@ __device__ __forceinline__ void decode(const AttnParams& p, int slot, Work& w) {
   const int ns = w.P > 0 ? (w.P + p.split_len - 1) / p.split_len : 1;
   w.nsplit = (ns + p.split_pad - 1) / p.split_pad * p.split_pad;  // trailing splits may be empty
   int rem = slot - p.wg_off[lo];
-  if (p.rc_group > 0) {  // wide: the row chunks of one (kv head, split) are consecutive slots
-    w.rc = rem % p.rc_group;
-    rem /= p.rc_group;
+  if (p.wide) {  // the row chunks of one (kv head, split) are consecutive slots
+    const int rcg = (w.rc_n + 3) / 4 * 4;
+    w.rc = rem % rcg;
+    rem /= rcg;
     w.split = rem % w.nsplit;
     w.kvh = rem / w.nsplit;
   } else {
@@ -217,9 +218,10 @@ __global__ void __launch_bounds__(256) merge_kernel(const AttnParams p, int per_
   w.nrows = min(rch, w.rows - w.row0);
   const int r0 = blockIdx.y * kMergeRows;
   if (r0 >= w.nrows) return;
-  if (p.rc_group > 0)  // wide: split s of this chunk is slot group (kvh, s), member rc
-    merge_partials(p, w, p.wg_off[lo] + w.kvh * w.nsplit * p.rc_group + w.rc, n, wt, r0,
-                   min(w.nrows, r0 + kMergeRows), p.rc_group);
+  const int rcg = (w.rc_n + 3) / 4 * 4;
+  if (p.wide)  // split s of this chunk is slot group (kvh, s), member rc
+    merge_partials(p, w, p.wg_off[lo] + w.kvh * w.nsplit * rcg + w.rc, n, wt, r0, min(w.nrows, r0 + kMergeRows),
+                   rcg);
   else
     merge_partials(p, w, (p.wg_off[lo] + rem * w.nsplit) / per_slot, n, wt, r0, min(w.nrows, r0 + kMergeRows), 1);
 }
@@ -269,10 +271,12 @@ __device__ __forceinline__ void wait_vmcnt() {
   __asm__ volatile("" ::: "memory");
 }
 
-// Wait until at most `ahead` tiles of ND DMAs each are outstanding (ahead <= 3).
+// Wait until at most `ahead` tiles of ND DMAs each are outstanding (ahead <= 5).
 template <int ND>
 __device__ __forceinline__ void wait_vmcnt_tiles(int ahead) {
-  if (ahead >= 3) wait_vmcnt<3 * ND>();
+  if (ahead >= 5) wait_vmcnt<5 * ND>();
+  else if (ahead == 4) wait_vmcnt<4 * ND>();
+  else if (ahead == 3) wait_vmcnt<3 * ND>();
   else if (ahead == 2) wait_vmcnt<2 * ND>();
   else if (ahead == 1) wait_vmcnt<ND>();
   else wait_vmcnt<0>();
@@ -342,7 +346,7 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
   // per pair: an S-stage ring of K/V tiles; per workgroup: the unit's Q^T
   // fragments (one conflict-free 16-byte read per use) and ancestor bitsets
   __shared__ __attribute__((aligned(16))) char ring_all[NR][S][TILE];
-  __shared__ __attribute__((aligned(16))) u32x4 qsh_all[NQ][RBU * 4 * 64];
+  __shared__ __attribute__((aligned(16))) u32x4 qsh_all[NQ][WIDE ? 1 : RBU * 4 * 64];  // WIDE: Q in registers
   __shared__ uint64_t tbits_all[NQ][RBU * 16];
   // WIDE: V^T fragments of a tile as fp16, converted once for all waves
   // (double-buffered: tile t is converted in step t and used in step t + 1)
@@ -365,10 +369,34 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
   u32x4* qsh = qsh_all[WIDE ? pair : 0];
   uint64_t* tbits_s = tbits_all[WIDE ? pair : 0];
 
+  // WIDE: the pair's row blocks, the first half (rounded up) on wave 0
+  const int nrb_pair = (w.nrows + 15) / 16;  // <= RB0 + RB1
+  const int nrb_w = h == 0 ? (nrb_pair + 1) / 2 : nrb_pair / 2;
+  const int rb0_w = h == 0 ? 0 : (nrb_pair + 1) / 2;
+  // WIDE: this wave's Q^T fragments in registers (d = 32ks + 8g + e)
+  bf16x8 qreg[WIDE ? RB0 : 1][4];
+  if constexpr (WIDE) {
+    static_assert(RB0 == RB1, "wide: equal halves");
+#pragma unroll
+    for (int rb = 0; rb < RB0; ++rb) {
+      const int rloc = (rb0_w + rb) * 16 + li;
+      const bool ok = rb < nrb_w && rloc < w.nrows;
+      const int row = ok ? w.row0 + rloc : 0;
+      const int node = w.o0 + row / p.G;
+      const int qh = w.kvh * p.G + row % p.G;
+      const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + ((size_t)node * p.Hq + qh) * D;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        u32x4 x = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * lg);
+        if (!ok) x = u32x4{0, 0, 0, 0};
+        qreg[rb][ks] = __builtin_bit_cast(bf16x8, x);
+      }
+    }
+  }
   // Q^T fragments into LDS. k-slot mapping of the QK product (shared by K and
   // Q): bf16 KV d = 32ks + 8g + e (bf16 operands); int8 KV d = 32g + 8ks + e
   // (fp16 operands, so a lane's 32 int8 codes are contiguous).
-  for (int f = WIDE ? h : wave; f < RBU * 4; f += WIDE ? 2 : NW) {  // WIDE: the pair loads its own chunk
+  for (int f = wave; f < (WIDE ? 0 : RBU * 4); f += NW) {
     const int rb = f >> 2, ks = f & 3;
     const int rloc = rb * 16 + li;
     const bool ok = rloc < w.nrows;
@@ -488,9 +516,9 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
   for (int q = 0; q < NP; ++q) nt_wg = max(nt_wg, s_nt[q]);
   // the fold (WIDE: each pair's output in turn) goes through LDS: the rings,
   // or for WIDE the Q fragments' space
-  float* mo = WIDE ? reinterpret_cast<float*>(&qsh_all[0][0]) : reinterpret_cast<float*>(&ring_all[0][0][0]);
+  float* mo = reinterpret_cast<float*>(&ring_all[0][0][0]);
   float* mml = mo + RBU * 32 * 64;  // mo: [RBU][8][4][64] lane-major o; mml: [RBU * 16][2] (m, l)
-  static_assert(RBU * 32 * 64 * 4 + RBU * 16 * 8 <= (WIDE ? NQ * RBU * 4 * 64 * 16 : NR * S * TILE), "fold area");
+  static_assert(RBU * 32 * 64 * 4 + RBU * 16 * 8 <= NR * S * TILE, "fold area");
   // Row-major stores of rows [0, wq.nrows) of a chunk from mo / mml, four
   // consecutive d per thread (coalesced): the unit's output if one partial
   // covers it, else partial slot `slot`. LDS holds o in the MFMA lane order:
@@ -609,7 +637,9 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
           }
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) {
-            const qk_t qv = __builtin_bit_cast(qk_t, qsh[((rb0 + rb) * 4 + ks) * 64 + lane]);
+            qk_t qv;
+            if constexpr (WIDE) qv = __builtin_bit_cast(qk_t, qreg[rb][ks]);
+            else qv = __builtin_bit_cast(qk_t, qsh[((rb0 + rb) * 4 + ks) * 64 + lane]);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
               const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -735,18 +765,20 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
         pprev[rb] = pr;
       }
     };
-    // this wave's key of every lane group of V tile t as fp16 into vT[t & 1]:
-    // fragment (db, lane (i, g)) element e holds V[8g + e][8i + db]; wave w
-    // converts e = w
+    // V^T fragments of V tile t as fp16 into vT[t & 1]: fragment (db, lane
+    // (i, g)) holds V[8g + e][8i + db], e = 0..7; wave w builds d-block
+    // db = w for every lane (eight dword reads, one 16-byte write)
     auto convert_v = [&](int t) {
-      const int r = 8 * lg + wave;
-      const u32x4 x = *reinterpret_cast<const u32x4*>(ring[t % S] + KBYTES + r * RBYTES + 16 * (li ^ lds_swz<false>(r)));
-      _Float16* dst = reinterpret_cast<_Float16*>(&vT[t & 1][0]) + wave;
+      const char* vt0 = ring[t % S] + KBYTES;
+      f16x8 f;
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const uint32_t wv = x[db >> 1];
-        dst[(db * 64 + lane) * 8] = static_cast<_Float16>(__uint_as_float((db & 1) ? (wv & 0xFFFF0000u) : (wv << 16)));
+      for (int e = 0; e < 8; ++e) {
+        const int r = 8 * lg + e;
+        const uint32_t x =
+            *reinterpret_cast<const uint32_t*>(vt0 + r * RBYTES + 16 * (li ^ lds_swz<false>(r)) + 4 * (wave >> 1));
+        f[e] = static_cast<_Float16>(__uint_as_float((wave & 1) ? (x & 0xFFFF0000u) : (x << 16)));
       }
+      vT[t & 1][wave * 64 + lane] = __builtin_bit_cast(u32x4, f);
     };
     auto pv_wide = [&](int t) {  // O^T += V^T P^T for tile t with the P of that tile
 #pragma unroll
@@ -908,18 +940,13 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
     }
   };
   if constexpr (WIDE) {
-    // the pair's row blocks, the first half (rounded up) on wave 0: each wave
-    // runs the variant for its own count, so small trees cost no idle MFMAs
-    const int nrb = (w.nrows + 15) / 16;  // <= RB0 + RB1
-    const int a = (nrb + 1) / 2;
-    const int nrb_w = h == 0 ? a : nrb - a;
-    const int rb0 = h == 0 ? 0 : a;
-    static_assert(RB0 == 3 && RB1 == 2, "wide variants");
+    // each wave runs the variant for its own row-block count, so small trees
+    // cost no idle MFMAs
+    static_assert(RB0 == 2 && RB1 == 2, "wide variants");
     switch (nrb_w) {
-      case 0: per_wave(std::integral_constant<int, 0>{}, rb0); break;
-      case 1: per_wave(std::integral_constant<int, 1>{}, rb0); break;
-      case 2: per_wave(std::integral_constant<int, 2>{}, rb0); break;
-      default: per_wave(std::integral_constant<int, 3>{}, rb0); break;
+      case 0: per_wave(std::integral_constant<int, 0>{}, rb0_w); break;
+      case 1: per_wave(std::integral_constant<int, 1>{}, rb0_w); break;
+      default: per_wave(std::integral_constant<int, 2>{}, rb0_w); break;
     }
   } else {
     if (h == 0) per_wave(std::integral_constant<int, RB0>{}, 0);
@@ -1676,17 +1703,16 @@ static ttv_status plan_attention(const ttv_batch* batch, int Hq, const ttv_kv_la
     const int ngrp = (nrb + 4 * kWideMaxRB - 1) / (4 * kWideMaxRB);
     return 16 * ((nrb + 4 * ngrp - 1) / (4 * ngrp));
   };
-  int max_rc = 0, max_rch = 0;
+  int max_rch = 0;
   for (int b = 0; b < B; ++b) {
     const int T = batch->node_off_h[b + 1] - batch->node_off_h[b];
     p.rchunk[b] = chunk_rows(T * G);
-    const int rc = (T * G + p.rchunk[b] - 1) / p.rchunk[b];
-    max_rc = rc > max_rc ? rc : max_rc;
     max_rch = p.rchunk[b] > max_rch ? p.rchunk[b] : max_rch;
   }
   if (pl.wide) p.rows_chunk = max_rch;  // the partials' row stride
-  // wide: every (kv head, split) takes rc_group slots (4 per workgroup)
-  p.rc_group = pl.wide ? (max_rc + 3) / 4 * 4 : 0;
+  // wide: every (kv head, split) takes its chunk count rounded up to 4 slots
+  // (one workgroup per 4)
+  p.wide = pl.wide ? 1 : 0;
   int64_t work = 0;
   for (int b = 0; b < B; ++b) {
     const int T = batch->node_off_h[b + 1] - batch->node_off_h[b];
@@ -1718,7 +1744,7 @@ static ttv_status plan_attention(const ttv_batch* batch, int Hq, const ttv_kv_la
     p.hist_len[b] = P;
     p.wg_off[b] = wg;
     p.unit_off[b] = units;
-    wg += p.Hkv * ns * (pl.wide ? (rc > 0 ? p.rc_group : 0) : rc);
+    wg += p.Hkv * ns * (pl.wide ? (rc + 3) / 4 * 4 : rc);
     units += p.Hkv * rc;
     if (rc > 0 && ns / p.split_pad > 1) pl.merge = true;
   }
@@ -1785,7 +1811,7 @@ extern "C" ttv_status tree_verify_attention(const ttv_batch* batch, const void* 
         default: TTV_SPLIT(5); break;
       }
     } else if (pl.wide) {
-      TTV_WIDE(3, 2);  // up to 5 row blocks per chunk; each wave runs its own count
+      TTV_WIDE(2, 2);  // up to 4 row blocks per chunk; each wave runs its own count
     } else switch (pl.rb) {  // row blocks of a chunk, split between the two waves of a pair
       case 1: case 2: TTV_MFMA_RB(1, 1); break;
       case 3: TTV_MFMA_RB(2, 1); break;
