@@ -35,6 +35,7 @@ __all__ = [
     "tree_verify_attention",
     "tree_verify_attention_dense",
     "vocab_argmax",
+    "vocab_sample",
     "tree_accept_walk",
     "rollback_selection",
     "gather_positions",
@@ -224,6 +225,62 @@ def vocab_argmax(logits) -> np.ndarray:
     Ties go to the lowest index; -0.0 equals +0.0; a NaN outranks every number
     and the first NaN wins (numpy.argmax semantics)."""
     return np.argmax(np.asarray(logits, dtype=np.float32), axis=-1).astype(np.int32)
+
+
+def vocab_sample(logits, uniforms, uniform_stride: int, temperature: float, top_k: int, top_p: float) -> np.ndarray:
+    """The target's sampled selection at every node ([S728] "Historical issue
+    and default question", "What it does": for sampled requests each node
+    draws from the nucleus-filtered distribution with its own uniform, node n
+    taking uniforms[n * uniform_stride], so stride 0 gives every node the same
+    uniform; "Results" quotes temperature 1, top-p 0.95, top-k 20).
+
+    Reading of the filter chain (the pages name its parts, not their order):
+      1. top-k: the top_k largest logits, compared in fp32, ties to the lower
+         index (the argmax convention; -0.0 == +0.0);
+      2. z = logit / temperature and p_i = exp(z_i - z_0) / sum_j exp(z_j - z_0)
+         over those k, in float64, summed in descending order;
+      3. top-p: keep the shortest descending prefix whose cumulative mass C_i
+         reaches top_p (C_{k-1} = 1, so some prefix always does);
+      4. draw: the first kept i with C_i > u * C_{i*}, where i* ends the
+         prefix and u in [0, 1) is the node's uniform (inverse CDF of the
+         renormalised prefix).
+    A NaN ranks above every number; a row whose top logit is NaN or +inf
+    selects that logit's index. top_k = 1, or top_p <= C_0, reduce to the
+    argmax."""
+    X = np.asarray(logits, dtype=np.float32)
+    U = np.asarray(uniforms, dtype=np.float32).reshape(-1)
+    n_rows, V = X.shape
+    k = int(min(top_k, V))
+    assert k >= 1 and temperature > 0.0
+    out = np.zeros(n_rows, np.int32)
+    for n in range(n_rows):
+        x = X[n].astype(np.float64)
+        # descending by value, ties by index: a stable sort of the keys
+        # (NaN first, as the largest)
+        nan = np.isnan(x)
+        order = np.lexsort((np.arange(V), np.where(nan, 0.0, -x), ~nan))[:k]
+        top = x[order[0]]
+        if np.isnan(top) or top == np.inf:
+            out[n] = order[0]
+            continue
+        z = x[order] / float(temperature)
+        e = np.exp(z - z[0])
+        c = np.zeros(k)
+        acc = 0.0
+        for i in range(k):  # sequential, descending order
+            acc += e[i]
+            c[i] = acc
+        C = c / acc
+        i_star = int(np.argmax(C >= float(top_p)))
+        u = float(U[n * int(uniform_stride)])
+        target = u * C[i_star]
+        pick = i_star
+        for i in range(i_star + 1):
+            if C[i] > target:
+                pick = i
+                break
+        out[n] = order[pick]
+    return out
 
 
 # ----------------------------------------------------------------------------

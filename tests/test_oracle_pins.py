@@ -540,3 +540,129 @@ def test_linear_tree_round_equals_chain_round():
         for name in c:
             np.testing.assert_array_equal(tree_cache[name][:, :, :live], c[name][:, :, :live])
     assert kinds == {"full", "partial", "zero"}
+
+
+# ---------------------------------------------------------------------------
+# sampled selection (nucleus-filtered draw per node)
+# ---------------------------------------------------------------------------
+
+def test_sample_golden_worked():
+    g = _golden("sample_worked.json")
+    x = np.array([g["logits"]], np.float32)
+    for c in g["cases"]:
+        got = O.vocab_sample(x, [c["u"]], 0, c["temperature"], c["top_k"], c["top_p"])
+        assert int(got[0]) == c["token"], c
+
+
+def _nucleus_reference(x, T, k, p):
+    """Kept tokens and their renormalised probabilities, via numpy's sort and
+    cumsum (a library route, not the oracle's loop)."""
+    order = np.argsort(-x.astype(np.float64), kind="stable")[:k]
+    z = x[order].astype(np.float64) / T
+    w = np.exp(z - z.max())
+    C = np.cumsum(w) / w.sum()
+    n = int(np.searchsorted(C, p, side="left")) + 1
+    return order[:n], w[:n] / w[:n].sum()
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_sample_top1_and_tiny_top_p_are_argmax(seed):
+    r = np.random.default_rng(700 + seed)
+    X = r.integers(-4, 5, size=(40, 300)).astype(np.float32)  # many ties
+    X[0, 7] = -0.0
+    X[0, 3] = 0.0
+    U = r.random(40).astype(np.float32)
+    want = np.argmax(X, axis=1)
+    assert (O.vocab_sample(X, U, 1, 1.0, 1, 0.95) == want).all()
+    assert (O.vocab_sample(X, U, 1, 0.7, 20, 1e-9) == want).all()
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_sample_full_softmax_is_inverse_cdf(seed):
+    """top-k = V and top-p = 1: the draw is the inverse CDF of softmax(x / T),
+    i.e. numpy's searchsorted on the cumulative softmax (distinct logits)."""
+    r = np.random.default_rng(710 + seed)
+    V = 50
+    X = (r.standard_normal((30, V)) * 2).astype(np.float32)
+    U = r.random(30).astype(np.float32)
+    T = 0.8
+    got = O.vocab_sample(X, U, 1, T, V, 1.0)
+    for n in range(30):
+        order = np.argsort(-X[n].astype(np.float64), kind="stable")
+        w = np.exp(X[n, order].astype(np.float64) / T - X[n, order[0]] / T)
+        C = np.cumsum(w) / w.sum()
+        i = int(np.searchsorted(C, float(U[n]), side="right"))
+        assert got[n] == order[i], n
+
+
+def test_sample_stratified_frequencies_match_nucleus():
+    """Equally spaced uniforms hit every kept token in proportion to its
+    renormalised nucleus probability, to within one draw."""
+    r = np.random.default_rng(720)
+    x = (r.standard_normal((1, 2000)) * 2).astype(np.float32)
+    M = 20000
+    U = ((np.arange(M) + 0.5) / M).astype(np.float32)
+    X = np.repeat(x, M, axis=0)
+    got = O.vocab_sample(X, U, 1, 1.0, 20, 0.95)
+    kept, prob = _nucleus_reference(x[0], 1.0, 20, 0.95)
+    counts = {int(t): int((got == t).sum()) for t in np.unique(got)}
+    assert set(counts) <= set(int(t) for t in kept)
+    for t, pr in zip(kept, prob):
+        assert abs(counts.get(int(t), 0) - M * pr) <= 1.5, (int(t), counts.get(int(t), 0), M * pr)
+
+
+def test_sample_chi_square_random_uniforms():
+    """The pages' check for sampled exactness: a chi-square test of drawn
+    tokens against the nucleus distribution (seeded uniforms)."""
+    from scipy.stats import chisquare
+    r = np.random.default_rng(730)
+    x = (r.standard_normal((1, 5000)) * 2).astype(np.float32)
+    M = 20000
+    U = r.random(M).astype(np.float32)
+    got = O.vocab_sample(np.repeat(x, M, axis=0), U, 1, 1.0, 20, 0.95)
+    kept, prob = _nucleus_reference(x[0], 1.0, 20, 0.95)
+    obs = np.array([(got == t).sum() for t in kept], np.float64)
+    assert obs.sum() == M
+    assert chisquare(obs, M * prob).pvalue > 1e-3
+
+
+def test_sample_uniform_stride_and_monotone_in_u():
+    r = np.random.default_rng(740)
+    X = (r.standard_normal((6, 100)) * 2).astype(np.float32)
+    U = r.random(12).astype(np.float32)
+    s0 = O.vocab_sample(X, U, 0, 1.0, 20, 0.95)
+    s2 = O.vocab_sample(X, U, 2, 1.0, 20, 0.95)
+    for n in range(6):
+        assert s0[n] == O.vocab_sample(X[n:n + 1], U[:1], 0, 1.0, 20, 0.95)[0]
+        assert s2[n] == O.vocab_sample(X[n:n + 1], U[2 * n:2 * n + 1], 0, 1.0, 20, 0.95)[0]
+    # a larger uniform never picks a higher-ranked (larger-logit) token
+    row = X[:1]
+    order = list(np.argsort(-row[0].astype(np.float64), kind="stable"))
+    ranks = [order.index(int(O.vocab_sample(row, [u], 0, 1.0, 20, 0.95)[0])) for u in np.linspace(0, 0.999, 200)]
+    assert ranks == sorted(ranks)
+
+
+def test_sample_nonfinite_top_selects_it():
+    X = np.zeros((3, 10), np.float32)
+    X[0, 4] = np.nan
+    X[0, 6] = np.nan
+    X[1, 2] = np.inf
+    X[2, 5] = -np.inf
+    X[2, 1] = 3.0
+    got = O.vocab_sample(X, [0.99, 0.99, 0.0], 1, 1.0, 5, 0.95)
+    assert list(got) == [4, 2, 1]
+
+
+def test_sampled_walk_commits_the_samples():
+    """A round with sampled targets: every emitted token is the sample at its
+    path node and the path is the one the walk takes for those targets."""
+    r = rng_for(750)
+    parent = random_tree(r, 30)
+    X = (r.standard_normal((30, 64)) * 2).astype(np.float32)
+    U = r.random(30).astype(np.float32)
+    tgt = O.vocab_sample(X, U, 1, 1.0, 20, 0.95)
+    token = np.array([0] + [int(tgt[parent[i]]) if r.random() < 0.5 else 63 for i in range(1, 30)])
+    path, emitted = O.tree_accept_walk(parent, token, tgt)
+    assert emitted == [int(tgt[n]) for n in path]
+    for a, b in zip(path, path[1:]):
+        assert parent[b] == a and token[b] == tgt[a]
