@@ -327,6 +327,30 @@ def main():
         }
     }
 
+    # sampled selection (temperature 1, top-k 20, top-p 0.95, one uniform per
+    # node): the temperature > 0 form of the argmax step, timed on its own
+    n_rows, V = logits.shape
+    uni = torch.rand(n_rows, dtype=torch.float32, device=dev, generator=torch.Generator(device=dev).manual_seed(9))
+    s_out = torch.empty(n_rows, dtype=torch.int32, device=dev)
+    s_ws = torch.empty(ttv.vocab_sample_ws(n_rows, V, 20), dtype=torch.uint8, device=dev)
+    ttv.vocab_sample(logits, uni, s_out, s_ws, 1.0, 20, 0.95)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(20):
+        ttv.vocab_sample(logits, uni, s_out, s_ws, 1.0, 20, 0.95)
+    e1.record()
+    torch.cuda.synchronize()
+    samp_ms = e0.elapsed_time(e1) / 20
+    sbytes = n_rows * V * 4
+    kernels["vocab_sample"] = {
+        "avg_us": round(samp_ms * 1e3, 2), "bytes": sbytes, "GBps": round(sbytes / (samp_ms / 1e3) / 1e9, 1),
+        "frac_hbm": round(sbytes / (samp_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        "what": f"{n_rows} x {V} logits, temperature 1, top-k 20, top-p 0.95 (both passes)",
+    }
+    print(f"[bench] sampled selection {samp_ms * 1e3:.1f} us ({kernels['vocab_sample']['GBps']} GB/s)",
+          file=sys.stderr, flush=True)
+
     # full-window out-of-place gather (the pages' take): every survivor of every layer rewritten
     if not args.no_take:
         dst_caches = [{k: torch.empty_like(t) for k, t in c.items()} for c in caches]

@@ -6,6 +6,8 @@
  *   tree_verify_attention tree-masked GQA attention over the KV prefix plus
  *                        each node's ancestors
  *   vocab_argmax         per-node argmax over the target's vocabulary logits
+ *   vocab_sample         per-node draw from the nucleus-filtered distribution
+ *                        (the sampled form of the target's selection)
  *   tree_accept_walk     descend the one child matching the target's argmax
  *   kv_gather_positions  compact the accepted path's K/V (and int8 scales)
  *                        along the sequence axis
@@ -166,6 +168,35 @@ ttv_status tree_verify_attention(const ttv_batch* batch, const void* q, int32_t 
 size_t vocab_argmax_ws(int64_t n_rows, int64_t vocab);
 ttv_status vocab_argmax(const float* logits, int64_t n_rows, int64_t vocab, int64_t row_stride,
                         int32_t* out_idx, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Step 3, sampled -- [S728] "Historical issue and default question", "What it
+ * does": for sampled requests every node draws from the target's
+ * nucleus-filtered distribution with its own uniform, so the committed tokens
+ * are distributed as a chain verify's; "Results": temperature 1, top-p 0.95,
+ * top-k 20. Per row r:
+ *   1. the top_k largest logits (ties to the lower index, as vocab_argmax);
+ *   2. p_i proportional to exp(logit_i / temperature) over those, in float64,
+ *      summed in descending order; C_i their cumulative fractions;
+ *   3. i* = the first i with C_i >= top_p;
+ *   4. out_idx[r] = the index of the first i <= i* with C_i > u * C_{i*},
+ *      u = uniforms[r * uniform_stride] (i* when none does).
+ * A row whose top logit is NaN (NaN outranks every number), +inf, or -inf
+ * selects that logit. top_k = 1, or top_p at most the top token's mass, gives
+ * vocab_argmax's answer. Feed out_idx to tree_accept_walk as its target.
+ *   logits   (device) float32, row r at logits + r * row_stride
+ *   uniforms (device) float32, u in [0, 1); uniform_stride >= 0 (0: one
+ *            uniform for every row)
+ *   out_idx  (device) int32 [n_rows]
+ * Limits (TTV_ERR_INVALID): 1 <= top_k <= 64, temperature positive and
+ * finite, 0 <= top_p <= 1, n_rows <= 65535, ceil(vocab / 2048) * min(top_k,
+ * vocab) <= 8192. ws: >= vocab_sample_ws(n_rows, vocab, top_k) bytes,
+ * contents on entry are irrelevant.
+ */
+size_t vocab_sample_ws(int64_t n_rows, int64_t vocab, int32_t top_k);
+ttv_status vocab_sample(const float* logits, int64_t n_rows, int64_t vocab, int64_t row_stride,
+                        const float* uniforms, int64_t uniform_stride, float temperature, int32_t top_k,
+                        float top_p, int32_t* out_idx, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Step 4 -- accept walk [I1204] "What this needs" (2), "Increment 1"; [S728]

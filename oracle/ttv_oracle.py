@@ -244,13 +244,16 @@ def vocab_sample(logits, uniforms, uniform_stride: int, temperature: float, top_
       4. draw: the first kept i with C_i > u * C_{i*}, where i* ends the
          prefix and u in [0, 1) is the node's uniform (inverse CDF of the
          renormalised prefix).
-    A NaN ranks above every number; a row whose top logit is NaN or +inf
-    selects that logit's index. top_k = 1, or top_p <= C_0, reduce to the
+    A NaN ranks above every number; a row whose top logit is not finite (NaN,
+    +inf, or -inf when every logit is -inf) selects that logit's index. top_k = 1, or top_p <= C_0, reduce to the
     argmax."""
     X = np.asarray(logits, dtype=np.float32)
     U = np.asarray(uniforms, dtype=np.float32).reshape(-1)
     n_rows, V = X.shape
     k = int(min(top_k, V))
+    # the parameters are fp32 values (as a caller passes them), widened exactly
+    temperature = float(np.float32(temperature))
+    top_p = float(np.float32(top_p))
     assert k >= 1 and temperature > 0.0
     out = np.zeros(n_rows, np.int32)
     for n in range(n_rows):
@@ -260,7 +263,7 @@ def vocab_sample(logits, uniforms, uniform_stride: int, temperature: float, top_
         nan = np.isnan(x)
         order = np.lexsort((np.arange(V), np.where(nan, 0.0, -x), ~nan))[:k]
         top = x[order[0]]
-        if np.isnan(top) or top == np.inf:
+        if np.isnan(top) or np.isinf(top):
             out[n] = order[0]
             continue
         z = x[order] / float(temperature)

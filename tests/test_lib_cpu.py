@@ -113,6 +113,35 @@ def test_argmax_validation():
     assert C["vocab_argmax_ws"](4096, 1024) == 0
 
 
+def test_sample_validation():
+    f = C["vocab_sample"]
+    need = C["vocab_sample_ws"](128, 248320, 20)
+    assert need == 128 * 122 * 20 * 8
+    ok = (FAKE, 128, 248320, 248320, FAKE, 1, 1.0, 20, 0.95, FAKE, FAKE, need, None)
+
+    def call(**kw):
+        a = list(ok)
+        names = ["logits", "n_rows", "vocab", "stride", "u", "ustride", "temp", "k", "p", "out", "ws", "wsb", "st"]
+        for n, v in kw.items():
+            a[names.index(n)] = v
+        return f(*a)
+
+    assert call(k=0) == ttv.TTV_ERR_INVALID
+    assert call(k=65) == ttv.TTV_ERR_INVALID
+    assert call(temp=0.0) == ttv.TTV_ERR_INVALID
+    assert call(temp=float("inf")) == ttv.TTV_ERR_INVALID
+    assert call(p=1.5) == ttv.TTV_ERR_INVALID
+    assert call(p=-0.1) == ttv.TTV_ERR_INVALID
+    assert call(ustride=-1) == ttv.TTV_ERR_INVALID
+    assert call(u=None) == ttv.TTV_ERR_INVALID
+    assert call(stride=100) == ttv.TTV_ERR_INVALID
+    assert call(n_rows=70000) == ttv.TTV_ERR_INVALID
+    assert call(wsb=need - 8) == ttv.TTV_ERR_WORKSPACE
+    assert call(k=64, vocab=600000, stride=600000, wsb=1 << 40) == ttv.TTV_ERR_INVALID  # too many candidates
+    assert "candidates" in ttv.last_error()
+    assert call(n_rows=0) == ttv.TTV_OK
+
+
 def test_walk_validation():
     b, keep = batch([0, 0], [5])
     f = C["tree_accept_walk"]

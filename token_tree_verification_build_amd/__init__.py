@@ -60,6 +60,9 @@ _c = {
                                   [_BP, _p, _i32, _i32, _LP, _p, ctypes.c_float, _p, _p, _sz, _p]),
     "vocab_argmax_ws": _sig("vocab_argmax_ws", _sz, [_i64, _i64]),
     "vocab_argmax": _sig("vocab_argmax", _i32, [_p, _i64, _i64, _i64, _p, _p, _sz, _p]),
+    "vocab_sample_ws": _sig("vocab_sample_ws", _sz, [_i64, _i64, _i32]),
+    "vocab_sample": _sig("vocab_sample", _i32, [_p, _i64, _i64, _i64, _p, _i64, ctypes.c_float, _i32,
+                                                ctypes.c_float, _p, _p, _sz, _p]),
     "tree_accept_walk": _sig("tree_accept_walk", _i32, [_BP, _p, _p, _p, _p, _p, _p, _p, _i32, _p, _p, _p]),
     "kv_gather_positions_ws": _sig("kv_gather_positions_ws", _sz, [_i32]),
     "kv_gather_positions": _sig("kv_gather_positions", _i32,
@@ -229,6 +232,29 @@ def vocab_argmax(logits, out_idx, ws=None, n_rows=None, vocab=None, row_stride=N
     _dev(out_idx, torch.int32, "out_idx")
     _check(_c["vocab_argmax"](_ptr(logits), n_rows, vocab, row_stride, _ptr(out_idx), _ptr(ws),
                               ws.numel() if ws is not None else 0, _stream(stream)), "vocab_argmax")
+
+
+def vocab_sample_ws(n_rows: int, vocab: int, top_k: int) -> int:
+    return int(_c["vocab_sample_ws"](n_rows, vocab, top_k))
+
+
+def vocab_sample(logits, uniforms, out_idx, ws, temperature: float, top_k: int, top_p: float,
+                 uniform_stride: int = 1, n_rows=None, vocab=None, row_stride=None, stream=None):
+    """logits: float32 device tensor [n_rows, >= vocab]; uniforms: float32 device
+    tensor, node n taking uniforms[n * uniform_stride]."""
+    import torch
+    if logits.dtype != torch.float32 or not logits.is_cuda or logits.stride(-1) != 1:
+        raise ValueError("logits must be a float32 device tensor with unit inner stride")
+    n_rows = logits.shape[0] if n_rows is None else n_rows
+    vocab = logits.shape[1] if vocab is None else vocab
+    row_stride = logits.stride(0) if row_stride is None else row_stride
+    _dev(uniforms, torch.float32, "uniforms")
+    if n_rows > 0 and uniforms.numel() <= (n_rows - 1) * uniform_stride:
+        raise ValueError("uniforms holds fewer than (n_rows - 1) * uniform_stride + 1 values")
+    _dev(out_idx, torch.int32, "out_idx")
+    _check(_c["vocab_sample"](_ptr(logits), n_rows, vocab, row_stride, _ptr(uniforms), uniform_stride,
+                              float(temperature), int(top_k), float(top_p), _ptr(out_idx), _ptr(ws),
+                              ws.numel() if ws is not None else 0, _stream(stream)), "vocab_sample")
 
 
 def tree_accept_walk(batch: Batch, parent, token, target_argmax, path, path_len, emitted, dev_status,
