@@ -189,8 +189,8 @@ ttv_status vocab_argmax(const float* logits, int64_t n_rows, int64_t vocab, int6
  *            uniform for every row)
  *   out_idx  (device) int32 [n_rows]
  * Limits (TTV_ERR_INVALID): 1 <= top_k <= 64, temperature positive and
- * finite, 0 <= top_p <= 1, n_rows <= 65535, ceil(vocab / 2048) * min(top_k,
- * vocab) <= 8192. ws: >= vocab_sample_ws(n_rows, vocab, top_k) bytes,
+ * finite, 0 <= top_p <= 1, n_rows <= 65535, ceil(vocab / 4096) * min(top_k,
+ * vocab) <= 65536. ws: >= vocab_sample_ws(n_rows, vocab, top_k) bytes,
  * contents on entry are irrelevant.
  */
 size_t vocab_sample_ws(int64_t n_rows, int64_t vocab, int32_t top_k);

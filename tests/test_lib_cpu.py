@@ -116,7 +116,7 @@ def test_argmax_validation():
 def test_sample_validation():
     f = C["vocab_sample"]
     need = C["vocab_sample_ws"](128, 248320, 20)
-    assert need == 128 * 122 * 20 * 8
+    assert need == 128 * 61 * 20 * 8
     ok = (FAKE, 128, 248320, 248320, FAKE, 1, 1.0, 20, 0.95, FAKE, FAKE, need, None)
 
     def call(**kw):
@@ -137,7 +137,7 @@ def test_sample_validation():
     assert call(stride=100) == ttv.TTV_ERR_INVALID
     assert call(n_rows=70000) == ttv.TTV_ERR_INVALID
     assert call(wsb=need - 8) == ttv.TTV_ERR_WORKSPACE
-    assert call(k=64, vocab=600000, stride=600000, wsb=1 << 40) == ttv.TTV_ERR_INVALID  # too many candidates
+    assert call(k=64, vocab=6000000, stride=6000000, wsb=1 << 40) == ttv.TTV_ERR_INVALID  # too many candidates
     assert "candidates" in ttv.last_error()
     assert call(n_rows=0) == ttv.TTV_OK
 

@@ -9,8 +9,8 @@
 // reaches top-p, and the first kept token whose cumulative mass exceeds
 // u times the prefix's mass.
 //
-// Pass 1 streams the logits (HBM-bound): one wave per 2048-element chunk of a
-// row, 32 values per lane in registers. The chunk's top-k is found without a
+// Pass 1 streams the logits (HBM-bound): one wave per 4096-element chunk of a
+// row, 64 ordered values per lane in registers. The chunk's top-k is found without a
 // k-round scan over all of it: the k-th largest of the 64 lane maxima bounds
 // the chunk's k-th largest value from below (k lanes hold a value at least
 // that large), so only values at or above it are candidates; they are
@@ -24,11 +24,11 @@ namespace ttv {
 
 constexpr int kSampleMaxK = 64;
 constexpr int kSampleLanes = 64;           // lanes per wave
-constexpr int kSamplePerLane = 32;         // values per lane
-constexpr int kSampleChunk = kSampleLanes * kSamplePerLane;  // 2048 values per wave
+constexpr int kSamplePerLane = 64;         // values per lane
+constexpr int kSampleChunk = kSampleLanes * kSamplePerLane;  // 4096 values per wave
 constexpr int kSampleWaves = 4;            // waves (chunks) per pass-1 workgroup
 constexpr int kSampleCap = 256;            // candidate slots per wave in LDS
-constexpr int kSampleMaxCand = 256 * 32;   // chunk candidates per row (pass 2 holds 32 per thread)
+constexpr int kSampleMaxCand = 1 << 16;    // chunk candidates per row (pass 2 streams them)
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // ordered key: larger value first, equal values by lower index; -0.0 folded
@@ -50,18 +50,46 @@ __device__ __forceinline__ float key_value(uint64_t k) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
+// Wave-wide selection without lane shuffles: the largest t such that at
+// least `need` of the wave's keys (n per lane) are >= t, built bit by bit from
+// the top (the count is non-increasing in t) with ballots and popcounts. For
+// unique keys that is the need-th largest key; 0 when fewer than `need` are
+// nonzero.
+template <int N>
+__device__ __forceinline__ uint64_t wave_kth_largest(const uint64_t (&key)[N], int need) {
+  uint64_t t = 0;
+  for (int bit = 63; bit >= 0; --bit) {
+    const uint64_t cand = t | (1ull << bit);
+    int cnt = 0;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint64_t o = __shfl_xor(k, off);
-    k = o > k ? o : k;
+    for (int s = 0; s < N; ++s) cnt += __popcll(__ballot(key[s] >= cand));
+    if (cnt >= need) t = cand;
   }
-  return k;
+  return t;
+}
+
+// the lane's position among the set lanes of a wave-wide mask
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u)));
+}
+
+// ordered 32-bit value (the key's high half): 0 only for "no value"
+__device__ __forceinline__ uint32_t sample_ord(float x) { return static_cast<uint32_t>(sample_key(x, 0u) >> 32); }
+
+// 32-bit form of wave_kth_largest (one value per lane)
+__device__ __forceinline__ uint32_t wave_kth_largest32(uint32_t v, int need) {
+  uint32_t t = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = t | (1u << bit);
+    if (__popcll(__ballot(v >= cand)) >= need) t = cand;
+  }
+  return t;
 }
 
 // Pass 1: wave w of workgroup (g, row) takes chunk c = 4g + w of the row and
-// writes its top k keys, descending (key 0, below every value, fills slots a
-// short chunk cannot), to cand[(row * n_chunks + c) * k ...].
+// writes its top k keys (in no particular order; key 0, below every value,
+// fills slots a short chunk cannot) to cand[(row * n_chunks + c) * k ...].
 __global__ void __launch_bounds__(kSampleLanes * kSampleWaves)
     sample_pass1(const float* __restrict__ logits, int64_t vocab, int64_t row_stride, int n_chunks, int k, int vec,
                  uint64_t* __restrict__ cand) {
@@ -73,163 +101,185 @@ __global__ void __launch_bounds__(kSampleLanes * kSampleWaves)
   if (c >= n_chunks) return;  // whole wave; pass 1 has no workgroup barrier
   const float* __restrict__ x = logits + static_cast<int64_t>(row) * row_stride;
   const int64_t c0 = static_cast<int64_t>(c) * kSampleChunk;
-  // the lane's values: element c0 + 4 (64 j + lane) + q, j < 8, q < 4; past
-  // vocab they do not exist
-  uint64_t kk[kSamplePerLane];  // the values' keys (0 past vocab: below every value)
+  // the lane's ordered values: element c0 + 4 (64 j + lane) + q; past vocab 0
+  uint32_t ov[kSamplePerLane];
+  auto idx_of = [&](int j) -> uint32_t { return static_cast<uint32_t>(c0 + 4 * (64 * (j >> 2) + lane) + (j & 3)); };
   if (vec && c0 + kSampleChunk <= vocab) {
     const f32x4* __restrict__ xv = reinterpret_cast<const f32x4*>(x + c0);
 #pragma unroll
     for (int j = 0; j < kSamplePerLane / 4; ++j) {
       const f32x4 a = __builtin_nontemporal_load(xv + 64 * j + lane);
-      const uint32_t i0 = static_cast<uint32_t>(c0 + 4 * (64 * j + lane));
-      kk[4 * j] = sample_key(a.x, i0);
-      kk[4 * j + 1] = sample_key(a.y, i0 + 1);
-      kk[4 * j + 2] = sample_key(a.z, i0 + 2);
-      kk[4 * j + 3] = sample_key(a.w, i0 + 3);
+      ov[4 * j] = sample_ord(a.x);
+      ov[4 * j + 1] = sample_ord(a.y);
+      ov[4 * j + 2] = sample_ord(a.z);
+      ov[4 * j + 3] = sample_ord(a.w);
     }
   } else {
 #pragma unroll
     for (int j = 0; j < kSamplePerLane; ++j) {
       const int64_t i = c0 + 4 * (64 * (j >> 2) + lane) + (j & 3);
-      kk[j] = i < vocab ? sample_key(x[i], static_cast<uint32_t>(i)) : 0ull;
+      ov[j] = i < vocab ? sample_ord(x[i]) : 0u;
     }
   }
-  auto key_of = [&](int j) -> uint64_t { return kk[j]; };
-  // the lane maximum and the k-th largest lane maximum: a lower bound tau on
-  // the chunk's k-th largest key
-  uint64_t lmax = 0;
+  // tau = the k-th largest lane maximum value, a lower bound on the chunk's
+  // k-th largest value (k lanes hold a value at least that large); 0 when the
+  // chunk holds fewer than k values
+  uint32_t lmax = 0;
 #pragma unroll
-  for (int j = 0; j < kSamplePerLane; ++j) {
-    const uint64_t kj = key_of(j);
-    lmax = kj > lmax ? kj : lmax;
-  }
-  uint64_t rest = lmax, tau = 0;
-  for (int r = 0; r < k; ++r) {
-    const uint64_t m = wave_max_u64(rest);
-    tau = m;
-    if (rest == m) rest = 0;
-  }
-  // compact the candidates (keys >= tau; tau = 0 when the chunk holds fewer
-  // than k values, then every value is one) into LDS
-  int cnt = 0;
-#pragma unroll
-  for (int j = 0; j < kSamplePerLane; ++j) {
-    const uint64_t kj = key_of(j);
-    cnt += (kj != 0 && kj >= tau) ? 1 : 0;
-  }
-  int incl = cnt;  // inclusive prefix sum over the wave
-#pragma unroll
-  for (int off = 1; off < kSampleLanes; off <<= 1) {
-    const int o = __shfl_up(incl, off);
-    if (lane >= off) incl += o;
-  }
-  const int total = __shfl(incl, kSampleLanes - 1);
-  uint64_t* out = cand + (static_cast<int64_t>(row) * n_chunks + c) * k;
+  for (int j = 0; j < kSamplePerLane; ++j) lmax = ov[j] > lmax ? ov[j] : lmax;
+  const uint32_t tau = max(wave_kth_largest32(lmax, k), 1u);
+  // compact the candidates' full keys (values >= tau) into LDS
   uint64_t* sc = s_cand[wave];
-  if (total <= kSampleCap) {
-    int at = incl - cnt;
+  int total = 0;
 #pragma unroll
-    for (int j = 0; j < kSamplePerLane; ++j) {
-      const uint64_t kj = key_of(j);
-      if (kj != 0 && kj >= tau) sc[at++] = kj;
-    }
+  for (int j = 0; j < kSamplePerLane; ++j) {
+    const bool is = ov[j] >= tau;
+    const uint64_t m = __ballot(is);
+    const int at = total + lanes_below(m);
+    if (is && at < kSampleCap) sc[at] = (static_cast<uint64_t>(ov[j]) << 32) | (0xFFFFFFFFu - idx_of(j));
+    total += __popcll(m);
+  }
+  uint64_t* out = cand + (static_cast<int64_t>(row) * n_chunks + c) * k;
+  int n_out = 0;
+  if (total <= kSampleCap) {
     __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // top k of the candidates, largest first: each lane holds slots lane,
-    // lane + 64, ... (up to 4)
+    // the k largest candidates: slots lane, lane + 64, ...
     uint64_t h[kSampleCap / kSampleLanes];
 #pragma unroll
     for (int s = 0; s < kSampleCap / kSampleLanes; ++s) {
-      const int at2 = lane + kSampleLanes * s;
-      h[s] = at2 < total ? sc[at2] : 0ull;
+      const int at = lane + kSampleLanes * s;
+      h[s] = at < total ? sc[at] : 0ull;
     }
-    for (int r = 0; r < k; ++r) {
-      uint64_t best = 0;
+    const uint64_t kth = wave_kth_largest(h, k);
 #pragma unroll
-      for (int s = 0; s < kSampleCap / kSampleLanes; ++s) best = h[s] > best ? h[s] : best;
-      const uint64_t m = wave_max_u64(best);
-      if (lane == 0) out[r] = m;
-#pragma unroll
-      for (int s = 0; s < kSampleCap / kSampleLanes; ++s)
-        if (h[s] == m) h[s] = 0;  // keys are unique: one slot of one lane
+    for (int s = 0; s < kSampleCap / kSampleLanes; ++s) {
+      const bool is = h[s] != 0 && h[s] >= kth;
+      const uint64_t m = __ballot(is);
+      if (is) out[n_out + lanes_below(m)] = h[s];
+      n_out += __popcll(m);
     }
   } else {
-    // more candidates than slots (many values tied near the bound): k rounds
-    // over the lane's own values, exact and slower
-    uint64_t lbest = lmax;
-    for (int r = 0; r < k; ++r) {
-      const uint64_t m = wave_max_u64(lbest);
-      if (lane == 0) out[r] = m;
-      if (lbest == m && m != 0) {  // this lane held it: drop it, rescan
-        uint64_t nb = 0;
+    // more candidates than slots (values tied near the bound): the same
+    // selection over every value's full key, computed again
+    uint64_t t = 0;
+    for (int bit = 63; bit >= 0; --bit) {
+      const uint64_t cb = t | (1ull << bit);
+      int cnt = 0;
 #pragma unroll
-        for (int j = 0; j < kSamplePerLane; ++j) {
-          const uint64_t kj = key_of(j);
-          if (kj < m && kj > nb) nb = kj;
-        }
-        lbest = nb;
+      for (int j = 0; j < kSamplePerLane; ++j) {
+        const uint64_t kj = ov[j] ? (static_cast<uint64_t>(ov[j]) << 32) | (0xFFFFFFFFu - idx_of(j)) : 0ull;
+        cnt += __popcll(__ballot(kj >= cb));
       }
+      if (cnt >= k) t = cb;
+    }
+#pragma unroll
+    for (int j = 0; j < kSamplePerLane; ++j) {
+      const uint64_t kj = ov[j] ? (static_cast<uint64_t>(ov[j]) << 32) | (0xFFFFFFFFu - idx_of(j)) : 0ull;
+      const bool is = kj != 0 && kj >= t;
+      const uint64_t m = __ballot(is);
+      if (is) out[n_out + lanes_below(m)] = kj;
+      n_out += __popcll(m);
     }
   }
+  for (int i = n_out + lane; i < k; i += kSampleLanes) out[i] = 0;  // a chunk with fewer than k values
 }
 
-// Pass 2: one workgroup per row: the row's top k over its chunks' candidates,
-// then the draw in one lane (float64).
-__global__ void __launch_bounds__(256) sample_pass2(const float* __restrict__ logits, int64_t row_stride,
-                                                    const uint64_t* __restrict__ cand, int n_cand, int k,
-                                                    const float* __restrict__ uniforms, int64_t uniform_stride,
-                                                    float temperature, float top_p, int32_t* __restrict__ out_idx) {
+// Pass 2: one wave per row: the row's top k over its chunks' candidates (the
+// same bound-and-compact scheme, streaming the candidates from the
+// workspace), sorted descending by rank, then the draw in one lane (float64).
+__global__ void __launch_bounds__(kSampleLanes) sample_pass2(const float* __restrict__ logits, int64_t row_stride,
+                                                             const uint64_t* __restrict__ cand, int n_cand, int k,
+                                                             const float* __restrict__ uniforms,
+                                                             int64_t uniform_stride, float temperature, float top_p,
+                                                             int32_t* __restrict__ out_idx) {
+  __shared__ uint64_t s_c[kSampleCap];
   __shared__ uint64_t s_top[kSampleMaxK];
-  __shared__ uint64_t s_wave[4];
   const int row = blockIdx.x;
-  const int lane = threadIdx.x % kSampleLanes;
-  const int wave = threadIdx.x / kSampleLanes;
+  const int lane = threadIdx.x;
   const uint64_t* cr = cand + static_cast<int64_t>(row) * n_cand;
-  // candidates held per thread (n_cand <= 256 * H)
-  constexpr int H = kSampleMaxCand / 256;
-  uint64_t h[H];
-#pragma unroll
-  for (int s = 0; s < H; ++s) {
-    const int at = static_cast<int>(threadIdx.x) + 256 * s;
-    h[s] = at < n_cand ? cr[at] : 0ull;
+  auto cand_at = [&](int at) -> uint64_t { return at < n_cand ? cr[at] : 0ull; };
+  uint64_t lmax[1] = {0};
+  for (int at = lane; at < n_cand; at += kSampleLanes) lmax[0] = cr[at] > lmax[0] ? cr[at] : lmax[0];
+  const uint64_t tau = wave_kth_largest(lmax, k);
+  int total = 0;
+  for (int base = 0; base < n_cand; base += kSampleLanes) {
+    const uint64_t v = cand_at(base + lane);
+    const bool is = v != 0 && v >= tau;
+    const uint64_t m = __ballot(is);
+    const int at = total + lanes_below(m);
+    if (is && at < kSampleCap) s_c[at] = v;
+    total += __popcll(m);
   }
-  for (int r = 0; r < k; ++r) {
-    uint64_t best = 0;
+  int n_w = 0;  // winners: the k largest keys (distinct, nonzero; the row has at least k values)
+  if (total <= kSampleCap) {
+    __builtin_amdgcn_wave_barrier();
+    uint64_t g[kSampleCap / kSampleLanes];
 #pragma unroll
-    for (int s = 0; s < H; ++s) best = h[s] > best ? h[s] : best;
-    const uint64_t wm = wave_max_u64(best);
-    if (lane == 0) s_wave[wave] = wm;
-    __syncthreads();
-    uint64_t m = s_wave[0];
+    for (int s = 0; s < kSampleCap / kSampleLanes; ++s) {
+      const int at = lane + kSampleLanes * s;
+      g[s] = at < total ? s_c[at] : 0ull;
+    }
+    const uint64_t kth = wave_kth_largest(g, k);
 #pragma unroll
-    for (int q = 1; q < 4; ++q) m = s_wave[q] > m ? s_wave[q] : m;
-    if (threadIdx.x == 0) s_top[r] = m;
-#pragma unroll
-    for (int s = 0; s < H; ++s)
-      if (h[s] == m) h[s] = 0;
-    __syncthreads();  // s_wave is rewritten next round
+    for (int s = 0; s < kSampleCap / kSampleLanes; ++s) {
+      const bool is = g[s] != 0 && g[s] >= kth;
+      const uint64_t m = __ballot(is);
+      if (is) s_top[n_w + lanes_below(m)] = g[s];
+      n_w += __popcll(m);
+    }
+  } else {
+    // more candidates than slots (values tied near the bound): the same
+    // bit-by-bit selection, counting over the streamed candidates
+    uint64_t t = 0;
+    for (int bit = 63; bit >= 0; --bit) {
+      const uint64_t cb = t | (1ull << bit);
+      int cnt = 0;
+      for (int base = 0; base < n_cand; base += kSampleLanes) cnt += __popcll(__ballot(cand_at(base + lane) >= cb));
+      if (cnt >= k) t = cb;
+    }
+    for (int base = 0; base < n_cand; base += kSampleLanes) {
+      const uint64_t v = cand_at(base + lane);
+      const bool is = v != 0 && v >= t;
+      const uint64_t m = __ballot(is);
+      if (is) s_top[n_w + lanes_below(m)] = v;
+      n_w += __popcll(m);
+    }
   }
-  if (threadIdx.x != 0) return;
+  __builtin_amdgcn_wave_barrier();
+  // sort the k winners descending: each lane's rank is the count of larger keys
+  const uint64_t mine = lane < k ? s_top[lane] : 0ull;
+  int rank = 0;
+  for (int j = 0; j < k; ++j) {
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(mine)), j));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(mine >> 32), j));
+    rank += ((static_cast<uint64_t>(hi) << 32) | lo) > mine ? 1 : 0;
+  }
+  __builtin_amdgcn_wave_barrier();
+  if (lane < k) s_top[rank] = mine;
+  __builtin_amdgcn_wave_barrier();
   const uint64_t k0 = s_top[0];
   const float x0 = key_value(k0);
   if (x0 != x0 || x0 == INFINITY || x0 == -INFINITY) {  // a non-finite top logit is the selection
-    out_idx[row] = static_cast<int32_t>(key_index(k0));
+    if (lane == 0) out_idx[row] = static_cast<int32_t>(key_index(k0));
     return;
   }
+  // exp(z_i - z_0) of the k winners, one per lane, then the running sums in
+  // descending order by one lane
+  __shared__ double s_e[kSampleMaxK];
   const float* __restrict__ xr = logits + static_cast<int64_t>(row) * row_stride;
   const double T = static_cast<double>(temperature);
   const double z0 = static_cast<double>(xr[key_index(k0)]) / T;
-  auto e = [&](int i) { return exp(static_cast<double>(xr[key_index(s_top[i])]) / T - z0); };
-  // running sums in descending order (recomputed per pass, identically)
+  if (lane < k) s_e[lane] = exp(static_cast<double>(xr[key_index(s_top[lane])]) / T - z0);
+  __builtin_amdgcn_wave_barrier();
+  if (lane != 0) return;
   double acc = 0.0;
-  for (int i = 0; i < k; ++i) acc += e(i);
+  for (int i = 0; i < k; ++i) acc += s_e[i];
   const double P = static_cast<double>(top_p);
   int i_star = k - 1;
   double c_star = acc;
   double c = 0.0;
   for (int i = 0; i < k; ++i) {
-    c += e(i);
+    c += s_e[i];
     if (c / acc >= P) {
       i_star = i;
       c_star = c;
@@ -241,7 +291,7 @@ __global__ void __launch_bounds__(256) sample_pass2(const float* __restrict__ lo
   int pick = i_star;
   c = 0.0;
   for (int i = 0; i <= i_star; ++i) {
-    c += e(i);
+    c += s_e[i];
     if (c / acc > target) {
       pick = i;
       break;
@@ -299,7 +349,7 @@ extern "C" ttv_status vocab_sample(const float* logits, int64_t n_rows, int64_t 
                      dim3(kSampleLanes * kSampleWaves), 0, s, logits, vocab, row_stride, n_chunks, k, vec, cand);
   ttv_status st = check_launch("vocab_sample pass 1");
   if (st != TTV_OK) return st;
-  hipLaunchKernelGGL(sample_pass2, dim3(static_cast<unsigned>(n_rows)), dim3(256), 0, s, logits, row_stride,
+  hipLaunchKernelGGL(sample_pass2, dim3(static_cast<unsigned>(n_rows)), dim3(kSampleLanes), 0, s, logits, row_stride,
                      static_cast<const uint64_t*>(cand), static_cast<int>(n_cand), k, uniforms, uniform_stride,
                      temperature, top_p, out_idx);
   return check_launch("vocab_sample pass 2");
