@@ -15,9 +15,11 @@
 // the chunk's k-th largest value from below (k lanes hold a value at least
 // that large), so only values at or above it are candidates; they are
 // compacted into LDS (rarely more than a few dozen) and the top k taken there.
-// Keys are 64-bit (ordered value << 32 | ~index), unique per element. Pass 2
-// takes each row's top k from the chunks' candidates and makes the draw in
-// one lane, in float64.
+// Keys are 64-bit (ordered value << 32 | ~index), unique per element;
+// selections run bit by bit on ballots and popcounts, with no lane shuffles.
+// Pass 2 takes each row's top k from the chunks' candidates with one wave and
+// makes the draw in float64: the exponentials one per lane, the running sums
+// in descending order in one lane, the prefix and draw tests by ballot.
 #include "common.hpp"
 
 namespace ttv {
@@ -135,6 +137,7 @@ __global__ void __launch_bounds__(kSampleLanes * kSampleWaves)
   for (int j = 0; j < kSamplePerLane; ++j) {
     const bool is = ov[j] >= tau;
     const uint64_t m = __ballot(is);
+    if (m == 0) continue;  // (most steps: candidates are few)
     const int at = total + lanes_below(m);
     if (is && at < kSampleCap) sc[at] = (static_cast<uint64_t>(ov[j]) << 32) | (0xFFFFFFFFu - idx_of(j));
     total += __popcll(m);
@@ -186,7 +189,7 @@ __global__ void __launch_bounds__(kSampleLanes * kSampleWaves)
 
 // Pass 2: one wave per row: the row's top k over its chunks' candidates (the
 // same bound-and-compact scheme, streaming the candidates from the
-// workspace), sorted descending by rank, then the draw in one lane (float64).
+// workspace), sorted descending by rank, then the draw (float64).
 __global__ void __launch_bounds__(kSampleLanes) sample_pass2(const float* __restrict__ logits, int64_t row_stride,
                                                              const uint64_t* __restrict__ cand, int n_cand, int k,
                                                              const float* __restrict__ uniforms,
@@ -198,17 +201,49 @@ __global__ void __launch_bounds__(kSampleLanes) sample_pass2(const float* __rest
   const int lane = threadIdx.x;
   const uint64_t* cr = cand + static_cast<int64_t>(row) * n_cand;
   auto cand_at = [&](int at) -> uint64_t { return at < n_cand ? cr[at] : 0ull; };
+  // up to 64 * kRegCand candidates are held in registers (all loads in
+  // flight at once); more are streamed, eight loads a step
+  constexpr int kRegCand = 32;
   uint64_t lmax[1] = {0};
-  for (int at = lane; at < n_cand; at += kSampleLanes) lmax[0] = cr[at] > lmax[0] ? cr[at] : lmax[0];
-  const uint64_t tau = wave_kth_largest(lmax, k);
   int total = 0;
-  for (int base = 0; base < n_cand; base += kSampleLanes) {
-    const uint64_t v = cand_at(base + lane);
-    const bool is = v != 0 && v >= tau;
-    const uint64_t m = __ballot(is);
-    const int at = total + lanes_below(m);
-    if (is && at < kSampleCap) s_c[at] = v;
-    total += __popcll(m);
+  uint64_t tau;
+  if (n_cand <= kSampleLanes * kRegCand) {
+    uint64_t v[kRegCand];
+#pragma unroll
+    for (int u = 0; u < kRegCand; ++u) v[u] = cand_at(u * kSampleLanes + lane);
+#pragma unroll
+    for (int u = 0; u < kRegCand; ++u) lmax[0] = v[u] > lmax[0] ? v[u] : lmax[0];
+    tau = wave_kth_largest(lmax, k);
+#pragma unroll
+    for (int u = 0; u < kRegCand; ++u) {
+      const bool is = v[u] != 0 && v[u] >= tau;
+      const uint64_t m = __ballot(is);
+      const int at = total + lanes_below(m);
+      if (is && at < kSampleCap) s_c[at] = v[u];
+      total += __popcll(m);
+    }
+  } else {
+    for (int base = 0; base < n_cand; base += 8 * kSampleLanes) {
+      uint64_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = cand_at(base + u * kSampleLanes + lane);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) lmax[0] = v[u] > lmax[0] ? v[u] : lmax[0];
+    }
+    tau = wave_kth_largest(lmax, k);
+    for (int base = 0; base < n_cand; base += 8 * kSampleLanes) {
+      uint64_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = cand_at(base + u * kSampleLanes + lane);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const bool is = v[u] != 0 && v[u] >= tau;
+        const uint64_t m = __ballot(is);
+        const int at = total + lanes_below(m);
+        if (is && at < kSampleCap) s_c[at] = v[u];
+        total += __popcll(m);
+      }
+    }
   }
   int n_w = 0;  // winners: the k largest keys (distinct, nonzero; the row has at least k values)
   if (total <= kSampleCap) {
@@ -271,33 +306,24 @@ __global__ void __launch_bounds__(kSampleLanes) sample_pass2(const float* __rest
   const double z0 = static_cast<double>(xr[key_index(k0)]) / T;
   if (lane < k) s_e[lane] = exp(static_cast<double>(xr[key_index(s_top[lane])]) / T - z0);
   __builtin_amdgcn_wave_barrier();
-  if (lane != 0) return;
-  double acc = 0.0;
-  for (int i = 0; i < k; ++i) acc += s_e[i];
-  const double P = static_cast<double>(top_p);
-  int i_star = k - 1;
-  double c_star = acc;
-  double c = 0.0;
-  for (int i = 0; i < k; ++i) {
-    c += s_e[i];
-    if (c / acc >= P) {
-      i_star = i;
-      c_star = c;
-      break;
+  if (lane == 0) {  // the running sums, in descending order
+    double acc = 0.0;
+    for (int i = 0; i < k; ++i) {
+      acc += s_e[i];
+      s_e[i] = acc;
     }
   }
-  const double u = static_cast<double>(uniforms[static_cast<int64_t>(row) * uniform_stride]);
-  const double target = u * (c_star / acc);
-  int pick = i_star;
-  c = 0.0;
-  for (int i = 0; i <= i_star; ++i) {
-    c += s_e[i];
-    if (c / acc > target) {
-      pick = i;
-      break;
-    }
-  }
-  out_idx[row] = static_cast<int32_t>(key_index(s_top[pick]));
+  __builtin_amdgcn_wave_barrier();
+  // C_i = c_i / c_{k-1} on lane i; the prefix end i* and the draw by ballots
+  const double acc = s_e[k - 1];
+  const double C = lane < k ? s_e[lane] / acc : 2.0;
+  const uint64_t reach = __ballot(lane < k && C >= static_cast<double>(top_p));
+  const int i_star = reach ? __builtin_ctzll(reach) : k - 1;
+  const double c_star = __shfl(C, i_star);
+  const double target = static_cast<double>(uniforms[static_cast<int64_t>(row) * uniform_stride]) * c_star;
+  const uint64_t past = __ballot(lane <= i_star && C > target);
+  const int pick = past ? __builtin_ctzll(past) : i_star;
+  if (lane == 0) out_idx[row] = static_cast<int32_t>(key_index(s_top[pick]));
 }
 
 static int sample_chunks(int64_t vocab) { return static_cast<int>((vocab + kSampleChunk - 1) / kSampleChunk); }
