@@ -30,6 +30,7 @@ __all__ = [
     "ancestor_bits",
     "node_depths",
     "additive_mask_with_history",
+    "sliding_mask_from_caller",
     "visible_keys",
     "attention_rows",
     "tree_verify_attention",
@@ -140,6 +141,26 @@ def additive_mask_with_history(parent, offset: int, masked: float = MASKED) -> n
     return m
 
 
+def sliding_mask_from_caller(caller, offset: int, window: int, masked: float = MASKED) -> np.ndarray:
+    """The sliding-window layers' mask ([PR1212] the commit intersecting the
+    caller mask with the sliding band, and the commit that pulls it into
+    sliding_mask_from_caller): the caller's [T, offset + T] additive mask
+    intersected (elementwise minimum) with the band that lets query row q,
+    at position offset + q, see column c only when offset + q - window < c
+    <= offset + q. The pages apply the band only where the two can disagree
+    (sliding live length + block length > window); below that the caller
+    mask comes back untouched, which the minimum also gives, since the band
+    is then all open."""
+    caller = np.asarray(caller, dtype=np.float32)
+    T, S = caller.shape
+    if offset + T <= window:
+        return caller.copy()
+    q = np.arange(T)[:, None] + offset
+    c = np.arange(S)[None, :]
+    band = np.where((c > q - window) & (c <= q), np.float32(0.0), np.float32(masked)).astype(np.float32)
+    return np.minimum(caller, band)
+
+
 # ----------------------------------------------------------------------------
 # Step 2: tree-masked GQA verify attention.
 # ----------------------------------------------------------------------------
@@ -166,7 +187,7 @@ def attention_rows(qrows, K, V, keys, softmax_scale: float) -> np.ndarray:
 
 
 def tree_verify_attention(q, layer: dict, node_off, hist_len, parents, softmax_scale: float,
-                          q_dtype: str, kv_dtype: str) -> np.ndarray:
+                          q_dtype: str, kv_dtype: str, window: int = 0) -> np.ndarray:
     """Explicit key-set form, batched over sequences ([I1204] "Redirection":
     the nodes are flattened into one sequence and the tree mask hides
     siblings; [PR1212] history-mask commit: full history plus ancestors).
@@ -174,7 +195,9 @@ def tree_verify_attention(q, layer: dict, node_off, hist_len, parents, softmax_s
     q: [n_nodes, Hq, D] (float32 or bf16 bits); layer: {'k','v'[, 'k_scale',
     'v_scale']} with [B, Hkv, cap, D] caches; parents: per-sequence parent
     arrays, or None for the causal (linear) reading. GQA: query head h reads
-    KV head h // (Hq / Hkv). Returns float64 [n_nodes, Hq, D]."""
+    KV head h // (Hq / Hkv). window > 0: the sliding-window layers' form,
+    node i (cache row P + i) keeping only keys c > P + i - window (see
+    sliding_mask_from_caller). Returns float64 [n_nodes, Hq, D]."""
     qf = np.asarray(q, dtype=np.float64) if q_dtype == "f32" else decode_bf16(q)
     n, Hq, D = qf.shape
     Hkv = layer["k"].shape[1]
@@ -194,6 +217,8 @@ def tree_verify_attention(q, layer: dict, node_off, hist_len, parents, softmax_s
             V = decode_kv(layer["v"][b, g, : P + T], kv_dtype, None if kv_dtype != "i8" else layer["v_scale"][b, g, : P + T])
             for i in range(T):
                 keys = visible_keys(P, sets[i])
+                if window > 0:
+                    keys = keys[keys > P + i - window]
                 out[o0 + i, g * G:(g + 1) * G] = attention_rows(qf[o0 + i, g * G:(g + 1) * G], K, V, keys, softmax_scale)
     return out
 

@@ -666,3 +666,54 @@ def test_sampled_walk_commits_the_samples():
     assert emitted == [int(tgt[n]) for n in path]
     for a, b in zip(path, path[1:]):
         assert parent[b] == a and token[b] == tgt[a]
+
+
+# ---------------------------------------------------------------------------
+# sliding window: caller mask intersected with the band
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(6))
+def test_sliding_mask_properties(seed):
+    """The three properties the pages state for sliding_mask_from_caller."""
+    r = np.random.default_rng(800 + seed)
+    T = int(r.integers(1, 20))
+    parent = random_tree(r, T)
+    offset = int(r.integers(0, 60))
+    caller = O.additive_mask_with_history(parent, offset)
+    # below the window the caller mask comes back untouched
+    W_big = offset + T + int(r.integers(0, 5))
+    assert np.array_equal(O.sliding_mask_from_caller(caller, offset, W_big), caller)
+    # past the window an all-attend caller mask reduces to the band
+    W = int(r.integers(1, offset + T)) if offset + T > 1 else 1
+    allow = np.zeros_like(caller)
+    band = O.sliding_mask_from_caller(allow, offset, W)
+    for q in range(T):
+        for c in range(offset + T):
+            want = 0.0 if (offset + q - W < c <= offset + q) else MASKED
+            assert band[q, c] == np.float32(want)
+    # a mask that already carries the band is unchanged by intersecting again
+    once = O.sliding_mask_from_caller(caller, offset, W)
+    assert np.array_equal(O.sliding_mask_from_caller(once, offset, W), once)
+    # every row keeps its own position
+    for q in range(T):
+        assert once[q, offset + q] == 0.0
+
+
+@pytest.mark.parametrize("seed,window", [(0, 5), (1, 40), (2, 70), (3, 1), (4, 200)])
+def test_sliding_attention_explicit_equals_dense_band(seed, window):
+    """The explicit key-set form with a window equals the dense form under
+    the intersected mask (two independent routes to the same set)."""
+    r = np.random.default_rng(820 + seed)
+    T, P, Hq, Hkv, D = 12, 64, 4, 2, 16
+    parent = random_tree(r, T)
+    K = r.standard_normal((1, Hkv, P + T, D)).astype(np.float32)
+    V = r.standard_normal((1, Hkv, P + T, D)).astype(np.float32)
+    q = r.standard_normal((T, Hq, D)).astype(np.float32)
+    got = O.tree_verify_attention(q, {"k": K, "v": V}, [0, T], [P], [parent], 0.25, "f32", "f32", window=window)
+    mask = O.sliding_mask_from_caller(O.additive_mask_with_history(parent, P), P, window)
+    want = O.tree_verify_attention_dense(q.astype(np.float64), K[0].astype(np.float64), V[0].astype(np.float64),
+                                         mask, 0.25, Hq // Hkv)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+    if window >= P + T:
+        full = O.tree_verify_attention(q, {"k": K, "v": V}, [0, T], [P], [parent], 0.25, "f32", "f32")
+        assert np.array_equal(got, full)
