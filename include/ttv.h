@@ -11,6 +11,9 @@
  *   tree_accept_walk     descend the one child matching the target's argmax
  *   kv_gather_positions  compact the accepted path's K/V (and int8 scales)
  *                        along the sequence axis
+ * and the sliding-window layers' variants: sliding_mask_from_caller (caller
+ * mask intersected with the window band) and kv_gather_within_tail (the
+ * rollback confined to the verify block, refusing a wrapped rotating cache).
  *
  * Sources are cited by page title and section:
  *   [I1204]  mlxcel issue #1204 "perf(speculative): draft a tree instead of a
@@ -126,6 +129,23 @@ ttv_status tree_build_mask(const ttv_batch* batch, const int32_t* parent, uint64
  */
 ttv_status tree_mask_expand_additive(const ttv_batch* batch, int32_t b, const uint64_t* anc,
                                      float masked, float* out, void* stream);
+
+/*
+ * Sliding-window layers' form of step 1 [PR1212] the commit intersecting the
+ * caller mask with the sliding band and the commit stating its properties.
+ * Query row q of caller[T][S] (float32, row-major, device) sits at cache
+ * position offset + q; the band keeps column c iff
+ * offset + q - window < c <= offset + q. Past the window (offset + T > window)
+ *   out[q][c] = min(caller[q][c], band ? 0 : masked)   (a NaN propagates)
+ * and below it (offset + T <= window) out is caller, untouched, as the pages'
+ * guard leaves it. Properties: an all-open caller past the window gives the
+ * band; applying the call to its own output changes nothing.
+ *   caller (device) float32 [T][S]; out (device) float32 [T][S], may be caller
+ *          itself (in place) but must not overlap it otherwise.
+ * Requires window >= 1, T <= 65535, offset >= 0.
+ */
+ttv_status sliding_mask_from_caller(const float* caller, int32_t T, int32_t S, int32_t offset, int32_t window,
+                                    float masked, float* out, void* stream);
 
 /*
  * Step 2 -- tree-masked GQA verify attention [I1204] "Redirection" (flatten the
@@ -258,6 +278,54 @@ ttv_status kv_gather_positions(const ttv_kv_layer* src, const ttv_kv_layer* dst,
  * TTV_ERR_UNSUPPORTED (or TTV_ERR_INVALID) with the reason in ttv_last_error().
  */
 ttv_status kv_can_gather(const ttv_kv_layer* layers, int32_t n_layers);
+
+/*
+ * Tail form of step 5 for one verify block per sequence [PR1212] the
+ * gather_within_tail commit (rewrite only the block's part of the window, so
+ * the cost follows the block, not the context; the rotating form needs an
+ * unwrapped ring and refuses by name once it has wrapped) and the commit
+ * making the tail question "is it still in logical order". In place, for every
+ * layer l, sequence b, head h and j < kept_len[b], with s = live_len_h[b] -
+ * tail_len_h[b]:
+ *   k[b][h][s + j] = k[b][h][s + kept[b][j]], likewise v and, for I8, the
+ *   k_scale/v_scale sidecars.
+ * The result equals kv_gather_positions in place with the absolute selection
+ * [0, s) ++ (s + kept[b]); rows before the first j with kept[j] != j and rows
+ * at and beyond s + kept_len[b] are not written; the new live length is
+ * s + kept_len[b].
+ *   layers      (host) n_layers descriptors (same shape and dtype).
+ *   kept        (device) int32 [B][kept_stride], offsets inside the tail,
+ *               strictly increasing, each in [0, tail_len_h[b]).
+ *   kept_len    (device) int32 [B], 0 <= kept_len[b] <= tail_len_h[b].
+ *   live_len_h  (host) int32 [B], current live rows (<= cap).
+ *   tail_len_h  (host) int32 [B], the verify block's rows at the end of the
+ *               live window, 0 <= tail_len <= min(live_len, 64).
+ *   ring_wrapped_h (host) int32 [B] or NULL: nonzero when sequence b's cache
+ *               is a rotating (sliding-window) ring that has wrapped, whose
+ *               rows are then no longer in logical order; the call returns
+ *               TTV_ERR_UNSUPPORTED naming the sequence and writes nothing.
+ *               NULL: every cache keeps its rows in logical order (a linear
+ *               cache, or a ring in the buffered regime that compacts from the
+ *               front instead of wrapping).
+ * All-or-nothing: a malformed kept/kept_len in any sequence stores
+ * TTV_DEV_BAD_SELECTION and no buffer is written.
+ * ws: >= kv_gather_within_tail_ws(B) bytes.
+ */
+size_t kv_gather_within_tail_ws(int32_t B);
+ttv_status kv_gather_within_tail(const ttv_kv_layer* layers, int32_t n_layers, int32_t B, const int32_t* kept,
+                                 int32_t kept_stride, const int32_t* kept_len, const int32_t* live_len_h,
+                                 const int32_t* tail_len_h, const int32_t* ring_wrapped_h, int32_t* dev_status,
+                                 void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Capability question for the tail form, answered from cache state (the
+ * answer can change between rounds: a ring that wraps stops being gatherable)
+ * [PR1212] the verify_finalize_tree and tree_round_is_available commits:
+ * kv_can_gather(layers) and no sequence's ring wrapped. ring_wrapped_h as in
+ * kv_gather_within_tail.
+ */
+ttv_status kv_can_gather_within_tail(const ttv_kv_layer* layers, int32_t n_layers, int32_t B,
+                                     const int32_t* ring_wrapped_h);
 
 /* Reason for the last non-OK status returned on this thread ("" if none). */
 const char* ttv_last_error(void);

@@ -41,6 +41,7 @@ __all__ = [
     "rollback_selection",
     "gather_positions",
     "gather_layer",
+    "gather_within_tail",
     "verify_round",
 ]
 
@@ -379,6 +380,24 @@ def gather_layer(layer: dict, sels, base: dict | None = None) -> dict:
                 out[name][b, :, :n] = gather_positions(layer[name][b], sel, axis=1)
             else:
                 out[name][b, :, :n, :] = gather_positions(layer[name][b], sel, axis=1)
+    return out
+
+
+def gather_within_tail(layer: dict, live_len, tail_len, kept) -> dict:
+    """Rollback confined to the verify block ([PR1212] gather_within_tail
+    commit: offsets within the block, only [tail_start, tail_start +
+    kept_len) is rewritten, so the cost follows the block and not the
+    context). For sequence b, s = live_len[b] - tail_len[b] and row s + j
+    takes row s + kept[b][j] of the input, j < len(kept[b]), in every
+    sequence-axis buffer (K, V and the int8 scale sidecars); every other row
+    is left as it was. The new live length is s + len(kept[b])."""
+    out = {name: np.array(layer[name], copy=True) for name in layer}
+    for b, kb in enumerate(kept):
+        s = int(live_len[b]) - int(tail_len[b])
+        src = s + np.asarray(kb, dtype=np.int64)
+        dst = s + np.arange(len(src), dtype=np.int64)
+        for name in layer:
+            out[name][b, :, dst] = layer[name][b, :, src]
     return out
 
 

@@ -1,0 +1,223 @@
+"""GPU parity of the sliding-window layers' variants against the CPU oracle:
+the caller mask intersected with the window band (bit-exact float32) and the
+rollback confined to the verify block, including the refusal of a wrapped
+rotating cache (bit-exact bytes)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from workloads import make_kv_cache, random_tree, rng_for
+
+from gpu_util import layer_to_dev, layer_to_host, log, status, to_dev, to_host, zeros_ws
+
+pytestmark = pytest.mark.gpu
+
+MASKED = np.float32(-1e9)
+
+
+@pytest.fixture(scope="module")
+def ttv():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from gpu_util import binding
+    return binding()
+
+
+# ------------------------------------------------------------ band mask ----
+
+def _band(ttv, caller, offset, window, in_place=False):
+    c = to_dev(np.ascontiguousarray(caller, np.float32))
+    out = c if in_place else torch.full_like(c, 7.0)
+    ttv.sliding_mask_from_caller(c, offset, window, float(MASKED), out)
+    return to_host(out)
+
+
+@pytest.mark.parametrize("T,offset", [(1, 0), (7, 3), (16, 100), (64, 1000), (33, 4097)])
+def test_band_of_tree_mask_matches_oracle(ttv, T, offset):
+    parent = random_tree(rng_for(1500, T), T)
+    caller = O.additive_mask_with_history(parent, offset)
+    for window in sorted({1, 2, max(1, (offset + T) // 2), offset + T - 1 if offset + T > 1 else 1, offset + T,
+                          offset + T + 9, 1024}):
+        want = O.sliding_mask_from_caller(caller, offset, window)
+        for in_place in (False, True):
+            got = _band(ttv, caller, offset, window, in_place)
+            np.testing.assert_array_equal(got, want, err_msg=f"T={T} P={offset} W={window} in_place={in_place}")
+    log(f"band: T={T} offset={offset} ok")
+
+
+def test_band_general_caller_values(ttv):
+    """Arbitrary float callers (positive entries, NaN, the masked value itself,
+    more columns than offset + T) and the pages' three properties on device."""
+    r = rng_for(1510)
+    T, offset = 40, 700
+    S = offset + T + 37
+    caller = (r.standard_normal((T, S)) * 3).astype(np.float32)
+    caller[3, 690] = np.nan
+    caller[5, :100] = MASKED
+    caller[9, 720] = np.inf
+    for window in (1, 17, 256, 739, 740, 741, 5000):
+        want = O.sliding_mask_from_caller(caller, offset, window)
+        np.testing.assert_array_equal(_band(ttv, caller, offset, window), want, err_msg=f"W={window}")
+    W = 256
+    allow = np.zeros((T, offset + T), np.float32)
+    band = _band(ttv, allow, offset, W)
+    q = np.arange(T)[:, None] + offset
+    c = np.arange(offset + T)[None, :]
+    np.testing.assert_array_equal(band, np.where((c > q - W) & (c <= q), 0.0, MASKED).astype(np.float32))
+    once = _band(ttv, caller, offset, W)
+    np.testing.assert_array_equal(_band(ttv, once, offset, W), once)
+    # below the window: untouched, also in place (nothing launches then)
+    np.testing.assert_array_equal(_band(ttv, caller, offset, offset + T), caller)
+    np.testing.assert_array_equal(_band(ttv, caller, offset, offset + T, in_place=True), caller)
+
+
+def test_band_expand_then_intersect_in_place(ttv):
+    """The tree mask expanded on device, then intersected in place: equals the
+    oracle's sliding form of the history mask, for every sequence of a batch."""
+    parents = [random_tree(rng_for(1520, s), n) for s, n in enumerate((5, 64, 17, 1))]
+    hist = np.array([1030, 0, 2000, 40], np.int32)
+    node_off = np.zeros(len(parents) + 1, np.int32)
+    node_off[1:] = np.cumsum([len(p) for p in parents])
+    batch = ttv.Batch(node_off, hist)
+    anc = to_dev(np.concatenate([O.ancestor_bits(p) for p in parents]))
+    for b, par in enumerate(parents):
+        T, P = len(par), int(hist[b])
+        out = torch.empty(T, P + T, dtype=torch.float32, device="cuda")
+        ttv.tree_mask_expand_additive(batch, b, anc, float(MASKED), out)
+        ttv.sliding_mask_from_caller(out, P, 1024, float(MASKED), out)
+        want = O.sliding_mask_from_caller(O.additive_mask_with_history(par, P), P, 1024)
+        np.testing.assert_array_equal(to_host(out), want, err_msg=f"sequence {b}")
+
+
+# ----------------------------------------------------------- tail gather ----
+
+def _tail_case(ttv, dtype, D, kept, live, tails, L=2, H=2, cap=200, seed=0, wrapped=None):
+    B = len(kept)
+    host = [make_kv_cache(1530 + seed, l, B, H, cap, D, dtype, unique_scales=dtype == "i8") for l in range(L)]
+    devs, layers = zip(*[layer_to_dev(ttv, h) for h in host])
+    stride = 64 + 3
+    kp = np.full((B, stride), -1, np.int32)
+    for b, k in enumerate(kept):
+        kp[b, :len(k)] = k
+    kl = np.array([len(k) for k in kept], np.int32)
+    st = status()
+    err = None
+    try:
+        ttv.kv_gather_within_tail(list(layers), to_dev(kp), to_dev(kl), np.asarray(live, np.int32),
+                                  np.asarray(tails, np.int32), st, zeros_ws(ttv.kv_gather_within_tail_ws(B)),
+                                  ring_wrapped=wrapped)
+    except ttv.TTVError as e:
+        err = e
+    torch.cuda.synchronize()
+    return host, [layer_to_host(d) for d in devs], int(st.item()), err
+
+
+def _kept_sets(r, tails, kind):
+    out = []
+    for t in tails:
+        if kind == "random":
+            out.append(np.sort(r.choice(t, size=int(r.integers(0, t + 1)), replace=False)))
+        elif kind == "path":      # a root-first accepted path: 0 then increasing labels
+            rest = r.choice(np.arange(1, t), size=int(r.integers(0, min(t - 1, 9) + 1)), replace=False) if t > 1 else []
+            out.append(np.array([0] + sorted(int(x) for x in rest), np.int64) if t else np.zeros(0, np.int64))
+        elif kind == "prefix":
+            out.append(np.arange(int(r.integers(0, t + 1))))
+        elif kind == "full":
+            out.append(np.arange(t))
+        elif kind == "last":      # only the block's last row survives
+            out.append(np.array([t - 1]) if t else np.zeros(0, np.int64))
+    return out
+
+
+@pytest.mark.parametrize("dtype,D", [("i8", 64), ("i8", 128), ("bf16", 128), ("f32", 64), ("f32", 256)])
+@pytest.mark.parametrize("kind", ["random", "path", "prefix", "full", "last"])
+def test_tail_gather_matches_oracle(ttv, dtype, D, kind):
+    r = rng_for(1540, hash((dtype, D, kind)) % 1000)
+    live = [200, 150, 64, 7, 120]
+    tails = [16, 64, 64, 7, 0]
+    kept = _kept_sets(r, tails, kind)
+    log(f"tail gather: {dtype} D={D} {kind}")
+    host, got, st, err = _tail_case(ttv, dtype, D, kept, live, tails)
+    assert err is None and st == 0
+    for l in range(len(host)):
+        want = O.gather_within_tail(host[l], live, tails, kept)
+        for n in want:
+            np.testing.assert_array_equal(got[l][n], want[n], err_msg=f"layer {l} {n}")
+
+
+def test_tail_gather_many_layers_and_sequences(ttv):
+    """18 layers (two launches of 16 layers at most) over 128 sequences."""
+    r = rng_for(1550)
+    B = 128
+    live = [int(x) for x in r.integers(64, 100, size=B)]
+    tails = [int(x) for x in r.integers(0, 65, size=B)]
+    kept = _kept_sets(r, tails, "random")
+    host, got, st, err = _tail_case(ttv, "i8", 64, kept, live, tails, L=18, H=1, cap=100, seed=1)
+    assert err is None and st == 0
+    for l in range(18):
+        want = O.gather_within_tail(host[l], live, tails, kept)
+        for n in want:
+            np.testing.assert_array_equal(got[l][n], want[n], err_msg=f"layer {l} {n}")
+
+
+def test_tail_gather_equals_absolute_gather(ttv):
+    """The same rollback said in absolute positions through kv_gather_positions
+    gives the same bytes."""
+    r = rng_for(1560)
+    live, tails = [200, 180, 90], [33, 64, 5]
+    kept = _kept_sets(r, tails, "path")
+    host, got, st, err = _tail_case(ttv, "bf16", 128, kept, live, tails, seed=2)
+    assert err is None and st == 0
+    sels = [np.concatenate([np.arange(lv - t), lv - t + np.asarray(k, np.int64)]) for lv, t, k in zip(live, tails, kept)]
+    devs, layers = zip(*[layer_to_dev(ttv, h) for h in host])
+    sel = np.full((3, 201), -1, np.int32)
+    for b, s in enumerate(sels):
+        sel[b, :len(s)] = s
+    st2 = status()
+    ttv.kv_gather_positions(list(layers), None, to_dev(sel), to_dev(np.array([len(s) for s in sels], np.int32)),
+                            np.asarray(live, np.int32), st2, zeros_ws(ttv.kv_gather_positions_ws(3)))
+    torch.cuda.synchronize()
+    assert int(st2.item()) == 0
+    for l, d in enumerate(devs):
+        absolute = layer_to_host(d)
+        for n in absolute:
+            np.testing.assert_array_equal(got[l][n], absolute[n], err_msg=f"layer {l} {n}")
+
+
+def test_tail_gather_bad_kept_writes_nothing(ttv):
+    r = rng_for(1570)
+    live, tails = [200, 150, 64], [16, 20, 64]
+    for bad_case in range(4):
+        kept = _kept_sets(r, tails, "path")
+        if bad_case == 0:
+            kept[1] = np.array([0, 5, 5])                  # not strictly increasing
+        elif bad_case == 1:
+            kept[2] = np.array([0, 64])                    # outside the tail
+        elif bad_case == 2:
+            kept[0] = np.array([-1, 3])                    # negative
+        else:
+            kept[1] = np.arange(21)                        # longer than the tail
+        host, got, st, err = _tail_case(ttv, "i8", 64, kept, live, tails, seed=3)
+        assert err is None and st == ttv.TTV_DEV_BAD_SELECTION, bad_case
+        for l in range(len(host)):
+            for n in host[l]:
+                np.testing.assert_array_equal(got[l][n], host[l][n], err_msg=f"case {bad_case} layer {l} {n}")
+
+
+def test_tail_gather_refuses_wrapped_ring(ttv):
+    r = rng_for(1580)
+    live, tails = [200, 150], [16, 16]
+    kept = _kept_sets(r, tails, "path")
+    host, got, st, err = _tail_case(ttv, "bf16", 64, kept, live, tails, seed=4, wrapped=[0, 1])
+    assert err is not None and err.status == ttv.TTV_ERR_UNSUPPORTED and "wrapped" in str(err)
+    assert st == 0
+    for l in range(len(host)):
+        for n in host[l]:
+            np.testing.assert_array_equal(got[l][n], host[l][n])
+    # an unwrapped (buffered) ring is gathered as usual
+    host, got, st, err = _tail_case(ttv, "bf16", 64, kept, live, tails, seed=4, wrapped=[0, 0])
+    assert err is None and st == 0
+    want = O.gather_within_tail(host[0], live, tails, kept)
+    for n in want:
+        np.testing.assert_array_equal(got[0][n], want[n])

@@ -187,3 +187,57 @@ def test_gather_validation():
     assert _gather([i8], None) == ttv.TTV_ERR_UNSUPPORTED
     # j0 and bad per sequence, plus a partial pair per validation chunk (at most 64)
     assert ttv.kv_gather_positions_ws(8) == 8 * (2 + 2 * 64) * 4
+
+
+def test_sliding_mask_validation():
+    f = C["sliding_mask_from_caller"]
+    assert f(FAKE, 4, 10, 6, 0, -1e9, FAKE + (1 << 20), None) == ttv.TTV_ERR_INVALID   # window 0
+    assert "window" in ttv.last_error()
+    assert f(FAKE, -1, 10, 6, 4, -1e9, FAKE + (1 << 20), None) == ttv.TTV_ERR_INVALID
+    assert f(FAKE, 4, 10, -6, 4, -1e9, FAKE + (1 << 20), None) == ttv.TTV_ERR_INVALID
+    assert f(FAKE, 70000, 10, 6, 4, -1e9, FAKE + (1 << 24), None) == ttv.TTV_ERR_INVALID
+    assert f(FAKE, 4, 10, 0x7FFFFFFF - 2, 4, -1e9, FAKE + (1 << 20), None) == ttv.TTV_ERR_INVALID
+    assert f(None, 4, 10, 6, 4, -1e9, FAKE, None) == ttv.TTV_ERR_INVALID
+    # out starting inside caller: partial overlap is refused, exact aliasing is not checked here
+    assert f(FAKE, 4, 10, 6, 4, -1e9, FAKE + 8, None) == ttv.TTV_ERR_INVALID
+    assert "overlap" in ttv.last_error()
+    # empty shapes are a no-op
+    assert f(None, 0, 10, 6, 4, -1e9, None, None) == ttv.TTV_OK
+    assert f(None, 3, 0, 6, 4, -1e9, None, None) == ttv.TTV_OK
+
+
+def _tail(layers, B=2, live=(100, 100), tail=(16, 16), wrapped=None, ws=1 << 20, stride=64):
+    live = np.asarray(live, np.int32)
+    tail = np.asarray(tail, np.int32)
+    w = None if wrapped is None else np.asarray(wrapped, np.int32)
+    return C["kv_gather_within_tail"]((ttv.TtvKvLayer * len(layers))(*layers), len(layers), B, FAKE, stride, FAKE,
+                                      live.ctypes.data, tail.ctypes.data, None if w is None else w.ctypes.data, FAKE,
+                                      FAKE, ws, None)
+
+
+def test_tail_gather_validation_and_ring_refusal():
+    L = [layer(cap=128)]
+    # a wrapped rotating cache is refused by name before anything launches
+    assert _tail(L, wrapped=(0, 1)) == ttv.TTV_ERR_UNSUPPORTED
+    assert "sequence 1 has wrapped" in ttv.last_error()
+    arr = (ttv.TtvKvLayer * 1)(*L)
+    w = np.array([1, 0], np.int32)
+    assert C["kv_can_gather_within_tail"](arr, 1, 2, w.ctypes.data) == ttv.TTV_ERR_UNSUPPORTED
+    assert "sequence 0" in ttv.last_error()
+    assert C["kv_can_gather_within_tail"](arr, 1, 2, None) == ttv.TTV_OK
+    w[:] = 0
+    assert C["kv_can_gather_within_tail"](arr, 1, 2, w.ctypes.data) == ttv.TTV_OK
+    # the layer refusals of kv_can_gather carry over
+    i8 = (ttv.TtvKvLayer * 1)(layer(dtype=ttv.TTV_I8))
+    assert C["kv_can_gather_within_tail"](i8, 1, 2, None) == ttv.TTV_ERR_UNSUPPORTED
+    # tail longer than the live window, than a tree block, or negative
+    assert _tail(L, tail=(16, 101)) == ttv.TTV_ERR_INVALID
+    assert _tail(L, live=(100, 120), tail=(16, 65)) == ttv.TTV_ERR_INVALID
+    assert "tail_len[1]" in ttv.last_error()
+    assert _tail(L, tail=(-1, 3)) == ttv.TTV_ERR_INVALID
+    assert _tail(L, live=(100, 129)) == ttv.TTV_ERR_INVALID                   # beyond cap
+    assert _tail(L, ws=4) == ttv.TTV_ERR_WORKSPACE
+    assert _tail(L, stride=-1) == ttv.TTV_ERR_INVALID
+    assert _tail([layer(cap=128), layer(cap=256)]) == ttv.TTV_ERR_INVALID     # layers differ
+    assert ttv.kv_gather_within_tail_ws(8) == 8 * 4 * 4
+    assert ttv.kv_gather_within_tail_ws(0) == 0

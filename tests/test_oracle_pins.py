@@ -469,6 +469,53 @@ def test_absolute_selection_equals_tail_form():
     got = O.gather_layer(c, [absolute, absolute])
     for n in c:
         np.testing.assert_array_equal(got[n], tail[n])
+    # the oracle's tail form (live 40, tail 10 -> tail_start 30) gives the same cache
+    via_tail = O.gather_within_tail(c, [40, 40], [10, 10], [kept, kept])
+    for n in c:
+        np.testing.assert_array_equal(via_tail[n], tail[n])
+
+
+def test_tail_gather_worked_example():
+    """Worked by hand: rows 10..15 with live 6 and tail 4 (tail_start 2);
+    kept offsets [1, 3] move rows 3 and 5 to rows 2 and 3, and rows 4, 5
+    keep their old contents (the live length becomes 4)."""
+    k = np.arange(10, 16, dtype=np.float32).reshape(1, 1, 6, 1)
+    got = O.gather_within_tail({"k": k}, [6], [4], [[1, 3]])["k"].ravel().tolist()
+    assert got == [10, 11, 13, 15, 14, 15]
+    # an empty kept set and the identity prefix move nothing
+    assert O.gather_within_tail({"k": k}, [6], [4], [[]])["k"].ravel().tolist() == list(range(10, 16))
+    assert O.gather_within_tail({"k": k}, [6], [4], [[0, 1]])["k"].ravel().tolist() == list(range(10, 16))
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_tail_gather_equals_absolute_selection(seed):
+    """Per-sequence tails of different lengths: the tail form equals the
+    in-place absolute gather of [0, s) ++ (s + kept), scales included, and a
+    prefix of the tail is the trim (nothing moves)."""
+    r = rng_for(996, seed)
+    c = _cache(10 + seed, B=3, cap=80)
+    live = [80, 61, 9]
+    tails = [16, 64 if seed % 2 else 5, 9]
+    tails[1] = min(tails[1], live[1])
+    kept, sels = [], []
+    for b in range(3):
+        k = np.sort(r.choice(tails[b], size=int(r.integers(0, tails[b] + 1)), replace=False))
+        kept.append(k)
+        s = live[b] - tails[b]
+        sels.append(np.concatenate([np.arange(s), s + k]))
+    got = O.gather_within_tail(c, live, tails, kept)
+    want = O.gather_layer(c, sels)
+    for n in c:
+        np.testing.assert_array_equal(got[n], want[n])
+    # scales travel with their rows: every moved row's scale is its source's
+    for b in range(3):
+        s = live[b] - tails[b]
+        for j, kj in enumerate(kept[b]):
+            assert np.array_equal(got["k_scale"][b, :, s + j], c["k_scale"][b, :, s + kj])
+    prefix = [np.arange(int(r.integers(0, t + 1))) for t in tails]
+    same = O.gather_within_tail(c, live, tails, prefix)
+    for n in c:
+        np.testing.assert_array_equal(same[n], c[n])
 
 
 @pytest.mark.parametrize("T", [1, 4, 8, 16])

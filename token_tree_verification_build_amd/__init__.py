@@ -68,6 +68,12 @@ _c = {
     "kv_gather_positions": _sig("kv_gather_positions", _i32,
                                 [_LP, _LP, _i32, _i32, _p, _i32, _p, _p, _p, _p, _sz, _p]),
     "kv_can_gather": _sig("kv_can_gather", _i32, [_LP, _i32]),
+    "sliding_mask_from_caller": _sig("sliding_mask_from_caller", _i32,
+                                     [_p, _i32, _i32, _i32, _i32, ctypes.c_float, _p, _p]),
+    "kv_gather_within_tail_ws": _sig("kv_gather_within_tail_ws", _sz, [_i32]),
+    "kv_gather_within_tail": _sig("kv_gather_within_tail", _i32,
+                                  [_LP, _i32, _i32, _p, _i32, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "kv_can_gather_within_tail": _sig("kv_can_gather_within_tail", _i32, [_LP, _i32, _i32, _p]),
     "ttv_last_error": _sig("ttv_last_error", ctypes.c_char_p, []),
 }
 
@@ -198,6 +204,18 @@ def tree_mask_expand_additive(batch: Batch, b: int, anc, masked: float, out, str
            "tree_mask_expand_additive")
 
 
+def sliding_mask_from_caller(caller, offset: int, window: int, masked: float, out, stream=None):
+    """caller, out: float32 device tensors [T, S] (out may be caller)."""
+    import torch
+    _dev(caller, torch.float32, "caller")
+    _dev(out, torch.float32, "out")
+    if caller.dim() != 2 or tuple(out.shape) != tuple(caller.shape):
+        raise ValueError("caller and out must be [T, S] of one shape")
+    T, S = caller.shape
+    _check(_c["sliding_mask_from_caller"](_ptr(caller), T, S, offset, window, masked, _ptr(out), _stream(stream)),
+           "sliding_mask_from_caller")
+
+
 def tree_verify_attention_ws(batch: Batch, Hq: int, layer: KVLayer, q_dtype: str) -> int:
     return int(_c["tree_verify_attention_ws"](batch.ref(), Hq, layer.ref(), _DT[q_dtype]))
 
@@ -300,4 +318,45 @@ def kv_can_gather_raw(layer_structs) -> tuple[int, str]:
     """Capability query on raw TtvKvLayer structs (no tensors needed)."""
     arr = (TtvKvLayer * len(layer_structs))(*layer_structs)
     st = _c["kv_can_gather"](arr, len(layer_structs))
+    return st, last_error()
+
+
+def kv_gather_within_tail_ws(B: int) -> int:
+    return int(_c["kv_gather_within_tail_ws"](B))
+
+
+def _wrapped_arg(ring_wrapped, B):
+    if ring_wrapped is None:
+        return None, None
+    w = np.ascontiguousarray(ring_wrapped, dtype=np.int32)
+    if w.shape != (B,):
+        raise ValueError("ring_wrapped must hold one flag per sequence")
+    return w, w.ctypes.data
+
+
+def kv_gather_within_tail(layers, kept, kept_len, live_len_h, tail_len_h, dev_status, ws, ring_wrapped=None,
+                          stream=None):
+    """In-place rollback confined to each sequence's last tail_len rows.
+    kept int32 [B, stride] offsets inside the tail; ring_wrapped: host flags or None."""
+    import torch
+    _dev(kept, torch.int32, "kept")
+    _dev(kept_len, torch.int32, "kept_len")
+    _dev(dev_status, torch.int32, "dev_status")
+    _dev(ws, None, "ws")
+    B = kept.shape[0]
+    live = np.ascontiguousarray(live_len_h, dtype=np.int32)
+    tail = np.ascontiguousarray(tail_len_h, dtype=np.int32)
+    if live.shape != (B,) or tail.shape != (B,):
+        raise ValueError("live_len_h and tail_len_h must hold one entry per sequence")
+    w, wp = _wrapped_arg(ring_wrapped, B)
+    arr = _layers_array(layers)
+    _check(_c["kv_gather_within_tail"](arr, len(layers), B, _ptr(kept), kept.shape[1], _ptr(kept_len),
+                                       live.ctypes.data, tail.ctypes.data, wp, _ptr(dev_status), _ptr(ws),
+                                       ws.numel() * ws.element_size(), _stream(stream)), "kv_gather_within_tail")
+
+
+def kv_can_gather_within_tail(layers, B: int, ring_wrapped=None) -> tuple[int, str]:
+    w, wp = _wrapped_arg(ring_wrapped, B)
+    arr = _layers_array(layers)
+    st = _c["kv_can_gather_within_tail"](arr, len(layers), B, wp)
     return st, last_error()

@@ -104,6 +104,49 @@ __global__ void __launch_bounds__(TTV_MAX_BATCH) sel_finalize_kernel(const int32
   if (bad) *status = TTV_DEV_BAD_SELECTION;
 }
 
+// Tail form: per sequence b, the tail starts at row start[b] and holds len[b]
+// (<= 64) rows; kept offsets index into it.
+struct TailSpec {
+  int32_t start[TTV_MAX_BATCH];
+  int32_t len[TTV_MAX_BATCH];
+};
+
+// One wave per sequence checks the kept offsets (at most 64, one per lane):
+// strictly increasing, inside the tail, no more than the tail or the row
+// stride holds. Writes j0 (absolute first moved row), the absolute end
+// start + kept_len, the tail start and a bad flag per sequence.
+__global__ void __launch_bounds__(kWave) tail_validate_kernel(const int32_t* __restrict__ kept, int kept_stride,
+                                                              const int32_t* __restrict__ kept_len, TailSpec tails,
+                                                              int32_t* __restrict__ j0s, int32_t* __restrict__ ends,
+                                                              int32_t* __restrict__ starts,
+                                                              int32_t* __restrict__ bad_out,
+                                                              int32_t* __restrict__ status) {
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int ts = tails.start[b];
+  const int tl = tails.len[b];
+  const int n = kept_len[b];
+  int f = (n < 0 || n > tl || n > kept_stride) ? 1 : 0;
+  int k = lane;
+  if (!f && lane < n) {
+    const int32_t* __restrict__ row = kept + static_cast<int64_t>(b) * kept_stride;
+    k = row[lane];
+    if (k < 0 || k >= tl) f = 1;
+    if (lane + 1 < n && row[lane + 1] <= k) f = 1;
+  }
+  const bool any = __ballot(f != 0) != 0;
+  const uint64_t moved = __ballot(lane < n && k != lane);
+  if (lane == 0) {
+    const int nn = any ? 0 : n;
+    const int j = (!any && moved != 0) ? __builtin_ctzll(moved) : nn;
+    j0s[b] = ts + j;
+    ends[b] = ts + nn;
+    starts[b] = ts;
+    bad_out[b] = any ? 1 : 0;
+    if (any) *status = TTV_DEV_BAD_SELECTION;
+  }
+}
+
 __device__ __forceinline__ bool any_bad(const int32_t* __restrict__ bad, int B) {
   // wave 0 of the block reads all flags; the answer is shared through LDS
   __shared__ int s_bad;
@@ -164,12 +207,17 @@ __global__ void __launch_bounds__(kGatherThreads) take_kernel(LayerPtrs L, int B
 }
 
 // In-place compaction of rows j >= j0 for one (layer, sequence, head).
-template <int PIECES>  // 16-byte pieces of K (and of V) held per thread per chunk
+// Absolute selection (TAIL = false): row j <- row sel[b][j], j < sel_len[b].
+// Tail form (TAIL = true): sel[b] holds offsets inside the tail that starts at
+// row tail_start[b], row tail_start + j <- row tail_start + sel[b][j], and
+// sel_len[b] is the absolute end tail_start + kept_len.
+template <int PIECES, bool TAIL>  // PIECES: 16-byte pieces of K (and of V) held per thread per chunk
 __global__ void __launch_bounds__(kGatherThreads) compact_kernel(LayerPtrs L, int B, int Hkv, int cap, int row_bytes,
                                                                  const int32_t* __restrict__ sel, int sel_stride,
                                                                  const int32_t* __restrict__ sel_len,
                                                                  const int32_t* __restrict__ j0s,
-                                                                 const int32_t* __restrict__ bad) {
+                                                                 const int32_t* __restrict__ bad,
+                                                                 const int32_t* __restrict__ tail_start) {
   if (any_bad(bad, B)) return;
   int w = blockIdx.x;
   const int h = w % Hkv;
@@ -180,6 +228,7 @@ __global__ void __launch_bounds__(kGatherThreads) compact_kernel(LayerPtrs L, in
   const int j0 = j0s[b];
   if (j0 >= n) return;  // identity or prefix selection: nothing moves
   const int32_t* __restrict__ srow = sel + static_cast<int64_t>(b) * sel_stride;
+  const int ts = TAIL ? tail_start[b] : 0;
   const int64_t base = (static_cast<int64_t>(b) * Hkv + h) * cap;
   const int U = row_bytes >> 4;
   const int rows_chunk = PIECES * kGatherThreads / U < kGatherThreads ? PIECES * kGatherThreads / U : kGatherThreads;
@@ -196,15 +245,15 @@ __global__ void __launch_bounds__(kGatherThreads) compact_kernel(LayerPtrs L, in
       const int q = threadIdx.x + p * kGatherThreads;  // piece id within the chunk
       const int j = c0 + q / U;
       if (j < c1) {
-        const int64_t src = (base + srow[j]) * row_bytes + 16 * (q % U);
+        const int64_t src = (base + ts + srow[j - ts]) * row_bytes + 16 * (q % U);
         kr[p] = *reinterpret_cast<const u32x4*>(kp + src);
         vr[p] = *reinterpret_cast<const u32x4*>(vp + src);
       }
     }
     const int js = c0 + threadIdx.x;
     if (ksp != nullptr && threadIdx.x < rows_chunk && js < c1) {
-      ksr = ksp[base + srow[js]];
-      vsr = vsp[base + srow[js]];
+      ksr = ksp[base + ts + srow[js - ts]];
+      vsr = vsp[base + ts + srow[js - ts]];
     }
     __syncthreads();
 #pragma unroll
@@ -336,8 +385,8 @@ extern "C" ttv_status kv_gather_positions(const ttv_kv_layer* src, const ttv_kv_
       const int64_t nblk = static_cast<int64_t>(nl) * B * L0.Hkv;
       TTV_REQUIRE(nblk <= 0x7FFFFFFF, TTV_ERR_INVALID, "kv_gather_positions: grid too large");
       // at most 4 pieces of 16 B per buffer per thread: 1024 rows of int8 D=64 ... 32 rows of f32 D=512
-      hipLaunchKernelGGL(compact_kernel<4>, dim3(static_cast<unsigned>(nblk)), dim3(kGatherThreads), 0, st, P, B,
-                         L0.Hkv, L0.cap, row_bytes, sel, sel_stride, sel_len, j0s, bad);
+      hipLaunchKernelGGL((compact_kernel<4, false>), dim3(static_cast<unsigned>(nblk)), dim3(kGatherThreads), 0, st, P,
+                         B, L0.Hkv, L0.cap, row_bytes, sel, sel_stride, sel_len, j0s, bad, nullptr);
     } else {
       const int chunks = (max_live + kTakeRows - 1) / kTakeRows;
       if (chunks == 0) continue;
@@ -349,6 +398,94 @@ extern "C" ttv_status kv_gather_positions(const ttv_kv_layer* src, const ttv_kv_
                          L0.cap, row_bytes, chunks, sel, sel_stride, sel_len, bad);
     }
     s = check_launch("kv_gather_positions copy");
+    if (s != TTV_OK) return s;
+  }
+  return TTV_OK;
+}
+
+extern "C" ttv_status kv_can_gather_within_tail(const ttv_kv_layer* layers, int32_t n_layers, int32_t B,
+                                                const int32_t* ring_wrapped_h) {
+  clear_error();
+  TTV_REQUIRE(B >= 0 && B <= TTV_MAX_BATCH, TTV_ERR_INVALID, "kv_can_gather_within_tail: B %d", B);
+  ttv_status s = kv_can_gather(layers, n_layers);
+  if (s != TTV_OK) return s;
+  if (ring_wrapped_h != nullptr)
+    for (int b = 0; b < B; ++b)
+      TTV_REQUIRE(ring_wrapped_h[b] == 0, TTV_ERR_UNSUPPORTED,
+                  "kv_gather_within_tail: the rotating cache of sequence %d has wrapped, so its tail is no longer "
+                  "in logical order", b);
+  return TTV_OK;
+}
+
+extern "C" size_t kv_gather_within_tail_ws(int32_t B) {
+  if (B <= 0) return 0;
+  return 4 * static_cast<size_t>(B) * sizeof(int32_t);
+}
+
+extern "C" ttv_status kv_gather_within_tail(const ttv_kv_layer* layers, int32_t n_layers, int32_t B,
+                                            const int32_t* kept, int32_t kept_stride, const int32_t* kept_len,
+                                            const int32_t* live_len_h, const int32_t* tail_len_h,
+                                            const int32_t* ring_wrapped_h, int32_t* dev_status, void* ws,
+                                            size_t ws_bytes, void* stream) {
+  clear_error();
+  TTV_REQUIRE(n_layers >= 0 && B >= 0 && B <= TTV_MAX_BATCH, TTV_ERR_INVALID,
+              "kv_gather_within_tail: n_layers %d, B %d", n_layers, B);
+  if (n_layers == 0 || B == 0) return TTV_OK;
+  ttv_status s = kv_can_gather_within_tail(layers, n_layers, B, ring_wrapped_h);
+  if (s != TTV_OK) return s;
+  TTV_REQUIRE(kept && kept_len && live_len_h && tail_len_h && dev_status, TTV_ERR_INVALID,
+              "kv_gather_within_tail: NULL pointer");
+  TTV_REQUIRE(kept_stride >= 0, TTV_ERR_INVALID, "kv_gather_within_tail: negative kept_stride");
+  const size_t need = kv_gather_within_tail_ws(B);
+  TTV_REQUIRE(ws && ws_bytes >= need, TTV_ERR_WORKSPACE, "kv_gather_within_tail: workspace %zu bytes < %zu",
+              ws_bytes, need);
+  const ttv_kv_layer& L0 = layers[0];
+  for (int l = 0; l < n_layers; ++l) {
+    const ttv_kv_layer& a = layers[l];
+    TTV_REQUIRE(a.dtype == L0.dtype && a.Hkv == L0.Hkv && a.D == L0.D && a.cap == L0.cap, TTV_ERR_INVALID,
+                "kv_gather_within_tail: layer %d shape/dtype differs from layer 0", l);
+  }
+  TailSpec tails{};
+  for (int b = 0; b < B; ++b) {
+    const int live = live_len_h[b], tl = tail_len_h[b];
+    TTV_REQUIRE(live >= 0 && live <= L0.cap, TTV_ERR_INVALID,
+                "kv_gather_within_tail: live_len[%d] = %d outside [0, cap %d]", b, live, L0.cap);
+    TTV_REQUIRE(tl >= 0 && tl <= live && tl <= TTV_MAX_NODES, TTV_ERR_INVALID,
+                "kv_gather_within_tail: tail_len[%d] = %d outside [0, min(live_len %d, %d)]", b, tl, live,
+                TTV_MAX_NODES);
+    tails.start[b] = live - tl;
+    tails.len[b] = tl;
+  }
+  const int esz = L0.dtype == TTV_F32 ? 4 : L0.dtype == TTV_BF16 ? 2 : 1;
+  const int row_bytes = L0.D * esz;
+  int32_t* j0s = static_cast<int32_t*>(ws);
+  int32_t* ends = j0s + B;
+  int32_t* starts = ends + B;
+  int32_t* bad = starts + B;
+  hipStream_t st = (hipStream_t)stream;
+  hipLaunchKernelGGL(tail_validate_kernel, dim3(B), dim3(kWave), 0, st, kept, kept_stride, kept_len, tails, j0s,
+                     ends, starts, bad, dev_status);
+  s = check_launch("kv_gather_within_tail validate");
+  if (s != TTV_OK) return s;
+  for (int l0 = 0; l0 < n_layers; l0 += kLayersPerLaunch) {
+    const int nl = n_layers - l0 < kLayersPerLaunch ? n_layers - l0 : kLayersPerLaunch;
+    LayerPtrs P{};
+    for (int i = 0; i < nl; ++i) {
+      const ttv_kv_layer& a = layers[l0 + i];
+      P.k[i] = static_cast<const char*>(a.k);
+      P.v[i] = static_cast<const char*>(a.v);
+      P.ks[i] = a.dtype == TTV_I8 ? a.k_scale : nullptr;
+      P.vs[i] = a.dtype == TTV_I8 ? a.v_scale : nullptr;
+      P.dk[i] = static_cast<char*>(a.k);
+      P.dv[i] = static_cast<char*>(a.v);
+      P.dks[i] = P.ks[i] ? a.k_scale : nullptr;
+      P.dvs[i] = P.vs[i] ? a.v_scale : nullptr;
+    }
+    const int64_t nblk = static_cast<int64_t>(nl) * B * L0.Hkv;
+    TTV_REQUIRE(nblk <= 0x7FFFFFFF, TTV_ERR_INVALID, "kv_gather_within_tail: grid too large");
+    hipLaunchKernelGGL((compact_kernel<4, true>), dim3(static_cast<unsigned>(nblk)), dim3(kGatherThreads), 0, st, P,
+                       B, L0.Hkv, L0.cap, row_bytes, kept, kept_stride, ends, j0s, bad, starts);
+    s = check_launch("kv_gather_within_tail copy");
     if (s != TTV_OK) return s;
   }
   return TTV_OK;

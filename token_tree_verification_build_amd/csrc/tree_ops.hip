@@ -96,6 +96,30 @@ __global__ void expand_kernel(const uint64_t* __restrict__ anc, int P, int T, fl
   }
 }
 
+// Sliding-window layers' form of a caller mask ([PR1212] the commit that
+// intersects the caller mask with the sliding band, and the commit stating its
+// properties): query row q sits at cache position offset + q and keeps column
+// c only when offset + q - window < c <= offset + q. Additive masks intersect
+// by elementwise minimum, so an open band entry is 0 and a blocked one is
+// `masked`; a NaN in either operand comes through as in numpy.minimum.
+__global__ void band_kernel(const float* caller, int S, int offset, int window, float masked, float* out) {
+  const int q = blockIdx.y;
+  const int pos = offset + q;
+  const float* __restrict__ src = caller + (size_t)q * S;
+  float* __restrict__ dst = out + (size_t)q * S;
+  for (int c = blockIdx.x * blockDim.x + threadIdx.x; c < S; c += gridDim.x * blockDim.x) {
+    const float m = src[c];
+    const float b = (c > pos - window && c <= pos) ? 0.0f : masked;
+    dst[c] = (m < b || m != m) ? m : b;
+  }
+}
+
+__global__ void copy_rows_kernel(const float* caller, int S, float* out) {
+  const int q = blockIdx.y;
+  for (int c = blockIdx.x * blockDim.x + threadIdx.x; c < S; c += gridDim.x * blockDim.x)
+    out[(size_t)q * S + c] = caller[(size_t)q * S + c];
+}
+
 // ------------------------------------------------------------------ walk ----
 // Wave 0 walks the tree: ballot over lanes whose parent is the current node
 // and whose token equals the target's selection there; the lowest set bit is
@@ -192,6 +216,32 @@ extern "C" ttv_status tree_mask_expand_additive(const ttv_batch* batch, int32_t 
   dim3 grid((W + 255) / 256 < 64 ? (W + 255) / 256 : 64, T);
   hipLaunchKernelGGL(expand_kernel, grid, dim3(256), 0, (hipStream_t)stream, anc + o0, P, T, masked, out);
   return check_launch("tree_mask_expand_additive");
+}
+
+extern "C" ttv_status sliding_mask_from_caller(const float* caller, int32_t T, int32_t S, int32_t offset,
+                                               int32_t window, float masked, float* out, void* stream) {
+  clear_error();
+  TTV_REQUIRE(T >= 0 && S >= 0 && offset >= 0, TTV_ERR_INVALID, "sliding_mask_from_caller: T %d, S %d, offset %d", T,
+              S, offset);
+  TTV_REQUIRE(window >= 1, TTV_ERR_INVALID, "sliding_mask_from_caller: window %d < 1", window);
+  TTV_REQUIRE(T <= 65535 && (int64_t)offset + T <= 0x7FFFFFFF, TTV_ERR_INVALID,
+              "sliding_mask_from_caller: %d rows at offset %d out of range", T, offset);
+  if (T == 0 || S == 0) return TTV_OK;
+  TTV_REQUIRE(caller && out, TTV_ERR_INVALID, "sliding_mask_from_caller: NULL pointer");
+  const size_t bytes = (size_t)T * S * sizeof(float);
+  const uintptr_t a = reinterpret_cast<uintptr_t>(caller), o = reinterpret_cast<uintptr_t>(out);
+  TTV_REQUIRE(a == o || a + bytes <= o || o + bytes <= a, TTV_ERR_INVALID,
+              "sliding_mask_from_caller: out partly overlaps caller (only out == caller is allowed)");
+  dim3 grid((S + 255) / 256 < 64 ? (S + 255) / 256 : 64, T);
+  // below the window the band and the caller mask cannot disagree: the caller
+  // mask comes back untouched
+  if ((int64_t)offset + T <= window) {
+    if (a == o) return TTV_OK;
+    hipLaunchKernelGGL(copy_rows_kernel, grid, dim3(256), 0, (hipStream_t)stream, caller, S, out);
+  } else {
+    hipLaunchKernelGGL(band_kernel, grid, dim3(256), 0, (hipStream_t)stream, caller, S, offset, window, masked, out);
+  }
+  return check_launch("sliding_mask_from_caller");
 }
 
 extern "C" ttv_status tree_accept_walk(const ttv_batch* batch, const int32_t* parent,
