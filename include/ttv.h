@@ -12,8 +12,9 @@
  *   kv_gather_positions  compact the accepted path's K/V (and int8 scales)
  *                        along the sequence axis
  * and the sliding-window layers' variants: sliding_mask_from_caller (caller
- * mask intersected with the window band) and kv_gather_within_tail (the
- * rollback confined to the verify block, refusing a wrapped rotating cache).
+ * mask intersected with the window band), tree_verify_attention_window (the
+ * attention under that band) and kv_gather_within_tail (the rollback confined
+ * to the verify block, refusing a wrapped rotating cache).
  *
  * Sources are cited by page title and section:
  *   [I1204]  mlxcel issue #1204 "perf(speculative): draft a tree instead of a
@@ -176,6 +177,25 @@ size_t tree_verify_attention_ws(const ttv_batch* batch, int32_t Hq, const ttv_kv
 ttv_status tree_verify_attention(const ttv_batch* batch, const void* q, int32_t q_dtype, int32_t Hq,
                                  const ttv_kv_layer* layer, const uint64_t* anc, float softmax_scale,
                                  float* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Sliding-window layers' form of step 2 [PR1212] the commit intersecting the
+ * caller mask with the sliding band: as tree_verify_attention, with node i of
+ * sequence b (cache row P_b + i) keeping only keys j > P_b + i - window, i.e.
+ * the key set of the tree mask intersected with the band that
+ * sliding_mask_from_caller applies. History keys below P_b - window + 1 are
+ * not read at all, so the cost follows the window rather than the context.
+ * Every row keeps its own key, so no row is empty. window >= 1 (a window of
+ * at least P_b + T_b for every b gives the same key sets as
+ * tree_verify_attention). Arguments, layouts, limits and accuracy as there;
+ * ws >= tree_verify_attention_window_ws(..., window) bytes. The band runs on
+ * the VALU path for every dtype.
+ */
+size_t tree_verify_attention_window_ws(const ttv_batch* batch, int32_t Hq, const ttv_kv_layer* layer,
+                                       int32_t q_dtype, int32_t window);
+ttv_status tree_verify_attention_window(const ttv_batch* batch, const void* q, int32_t q_dtype, int32_t Hq,
+                                        const ttv_kv_layer* layer, const uint64_t* anc, float softmax_scale,
+                                        int32_t window, float* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Step 3 -- per-node argmax [I1204] "Increment 1" (the target emits one argmax

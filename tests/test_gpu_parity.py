@@ -3,6 +3,7 @@ seeded inputs. Integer/index/byte outputs must match bit for bit; attention
 within max-abs 2e-3 (bf16 or int8 KV, fp32 accumulation) or 1e-5 (fp32)."""
 
 import math
+import zlib
 
 import numpy as np
 import pytest
@@ -270,7 +271,7 @@ def _selections(rng, live, kind):
 @pytest.mark.parametrize("in_place", [True, False])
 @pytest.mark.parametrize("kind", ["rollback", "prefix", "identity", "scatter", "wide", "empty"])
 def test_gather_matches_oracle(ttv, dtype, D, in_place, kind):
-    rng = rng_for(1180, hash((dtype, D, in_place, kind)) % 1000)
+    rng = rng_for(1180, zlib.crc32(repr((dtype, D, in_place, kind)).encode()) % 1000)
     B, cap = 3, 700
     live = np.array([cap - 3 * b for b in range(B)])
     sels = _selections(rng, live, kind)

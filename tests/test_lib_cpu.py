@@ -241,3 +241,17 @@ def test_tail_gather_validation_and_ring_refusal():
     assert _tail([layer(cap=128), layer(cap=256)]) == ttv.TTV_ERR_INVALID     # layers differ
     assert ttv.kv_gather_within_tail_ws(8) == 8 * 4 * 4
     assert ttv.kv_gather_within_tail_ws(0) == 0
+
+
+def test_window_attention_validation():
+    b, keep = batch([0, 4], [10])
+    L = layer()
+    assert C["tree_verify_attention_window_ws"](ctypes.byref(b), 40, ctypes.byref(L), ttv.TTV_BF16, 0) == 0
+    assert C["tree_verify_attention_window_ws"](ctypes.byref(b), 40, ctypes.byref(L), ttv.TTV_BF16, 64) > 0
+    st = C["tree_verify_attention_window"](ctypes.byref(b), FAKE, ttv.TTV_BF16, 40, ctypes.byref(L), None, 0.1, 0,
+                                           FAKE, FAKE, 1 << 30, None)
+    assert st == ttv.TTV_ERR_INVALID and "window" in ttv.last_error()
+    # a small workspace is refused before anything launches
+    st = C["tree_verify_attention_window"](ctypes.byref(b), FAKE, ttv.TTV_BF16, 40, ctypes.byref(L), None, 0.1, 8,
+                                           FAKE, FAKE, 4, None)
+    assert st == ttv.TTV_ERR_WORKSPACE

@@ -58,6 +58,9 @@ _c = {
     "tree_verify_attention_ws": _sig("tree_verify_attention_ws", _sz, [_BP, _i32, _LP, _i32]),
     "tree_verify_attention": _sig("tree_verify_attention", _i32,
                                   [_BP, _p, _i32, _i32, _LP, _p, ctypes.c_float, _p, _p, _sz, _p]),
+    "tree_verify_attention_window_ws": _sig("tree_verify_attention_window_ws", _sz, [_BP, _i32, _LP, _i32, _i32]),
+    "tree_verify_attention_window": _sig("tree_verify_attention_window", _i32,
+                                         [_BP, _p, _i32, _i32, _LP, _p, ctypes.c_float, _i32, _p, _p, _sz, _p]),
     "vocab_argmax_ws": _sig("vocab_argmax_ws", _sz, [_i64, _i64]),
     "vocab_argmax": _sig("vocab_argmax", _i32, [_p, _i64, _i64, _i64, _p, _p, _sz, _p]),
     "vocab_sample_ws": _sig("vocab_sample_ws", _sz, [_i64, _i64, _i32]),
@@ -233,6 +236,26 @@ def tree_verify_attention(batch: Batch, q, layer: KVLayer, anc, softmax_scale: f
     _check(_c["tree_verify_attention"](batch.ref(), _ptr(q), _DT[qd], Hq, layer.ref(), _ptr(anc), softmax_scale,
                                        _ptr(out), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)),
            "tree_verify_attention")
+
+
+def tree_verify_attention_window_ws(batch: Batch, Hq: int, layer: KVLayer, q_dtype: str, window: int) -> int:
+    return int(_c["tree_verify_attention_window_ws"](batch.ref(), Hq, layer.ref(), _DT[q_dtype], window))
+
+
+def tree_verify_attention_window(batch: Batch, q, layer: KVLayer, anc, softmax_scale: float, window: int, out, ws,
+                                 stream=None):
+    """tree_verify_attention with node i keeping only keys > P + i - window."""
+    import torch
+    _dev(q, name="q")
+    qd = {torch.float32: "f32", torch.bfloat16: "bf16"}[q.dtype]
+    _dev(out, torch.float32, "out")
+    _dev(anc, torch.int64, "anc")
+    _dev(ws, torch.uint8, "ws")
+    Hq = q.shape[1]
+    _check(_c["tree_verify_attention_window"](batch.ref(), _ptr(q), _DT[qd], Hq, layer.ref(), _ptr(anc),
+                                              softmax_scale, window, _ptr(out), _ptr(ws),
+                                              ws.numel() if ws is not None else 0, _stream(stream)),
+           "tree_verify_attention_window")
 
 
 def vocab_argmax_ws(n_rows: int, vocab: int) -> int:

@@ -46,6 +46,7 @@
 // scores, one d per lane for the output, queries and probabilities in LDS.
 #include "common.hpp"
 
+#include <climits>
 #include <type_traits>
 
 namespace ttv {
@@ -77,6 +78,7 @@ struct AttnParams {
   float* part_ml;
   int B, Hq, Hkv, G, D, cap, split_len, rows_chunk, nwg, split_pad;
   int wide;  // wide layout: the row chunks of one (kv head, split) take ceil(rc_n / 4) * 4 consecutive slots
+  int window;  // sliding-window layers: node i (cache row P + i) keeps keys > P + i - window; 0 = none
   float scale_log2;
   int32_t node_off[TTV_MAX_BATCH + 1];
   int32_t hist_len[TTV_MAX_BATCH];
@@ -89,6 +91,13 @@ struct Work {
   int b, kvh, split, rc, nsplit, rc_n, P, T, o0, rows, row0, nrows, unit, slot, k_lo, k_hi;
   bool last;
 };
+
+// First history key any row of a sequence can see: with a window, node 0
+// (row P) keeps keys > P - window, so history keys below P - window + 1 are
+// read by no row and the unit's splits start there.
+__host__ __device__ __forceinline__ int hist_key_start(int P, int window) {
+  return (window > 0 && P - window + 1 > 0) ? P - window + 1 : 0;
+}
 
 __device__ __forceinline__ void decode(const AttnParams& p, int slot, Work& w) {
   int lo = 0, hi = p.B;  // wg_off[lo] <= slot < wg_off[hi]
@@ -103,7 +112,8 @@ __device__ __forceinline__ void decode(const AttnParams& p, int slot, Work& w) {
   w.rows = w.T * p.G;
   const int rch = p.rchunk[lo];
   w.rc_n = (w.rows + rch - 1) / rch;
-  const int ns = w.P > 0 ? (w.P + p.split_len - 1) / p.split_len : 1;
+  const int ks = hist_key_start(w.P, p.window);
+  const int ns = w.P > ks ? (w.P - ks + p.split_len - 1) / p.split_len : 1;
   w.nsplit = (ns + p.split_pad - 1) / p.split_pad * p.split_pad;  // trailing splits may be empty
   int rem = slot - p.wg_off[lo];
   if (p.wide) {  // the row chunks of one (kv head, split) are consecutive slots
@@ -122,7 +132,7 @@ __device__ __forceinline__ void decode(const AttnParams& p, int slot, Work& w) {
   w.slot = slot;
   w.row0 = w.rc * rch;
   w.nrows = max(0, min(rch, w.rows - w.row0));  // 0: a padding chunk of the wide layout
-  w.k_lo = w.split * p.split_len;
+  w.k_lo = ks + w.split * p.split_len;
   w.k_hi = min(w.P, w.k_lo + p.split_len);
   w.last = w.split == w.nsplit - 1;
 }
@@ -207,7 +217,8 @@ __global__ void __launch_bounds__(256) merge_kernel(const AttnParams p, int per_
   w.rows = w.T * p.G;
   const int rch = p.rchunk[lo];
   w.rc_n = (w.rows + rch - 1) / rch;
-  const int ns = w.P > 0 ? (w.P + p.split_len - 1) / p.split_len : 1;
+  const int ks = hist_key_start(w.P, p.window);
+  const int ns = w.P > ks ? (w.P - ks + p.split_len - 1) / p.split_len : 1;
   w.nsplit = (ns + p.split_pad - 1) / p.split_pad * p.split_pad;
   const int n = w.nsplit / per_slot;
   if (u >= p.unit_off[lo + 1] || n <= 1) return;
@@ -1535,6 +1546,11 @@ __global__ void __launch_bounds__(64) attn_valu_kernel(const AttnParams p) {
   uint64_t bits[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) bits[r] = ~0ull;
+  // window band: row r (node t, cache row P + t) keeps keys >= P + t - window + 1
+  int lo[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    lo[r] = (p.window > 0 && r < w.nrows) ? w.P + (w.row0 + r) / p.G - p.window + 1 : INT_MIN;
 
   auto tile = [&](int t0, int mode, int limit) {
     const int key = t0 + lane;
@@ -1560,7 +1576,7 @@ __global__ void __launch_bounds__(64) attn_valu_kernel(const AttnParams p) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       float x = s[r] * fk;
-      if (!valid || (mode == 2 && !((bits[r] >> (key - w.P)) & 1ull))) x = -INFINITY;
+      if (!valid || key < lo[r] || (mode == 2 && !((bits[r] >> (key - w.P)) & 1ull))) x = -INFINITY;
       const float mnew = fmaxf(m[r], wave_max(x));
       const float msub = mnew == -INFINITY ? 0.f : mnew;
       const float alpha = exp2f(m[r] - msub);
@@ -1639,9 +1655,10 @@ struct AttnPlan {
 };
 
 static ttv_status plan_attention(const ttv_batch* batch, int Hq, const ttv_kv_layer* L, int q_dtype,
-                                 AttnPlan& pl) {
+                                 AttnPlan& pl, int window = 0) {
   ttv_status s = check_batch(batch, false);
   if (s != TTV_OK) return s;
+  TTV_REQUIRE(window >= 0, TTV_ERR_INVALID, "tree_verify_attention: window %d < 1", window);
   TTV_REQUIRE(L != nullptr, TTV_ERR_INVALID, "tree_verify_attention: layer is NULL");
   TTV_REQUIRE(L->Hkv > 0 && Hq > 0 && Hq % L->Hkv == 0, TTV_ERR_INVALID,
               "tree_verify_attention: Hq %d is not a multiple of Hkv %d", Hq, L->Hkv);
@@ -1664,9 +1681,12 @@ static ttv_status plan_attention(const ttv_batch* batch, int Hq, const ttv_kv_la
     TTV_REQUIRE((int64_t)P + T <= L->cap, TTV_ERR_INVALID,
                 "tree_verify_attention: sequence %d needs P + T = %d rows, cache holds %d", b, P + T, L->cap);
     max_rows = T * G > max_rows ? T * G : max_rows;
-    maxP = P > maxP ? P : maxP;
+    const int ph = P - hist_key_start(P, window);  // history keys the sequence's rows read
+    maxP = ph > maxP ? ph : maxP;
   }
-  pl.mfma = bf && L->D == 128 && max_rows >= 16 && L->cap >= 32;
+  // the window's band runs on the VALU path (its per-row lower bound is one
+  // compare per key there)
+  pl.mfma = bf && L->D == 128 && max_rows >= 16 && L->cap >= 32 && window == 0;
   pl.wide = pl.mfma && L->dtype != TTV_I8 && max_rows > 16 * kMfmaMaxRB;
   if (pl.wide) {
     // up to four balanced chunks of at most 80 rows side by side (more rows
@@ -1713,12 +1733,14 @@ static ttv_status plan_attention(const ttv_batch* batch, int Hq, const ttv_kv_la
   // wide: every (kv head, split) takes its chunk count rounded up to 4 slots
   // (one workgroup per 4)
   p.wide = pl.wide ? 1 : 0;
+  p.window = window;
   int64_t work = 0;
   for (int b = 0; b < B; ++b) {
     const int T = batch->node_off_h[b + 1] - batch->node_off_h[b];
     const int rc = (T * G + p.rchunk[b] - 1) / p.rchunk[b];
     const int P = batch->hist_len_h[b];
-    work += (int64_t)p.Hkv * (pl.wide ? (rc + 3) / 4 : rc) * (P > 0 ? P : 1);
+    const int ph = P - hist_key_start(P, window);
+    work += (int64_t)p.Hkv * (pl.wide ? (rc + 3) / 4 : rc) * (ph > 0 ? ph : 1);
   }
   // a wide workgroup's partial is up to 384 rows of fp32: its split is kept
   // long (about two workgroups per compute unit)
@@ -1738,7 +1760,8 @@ static ttv_status plan_attention(const ttv_batch* batch, int Hq, const ttv_kv_la
     const int T = batch->node_off_h[b + 1] - batch->node_off_h[b];
     const int P = batch->hist_len_h[b];
     const int rc = (T * G + p.rchunk[b] - 1) / p.rchunk[b];
-    const int ns0 = P > 0 ? (P + p.split_len - 1) / p.split_len : 1;
+    const int ph = P - hist_key_start(P, window);
+    const int ns0 = ph > 0 ? (ph + p.split_len - 1) / p.split_len : 1;
     const int ns = (ns0 + p.split_pad - 1) / p.split_pad * p.split_pad;
     p.node_off[b] = batch->node_off_h[b];
     p.hist_len[b] = P;
@@ -1770,12 +1793,18 @@ extern "C" size_t tree_verify_attention_ws(const ttv_batch* batch, int32_t Hq, c
   return pl.ws_bytes;
 }
 
-extern "C" ttv_status tree_verify_attention(const ttv_batch* batch, const void* q, int32_t q_dtype, int32_t Hq,
-                                            const ttv_kv_layer* layer, const uint64_t* anc, float softmax_scale,
-                                            float* out, void* ws, size_t ws_bytes, void* stream) {
-  clear_error();
+extern "C" size_t tree_verify_attention_window_ws(const ttv_batch* batch, int32_t Hq, const ttv_kv_layer* layer,
+                                                  int32_t q_dtype, int32_t window) {
   AttnPlan pl;
-  ttv_status s = plan_attention(batch, Hq, layer, q_dtype, pl);
+  if (window < 1 || plan_attention(batch, Hq, layer, q_dtype, pl, window) != TTV_OK) return 0;
+  return pl.ws_bytes;
+}
+
+static ttv_status run_attention(const ttv_batch* batch, const void* q, int32_t q_dtype, int32_t Hq,
+                                const ttv_kv_layer* layer, const uint64_t* anc, float softmax_scale, int window,
+                                float* out, void* ws, size_t ws_bytes, void* stream) {
+  AttnPlan pl;
+  ttv_status s = plan_attention(batch, Hq, layer, q_dtype, pl, window);
   if (s != TTV_OK) return s;
   if (pl.prm.nwg == 0) return TTV_OK;
   TTV_REQUIRE(q && out && layer->k && layer->v, TTV_ERR_INVALID, "tree_verify_attention: NULL pointer");
@@ -1840,4 +1869,20 @@ extern "C" ttv_status tree_verify_attention(const ttv_batch* batch, const void* 
                      dim3(static_cast<unsigned>(pl.nunits), static_cast<unsigned>((p.rows_chunk + kMergeRows - 1) / kMergeRows)),
                      dim3(128), 0, st, p, pl.mfma && !pl.wide ? 4 : 1);
   return check_launch("tree_verify_attention merge");
+}
+
+extern "C" ttv_status tree_verify_attention(const ttv_batch* batch, const void* q, int32_t q_dtype, int32_t Hq,
+                                            const ttv_kv_layer* layer, const uint64_t* anc, float softmax_scale,
+                                            float* out, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  return run_attention(batch, q, q_dtype, Hq, layer, anc, softmax_scale, 0, out, ws, ws_bytes, stream);
+}
+
+extern "C" ttv_status tree_verify_attention_window(const ttv_batch* batch, const void* q, int32_t q_dtype,
+                                                   int32_t Hq, const ttv_kv_layer* layer, const uint64_t* anc,
+                                                   float softmax_scale, int32_t window, float* out, void* ws,
+                                                   size_t ws_bytes, void* stream) {
+  clear_error();
+  TTV_REQUIRE(window >= 1, TTV_ERR_INVALID, "tree_verify_attention_window: window %d < 1", window);
+  return run_attention(batch, q, q_dtype, Hq, layer, anc, softmax_scale, window, out, ws, ws_bytes, stream);
 }
