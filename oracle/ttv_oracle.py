@@ -38,6 +38,10 @@ __all__ = [
     "vocab_argmax",
     "vocab_sample",
     "tree_accept_walk",
+    "draft_tree_new",
+    "draft_tree_expand",
+    "draft_tree_select",
+    "draft_tree",
     "rollback_selection",
     "gather_positions",
     "gather_layer",
@@ -310,6 +314,110 @@ def vocab_sample(logits, uniforms, uniform_stride: int, temperature: float, top_
                 break
         out[n] = order[pick]
     return out
+
+
+# ----------------------------------------------------------------------------
+# Before step 1: growing the draft tree from the drafter's confidence.
+# ----------------------------------------------------------------------------
+#
+# The pages name the choice and its signal, not the procedure: the branches
+# go where the drafter is confident (EAGLE-2), which needs the drafter's
+# per-step logits beyond their argmax ([I1204] "What this needs", the fourth
+# decision); a drafter that does not branch yields a linear tree, and the
+# runner-up at an uncertain step is the alternative worth a verify position
+# ([PR1212] Drafter::draft_tree commit); one verify holds the draft chain plus
+# alternative leaves picked by a top-16 selector, sixteen unique shared-prefix
+# candidates ([S728] "What it does", description). The reading taken is the
+# published EAGLE-2 procedure (Li et al. 2024, "EAGLE-2: Faster Inference of
+# Language Models with Dynamic Draft Trees"), stated in our own terms:
+#   * a candidate's score is the log of its path probability, the sum of the
+#     drafter's log-softmax at every step from the root;
+#   * expansion, one depth at a time: every frontier node's drafter row gives
+#     its top_k tokens by logit as children; the next frontier is the top_k
+#     of the new candidates by score; the first frontier is the root alone;
+#   * rerank: the tree is the root plus the n_nodes - 1 best candidates by
+#     score over every depth. A child's score never exceeds its parent's and
+#     ties go to the candidate made first (parents are made before children),
+#     so the chosen set is closed under parents. Labels follow that rank, which
+#     is a topological order.
+# Ties among a row's logits go to the lower token index (the argmax order);
+# equal scores go to the lower candidate index. Scores are float64.
+
+def draft_tree_new(root_token: int) -> dict:
+    """An empty candidate table for one sequence whose committed token (node
+    0 of the tree) is root_token; the first frontier is the root alone."""
+    return {"root": int(root_token), "token": [], "parent": [], "score": [], "depth": [],
+            "frontier": [-1]}
+
+
+def _log_softmax_row(x32) -> np.ndarray:
+    x = np.asarray(x32, dtype=np.float32).astype(np.float64)
+    if not np.isfinite(x).all():
+        raise ValueError("drafter logits must be finite")
+    m = x.max()
+    return x - (m + np.log(np.sum(np.exp(x - m))))
+
+
+def draft_tree_expand(state: dict, rows, top_k: int) -> dict:
+    """One depth of confidence branching: rows[f] is the drafter's logit row
+    for frontier node f (in frontier order). Each row contributes its top_k
+    tokens (fp32 logits, ties to the lower index) as children of that frontier
+    node, scored parent score + log-softmax; the new frontier is the top_k of
+    this depth's candidates by score (ties to the lower candidate index), best
+    first. Mutates and returns state."""
+    rows = np.asarray(rows, dtype=np.float32)
+    frontier = state["frontier"]
+    assert rows.ndim == 2 and rows.shape[0] == len(frontier), "one row per frontier node"
+    V = rows.shape[1]
+    assert 1 <= top_k <= V
+    first = len(state["token"])
+    for f, u in enumerate(frontier):
+        lp = _log_softmax_row(rows[f])
+        base = 0.0 if u < 0 else state["score"][u]
+        d = 1 if u < 0 else state["depth"][u] + 1
+        # descending by fp32 logit, ties by index: a stable sort of -x
+        order = np.argsort(-rows[f], kind="stable")[:top_k]
+        for tok in order:
+            state["token"].append(int(tok))
+            state["parent"].append(int(u))
+            state["score"].append(base + float(lp[tok]))
+            state["depth"].append(d)
+    new = list(range(first, len(state["token"])))
+    new.sort(key=lambda c: (-state["score"][c], c))
+    state["frontier"] = new[:top_k]
+    return state
+
+
+def draft_tree_select(state: dict, n_nodes: int):
+    """Rerank: node 0 is the root; nodes 1..n_nodes-1 are the best candidates
+    by score (ties to the lower candidate index), labelled in that order.
+    Returns (parent int32 [n], token int32 [n], score float64 [n]); the root's
+    parent is -1 and its score 0."""
+    n_cand = len(state["token"])
+    if n_nodes < 1 or n_nodes - 1 > n_cand:
+        raise ValueError(f"{n_nodes} nodes need {n_nodes - 1} candidates, the table holds {n_cand}")
+    ranked = sorted(range(n_cand), key=lambda c: (-state["score"][c], c))[: n_nodes - 1]
+    label = {c: r + 1 for r, c in enumerate(ranked)}
+    parent = np.full(n_nodes, -1, np.int32)
+    token = np.zeros(n_nodes, np.int32)
+    score = np.zeros(n_nodes, np.float64)
+    token[0] = state["root"]
+    for c in ranked:
+        u = state["parent"][c]
+        parent[label[c]] = 0 if u < 0 else label[u]
+        token[label[c]] = state["token"][c]
+        score[label[c]] = state["score"][c]
+    return parent, token, score
+
+
+def draft_tree(root_token: int, depth_rows, top_k: int, n_nodes: int):
+    """The whole construction for one sequence: depth_rows[d] holds the
+    drafter's rows for the frontier at depth d + 1 (one row at d = 0, top_k
+    rows after). Returns draft_tree_select's result and the state."""
+    st = draft_tree_new(root_token)
+    for rows in depth_rows:
+        draft_tree_expand(st, rows, top_k)
+    return draft_tree_select(st, n_nodes) + (st,)
 
 
 # ----------------------------------------------------------------------------

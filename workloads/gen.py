@@ -34,6 +34,7 @@ __all__ = [
     "unique_fp16_scales",
     "make_kv_cache",
     "make_queries",
+    "draft_rows",
 ]
 
 
@@ -308,3 +309,16 @@ def make_queries(seed: int, stream: int, n_nodes: int, Hq: int, D: int, dtype: s
     """Q [n_nodes, Hq, D] ~ N(0, 1): float32, or bf16 bit patterns."""
     x = rng_for(seed, stream).standard_normal((n_nodes, Hq, D), dtype=np.float32)
     return x if dtype == "f32" else to_bf16_bits(x)
+
+
+def draft_rows(seed: int, B: int, n_depths: int, top_k: int, vocab: int, sigma: float = 2.0) -> list:
+    """Synthetic drafter logits for confidence branching, fp32 N(0, sigma^2):
+    entry d is [B, F_d, vocab] with F_0 = 1 (the root's row) and F_d = top_k
+    after (one row per frontier slot). The rows stand in for a drafter run on
+    the frontier; they do not depend on which candidates the frontier holds."""
+    out = []
+    for d in range(n_depths):
+        F = 1 if d == 0 else top_k
+        r = rng_for(seed, 40, d)
+        out.append((r.standard_normal((B, F, vocab), dtype=np.float32) * np.float32(sigma)).astype(np.float32))
+    return out
