@@ -2,6 +2,8 @@
  * ttv.h -- token-tree verification hot path on AMD Instinct MI355X (gfx950).
  *
  * One speculative verify round over a batch of draft trees:
+ *   draft_tree_expand,   grow each round's tree from the drafter's
+ *   draft_tree_select    confidence (expand by top-k, rerank by path score)
  *   tree_build_mask      ancestor bitsets from a per-round parent[] topology
  *   tree_verify_attention tree-masked GQA attention over the KV prefix plus
  *                        each node's ancestors
@@ -64,6 +66,8 @@ typedef enum ttv_status {
 #define TTV_DEV_OK 0
 #define TTV_DEV_BAD_PARENT 1    /* parent[0] != -1 or parent[i] not in [0, i) */
 #define TTV_DEV_BAD_SELECTION 2 /* selection not strictly increasing / out of range / too long */
+#define TTV_DEV_BAD_LOGITS 3    /* a drafter logit row holds a NaN or an infinity */
+#define TTV_DEV_DRAFT_STATE 4   /* a draft candidate table cannot take the call (see draft_tree_expand) */
 
 typedef enum ttv_dtype {
   TTV_F32 = 0,  /* float32 */
@@ -104,6 +108,62 @@ typedef struct ttv_kv_layer {
   int32_t D;
   int32_t cap;        /* allocated rows per (b, head) */
 } ttv_kv_layer;
+
+/*
+ * Before step 1 -- growing the draft tree from drafter confidence [I1204]
+ * "What this needs" (where the branches go: EAGLE-2 branches by drafter
+ * confidence, which needs the drafter's logits past their argmax); [PR1212]
+ * Drafter::draft_tree commit (a non-branching drafter gives a linear tree;
+ * the runner-up at an uncertain step is the alternative worth verifying);
+ * [S728] "What it does" (the chain plus alternatives from a top-k selector).
+ * Reading: EAGLE-2's expand-then-rerank. A candidate's score is its float64
+ * path log-probability, the sum of the drafter's log-softmax along the path.
+ *
+ * Per sequence b the caller owns a candidate table of cand_cap entries
+ * (cand_cap <= 4096) and a frontier of top_k slots:
+ *   cand_token, cand_parent (device) int32 [B][cand_cap]; parent is a
+ *                       candidate index of the same sequence, -1 = the root
+ *   cand_score  (device) float64 [B][cand_cap]
+ *   cand_count  (device) int32 [B]       candidates in the table
+ *   frontier    (device) int32 [B][top_k] candidate indices, best first
+ *
+ * draft_tree_expand adds one depth to every sequence's table. depth == 1
+ * starts afresh (the count is reset, the frontier is the root alone, one row
+ * per sequence); depth > 1 expands the frontier the previous call left.
+ *   logits (device) fp32, row b * F + f at logits + row * row_stride is the
+ *          drafter's row for frontier slot f of sequence b; F = 1 at depth 1
+ *          and top_k after. Rows must be finite.
+ * Each row's top_k tokens (by fp32 logit, ties to the lower token) are
+ * appended, row by row and best first, as children of that frontier node,
+ * scored parent score + logit - log(sum(exp(row))); the new frontier is the
+ * top_k of those F * top_k candidates by score (ties to the lower index).
+ * Limits (TTV_ERR_INVALID): 1 <= B <= TTV_MAX_BATCH, 1 <= top_k <= 16,
+ * top_k <= vocab <= 2^31 - 1, row_stride >= vocab, top_k <= cand_cap <= 4096,
+ * ceil(vocab / 4096) * top_k <= 65536. ws: >= draft_tree_expand_ws(B * F,
+ * vocab, top_k) bytes, contents irrelevant. Device checks: a row with a NaN
+ * or an infinity stores TTV_DEV_BAD_LOGITS; a table without room for the
+ * depth (count + F * top_k > cand_cap) or without a frontier stores
+ * TTV_DEV_DRAFT_STATE. Either leaves that sequence's table untouched.
+ *
+ * draft_tree_select writes each sequence's tree of n_nodes (<= 64) nodes at
+ * parent/token[b * n_nodes ...] (so node_off[b] = b * n_nodes for the calls
+ * below): node 0 is root_token[b] with parent -1; nodes 1.. are the
+ * n_nodes - 1 best candidates of the table by score (ties to the lower
+ * index), labelled in that order, which is topological. node_score (device,
+ * nullable) float64 [B * n_nodes] gets the scores (0 for the root). A table
+ * with fewer than n_nodes - 1 candidates, or one whose chosen set is not
+ * closed under parents, stores TTV_DEV_DRAFT_STATE and writes nothing for
+ * that sequence.
+ */
+size_t draft_tree_expand_ws(int32_t n_rows, int64_t vocab, int32_t top_k);
+ttv_status draft_tree_expand(int32_t B, int32_t depth, int32_t top_k, const float* logits, int64_t vocab,
+                             int64_t row_stride, int32_t* cand_token, int32_t* cand_parent, double* cand_score,
+                             int32_t* cand_count, int32_t cand_cap, int32_t* frontier, int32_t* dev_status, void* ws,
+                             size_t ws_bytes, void* stream);
+ttv_status draft_tree_select(int32_t B, int32_t n_nodes, const int32_t* root_token, const int32_t* cand_token,
+                             const int32_t* cand_parent, const double* cand_score, const int32_t* cand_count,
+                             int32_t cand_cap, int32_t* parent, int32_t* token, double* node_score,
+                             int32_t* dev_status, void* stream);
 
 /*
  * Step 1 -- ancestor mask [I1204] "What this needs" (1), "Increment 3";

@@ -255,3 +255,36 @@ def test_window_attention_validation():
     st = C["tree_verify_attention_window"](ctypes.byref(b), FAKE, ttv.TTV_BF16, 40, ctypes.byref(L), None, 0.1, 8,
                                            FAKE, FAKE, 4, None)
     assert st == ttv.TTV_ERR_WORKSPACE
+
+
+def test_draft_validation():
+    E, S = C["draft_tree_expand"], C["draft_tree_select"]
+    V = 248320
+    ws = C["draft_tree_expand_ws"](16, V, 4)
+    nc = (V + 4095) // 4096
+    assert ws == 16 * nc * 4 * 8 + 16 * nc * 16
+
+    def expand(B=2, depth=1, k=4, vocab=V, stride=V, cap=128, ws_bytes=ws, logits=FAKE):
+        return E(B, depth, k, logits, vocab, stride, FAKE, FAKE, FAKE, FAKE, cap, FAKE, FAKE, FAKE, ws_bytes, None)
+
+    assert expand(B=0) == ttv.TTV_ERR_INVALID and "B 0" in ttv.last_error()
+    assert expand(depth=0) == ttv.TTV_ERR_INVALID
+    assert expand(k=17) == ttv.TTV_ERR_INVALID and "top_k 17" in ttv.last_error()
+    assert expand(vocab=3) == ttv.TTV_ERR_INVALID
+    assert expand(stride=V - 1) == ttv.TTV_ERR_INVALID and "row_stride" in ttv.last_error()
+    assert expand(cap=4097) == ttv.TTV_ERR_INVALID and "cand_cap" in ttv.last_error()
+    assert expand(cap=3) == ttv.TTV_ERR_INVALID
+    assert expand(logits=None) == ttv.TTV_ERR_INVALID and "NULL" in ttv.last_error()
+    assert expand(ws_bytes=ws - 1, B=16) == ttv.TTV_ERR_WORKSPACE
+    # depth > 1 reads top_k rows per sequence: 4 sequences need the ws of 16 rows
+    assert expand(B=4, depth=2, ws_bytes=ws - 1) == ttv.TTV_ERR_WORKSPACE
+    assert expand(k=16, vocab=1 << 30, stride=1 << 30, ws_bytes=1 << 62) == ttv.TTV_ERR_INVALID
+
+    def select(B=2, n=16, cap=128, out=FAKE):
+        return S(B, n, FAKE, FAKE, FAKE, FAKE, FAKE, cap, out, FAKE, None, FAKE, None)
+
+    assert select(n=65) == ttv.TTV_ERR_INVALID and "n_nodes 65" in ttv.last_error()
+    assert select(n=0) == ttv.TTV_ERR_INVALID
+    assert select(B=129) == ttv.TTV_ERR_INVALID
+    assert select(cap=0) == ttv.TTV_ERR_INVALID
+    assert select(out=None) == ttv.TTV_ERR_INVALID

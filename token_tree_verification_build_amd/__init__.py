@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libttv.so")
 
 TTV_OK, TTV_ERR_INVALID, TTV_ERR_UNSUPPORTED, TTV_ERR_WORKSPACE, TTV_ERR_HIP = range(5)
-TTV_DEV_OK, TTV_DEV_BAD_PARENT, TTV_DEV_BAD_SELECTION = 0, 1, 2
+TTV_DEV_OK, TTV_DEV_BAD_PARENT, TTV_DEV_BAD_SELECTION, TTV_DEV_BAD_LOGITS, TTV_DEV_DRAFT_STATE = 0, 1, 2, 3, 4
 TTV_F32, TTV_BF16, TTV_I8 = 0, 1, 2
 MAX_NODES = 64
 MAX_BATCH = 128
@@ -77,6 +77,10 @@ _c = {
     "kv_gather_within_tail": _sig("kv_gather_within_tail", _i32,
                                   [_LP, _i32, _i32, _p, _i32, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "kv_can_gather_within_tail": _sig("kv_can_gather_within_tail", _i32, [_LP, _i32, _i32, _p]),
+    "draft_tree_expand_ws": _sig("draft_tree_expand_ws", _sz, [_i32, _i64, _i32]),
+    "draft_tree_expand": _sig("draft_tree_expand", _i32, [_i32, _i32, _i32, _p, _i64, _i64, _p, _p, _p, _p, _i32,
+                                                          _p, _p, _p, _sz, _p]),
+    "draft_tree_select": _sig("draft_tree_select", _i32, [_i32, _i32, _p, _p, _p, _p, _p, _i32, _p, _p, _p, _p, _p]),
     "ttv_last_error": _sig("ttv_last_error", ctypes.c_char_p, []),
 }
 
@@ -383,3 +387,77 @@ def kv_can_gather_within_tail(layers, B: int, ring_wrapped=None) -> tuple[int, s
     arr = _layers_array(layers)
     st = _c["kv_can_gather_within_tail"](arr, len(layers), B, wp)
     return st, last_error()
+
+
+class DraftTable:
+    """Device candidate tables of a batch of draft trees (one per sequence):
+    cand_token / cand_parent int32 [B, cap], cand_score float64 [B, cap],
+    cand_count int32 [B], frontier int32 [B, top_k]."""
+
+    def __init__(self, B: int, top_k: int, cap: int, device="cuda"):
+        import torch
+        self.B, self.top_k, self.cap = int(B), int(top_k), int(cap)
+        self.cand_token = torch.zeros(B, cap, dtype=torch.int32, device=device)
+        self.cand_parent = torch.zeros(B, cap, dtype=torch.int32, device=device)
+        self.cand_score = torch.zeros(B, cap, dtype=torch.float64, device=device)
+        self.cand_count = torch.zeros(B, dtype=torch.int32, device=device)
+        self.frontier = torch.zeros(B, top_k, dtype=torch.int32, device=device)
+
+
+def draft_tree_expand_ws(n_rows: int, vocab: int, top_k: int) -> int:
+    return int(_c["draft_tree_expand_ws"](n_rows, vocab, top_k))
+
+
+def draft_tree_expand(table: DraftTable, depth: int, logits, status, ws, vocab=None, stream=None):
+    """One depth of confidence branching for every sequence. logits: float32
+    device tensor [B * F, >= vocab] or [B, F, >= vocab] with unit inner
+    stride, F = 1 at depth 1 and top_k after."""
+    import torch
+    if logits.dtype != torch.float32 or not logits.is_cuda or logits.stride(-1) != 1:
+        raise ValueError("logits must be a float32 device tensor with unit inner stride")
+    F = 1 if depth == 1 else table.top_k
+    B = table.B
+    if logits.dim() == 3:
+        if logits.shape[0] != B or logits.shape[1] != F:
+            raise ValueError(f"logits must be [B={B}, F={F}, V]")
+        if B * F == 1:
+            row_stride = logits.shape[-1]  # one row: any stride >= vocab
+        elif F == 1:
+            row_stride = logits.stride(0)
+        elif B == 1 or logits.stride(0) == F * logits.stride(1):
+            row_stride = logits.stride(1)
+        else:
+            raise ValueError("logits rows must be evenly spaced")
+    elif logits.dim() == 2:
+        if logits.shape[0] != B * F:
+            raise ValueError(f"logits must hold B * F = {B * F} rows")
+        row_stride = logits.stride(0) if B * F > 1 else logits.shape[-1]
+    else:
+        raise ValueError("logits must be 2-D or 3-D")
+    vocab = logits.shape[-1] if vocab is None else vocab
+    _dev(status, torch.int32, "status")
+    _check(_c["draft_tree_expand"](table.B, int(depth), table.top_k, _ptr(logits), vocab, row_stride,
+                                   _ptr(table.cand_token), _ptr(table.cand_parent), _ptr(table.cand_score),
+                                   _ptr(table.cand_count), table.cap, _ptr(table.frontier), _ptr(status), _ptr(ws),
+                                   ws.numel() if ws is not None else 0, _stream(stream)), "draft_tree_expand")
+
+
+def draft_tree_select(table: DraftTable, n_nodes: int, root_token, parent, token, status, node_score=None,
+                      stream=None):
+    """Trees of n_nodes nodes per sequence into parent / token int32 [B * n_nodes]
+    (node_off[b] = b * n_nodes); node_score float64 [B * n_nodes] optional."""
+    import torch
+    _dev(root_token, torch.int32, "root_token")
+    _dev(parent, torch.int32, "parent")
+    _dev(token, torch.int32, "token")
+    _dev(status, torch.int32, "status")
+    if parent.numel() < table.B * n_nodes or token.numel() < table.B * n_nodes or root_token.numel() < table.B:
+        raise ValueError("parent / token must hold B * n_nodes entries and root_token B")
+    if node_score is not None:
+        _dev(node_score, torch.float64, "node_score")
+        if node_score.numel() < table.B * n_nodes:
+            raise ValueError("node_score must hold B * n_nodes entries")
+    _check(_c["draft_tree_select"](table.B, int(n_nodes), _ptr(root_token), _ptr(table.cand_token),
+                                   _ptr(table.cand_parent), _ptr(table.cand_score), _ptr(table.cand_count), table.cap,
+                                   _ptr(parent), _ptr(token), _ptr(node_score), _ptr(status), _stream(stream)),
+           "draft_tree_select")

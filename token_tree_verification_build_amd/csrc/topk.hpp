@@ -1,0 +1,326 @@
+// Chunked top-k selection over vocabulary rows, shared by the sampled target
+// selection and the draft tree's expansion.
+//
+// Pass 1 streams the logits (HBM-bound): one wave per 4096-element chunk of a
+// row, 64 ordered values per lane in registers. The chunk's top-k is found without a
+// k-round scan over all of it: the k-th largest of the 64 lane maxima bounds
+// the chunk's k-th largest value from below (k lanes hold a value at least
+// that large), so only values at or above it are candidates; they are
+// compacted into LDS (rarely more than a few dozen) and the top k taken there.
+// Keys are 64-bit (ordered value << 32 | ~index), unique per element;
+// selections run bit by bit on ballots and popcounts, with no lane shuffles.
+// Optionally the same pass records each chunk's maximum and the float64 sum
+// of exp(x - max), from which a row's log-normaliser follows.
+// A row's top k over its chunks' candidates is then taken by one wave with
+// the same bound-and-compact scheme (row_topk_sorted).
+#pragma once
+
+#include "common.hpp"
+
+namespace ttv {
+
+constexpr int kSelMaxK = 64;
+constexpr int kSelLanes = 64;                         // lanes per wave
+constexpr int kSelPerLane = 64;                       // values per lane
+constexpr int kSelChunk = kSelLanes * kSelPerLane;    // 4096 values per wave
+constexpr int kSelWaves = 4;                          // waves (chunks) per pass-1 workgroup
+constexpr int kSelCap = 256;                          // candidate slots per wave in LDS
+constexpr int kSelMaxCand = 1 << 16;                  // chunk candidates per row (row_topk_sorted streams them)
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// per-chunk statistics of a row: max over the chunk, the float64 sum of
+// exp(x - max), and whether any value is NaN or infinite
+struct ChunkStats {
+  double sum;
+  float max;
+  int bad;
+};
+
+// ordered key: larger value first, equal values by lower index; -0.0 folded
+// onto +0.0, every NaN above every number
+__device__ __forceinline__ uint64_t sample_key(float x, uint32_t idx) {
+  uint32_t o;
+  if (x != x) {
+    o = 0xFFFFFFFFu;
+  } else {
+    uint32_t u = __float_as_uint(x);
+    if ((u << 1) == 0u) u = 0u;
+    o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  }
+  return (static_cast<uint64_t>(o) << 32) | static_cast<uint32_t>(0xFFFFFFFFu - idx);
+}
+__device__ __forceinline__ uint32_t key_index(uint64_t k) { return 0xFFFFFFFFu - static_cast<uint32_t>(k); }
+__device__ __forceinline__ float key_value(uint64_t k) {
+  const uint32_t o = static_cast<uint32_t>(k >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+// Wave-wide selection without lane shuffles: the largest t such that at
+// least `need` of the wave's keys (n per lane) are >= t, built bit by bit from
+// the top (the count is non-increasing in t) with ballots and popcounts. For
+// unique keys that is the need-th largest key; 0 when fewer than `need` are
+// nonzero.
+template <int N>
+__device__ __forceinline__ uint64_t wave_kth_largest(const uint64_t (&key)[N], int need) {
+  uint64_t t = 0;
+  for (int bit = 63; bit >= 0; --bit) {
+    const uint64_t cand = t | (1ull << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int s = 0; s < N; ++s) cnt += __popcll(__ballot(key[s] >= cand));
+    if (cnt >= need) t = cand;
+  }
+  return t;
+}
+
+// the lane's position among the set lanes of a wave-wide mask
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u)));
+}
+
+// ordered 32-bit value (the key's high half): 0 only for "no value"
+__device__ __forceinline__ uint32_t sample_ord(float x) { return static_cast<uint32_t>(sample_key(x, 0u) >> 32); }
+
+// 32-bit form of wave_kth_largest (one value per lane)
+__device__ __forceinline__ uint32_t wave_kth_largest32(uint32_t v, int need) {
+  uint32_t t = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = t | (1u << bit);
+    if (__popcll(__ballot(v >= cand)) >= need) t = cand;
+  }
+  return t;
+}
+
+// Pass 1: wave w of workgroup (g, row) takes chunk c = 4g + w of the row and
+// writes its top k keys (in no particular order; key 0, below every value,
+// fills slots a short chunk cannot) to cand[(row * n_chunks + c) * k ...].
+// With kStats, lane 0 also writes the chunk's ChunkStats to
+// stats[row * n_chunks + c].
+template <bool kStats>
+__global__ void __launch_bounds__(kSelLanes * kSelWaves)
+    chunk_topk(const float* __restrict__ logits, int64_t vocab, int64_t row_stride, int n_chunks, int k, int vec,
+               uint64_t* __restrict__ cand, ChunkStats* __restrict__ stats) {
+  __shared__ uint64_t s_cand[kSelWaves][kSelCap];
+  const int wave = threadIdx.x / kSelLanes;
+  const int lane = threadIdx.x % kSelLanes;
+  const int row = blockIdx.y;
+  const int c = blockIdx.x * kSelWaves + wave;
+  if (c >= n_chunks) return;  // whole wave; pass 1 has no workgroup barrier
+  const float* __restrict__ x = logits + static_cast<int64_t>(row) * row_stride;
+  const int64_t c0 = static_cast<int64_t>(c) * kSelChunk;
+  // the lane's ordered values: element c0 + 4 (64 j + lane) + q; past vocab 0
+  uint32_t ov[kSelPerLane];
+  auto idx_of = [&](int j) -> uint32_t { return static_cast<uint32_t>(c0 + 4 * (64 * (j >> 2) + lane) + (j & 3)); };
+  if (vec && c0 + kSelChunk <= vocab) {
+    const f32x4* __restrict__ xv = reinterpret_cast<const f32x4*>(x + c0);
+#pragma unroll
+    for (int j = 0; j < kSelPerLane / 4; ++j) {
+      const f32x4 a = __builtin_nontemporal_load(xv + 64 * j + lane);
+      ov[4 * j] = sample_ord(a.x);
+      ov[4 * j + 1] = sample_ord(a.y);
+      ov[4 * j + 2] = sample_ord(a.z);
+      ov[4 * j + 3] = sample_ord(a.w);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kSelPerLane; ++j) {
+      const int64_t i = c0 + 4 * (64 * (j >> 2) + lane) + (j & 3);
+      ov[j] = i < vocab ? sample_ord(x[i]) : 0u;
+    }
+  }
+  // tau = the k-th largest lane maximum value, a lower bound on the chunk's
+  // k-th largest value (k lanes hold a value at least that large); 0 when the
+  // chunk holds fewer than k values
+  uint32_t lmax = 0;
+#pragma unroll
+  for (int j = 0; j < kSelPerLane; ++j) lmax = ov[j] > lmax ? ov[j] : lmax;
+  if constexpr (kStats) {
+    // chunk maximum; NaN orders as 0xFFFFFFFF, +inf as 0xFF800000 and -inf
+    // as 0x007FFFFF, so those are the non-finite values
+    uint32_t wm = lmax;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const uint32_t o = static_cast<uint32_t>(__shfl_xor(static_cast<int>(wm), off));
+      wm = o > wm ? o : wm;
+    }
+    const double m = static_cast<double>(key_value(static_cast<uint64_t>(wm) << 32));
+    bool bad = false;
+    double s = 0.0;
+#pragma unroll
+    for (int j = 0; j < kSelPerLane; ++j) {
+      bad |= ov[j] >= 0xFF800000u || ov[j] == 0x007FFFFFu;
+      if (ov[j]) s += exp(static_cast<double>(key_value(static_cast<uint64_t>(ov[j]) << 32)) - m);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+    const bool any_bad = __ballot(bad) != 0;
+    if (lane == 0) {
+      ChunkStats st;
+      st.sum = s;
+      st.max = static_cast<float>(m);
+      st.bad = any_bad ? 1 : 0;
+      stats[static_cast<int64_t>(row) * n_chunks + c] = st;
+    }
+  }
+  const uint32_t tau = max(wave_kth_largest32(lmax, k), 1u);
+  // compact the candidates' full keys (values >= tau) into LDS
+  uint64_t* sc = s_cand[wave];
+  int total = 0;
+#pragma unroll
+  for (int j = 0; j < kSelPerLane; ++j) {
+    const bool is = ov[j] >= tau;
+    const uint64_t m = __ballot(is);
+    if (m == 0) continue;  // (most steps: candidates are few)
+    const int at = total + lanes_below(m);
+    if (is && at < kSelCap) sc[at] = (static_cast<uint64_t>(ov[j]) << 32) | (0xFFFFFFFFu - idx_of(j));
+    total += __popcll(m);
+  }
+  uint64_t* out = cand + (static_cast<int64_t>(row) * n_chunks + c) * k;
+  int n_out = 0;
+  if (total <= kSelCap) {
+    __builtin_amdgcn_wave_barrier();
+    // the k largest candidates: slots lane, lane + 64, ...
+    uint64_t h[kSelCap / kSelLanes];
+#pragma unroll
+    for (int s = 0; s < kSelCap / kSelLanes; ++s) {
+      const int at = lane + kSelLanes * s;
+      h[s] = at < total ? sc[at] : 0ull;
+    }
+    const uint64_t kth = wave_kth_largest(h, k);
+#pragma unroll
+    for (int s = 0; s < kSelCap / kSelLanes; ++s) {
+      const bool is = h[s] != 0 && h[s] >= kth;
+      const uint64_t m = __ballot(is);
+      if (is) out[n_out + lanes_below(m)] = h[s];
+      n_out += __popcll(m);
+    }
+  } else {
+    // more candidates than slots (values tied near the bound): the same
+    // selection over every value's full key, computed again
+    uint64_t t = 0;
+    for (int bit = 63; bit >= 0; --bit) {
+      const uint64_t cb = t | (1ull << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int j = 0; j < kSelPerLane; ++j) {
+        const uint64_t kj = ov[j] ? (static_cast<uint64_t>(ov[j]) << 32) | (0xFFFFFFFFu - idx_of(j)) : 0ull;
+        cnt += __popcll(__ballot(kj >= cb));
+      }
+      if (cnt >= k) t = cb;
+    }
+#pragma unroll
+    for (int j = 0; j < kSelPerLane; ++j) {
+      const uint64_t kj = ov[j] ? (static_cast<uint64_t>(ov[j]) << 32) | (0xFFFFFFFFu - idx_of(j)) : 0ull;
+      const bool is = kj != 0 && kj >= t;
+      const uint64_t m = __ballot(is);
+      if (is) out[n_out + lanes_below(m)] = kj;
+      n_out += __popcll(m);
+    }
+  }
+  for (int i = n_out + lane; i < k; i += kSelLanes) out[i] = 0;  // a chunk with fewer than k values
+}
+
+// One wave: the k largest of a row's n_cand chunk candidates cr[0..n_cand)
+// (the same bound-and-compact scheme, streaming the candidates), sorted
+// descending into s_top[0..k). s_c is kSelCap slots of LDS scratch. The row
+// must hold at least k values.
+__device__ __forceinline__ void row_topk_sorted(const uint64_t* __restrict__ cr, int n_cand, int k, int lane,
+                                                uint64_t* s_c, uint64_t* s_top) {
+  auto cand_at = [&](int at) -> uint64_t { return at < n_cand ? cr[at] : 0ull; };
+  // up to 64 * kRegCand candidates are held in registers (all loads in
+  // flight at once); more are streamed, eight loads a step
+  constexpr int kRegCand = 32;
+  uint64_t lmax[1] = {0};
+  int total = 0;
+  uint64_t tau;
+  if (n_cand <= kSelLanes * kRegCand) {
+    uint64_t v[kRegCand];
+#pragma unroll
+    for (int u = 0; u < kRegCand; ++u) v[u] = cand_at(u * kSelLanes + lane);
+#pragma unroll
+    for (int u = 0; u < kRegCand; ++u) lmax[0] = v[u] > lmax[0] ? v[u] : lmax[0];
+    tau = wave_kth_largest(lmax, k);
+#pragma unroll
+    for (int u = 0; u < kRegCand; ++u) {
+      const bool is = v[u] != 0 && v[u] >= tau;
+      const uint64_t m = __ballot(is);
+      const int at = total + lanes_below(m);
+      if (is && at < kSelCap) s_c[at] = v[u];
+      total += __popcll(m);
+    }
+  } else {
+    for (int base = 0; base < n_cand; base += 8 * kSelLanes) {
+      uint64_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = cand_at(base + u * kSelLanes + lane);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) lmax[0] = v[u] > lmax[0] ? v[u] : lmax[0];
+    }
+    tau = wave_kth_largest(lmax, k);
+    for (int base = 0; base < n_cand; base += 8 * kSelLanes) {
+      uint64_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = cand_at(base + u * kSelLanes + lane);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const bool is = v[u] != 0 && v[u] >= tau;
+        const uint64_t m = __ballot(is);
+        const int at = total + lanes_below(m);
+        if (is && at < kSelCap) s_c[at] = v[u];
+        total += __popcll(m);
+      }
+    }
+  }
+  int n_w = 0;  // winners: the k largest keys (distinct, nonzero; the row has at least k values)
+  if (total <= kSelCap) {
+    __builtin_amdgcn_wave_barrier();
+    uint64_t g[kSelCap / kSelLanes];
+#pragma unroll
+    for (int s = 0; s < kSelCap / kSelLanes; ++s) {
+      const int at = lane + kSelLanes * s;
+      g[s] = at < total ? s_c[at] : 0ull;
+    }
+    const uint64_t kth = wave_kth_largest(g, k);
+#pragma unroll
+    for (int s = 0; s < kSelCap / kSelLanes; ++s) {
+      const bool is = g[s] != 0 && g[s] >= kth;
+      const uint64_t m = __ballot(is);
+      if (is) s_top[n_w + lanes_below(m)] = g[s];
+      n_w += __popcll(m);
+    }
+  } else {
+    // more candidates than slots (values tied near the bound): the same
+    // bit-by-bit selection, counting over the streamed candidates
+    uint64_t t = 0;
+    for (int bit = 63; bit >= 0; --bit) {
+      const uint64_t cb = t | (1ull << bit);
+      int cnt = 0;
+      for (int base = 0; base < n_cand; base += kSelLanes) cnt += __popcll(__ballot(cand_at(base + lane) >= cb));
+      if (cnt >= k) t = cb;
+    }
+    for (int base = 0; base < n_cand; base += kSelLanes) {
+      const uint64_t v = cand_at(base + lane);
+      const bool is = v != 0 && v >= t;
+      const uint64_t m = __ballot(is);
+      if (is) s_top[n_w + lanes_below(m)] = v;
+      n_w += __popcll(m);
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  // sort the k winners descending: each lane's rank is the count of larger keys
+  const uint64_t mine = lane < k ? s_top[lane] : 0ull;
+  int rank = 0;
+  for (int j = 0; j < k; ++j) {
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(mine)), j));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(mine >> 32), j));
+    rank += ((static_cast<uint64_t>(hi) << 32) | lo) > mine ? 1 : 0;
+  }
+  __builtin_amdgcn_wave_barrier();
+  if (lane < k) s_top[rank] = mine;
+  __builtin_amdgcn_wave_barrier();
+}
+
+inline int sel_chunks(int64_t vocab) { return static_cast<int>((vocab + kSelChunk - 1) / kSelChunk); }
+
+}  // namespace ttv
