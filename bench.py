@@ -351,6 +351,45 @@ def main():
     print(f"[bench] sampled selection {samp_ms * 1e3:.1f} us ({kernels['vocab_sample']['GBps']} GB/s)",
           file=sys.stderr, flush=True)
 
+    # draft tree construction (the step before the mask): per sequence, 8
+    # depths of top-4 confidence branching over the drafter's rows, then the
+    # 16-node rerank; the drafter's rows are synthetic N(0, 2^2)
+    Bd, kd, depths_d, nd = batch.B, 4, 8, 16
+    gen_d = torch.Generator(device=dev).manual_seed(11)
+    d_rows = [torch.randn(Bd, 1 if d == 0 else kd, V, device=dev, generator=gen_d) * 2.0 for d in range(depths_d)]
+    d_table = ttv.DraftTable(Bd, kd, kd + (depths_d - 1) * kd * kd, device=dev)
+    d_ws = torch.empty(ttv.draft_tree_expand_ws(Bd * kd, V, kd), dtype=torch.uint8, device=dev)
+    d_st = torch.zeros(1, dtype=torch.int32, device=dev)
+    d_root = torch.zeros(Bd, dtype=torch.int32, device=dev)
+    d_parent = torch.empty(Bd * nd, dtype=torch.int32, device=dev)
+    d_token = torch.empty(Bd * nd, dtype=torch.int32, device=dev)
+
+    def build_draft():
+        for d in range(depths_d):
+            ttv.draft_tree_expand(d_table, d + 1, d_rows[d], d_st, d_ws)
+        ttv.draft_tree_select(d_table, nd, d_root, d_parent, d_token, d_st)
+
+    build_draft()
+    torch.cuda.synchronize()
+    assert int(d_st.item()) == 0, "draft tree status"
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        build_draft()
+    e1.record()
+    torch.cuda.synchronize()
+    draft_ms = e0.elapsed_time(e1) / 20
+    dbytes = sum(r.numel() for r in d_rows) * 4
+    kernels["draft_tree"] = {
+        "avg_us": round(draft_ms * 1e3, 2), "bytes": dbytes, "GBps": round(dbytes / (draft_ms / 1e3) / 1e9, 1),
+        "frac_hbm": round(dbytes / (draft_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        "what": f"{Bd} trees of {nd} nodes: {depths_d} expansions of top-{kd} over {V}-logit drafter rows "
+                f"(1 row, then {kd} per sequence) + rerank",
+    }
+    print(f"[bench] draft tree {draft_ms * 1e3:.1f} us ({kernels['draft_tree']['GBps']} GB/s)",
+          file=sys.stderr, flush=True)
+    del d_rows
+
     # full-window out-of-place gather (the pages' take): every survivor of every layer rewritten
     if not args.no_take:
         dst_caches = [{k: torch.empty_like(t) for k, t in c.items()} for c in caches]

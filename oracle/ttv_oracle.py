@@ -12,6 +12,9 @@ Sources, cited by page title and section:
           widening the gather to every sequence-axis buffer, the history-mask
           commit, the Gemma 4 tree-verify commit, the verify_finalize_tree
           commit, the gather_within_tail commit, the rollback-to-path commit.
+  [I1185] mlxcel issue #1185, "cut the MTP drafter's per-step cost" --
+          "Proposed work" (Phase 2a: fuse the LM-head projection and the
+          argmax).
   [S728]  splash issue #728, "Experiment: qualify shared-prefix tree
           verification and conservative admission" -- "What it does",
           "Results", "Earlier controlled experiments".
@@ -37,6 +40,8 @@ __all__ = [
     "tree_verify_attention_dense",
     "vocab_argmax",
     "vocab_sample",
+    "lm_head_logits",
+    "lm_head_argmax",
     "tree_accept_walk",
     "draft_tree_new",
     "draft_tree_expand",
@@ -255,6 +260,25 @@ def vocab_argmax(logits) -> np.ndarray:
     Ties go to the lowest index; -0.0 equals +0.0; a NaN outranks every number
     and the first NaN wins (numpy.argmax semantics)."""
     return np.argmax(np.asarray(logits, dtype=np.float32), axis=-1).astype(np.int32)
+
+
+def lm_head_logits(hidden_bits, weight_bits) -> np.ndarray:
+    """The target's logits at every node from its final hidden state: the LM
+    head's projection logits[n, v] = sum_i hidden[n, i] * weight[v, i], with
+    bf16 hidden states [N, H] and a bf16 head weight [V, H] (vocabulary rows),
+    in float64 ([I1185] "Proposed work", Phase 2a: at temperature 0 the
+    vocabulary-wide logits exist only to take their argmax)."""
+    X = decode_bf16(hidden_bits)
+    W = decode_bf16(weight_bits)
+    return X @ W.T
+
+
+def lm_head_argmax(hidden_bits, weight_bits) -> np.ndarray:
+    """The fused projection-plus-argmax of [I1185] Phase 2a: the index of the
+    largest logit of lm_head_logits, ties to the lowest index. The fused form
+    never writes the logits; its result is this argmax wherever the float32
+    accumulation of the projection cannot reorder the top logits."""
+    return np.argmax(lm_head_logits(hidden_bits, weight_bits), axis=-1).astype(np.int32)
 
 
 def vocab_sample(logits, uniforms, uniform_stride: int, temperature: float, top_k: int, top_p: float) -> np.ndarray:

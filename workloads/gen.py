@@ -35,6 +35,7 @@ __all__ = [
     "make_kv_cache",
     "make_queries",
     "draft_rows",
+    "lm_head_inputs",
 ]
 
 
@@ -322,3 +323,24 @@ def draft_rows(seed: int, B: int, n_depths: int, top_k: int, vocab: int, sigma: 
         r = rng_for(seed, 40, d)
         out.append((r.standard_normal((B, F, vocab), dtype=np.float32) * np.float32(sigma)).astype(np.float32))
     return out
+
+
+def lm_head_inputs(seed: int, N: int, H: int, V: int, planted=None, duplicate=None):
+    """Synthetic LM-head operands as bf16 bit patterns: hidden states [N, H]
+    N(0, 1) and a head weight [V, H] N(0, 1/H) (unit-variance logits).
+    planted: {node n: vocab row t} makes row t a multiple of hidden[n]'s
+    direction, so t carries node n's largest logit by a wide margin.
+    duplicate: [(a, b)] copies weight row a onto row b (equal logits)."""
+    r = rng_for(seed, 50)
+    X = r.standard_normal((N, H), dtype=np.float32)
+    W = r.standard_normal((V, H), dtype=np.float32) * np.float32(1.0 / np.sqrt(H))
+    hb = to_bf16_bits(X)
+    if planted:
+        for n, t in planted.items():
+            W[t] = bf16_bits_to_f32(hb[n]) * np.float32(4.0 / np.sqrt(H))
+    wb = to_bf16_bits(W)
+    if duplicate:
+        for a, b in duplicate:
+            wb[b] = wb[a]
+    return hb, wb
+
