@@ -390,6 +390,38 @@ def main():
           file=sys.stderr, flush=True)
     del d_rows
 
+    # the argmax fused with the LM-head projection (logits never written):
+    # the pages' head, 248,320 vocabulary rows of a 5,120-wide hidden state,
+    # bf16 synthetic weights, for this round's nodes and for one 16-node tree
+    H_lm = 5120
+    gen_lm = torch.Generator(device=dev).manual_seed(12)
+    w_lm = (torch.randn(V, H_lm, device=dev, generator=gen_lm) * (1.0 / H_lm ** 0.5)).to(torch.bfloat16)
+    for n_lm in sorted({int(batch.n_nodes), 16}):
+        x_lm = torch.randn(n_lm, H_lm, device=dev, generator=gen_lm).to(torch.bfloat16)
+        o_lm = torch.empty(n_lm, dtype=torch.int32, device=dev)
+        ws_lm = torch.empty(ttv.lm_head_argmax_ws(n_lm, V), dtype=torch.uint8, device=dev)
+        ttv.lm_head_argmax(x_lm, w_lm, o_lm, ws_lm)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            ttv.lm_head_argmax(x_lm, w_lm, o_lm, ws_lm)
+        e1.record()
+        torch.cuda.synchronize()
+        lm_ms = e0.elapsed_time(e1) / 10
+        lbytes = V * H_lm * 2 + n_lm * H_lm * 2
+        lflops = 2 * n_lm * V * H_lm
+        kernels[f"lm_head_argmax_n{n_lm}"] = {
+            "avg_us": round(lm_ms * 1e3, 2), "bytes": lbytes, "GBps": round(lbytes / (lm_ms / 1e3) / 1e9, 1),
+            "frac_hbm": round(lbytes / (lm_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4), "flops": lflops,
+            "TFLOPs": round(lflops / (lm_ms / 1e3) / 1e12, 1),
+            "what": f"{n_lm} nodes x {V} x {H_lm} bf16 head, fused argmax (main + reduce launches)",
+        }
+        print(f"[bench] lm head + argmax, {n_lm} nodes: {lm_ms * 1e3:.1f} us "
+              f"({kernels[f'lm_head_argmax_n{n_lm}']['GBps']} GB/s)", file=sys.stderr, flush=True)
+        del x_lm
+    del w_lm
+
     # full-window out-of-place gather (the pages' take): every survivor of every layer rewritten
     if not args.no_take:
         dst_caches = [{k: torch.empty_like(t) for k, t in c.items()} for c in caches]

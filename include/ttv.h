@@ -10,6 +10,8 @@
  *   vocab_argmax         per-node argmax over the target's vocabulary logits
  *   vocab_sample         per-node draw from the nucleus-filtered distribution
  *                        (the sampled form of the target's selection)
+ *   lm_head_argmax       the argmax fused with the LM-head projection, the
+ *                        logits never written
  *   tree_accept_walk     descend the one child matching the target's argmax
  *   kv_gather_positions  compact the accepted path's K/V (and int8 scales)
  *                        along the sequence axis
@@ -23,6 +25,8 @@
  *            chain, so an MTP round emits more than 2.33 tokens"
  *   [PR1212] mlxcel PR #1212 "feat(speculative): draft and verify a token
  *            tree, behind a flag, default off" (its commit messages)
+ *   [I1185]  mlxcel issue #1185 "perf(speculative): cut the MTP drafter's
+ *            per-step cost" (its "Proposed work" phases)
  *   [S728]   splash issue #728 "Experiment: qualify shared-prefix tree
  *            verification and conservative admission"
  *
@@ -297,6 +301,27 @@ size_t vocab_sample_ws(int64_t n_rows, int64_t vocab, int32_t top_k);
 ttv_status vocab_sample(const float* logits, int64_t n_rows, int64_t vocab, int64_t row_stride,
                         const float* uniforms, int64_t uniform_stride, float temperature, int32_t top_k,
                         float top_p, int32_t* out_idx, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Step 3, fused with the LM head -- [I1185] mlxcel issue #1185 "Proposed
+ * work", Phase 2a: at temperature 0 the vocabulary-wide logits exist only for
+ * their argmax, so the projection and the argmax are fused and the logits are
+ * never written. out_idx[n] = the lowest v maximising
+ * sum_i hidden[n][i] * weight[v][i] (fp32 accumulation of exact bf16
+ * products; -0.0 == +0.0; a NaN outranks every number).
+ *   hidden (device) bf16 [n_rows][hidden_stride], the nodes' final hidden states
+ *   weight (device) bf16 [vocab][weight_stride], one vocabulary row per H-vector
+ *   out_idx (device) int32 [n_rows]
+ * Limits (TTV_ERR_INVALID): 0 <= n_rows <= 2^24, 1 <= vocab <= 2^31 - 1,
+ * hidden_dim a positive multiple of 64 (<= 2^20), strides >= hidden_dim and
+ * multiples of 8, hidden and weight 16-byte aligned. ws: >=
+ * lm_head_argmax_ws(n_rows, vocab) bytes, contents irrelevant. The weight is
+ * read once per 128 nodes.
+ */
+size_t lm_head_argmax_ws(int64_t n_rows, int64_t vocab);
+ttv_status lm_head_argmax(const uint16_t* hidden, int64_t n_rows, int64_t hidden_stride, const uint16_t* weight,
+                          int64_t vocab, int64_t hidden_dim, int64_t weight_stride, int32_t* out_idx, void* ws,
+                          size_t ws_bytes, void* stream);
 
 /*
  * Step 4 -- accept walk [I1204] "What this needs" (2), "Increment 1"; [S728]

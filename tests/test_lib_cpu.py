@@ -288,3 +288,23 @@ def test_draft_validation():
     assert select(B=129) == ttv.TTV_ERR_INVALID
     assert select(cap=0) == ttv.TTV_ERR_INVALID
     assert select(out=None) == ttv.TTV_ERR_INVALID
+
+
+def test_lm_head_validation():
+    A = C["lm_head_argmax"]
+    V, H = 248320, 5120
+    ws = C["lm_head_argmax_ws"](16, V)
+    assert ws == 16 * ((V + 511) // 512) * 8
+
+    def call(n=16, hs=H, w=FAKE, v=V, h=H, wst=H, out=FAKE, ws_bytes=ws, x=FAKE):
+        return A(x, n, hs, w, v, h, wst, out, FAKE, ws_bytes, None)
+
+    assert call(n=0) == ttv.TTV_OK  # nothing to do
+    assert call(n=-1) == ttv.TTV_ERR_INVALID
+    assert call(v=0) == ttv.TTV_ERR_INVALID and "vocab" in ttv.last_error()
+    assert call(h=100, hs=104, wst=104) == ttv.TTV_ERR_INVALID and "multiple of 64" in ttv.last_error()
+    assert call(hs=H - 8) == ttv.TTV_ERR_INVALID and "strides" in ttv.last_error()
+    assert call(wst=H + 4) == ttv.TTV_ERR_INVALID
+    assert call(w=None) == ttv.TTV_ERR_INVALID and "NULL" in ttv.last_error()
+    assert call(x=FAKE + 2) == ttv.TTV_ERR_INVALID and "aligned" in ttv.last_error()
+    assert call(ws_bytes=ws - 1) == ttv.TTV_ERR_WORKSPACE

@@ -81,6 +81,8 @@ _c = {
     "draft_tree_expand": _sig("draft_tree_expand", _i32, [_i32, _i32, _i32, _p, _i64, _i64, _p, _p, _p, _p, _i32,
                                                           _p, _p, _p, _sz, _p]),
     "draft_tree_select": _sig("draft_tree_select", _i32, [_i32, _i32, _p, _p, _p, _p, _p, _i32, _p, _p, _p, _p, _p]),
+    "lm_head_argmax_ws": _sig("lm_head_argmax_ws", _sz, [_i64, _i64]),
+    "lm_head_argmax": _sig("lm_head_argmax", _i32, [_p, _i64, _i64, _p, _i64, _i64, _i64, _p, _p, _sz, _p]),
     "ttv_last_error": _sig("ttv_last_error", ctypes.c_char_p, []),
 }
 
@@ -461,3 +463,28 @@ def draft_tree_select(table: DraftTable, n_nodes: int, root_token, parent, token
                                    _ptr(table.cand_parent), _ptr(table.cand_score), _ptr(table.cand_count), table.cap,
                                    _ptr(parent), _ptr(token), _ptr(node_score), _ptr(status), _stream(stream)),
            "draft_tree_select")
+
+
+def lm_head_argmax_ws(n_rows: int, vocab: int) -> int:
+    return int(_c["lm_head_argmax_ws"](n_rows, vocab))
+
+
+def lm_head_argmax(hidden, weight, out_idx, ws, stream=None):
+    """hidden: bf16 device tensor [N, >= H]; weight: bf16 device tensor
+    [V, >= H] (H = hidden.shape[1] unless the views differ), unit inner
+    strides; out_idx int32 [N]."""
+    import torch
+    for t, name in ((hidden, "hidden"), (weight, "weight")):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or t.dim() != 2 or t.stride(-1) != 1:
+            raise ValueError(f"{name} must be a 2-D bf16 device tensor with unit inner stride")
+    if hidden.shape[1] != weight.shape[1]:
+        raise ValueError("hidden and weight must share the hidden dimension")
+    _dev(out_idx, torch.int32, "out_idx")
+    N, H = hidden.shape
+    V = weight.shape[0]
+    if out_idx.numel() < N:
+        raise ValueError("out_idx must hold one index per hidden row")
+    hs = hidden.stride(0) if N > 1 else H + (-H) % 8
+    wst = weight.stride(0) if V > 1 else H + (-H) % 8
+    _check(_c["lm_head_argmax"](_ptr(hidden), N, hs, _ptr(weight), V, H, wst, _ptr(out_idx), _ptr(ws),
+                                ws.numel() if ws is not None else 0, _stream(stream)), "lm_head_argmax")

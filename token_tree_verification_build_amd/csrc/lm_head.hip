@@ -1,0 +1,274 @@
+// The LM-head projection fused with the greedy selection: the target's logit
+// row of every node is the product of its final hidden state with the head
+// weight, and at temperature 0 the row exists only for its argmax ([I1185]
+// mlxcel issue #1185, "Proposed work", Phase 2a: a fused projection-plus-
+// argmax kernel never writes the logits). Ties go to the lowest index, as in
+// vocab_argmax (-0.0 equals +0.0, a NaN outranks every number).
+//
+// Operands: hidden states X [N][H] and the head weight W [V][H] (one
+// vocabulary row per H-vector), both bf16; fp32 accumulation on the matrix
+// cores (v_mfma_f32_16x16x32_bf16: bf16 x bf16 products are exact in fp32).
+// The weight dominates the bytes (V * H * 2), each element is used by one
+// wave only, so it goes straight from HBM to registers: a wave owns 64
+// vocabulary rows (four 16-row blocks) and streams them along H, 128
+// contiguous bytes per row per 64-element step, the next step's loads in
+// flight while the current one multiplies. The hidden states are shared by
+// the workgroup's 8 waves and staged through LDS in 64-element slices
+// (double buffered, rows padded against bank conflicts). With lane = (i =
+// lane % 16, g = lane / 16): A = W block (16 rows x 32 k, lane (i, g) holds
+// row i, k = 8g .. 8g+7), B = X block transposed (lane (i, g) holds node i's
+// k = 8g .. 8g+7), and the output lane (i, g) holds vocabulary rows 4g .. 4g+3
+// of node i. A workgroup covers 512 rows x up to 128 nodes; more nodes take
+// more node slices (each re-reads the weight; slices of one vocabulary slab
+// are dealt to the same XCD back to back so the re-reads tend to hit L2).
+// The epilogue reduces each node's 64-bit keys (ordered logit << 32 | ~index)
+// over the wave's rows, the workgroup's waves, and finally, in a second
+// launch, over the vocabulary slabs.
+#include "common.hpp"
+
+namespace ttv {
+
+constexpr int kLmWaves = 8;
+constexpr int kLmThreads = kLmWaves * kWave;
+constexpr int kLmRowsPerWave = 64;                       // 4 blocks of 16 vocabulary rows
+constexpr int kLmSlab = kLmWaves * kLmRowsPerWave;       // 512 vocabulary rows per workgroup
+constexpr int kLmKc = 64;                                // k elements per LDS slice (two MFMA steps)
+constexpr int kLmXPitch = kLmKc * 2 + 16;                // bytes per staged hidden row (padded)
+constexpr int kLmMaxNB = 8;                              // 16-node blocks per slice (128 nodes)
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint64_t lm_key(float x, uint32_t idx) {
+  uint32_t o;
+  if (x != x) {
+    o = 0xFFFFFFFFu;
+  } else {
+    uint32_t u = __float_as_uint(x);
+    if ((u << 1) == 0u) u = 0u;  // -0.0 == +0.0
+    o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  }
+  return (static_cast<uint64_t>(o) << 32) | static_cast<uint32_t>(0xFFFFFFFFu - idx);
+}
+
+struct LmParams {
+  const uint16_t* x;    // [N][x_stride] bf16
+  const uint16_t* w;    // [V][w_stride] bf16
+  uint64_t* part;       // [N][n_slabs] best key per (node, slab)
+  int64_t x_stride;
+  int64_t w_stride;
+  int N, V, H;
+  int n_slabs, n_slices;
+};
+
+template <int NB>
+__global__ void __launch_bounds__(kLmThreads) lm_head_main(const LmParams p) {
+  __shared__ __attribute__((aligned(16))) unsigned char s_x[2][16 * NB * kLmXPitch];
+  __shared__ uint64_t s_best[kLmWaves][16 * NB];
+  const int slot = xcd_slot(blockIdx.x, p.n_slabs * p.n_slices);
+  if (slot < 0) return;  // padding workgroup (whole block, before any barrier)
+  const int slab = slot / p.n_slices;
+  const int slice = slot % p.n_slices;
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int li = lane % 16, lg = lane / 16;
+  const int n0 = slice * 16 * kLmMaxNB;
+  const int v_wave = slab * kLmSlab + wave * kLmRowsPerWave;
+
+  // weight rows of this lane (clamped into range; rows past V are ignored)
+  const unsigned char* wrow[4];
+#pragma unroll
+  for (int vb = 0; vb < 4; ++vb) {
+    const int v = min(v_wave + 16 * vb + li, p.V - 1);
+    wrow[vb] = reinterpret_cast<const unsigned char*>(p.w + static_cast<int64_t>(v) * p.w_stride) + 16 * lg;
+  }
+  // hidden-state staging: piece t = threadIdx.x + 512 r covers row t / 8,
+  // bytes 16 (t % 8) of the slice
+  constexpr int kPieces = 16 * NB * 8;
+  constexpr int kPiecesPerThread = (kPieces + kLmThreads - 1) / kLmThreads;
+  auto x_piece = [&](int c, int r) -> u32x4 {
+    const int t = threadIdx.x + kLmThreads * r;
+    const int row = min(n0 + t / 8, p.N - 1);
+    const unsigned char* src = reinterpret_cast<const unsigned char*>(p.x + static_cast<int64_t>(row) * p.x_stride) +
+                               c * (kLmKc * 2) + 16 * (t % 8);
+    return *reinterpret_cast<const u32x4*>(src);
+  };
+  auto x_store = [&](int buf, int r, u32x4 v) {
+    const int t = threadIdx.x + kLmThreads * r;
+    *reinterpret_cast<u32x4*>(&s_x[buf][(t / 8) * kLmXPitch + 16 * (t % 8)]) = v;
+  };
+
+  f32x4 acc[4][NB];
+#pragma unroll
+  for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[vb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int n_chunks = p.H / kLmKc;
+  // prologue: slice 0 of the hidden states into LDS, weight step 0 in flight
+  u32x4 xs[kPiecesPerThread];
+#pragma unroll
+  for (int r = 0; r < kPiecesPerThread; ++r)
+    if (threadIdx.x + kLmThreads * r < kPieces) xs[r] = x_piece(0, r);
+#pragma unroll
+  for (int r = 0; r < kPiecesPerThread; ++r)
+    if (threadIdx.x + kLmThreads * r < kPieces) x_store(0, r, xs[r]);
+  u32x4 wcur[2][4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int vb = 0; vb < 4; ++vb) wcur[h][vb] = *reinterpret_cast<const u32x4*>(wrow[vb] + 64 * h);
+  __syncthreads();
+
+  for (int c = 0; c < n_chunks; ++c) {
+    const int buf = c & 1;
+    const bool more = c + 1 < n_chunks;
+    // next slice: hidden pieces and weight fragments in flight
+    u32x4 wnext[2][4];
+    if (more) {
+#pragma unroll
+      for (int r = 0; r < kPiecesPerThread; ++r)
+        if (threadIdx.x + kLmThreads * r < kPieces) xs[r] = x_piece(c + 1, r);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int vb = 0; vb < 4; ++vb)
+          wnext[h][vb] = *reinterpret_cast<const u32x4*>(wrow[vb] + (c + 1) * (kLmKc * 2) + 64 * h);
+    }
+    // two 32-k steps on the current slice
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      bf16x8 xf[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        xf[nb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                &s_x[buf][(16 * nb + li) * kLmXPitch + 64 * h + 16 * lg]));
+#pragma unroll
+      for (int vb = 0; vb < 4; ++vb) {
+        const bf16x8 wf = __builtin_bit_cast(bf16x8, wcur[h][vb]);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[vb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xf[nb], acc[vb][nb], 0, 0, 0);
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int r = 0; r < kPiecesPerThread; ++r)
+        if (threadIdx.x + kLmThreads * r < kPieces) x_store(buf ^ 1, r, xs[r]);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int vb = 0; vb < 4; ++vb) wcur[h][vb] = wnext[h][vb];
+    }
+    __syncthreads();
+  }
+
+  // epilogue: node 16 nb + li's best over the lane's rows 16 vb + 4 lg + j
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int v = v_wave + 16 * vb + 4 * lg + j;
+        if (v < p.V) {
+          const uint64_t k = lm_key(acc[vb][nb][j], static_cast<uint32_t>(v));
+          best = k > best ? k : best;
+        }
+      }
+#pragma unroll
+    for (int off = 16; off <= 32; off <<= 1) {
+      const uint64_t o = __shfl_xor(best, off);
+      best = o > best ? o : best;
+    }
+    if (lg == 0) s_best[wave][16 * nb + li] = best;
+  }
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < 16 * NB && n0 + t < p.N) {
+    uint64_t best = s_best[0][t];
+#pragma unroll
+    for (int w = 1; w < kLmWaves; ++w) best = s_best[w][t] > best ? s_best[w][t] : best;
+    p.part[static_cast<int64_t>(n0 + t) * p.n_slabs + slab] = best;
+  }
+}
+
+// one wave per node: the best key over the vocabulary slabs
+__global__ void __launch_bounds__(kWave) lm_head_reduce(const uint64_t* __restrict__ part, int n_slabs,
+                                                        int32_t* __restrict__ out_idx) {
+  const int n = blockIdx.x;
+  const uint64_t* __restrict__ r = part + static_cast<int64_t>(n) * n_slabs;
+  uint64_t best = 0;
+  for (int s = threadIdx.x; s < n_slabs; s += kWave) best = r[s] > best ? r[s] : best;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint64_t o = __shfl_xor(best, off);
+    best = o > best ? o : best;
+  }
+  if (threadIdx.x == 0) out_idx[n] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(best));
+}
+
+static int lm_slabs(int64_t vocab) { return static_cast<int>((vocab + kLmSlab - 1) / kLmSlab); }
+
+}  // namespace ttv
+
+using namespace ttv;
+
+extern "C" size_t lm_head_argmax_ws(int64_t n_rows, int64_t vocab) {
+  if (n_rows <= 0 || vocab <= 0) return 0;
+  return static_cast<size_t>(n_rows) * lm_slabs(vocab) * sizeof(uint64_t);
+}
+
+extern "C" ttv_status lm_head_argmax(const uint16_t* hidden, int64_t n_rows, int64_t hidden_stride,
+                                     const uint16_t* weight, int64_t vocab, int64_t hidden_dim, int64_t weight_stride,
+                                     int32_t* out_idx, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  TTV_REQUIRE(n_rows >= 0 && n_rows <= (1 << 24), TTV_ERR_INVALID, "lm_head_argmax: n_rows %lld not in [0, 2^24]",
+              (long long)n_rows);
+  if (n_rows == 0) return TTV_OK;
+  TTV_REQUIRE(vocab >= 1 && vocab <= 0x7FFFFFFF, TTV_ERR_INVALID, "lm_head_argmax: vocab %lld not in [1, 2^31 - 1]",
+              (long long)vocab);
+  TTV_REQUIRE(hidden_dim >= kLmKc && hidden_dim % kLmKc == 0 && hidden_dim <= (1 << 20), TTV_ERR_INVALID,
+              "lm_head_argmax: hidden_dim %lld is not a positive multiple of %d (<= 2^20)", (long long)hidden_dim,
+              kLmKc);
+  TTV_REQUIRE(hidden_stride >= hidden_dim && hidden_stride % 8 == 0 && weight_stride >= hidden_dim &&
+                  weight_stride % 8 == 0,
+              TTV_ERR_INVALID, "lm_head_argmax: strides (%lld, %lld) must be >= hidden_dim and multiples of 8",
+              (long long)hidden_stride, (long long)weight_stride);
+  TTV_REQUIRE(hidden && weight && out_idx, TTV_ERR_INVALID, "lm_head_argmax: NULL pointer");
+  TTV_REQUIRE(reinterpret_cast<uintptr_t>(hidden) % 16 == 0 && reinterpret_cast<uintptr_t>(weight) % 16 == 0,
+              TTV_ERR_INVALID, "lm_head_argmax: hidden and weight must be 16-byte aligned");
+  const size_t need = lm_head_argmax_ws(n_rows, vocab);
+  TTV_REQUIRE(ws && ws_bytes >= need, TTV_ERR_WORKSPACE, "lm_head_argmax: workspace %zu bytes < %zu", ws_bytes, need);
+  LmParams p;
+  p.x = hidden;
+  p.w = weight;
+  p.part = static_cast<uint64_t*>(ws);
+  p.x_stride = hidden_stride;
+  p.w_stride = weight_stride;
+  p.N = static_cast<int>(n_rows);
+  p.V = static_cast<int>(vocab);
+  p.H = static_cast<int>(hidden_dim);
+  p.n_slabs = lm_slabs(vocab);
+  p.n_slices = static_cast<int>((n_rows + 16 * kLmMaxNB - 1) / (16 * kLmMaxNB));
+  const int64_t n_wg = static_cast<int64_t>(p.n_slabs) * p.n_slices;
+  TTV_REQUIRE(n_wg <= (1ll << 30), TTV_ERR_INVALID, "lm_head_argmax: too many workgroups");
+  const unsigned grid = static_cast<unsigned>((n_wg + kNumXcd - 1) / kNumXcd * kNumXcd);
+  // node blocks per slice: enough for the nodes of the (first) slice
+  const int rows0 = static_cast<int>(n_rows < 16 * kLmMaxNB ? n_rows : 16 * kLmMaxNB);
+  const int nb = (rows0 + 15) / 16;
+  hipStream_t s = (hipStream_t)stream;
+  switch (nb) {
+#define TTV_LM(NB) \
+  case NB: hipLaunchKernelGGL(lm_head_main<NB>, dim3(grid), dim3(kLmThreads), 0, s, p); break;
+    TTV_LM(1) TTV_LM(2) TTV_LM(3) TTV_LM(4) TTV_LM(5) TTV_LM(6) TTV_LM(7) TTV_LM(8)
+#undef TTV_LM
+    default: return fail(TTV_ERR_INVALID, "lm_head_argmax: internal node-block count");
+  }
+  ttv_status st = check_launch("lm_head_argmax main");
+  if (st != TTV_OK) return st;
+  hipLaunchKernelGGL(lm_head_reduce, dim3(static_cast<unsigned>(n_rows)), dim3(kWave), 0, s,
+                     static_cast<const uint64_t*>(p.part), p.n_slabs, out_idx);
+  return check_launch("lm_head_argmax reduce");
+}
