@@ -262,3 +262,21 @@ def test_tree_feeds_mask_and_walk(ttv):
         wp, wt, _ = O.draft_tree_select(states[b], n)
         want, _ = O.tree_accept_walk(wp, wt, np.asarray(targets[b * n:(b + 1) * n], np.int32))
         assert to_host(path)[b, :len(want)].tolist() == list(want)
+
+
+def test_wide_logit_ranges(ttv):
+    # rows whose terms exp(x - max) underflow to subnormals and to zero, and a
+    # row dominated by one huge logit: the float64 normalisers must still
+    # agree with the oracle's
+    B, k, V = 2, 4, 9000
+    rows = draft_rows(61, B, 2, k, V)
+    r0 = rows[0].copy()
+    r0[0, 0, :100] = -720.0     # subnormal terms
+    r0[0, 0, 100:200] = -1e4    # zero terms
+    r0[1, 0, 5] = 600.0         # everything else ~e^-600
+    r1 = rows[1].copy()
+    r1[:, :, 7::3] -= 730.0
+    table = ttv.DraftTable(B, k, 64)
+    assert gpu_expand(ttv, table, 1, r0) == 0
+    assert gpu_expand(ttv, table, 2, r1) == 0
+    check_table(ttv, table, oracle_states([0, 1], [r0, r1], k))

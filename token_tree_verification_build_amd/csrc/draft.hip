@@ -24,6 +24,8 @@
 namespace ttv {
 
 constexpr int kDraftMaxK = 16;        // top_k limit: <= 16 frontier rows, <= 256 new candidates a depth
+constexpr int kDraftPerLane = kSelPerLane;  // chunks of 4096 logits, as the sampled selection
+constexpr int kDraftChunk = kSelLanes * kDraftPerLane;
 constexpr int kDraftMaxCand = 4096;   // candidate table limit per sequence
 
 __device__ __forceinline__ bool draft_better(double su, int u, double st, int t) {
@@ -39,25 +41,20 @@ __global__ void __launch_bounds__(kSelLanes * kDraftMaxK)
   __shared__ uint64_t s_c[kDraftMaxK][kSelCap];
   __shared__ uint64_t s_top[kDraftMaxK][kDraftMaxK];
   __shared__ double s_score[kDraftMaxK * kDraftMaxK];
-  __shared__ int s_front[kDraftMaxK];
-  __shared__ int s_bad;
-  __shared__ int s_bad_state;
   const int b = blockIdx.x;
-  const int wave = threadIdx.x / kSelLanes;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kSelLanes));
   const int lane = threadIdx.x % kSelLanes;
   const int64_t base = static_cast<int64_t>(b) * cap;
+  // The loads are ordered so that few of them wait on another: the table's
+  // count, this wave's frontier slot and its parent's score are scalar
+  // loads; the chunk statistics and candidates are vector loads issued
+  // together. Nothing is written before every check has passed.
   const int n_old = depth == 1 ? 0 : cand_count[b];
-  if (threadIdx.x == 0) {
-    s_bad = 0;
-    // the table must hold a frontier to expand and room for F * k more
-    s_bad_state = (depth > 1 && (n_old < k || n_old > cap)) || n_old + F * k > cap;
-  }
-  __syncthreads();
-  if (threadIdx.x < F) {
-    const int f = depth == 1 ? -1 : frontier[b * k + threadIdx.x];
-    if (depth > 1 && (f < 0 || f >= n_old)) s_bad_state = 1;
-    s_front[threadIdx.x] = f;
-  }
+  const int u = depth == 1 ? -1 : frontier[b * k + wave];
+  // the table must hold a frontier to expand (slots in range) and room for F * k more
+  const bool bad_state =
+      (depth > 1 && (n_old < k || n_old > cap || u < 0 || u >= n_old)) || n_old + F * k > cap;
+  const double pscore = (u >= 0 && !bad_state) ? cand_score[base + u] : 0.0;
   // the row's maximum and whether any value is not finite
   const int64_t row = static_cast<int64_t>(b) * F + wave;
   const ChunkStats* __restrict__ rs = stats + row * n_chunks;
@@ -68,11 +65,12 @@ __global__ void __launch_bounds__(kSelLanes * kDraftMaxK)
     bad |= st.bad != 0;
     m = st.max > m ? st.max : m;
   }
-  if (__ballot(bad) != 0 && lane == 0) s_bad = 1;
-  __syncthreads();
-  const bool bad_state = s_bad_state != 0;
-  if (bad_state || s_bad) {
-    if (threadIdx.x == 0) *dev_status = bad_state ? TTV_DEV_DRAFT_STATE : TTV_DEV_BAD_LOGITS;
+  // the row's top k, best first (into this wave's LDS only)
+  row_topk_sorted(cand + row * n_cand_row, n_cand_row, k, lane, s_c[wave], s_top[wave]);
+  const int any_state = __syncthreads_or(bad_state ? 1 : 0);
+  const int any_logits = __syncthreads_or(bad ? 1 : 0);
+  if (any_state || any_logits) {
+    if (threadIdx.x == 0) *dev_status = any_state ? TTV_DEV_DRAFT_STATE : TTV_DEV_BAD_LOGITS;
     return;  // nothing written for this sequence
   }
 #pragma unroll
@@ -84,15 +82,11 @@ __global__ void __launch_bounds__(kSelLanes * kDraftMaxK)
   double S = 0.0;
   for (int c = lane; c < n_chunks; c += kSelLanes) {
     const ChunkStats st = rs[c];
-    S += st.sum * exp(static_cast<double>(st.max) - M);
+    S += st.sum * exp_nonpos_f64(static_cast<double>(st.max) - M);
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) S += __shfl_xor(S, off);
   const double lse = M + log(S);
-  // the row's top k, best first
-  row_topk_sorted(cand + row * n_cand_row, n_cand_row, k, lane, s_c[wave], s_top[wave]);
-  const int u = s_front[wave];
-  const double pscore = u < 0 ? 0.0 : cand_score[base + u];
   if (lane < k) {
     const uint64_t key = s_top[wave][lane];
     const double sc = pscore + (static_cast<double>(key_value(key)) - lse);
@@ -171,7 +165,7 @@ __global__ void __launch_bounds__(1024)
 }
 
 static size_t draft_ws_bytes(int64_t n_rows, int64_t vocab, int k) {
-  const int64_t nc = sel_chunks(vocab);
+  const int64_t nc = sel_chunks(vocab, kDraftChunk);
   return static_cast<size_t>(n_rows * nc * k) * sizeof(uint64_t) + static_cast<size_t>(n_rows * nc) * sizeof(ChunkStats);
 }
 
@@ -204,7 +198,7 @@ extern "C" ttv_status draft_tree_expand(int32_t B, int32_t depth, int32_t top_k,
               TTV_ERR_INVALID, "draft_tree_expand: NULL pointer");
   const int F = depth == 1 ? 1 : top_k;
   const int64_t n_rows = static_cast<int64_t>(B) * F;
-  const int n_chunks = sel_chunks(vocab);
+  const int n_chunks = sel_chunks(vocab, kDraftChunk);
   const int64_t n_cand_row = static_cast<int64_t>(n_chunks) * top_k;
   TTV_REQUIRE(n_cand_row <= kSelMaxCand, TTV_ERR_INVALID,
               "draft_tree_expand: %d chunks x top_k %d candidates per row exceed %d", n_chunks, top_k, kSelMaxCand);
@@ -215,7 +209,7 @@ extern "C" ttv_status draft_tree_expand(int32_t B, int32_t depth, int32_t top_k,
   hipStream_t s = (hipStream_t)stream;
   uint64_t* cand = static_cast<uint64_t*>(ws);
   ChunkStats* stats = reinterpret_cast<ChunkStats*>(cand + n_rows * n_cand_row);
-  hipLaunchKernelGGL(chunk_topk<true>,
+  hipLaunchKernelGGL((chunk_topk<true, kDraftPerLane>),
                      dim3(static_cast<unsigned>((n_chunks + kSelWaves - 1) / kSelWaves), static_cast<unsigned>(n_rows)),
                      dim3(kSelLanes * kSelWaves), 0, s, logits, vocab, row_stride, n_chunks, top_k, vec, cand, stats);
   ttv_status st = check_launch("draft_tree_expand chunk pass");

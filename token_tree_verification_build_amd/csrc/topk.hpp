@@ -21,7 +21,7 @@ namespace ttv {
 
 constexpr int kSelMaxK = 64;
 constexpr int kSelLanes = 64;                         // lanes per wave
-constexpr int kSelPerLane = 64;                       // values per lane
+constexpr int kSelPerLane = 64;                       // values per lane (the default chunk)
 constexpr int kSelChunk = kSelLanes * kSelPerLane;    // 4096 values per wave
 constexpr int kSelWaves = 4;                          // waves (chunks) per pass-1 workgroup
 constexpr int kSelCap = 256;                          // candidate slots per wave in LDS
@@ -92,15 +92,41 @@ __device__ __forceinline__ uint32_t wave_kth_largest32(uint32_t v, int need) {
   return t;
 }
 
-// Pass 1: wave w of workgroup (g, row) takes chunk c = 4g + w of the row and
-// writes its top k keys (in no particular order; key 0, below every value,
-// fills slots a short chunk cannot) to cand[(row * n_chunks + c) * k ...].
-// With kStats, lane 0 also writes the chunk's ChunkStats to
-// stats[row * n_chunks + c].
-template <bool kStats>
+// e^t for t <= 0 in float64, a few ulp: Cody-Waite argument reduction
+// t = n ln2 + r with |r| <= ln2 / 2 (ln2 split into a high part with
+// trailing zero bits, so n * ln2_hi is exact, and a low part; the split of
+// fdlibm), e^r by its Taylor series through r^13 (the next term is below
+// 4e-18 relative) evaluated by Estrin's scheme (dependency depth 4 rather
+// than 13, so the many exponentials of a wave overlap), scaled by 2^n with
+// v_ldexp_f64 (subnormal results included); 0 below -745, under the
+// smallest subnormal.
+__device__ __forceinline__ double exp_nonpos_f64(double t) {
+  if (t < -745.0) return 0.0;
+  const double n = rint(t * 1.4426950408889634074);
+  const double r = fma(-n, 1.90821492927058770002e-10, fma(-n, 6.93147180369123816490e-01, t));
+  constexpr double f2 = 1.0 / 2, f3 = f2 / 3, f4 = f3 / 4, f5 = f4 / 5, f6 = f5 / 6, f7 = f6 / 7, f8 = f7 / 8,
+                   f9 = f8 / 9, f10 = f9 / 10, f11 = f10 / 11, f12 = f11 / 12, f13 = f12 / 13;
+  const double r2 = r * r;
+  const double r4 = r2 * r2;
+  const double r8 = r4 * r4;
+  const double a0 = r + 1.0, a1 = fma(f3, r, f2), a2 = fma(f5, r, f4), a3 = fma(f7, r, f6);
+  const double a4 = fma(f9, r, f8), a5 = fma(f11, r, f10), a6 = fma(f13, r, f12);
+  const double b0 = fma(a1, r2, a0), b1 = fma(a3, r2, a2), b2 = fma(a5, r2, a4);
+  const double d0 = fma(b1, r4, b0), d1 = fma(a6, r4, b2);
+  return ldexp(fma(d1, r8, d0), static_cast<int>(n));
+}
+
+// Pass 1: wave w of workgroup (g, row) takes chunk c = 4g + w (of 64 *
+// PER_LANE values) of the row and writes its top k keys (in no particular
+// order; key 0, below every value, fills slots a short chunk cannot) to
+// cand[(row * n_chunks + c) * k ...]. With kStats, lane 0 also writes the
+// chunk's ChunkStats to stats[row * n_chunks + c].
+template <bool kStats, int PER_LANE = kSelPerLane>
 __global__ void __launch_bounds__(kSelLanes * kSelWaves)
     chunk_topk(const float* __restrict__ logits, int64_t vocab, int64_t row_stride, int n_chunks, int k, int vec,
                uint64_t* __restrict__ cand, ChunkStats* __restrict__ stats) {
+  static_assert(PER_LANE % 4 == 0 && PER_LANE <= kSelPerLane, "chunk of 64 * PER_LANE values");
+  constexpr int kChunk = kSelLanes * PER_LANE;
   __shared__ uint64_t s_cand[kSelWaves][kSelCap];
   const int wave = threadIdx.x / kSelLanes;
   const int lane = threadIdx.x % kSelLanes;
@@ -108,14 +134,14 @@ __global__ void __launch_bounds__(kSelLanes * kSelWaves)
   const int c = blockIdx.x * kSelWaves + wave;
   if (c >= n_chunks) return;  // whole wave; pass 1 has no workgroup barrier
   const float* __restrict__ x = logits + static_cast<int64_t>(row) * row_stride;
-  const int64_t c0 = static_cast<int64_t>(c) * kSelChunk;
+  const int64_t c0 = static_cast<int64_t>(c) * kChunk;
   // the lane's ordered values: element c0 + 4 (64 j + lane) + q; past vocab 0
-  uint32_t ov[kSelPerLane];
+  uint32_t ov[PER_LANE];
   auto idx_of = [&](int j) -> uint32_t { return static_cast<uint32_t>(c0 + 4 * (64 * (j >> 2) + lane) + (j & 3)); };
-  if (vec && c0 + kSelChunk <= vocab) {
+  if (vec && c0 + kChunk <= vocab) {
     const f32x4* __restrict__ xv = reinterpret_cast<const f32x4*>(x + c0);
 #pragma unroll
-    for (int j = 0; j < kSelPerLane / 4; ++j) {
+    for (int j = 0; j < PER_LANE / 4; ++j) {
       const f32x4 a = __builtin_nontemporal_load(xv + 64 * j + lane);
       ov[4 * j] = sample_ord(a.x);
       ov[4 * j + 1] = sample_ord(a.y);
@@ -124,7 +150,7 @@ __global__ void __launch_bounds__(kSelLanes * kSelWaves)
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < kSelPerLane; ++j) {
+    for (int j = 0; j < PER_LANE; ++j) {
       const int64_t i = c0 + 4 * (64 * (j >> 2) + lane) + (j & 3);
       ov[j] = i < vocab ? sample_ord(x[i]) : 0u;
     }
@@ -134,7 +160,7 @@ __global__ void __launch_bounds__(kSelLanes * kSelWaves)
   // chunk holds fewer than k values
   uint32_t lmax = 0;
 #pragma unroll
-  for (int j = 0; j < kSelPerLane; ++j) lmax = ov[j] > lmax ? ov[j] : lmax;
+  for (int j = 0; j < PER_LANE; ++j) lmax = ov[j] > lmax ? ov[j] : lmax;
   if constexpr (kStats) {
     // chunk maximum; NaN orders as 0xFFFFFFFF, +inf as 0xFF800000 and -inf
     // as 0x007FFFFF, so those are the non-finite values
@@ -148,9 +174,9 @@ __global__ void __launch_bounds__(kSelLanes * kSelWaves)
     bool bad = false;
     double s = 0.0;
 #pragma unroll
-    for (int j = 0; j < kSelPerLane; ++j) {
+    for (int j = 0; j < PER_LANE; ++j) {
       bad |= ov[j] >= 0xFF800000u || ov[j] == 0x007FFFFFu;
-      if (ov[j]) s += exp(static_cast<double>(key_value(static_cast<uint64_t>(ov[j]) << 32)) - m);
+      if (ov[j]) s += exp_nonpos_f64(static_cast<double>(key_value(static_cast<uint64_t>(ov[j]) << 32)) - m);
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
@@ -168,7 +194,7 @@ __global__ void __launch_bounds__(kSelLanes * kSelWaves)
   uint64_t* sc = s_cand[wave];
   int total = 0;
 #pragma unroll
-  for (int j = 0; j < kSelPerLane; ++j) {
+  for (int j = 0; j < PER_LANE; ++j) {
     const bool is = ov[j] >= tau;
     const uint64_t m = __ballot(is);
     if (m == 0) continue;  // (most steps: candidates are few)
@@ -203,14 +229,14 @@ __global__ void __launch_bounds__(kSelLanes * kSelWaves)
       const uint64_t cb = t | (1ull << bit);
       int cnt = 0;
 #pragma unroll
-      for (int j = 0; j < kSelPerLane; ++j) {
+      for (int j = 0; j < PER_LANE; ++j) {
         const uint64_t kj = ov[j] ? (static_cast<uint64_t>(ov[j]) << 32) | (0xFFFFFFFFu - idx_of(j)) : 0ull;
         cnt += __popcll(__ballot(kj >= cb));
       }
       if (cnt >= k) t = cb;
     }
 #pragma unroll
-    for (int j = 0; j < kSelPerLane; ++j) {
+    for (int j = 0; j < PER_LANE; ++j) {
       const uint64_t kj = ov[j] ? (static_cast<uint64_t>(ov[j]) << 32) | (0xFFFFFFFFu - idx_of(j)) : 0ull;
       const bool is = kj != 0 && kj >= t;
       const uint64_t m = __ballot(is);
@@ -321,6 +347,6 @@ __device__ __forceinline__ void row_topk_sorted(const uint64_t* __restrict__ cr,
   __builtin_amdgcn_wave_barrier();
 }
 
-inline int sel_chunks(int64_t vocab) { return static_cast<int>((vocab + kSelChunk - 1) / kSelChunk); }
+inline int sel_chunks(int64_t vocab, int chunk = kSelChunk) { return static_cast<int>((vocab + chunk - 1) / chunk); }
 
 }  // namespace ttv
