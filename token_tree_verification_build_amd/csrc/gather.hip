@@ -32,7 +32,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGatherThreads = 256;
 constexpr int kLayersPerLaunch = 16;
-constexpr int kTakeRows = 256;  // rows per out-of-place workgroup
+constexpr int kTakeRows = 512;  // rows per out-of-place workgroup
 constexpr int kMaxSelChunks = 64;     // validation workgroups per sequence, at most
 constexpr int kMinSelChunk = 2048;    // selection entries per validation workgroup, at least
 
@@ -189,13 +189,35 @@ __global__ void __launch_bounds__(kGatherThreads) take_kernel(LayerPtrs L, int B
   const char* __restrict__ vs = L.v[l];
   char* __restrict__ kd = L.dk[l];
   char* __restrict__ vd = L.dv[l];
-  for (int j = r0 + rr; copier && j < r1; j += rows_per_pass) {
-    const int64_t src = (base + srow[j]) * row_bytes + 16 * u;
-    const int64_t dst = (base + j) * row_bytes + 16 * u;
-    const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ks + src));
-    const u32x4 c = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vs + src));
-    __builtin_nontemporal_store(a, reinterpret_cast<u32x4*>(kd + dst));
-    __builtin_nontemporal_store(c, reinterpret_cast<u32x4*>(vd + dst));
+  // batches of kTakeBatch passes: every index, then every K/V piece of the
+  // batch in flight before the first store (a thread keeps up to 2 x 16 x 16
+  // bytes moving instead of 2 x 16)
+  constexpr int kTakeBatch = 16;
+  for (int jb = r0 + rr; copier && jb < r1; jb += kTakeBatch * rows_per_pass) {
+    int sj[kTakeBatch];
+#pragma unroll
+    for (int q = 0; q < kTakeBatch; ++q) {
+      const int j = jb + q * rows_per_pass;
+      sj[q] = j < r1 ? srow[j] : 0;
+    }
+    u32x4 a[kTakeBatch], c[kTakeBatch];
+#pragma unroll
+    for (int q = 0; q < kTakeBatch; ++q) {
+      if (jb + q * rows_per_pass < r1) {
+        const int64_t src = (base + sj[q]) * row_bytes + 16 * u;
+        a[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ks + src));
+        c[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vs + src));
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kTakeBatch; ++q) {
+      const int j = jb + q * rows_per_pass;
+      if (j < r1) {
+        const int64_t dst = (base + j) * row_bytes + 16 * u;
+        __builtin_nontemporal_store(a[q], reinterpret_cast<u32x4*>(kd + dst));
+        __builtin_nontemporal_store(c[q], reinterpret_cast<u32x4*>(vd + dst));
+      }
+    }
   }
   if (L.ks[l] != nullptr) {
     for (int j = r0 + threadIdx.x; j < r1; j += kGatherThreads) {
