@@ -181,7 +181,10 @@ def pmc_summary(fetch_csv: str, write_csv: str, calib_mib: int) -> None:
     nbytes = calib_mib << 20
 
     def copy_value(rows):
-        cands = [(k, v) for k, v in rows.items() if "copy" in k.lower()]
+        # the calibration copy is a runtime buffer copy (torch's own copy
+        # kernels, e.g. dtype conversions, are not calibrated transfers)
+        cands = [(k, v) for k, v in rows.items() if "copybuffer" in k.lower()]
+        cands = cands or [(k, v) for k, v in rows.items() if "copy" in k.lower()]
         # the calibration copy is the dispatch whose counter reads closest to its size
         k, v = min(cands, key=lambda kv: abs(max(kv[1]) * 1024 - nbytes))
         return k, max(v)
