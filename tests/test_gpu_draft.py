@@ -127,6 +127,8 @@ CASES = [  # (B, top_k, depths, n_nodes, V, stride_pad)
     (2, 2, 6, 12, 100, 0),      # a vocabulary smaller than one chunk
     (3, 4, 3, 16, 9001, 3),     # unaligned row stride
     (5, 3, 2, 13, 12288, 0),    # every candidate chosen (1 + 3 + 9)
+    (128, 16, 2, 64, 1000, 0),  # the largest batch with the widest frontier (1024-thread merge)
+    (3, 3, 3, 13, 3, 0),        # vocabulary == top_k: every token is a child
 ]
 
 
