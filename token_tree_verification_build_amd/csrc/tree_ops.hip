@@ -126,6 +126,22 @@ __global__ void copy_rows_kernel(const float* caller, int S, float* out) {
 // the lowest-labelled matching child. Every step moves to a larger label, so
 // the loop ends within T - 1 steps. All 256 threads then write the rollback
 // selection [0, P) ++ (P + path).
+constexpr int kWalkPrefixChunk = 256 * 16;  // identity-prefix entries per prefix workgroup
+
+// parent[] of one tree is a rooted topological labelling (one wave, lane = node)
+__device__ __forceinline__ bool walk_tree_ok(const int32_t* __restrict__ parent, int o0, int T, int lane) {
+  const bool active = lane < T;
+  const int p = active ? parent[o0 + lane] : -2;
+  const bool ok = !active || (lane == 0 ? p == -1 : (p >= 0 && p < lane));
+  return __ballot(!ok) == 0 && T > 0;
+}
+
+// Grid (1 + prefix chunks, B). Workgroup x = 0 of sequence b walks its tree
+// and writes the path, the emitted tokens and the selection's block part
+// sel[P + k] = P + path[k]; workgroups x >= 1 write the identity prefix
+// sel[j] = j over their chunk of [0, P), so a long history is written by many
+// workgroups at once. Every workgroup checks the tree first: an invalid tree
+// writes nothing.
 __global__ void __launch_bounds__(256) walk_kernel(
     const int32_t* __restrict__ node_off, const int32_t* __restrict__ hist_len,
     const int32_t* __restrict__ parent, const int32_t* __restrict__ token,
@@ -134,17 +150,31 @@ __global__ void __launch_bounds__(256) walk_kernel(
     int32_t* __restrict__ sel_len_out, int32_t* __restrict__ status) {
   __shared__ int s_path[TTV_MAX_NODES];
   __shared__ int s_len;
-  const int b = blockIdx.x;
+  const int b = blockIdx.y;
   const int tid = threadIdx.x;
   const int o0 = node_off[b];
   const int T = node_off[b + 1] - o0;
+  if (blockIdx.x > 0) {  // identity prefix chunk (only launched with sel)
+    const int P = hist_len[b];
+    const int j0 = (blockIdx.x - 1) * kWalkPrefixChunk;
+    if (j0 >= P) return;  // whole workgroup
+    if (tid < kWave) {
+      const bool ok = walk_tree_ok(parent, o0, T, tid);
+      if (tid == 0) s_len = ok ? 1 : -1;
+    }
+    __syncthreads();
+    if (s_len < 0) return;
+    int32_t* row = sel + (size_t)b * sel_stride;
+    const int j1 = min(P, j0 + kWalkPrefixChunk);
+    for (int j = j0 + tid; j < j1; j += blockDim.x) row[j] = j;
+    return;
+  }
   if (tid < kWave) {
     const int lane = tid;
     const bool active = lane < T;
     const int p = active ? parent[o0 + lane] : -2;
     const int tok = active ? token[o0 + lane] : 0;
-    const bool ok = !active || (lane == 0 ? p == -1 : (p >= 0 && p < lane));
-    const bool bad = __ballot(!ok) != 0 || T <= 0;
+    const bool bad = !walk_tree_ok(parent, o0, T, lane);
     int len = 0;
     if (!bad) {
       int cur = 0;
@@ -178,7 +208,6 @@ __global__ void __launch_bounds__(256) walk_kernel(
   }
   const int P = hist_len[b];
   int32_t* row = sel + (size_t)b * sel_stride;
-  for (int j = tid; j < P; j += blockDim.x) row[j] = j;
   if (tid < len) row[P + tid] = P + s_path[tid];
   if (tid == 0 && sel_len_out) sel_len_out[b] = P + len;
 }
@@ -263,7 +292,11 @@ extern "C" ttv_status tree_accept_walk(const ttv_batch* batch, const int32_t* pa
                   "tree_accept_walk: sel_stride %d < P + T = %d for sequence %d", sel_stride,
                   batch->hist_len_h[b] + T, b);
   }
-  hipLaunchKernelGGL(walk_kernel, dim3(batch->B), dim3(256), 0, (hipStream_t)stream, batch->node_off_d,
+  int max_p = 0;
+  for (int b = 0; b < batch->B; ++b) max_p = batch->hist_len_h[b] > max_p ? batch->hist_len_h[b] : max_p;
+  const int prefix_chunks = sel ? (max_p + kWalkPrefixChunk - 1) / kWalkPrefixChunk : 0;
+  hipLaunchKernelGGL(walk_kernel, dim3(1 + prefix_chunks, batch->B), dim3(256), 0, (hipStream_t)stream,
+                     batch->node_off_d,
                      batch->hist_len_d, parent, token, target_argmax, path, path_len, emitted, sel,
                      sel_stride, sel_len_out, dev_status);
   return check_launch("tree_accept_walk");
