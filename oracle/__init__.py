@@ -8,10 +8,11 @@ the library and its Python binding never do, and nothing here imports them.
 Floating point is float64 throughout. Storage formats (bf16 bit patterns,
 fp16 scales, int8 codes) are decoded here by the oracle's own code.
 
-Parity status: every function is pinned by ``tests/test_oracle_pins.py``
-against closed forms, brute force, library routines (torch SDPA in float64,
-Python's list max/index) or the pages' stated equivalences; no function is
-parity-unpinned.
+Parity status: every function is pinned by ``tests/test_oracle_pins.py``,
+``tests/test_oracle_draft.py`` or ``tests/test_oracle_lm_head.py`` against
+closed forms, brute force, hand-worked examples, library routines (torch SDPA
+in float64, scipy's softmax, math.fsum, Python's list max/index) or the pages'
+stated equivalences; no function is parity-unpinned.
 """
 
 from .ttv_oracle import *  # noqa: F401,F403
