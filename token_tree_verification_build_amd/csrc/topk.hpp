@@ -204,7 +204,16 @@ __global__ void __launch_bounds__(kSelLanes * kSelWaves)
   }
   uint64_t* out = cand + (static_cast<int64_t>(row) * n_chunks + c) * k;
   int n_out = 0;
-  if (total <= kSelCap) {
+  if (total <= kSelLanes) {
+    // the usual case, a few dozen candidates: one slot per lane
+    __builtin_amdgcn_wave_barrier();
+    const uint64_t h1[1] = {lane < total ? sc[lane] : 0ull};
+    const uint64_t kth = wave_kth_largest(h1, k);
+    const bool is = h1[0] != 0 && h1[0] >= kth;
+    const uint64_t m = __ballot(is);
+    if (is) out[lanes_below(m)] = h1[0];
+    n_out = __popcll(m);
+  } else if (total <= kSelCap) {
     __builtin_amdgcn_wave_barrier();
     // the k largest candidates: slots lane, lane + 64, ...
     uint64_t h[kSelCap / kSelLanes];
@@ -299,7 +308,15 @@ __device__ __forceinline__ void row_topk_sorted(const uint64_t* __restrict__ cr,
     }
   }
   int n_w = 0;  // winners: the k largest keys (distinct, nonzero; the row has at least k values)
-  if (total <= kSelCap) {
+  if (total <= kSelLanes) {
+    __builtin_amdgcn_wave_barrier();
+    const uint64_t g1[1] = {lane < total ? s_c[lane] : 0ull};
+    const uint64_t kth = wave_kth_largest(g1, k);
+    const bool is = g1[0] != 0 && g1[0] >= kth;
+    const uint64_t m = __ballot(is);
+    if (is) s_top[lanes_below(m)] = g1[0];
+    n_w = __popcll(m);
+  } else if (total <= kSelCap) {
     __builtin_amdgcn_wave_barrier();
     uint64_t g[kSelCap / kSelLanes];
 #pragma unroll
