@@ -42,6 +42,9 @@ __all__ = [
     "vocab_sample",
     "lm_head_logits",
     "lm_head_argmax",
+    "lm_head_q4_weight",
+    "lm_head_q4_logits",
+    "lm_head_q4_argmax",
     "tree_accept_walk",
     "draft_tree_new",
     "draft_tree_expand",
@@ -279,6 +282,43 @@ def lm_head_argmax(hidden_bits, weight_bits) -> np.ndarray:
     never writes the logits; its result is this argmax wherever the float32
     accumulation of the projection cannot reorder the top logits."""
     return np.argmax(lm_head_logits(hidden_bits, weight_bits), axis=-1).astype(np.int32)
+
+
+def lm_head_q4_weight(wq, sb_bits) -> np.ndarray:
+    """The LM head stored the way the pages' engine holds it: affine 4-bit
+    codes with one 16-bit scale and bias per group of 64 hidden elements
+    ([I1185] "The cost model": the borrowed head is weight 635.7 + scales
+    39.7 + biases 39.7 MB for 248,320 x 5,120; the "Phase 3 done" comment:
+    affine group-64 4-bit). Value = scale * code + bias, code in 0..15.
+    Layout (a reading; the pages give sizes, not layouts): wq uint32 [V, H/8]
+    with hidden element i in bits 4 (i mod 8) of word i / 8; sb_bits bf16 bit
+    patterns [H/64, V, 2] holding (scale, bias) of group g of row v, group-major.
+    Returns the float64 weight [V, H]."""
+    wq = np.asarray(wq, dtype=np.uint32)
+    sb = np.asarray(sb_bits, dtype=np.uint16)
+    V, W8 = wq.shape
+    H = 8 * W8
+    G = H // 64
+    assert sb.shape == (G, V, 2)
+    code = np.zeros((V, H), dtype=np.float64)
+    for j in range(8):
+        code[:, j::8] = (wq >> np.uint32(4 * j)) & np.uint32(15)
+    scale = np.repeat(decode_bf16(sb[:, :, 0]).T, 64, axis=1)
+    bias = np.repeat(decode_bf16(sb[:, :, 1]).T, 64, axis=1)
+    return scale * code + bias
+
+
+def lm_head_q4_logits(hidden_bits, wq, sb_bits) -> np.ndarray:
+    """logits[n, v] = sum_i hidden[n, i] * weight[v, i] over the 4-bit head's
+    values, in float64."""
+    return decode_bf16(hidden_bits) @ lm_head_q4_weight(wq, sb_bits).T
+
+
+def lm_head_q4_argmax(hidden_bits, wq, sb_bits) -> np.ndarray:
+    """The fused projection-plus-argmax over the 4-bit head ([I1185]
+    "Proposed work" Phase 2a and its verdict: a quantised-matmul-with-argmax
+    kernel): ties to the lowest index."""
+    return np.argmax(lm_head_q4_logits(hidden_bits, wq, sb_bits), axis=-1).astype(np.int32)
 
 
 def vocab_sample(logits, uniforms, uniform_stride: int, temperature: float, top_k: int, top_p: float) -> np.ndarray:

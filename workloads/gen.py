@@ -36,6 +36,8 @@ __all__ = [
     "make_queries",
     "draft_rows",
     "lm_head_inputs",
+    "quantize_q4_groups",
+    "lm_head_q4_inputs",
 ]
 
 
@@ -343,4 +345,46 @@ def lm_head_inputs(seed: int, N: int, H: int, V: int, planted=None, duplicate=No
         for a, b in duplicate:
             wb[b] = wb[a]
     return hb, wb
+
+
+def quantize_q4_groups(W) -> tuple:
+    """Affine 4-bit quantisation of W [V, H] in groups of 64 along H: per
+    group scale = (max - min) / 15 and bias = min, both rounded to bf16, codes
+    round((w - bias) / scale) clipped to 0..15 (a constant group gets scale 0
+    and code 0). Returns (wq uint32 [V, H/8], element i in bits 4 (i mod 8) of
+    word i / 8; sb bf16 bits [H/64, V, 2] holding (scale, bias))."""
+    W = np.asarray(W, dtype=np.float32)
+    V, H = W.shape
+    G = H // 64
+    g = W.reshape(V, G, 64)
+    lo = g.min(axis=2)
+    hi = g.max(axis=2)
+    s_bits = to_bf16_bits((hi - lo) / np.float32(15))
+    b_bits = to_bf16_bits(lo)
+    s = bf16_bits_to_f32(s_bits).astype(np.float64)[:, :, None]
+    b = bf16_bits_to_f32(b_bits).astype(np.float64)[:, :, None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(s > 0, np.rint((g - b) / np.where(s > 0, s, 1.0)), 0.0)
+    q = np.clip(q, 0, 15).astype(np.uint32).reshape(V, H)
+    wq = np.zeros((V, H // 8), dtype=np.uint32)
+    for j in range(8):
+        wq |= q[:, j::8] << np.uint32(4 * j)
+    sb = np.stack([s_bits.T, b_bits.T], axis=2).astype(np.uint16)
+    return wq, np.ascontiguousarray(sb)
+
+
+def lm_head_q4_inputs(seed: int, N: int, H: int, V: int, planted=None):
+    """Hidden states [N, H] N(0, 1) as bf16 bits and a 4-bit head quantised
+    from N(0, 1/H) weights. planted: {node n: vocab row t} quantises row t
+    from a multiple of hidden[n], so t carries node n's largest logit by a
+    wide margin."""
+    r = rng_for(seed, 51)
+    X = r.standard_normal((N, H), dtype=np.float32)
+    W = r.standard_normal((V, H), dtype=np.float32) * np.float32(1.0 / np.sqrt(H))
+    hb = to_bf16_bits(X)
+    if planted:
+        for n, t in planted.items():
+            W[t] = bf16_bits_to_f32(hb[n]) * np.float32(4.0 / np.sqrt(H))
+    wq, sb = quantize_q4_groups(W)
+    return hb, wq, sb
 
