@@ -424,6 +424,37 @@ def main():
               f"({kernels[f'lm_head_argmax_n{n_lm}']['GBps']} GB/s)", file=sys.stderr, flush=True)
         del x_lm
     del w_lm
+    # the same over the pages' 4-bit head (codes + a bf16 scale and bias per
+    # 64-element group: 635.7 + 39.7 + 39.7 MB), synthetic packed codes
+    G_lm = H_lm // 64
+    wq_lm = torch.randint(-2 ** 31, 2 ** 31 - 1, (V, H_lm // 8), dtype=torch.int32, device=dev, generator=gen_lm)
+    sc_lm = (torch.rand(G_lm, V, device=dev, generator=gen_lm) + 0.5) / (4.6 * H_lm ** 0.5)
+    sb_lm = torch.stack([sc_lm, -7.5 * sc_lm], dim=2).to(torch.bfloat16).contiguous()
+    for n_lm in sorted({int(batch.n_nodes), 16}):
+        x_lm = torch.randn(n_lm, H_lm, device=dev, generator=gen_lm).to(torch.bfloat16)
+        o_lm = torch.empty(n_lm, dtype=torch.int32, device=dev)
+        ws_lm = torch.empty(ttv.lm_head_argmax_ws(n_lm, V), dtype=torch.uint8, device=dev)
+        ttv.lm_head_q4_argmax(x_lm, wq_lm, sb_lm, o_lm, ws_lm)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            ttv.lm_head_q4_argmax(x_lm, wq_lm, sb_lm, o_lm, ws_lm)
+        e1.record()
+        torch.cuda.synchronize()
+        lm_ms = e0.elapsed_time(e1) / 10
+        lbytes = V * H_lm // 2 + G_lm * V * 4 + n_lm * H_lm * 2
+        lflops = 2 * n_lm * V * H_lm
+        kernels[f"lm_head_q4_argmax_n{n_lm}"] = {
+            "avg_us": round(lm_ms * 1e3, 2), "bytes": lbytes, "GBps": round(lbytes / (lm_ms / 1e3) / 1e9, 1),
+            "frac_hbm": round(lbytes / (lm_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4), "flops": lflops,
+            "TFLOPs": round(lflops / (lm_ms / 1e3) / 1e12, 1),
+            "what": f"{n_lm} nodes x {V} x {H_lm} 4-bit head (group 64, bf16 scale/bias), fused argmax",
+        }
+        print(f"[bench] 4-bit lm head + argmax, {n_lm} nodes: {lm_ms * 1e3:.1f} us "
+              f"({kernels[f'lm_head_q4_argmax_n{n_lm}']['GBps']} GB/s)", file=sys.stderr, flush=True)
+        del x_lm
+    del wq_lm, sb_lm
 
     # full-window out-of-place gather (the pages' take): every survivor of every layer rewritten
     if not args.no_take:

@@ -11,7 +11,7 @@
  *   vocab_sample         per-node draw from the nucleus-filtered distribution
  *                        (the sampled form of the target's selection)
  *   lm_head_argmax       the argmax fused with the LM-head projection, the
- *                        logits never written
+ *                        logits never written (lm_head_q4_argmax: 4-bit head)
  *   tree_accept_walk     descend the one child matching the target's argmax
  *   kv_gather_positions  compact the accepted path's K/V (and int8 scales)
  *                        along the sequence axis
@@ -322,6 +322,29 @@ size_t lm_head_argmax_ws(int64_t n_rows, int64_t vocab);
 ttv_status lm_head_argmax(const uint16_t* hidden, int64_t n_rows, int64_t hidden_stride, const uint16_t* weight,
                           int64_t vocab, int64_t hidden_dim, int64_t weight_stride, int32_t* out_idx, void* ws,
                           size_t ws_bytes, void* stream);
+
+/*
+ * The same fused argmax over a 4-bit head, the form the pages' engine holds
+ * the head in ([I1185] "The cost model": 248,320 x 5,120 codes plus a scale
+ * and a bias per group, 715.2 MB; the "Phase 3 done" comment: affine
+ * group-64 4-bit; "Proposed work" Phase 2a and its verdict: a quantised
+ * matmul with argmax). weight[v][i] = scale[g][v] * code[v][i] + bias[g][v],
+ * g = i / 64, code in 0..15.
+ *   hidden     (device) bf16 [n_rows][hidden_stride]
+ *   wq         (device) uint32 [vocab][hidden_dim / 8], 8-byte aligned: hidden
+ *                       element i of row v in bits 4 (i mod 8) of word i / 8
+ *   scale_bias (device) bf16 [hidden_dim / 64][vocab][2] (scale, bias),
+ *                       group-major, 16-byte aligned
+ *   out_idx    (device) int32 [n_rows]: lowest index of the largest logit
+ * Each group's products accumulate in fp32 from exact bf16 codes and are
+ * folded in as scale * partial + bias * (sum of the group's hidden values).
+ * Limits (TTV_ERR_INVALID): 0 <= n_rows <= 2^24, vocab a multiple of 4,
+ * hidden_dim a positive multiple of 64 (<= 2^20), hidden_stride >= hidden_dim
+ * and a multiple of 8. ws: >= lm_head_argmax_ws(n_rows, vocab) bytes.
+ */
+ttv_status lm_head_q4_argmax(const uint16_t* hidden, int64_t n_rows, int64_t hidden_stride, const uint32_t* wq,
+                             const uint16_t* scale_bias, int64_t vocab, int64_t hidden_dim, int32_t* out_idx,
+                             void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Step 4 -- accept walk [I1204] "What this needs" (2), "Increment 1"; [S728]

@@ -135,3 +135,87 @@ def test_full_size_sampled(ttv, N):
     rows = sorted(set([0, N // 3, N - 2] + list(rng_for(N, 3).choice(N, size=min(N, 5), replace=False))))
     rows = [n for n in rows if n not in plant]
     assert check(got, hb, wb, rows) >= len(rows) // 2
+
+
+# ---------------------------------------------------------------------------
+# the 4-bit head
+# ---------------------------------------------------------------------------
+
+from workloads import lm_head_q4_inputs, lm_head_q4_random  # noqa: E402
+
+
+def run_q4(ttv, hb, wq, sb):
+    N = hb.shape[0]
+    V = wq.shape[0]
+    out = torch.full((max(N, 1),), -3, dtype=torch.int32, device="cuda")
+    ws = zeros_ws(ttv.lm_head_argmax_ws(N, V))
+    ws.fill_(0x5A)
+    ttv.lm_head_q4_argmax(to_dev(hb, "bf16"), torch.from_numpy(wq.view(np.int32)).to("cuda"),
+                          to_dev(sb, "bf16"), out, ws)
+    return to_host(out)[:N]
+
+
+def check_q4(got, hb, wq, sb, rows, block=16384):
+    """Exact where the top two float64 logits are further apart than twice
+    the bound on the kernel's error, and within the bound everywhere. Bound:
+    each group's 64 products and hidden sum accumulate in fp32 and every
+    group is folded with two fma, so the error is at most
+    2^-24 (64 + 2 G + 8) sum_k |x_k| (s q_k + |b|) (G groups)."""
+    H = hb.shape[1]
+    G = H // 64
+    Xa = np.abs(bf16_bits_to_f32(hb[rows]).astype(np.float64))
+    L, A = [], []
+    for v0 in range(0, wq.shape[0], block):
+        wqb, sbb = wq[v0:v0 + block], sb[:, v0:v0 + block]
+        L.append(O.lm_head_q4_logits(hb[rows], wqb, sbb))
+        Wv = O.lm_head_q4_weight(wqb, sbb)
+        Bv = np.repeat(np.abs(bf16_bits_to_f32(sbb[:, :, 1]).astype(np.float64)).T, 64, axis=1)
+        A.append(Xa @ (np.abs(Wv - np.repeat(bf16_bits_to_f32(sbb[:, :, 1]).astype(np.float64).T, 64, axis=1))
+                       + Bv).T)
+    L, A = np.concatenate(L, axis=1), np.concatenate(A, axis=1)
+    want = np.argmax(L, axis=1)
+    decided = 0
+    for r, n in enumerate(rows):
+        tol = 2.0 ** -24 * (64 + 2 * G + 8) * A[r].max()
+        top = np.sort(L[r])[-2:]
+        assert 0 <= got[n] < wq.shape[0]
+        assert L[r, got[n]] >= top[-1] - 2 * tol, f"node {n}: {L[r, got[n]]} vs {top[-1]} (tol {tol})"
+        if top[-1] - top[-2] > 2 * tol:
+            assert got[n] == want[r], f"node {n}: {got[n]} != {want[r]}"
+            decided += 1
+    return decided
+
+
+Q4_SMALL = [(1, 64, 4), (5, 128, 20), (16, 64, 512), (40, 128, 516), (64, 256, 5000), (65, 64, 3000),
+            (130, 128, 1500), (7, 1024, 4100)]
+
+
+@pytest.mark.parametrize("N,H,V", Q4_SMALL)
+def test_q4_small_against_oracle(ttv, N, H, V):
+    log(f"lm_head_q4 N={N} H={H} V={V}")
+    hb, wq, sb = lm_head_q4_inputs(N * 3 + H + V, N, H, V)
+    got = run_q4(ttv, hb, wq, sb)
+    assert check_q4(got, hb, wq, sb, list(range(N))) >= N // 2
+
+
+def test_q4_planted(ttv):
+    N, H, V = 24, 256, 20000
+    plant = {n: (n * 811 + 5) % V for n in range(N)}
+    hb, wq, sb = lm_head_q4_inputs(19, N, H, V, planted=plant)
+    assert (run_q4(ttv, hb, wq, sb) == O.lm_head_q4_argmax(hb, wq, sb)).all()
+    assert [plant[n] for n in range(N)] == O.lm_head_q4_argmax(hb, wq, sb).tolist()
+
+
+@pytest.mark.parametrize("N", [16, 128])
+def test_q4_full_size_sampled(ttv, N):
+    # the pages' head: 248,320 rows of 5,120 four-bit codes (80 groups)
+    H, V = 5120, V5
+    plant = {0: V - 1, N // 2: 4097, N - 1: 0}
+    log(f"lm_head_q4 full size N={N}")
+    hb, wq, sb = lm_head_q4_random(200 + N, N, H, V, planted=plant)
+    got = run_q4(ttv, hb, wq, sb)
+    for n, t in plant.items():
+        assert got[n] == t
+    rows = sorted(set([1, N // 3, N - 2] + list(rng_for(N, 4).choice(N, size=min(N, 5), replace=False))))
+    rows = [n for n in rows if n not in plant]
+    assert check_q4(got, hb, wq, sb, rows) >= len(rows) // 2

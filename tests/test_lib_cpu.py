@@ -308,3 +308,21 @@ def test_lm_head_validation():
     assert call(w=None) == ttv.TTV_ERR_INVALID and "NULL" in ttv.last_error()
     assert call(x=FAKE + 2) == ttv.TTV_ERR_INVALID and "aligned" in ttv.last_error()
     assert call(ws_bytes=ws - 1) == ttv.TTV_ERR_WORKSPACE
+
+
+def test_lm_head_q4_validation():
+    A = C["lm_head_q4_argmax"]
+    V, H = 248320, 5120
+    ws = C["lm_head_argmax_ws"](16, V)
+
+    def call(n=16, hs=H, v=V, h=H, wq=FAKE, sb=FAKE, x=FAKE, ws_bytes=ws):
+        return A(x, n, hs, wq, sb, v, h, FAKE, FAKE, ws_bytes, None)
+
+    assert call(n=0) == ttv.TTV_OK
+    assert call(v=V + 2) == ttv.TTV_ERR_INVALID and "multiple of 4" in ttv.last_error()
+    assert call(h=96, hs=96) == ttv.TTV_ERR_INVALID and "multiple of 64" in ttv.last_error()
+    assert call(hs=H + 4) == ttv.TTV_ERR_INVALID
+    assert call(sb=None) == ttv.TTV_ERR_INVALID and "NULL" in ttv.last_error()
+    assert call(sb=FAKE + 8) == ttv.TTV_ERR_INVALID and "aligned" in ttv.last_error()
+    assert call(wq=FAKE + 4) == ttv.TTV_ERR_INVALID
+    assert call(ws_bytes=ws - 1) == ttv.TTV_ERR_WORKSPACE

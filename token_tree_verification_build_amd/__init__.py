@@ -83,6 +83,7 @@ _c = {
     "draft_tree_select": _sig("draft_tree_select", _i32, [_i32, _i32, _p, _p, _p, _p, _p, _i32, _p, _p, _p, _p, _p]),
     "lm_head_argmax_ws": _sig("lm_head_argmax_ws", _sz, [_i64, _i64]),
     "lm_head_argmax": _sig("lm_head_argmax", _i32, [_p, _i64, _i64, _p, _i64, _i64, _i64, _p, _p, _sz, _p]),
+    "lm_head_q4_argmax": _sig("lm_head_q4_argmax", _i32, [_p, _i64, _i64, _p, _p, _i64, _i64, _p, _p, _sz, _p]),
     "ttv_last_error": _sig("ttv_last_error", ctypes.c_char_p, []),
 }
 
@@ -488,3 +489,26 @@ def lm_head_argmax(hidden, weight, out_idx, ws, stream=None):
     wst = weight.stride(0) if V > 1 else H + (-H) % 8
     _check(_c["lm_head_argmax"](_ptr(hidden), N, hs, _ptr(weight), V, H, wst, _ptr(out_idx), _ptr(ws),
                                 ws.numel() if ws is not None else 0, _stream(stream)), "lm_head_argmax")
+
+
+def lm_head_q4_argmax(hidden, wq, scale_bias, out_idx, ws, stream=None):
+    """hidden: bf16 device tensor [N, >= H]; wq: int32 device tensor
+    [V, H / 8] of packed 4-bit codes; scale_bias: bf16 device tensor
+    [H / 64, V, 2] of (scale, bias); out_idx int32 [N]."""
+    import torch
+    if hidden.dtype != torch.bfloat16 or not hidden.is_cuda or hidden.dim() != 2 or hidden.stride(-1) != 1:
+        raise ValueError("hidden must be a 2-D bf16 device tensor with unit inner stride")
+    _dev(wq, None, "wq")
+    _dev(scale_bias, torch.bfloat16, "scale_bias")
+    if wq.dtype not in (torch.int32, torch.uint32) or wq.dim() != 2:
+        raise ValueError("wq must be a 2-D 32-bit tensor of packed codes")
+    N, H = hidden.shape
+    V = wq.shape[0]
+    if wq.shape[1] * 8 != H or tuple(scale_bias.shape) != (H // 64, V, 2):
+        raise ValueError("wq must be [V, H / 8] and scale_bias [H / 64, V, 2] for hidden [N, H]")
+    _dev(out_idx, torch.int32, "out_idx")
+    if out_idx.numel() < N:
+        raise ValueError("out_idx must hold one index per hidden row")
+    hs = hidden.stride(0) if N > 1 else H + (-H) % 8
+    _check(_c["lm_head_q4_argmax"](_ptr(hidden), N, hs, _ptr(wq), _ptr(scale_bias), V, H, _ptr(out_idx), _ptr(ws),
+                                   ws.numel() if ws is not None else 0, _stream(stream)), "lm_head_q4_argmax")

@@ -194,6 +194,219 @@ __global__ void __launch_bounds__(kLmThreads) lm_head_main(const LmParams p) {
   }
 }
 
+// The 4-bit head ([I1185] "The cost model": the borrowed head is 248,320 x
+// 5,120 codes + a scale and a bias per 64-element group; the "Phase 3 done"
+// comment: affine group-64 4-bit). Value = scale * code + bias, code 0..15,
+// 8 codes per 32-bit word (hidden element i in bits 4 (i mod 8) of word
+// i / 8), (scale, bias) bf16 pairs stored group-major [H/64][V][2].
+//
+// Same tiling as the bf16 kernel (a wave owns 64 vocabulary rows, the
+// hidden states are staged through LDS one 64-element group at a time), but
+// each 32-k MFMA step stays inside one group: lane (i, g) takes hidden
+// elements 64 gi + 8 (2g + h) .. +8 in step h, i.e. code words 8 gi + 2g and
+// 8 gi + 2g + 1 (one 8-byte load). Codes become bf16 small integers exactly,
+// each group's products accumulate from zero on the matrix cores, and the
+// group is folded in as acc += scale * partial + bias * sum(hidden over the
+// group); the group sums come from the staging. At most 64 nodes per slice
+// (the per-group accumulators double the register use).
+constexpr int kLmQ4MaxNB = 4;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u32x4 q4_to_bf16x8(uint32_t w) {
+  const uint32_t lo = w & 0x0F0F0F0Fu;         // codes 0, 2, 4, 6 in bytes 0..3
+  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // codes 1, 3, 5, 7
+  u32x4 r;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    // small integers are exact in bf16: the float's top half is the bf16
+    const uint32_t a = __float_as_uint(static_cast<float>((lo >> (8 * q)) & 0xFFu));
+    const uint32_t b = __float_as_uint(static_cast<float>((hi >> (8 * q)) & 0xFFu));
+    r[q] = (a >> 16) | (b & 0xFFFF0000u);
+  }
+  return r;
+}
+
+struct LmQ4Params {
+  const uint16_t* x;    // [N][x_stride] bf16
+  const uint32_t* wq;   // [V][H/8] packed codes
+  const uint16_t* sb;   // [H/64][V][2] bf16 (scale, bias)
+  uint64_t* part;       // [N][n_slabs]
+  int64_t x_stride;
+  int N, V, H;
+  int n_slabs, n_slices;
+};
+
+template <int NB>
+__global__ void __launch_bounds__(kLmThreads) lm_head_q4_main(const LmQ4Params p) {
+  __shared__ __attribute__((aligned(16))) unsigned char s_x[2][16 * NB * kLmXPitch];
+  __shared__ float s_xs[2][16 * NB];  // per staged row: the sum over the group
+  __shared__ uint64_t s_best[kLmWaves][16 * NB];
+  const int slot = xcd_slot(blockIdx.x, p.n_slabs * p.n_slices);
+  if (slot < 0) return;  // padding workgroup (whole block, before any barrier)
+  const int slab = slot / p.n_slices;
+  const int slice = slot % p.n_slices;
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int li = lane % 16, lg = lane / 16;
+  const int n0 = slice * 16 * kLmQ4MaxNB;
+  const int v_wave = slab * kLmSlab + wave * kLmRowsPerWave;
+  const int G = p.H / 64;
+  const int words = p.H / 8;
+
+  // code words of this lane's rows (clamped into range; rows past V are ignored)
+  const uint32_t* wrow[4];
+  int vrow[4];
+#pragma unroll
+  for (int vb = 0; vb < 4; ++vb) {
+    vrow[vb] = min(v_wave + 16 * vb + li, p.V - 1);
+    wrow[vb] = p.wq + static_cast<int64_t>(vrow[vb]) * words + 2 * lg;
+  }
+  // (scale, bias) of the lane's output rows 16 vb + 4 lg .. +3 (V % 4 == 0,
+  // so the four pairs are one aligned 16-byte load; clamped rows stay in range)
+  int srow[4];
+#pragma unroll
+  for (int vb = 0; vb < 4; ++vb) srow[vb] = min(v_wave + 16 * vb + 4 * lg, p.V - 4);
+  // hidden-state staging: piece t covers row t / 8, bytes 16 (t % 8) of the
+  // group; the 8 pieces of a row sit in 8 consecutive lanes, which also sum it
+  constexpr int kPieces = 16 * NB * 8;
+  constexpr int kPiecesPerThread = (kPieces + kLmThreads - 1) / kLmThreads;
+  auto x_piece = [&](int c, int r) -> u32x4 {
+    const int t = threadIdx.x + kLmThreads * r;
+    const int row = min(n0 + t / 8, p.N - 1);
+    const unsigned char* src = reinterpret_cast<const unsigned char*>(p.x + static_cast<int64_t>(row) * p.x_stride) +
+                               c * (kLmKc * 2) + 16 * (t % 8);
+    return *reinterpret_cast<const u32x4*>(src);
+  };
+  auto x_store = [&](int buf, int r, u32x4 v) {
+    const int t = threadIdx.x + kLmThreads * r;
+    *reinterpret_cast<u32x4*>(&s_x[buf][(t / 8) * kLmXPitch + 16 * (t % 8)]) = v;
+    float sum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sum += __uint_as_float(v[e] << 16);
+      sum += __uint_as_float(v[e] & 0xFFFF0000u);
+    }
+    sum += __shfl_xor(sum, 1);
+    sum += __shfl_xor(sum, 2);
+    sum += __shfl_xor(sum, 4);
+    if (t % 8 == 0) s_xs[buf][t / 8] = sum;
+  };
+
+  f32x4 acc[4][NB];
+#pragma unroll
+  for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[vb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 xs[kPiecesPerThread];
+#pragma unroll
+  for (int r = 0; r < kPiecesPerThread; ++r)
+    if (threadIdx.x + kLmThreads * r < kPieces) xs[r] = x_piece(0, r);
+#pragma unroll
+  for (int r = 0; r < kPiecesPerThread; ++r)
+    if (threadIdx.x + kLmThreads * r < kPieces) x_store(0, r, xs[r]);
+  u32x2 wcur[4];
+  u32x4 sbcur[4];
+#pragma unroll
+  for (int vb = 0; vb < 4; ++vb) {
+    wcur[vb] = *reinterpret_cast<const u32x2*>(wrow[vb]);
+    sbcur[vb] = *reinterpret_cast<const u32x4*>(p.sb + 2 * static_cast<int64_t>(srow[vb]));
+  }
+  __syncthreads();
+
+  for (int c = 0; c < G; ++c) {
+    const int buf = c & 1;
+    const bool more = c + 1 < G;
+    u32x2 wnext[4];
+    u32x4 sbnext[4];
+    if (more) {
+#pragma unroll
+      for (int r = 0; r < kPiecesPerThread; ++r)
+        if (threadIdx.x + kLmThreads * r < kPieces) xs[r] = x_piece(c + 1, r);
+#pragma unroll
+      for (int vb = 0; vb < 4; ++vb) {
+        wnext[vb] = *reinterpret_cast<const u32x2*>(wrow[vb] + 8 * (c + 1));
+        sbnext[vb] = *reinterpret_cast<const u32x4*>(p.sb + 2 * (static_cast<int64_t>(c + 1) * p.V + srow[vb]));
+      }
+    }
+    // the group's partial sums, from zero
+    f32x4 part[4][NB];
+#pragma unroll
+    for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) part[vb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      bf16x8 xf[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        xf[nb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                &s_x[buf][(16 * nb + li) * kLmXPitch + 32 * lg + 16 * h]));
+#pragma unroll
+      for (int vb = 0; vb < 4; ++vb) {
+        const bf16x8 wf = __builtin_bit_cast(bf16x8, q4_to_bf16x8(wcur[vb][h]));
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          part[vb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xf[nb], part[vb][nb], 0, 0, 0);
+      }
+    }
+    // fold the group in: output (row 16 vb + 4 lg + j, node 16 nb + li)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const float xsum = s_xs[buf][16 * nb + li];
+#pragma unroll
+      for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float sc = __uint_as_float(sbcur[vb][j] << 16);
+          const float bi = __uint_as_float(sbcur[vb][j] & 0xFFFF0000u);
+          acc[vb][nb][j] = fmaf(sc, part[vb][nb][j], fmaf(bi, xsum, acc[vb][nb][j]));
+        }
+    }
+    if (more) {
+#pragma unroll
+      for (int r = 0; r < kPiecesPerThread; ++r)
+        if (threadIdx.x + kLmThreads * r < kPieces) x_store(buf ^ 1, r, xs[r]);
+#pragma unroll
+      for (int vb = 0; vb < 4; ++vb) {
+        wcur[vb] = wnext[vb];
+        sbcur[vb] = sbnext[vb];
+      }
+    }
+    __syncthreads();
+  }
+
+  // epilogue: node 16 nb + li's best over the lane's rows 16 vb + 4 lg + j
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int v = v_wave + 16 * vb + 4 * lg + j;
+        if (v < p.V) {
+          const uint64_t k = lm_key(acc[vb][nb][j], static_cast<uint32_t>(v));
+          best = k > best ? k : best;
+        }
+      }
+#pragma unroll
+    for (int off = 16; off <= 32; off <<= 1) {
+      const uint64_t o = __shfl_xor(best, off);
+      best = o > best ? o : best;
+    }
+    if (lg == 0) s_best[wave][16 * nb + li] = best;
+  }
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < 16 * NB && n0 + t < p.N) {
+    uint64_t best = s_best[0][t];
+#pragma unroll
+    for (int w = 1; w < kLmWaves; ++w) best = s_best[w][t] > best ? s_best[w][t] : best;
+    p.part[static_cast<int64_t>(n0 + t) * p.n_slabs + slab] = best;
+  }
+}
+
 // one wave per node: the best key over the vocabulary slabs
 __global__ void __launch_bounds__(kWave) lm_head_reduce(const uint64_t* __restrict__ part, int n_slabs,
                                                         int32_t* __restrict__ out_idx) {
@@ -271,4 +484,59 @@ extern "C" ttv_status lm_head_argmax(const uint16_t* hidden, int64_t n_rows, int
   hipLaunchKernelGGL(lm_head_reduce, dim3(static_cast<unsigned>(n_rows)), dim3(kWave), 0, s,
                      static_cast<const uint64_t*>(p.part), p.n_slabs, out_idx);
   return check_launch("lm_head_argmax reduce");
+}
+
+extern "C" ttv_status lm_head_q4_argmax(const uint16_t* hidden, int64_t n_rows, int64_t hidden_stride,
+                                        const uint32_t* wq, const uint16_t* scale_bias, int64_t vocab,
+                                        int64_t hidden_dim, int32_t* out_idx, void* ws, size_t ws_bytes,
+                                        void* stream) {
+  clear_error();
+  TTV_REQUIRE(n_rows >= 0 && n_rows <= (1 << 24), TTV_ERR_INVALID,
+              "lm_head_q4_argmax: n_rows %lld not in [0, 2^24]", (long long)n_rows);
+  if (n_rows == 0) return TTV_OK;
+  TTV_REQUIRE(vocab >= 4 && vocab % 4 == 0 && vocab <= 0x7FFFFFFF, TTV_ERR_INVALID,
+              "lm_head_q4_argmax: vocab %lld must be a multiple of 4 in [4, 2^31 - 1]", (long long)vocab);
+  TTV_REQUIRE(hidden_dim >= 64 && hidden_dim % 64 == 0 && hidden_dim <= (1 << 20), TTV_ERR_INVALID,
+              "lm_head_q4_argmax: hidden_dim %lld is not a positive multiple of 64 (<= 2^20)",
+              (long long)hidden_dim);
+  TTV_REQUIRE(hidden_stride >= hidden_dim && hidden_stride % 8 == 0, TTV_ERR_INVALID,
+              "lm_head_q4_argmax: hidden_stride %lld must be >= hidden_dim and a multiple of 8",
+              (long long)hidden_stride);
+  TTV_REQUIRE(hidden && wq && scale_bias && out_idx, TTV_ERR_INVALID, "lm_head_q4_argmax: NULL pointer");
+  TTV_REQUIRE(reinterpret_cast<uintptr_t>(hidden) % 16 == 0 && reinterpret_cast<uintptr_t>(wq) % 8 == 0 &&
+                  reinterpret_cast<uintptr_t>(scale_bias) % 16 == 0,
+              TTV_ERR_INVALID, "lm_head_q4_argmax: hidden and scale_bias must be 16-byte aligned, wq 8-byte");
+  TTV_REQUIRE(vocab * (hidden_dim / 8) <= (int64_t{1} << 40), TTV_ERR_INVALID, "lm_head_q4_argmax: head too large");
+  const size_t need = lm_head_argmax_ws(n_rows, vocab);
+  TTV_REQUIRE(ws && ws_bytes >= need, TTV_ERR_WORKSPACE, "lm_head_q4_argmax: workspace %zu bytes < %zu", ws_bytes,
+              need);
+  LmQ4Params p;
+  p.x = hidden;
+  p.wq = wq;
+  p.sb = scale_bias;
+  p.part = static_cast<uint64_t*>(ws);
+  p.x_stride = hidden_stride;
+  p.N = static_cast<int>(n_rows);
+  p.V = static_cast<int>(vocab);
+  p.H = static_cast<int>(hidden_dim);
+  p.n_slabs = lm_slabs(vocab);
+  p.n_slices = static_cast<int>((n_rows + 16 * kLmQ4MaxNB - 1) / (16 * kLmQ4MaxNB));
+  const int64_t n_wg = static_cast<int64_t>(p.n_slabs) * p.n_slices;
+  TTV_REQUIRE(n_wg <= (1ll << 30), TTV_ERR_INVALID, "lm_head_q4_argmax: too many workgroups");
+  const unsigned grid = static_cast<unsigned>((n_wg + kNumXcd - 1) / kNumXcd * kNumXcd);
+  const int rows0 = static_cast<int>(n_rows < 16 * kLmQ4MaxNB ? n_rows : 16 * kLmQ4MaxNB);
+  const int nb = (rows0 + 15) / 16;
+  hipStream_t s = (hipStream_t)stream;
+  switch (nb) {
+#define TTV_LMQ(NB) \
+  case NB: hipLaunchKernelGGL(lm_head_q4_main<NB>, dim3(grid), dim3(kLmThreads), 0, s, p); break;
+    TTV_LMQ(1) TTV_LMQ(2) TTV_LMQ(3) TTV_LMQ(4)
+#undef TTV_LMQ
+    default: return fail(TTV_ERR_INVALID, "lm_head_q4_argmax: internal node-block count");
+  }
+  ttv_status st = check_launch("lm_head_q4_argmax main");
+  if (st != TTV_OK) return st;
+  hipLaunchKernelGGL(lm_head_reduce, dim3(static_cast<unsigned>(n_rows)), dim3(kWave), 0, s,
+                     static_cast<const uint64_t*>(p.part), p.n_slabs, out_idx);
+  return check_launch("lm_head_q4_argmax reduce");
 }

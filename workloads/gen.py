@@ -38,6 +38,7 @@ __all__ = [
     "lm_head_inputs",
     "quantize_q4_groups",
     "lm_head_q4_inputs",
+    "lm_head_q4_random",
 ]
 
 
@@ -387,4 +388,28 @@ def lm_head_q4_inputs(seed: int, N: int, H: int, V: int, planted=None):
             W[t] = bf16_bits_to_f32(hb[n]) * np.float32(4.0 / np.sqrt(H))
     wq, sb = quantize_q4_groups(W)
     return hb, wq, sb
+
+
+def lm_head_q4_random(seed: int, N: int, H: int, V: int, planted=None):
+    """A 4-bit head drawn directly in packed form (no float copy of the
+    weight, so the full 248,320 x 5,120 head fits in host memory): uniform
+    codes 0..15, per group scale s ~ U(0.5, 1.5) / (4.6 sqrt(H)) and bias
+    about -7.5 s (values centred, unit-variance logits), both bf16; hidden
+    states N(0, 1). planted: {node n: row t} re-quantises row t from a
+    multiple of hidden[n]."""
+    r = rng_for(seed, 52)
+    X = r.standard_normal((N, H), dtype=np.float32)
+    hb = to_bf16_bits(X)
+    G = H // 64
+    wq = r.integers(0, 2 ** 32, size=(V, H // 8), dtype=np.uint32)
+    sc = (r.uniform(0.5, 1.5, size=(G, V)) / (4.6 * np.sqrt(H))).astype(np.float32)
+    bi = (-7.5 * sc * r.uniform(0.9, 1.1, size=(G, V))).astype(np.float32)
+    sb = np.stack([to_bf16_bits(sc), to_bf16_bits(bi)], axis=2).astype(np.uint16)
+    if planted:
+        for n, t in planted.items():
+            row = bf16_bits_to_f32(hb[n]) * np.float32(4.0 / np.sqrt(H))
+            q1, sb1 = quantize_q4_groups(row[None, :])
+            wq[t] = q1[0]
+            sb[:, t, :] = sb1[:, 0, :]
+    return hb, wq, np.ascontiguousarray(sb)
 
