@@ -148,7 +148,7 @@ def run_q4(ttv, hb, wq, sb):
     N = hb.shape[0]
     V = wq.shape[0]
     out = torch.full((max(N, 1),), -3, dtype=torch.int32, device="cuda")
-    ws = zeros_ws(ttv.lm_head_argmax_ws(N, V))
+    ws = zeros_ws(ttv.lm_head_q4_argmax_ws(N, V))
     ws.fill_(0x5A)
     ttv.lm_head_q4_argmax(to_dev(hb, "bf16"), torch.from_numpy(wq.view(np.int32)).to("cuda"),
                           to_dev(sb, "bf16"), out, ws)

@@ -313,7 +313,8 @@ def test_lm_head_validation():
 def test_lm_head_q4_validation():
     A = C["lm_head_q4_argmax"]
     V, H = 248320, 5120
-    ws = C["lm_head_argmax_ws"](16, V)
+    ws = C["lm_head_q4_argmax_ws"](16, V)
+    assert ws == 16 * ((V + 255) // 256) * 8
 
     def call(n=16, hs=H, v=V, h=H, wq=FAKE, sb=FAKE, x=FAKE, ws_bytes=ws):
         return A(x, n, hs, wq, sb, v, h, FAKE, FAKE, ws_bytes, None)

@@ -210,19 +210,34 @@ __global__ void __launch_bounds__(kLmThreads) lm_head_main(const LmParams p) {
 // group); the group sums come from the staging. At most 64 nodes per slice
 // (the per-group accumulators double the register use).
 constexpr int kLmQ4MaxNB = 4;
+// up to 32 nodes: 4-wave workgroups (256 vocabulary rows), three per CU, for
+// more loads in flight; more nodes: 8-wave workgroups (512 rows), which halve
+// the hidden-state staging per weight byte
+constexpr int kLmQ4Slab = 4 * kLmRowsPerWave;              // the smaller slab, for the workspace
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// byte B of x as a float (v_cvt_f32_ubyte<B>: one instruction, where the
+// compiler otherwise extracts the byte first)
+template <int B>
+__device__ __forceinline__ float ubyte_f32(uint32_t x) {
+  float f;
+  if constexpr (B == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(f) : "v"(x));
+  else if constexpr (B == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(f) : "v"(x));
+  else if constexpr (B == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(f) : "v"(x));
+  else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(f) : "v"(x));
+  return f;
+}
+
+// 8 codes of one word as bf16x8: small integers are exact in bf16, so a
+// float's top half is the bf16; one byte permute packs two of them
 __device__ __forceinline__ u32x4 q4_to_bf16x8(uint32_t w) {
   const uint32_t lo = w & 0x0F0F0F0Fu;         // codes 0, 2, 4, 6 in bytes 0..3
   const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // codes 1, 3, 5, 7
   u32x4 r;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    // small integers are exact in bf16: the float's top half is the bf16
-    const uint32_t a = __float_as_uint(static_cast<float>((lo >> (8 * q)) & 0xFFu));
-    const uint32_t b = __float_as_uint(static_cast<float>((hi >> (8 * q)) & 0xFFu));
-    r[q] = (a >> 16) | (b & 0xFFFF0000u);
-  }
+  r[0] = __builtin_amdgcn_perm(__float_as_uint(ubyte_f32<0>(hi)), __float_as_uint(ubyte_f32<0>(lo)), 0x07060302u);
+  r[1] = __builtin_amdgcn_perm(__float_as_uint(ubyte_f32<1>(hi)), __float_as_uint(ubyte_f32<1>(lo)), 0x07060302u);
+  r[2] = __builtin_amdgcn_perm(__float_as_uint(ubyte_f32<2>(hi)), __float_as_uint(ubyte_f32<2>(lo)), 0x07060302u);
+  r[3] = __builtin_amdgcn_perm(__float_as_uint(ubyte_f32<3>(hi)), __float_as_uint(ubyte_f32<3>(lo)), 0x07060302u);
   return r;
 }
 
@@ -236,20 +251,22 @@ struct LmQ4Params {
   int n_slabs, n_slices;
 };
 
-template <int NB>
-__global__ void __launch_bounds__(kLmThreads) lm_head_q4_main(const LmQ4Params p) {
+template <int NB, int NW>
+__global__ void __launch_bounds__(NW * kWave) lm_head_q4_main(const LmQ4Params p) {
+  constexpr int kLmQ4Threads = NW * kWave;
+  constexpr int kSlab = NW * kLmRowsPerWave;
   __shared__ __attribute__((aligned(16))) unsigned char s_x[2][16 * NB * kLmXPitch];
   __shared__ float s_xs[2][16 * NB];  // per staged row: the sum over the group
-  __shared__ uint64_t s_best[kLmWaves][16 * NB];
+  __shared__ uint64_t s_best[NW][16 * NB];
   const int slot = xcd_slot(blockIdx.x, p.n_slabs * p.n_slices);
   if (slot < 0) return;  // padding workgroup (whole block, before any barrier)
   const int slab = slot / p.n_slices;
   const int slice = slot % p.n_slices;
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave));
   const int lane = threadIdx.x % kWave;
   const int li = lane % 16, lg = lane / 16;
   const int n0 = slice * 16 * kLmQ4MaxNB;
-  const int v_wave = slab * kLmSlab + wave * kLmRowsPerWave;
+  const int v_wave = slab * kSlab + wave * kLmRowsPerWave;
   const int G = p.H / 64;
   const int words = p.H / 8;
 
@@ -269,16 +286,16 @@ __global__ void __launch_bounds__(kLmThreads) lm_head_q4_main(const LmQ4Params p
   // hidden-state staging: piece t covers row t / 8, bytes 16 (t % 8) of the
   // group; the 8 pieces of a row sit in 8 consecutive lanes, which also sum it
   constexpr int kPieces = 16 * NB * 8;
-  constexpr int kPiecesPerThread = (kPieces + kLmThreads - 1) / kLmThreads;
+  constexpr int kPiecesPerThread = (kPieces + kLmQ4Threads - 1) / kLmQ4Threads;
   auto x_piece = [&](int c, int r) -> u32x4 {
-    const int t = threadIdx.x + kLmThreads * r;
+    const int t = threadIdx.x + kLmQ4Threads * r;
     const int row = min(n0 + t / 8, p.N - 1);
     const unsigned char* src = reinterpret_cast<const unsigned char*>(p.x + static_cast<int64_t>(row) * p.x_stride) +
                                c * (kLmKc * 2) + 16 * (t % 8);
     return *reinterpret_cast<const u32x4*>(src);
   };
   auto x_store = [&](int buf, int r, u32x4 v) {
-    const int t = threadIdx.x + kLmThreads * r;
+    const int t = threadIdx.x + kLmQ4Threads * r;
     *reinterpret_cast<u32x4*>(&s_x[buf][(t / 8) * kLmXPitch + 16 * (t % 8)]) = v;
     float sum = 0.f;
 #pragma unroll
@@ -301,33 +318,44 @@ __global__ void __launch_bounds__(kLmThreads) lm_head_q4_main(const LmQ4Params p
   u32x4 xs[kPiecesPerThread];
 #pragma unroll
   for (int r = 0; r < kPiecesPerThread; ++r)
-    if (threadIdx.x + kLmThreads * r < kPieces) xs[r] = x_piece(0, r);
+    if (threadIdx.x + kLmQ4Threads * r < kPieces) xs[r] = x_piece(0, r);
 #pragma unroll
   for (int r = 0; r < kPiecesPerThread; ++r)
-    if (threadIdx.x + kLmThreads * r < kPieces) x_store(0, r, xs[r]);
-  u32x2 wcur[4];
-  u32x4 sbcur[4];
+    if (threadIdx.x + kLmQ4Threads * r < kPieces) x_store(0, r, xs[r]);
+  // code words and (scale, bias) pairs two groups ahead: group c is used
+  // while c + 1 and c + 2 load. The next group's hidden pieces are issued
+  // before group c + 2's words, so waiting for them at the end of the step
+  // (the load counter completes in issue order) never waits for c + 2.
+  u32x2 wcur[4], wnext[4];
+  u32x4 sbcur[4], sbnext[4];
+  const int last = G - 1;
 #pragma unroll
   for (int vb = 0; vb < 4; ++vb) {
     wcur[vb] = *reinterpret_cast<const u32x2*>(wrow[vb]);
     sbcur[vb] = *reinterpret_cast<const u32x4*>(p.sb + 2 * static_cast<int64_t>(srow[vb]));
+  }
+#pragma unroll
+  for (int vb = 0; vb < 4; ++vb) {
+    wnext[vb] = *reinterpret_cast<const u32x2*>(wrow[vb] + 8 * min(1, last));
+    sbnext[vb] = *reinterpret_cast<const u32x4*>(p.sb + 2 * (static_cast<int64_t>(min(1, last)) * p.V + srow[vb]));
   }
   __syncthreads();
 
   for (int c = 0; c < G; ++c) {
     const int buf = c & 1;
     const bool more = c + 1 < G;
-    u32x2 wnext[4];
-    u32x4 sbnext[4];
     if (more) {
 #pragma unroll
       for (int r = 0; r < kPiecesPerThread; ++r)
-        if (threadIdx.x + kLmThreads * r < kPieces) xs[r] = x_piece(c + 1, r);
+        if (threadIdx.x + kLmQ4Threads * r < kPieces) xs[r] = x_piece(c + 1, r);
+    }
+    u32x2 wn2[4];
+    u32x4 sbn2[4];
+    const int c2 = min(c + 2, last);  // past the end: a re-read of the last group (L2), never used
 #pragma unroll
-      for (int vb = 0; vb < 4; ++vb) {
-        wnext[vb] = *reinterpret_cast<const u32x2*>(wrow[vb] + 8 * (c + 1));
-        sbnext[vb] = *reinterpret_cast<const u32x4*>(p.sb + 2 * (static_cast<int64_t>(c + 1) * p.V + srow[vb]));
-      }
+    for (int vb = 0; vb < 4; ++vb) {
+      wn2[vb] = *reinterpret_cast<const u32x2*>(wrow[vb] + 8 * c2);
+      sbn2[vb] = *reinterpret_cast<const u32x4*>(p.sb + 2 * (static_cast<int64_t>(c2) * p.V + srow[vb]));
     }
     // the group's partial sums, from zero
     f32x4 part[4][NB];
@@ -366,12 +394,14 @@ __global__ void __launch_bounds__(kLmThreads) lm_head_q4_main(const LmQ4Params p
     if (more) {
 #pragma unroll
       for (int r = 0; r < kPiecesPerThread; ++r)
-        if (threadIdx.x + kLmThreads * r < kPieces) x_store(buf ^ 1, r, xs[r]);
+        if (threadIdx.x + kLmQ4Threads * r < kPieces) x_store(buf ^ 1, r, xs[r]);
+    }
 #pragma unroll
-      for (int vb = 0; vb < 4; ++vb) {
-        wcur[vb] = wnext[vb];
-        sbcur[vb] = sbnext[vb];
-      }
+    for (int vb = 0; vb < 4; ++vb) {
+      wcur[vb] = wnext[vb];
+      sbcur[vb] = sbnext[vb];
+      wnext[vb] = wn2[vb];
+      sbnext[vb] = sbn2[vb];
     }
     __syncthreads();
   }
@@ -402,7 +432,7 @@ __global__ void __launch_bounds__(kLmThreads) lm_head_q4_main(const LmQ4Params p
   if (t < 16 * NB && n0 + t < p.N) {
     uint64_t best = s_best[0][t];
 #pragma unroll
-    for (int w = 1; w < kLmWaves; ++w) best = s_best[w][t] > best ? s_best[w][t] : best;
+    for (int w = 1; w < NW; ++w) best = s_best[w][t] > best ? s_best[w][t] : best;
     p.part[static_cast<int64_t>(n0 + t) * p.n_slabs + slab] = best;
   }
 }
@@ -486,6 +516,11 @@ extern "C" ttv_status lm_head_argmax(const uint16_t* hidden, int64_t n_rows, int
   return check_launch("lm_head_argmax reduce");
 }
 
+extern "C" size_t lm_head_q4_argmax_ws(int64_t n_rows, int64_t vocab) {
+  if (n_rows <= 0 || vocab <= 0) return 0;
+  return static_cast<size_t>(n_rows) * static_cast<size_t>((vocab + kLmQ4Slab - 1) / kLmQ4Slab) * sizeof(uint64_t);
+}
+
 extern "C" ttv_status lm_head_q4_argmax(const uint16_t* hidden, int64_t n_rows, int64_t hidden_stride,
                                         const uint32_t* wq, const uint16_t* scale_bias, int64_t vocab,
                                         int64_t hidden_dim, int32_t* out_idx, void* ws, size_t ws_bytes,
@@ -507,7 +542,7 @@ extern "C" ttv_status lm_head_q4_argmax(const uint16_t* hidden, int64_t n_rows, 
                   reinterpret_cast<uintptr_t>(scale_bias) % 16 == 0,
               TTV_ERR_INVALID, "lm_head_q4_argmax: hidden and scale_bias must be 16-byte aligned, wq 8-byte");
   TTV_REQUIRE(vocab * (hidden_dim / 8) <= (int64_t{1} << 40), TTV_ERR_INVALID, "lm_head_q4_argmax: head too large");
-  const size_t need = lm_head_argmax_ws(n_rows, vocab);
+  const size_t need = lm_head_q4_argmax_ws(n_rows, vocab);
   TTV_REQUIRE(ws && ws_bytes >= need, TTV_ERR_WORKSPACE, "lm_head_q4_argmax: workspace %zu bytes < %zu", ws_bytes,
               need);
   LmQ4Params p;
@@ -519,18 +554,19 @@ extern "C" ttv_status lm_head_q4_argmax(const uint16_t* hidden, int64_t n_rows, 
   p.N = static_cast<int>(n_rows);
   p.V = static_cast<int>(vocab);
   p.H = static_cast<int>(hidden_dim);
-  p.n_slabs = lm_slabs(vocab);
+  const int rows0 = static_cast<int>(n_rows < 16 * kLmQ4MaxNB ? n_rows : 16 * kLmQ4MaxNB);
+  const int nb = (rows0 + 15) / 16;
+  const int nw = nb <= 2 ? 4 : 8;
+  p.n_slabs = static_cast<int>((vocab + nw * kLmRowsPerWave - 1) / (nw * kLmRowsPerWave));
   p.n_slices = static_cast<int>((n_rows + 16 * kLmQ4MaxNB - 1) / (16 * kLmQ4MaxNB));
   const int64_t n_wg = static_cast<int64_t>(p.n_slabs) * p.n_slices;
   TTV_REQUIRE(n_wg <= (1ll << 30), TTV_ERR_INVALID, "lm_head_q4_argmax: too many workgroups");
   const unsigned grid = static_cast<unsigned>((n_wg + kNumXcd - 1) / kNumXcd * kNumXcd);
-  const int rows0 = static_cast<int>(n_rows < 16 * kLmQ4MaxNB ? n_rows : 16 * kLmQ4MaxNB);
-  const int nb = (rows0 + 15) / 16;
   hipStream_t s = (hipStream_t)stream;
   switch (nb) {
-#define TTV_LMQ(NB) \
-  case NB: hipLaunchKernelGGL(lm_head_q4_main<NB>, dim3(grid), dim3(kLmThreads), 0, s, p); break;
-    TTV_LMQ(1) TTV_LMQ(2) TTV_LMQ(3) TTV_LMQ(4)
+#define TTV_LMQ(NB, NW) \
+  case NB: hipLaunchKernelGGL((lm_head_q4_main<NB, NW>), dim3(grid), dim3(NW * kWave), 0, s, p); break;
+    TTV_LMQ(1, 4) TTV_LMQ(2, 4) TTV_LMQ(3, 8) TTV_LMQ(4, 8)
 #undef TTV_LMQ
     default: return fail(TTV_ERR_INVALID, "lm_head_q4_argmax: internal node-block count");
   }
