@@ -187,7 +187,7 @@ def check_q4(got, hb, wq, sb, rows, block=16384):
 
 
 Q4_SMALL = [(1, 64, 4), (5, 128, 20), (16, 64, 512), (40, 128, 516), (64, 256, 5000), (65, 64, 3000),
-            (130, 128, 1500), (7, 1024, 4100)]
+            (130, 128, 1500), (7, 1024, 4100), (20, 320, 1000), (32, 192, 772)]
 
 
 @pytest.mark.parametrize("N,H,V", Q4_SMALL)
