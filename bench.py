@@ -315,7 +315,25 @@ def main():
             ttv.tree_verify_attention(batch, qs[l], layers[l], anc, scale, out, ws)
             e1.record()
     torch.cuda.synchronize()
-    attn_ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / len(evs)
+    attn_all = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    attn_ms = sum(attn_all) / len(attn_all)
+    # per-step durations (a further pass, events around each whole step):
+    # median and spread next to the block-timed mean
+    sevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for e0, e1 in sevs:
+        e0.record()
+        step()
+        e1.record()
+    torch.cuda.synchronize()
+    step_all = sorted(e0.elapsed_time(e1) for e0, e1 in sevs)
+
+    def quantiles(xs):
+        def q(f):
+            return xs[min(len(xs) - 1, int(round(f * (len(xs) - 1))))]
+        return {"median": round(q(0.5), 4), "p10": round(q(0.1), 4), "p90": round(q(0.9), 4),
+                "min": round(xs[0], 4), "max": round(xs[-1], 4)}
+
     abytes = attention_bytes(spec)
     aflops = attention_flops(spec)
     attn_gbs = abytes / (attn_ms / 1e3) / 1e9
@@ -327,6 +345,7 @@ def main():
             "avg_us": round(attn_ms * 1e3, 2), "bytes": abytes, "GBps": round(attn_gbs, 1),
             "frac_hbm": round(attn_gbs / HBM_PEAK_GBS, 4), "flops": aflops,
             "TFLOPs": round(aflops / (attn_ms / 1e3) / 1e12, 1),
+            "us_quantiles": {k: round(v * 1e3, 2) for k, v in quantiles(attn_all).items()},
         }
     }
 
@@ -524,6 +543,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "step_ms_quantiles": quantiles(step_all),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
