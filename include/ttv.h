@@ -341,7 +341,7 @@ ttv_status lm_head_argmax(const uint16_t* hidden, int64_t n_rows, int64_t hidden
  * Limits (TTV_ERR_INVALID): 0 <= n_rows <= 2^24, vocab a multiple of 4,
  * hidden_dim a positive multiple of 64 (<= 2^20), hidden_stride >= hidden_dim
  * and a multiple of 8. ws: >= lm_head_q4_argmax_ws(n_rows, vocab) bytes,
- * contents irrelevant.
+ * contents irrelevant. The codes are read once per 64 nodes.
  */
 size_t lm_head_q4_argmax_ws(int64_t n_rows, int64_t vocab);
 ttv_status lm_head_q4_argmax(const uint16_t* hidden, int64_t n_rows, int64_t hidden_stride, const uint32_t* wq,
