@@ -135,20 +135,123 @@ __global__ void __launch_bounds__(kSelLanes * kSelWaves)
   if (c >= n_chunks) return;  // whole wave; pass 1 has no workgroup barrier
   const float* __restrict__ x = logits + static_cast<int64_t>(row) * row_stride;
   const int64_t c0 = static_cast<int64_t>(c) * kChunk;
-  // the lane's ordered values: element c0 + 4 (64 j + lane) + q; past vocab 0
-  uint32_t ov[PER_LANE];
   auto idx_of = [&](int j) -> uint32_t { return static_cast<uint32_t>(c0 + 4 * (64 * (j >> 2) + lane) + (j & 3)); };
+  uint64_t* out = cand + (static_cast<int64_t>(row) * n_chunks + c) * k;
   if (vec && c0 + kChunk <= vocab) {
+    // A full, aligned chunk: the values stay floats. The lane maxima, the
+    // candidate test and the statistics run on them; only candidates become
+    // ordered keys. x >= value(tau) is the same test as ord(x) >= tau for
+    // every number (ord is monotone, -0.0 and +0.0 compare equal both ways),
+    // and a NaN, which ranks above every number, is always a candidate.
+    float xf[PER_LANE];
     const f32x4* __restrict__ xv = reinterpret_cast<const f32x4*>(x + c0);
 #pragma unroll
     for (int j = 0; j < PER_LANE / 4; ++j) {
       const f32x4 a = __builtin_nontemporal_load(xv + 64 * j + lane);
-      ov[4 * j] = sample_ord(a.x);
-      ov[4 * j + 1] = sample_ord(a.y);
-      ov[4 * j + 2] = sample_ord(a.z);
-      ov[4 * j + 3] = sample_ord(a.w);
+      xf[4 * j] = a.x;
+      xf[4 * j + 1] = a.y;
+      xf[4 * j + 2] = a.z;
+      xf[4 * j + 3] = a.w;
     }
-  } else {
+    float lmf = -INFINITY, lmin = INFINITY;
+    bool lnan = false;
+#pragma unroll
+    for (int j = 0; j < PER_LANE; ++j) {
+      lmf = fmaxf(lmf, xf[j]);  // a NaN operand is skipped; NaNs are tracked apart
+      lnan |= xf[j] != xf[j];
+      if constexpr (kStats) lmin = fminf(lmin, xf[j]);
+    }
+    const uint32_t lmax = lnan ? 0xFFFFFFFFu : sample_ord(lmf);
+    if constexpr (kStats) {
+      uint32_t wm = lmax;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const uint32_t o = static_cast<uint32_t>(__shfl_xor(static_cast<int>(wm), off));
+        wm = o > wm ? o : wm;
+      }
+      const double m = static_cast<double>(key_value(static_cast<uint64_t>(wm) << 32));
+      const bool bad = lnan || lmf == INFINITY || lmin == -INFINITY;
+      double sum = 0.0;
+#pragma unroll
+      for (int j = 0; j < PER_LANE; ++j) sum += exp_nonpos_f64(static_cast<double>(xf[j]) - m);
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+      const bool any_bad = __ballot(bad) != 0;
+      if (lane == 0) {
+        ChunkStats st;
+        st.sum = sum;
+        st.max = static_cast<float>(m);
+        st.bad = any_bad ? 1 : 0;
+        stats[static_cast<int64_t>(row) * n_chunks + c] = st;
+      }
+    }
+    const uint32_t tau = max(wave_kth_largest32(lmax, k), 1u);
+    const float tau_f = key_value(static_cast<uint64_t>(tau) << 32);  // NaN when tau is the NaN rank
+    auto fkey = [&](int j) -> uint64_t {
+      return (static_cast<uint64_t>(sample_ord(xf[j])) << 32) | (0xFFFFFFFFu - idx_of(j));
+    };
+    uint64_t* sc = s_cand[wave];
+    int total = 0;
+#pragma unroll
+    for (int j = 0; j < PER_LANE; ++j) {
+      const bool is = xf[j] >= tau_f || xf[j] != xf[j];
+      const uint64_t m = __ballot(is);
+      if (m == 0) continue;
+      const int at = total + lanes_below(m);
+      if (is && at < kSelCap) sc[at] = fkey(j);
+      total += __popcll(m);
+    }
+    int n_out = 0;
+    if (total <= kSelLanes) {
+      __builtin_amdgcn_wave_barrier();
+      const uint64_t h1[1] = {lane < total ? sc[lane] : 0ull};
+      const uint64_t kth = wave_kth_largest(h1, k);
+      const bool is = h1[0] != 0 && h1[0] >= kth;
+      const uint64_t m = __ballot(is);
+      if (is) out[lanes_below(m)] = h1[0];
+      n_out = __popcll(m);
+    } else if (total <= kSelCap) {
+      __builtin_amdgcn_wave_barrier();
+      uint64_t h[kSelCap / kSelLanes];
+#pragma unroll
+      for (int q = 0; q < kSelCap / kSelLanes; ++q) {
+        const int at = lane + kSelLanes * q;
+        h[q] = at < total ? sc[at] : 0ull;
+      }
+      const uint64_t kth = wave_kth_largest(h, k);
+#pragma unroll
+      for (int q = 0; q < kSelCap / kSelLanes; ++q) {
+        const bool is = h[q] != 0 && h[q] >= kth;
+        const uint64_t m = __ballot(is);
+        if (is) out[n_out + lanes_below(m)] = h[q];
+        n_out += __popcll(m);
+      }
+    } else {
+      // more candidates than slots (values tied near the bound): the
+      // selection over every value's full key, computed again
+      uint64_t t = 0;
+      for (int bit = 63; bit >= 0; --bit) {
+        const uint64_t cb = t | (1ull << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < PER_LANE; ++j) cnt += __popcll(__ballot(fkey(j) >= cb));
+        if (cnt >= k) t = cb;
+      }
+#pragma unroll
+      for (int j = 0; j < PER_LANE; ++j) {
+        const uint64_t kj = fkey(j);
+        const bool is = kj >= t;
+        const uint64_t m = __ballot(is);
+        if (is) out[n_out + lanes_below(m)] = kj;
+        n_out += __popcll(m);
+      }
+    }
+    for (int i = n_out + lane; i < k; i += kSelLanes) out[i] = 0;  // (never: a full chunk holds k values)
+    return;
+  }
+  // the lane's ordered values: element c0 + 4 (64 j + lane) + q; past vocab 0
+  uint32_t ov[PER_LANE];
+  {  // a ragged or unaligned chunk: ordered values, 0 past the vocabulary
 #pragma unroll
     for (int j = 0; j < PER_LANE; ++j) {
       const int64_t i = c0 + 4 * (64 * (j >> 2) + lane) + (j & 3);
@@ -202,7 +305,6 @@ __global__ void __launch_bounds__(kSelLanes * kSelWaves)
     if (is && at < kSelCap) sc[at] = (static_cast<uint64_t>(ov[j]) << 32) | (0xFFFFFFFFu - idx_of(j));
     total += __popcll(m);
   }
-  uint64_t* out = cand + (static_cast<int64_t>(row) * n_chunks + c) * k;
   int n_out = 0;
   if (total <= kSelLanes) {
     // the usual case, a few dozen candidates: one slot per lane
