@@ -282,6 +282,13 @@ __device__ __forceinline__ void wait_vmcnt() {
   __asm__ volatile("" ::: "memory");
 }
 
+// Wait until this wave's LDS reads (and scalar loads) have returned.
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+  __asm__ volatile("" ::: "memory");
+}
+
 // Wait until at most `ahead` tiles of ND DMAs each are outstanding (ahead <= 5).
 template <int ND>
 __device__ __forceinline__ void wait_vmcnt_tiles(int ahead) {
@@ -973,7 +980,7 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
 // P' = P * v_scale, and hands P' to the value wave (h = 1) through a
 // double-buffered LDS block; the value wave accumulates O += P' V for tile
 // t - 1 in the same step and issues every staging load of the pair (K tile
-// t + 2 with both scale groups, V tile t + 2), so the score wave never waits
+// t + 3 with both scale groups, V tile t + 2), so the score wave never waits
 // on memory counters. Every K and V byte is converted once, the two waves
 // share one SIMD (2 waves per SIMD, 256 registers each), and one workgroup
 // barrier per step orders the hand-over.
@@ -995,7 +1002,11 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
   constexpr int NK = KBYTES / 1024;          // DMA instructions per K (or V) tile
   constexpr int KSLOT = KBYTES + 128;        // K codes + 32 k-scales + 32 v-scales (fp16)
   constexpr int VSLOT = KBYTES;              // V codes
-  constexpr int SK = 3, SV = 4;              // K ring and V ring stages (V is used a step after K)
+  // K ring and V ring stages. Loads run three steps ahead: K s + 3 and V s + 2
+  // are issued at step s. K s + 3 goes where K s - 1 was (scored a step
+  // earlier); V s + 2 goes where V s - 1 was, which the value wave reads into
+  // registers just before, so V needs one stage fewer.
+  constexpr int SK = 4, SV = 3;
   constexpr int NDK = NK + 1, NDV = NK;      // DMA instructions per staged tile, always all issued
   __shared__ __attribute__((aligned(16))) char kring_all[NP][SK][KSLOT];
   __shared__ __attribute__((aligned(16))) char vring_all[NP][SV][VSLOT];
@@ -1085,27 +1096,25 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
     if (lane < 8) dma16v_at(sbase + min(t0 + 8 * (lane & 3), p.cap - 8), dst + KBYTES);
   };
   auto issue_v = [&](int t) { issue_codes(vbase, t, vring_lds + static_cast<uint32_t>((t % SV) * VSLOT)); };
-  // Issue order: K 0, V 0; K 1, V 1; then at step s: K s + 2, V s + 2.
-  // Before barrier s the value wave needs K s (issued at step s - 2) and
-  // V s - 1 (a step earlier still), so only the loads of step s - 1 may
-  // still be in flight.
-  auto stage_head = [&]() {
+  // Issue order: step s issues K s + 3, then V s + 2 (those that exist); the
+  // head stands in for steps -3 .. -1 (K 0; K 1, V 0; K 2, V 1). Before
+  // barrier s the value wave needs K s and V s - 1, both issued at step
+  // s - 3, so the loads of steps s - 2 and s - 1 may still be in flight:
+  // NDK + NDV each while both tiles exist, fewer at the end of the list.
+  auto stage_step = [&](int s) __attribute__((always_inline)) {
+    if (s + 3 < ntile) issue_k(s + 3);
+    if (s + 2 >= 0 && s + 2 < ntile) issue_v(s + 2);
+  };
+  auto stage_head = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-      if (t < ntile) {
-        issue_k(t);
-        issue_v(t);
-      }
+    for (int s = -3; s < 0; ++s) stage_step(s);
   };
   auto wait_step = [&](int s) {
-    if (s + 1 < ntile) wait_vmcnt<NDK + NDV>();
+    const int left = ntile - s;
+    if (left >= 3) wait_vmcnt<2 * (NDK + NDV)>();
+    else if (left == 2) wait_vmcnt<NDK + 2 * NDV>();
+    else if (left == 1) wait_vmcnt<NDV>();
     else wait_vmcnt<0>();
-  };
-  auto stage_step = [&](int s) {
-    if (s + 2 < ntile) {
-      issue_k(s + 2);
-      issue_v(s + 2);
-    }
   };
   // the lane group's 8 scales (keys 8g + e of tile t), as fp16 pairs; off 0:
   // k-scales, 64: v-scales
@@ -1334,11 +1343,11 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
   } else {
     // ------------------------------------------------------ value wave ----
     f32x4 o[8][RB], osum[RB];
-    // O^T += V^T P'^T for tile t from P buffer b: lane (i, g) reads V rows
-    // 8g + e, d = 8i .. 8i+7
-    auto accumulate = [&](int t, int b) {
+    // V tile t into registers: lane (i, g) reads V rows 8g + e, d = 8i ..
+    // 8i+7; the slot is free for the next DMA once these reads returned
+    uint32_t a[8][2];
+    auto load_v = [&](int t) {
       const char* sl = vring_all[pair][t % SV];
-      uint32_t a[8][2];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int r = 8 * lg + e;
@@ -1347,6 +1356,10 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
         a[e][0] = v2[0] ^ 0x80808080u;
         a[e][1] = v2[1] ^ 0x80808080u;
       }
+      wait_lgkmcnt0();
+    };
+    // O^T += V^T P'^T for the loaded tile from P buffer b
+    auto accumulate = [&](int b) {
       // V^T fragments (codes + 1152) of d-blocks 4hh .. 4hh + 3, half at a
       // time (register budget: o holds 32 RB): d-block db = 4hh + j takes
       // byte j of dword hh of keys e = 0..7
@@ -1390,8 +1403,9 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
       for (int s = 1; s <= ntile; ++s) {
         wait_step(s);  // K tile s and V tile s - 1 have landed
         __syncthreads();  // P of tile s - 1 is in buffer (s - 1) % 2
-        stage_step(s);
-        accumulate(s - 1, (s - 1) & 1);
+        load_v(s - 1);
+        stage_step(s);  // V s + 2 reuses the slot of V s - 1
+        accumulate((s - 1) & 1);
       }
       for (int s = ntile + 1; s <= nt_wg; ++s) __syncthreads();
       bool bad = false;
