@@ -396,6 +396,9 @@ GRID = [
     ("i8", 1, 0, "chain", 40, 8), ("i8", 3, 65, "random", 40, 8), ("i8", 16, 4095, "conf", 40, 8),
     ("i8", 64, 2000, "random", 40, 8), ("i8", 7, 9000, "random", 32, 4),
     ("f32", 7, 64, "binary", 4, 2), ("f32", 64, 300, "random", 8, 2), ("f32", 1, 0, "chain", 4, 2),
+    # int8 splits with exactly two tiles: a ragged last split (one partial prefix
+    # tile + one block tile) and two block tiles with no prefix at all
+    ("i8", 5, 276, "random", 40, 8), ("i8", 40, 0, "random", 40, 8),
 ]
 
 
