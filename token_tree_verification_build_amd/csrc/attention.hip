@@ -162,9 +162,48 @@ __device__ __forceinline__ float wave_sum(float x) {
 // (m = -inf marks an empty split). wt is LDS scratch for rows_chunk * n weights: per
 // row, w_s = 2^(m_s - M) / L with M = max m_s and L = sum 2^(m_s - M) l_s;
 // then out = sum_s w_s o_s.
+// Up to kMergeFast partials, every thread forms the weights of its own row
+// and loads (m, l) and its 4 output columns of all partials at once: one
+// round of loads instead of two.
+constexpr int kMergeFast = 8;
 __device__ void merge_partials(const AttnParams& p, const Work& w, int slot0, int n, float* wt, int r0, int r1,
                                int stride) {
   const int tid = threadIdx.x, nthr = blockDim.x;
+  if (n <= kMergeFast) {
+    const int D4 = p.D / 4;
+    for (int idx = tid; idx < (r1 - r0) * D4; idx += nthr) {
+      const int r = r0 + idx / D4, d4 = idx % D4;
+      float ms[kMergeFast], ls[kMergeFast];
+      f32x4 os[kMergeFast];
+      // slots past n reload partial n - 1 (no branch between the loads, so
+      // they are all in flight together) and are left out below
+#pragma unroll
+      for (int s = 0; s < kMergeFast; ++s) {
+        const size_t pr = (size_t)(slot0 + min(s, n - 1) * stride) * p.rows_chunk + r;
+        ms[s] = p.part_ml[pr * 2];
+        ls[s] = p.part_ml[pr * 2 + 1];
+        os[s] = reinterpret_cast<const f32x4*>(p.part_o + pr * p.D)[d4];
+      }
+      float M = -INFINITY;
+#pragma unroll
+      for (int s = 0; s < kMergeFast; ++s) M = fmaxf(M, ms[s]);  // the repeats change no maximum
+      float L = 0.f;
+#pragma unroll
+      for (int s = 0; s < kMergeFast; ++s) {
+        ms[s] = s >= n || ms[s] == -INFINITY ? 0.f : exp2f(ms[s] - M);  // the weight, before 1 / L
+        L += ms[s] * ls[s];
+      }
+      const float inv = 1.0f / L;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < kMergeFast; ++s) acc += (ms[s] * inv) * os[s];
+      const int row = w.row0 + r;
+      const int node = w.o0 + row / p.G;
+      const int qh = w.kvh * p.G + row % p.G;
+      reinterpret_cast<f32x4*>(p.out + ((size_t)node * p.Hq + qh) * p.D)[d4] = acc;
+    }
+    return;
+  }
   for (int r = r0 + tid; r < r1; r += nthr) {
     float M = -INFINITY;
     for (int s = 0; s < n; ++s) M = fmaxf(M, p.part_ml[((size_t)(slot0 + s * stride) * p.rows_chunk + r) * 2]);
