@@ -1187,6 +1187,9 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
   constexpr float kMargin = 2.0f;
   if (h == 0) {
     // ------------------------------------------------------ score wave ----
+    // The score wave's chain (S, exp, row sums, P') is the longer one on the
+    // shared SIMD: its instructions go first when both waves are ready.
+    __builtin_amdgcn_s_setprio(3);
     // Q^T fragments in registers: d = 32g + 8ks + e (fp16; a lane's 32 codes
     // of a K row are contiguous)
     f16x8 qf[RB][4];
