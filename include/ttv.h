@@ -231,9 +231,19 @@ ttv_status sliding_mask_from_caller(const float* caller, int32_t T, int32_t S, i
  * Supported: D in {64, 128}; F32 q requires F32 KV and vice versa (fp32 VALU
  * path); BF16 q with BF16 or I8 KV (MFMA path when D == 128 and
  * T_b * Hq/Hkv >= 16, otherwise VALU). The MFMA path forms P.V in fp16, so
- * BF16 V entries must lie within fp16 range (|v| <= 65504). Requires
- * Hq % Hkv == 0, cap >= P_b + T_b. Accuracy against float64: max-abs error
- * below 2e-3 (bf16 / int8 KV) and 1e-5 (fp32) on N(0,1) data.
+ * BF16 V entries must lie within fp16 range (|v| <= 65504). With BF16 KV the
+ * scores take Q as bf16. With I8 KV the scores take Q as fp16: the rows of
+ * one KV head (T_b * Hq/Hkv of them, in chunks of at most 80) are multiplied
+ * by one power of two that brings the chunk's largest |q| into
+ * [2^14, 2^15) -- exact for every bf16 entry within a factor 2^28 of that
+ * largest -- and the score scale takes the factor back out. The codes then
+ * enter the matrix cores as c + 1152 with the score accumulators starting at
+ * -1152 * sum_d q_d while every row of the chunk has
+ * sum_d |q_d| * softmax_scale * log2(e) <= 128; past that they are converted
+ * to c exactly and the accumulators start at zero. Requires Hq % Hkv == 0,
+ * cap >= P_b + T_b. Accuracy against float64: max-abs error below 2e-3
+ * (bf16 / int8 KV) and 1e-5 (fp32) on N(0,1) keys and values with queries
+ * N(0, s^2), s from 1e-6 to 300 (tested).
  * Concurrent calls on one GPU must not share a workspace.
  */
 size_t tree_verify_attention_ws(const ttv_batch* batch, int32_t Hq, const ttv_kv_layer* layer,
@@ -406,6 +416,9 @@ ttv_status kv_gather_positions(const ttv_kv_layer* src, const ttv_kv_layer* dst,
  * on the cache a refusal has no recovery. Returns TTV_OK when every layer can
  * be verified as a tree and rolled back by kv_gather_positions, else
  * TTV_ERR_UNSUPPORTED (or TTV_ERR_INVALID) with the reason in ttv_last_error().
+ * The gather moves rows of whole 16-byte pieces up to 4096 bytes (D * element
+ * size; e.g. f32 up to D = 1024): wider rows, or an int8 cache without its
+ * scale sidecars, are refused here and by every gather entry point.
  */
 ttv_status kv_can_gather(const ttv_kv_layer* layers, int32_t n_layers);
 

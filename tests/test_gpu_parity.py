@@ -399,6 +399,9 @@ GRID = [
     # int8 splits with exactly two tiles: a ragged last split (one partial prefix
     # tile + one block tile) and two block tiles with no prefix at all
     ("i8", 5, 276, "random", 40, 8), ("i8", 40, 0, "random", 40, 8),
+    # a wide bf16 unit whose keys split into 64 partials: the merge takes its
+    # many-partials form over 48-row chunks
+    ("bf16", 64, 16384, "random", 40, 8),
 ]
 
 
@@ -447,6 +450,73 @@ def test_attention_peaked_scores(ttv, kv):
     layer["q"] = to_bf16_bits(q)
     log(f"attention peaked {kv}")
     _attn_check(ttv, spec, {"layers": [layer]}, TOL_BF16, label=f"peaked {kv}")
+
+
+@pytest.mark.parametrize("kv", ["i8", "bf16"])
+@pytest.mark.parametrize("qscale", [1e-6, 8.0, 30.0, 300.0])
+def test_attention_query_magnitudes(ttv, kv, qscale):
+    """Queries far from unit size: N(0, s^2) for s from 1e-6 (entries below
+    fp16's normal range) to 300 (scores hundreds of log units apart, row sums
+    of |q| past the offset code conversion's bound on the int8 path). The
+    int8 path scales each row chunk's queries by a power of two into fp16
+    range and converts codes exactly once the rows' |q| sums grow; both KV
+    dtypes must stay within the tolerance of the float64 oracle."""
+    from workloads.configs import _spec
+    from workloads.gen import bf16_bits_to_f32, to_bf16_bits
+    r = rng_for(1260, int(qscale * 1000) % 997, 0 if kv == "i8" else 1)
+    T, P, Hq, Hkv, D = 16, 3000, 40, 8, 128
+    parent = confidence_tree(r, T, 8, 1000, 4)[0]
+    spec = _spec(1260, 1, 1, Hq, Hkv, D, 16, 1.0, kv, "bf16", [P], [parent], [np.zeros(T, np.int64)],
+                 [np.zeros(T, np.int64)], [[0]])
+    q = to_bf16_bits(bf16_bits_to_f32(make_queries(1261, 0, T, Hq, D, "bf16")) * np.float32(qscale))
+    layer = dict(make_kv_cache(1262, 0, 1, Hkv, P + T + 3, D, kv), q=q)
+    log(f"attention query scale {qscale} {kv}")
+    _attn_check(ttv, spec, {"layers": [layer]}, TOL_BF16, label=f"qscale {qscale} {kv}")
+
+
+def _oracle_node_rows(slab: dict, kv: str, qrows, P: int, parent, t: int, scale: float):
+    """The oracle's attention rows of one node and one KV head from that
+    head's cache slab ({'k','v'[, scales]} [P + T, D] / [P + T]): the node's
+    explicit key set, decoded keys and values, float64 softmax."""
+    keys = O.visible_keys(P, O.ancestor_sets(parent)[t])
+    K = O.decode_kv(slab["k"], kv, slab.get("k_scale"))
+    V = O.decode_kv(slab["v"], kv, slab.get("v_scale"))
+    return O.attention_rows(O.decode_bf16(qrows), K, V, keys, scale)
+
+
+@pytest.mark.parametrize("T", [64, 40])
+def test_wide_bf16_long_prefix_sampled(ttv, T):
+    """One sequence of T nodes (T * 5 = 320 or 200 query rows per KV head, the
+    wide bf16 layout) over a 131,072-token bf16 prefix: 64 key splits per
+    unit, merged in the many-partials form. Sampled (node, KV head) rows of
+    every row chunk are checked against the oracle."""
+    from workloads.device import dev_kv_cache, dev_queries
+    P, Hq, Hkv, D = 131072, 40, 8, 128
+    parent = random_tree(rng_for(1270, T), T)
+    node_off = np.array([0, T], np.int32)
+    batch = ttv.Batch(node_off, np.array([P], np.int32))
+    c = dev_kv_cache(1270, T, 1, Hkv, P + T, D, "bf16", "cuda")
+    layer = ttv.KVLayer(c["k"], c["v"])
+    q = dev_queries(1271, T, T, Hq, D, "bf16", "cuda")
+    anc, _, st = run_mask(ttv, batch, to_dev(parent))
+    out, _ = run_attention(ttv, batch, q, layer, anc, 1 / math.sqrt(D))
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    G = Hq // Hkv
+    r = rng_for(1272, T)
+    worst = 0.0
+    # nodes spread over the tree, so every row chunk of the unit is sampled; random KV heads
+    for t in sorted({0, T // 4, T // 2, (3 * T) // 4, T - 1, int(r.integers(0, T))}):
+        g = int(r.integers(0, Hkv))
+        slab = {n: to_host(c[n][0, g, :P + T]) for n in ("k", "v")}
+        qrows = to_host(q[t, g * G:(g + 1) * G])
+        want = _oracle_node_rows(slab, "bf16", qrows, P, parent, t, 1 / math.sqrt(D))
+        got = to_host(out[t, g * G:(g + 1) * G])
+        err = float(np.abs(got - want).max())
+        log(f"wide long-prefix T={T}: node {t} kv head {g}: max|err| {err:.3e}")
+        worst = max(worst, err)
+    assert worst <= TOL_BF16
+    assert np.isfinite(to_host(out)).all()
 
 
 def test_attention_ragged_batch(ttv):

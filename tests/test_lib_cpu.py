@@ -102,6 +102,35 @@ def test_attention_ws_sizes():
     assert C["tree_verify_attention_ws"](ctypes.byref(bad), 41, ctypes.byref(L), ttv.TTV_BF16) == 0
 
 
+def test_attention_planner_partial_bound():
+    """Replays the attention planner on the host over the shapes the merge
+    launch must take: every plan keeps a unit's partials within the merge
+    workgroup's weight table (the planner refuses a plan that would not, so a
+    workspace size of 0 here would mean such a refusal)."""
+    hist = [0, 1, 31, 1000, 4096, 10999, 11000, 16384, 50000, 131072]
+    n_plans = 0
+    for dt, scales in ((ttv.TTV_BF16, False), (ttv.TTV_I8, True)):
+        for B in (1, 2, 4):
+            for T in (1, 16, 20, 33, 48, 64):
+                for P in hist:
+                    L = layer(dtype=dt, scales=scales, cap=P + 64)
+                    b, keep = batch(np.arange(B + 1) * T, [P] * B)
+                    for window in (0, 1024):
+                        if window:
+                            n = C["tree_verify_attention_window_ws"](ctypes.byref(b), 40, ctypes.byref(L),
+                                                                     ttv.TTV_BF16, window)
+                        else:
+                            n = C["tree_verify_attention_ws"](ctypes.byref(b), 40, ctypes.byref(L), ttv.TTV_BF16)
+                        assert n > 0, (dt, B, T, P, window, ttv.last_error())
+                        n_plans += 1
+    # ragged batches: one long sequence among short ones
+    for dt, scales in ((ttv.TTV_BF16, False), (ttv.TTV_I8, True)):
+        L = layer(dtype=dt, scales=scales, cap=131072 + 64)
+        b, keep = batch([0, 64, 65, 105], [131072, 3, 20000])
+        assert C["tree_verify_attention_ws"](ctypes.byref(b), 40, ctypes.byref(L), ttv.TTV_BF16) > 0
+    assert n_plans == 2 * 3 * 6 * len(hist) * 2
+
+
 def test_argmax_validation():
     f = C["vocab_argmax"]
     assert f(FAKE, 4, 100, 99, FAKE, None, 0, None) == ttv.TTV_ERR_INVALID       # stride < vocab
@@ -187,6 +216,26 @@ def test_gather_validation():
     assert _gather([i8], None) == ttv.TTV_ERR_UNSUPPORTED
     # j0 and bad per sequence, plus a partial pair per validation chunk (at most 64)
     assert ttv.kv_gather_positions_ws(8) == 8 * (2 + 2 * 64) * 4
+
+
+def test_gather_refuses_rows_wider_than_one_pass():
+    """Rows over 4096 bytes are refused by the capability question and by
+    both gather entry points (in place and out of place) before anything is
+    launched; 4096-byte rows are accepted."""
+    base = 1 << 30
+    wide = ttv.TtvKvLayer(base, base + (1 << 28), None, None, ttv.TTV_F32, 2, 1040, 128)   # 4160-byte rows
+    edge = ttv.TtvKvLayer(base, base + (1 << 28), None, None, ttv.TTV_F32, 2, 1024, 128)   # 4096-byte rows
+    st, msg = ttv.kv_can_gather_raw([wide])
+    assert st == ttv.TTV_ERR_UNSUPPORTED and "4160-byte rows" in msg
+    assert ttv.kv_can_gather_raw([edge])[0] == ttv.TTV_OK
+    big8 = ttv.TtvKvLayer(base, base + (1 << 28), FAKE, FAKE, ttv.TTV_I8, 2, 4112, 128)
+    assert ttv.kv_can_gather_raw([big8])[0] == ttv.TTV_ERR_UNSUPPORTED
+    assert _gather([wide], None) == ttv.TTV_ERR_UNSUPPORTED                  # in place
+    assert "wider than the gather moves" in ttv.last_error()
+    dst = ttv.TtvKvLayer(base + (1 << 29), base + (1 << 29) + (1 << 28), None, None, ttv.TTV_F32, 2, 1040, 128)
+    assert _gather([wide], [dst]) == ttv.TTV_ERR_UNSUPPORTED                 # out of place
+    assert _tail([wide]) == ttv.TTV_ERR_UNSUPPORTED                          # tail form
+    assert "wider than the gather moves" in ttv.last_error()
 
 
 def test_sliding_mask_validation():

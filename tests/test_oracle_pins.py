@@ -764,3 +764,65 @@ def test_sliding_attention_explicit_equals_dense_band(seed, window):
     if window >= P + T:
         full = O.tree_verify_attention(q, {"k": K, "v": V}, [0, T], [P], [parent], 0.25, "f32", "f32")
         assert np.array_equal(got, full)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_sliding_band_holds_window_keys(seed):
+    """Count pin for the band edge: a window of W tokens holds W keys, the
+    query's own included. Under an all-open caller past the window, row q (at
+    position offset + q) keeps exactly min(W, offset + q + 1) columns, and
+    they are the newest ones, counted back from its own position. The
+    expected set is built by counting back, not from the band inequality, so
+    a band one key too wide or too narrow fails here."""
+    r = np.random.default_rng(840 + seed)
+    T = int(r.integers(1, 20))
+    offset = int(r.integers(0, 60))
+    W = int(r.integers(1, offset + T + 1))
+    if offset + T <= W:
+        W = max(1, offset + T - 1)
+        if offset + T <= W:
+            pytest.skip("no row past the window")
+    got = O.sliding_mask_from_caller(np.zeros((T, offset + T), np.float32), offset, W)
+    for q in range(T):
+        open_cols = [c for c in range(offset + T) if got[q, c] == 0.0]
+        assert len(open_cols) == min(W, offset + q + 1), (q, W, offset)
+        expect, pos = [], offset + q
+        while len(expect) < W and pos >= 0:
+            expect.append(pos)
+            pos -= 1
+        assert open_cols == sorted(expect)
+
+
+@pytest.mark.parametrize("window", [1, 5, 20, 63])
+def test_sliding_attention_ignores_the_key_just_past_the_window(window):
+    """Windowed attention at the band edge: node i (cache row P + i) of a chain
+    sees the W newest rows, down to P + i - W + 1. A key planted at
+    P + i - W with a huge score for node i must not move node i's output; the
+    same spike one row later (P + i - W + 1), and the planted key as seen by
+    the earlier node i - 1, must move it (so the check is not vacuous)."""
+    r = np.random.default_rng(860 + window)
+    T, P, Hq, Hkv, D = 8, 64, 2, 1, 16
+    parent = chain_tree(T)
+    K = r.standard_normal((1, Hkv, P + T, D))
+    V = r.standard_normal((1, Hkv, P + T, D))
+    q = r.standard_normal((T, Hq, D))
+    base = O.tree_verify_attention(q, {"k": K, "v": V}, [0, T], [P], [parent], 0.25, "f32", "f32", window=window)
+    for i in range(T):
+        edge = P + i - window
+        if edge < 0:
+            continue
+        for key, moves in ((edge, False), (edge + 1, True)):
+            Kp = K.copy()
+            Kp[0, 0, key] = 40.0 * q[i, 0]            # score ~ 10 |q|^2: dominates node i's row if visible
+            Vp = V.copy()
+            Vp[0, 0, key] = 25.0
+            got = O.tree_verify_attention(q, {"k": Kp, "v": Vp}, [0, T], [P], [parent], 0.25, "f32", "f32",
+                                          window=window)
+            delta = float(np.abs(got[i, 0] - base[i, 0]).max())
+            if moves:
+                assert delta > 1.0, (i, key, window, delta)
+            else:
+                assert delta == 0.0, (i, key, window, delta)
+            if not moves and i > 0 and edge > P + (i - 1) - window:
+                # the earlier node's window still holds the planted row
+                assert float(np.abs(got[i - 1] - base[i - 1]).max()) > 0.0

@@ -233,7 +233,8 @@ def tree_verify_attention_ws(batch: Batch, Hq: int, layer: KVLayer, q_dtype: str
 
 def tree_verify_attention(batch: Batch, q, layer: KVLayer, anc, softmax_scale: float, out, ws, stream=None):
     """q [n_nodes, Hq, D] float32 or bfloat16; out float32 like q; anc int64 or None (causal);
-    ws: zero-initialised uint8 device tensor of at least tree_verify_attention_ws bytes."""
+    ws: uint8 device tensor of at least tree_verify_attention_ws bytes, any contents (the call writes every
+    workspace byte it reads)."""
     import torch
     _dev(q, name="q")
     qd = {torch.float32: "f32", torch.bfloat16: "bf16"}[q.dtype]

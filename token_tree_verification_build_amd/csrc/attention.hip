@@ -157,11 +157,12 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // Merge of n partials of one unit by log-sum-exp, by the whole workgroup,
-// over rows [r0, r1) of the unit's chunk. Partials: o [slot][rows_chunk][D]
-// and (m, l) [slot][rows_chunk][2] for slots slot0 + s * stride, s < n
-// (m = -inf marks an empty split). wt is LDS scratch for rows_chunk * n weights: per
-// row, w_s = 2^(m_s - M) / L with M = max m_s and L = sum 2^(m_s - M) l_s;
-// then out = sum_s w_s o_s.
+// over rows [r0, r1) of the unit's chunk (r1 - r0 <= kMergeRows). Partials:
+// o [slot][rows_chunk][D] and (m, l) [slot][rows_chunk][2] for slots
+// slot0 + s * stride, s < n <= kMaxSplits (m = -inf marks an empty split). wt
+// is LDS scratch for (r1 - r0) * n weights, indexed by the row's place in
+// [r0, r1): per row, w_s = 2^(m_s - M) / L with M = max m_s and
+// L = sum 2^(m_s - M) l_s; then out = sum_s w_s o_s.
 // Up to kMergeFast partials, every thread forms the weights of its own row
 // and loads (m, l) and its 4 output columns of all partials at once: one
 // round of loads instead of two.
@@ -212,11 +213,11 @@ __device__ void merge_partials(const AttnParams& p, const Work& w, int slot0, in
       const size_t pr = (size_t)(slot0 + s * stride) * p.rows_chunk + r;
       const float ms = p.part_ml[pr * 2];
       const float ws = ms == -INFINITY ? 0.f : exp2f(ms - M);
-      wt[r * n + s] = ws;
+      wt[(r - r0) * n + s] = ws;
       L += ws * p.part_ml[pr * 2 + 1];
     }
     const float inv = 1.0f / L;
-    for (int s = 0; s < n; ++s) wt[r * n + s] *= inv;
+    for (int s = 0; s < n; ++s) wt[(r - r0) * n + s] *= inv;
   }
   __syncthreads();
   const int D4 = p.D / 4;
@@ -224,7 +225,7 @@ __device__ void merge_partials(const AttnParams& p, const Work& w, int slot0, in
     const int r = r0 + idx / D4, d4 = idx % D4;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < n; ++s)
-      acc += wt[r * n + s] *
+      acc += wt[(r - r0) * n + s] *
              reinterpret_cast<const f32x4*>(p.part_o + ((size_t)(slot0 + s * stride) * p.rows_chunk + r) * p.D)[d4];
     const int row = w.row0 + r;
     const int node = w.o0 + row / p.G;
@@ -238,8 +239,9 @@ __device__ void merge_partials(const AttnParams& p, const Work& w, int slot0, in
 // before these loads; an in-kernel device-scope fence would write back whole
 // L2 caches). per_slot: key splits per stored partial (4 for the MFMA path,
 // whose workgroups fold their 4 splits first; 1 for the VALU path).
-constexpr int kMergeWt = 2048;   // rows_chunk * partials per unit, at most
 constexpr int kMergeRows = 16;   // rows per merge workgroup (grid y)
+constexpr int kMergeWt = kMergeRows * kMaxSplits;  // weights of one merge workgroup, at most
+static_assert(kMergeWt * sizeof(float) <= 8192, "merge weight table");
 __global__ void __launch_bounds__(256) merge_kernel(const AttnParams p, int per_slot) {
   __shared__ float wt[kMergeWt];
   const int u = blockIdx.x;
@@ -1029,6 +1031,10 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
 // per row, and leaves O through the row sums of P' (a matrix-core product
 // with a ones operand): O -= 1152 sum_j P'_j.
 constexpr int kMaxAttempts = 8;  // passes over a split, at most (inputs with infinite scores stop there)
+// Largest row sum of |q| (times the log2 score scale) that keeps the offset
+// code conversion: its extra rounding stays below 4 * 2^-24 * 1279 * 128 *
+// k_scale ~ 4e-2 k_scale log2 units (~3e-4 |k|max), under the fp16 rounding of p.
+constexpr float kOffsetQ1Max = 128.0f;
 template <int RB>
 __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) {
   constexpr int NP = 4;                      // wave pairs = consecutive key splits of one unit
@@ -1190,10 +1196,58 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
     // The score wave's chain (S, exp, row sums, P') is the longer one on the
     // shared SIMD: its instructions go first when both waves are ready.
     __builtin_amdgcn_s_setprio(3);
+    // The queries enter the matrix cores as fp16, scaled by one power of two
+    // per row chunk that brings the chunk's largest |q| into [2^14, 2^15):
+    // every bf16 value within 2^28 of that largest converts exactly, and the
+    // factor comes back out of the score scale. The chunk's largest row sum
+    // of |q| picks the code conversion (see below).
+    float amax = 0.f, r1max = 0.f;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int rloc = rb * 16 + li;
+      const bool ok = rloc < w.nrows;
+      const int row = w.row0 + (ok ? rloc : 0);
+      const uint16_t* qrow =
+          static_cast<const uint16_t*>(p.q) + ((size_t)(w.o0 + row / p.G) * p.Hq + w.kvh * p.G + row % p.G) * D;
+      float r1 = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        u32x4 x = *reinterpret_cast<const u32x4*>(qrow + 32 * lg + 8 * ks);
+        if (!ok) x = u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float a = fabsf(__uint_as_float((e & 1) ? (x[e >> 1] & 0xFFFF0000u) : (x[e >> 1] << 16)));
+          amax = fmaxf(amax, a);
+          r1 += a;
+        }
+      }
+      r1 += __shfl_xor(r1, 16);
+      r1 += __shfl_xor(r1, 32);
+      r1max = fmaxf(r1max, r1);
+    }
+    amax = wave_max(amax);
+    r1max = wave_max(r1max);
+    int qexp = 0;
+    frexpf(amax, &qexp);
+    const int qe = __builtin_amdgcn_readfirstlane(amax > 0.f ? min(max(15 - qexp, -126), 126) : 0);
+    const float qmul = ldexpf(1.0f, qe);
+    // the score scale with the query factor taken back out (wave-uniform)
+    const float sl2 = __builtin_bit_cast(
+        float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, p.scale_log2 * ldexpf(1.0f, -qe))));
+    const bool exact_codes =
+        __builtin_amdgcn_readfirstlane((r1max * p.scale_log2 > kOffsetQ1Max || !__builtin_isfinite(r1max)) ? 1 : 0) != 0;
+    // Codes enter the matrix cores as fp16 of c + 1152 (one v_perm per pair)
+    // with the S accumulators starting at -1152 sum_d q_d, which cancels the
+    // offset; the partial sums then run up to ~1279 sum_d |q_d|, so their
+    // rounding grows with the rows' |q|. Past kOffsetQ1Max (in log2 score
+    // units) the codes are converted exactly instead (one more packed add per
+    // pair) and the accumulators start at zero.
+    auto score_wave = [&](auto exact_tag) {
+    constexpr bool EXACT = decltype(exact_tag)::value;
     // Q^T fragments in registers: d = 32g + 8ks + e (fp16; a lane's 32 codes
     // of a K row are contiguous)
     f16x8 qf[RB][4];
-    f32x4 kinit[RB];  // -1152 sum_d q_d of the lane's row: the S accumulators' start
+    f32x4 kinit[RB];  // the S accumulators' start: -1152 sum_d q_d of the lane's row, or 0 (EXACT)
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int rloc = rb * 16 + li;
@@ -1209,14 +1263,14 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
         if (!ok) x = u32x4{0, 0, 0, 0};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          qf[rb][ks][e] =
-              static_cast<_Float16>(__uint_as_float((e & 1) ? (x[e >> 1] & 0xFFFF0000u) : (x[e >> 1] << 16)));
+          qf[rb][ks][e] = static_cast<_Float16>(
+              __uint_as_float((e & 1) ? (x[e >> 1] & 0xFFFF0000u) : (x[e >> 1] << 16)) * qmul);
           qsum += static_cast<float>(qf[rb][ks][e]);
         }
       }
       qsum += __shfl_xor(qsum, 16);
       qsum += __shfl_xor(qsum, 32);
-      const float c = -kCodeBias * qsum;
+      const float c = EXACT ? 0.f : -kCodeBias * qsum;
       kinit[rb] = f32x4{c, c, c, c};
     }
     float negm[RB], tmax[RB], l[RB];  // negm: minus the references (0 for the first tile's raw scores)
@@ -1234,7 +1288,7 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
       vsc = scales(sl, t0, 64);
       float kss[8];  // score scale of key 8g + e, log2 units
 #pragma unroll
-      for (int e = 0; e < 8; ++e) kss[e] = static_cast<float>(__builtin_bit_cast(f16x8, ksc)[e]) * p.scale_log2;
+      for (int e = 0; e < 8; ++e) kss[e] = static_cast<float>(__builtin_bit_cast(f16x8, ksc)[e]) * sl2;
       // S^T = K Q^T: block kb takes tile rows 8(i/4) + 4kb + i%4
       u32x4 kraw[2][2];
 #pragma unroll
@@ -1251,7 +1305,8 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const u32x4& src = kraw[kb][ks >> 1];
-          kf[kb] = i8x8_to_f16_biased(src[2 * (ks & 1)], src[2 * (ks & 1) + 1]);
+          if constexpr (EXACT) kf[kb] = i8x8_to_f16(src[2 * (ks & 1)], src[2 * (ks & 1) + 1]);
+          else kf[kb] = i8x8_to_f16_biased(src[2 * (ks & 1)], src[2 * (ks & 1) + 1]);
         }
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
@@ -1382,6 +1437,9 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
     }
     __syncthreads();  // references visible, rings idle
     for (int step = 0; step < NP; ++step) __syncthreads();  // the value waves fold
+    };
+    if (exact_codes) score_wave(std::true_type{});
+    else score_wave(std::false_type{});
   } else {
     // ------------------------------------------------------ value wave ----
     f32x4 o[8][RB], osum[RB];
@@ -1819,6 +1877,10 @@ static ttv_status plan_attention(const ttv_batch* batch, int Hq, const ttv_kv_la
     const int ph = P - hist_key_start(P, window);
     const int ns0 = ph > 0 ? (ph + p.split_len - 1) / p.split_len : 1;
     const int ns = (ns0 + p.split_pad - 1) / p.split_pad * p.split_pad;
+    // the merge launch keeps one weight per (row, partial) of its rows in LDS
+    TTV_REQUIRE(ns / p.split_pad <= kMaxSplits, TTV_ERR_INVALID,
+                "tree_verify_attention: sequence %d would need %d partials per unit (at most %d)", b,
+                ns / p.split_pad, kMaxSplits);
     p.node_off[b] = batch->node_off_h[b];
     p.hist_len[b] = P;
     p.wg_off[b] = wg;

@@ -43,6 +43,10 @@ ttv_status check_batch(const ttv_batch* batch, bool need_device = true);
 
 // ------------------------------------------------------------ constants ----
 constexpr int kWave = 64;
+// Widest K (or V) row the gather moves: one 256-thread pass of 16-byte pieces
+// (the out-of-place take copies a row per pass; the in-place form holds at
+// least one whole row per chunk).
+constexpr int kMaxGatherRowBytes = 4096;
 constexpr int kNumXcd = 8;   // MI355X: 8 XCDs, round-robin workgroup dispatch
 
 // Remap a linear workgroup id so that consecutive logical slots land on the

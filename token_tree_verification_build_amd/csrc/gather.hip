@@ -31,6 +31,7 @@ namespace ttv {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGatherThreads = 256;
+static_assert(kMaxGatherRowBytes == 16 * kGatherThreads, "one row per pass of 16-byte pieces");
 constexpr int kLayersPerLaunch = 16;
 constexpr int kTakeRows = 512;  // rows per out-of-place workgroup
 constexpr int kMaxSelChunks = 64;     // validation workgroups per sequence, at most
@@ -252,7 +253,7 @@ __global__ void __launch_bounds__(kGatherThreads) compact_kernel(LayerPtrs L, in
   const int32_t* __restrict__ srow = sel + static_cast<int64_t>(b) * sel_stride;
   const int ts = TAIL ? tail_start[b] : 0;
   const int64_t base = (static_cast<int64_t>(b) * Hkv + h) * cap;
-  const int U = row_bytes >> 4;
+  const int U = row_bytes >> 4;  // <= kGatherThreads (kv_can_gather), so a chunk holds >= PIECES rows
   const int rows_chunk = PIECES * kGatherThreads / U < kGatherThreads ? PIECES * kGatherThreads / U : kGatherThreads;
   char* __restrict__ kp = const_cast<char*>(L.k[l]);
   char* __restrict__ vp = const_cast<char*>(L.v[l]);
@@ -414,8 +415,6 @@ extern "C" ttv_status kv_gather_positions(const ttv_kv_layer* src, const ttv_kv_
       if (chunks == 0) continue;
       const int64_t nblk = static_cast<int64_t>(nl) * B * L0.Hkv * chunks;
       TTV_REQUIRE(nblk <= 0x7FFFFFFF, TTV_ERR_INVALID, "kv_gather_positions: grid too large");
-      TTV_REQUIRE(row_bytes <= 16 * kGatherThreads, TTV_ERR_UNSUPPORTED,
-                  "kv_gather_positions: rows of %d bytes exceed one pass", row_bytes);
       hipLaunchKernelGGL(take_kernel, dim3(static_cast<unsigned>(nblk)), dim3(kGatherThreads), 0, st, P, B, L0.Hkv,
                          L0.cap, row_bytes, chunks, sel, sel_stride, sel_len, bad);
     }

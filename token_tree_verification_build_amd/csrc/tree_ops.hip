@@ -314,6 +314,9 @@ extern "C" ttv_status kv_can_gather(const ttv_kv_layer* layers, int32_t n_layers
     const int esz = L.dtype == TTV_F32 ? 4 : L.dtype == TTV_BF16 ? 2 : 1;
     TTV_REQUIRE((L.D * esz) % 16 == 0, TTV_ERR_UNSUPPORTED,
                 "layer %d: a %d-byte row is not a whole number of 16-byte chunks", l, L.D * esz);
+    TTV_REQUIRE(L.D * esz <= kMaxGatherRowBytes, TTV_ERR_UNSUPPORTED,
+                "layer %d: %d-byte rows are wider than the gather moves (at most %d bytes)", l, L.D * esz,
+                kMaxGatherRowBytes);
     if (L.dtype == TTV_I8)
       TTV_REQUIRE(L.k_scale && L.v_scale, TTV_ERR_UNSUPPORTED,
                   "layer %d: int8 cache without per-token scale sidecars; moving codes without "
