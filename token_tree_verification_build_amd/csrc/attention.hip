@@ -1894,9 +1894,12 @@ static ttv_status plan_attention(const ttv_batch* batch, int Hq, const ttv_kv_la
   p.unit_off[B] = units;
   p.nwg = wg;
   pl.nunits = units;
+  // partial slots: one per workgroup on the narrow MFMA paths (its four pairs
+  // fold their splits first), one per split (VALU) or per pair (wide)
+  const size_t nslot = pl.mfma && !pl.wide ? (size_t)wg / 4 : (size_t)wg;
   pl.off_ml = 0;
-  pl.off_o = pl.off_ml + ((size_t)wg * p.rows_chunk * 2 * 4 + 255) / 256 * 256;
-  pl.ws_bytes = pl.off_o + (size_t)wg * p.rows_chunk * p.D * 4;
+  pl.off_o = pl.off_ml + (nslot * p.rows_chunk * 2 * 4 + 255) / 256 * 256;
+  pl.ws_bytes = pl.off_o + nslot * p.rows_chunk * p.D * 4;
   return TTV_OK;
 }
 
