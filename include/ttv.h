@@ -253,6 +253,25 @@ ttv_status tree_verify_attention(const ttv_batch* batch, const void* q, int32_t 
                                  float* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * tree_verify_attention without a workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same computation and kernels, with
+ * the partials kept in a static device scratch array of the library, 32 MiB
+ * per device (TTV_STATIC_SCRATCH_BYTES), that every device running the
+ * library holds until the process ends. Its address is looked up once per
+ * device on the first call there. A call whose tree_verify_attention_ws size
+ * exceeds the scratch returns TTV_ERR_UNSUPPORTED before anything is launched.
+ * The call allocates nothing. Every call on one device uses that device's one
+ * scratch array, which keeps the last call's contents (nothing in it needs to
+ * start at zero): calls that overlap on one device, on any streams, race and
+ * must be ordered by the caller. Arguments as tree_verify_attention.
+ */
+#define TTV_STATIC_SCRATCH_BYTES (32u << 20)
+ttv_status tree_verify_attention_static(const ttv_batch* batch, const void* q, int32_t q_dtype, int32_t Hq,
+                                        const ttv_kv_layer* layer, const uint64_t* anc, float softmax_scale,
+                                        float* out, void* stream);
+
+/*
  * Sliding-window layers' form of step 2 [PR1212] the commit intersecting the
  * caller mask with the sliding band: as tree_verify_attention, with node i of
  * sequence b (cache row P_b + i) keeping only keys j > P_b + i - window, i.e.

@@ -131,6 +131,32 @@ def test_attention_planner_partial_bound():
     assert n_plans == 2 * 3 * 6 * len(hist) * 2
 
 
+def test_static_attention_refuses_beyond_its_scratch():
+    """The allocation-free attention entry point plans on the host and
+    refuses, before any device call, a call whose partials exceed its static
+    scratch; the long-context layer fits."""
+    from workloads import config4_round, config5_round
+    assert ttv.STATIC_SCRATCH_BYTES == 32 << 20
+    text = open(HEADER).read()
+    assert "#define TTV_STATIC_SCRATCH_BYTES (32u << 20)" in text
+    spec = config4_round()
+    b, keep = batch(spec.node_off, spec.hist_len)
+    L = layer(cap=int(max(spec.hist_len + np.diff(spec.node_off))))
+    assert C["tree_verify_attention_ws"](ctypes.byref(b), 40, ctypes.byref(L), ttv.TTV_BF16) > ttv.STATIC_SCRATCH_BYTES
+    st = C["tree_verify_attention_static"](ctypes.byref(b), FAKE, ttv.TTV_BF16, 40, ctypes.byref(L), None, 0.1, FAKE,
+                                           None)
+    assert st == ttv.TTV_ERR_UNSUPPORTED and "static scratch" in ttv.last_error()
+    # host validation runs first, as for the workspace form
+    bad, keep2 = batch([0, 16], [4096])
+    assert C["tree_verify_attention_static"](ctypes.byref(bad), FAKE, ttv.TTV_BF16, 42, ctypes.byref(layer()), None,
+                                             0.1, FAKE, None) == ttv.TTV_ERR_INVALID
+    spec5 = config5_round(0, [131072] * 8, "tree", L=1)
+    b5, keep5 = batch(spec5.node_off, spec5.hist_len)
+    L5 = layer(dtype=ttv.TTV_I8, scales=True, cap=131072 + 16)
+    assert 0 < C["tree_verify_attention_ws"](ctypes.byref(b5), 40, ctypes.byref(L5), ttv.TTV_BF16) <= \
+        ttv.STATIC_SCRATCH_BYTES
+
+
 def test_argmax_validation():
     f = C["vocab_argmax"]
     assert f(FAKE, 4, 100, 99, FAKE, None, 0, None) == ttv.TTV_ERR_INVALID       # stride < vocab

@@ -21,6 +21,7 @@ TTV_OK, TTV_ERR_INVALID, TTV_ERR_UNSUPPORTED, TTV_ERR_WORKSPACE, TTV_ERR_HIP = r
 TTV_DEV_OK, TTV_DEV_BAD_PARENT, TTV_DEV_BAD_SELECTION, TTV_DEV_BAD_LOGITS, TTV_DEV_DRAFT_STATE = 0, 1, 2, 3, 4
 TTV_F32, TTV_BF16, TTV_I8 = 0, 1, 2
 MAX_NODES = 64
+STATIC_SCRATCH_BYTES = 32 << 20
 MAX_BATCH = 128
 
 if not os.path.exists(LIB_PATH):
@@ -58,6 +59,8 @@ _c = {
     "tree_verify_attention_ws": _sig("tree_verify_attention_ws", _sz, [_BP, _i32, _LP, _i32]),
     "tree_verify_attention": _sig("tree_verify_attention", _i32,
                                   [_BP, _p, _i32, _i32, _LP, _p, ctypes.c_float, _p, _p, _sz, _p]),
+    "tree_verify_attention_static": _sig("tree_verify_attention_static", _i32,
+                                         [_BP, _p, _i32, _i32, _LP, _p, ctypes.c_float, _p, _p]),
     "tree_verify_attention_window_ws": _sig("tree_verify_attention_window_ws", _sz, [_BP, _i32, _LP, _i32, _i32]),
     "tree_verify_attention_window": _sig("tree_verify_attention_window", _i32,
                                          [_BP, _p, _i32, _i32, _LP, _p, ctypes.c_float, _i32, _p, _p, _sz, _p]),
@@ -245,6 +248,20 @@ def tree_verify_attention(batch: Batch, q, layer: KVLayer, anc, softmax_scale: f
     _check(_c["tree_verify_attention"](batch.ref(), _ptr(q), _DT[qd], Hq, layer.ref(), _ptr(anc), softmax_scale,
                                        _ptr(out), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)),
            "tree_verify_attention")
+
+
+def tree_verify_attention_static(batch: Batch, q, layer: KVLayer, anc, softmax_scale: float, out, stream=None):
+    """tree_verify_attention with the library's static per-device scratch in place of a workspace (allocates
+    nothing; calls that overlap on one device race). Raises TTVError (TTV_ERR_UNSUPPORTED) when the call's
+    partials exceed STATIC_SCRATCH_BYTES."""
+    import torch
+    _dev(q, name="q")
+    qd = {torch.float32: "f32", torch.bfloat16: "bf16"}[q.dtype]
+    _dev(out, torch.float32, "out")
+    _dev(anc, torch.int64, "anc")
+    _check(_c["tree_verify_attention_static"](batch.ref(), _ptr(q), _DT[qd], q.shape[1], layer.ref(), _ptr(anc),
+                                              softmax_scale, _ptr(out), _stream(stream)),
+           "tree_verify_attention_static")
 
 
 def tree_verify_attention_window_ws(batch: Batch, Hq: int, layer: KVLayer, q_dtype: str, window: int) -> int:

@@ -47,6 +47,7 @@
 #include "common.hpp"
 
 #include <climits>
+#include <mutex>
 #include <type_traits>
 
 namespace ttv {
@@ -1997,6 +1998,74 @@ extern "C" ttv_status tree_verify_attention(const ttv_batch* batch, const void* 
                                             float* out, void* ws, size_t ws_bytes, void* stream) {
   clear_error();
   return run_attention(batch, q, q_dtype, Hq, layer, anc, softmax_scale, 0, out, ws, ws_bytes, stream);
+}
+
+// ------------------------------------------------ allocation-free form ----
+// tree_verify_attention_static keeps the partials in this file-scope device
+// array instead of a caller workspace. Every device that runs the library
+// holds its own copy until the process ends. In host code the array's name
+// is only a stand-in: the per-device address comes from hipGetSymbolAddress,
+// taken once per device with that device current, and only that address is
+// passed to kernels.
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // per device: the address of its scratch copy
+}  // namespace
+
+// The scratch address on the device `stream` runs on (the current device for
+// the NULL stream); looked up on the first call for that device.
+static ttv_status static_scratch(void* stream, void** out) {
+  int cur = -1, dev = -1;
+  hipError_t e = hipGetDevice(&cur);
+  TTV_REQUIRE(e == hipSuccess, TTV_ERR_HIP, "tree_verify_attention_static: no current device: %s",
+              hipGetErrorString(e));
+  dev = cur;
+  if (stream != nullptr) {
+    e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev);
+    TTV_REQUIRE(e == hipSuccess, TTV_ERR_HIP, "tree_verify_attention_static: stream device: %s",
+                hipGetErrorString(e));
+  }
+  TTV_REQUIRE(dev >= 0 && dev < kMaxDevices, TTV_ERR_UNSUPPORTED,
+              "tree_verify_attention_static: device %d is beyond the %d devices the scratch table holds", dev,
+              kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    if (dev != cur) {
+      e = hipSetDevice(dev);
+      TTV_REQUIRE(e == hipSuccess, TTV_ERR_HIP, "tree_verify_attention_static: hipSetDevice(%d): %s", dev,
+                  hipGetErrorString(e));
+    }
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    TTV_REQUIRE(e == hipSuccess && ptr != nullptr, TTV_ERR_HIP,
+                "tree_verify_attention_static: hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return TTV_OK;
+}
+
+extern "C" ttv_status tree_verify_attention_static(const ttv_batch* batch, const void* q, int32_t q_dtype,
+                                                   int32_t Hq, const ttv_kv_layer* layer, const uint64_t* anc,
+                                                   float softmax_scale, float* out, void* stream) {
+  clear_error();
+  AttnPlan pl;
+  ttv_status s = plan_attention(batch, Hq, layer, q_dtype, pl);
+  if (s != TTV_OK) return s;
+  TTV_REQUIRE(pl.ws_bytes <= kStaticScratchBytes, TTV_ERR_UNSUPPORTED,
+              "tree_verify_attention_static: the call needs %zu bytes of partials, the static scratch holds %zu "
+              "(tree_verify_attention takes a workspace of any size)", pl.ws_bytes, kStaticScratchBytes);
+  if (pl.prm.nwg == 0) return TTV_OK;
+  void* ws = nullptr;
+  s = static_scratch(stream, &ws);
+  if (s != TTV_OK) return s;
+  return run_attention(batch, q, q_dtype, Hq, layer, anc, softmax_scale, 0, out, ws, kStaticScratchBytes, stream);
 }
 
 extern "C" ttv_status tree_verify_attention_window(const ttv_batch* batch, const void* q, int32_t q_dtype,
