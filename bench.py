@@ -42,6 +42,11 @@ def parse():
                     help="summarise two rocprofv3 --pmc counter CSVs (FETCH_SIZE run, WRITE_SIZE run) of "
                          "'bench.py --copy-calib-mib N' into HBM traffic per kernel, then exit")
     ap.add_argument("--calib-mib", type=int, default=1024, help="the --copy-calib-mib of the summarised runs")
+    ap.add_argument("--sq-summary", metavar="SQ_CSV",
+                    help="summarise a rocprofv3 --pmc counter CSV of SQ_VALU_MFMA_BUSY_CYCLES, SQ_ACTIVE_INST_VALU, "
+                         "SQ_VALU_MFMA_COEXEC_CYCLES, SQ_BUSY_CYCLES, SQ_WAIT_INST_ANY, SQ_ACTIVE_INST_LDS, "
+                         "SQ_INSTS_VALU, SQ_INSTS_MFMA and GRBM_GUI_ACTIVE into per-kernel MFMA / VALU busy "
+                         "fractions, then exit")
     return ap.parse_args()
 
 
@@ -215,6 +220,72 @@ def pmc_summary(fetch_csv: str, write_csv: str, calib_mib: int) -> None:
         print(TRAFFIC_TAG + json.dumps(rec))
 
 
+MFMA_FILE = os.path.join(ROOT, "profiles", "tree_verify_attention_mfma_busy.txt")
+MFMA_TAG = "bench-mfma: "
+N_CU, N_SIMD, N_XCD = 256, 1024, 8
+
+
+def sq_summary(csv_path: str) -> None:
+    """Per kernel (averaged over its dispatches): the clock from GRBM_GUI_ACTIVE
+    (counted on each of the 8 XCDs, so divided by 8) over the dispatch's
+    duration; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024 SIMDs);
+    VALU busy = SQ_ACTIVE_INST_VALU / (cycles x 256 CUs); co-execution =
+    SQ_VALU_MFMA_COEXEC_CYCLES / (cycles x 1024 SIMDs); instruction counts per
+    dispatch. The attention kernels' figures are tagged with the SHA-256 of
+    their source for the bench line."""
+    import csv
+    rows: dict = {}
+    for r in csv.DictReader(open(csv_path)):
+        key = (r["Kernel_Name"], r["Dispatch_Id"])
+        d = rows.setdefault(key, {"ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    per: dict = {}
+    for (name, _), d in rows.items():
+        per.setdefault(name, []).append(d)
+    print(f"{'kernel':80s} {'n':>3s} {'us':>8s} {'GHz':>5s} {'MFMA%':>6s} {'VALU%':>6s} {'coex%':>6s} "
+          f"{'VALU/disp':>10s} {'MFMA/disp':>10s}")
+    attn = None
+    for name, ds in sorted(per.items(), key=lambda kv: -sum(x["ns"] for x in kv[1])):
+        n = len(ds)
+
+        def avg(k):
+            return sum(x.get(k, 0.0) for x in ds) / n
+        ns = avg("ns")
+        cyc = avg("GRBM_GUI_ACTIVE") / N_XCD
+        if cyc <= 0 or ns <= 0:
+            continue
+        mf = 100 * avg("SQ_VALU_MFMA_BUSY_CYCLES") / (cyc * N_SIMD)
+        va = 100 * avg("SQ_ACTIVE_INST_VALU") / (cyc * N_CU)
+        co = 100 * avg("SQ_VALU_MFMA_COEXEC_CYCLES") / (cyc * N_SIMD)
+        print(f"{name[:80]:80s} {n:3d} {ns / 1e3:8.1f} {cyc / ns:5.2f} {mf:6.1f} {va:6.1f} {co:6.1f} "
+              f"{avg('SQ_INSTS_VALU'):10.3g} {avg('SQ_INSTS_MFMA'):10.3g}")
+        if ("attn_i8_split_kernel" in name or "attn_mfma_kernel" in name) and (attn is None or ns > attn[1]):
+            attn = (name, ns, mf, va, co)
+    if attn is not None:
+        print(MFMA_TAG + json.dumps({"kernel": attn[0], "mfma_busy_pct": round(attn[2], 1),
+                                     "valu_busy_pct": round(attn[3], 1), "coexec_pct": round(attn[4], 1),
+                                     "kernel_source_sha256": source_digest(ATTN_SOURCE)}))
+
+
+def recorded_mfma(workload: str):
+    """MFMA busy fraction of the dominant attention kernel recorded under
+    profiles/ for this workload, or None when the attention source has changed
+    since the counters were taken."""
+    try:
+        with open(MFMA_FILE) as f:
+            cur = None
+            for line in f:
+                if line.startswith("workload: "):
+                    cur = line[len("workload: "):].strip()
+                if line.startswith(MFMA_TAG) and cur == workload:
+                    rec = json.loads(line[len(MFMA_TAG):])
+                    if rec.get("kernel_source_sha256") == source_digest(ATTN_SOURCE):
+                        return rec
+    except OSError:
+        pass
+    return None
+
+
 def recorded_traffic():
     """Scaled HBM bytes per attention launch recorded under profiles/, or None
     when the attention source has changed since the counters were taken."""
@@ -239,6 +310,9 @@ def main():
     args = parse()
     if args.pmc_summary:
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.calib_mib)
+        return
+    if args.sq_summary:
+        sq_summary(args.sq_summary)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -77,6 +77,7 @@ struct AttnParams {
   float* out;
   float* part_o;
   float* part_ml;
+  int32_t* exact_flags;  // int8 path: per workgroup, 1 = its rows take the exact code conversion
   int B, Hq, Hkv, G, D, cap, split_len, rows_chunk, nwg, split_pad;
   int wide;  // wide layout: the row chunks of one (kv head, split) take ceil(rc_n / 4) * 4 consecutive slots
   int window;  // sliding-window layers: node i (cache row P + i) keeps keys > P + i - window; 0 = none
@@ -1036,7 +1037,13 @@ constexpr int kMaxAttempts = 8;  // passes over a split, at most (inputs with in
 // code conversion: its extra rounding stays below 4 * 2^-24 * 1279 * 128 *
 // k_scale ~ 4e-2 k_scale log2 units (~3e-4 |k|max), under the fp16 rounding of p.
 constexpr float kOffsetQ1Max = 128.0f;
-template <int RB>
+//
+// The choice between the two conversions is made per workgroup from its rows
+// and the kernel is instantiated once per choice (one instantiation holding
+// both schedules the offset loop worse): the EXACT = false launch runs every
+// workgroup whose rows keep the offset form and flags the others in
+// exact_flags; the EXACT = true launch that follows runs the flagged ones.
+template <int RB, bool EXACT>
 __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) {
   constexpr int NP = 4;                      // wave pairs = consecutive key splits of one unit
   constexpr int NW = 2 * NP;                 // waves
@@ -1062,9 +1069,13 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
   __shared__ float lref_s[NP][RB * 16];
   __shared__ int s_nt[NP];
   __shared__ int s_bad[NP];  // the value wave's row sums of P' overflowed in this pass
+  __shared__ int s_exact;    // this workgroup's rows take the exact code conversion
 
   const int wgi = xcd_slot(blockIdx.x, p.nwg / NP);
   if (wgi < 0) return;  // whole workgroup
+  if constexpr (EXACT) {
+    if (p.exact_flags[wgi] == 0) return;  // the offset launch ran it
+  }
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int pair = wave & (NP - 1);  // the pair's two waves sit on one SIMD
   const int h = wave / NP;           // 0: score wave, 1: value wave
@@ -1174,34 +1185,14 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
     return r;
   };
 
-  if (h == 1) {
-    stage_head();
-    wait_step(0);  // K tile 0 has landed: the score wave sets its references from it
-  }
-  if (lane == 0 && h == 0) s_nt[pair] = ntile;
-  __syncthreads();
-  int nt_wg = 0;
-#pragma unroll
-  for (int q = 0; q < NP; ++q) nt_wg = max(nt_wg, s_nt[q]);
-
-  // References without rescaling: set from the scores of the split's first
-  // tile (row max + kMargin) and fixed for the pass. If a probability (or its
-  // v-scaled copy) overflowed fp16, its row sum is not finite and the split
-  // runs again from zero, tracking how far the scores went past the
-  // references, and then again with references raised past them. Every row's
-  // first-tile max is finite: a row sees every key of a prefix tile and, in a
-  // block tile, the root.
-  constexpr float kMargin = 2.0f;
+  // The queries enter the matrix cores as fp16, scaled by one power of two
+  // per row chunk that brings the chunk's largest |q| into [2^14, 2^15):
+  // every bf16 value within 2^28 of that largest converts exactly, and the
+  // factor comes back out of the score scale. The chunk's largest row sum of
+  // |q| picks the code conversion (see above). The score waves take these
+  // statistics while the value waves issue the first loads.
+  float qmul = 1.0f, sl2 = p.scale_log2;
   if (h == 0) {
-    // ------------------------------------------------------ score wave ----
-    // The score wave's chain (S, exp, row sums, P') is the longer one on the
-    // shared SIMD: its instructions go first when both waves are ready.
-    __builtin_amdgcn_s_setprio(3);
-    // The queries enter the matrix cores as fp16, scaled by one power of two
-    // per row chunk that brings the chunk's largest |q| into [2^14, 2^15):
-    // every bf16 value within 2^28 of that largest converts exactly, and the
-    // factor comes back out of the score scale. The chunk's largest row sum
-    // of |q| picks the code conversion (see below).
     float amax = 0.f, r1max = 0.f;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -1231,12 +1222,43 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
     int qexp = 0;
     frexpf(amax, &qexp);
     const int qe = __builtin_amdgcn_readfirstlane(amax > 0.f ? min(max(15 - qexp, -126), 126) : 0);
-    const float qmul = ldexpf(1.0f, qe);
+    qmul = ldexpf(1.0f, qe);
     // the score scale with the query factor taken back out (wave-uniform)
-    const float sl2 = __builtin_bit_cast(
+    sl2 = __builtin_bit_cast(
         float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, p.scale_log2 * ldexpf(1.0f, -qe))));
-    const bool exact_codes =
-        __builtin_amdgcn_readfirstlane((r1max * p.scale_log2 > kOffsetQ1Max || !__builtin_isfinite(r1max)) ? 1 : 0) != 0;
+    if (pair == 0 && lane == 0) s_exact = (r1max * p.scale_log2 > kOffsetQ1Max || !__builtin_isfinite(r1max)) ? 1 : 0;
+  }
+  if (h == 1) {
+    stage_head();
+    wait_step(0);  // K tile 0 has landed: the score wave sets its references from it
+  }
+  if (lane == 0 && h == 0) s_nt[pair] = ntile;
+  __syncthreads();
+  if constexpr (!EXACT) {
+    const bool skip = s_exact != 0;
+    if (threadIdx.x == 0) p.exact_flags[wgi] = skip ? 1 : 0;
+    if (skip) {  // left to the exact launch, once this wave's loads have landed
+      if (h == 1) wait_vmcnt<0>();
+      return;
+    }
+  }
+  int nt_wg = 0;
+#pragma unroll
+  for (int q = 0; q < NP; ++q) nt_wg = max(nt_wg, s_nt[q]);
+
+  // References without rescaling: set from the scores of the split's first
+  // tile (row max + kMargin) and fixed for the pass. If a probability (or its
+  // v-scaled copy) overflowed fp16, its row sum is not finite and the split
+  // runs again from zero, tracking how far the scores went past the
+  // references, and then again with references raised past them. Every row's
+  // first-tile max is finite: a row sees every key of a prefix tile and, in a
+  // block tile, the root.
+  constexpr float kMargin = 2.0f;
+  if (h == 0) {
+    // ------------------------------------------------------ score wave ----
+    // The score wave's chain (S, exp, row sums, P') is the longer one on the
+    // shared SIMD: its instructions go first when both waves are ready.
+    __builtin_amdgcn_s_setprio(3);
     // Codes enter the matrix cores as fp16 of c + 1152 (one v_perm per pair)
     // with the S accumulators starting at -1152 sum_d q_d, which cancels the
     // offset; the partial sums then run up to ~1279 sum_d |q_d|, so their
@@ -1244,11 +1266,11 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
     // units) the codes are converted exactly instead (one more packed add per
     // pair) and the accumulators start at zero.
     auto score_wave = [&](auto exact_tag) {
-    constexpr bool EXACT = decltype(exact_tag)::value;
+    constexpr bool EXACT_CODES = decltype(exact_tag)::value;
     // Q^T fragments in registers: d = 32g + 8ks + e (fp16; a lane's 32 codes
     // of a K row are contiguous)
     f16x8 qf[RB][4];
-    f32x4 kinit[RB];  // the S accumulators' start: -1152 sum_d q_d of the lane's row, or 0 (EXACT)
+    f32x4 kinit[RB];  // the S accumulators' start: -1152 sum_d q_d of the lane's row, or 0 (exact codes)
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int rloc = rb * 16 + li;
@@ -1271,7 +1293,7 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
       }
       qsum += __shfl_xor(qsum, 16);
       qsum += __shfl_xor(qsum, 32);
-      const float c = EXACT ? 0.f : -kCodeBias * qsum;
+      const float c = EXACT_CODES ? 0.f : -kCodeBias * qsum;
       kinit[rb] = f32x4{c, c, c, c};
     }
     float negm[RB], tmax[RB], l[RB];  // negm: minus the references (0 for the first tile's raw scores)
@@ -1306,7 +1328,7 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const u32x4& src = kraw[kb][ks >> 1];
-          if constexpr (EXACT) kf[kb] = i8x8_to_f16(src[2 * (ks & 1)], src[2 * (ks & 1) + 1]);
+          if constexpr (EXACT_CODES) kf[kb] = i8x8_to_f16(src[2 * (ks & 1)], src[2 * (ks & 1) + 1]);
           else kf[kb] = i8x8_to_f16_biased(src[2 * (ks & 1)], src[2 * (ks & 1) + 1]);
         }
 #pragma unroll
@@ -1439,8 +1461,7 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
     __syncthreads();  // references visible, rings idle
     for (int step = 0; step < NP; ++step) __syncthreads();  // the value waves fold
     };
-    if (exact_codes) score_wave(std::true_type{});
-    else score_wave(std::false_type{});
+    score_wave(std::integral_constant<bool, EXACT>{});
   } else {
     // ------------------------------------------------------ value wave ----
     f32x4 o[8][RB], osum[RB];
@@ -1766,7 +1787,7 @@ struct AttnPlan {
   AttnParams prm;  // everything except pointers
   int nunits;
   bool merge;  // some unit has more than one partial
-  size_t off_ml, off_o, ws_bytes;
+  size_t off_ml, off_o, off_flags, ws_bytes;
 };
 
 static ttv_status plan_attention(const ttv_batch* batch, int Hq, const ttv_kv_layer* L, int q_dtype,
@@ -1900,7 +1921,9 @@ static ttv_status plan_attention(const ttv_batch* batch, int Hq, const ttv_kv_la
   const size_t nslot = pl.mfma && !pl.wide ? (size_t)wg / 4 : (size_t)wg;
   pl.off_ml = 0;
   pl.off_o = pl.off_ml + (nslot * p.rows_chunk * 2 * 4 + 255) / 256 * 256;
-  pl.ws_bytes = pl.off_o + nslot * p.rows_chunk * p.D * 4;
+  pl.off_flags = pl.off_o + nslot * p.rows_chunk * p.D * 4;
+  // the int8 MFMA path's per-workgroup conversion flags
+  pl.ws_bytes = pl.off_flags + (pl.mfma && L->dtype == TTV_I8 ? (size_t)wg / 4 * 4 : 0);
   return TTV_OK;
 }
 
@@ -1942,6 +1965,7 @@ static ttv_status run_attention(const ttv_batch* batch, const void* q, int32_t q
   p.out = out;
   p.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.off_ml);
   p.part_o = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.off_o);
+  p.exact_flags = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + pl.off_flags);
   p.scale_log2 = softmax_scale * kLog2e;
   const unsigned grid = static_cast<unsigned>((p.nwg + kNumXcd - 1) / kNumXcd * kNumXcd);
   const unsigned mgrid = static_cast<unsigned>((p.nwg / 4 + kNumXcd - 1) / kNumXcd * kNumXcd);
@@ -1952,7 +1976,11 @@ static ttv_status run_attention(const ttv_batch* batch, const void* q, int32_t q
   hipLaunchKernelGGL((attn_mfma_kernel<I, false, R0, R1, (I) ? 4 : 2>), dim3(mgrid), dim3(512), 0, st, p)
 #define TTV_WIDE(R0, R1) hipLaunchKernelGGL((attn_mfma_kernel<false, true, R0, R1, 3>), dim3(mgrid), dim3(512), 0, st, p)
 #define TTV_MFMA_RB(R0, R1) TTV_MFMA(false, R0, R1)
-#define TTV_SPLIT(R) hipLaunchKernelGGL((attn_i8_split_kernel<R>), dim3(mgrid), dim3(512), 0, st, p)
+#define TTV_SPLIT(R)                                                                            \
+  do {                                                                                          \
+    hipLaunchKernelGGL((attn_i8_split_kernel<R, false>), dim3(mgrid), dim3(512), 0, st, p);      \
+    hipLaunchKernelGGL((attn_i8_split_kernel<R, true>), dim3(mgrid), dim3(512), 0, st, p);       \
+  } while (0)
     if (i8) {
       switch (pl.rb) {
         case 1: TTV_SPLIT(1); break;
