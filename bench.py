@@ -261,6 +261,10 @@ def sq_summary(csv_path: str) -> None:
               f"{avg('SQ_INSTS_VALU'):10.3g} {avg('SQ_INSTS_MFMA'):10.3g}")
         if ("attn_i8_split_kernel" in name or "attn_mfma_kernel" in name) and (attn is None or ns > attn[1]):
             attn = (name, ns, mf, va, co)
+    # every counter of the two busiest kernels, per dispatch
+    for name, ds in sorted(per.items(), key=lambda kv: -sum(x["ns"] for x in kv[1]))[:2]:
+        keys = sorted(k for k in ds[0] if k != "ns")
+        print(f"  {name[:60]}: " + ", ".join(f"{k} {sum(x.get(k, 0.0) for x in ds) / len(ds):.4g}" for k in keys))
     if attn is not None:
         print(MFMA_TAG + json.dumps({"kernel": attn[0], "mfma_busy_pct": round(attn[2], 1),
                                      "valu_busy_pct": round(attn[3], 1), "coexec_pct": round(attn[4], 1),

@@ -63,7 +63,7 @@ constexpr int kI8MaxRB = 5;     // int8: both waves of a pair hold all row block
 constexpr int kValuRows = 16;   // rows per VALU workgroup
 constexpr int kTargetWG = 1024;
 constexpr int kWideTargetWG = 1024;
-constexpr int kWideMaxRB = 4;  // bf16 wide layout: row blocks per chunk (two per wave, Q in registers)
+constexpr int kWideMaxRB = 5;  // bf16 wide layout: row blocks per row chunk (one pair of waves each)
 constexpr int kMaxSplits = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -1609,6 +1609,415 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
   }
 }
 
+// bf16 KV with more than 16 * kMfmaMaxRB rows per KV head, MFMA path, by
+// phase. A workgroup is NP = 4 wave pairs taking up to 4 row chunks (of at
+// most RBMAX row blocks each) of one (sequence, KV head, key split) side by
+// side, so each K/V byte is read once for up to 4 * 80 rows; the pairs share
+// one ring of 32-key K and V tiles. The score wave of a pair holds its chunk's
+// Q^T in registers, forms S = K Q^T, the fp16 probabilities and their row sums
+// and hands P to its value wave through a double-buffered LDS block. The value
+// wave accumulates O += P V for the previous tile and issues its quarter of
+// every staging load; V is converted to fp16 once per workgroup, each value
+// wave building two of the eight d-blocks of the tile's V^T fragments. One
+// workgroup barrier per step orders the hand-overs. Both waves of a pair run
+// the variant compiled for the pair's own row-block count.
+template <int RBMAX>
+__global__ void __launch_bounds__(512) attn_bf16_split_kernel(const AttnParams p) {
+  constexpr int NP = 4;                 // wave pairs = row chunks side by side
+  constexpr int NW = 2 * NP;
+  constexpr int D = 128;
+  constexpr int RBYTES = 2 * D;         // one bf16 K (or V) row
+  constexpr int CH = RBYTES / 16;       // 16-byte chunks per row
+  constexpr int KT = 32;                // keys per tile
+  constexpr int KBYTES = KT * RBYTES;   // one K (or V) tile
+  constexpr int NK = KBYTES / 1024;     // DMA instructions per K (or V) tile
+  constexpr int NKW = NK / NP;          // ... per value wave
+  constexpr int AHEAD = 3;              // tiles staged ahead of the one in use
+  constexpr int S = AHEAD + 1;          // ring stages (K and V alike)
+  constexpr int NDS = 2 * NKW;          // DMA instructions of one value wave per step
+  __shared__ __attribute__((aligned(16))) char kring[S][KBYTES];
+  __shared__ __attribute__((aligned(16))) char vring[S][KBYTES];
+  __shared__ __attribute__((aligned(16))) u32x4 vT[2][8 * 64];  // fp16 V^T fragments, by d-block
+  __shared__ __attribute__((aligned(16))) u32x4 pbuf_all[NP][2][RBMAX * 64];
+  __shared__ uint64_t tbits_all[NP][RBMAX * 16];
+  __shared__ float mref_all[NP][RBMAX * 16];
+  __shared__ float lref_all[NP][RBMAX * 16];
+
+  // Workgroups are dealt to the XCDs round-robin in launch order: sequences
+  // of very different lengths then spread their work over every XCD (no two
+  // workgroups share K/V, so nothing is lost by leaving the XCD-contiguous map)
+  const int wgi = static_cast<int>(blockIdx.x);
+  if (wgi >= p.nwg / NP) return;  // whole workgroup
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int pair = wave & (NP - 1);  // the pair's two waves sit on one SIMD
+  const int h = wave / NP;           // 0: score wave, 1: value wave
+  const int lane = threadIdx.x & 63;
+  const int li = lane & 15;
+  const int lg = lane >> 4;
+  Work w;
+  decode(p, wgi * NP + pair, w);  // the pairs share (b, kv head, split); row chunk rc = pair's slot
+  const int nrb = (w.nrows + 15) / 16;  // <= RBMAX; 0 for a padding chunk
+  uint64_t* tbits_s = tbits_all[pair];
+  u32x4(*pbuf)[RBMAX * 64] = pbuf_all[pair];
+
+  for (int r = lane + (h ? 64 : 0); r < RBMAX * 16; r += 128)
+    tbits_s[r] = r < w.nrows ? row_bits(p, w, w.row0 + r) : 1ull;
+
+  const size_t head = (size_t)w.b * p.Hkv + w.kvh;
+  const char* kbase = static_cast<const char*>(p.k) + head * p.cap * RBYTES;
+  const char* vbase = static_cast<const char*>(p.v) + head * p.cap * RBYTES;
+  const uint32_t kring_lds = lds_u32(kring[0]);
+  const uint32_t vring_lds = lds_u32(vring[0]);
+
+  // Per-lane DMA geometry: piece j of a tile is tile row (64 j + lane) / CH,
+  // 16-byte chunk (64 j + lane) % CH of that row (swizzled); value wave q
+  // stages pieces NKW * q .. NKW * q + NKW - 1 of every K and V tile.
+  const int j0 = NKW * pair;
+  auto piece_row = [&](int j) { return (64 * j + lane) / CH; };
+  auto piece_col = [&](int j) {
+    return 16u * static_cast<uint32_t>(((64 * j + lane) % CH) ^ lds_swz<false>(piece_row(j)));
+  };
+  uint32_t koff[NKW];
+#pragma unroll
+  for (int j = 0; j < NKW; ++j) koff[j] = static_cast<uint32_t>(piece_row(j0 + j) * RBYTES) + piece_col(j0 + j);
+
+  // Tile list: prefix tiles over [k_lo, k_hi) (the last may be partial), then
+  // on the last split the block tiles over [P, P + T). Every pair has the same.
+  const int n_pref = w.k_hi > w.k_lo ? (w.k_hi - w.k_lo + KT - 1) / KT : 0;
+  const int ntile = n_pref + (w.last ? (w.T + KT - 1) / KT : 0);
+  const int n_full = w.k_hi > w.k_lo ? (w.k_hi - w.k_lo) / KT : 0;
+  auto geom = [&](int t, int& t0, int& mode, int& limit) {
+    if (t < n_pref) {
+      t0 = w.k_lo + KT * t;
+      limit = w.k_hi;
+      mode = t0 + KT <= w.k_hi ? 0 : 1;
+    } else {
+      t0 = w.P + KT * (t - n_pref);
+      limit = w.P + w.T;
+      mode = 2;
+    }
+  };
+  // this value wave's pieces of tile t of K (or V) into ring slot t % S;
+  // boundary tiles clamp every row into [t0, limit)
+  auto issue_tile = [&](const char* base, uint32_t ring_lds, int t) {
+    int t0, mode, limit;
+    geom(t, t0, mode, limit);
+    const char* src = base + (size_t)t0 * RBYTES;
+    const uint32_t dst = ring_lds + static_cast<uint32_t>((t % S) * KBYTES + 1024 * j0);
+    if (mode == 0) {
+#pragma unroll
+      for (int j = 0; j < NKW; ++j) dma16_at(src, koff[j], dst + 1024 * j);
+    } else {
+      const int lim = limit - 1 - t0;
+#pragma unroll
+      for (int j = 0; j < NKW; ++j)
+        dma16_at(src, static_cast<uint32_t>(min(piece_row(j0 + j), lim) * RBYTES) + piece_col(j0 + j),
+                 dst + 1024 * j);
+    }
+  };
+  // step s stages K and V of tile s + AHEAD; the head stands in for steps
+  // -AHEAD .. -1. Before barrier s the value waves need K s and V s (staged at
+  // step s - AHEAD): the loads of the AHEAD - 1 later steps may be in flight.
+  auto stage = [&](int s) __attribute__((always_inline)) {
+    if (s + AHEAD < ntile) {
+      issue_tile(kbase, kring_lds, s + AHEAD);
+      issue_tile(vbase, vring_lds, s + AHEAD);
+    }
+  };
+  auto stage_head = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < AHEAD; ++t)
+      if (t < ntile) {
+        issue_tile(kbase, kring_lds, t);
+        issue_tile(vbase, vring_lds, t);
+      }
+  };
+  auto wait_step = [&](int s) {
+    const int later = min(AHEAD - 1, ntile - 1 - s);  // steps after s whose tiles are staged
+    if (later >= 2) wait_vmcnt<2 * NDS>();
+    else if (later == 1) wait_vmcnt<NDS>();
+    else wait_vmcnt<0>();
+  };
+
+  if (h == 1) {
+    stage_head();
+    if (ntile > 0) wait_step(0);
+  }
+  __syncthreads();
+
+  constexpr float kMargin = 2.0f;
+  auto score_wave = [&](auto rb_count) {
+    constexpr int RB = decltype(rb_count)::value;
+    constexpr int RBA = RB > 0 ? RB : 1;
+    // Q^T fragments in registers: d = 32 ks + 8 g + e (bf16)
+    bf16x8 qf[RBA][4];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int rloc = rb * 16 + li;
+      const bool ok = rloc < w.nrows;
+      const int row = w.row0 + (ok ? rloc : 0);
+      const uint16_t* qrow =
+          static_cast<const uint16_t*>(p.q) + ((size_t)(w.o0 + row / p.G) * p.Hq + w.kvh * p.G + row % p.G) * D;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        u32x4 x = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * lg);
+        if (!ok) x = u32x4{0, 0, 0, 0};
+        qf[rb][ks] = __builtin_bit_cast(bf16x8, x);
+      }
+    }
+    float negm[RBA], tmax[RBA], l[RBA];
+    f32x4 sacc[2][RBA];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) negm[rb] = 0.f;
+    // scores of tile t: t = s * scale - m in place of the scores, boundary
+    // masks; with tracking, the running per-row max of t
+    auto scores = [&](int t, auto masked, auto track) {
+      int t0, mode, limit;
+      geom(t, t0, mode, limit);
+      const char* sl = kring[t % S];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        bf16x8 kf[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int r = 8 * (li >> 2) + 4 * kb + (li & 3);
+          kf[kb] = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(sl + r * RBYTES + 16 * ((4 * ks + lg) ^ lds_swz<false>(r))));
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+            sacc[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb], qf[rb][ks], ks == 0 ? zero : sacc[kb][rb],
+                                                                   0, 0, 0);
+          }
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sacc[e >> 2][rb][e & 3] = fmaf(sacc[e >> 2][rb][e & 3], p.scale_log2, negm[rb]);
+      if (decltype(masked)::value && mode != 0) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const uint64_t bits = mode == 2 ? tbits_s[rb * 16 + li] : ~0ull;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int key = t0 + 8 * lg + e;
+            const bool keep = key < limit && ((bits >> ((key - w.P) & 63)) & 1ull);
+            sacc[e >> 2][rb][e & 3] = keep ? sacc[e >> 2][rb][e & 3] : -INFINITY;
+          }
+        }
+      }
+      if constexpr (decltype(track)::value) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            tmax[rb] = fmaxf(fmaxf(tmax[rb], sacc[kb][rb][0]), sacc[kb][rb][1]);
+            tmax[rb] = fmaxf(fmaxf(tmax[rb], sacc[kb][rb][2]), sacc[kb][rb][3]);
+          }
+      }
+    };
+    // fp16 probabilities of the scored tile into P buffer b, and their row sums
+    auto hand_over = [&](int b) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        f16x8 pr;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pr[e] = static_cast<_Float16>(__builtin_amdgcn_exp2f(sacc[e >> 2][rb][e & 3]));
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          l[rb] = __builtin_amdgcn_fdot2(f16x2{pr[2 * k], pr[2 * k + 1]}, f16x2{1, 1}, l[rb], false);
+        pbuf[b][rb * 64 + lane] = __builtin_bit_cast(u32x4, pr);
+      }
+    };
+    auto past_refs = [&](float (&mx)[RBA]) -> bool {
+      bool past = false;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        mx[rb] = fmaxf(tmax[rb], __shfl_xor(tmax[rb], 16));
+        mx[rb] = fmaxf(mx[rb], __shfl_xor(mx[rb], 32));
+        past |= __ballot(mx[rb] > 6.0f) != 0;
+      }
+      return past;
+    };
+    if (ntile > 0) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) tmax[rb] = -INFINITY;
+      scores(0, std::true_type{}, std::true_type{});  // with negm = 0: t is the score itself
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        float mx = fmaxf(tmax[rb], __shfl_xor(tmax[rb], 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        negm[rb] = -(mx + kMargin);
+      }
+    }
+    float margin = 2.0f * kMargin;
+    for (int attempt = 0;; ++attempt) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        tmax[rb] = -INFINITY;
+        l[rb] = 0.f;
+      }
+      auto step = [&](int t, auto masked, auto track) {
+        __syncthreads();  // K tile t landed; P buffer t % 2 was read a step ago
+        scores(t, masked, track);
+        hand_over(t & 1);
+      };
+      if (attempt == 0) {
+#pragma nounroll
+        for (int t = 0; t < n_full; ++t) step(t, std::false_type{}, std::false_type{});
+#pragma nounroll
+        for (int t = n_full; t < ntile; ++t) step(t, std::true_type{}, std::false_type{});
+      } else {
+#pragma nounroll
+        for (int t = 0; t < ntile; ++t) step(t, std::true_type{}, std::true_type{});
+      }
+      __syncthreads();  // the value waves' last step
+      bool bad = false;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) bad |= !__builtin_isfinite(l[rb]);
+      float mx[RBA];
+      const bool past = attempt > 0 && RB > 0 && past_refs(mx);
+      const bool redo = __syncthreads_or(bad || past) && attempt + 1 < kMaxAttempts;
+      if (!redo) break;
+      if (attempt > 0) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          if (__ballot(mx[rb] > 6.0f) != 0) negm[rb] -= mx[rb] + margin;
+      }
+      margin += kMargin;
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      l[rb] += __shfl_xor(l[rb], 16);
+      l[rb] += __shfl_xor(l[rb], 32);
+      if (lg == 0) {
+        mref_all[pair][rb * 16 + li] = ntile > 0 ? -negm[rb] : -INFINITY;  // -inf: an empty split
+        lref_all[pair][rb * 16 + li] = l[rb];
+      }
+    }
+    __syncthreads();  // references and row sums visible
+  };
+
+  auto value_wave = [&](auto rb_count) {
+    constexpr int RB = decltype(rb_count)::value;
+    constexpr int RBA = RB > 0 ? RB : 1;
+    f32x4 o[8][RBA];
+    // V^T fragments of V tile t as fp16 into vT[t & 1]: fragment (db, lane
+    // (i, g)) holds V[8g + e][8i + db], e = 0..7. Value wave q builds the
+    // fragments of lanes g = q, i.e. keys 8 q .. 8 q + 7: its lane (i, j)
+    // reads dword j of 16-byte chunk i of each of those 8 rows (a whole row
+    // per read, free of bank conflicts) and writes d-blocks 2 j and 2 j + 1.
+    auto convert_v = [&](int t) {
+      const char* vt0 = vring[t % S];
+      f16x8 f0, f1;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 8 * pair + e;
+        const uint32_t x = *reinterpret_cast<const uint32_t*>(vt0 + r * RBYTES + 16 * (li ^ lds_swz<false>(r)) + 4 * lg);
+        f0[e] = static_cast<_Float16>(__uint_as_float(x << 16));
+        f1[e] = static_cast<_Float16>(__uint_as_float(x & 0xFFFF0000u));
+      }
+      vT[t & 1][(2 * lg) * 64 + 16 * pair + li] = __builtin_bit_cast(u32x4, f0);
+      vT[t & 1][(2 * lg + 1) * 64 + 16 * pair + li] = __builtin_bit_cast(u32x4, f1);
+    };
+    // O^T += V^T P^T for tile t from vT[t & 1] and P buffer t & 1
+    auto accumulate = [&](int t) {
+      f16x8 pw[RBA];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) pw[rb] = __builtin_bit_cast(f16x8, pbuf[t & 1][rb * 64 + lane]);
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const f16x8 vf = __builtin_bit_cast(f16x8, vT[t & 1][db * 64 + lane]);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) o[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pw[rb], o[db][rb], 0, 0, 0);
+      }
+    };
+    for (int attempt = 0;; ++attempt) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int db = 0; db < 8; ++db) o[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (attempt > 0) {
+        stage_head();
+        if (ntile > 0) wait_step(0);
+      }
+#pragma nounroll
+      for (int s = 0; s <= ntile; ++s) {
+        if (s > 0 && s < ntile) wait_step(s);  // K and V of tile s have landed (step 0 waited above)
+        __syncthreads();  // and every pair's P of tile s - 1 is in its buffer
+        stage(s);
+        if (s < ntile) convert_v(s);
+        if (s > 0) accumulate(s - 1);
+      }
+      const bool redo = __syncthreads_or(false) && attempt + 1 < kMaxAttempts;
+      if (!redo) break;
+    }
+    __syncthreads();  // the score wave's references and row sums
+    if (RB == 0) return;
+    // output rows: lane (i, g) holds d = 32 g + 8 r + db of row 16 rb + i in
+    // o[db][rb][r]; the unit's output when one split covers it, else a
+    // partial of this chunk
+    const bool whole = w.nsplit == 1;
+    const int slot = wgi * NP + pair;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int rloc = rb * 16 + li;
+      if (rloc >= w.nrows) continue;
+      const float m = mref_all[pair][rloc];
+      const float lsum = lref_all[pair][rloc];
+      float* dst;
+      float scl;
+      if (whole) {
+        const int row = w.row0 + rloc;
+        dst = p.out + ((size_t)(w.o0 + row / p.G) * p.Hq + w.kvh * p.G + row % p.G) * D;
+        scl = 1.0f / lsum;
+      } else {
+        const size_t pr = (size_t)slot * p.rows_chunk + rloc;
+        dst = p.part_o + pr * D;
+        scl = 1.0f;
+        if (lg == 0) {
+          p.part_ml[pr * 2] = m;
+          p.part_ml[pr * 2 + 1] = lsum;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        f32x4 v0, v1;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          v0[u] = o[u][rb][r] * scl;
+          v1[u] = o[4 + u][rb][r] * scl;
+        }
+        *reinterpret_cast<f32x4*>(dst + 32 * lg + 8 * r) = v0;
+        *reinterpret_cast<f32x4*>(dst + 32 * lg + 8 * r + 4) = v1;
+      }
+    }
+  };
+
+  switch (nrb) {
+#define TTV_BF16_ROLE(N)                                                            \
+  case N:                                                                           \
+    if constexpr (N <= RBMAX) {                                                     \
+      if (h == 0) score_wave(std::integral_constant<int, N>{});                     \
+      else value_wave(std::integral_constant<int, N>{});                            \
+    }                                                                               \
+    break;
+    TTV_BF16_ROLE(0)
+    TTV_BF16_ROLE(1)
+    TTV_BF16_ROLE(2)
+    TTV_BF16_ROLE(3)
+    TTV_BF16_ROLE(4)
+    default:
+      if (h == 0) score_wave(std::integral_constant<int, RBMAX>{});
+      else value_wave(std::integral_constant<int, RBMAX>{});
+      break;
+#undef TTV_BF16_ROLE
+  }
+}
+
 // ------------------------------------------------------------- VALU path ----
 
 template <int KT>
@@ -1974,7 +2383,7 @@ static ttv_status run_attention(const ttv_batch* batch, const void* q, int32_t q
   if (pl.mfma) {
 #define TTV_MFMA(I, R0, R1) \
   hipLaunchKernelGGL((attn_mfma_kernel<I, false, R0, R1, (I) ? 4 : 2>), dim3(mgrid), dim3(512), 0, st, p)
-#define TTV_WIDE(R0, R1) hipLaunchKernelGGL((attn_mfma_kernel<false, true, R0, R1, 3>), dim3(mgrid), dim3(512), 0, st, p)
+#define TTV_WIDE(R0, R1) hipLaunchKernelGGL((attn_bf16_split_kernel<kWideMaxRB>), dim3(mgrid), dim3(512), 0, st, p)
 #define TTV_MFMA_RB(R0, R1) TTV_MFMA(false, R0, R1)
 #define TTV_SPLIT(R)                                                                            \
   do {                                                                                          \
