@@ -33,6 +33,7 @@ def parse():
     ap.add_argument("--take-reps", type=int, default=3, help="timed reps of the full-window out-of-place gather")
     ap.add_argument("--no-take", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-small", action="store_true", help="skip the tiny, chain and 16-layer int8 round timings")
     ap.add_argument("--cpu-heads", type=int, default=8, help="KV heads per sampled sequence in the CPU oracle sample")
     ap.add_argument("--cpu-seqs", type=int, default=2, help="sequences in the CPU oracle sample")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -154,6 +155,136 @@ def cpu_baseline(spec, caches, qs, logits, heads: int, seqs: int):
                    f"and argmax/walk x{spec.B / seqs:.0f} to the full round"),
         "sample_seconds": round(sampled, 2),
     }
+
+
+def small_rounds(dev: str, steps: int = 100) -> dict:
+    """One verify round per step for the tiny fp32 workload, the linear chains
+    (T = 3, 4, 8) and the 16-node int8 tree over 16 layers, each timed with
+    events over `steps` rounds. The chain and int8-tree workloads fit in the
+    256 MB Infinity Cache, so every step takes the next of a rotation of
+    buffer copies that together hold at least 1 GiB; the tiny round is
+    latency-bound and reported as it is. Also the attention-only cost of a
+    chain of T = 4 and T = 8 nodes relative to T = 1 at the chain shape."""
+    import numpy as np
+    import torch
+
+    import token_tree_verification_build_amd as ttv
+    from workloads import config1_round, config2_round, config3_round, host_tensors
+    from workloads.device import dev_kv_cache, dev_planted_logits, dev_queries
+
+    def timed(fn, n):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3  # us
+
+    def round_runner(spec, layer_sets, q_sets, logit_sets):
+        """step(i): mask + attention per layer + argmax + walk + in-place
+        gather on rotation copy i % len(layer_sets)."""
+        B = spec.B
+        batch = ttv.Batch(spec.node_off, spec.hist_len, device=dev)
+        parent = torch.from_numpy(spec.flat("parents")).to(dev)
+        token = torch.from_numpy(spec.flat("tokens").astype(np.int32)).to(dev)
+        n = spec.n_nodes
+        st = torch.zeros(1, dtype=torch.int32, device=dev)
+        anc = torch.empty(n, dtype=torch.int64, device=dev)
+        out = torch.empty(n, spec.Hq, spec.D, dtype=torch.float32, device=dev)
+        ws = torch.zeros(ttv.tree_verify_attention_ws(batch, spec.Hq, layer_sets[0][0], spec.q_dtype),
+                         dtype=torch.uint8, device=dev)
+        am = torch.empty(n, dtype=torch.int32, device=dev)
+        aws = torch.zeros(max(1, ttv.vocab_argmax_ws(n, spec.vocab)), dtype=torch.uint8, device=dev)
+        path = torch.empty(B, 64, dtype=torch.int32, device=dev)
+        plen = torch.empty(B, dtype=torch.int32, device=dev)
+        emitted = torch.empty(B, 64, dtype=torch.int32, device=dev)
+        cap = int(max(spec.hist_len + np.diff(spec.node_off)))
+        sel = torch.empty(B, cap, dtype=torch.int32, device=dev)
+        sel_len = torch.empty(B, dtype=torch.int32, device=dev)
+        live = (spec.hist_len + np.diff(spec.node_off)).astype(np.int32)
+        gws = torch.zeros(ttv.kv_gather_positions_ws(B), dtype=torch.uint8, device=dev)
+        scale = 1.0 / math.sqrt(spec.D)
+
+        def step(i):
+            layers, qs, logits = layer_sets[i % len(layer_sets)], q_sets[i % len(q_sets)], logit_sets[i % len(logit_sets)]
+            ttv.tree_build_mask(batch, parent, anc, None, st)
+            for l, lay in enumerate(layers):
+                ttv.tree_verify_attention(batch, qs[l], lay, anc, scale, out, ws)
+            ttv.vocab_argmax(logits, am, aws)
+            ttv.tree_accept_walk(batch, parent, token, am, path, plen, emitted, st, sel, sel_len)
+            ttv.kv_gather_positions(layers, None, sel, sel_len, live, st, gws)
+        return step
+
+    def rotation(nbytes_per_copy):
+        return max(1, -(-(1 << 30) // max(1, nbytes_per_copy)))
+
+    res = {}
+    # tiny fp32 round (latency-bound; no rotation)
+    spec = config1_round(accepted=2)
+    tens = host_tensors(spec)
+    L0 = tens["layers"][0]
+    k = torch.from_numpy(L0["k"]).to(dev)
+    v = torch.from_numpy(L0["v"]).to(dev)
+    step = round_runner(spec, [[ttv.KVLayer(k, v)]], [[torch.from_numpy(L0["q"]).to(dev)]],
+                        [torch.from_numpy(tens["logits"]).to(dev)])
+    us = timed(step, steps)
+    res["config1"] = {"us_per_step": round(us, 2), "nodes_per_s": round(spec.n_nodes / us * 1e6, 1),
+                      "nodes": spec.n_nodes, "rotation_copies": 1,
+                      "what": "7-node fp32 tree, 4/2 heads, D 64, prefix 64, vocab 1024"}
+    # linear chains over a 2048-token bf16 prefix, and the chain-shape attention cost ratios
+    attn_us = {}
+    for T in (1, 3, 4, 8):
+        spec = config2_round(T, T // 2)
+        cap = int(spec.hist_len[0]) + T
+        c = dev_kv_cache(spec.seed, 100, 1, spec.Hkv, cap, spec.D, "bf16", dev)
+        per_copy = 2 * c["k"].numel() * 2 + T * spec.vocab * 4
+        nrot = rotation(per_copy)
+        kvs = [(c["k"].clone(), c["v"].clone()) for _ in range(nrot)]
+        layer_sets = [[ttv.KVLayer(a, b)] for a, b in kvs]
+        q = dev_queries(spec.seed, 200, T, spec.Hq, spec.D, "bf16", dev)
+        logits = dev_planted_logits(spec.seed, spec.flat_targets, spec.vocab, spec.sigma, dev)
+        logit_sets = [logits.clone() for _ in range(nrot)]
+        if T > 1:
+            step = round_runner(spec, layer_sets, [[q]], logit_sets)
+            us = timed(step, max(steps, 2 * nrot))
+            res[f"config2_T{T}"] = {"us_per_step": round(us, 2), "nodes_per_s": round(T / us * 1e6, 1), "nodes": T,
+                                    "rotation_copies": nrot, "rotated_bytes": nrot * per_copy,
+                                    "what": f"chain of {T} nodes, bf16, 40/8 heads, prefix 2048, vocab 248320"}
+        batch = ttv.Batch(spec.node_off, spec.hist_len, device=dev)
+        out = torch.empty(T, spec.Hq, spec.D, dtype=torch.float32, device=dev)
+        ws = torch.zeros(max(1, ttv.tree_verify_attention_ws(batch, spec.Hq, layer_sets[0][0], "bf16")),
+                         dtype=torch.uint8, device=dev)
+        attn_us[T] = timed(lambda i: ttv.tree_verify_attention(batch, q, layer_sets[i % nrot][0], None,
+                                                               1 / math.sqrt(spec.D), out, ws), max(steps, 2 * nrot))
+        del kvs, layer_sets, logit_sets
+    res["verify_cost_ratio"] = {
+        "attention_us": {f"T{T}": round(u, 2) for T, u in attn_us.items()},
+        "T4_over_T1": round(attn_us[4] / attn_us[1], 3), "T8_over_T1": round(attn_us[8] / attn_us[1], 3),
+        "context_pages": {"T4_over_T1": 1.29, "T8_over_T1": 2.48, "what": "whole verify forward, Apple M5 Max, "
+                          "4-bit 27B target: context only, not a like-for-like comparison"},
+        "what": "attention only (causal chain), bf16 KV, 40/8 heads, prefix 2048, rotated over >= 1 GiB"}
+    # 16-node int8 tree over 16 layers
+    spec = config3_round()
+    cap = int(spec.hist_len[0]) + spec.n_nodes
+    base = [dev_kv_cache(spec.seed, 100 + l, 1, spec.Hkv, cap, spec.D, "i8", dev) for l in range(spec.L)]
+    per_copy = sum(t.numel() * t.element_size() for c in base for t in c.values()) + spec.n_nodes * spec.vocab * 4
+    nrot = rotation(per_copy)
+    copies = [[{n: t.clone() for n, t in c.items()} for c in base] for _ in range(nrot)]
+    layer_sets = [[ttv.KVLayer(c["k"], c["v"], c["k_scale"], c["v_scale"]) for c in cp] for cp in copies]
+    qs = [dev_queries(spec.seed, 200 + l, spec.n_nodes, spec.Hq, spec.D, "bf16", dev) for l in range(spec.L)]
+    logits = dev_planted_logits(spec.seed, spec.flat_targets, spec.vocab, spec.sigma, dev)
+    step = round_runner(spec, layer_sets, [qs], [logits.clone() for _ in range(nrot)])
+    us = timed(step, max(steps, 2 * nrot))
+    res["config3"] = {"us_per_step": round(us, 2), "nodes_per_s": round(spec.n_nodes / us * 1e6, 1),
+                      "nodes": spec.n_nodes, "rotation_copies": nrot, "rotated_bytes": nrot * per_copy,
+                      "what": "16-node int8 tree, 16 layers, 40/8 heads, prefix 4096, vocab 248320"}
+    del copies, layer_sets, base
+    torch.cuda.empty_cache()
+    return res
 
 
 ATTN_SOURCE = os.path.join(ROOT, "token_tree_verification_build_amd", "csrc", "attention.hip")
@@ -576,6 +707,35 @@ def main():
         }
         print(f"[bench] full-window take {take_ms:.3f} ms ({kernels['kv_gather_positions_take']['GBps']} GB/s)",
               file=sys.stderr, flush=True)
+        # the same take of a 50%-scattered selection: half of every sequence's
+        # live rows, chosen at random (seeded), in increasing order
+        rng = np.random.default_rng(17)
+        half = torch.empty(B, cap, dtype=torch.int32, device=dev)
+        half_len = np.zeros(B, np.int32)
+        for b in range(B):
+            keep = np.sort(rng.choice(int(live[b]), size=int(live[b]) // 2, replace=False)).astype(np.int32)
+            half[b, :len(keep)] = torch.from_numpy(keep).to(dev)
+            half_len[b] = len(keep)
+        half_len_d = torch.from_numpy(half_len).to(dev)
+        ttv.kv_gather_positions(layers, dst_layers, half, half_len_d, live, st, gws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.take_reps):
+            ttv.kv_gather_positions(layers, dst_layers, half, half_len_d, live, st, gws)
+        e1.record()
+        torch.cuda.synchronize()
+        half_ms = e0.elapsed_time(e1) / args.take_reps
+        hrows = int(half_len.sum())
+        hbytes = 2 * hrows * spec.Hkv * kv_row_bytes(spec) * L + hrows * 4 * 2
+        kernels["kv_gather_positions_take_scatter50"] = {
+            "avg_us": round(half_ms * 1e3, 1), "bytes": hbytes, "GBps": round(hbytes / (half_ms / 1e3) / 1e9, 1),
+            "frac_hbm": round(hbytes / (half_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "what": "out-of-place take of a random half of every sequence's live rows, all layers",
+        }
+        print(f"[bench] 50%-scattered take {half_ms:.3f} ms "
+              f"({kernels['kv_gather_positions_take_scatter50']['GBps']} GB/s)", file=sys.stderr, flush=True)
+        del half
         del dst_caches, dst_layers
         # the practically reachable ceiling for a read+write stream: a plain
         # device copy of 4 GiB (torch's copy kernel), bytes read + written
@@ -599,6 +759,41 @@ def main():
         print(f"[bench] plain copy {kernels['plain_copy_4GiB']['GBps']} GB/s", file=sys.stderr, flush=True)
         del a, b2
     assert int(st.item()) == 0, "device status"
+
+    # the in-place rollback of the timed step on its own: the rows it moves
+    # (every row from the first non-identity selection entry on, all layers
+    # and heads, read and written) and its time
+    ttv.kv_gather_positions(layers, None, sel, sel_len, live, st, gws)
+    torch.cuda.synchronize()
+    pl_h, ph_h = plen.cpu().numpy(), path.cpu().numpy()
+    moved_rows = 0
+    for b in range(B):
+        pth = ph_h[b, :pl_h[b]]
+        j0 = next((k for k in range(len(pth)) if pth[k] != k), len(pth))
+        moved_rows += len(pth) - j0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        ttv.kv_gather_positions(layers, None, sel, sel_len, live, st, gws)
+    e1.record()
+    torch.cuda.synchronize()
+    kernels["kv_gather_positions_rollback"] = {
+        "avg_us": round(e0.elapsed_time(e1) / 20 * 1e3, 2),
+        "bytes_moved": 2 * moved_rows * spec.Hkv * kv_row_bytes(spec) * L,
+        "rows_moved_per_layer_and_head": moved_rows,
+        "what": "in-place rollback of the timed round (validate + finalize + compact launches), all layers",
+    }
+
+    small = None
+    if not args.no_small:
+        print("[bench] timing the tiny, chain and 16-layer int8 rounds", file=sys.stderr, flush=True)
+        small = small_rounds(dev)
+        for k, r in small.items():
+            if "us_per_step" in r:
+                print(f"[bench] {k}: {r['us_per_step']} us/step, {r['nodes_per_s']} nodes/s", file=sys.stderr,
+                      flush=True)
+        print(f"[bench] attention T4/T1 {small['verify_cost_ratio']['T4_over_T1']}, "
+              f"T8/T1 {small['verify_cost_ratio']['T8_over_T1']}", file=sys.stderr, flush=True)
 
     if args.copy_calib_mib > 0:
         a = torch.ones(args.copy_calib_mib << 20, dtype=torch.uint8, device=dev)
@@ -638,6 +833,7 @@ def main():
                      "kernel": "tree_verify_attention"},
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "other_rounds": small,
     }
     print(json.dumps(res), flush=True)
 

@@ -229,8 +229,8 @@ ttv_status sliding_mask_from_caller(const float* caller, int32_t T, int32_t S, i
  *                    workgroups, merged by a second kernel the call enqueues.
  *                    Any contents on entry (every byte read is written first).
  * Supported: D in {64, 128}; F32 q requires F32 KV and vice versa (fp32 VALU
- * path); BF16 q with BF16 or I8 KV (MFMA path when D == 128 and
- * T_b * Hq/Hkv >= 16, otherwise VALU). The MFMA path forms P.V in fp16, so
+ * path); BF16 q with BF16 or I8 KV (MFMA path when D == 128 and cap >= 32,
+ * otherwise VALU). The MFMA path forms P.V in fp16, so
  * BF16 V entries must lie within fp16 range (|v| <= 65504). With BF16 KV the
  * scores take Q as bf16. With I8 KV the scores take Q as fp16: the rows of
  * one KV head (T_b * Hq/Hkv of them, in chunks of at most 80) are multiplied

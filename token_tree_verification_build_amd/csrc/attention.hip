@@ -2230,8 +2230,10 @@ static ttv_status plan_attention(const ttv_batch* batch, int Hq, const ttv_kv_la
     maxP = ph > maxP ? ph : maxP;
   }
   // the window's band runs on the VALU path (its per-row lower bound is one
-  // compare per key there)
-  pl.mfma = bf && L->D == 128 && max_rows >= 16 && L->cap >= 32 && window == 0;
+  // compare per key there); fewer than 16 rows still take the matrix cores,
+  // with the block's missing rows as zero queries: the VALU kernel's one wave
+  // per 16 rows and split would leave most of the chip idle
+  pl.mfma = bf && L->D == 128 && max_rows >= 1 && L->cap >= 32 && window == 0;
   pl.wide = pl.mfma && L->dtype != TTV_I8 && max_rows > 16 * kMfmaMaxRB;
   if (pl.wide) {
     // up to four balanced chunks of at most 80 rows side by side (more rows
