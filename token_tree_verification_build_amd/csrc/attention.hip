@@ -1732,9 +1732,12 @@ __global__ void __launch_bounds__(512) attn_bf16_split_kernel(const AttnParams p
         issue_tile(vbase, vring_lds, t);
       }
   };
+  static_assert(AHEAD >= 1 && AHEAD <= 5, "wait_step covers up to four later steps");
   auto wait_step = [&](int s) {
     const int later = min(AHEAD - 1, ntile - 1 - s);  // steps after s whose tiles are staged
-    if (later >= 2) wait_vmcnt<2 * NDS>();
+    if (later >= 4) wait_vmcnt<4 * NDS>();
+    else if (later == 3) wait_vmcnt<3 * NDS>();
+    else if (later == 2) wait_vmcnt<2 * NDS>();
     else if (later == 1) wait_vmcnt<NDS>();
     else wait_vmcnt<0>();
   };
