@@ -158,77 +158,76 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// Merge of n partials of one unit by log-sum-exp, by the whole workgroup,
-// over rows [r0, r1) of the unit's chunk (r1 - r0 <= kMergeRows). Partials:
-// o [slot][rows_chunk][D] and (m, l) [slot][rows_chunk][2] for slots
-// slot0 + s * stride, s < n <= kMaxSplits (m = -inf marks an empty split). wt
-// is LDS scratch for (r1 - r0) * n weights, indexed by the row's place in
-// [r0, r1): per row, w_s = 2^(m_s - M) / L with M = max m_s and
-// L = sum 2^(m_s - M) l_s; then out = sum_s w_s o_s.
-// Up to kMergeFast partials, every thread forms the weights of its own row
-// and loads (m, l) and its 4 output columns of all partials at once: one
-// round of loads instead of two.
-constexpr int kMergeFast = 8;
+// Merge of n partials of one unit by log-sum-exp, by the whole workgroup of
+// kMergeThreads, over rows [r0, r1) of the unit's chunk (r1 - r0 <=
+// kMergeRows). Partials: o [slot][rows_chunk][D] and (m, l)
+// [slot][rows_chunk][2] for slots slot0 + s * stride, s < n <= kMaxSplits
+// (m = -inf marks an empty split). First the weights: the 8 lanes of row r
+// take partials j, j + 8, ... of it, and with M = max m_s and
+// L = sum 2^(m_s - M) l_s write w_s = 2^(m_s - M) / L into wt (LDS, by the
+// row's place in [r0, r1)); then out = sum_s w_s o_s, every thread with the
+// loads of 8 partials of its output in flight at once.
+constexpr int kMergeRows = 16;                     // rows per merge workgroup (grid y)
+constexpr int kMergeThreads = 8 * kMergeRows;      // 8 lanes per row for the weights
+constexpr int kMergeWt = kMergeRows * kMaxSplits;  // weights of one merge workgroup, at most
+static_assert(kMergeWt * sizeof(float) <= 8192, "merge weight table");
 __device__ void merge_partials(const AttnParams& p, const Work& w, int slot0, int n, float* wt, int r0, int r1,
                                int stride) {
-  const int tid = threadIdx.x, nthr = blockDim.x;
-  if (n <= kMergeFast) {
-    const int D4 = p.D / 4;
-    for (int idx = tid; idx < (r1 - r0) * D4; idx += nthr) {
-      const int r = r0 + idx / D4, d4 = idx % D4;
-      float ms[kMergeFast], ls[kMergeFast];
-      f32x4 os[kMergeFast];
-      // slots past n reload partial n - 1 (no branch between the loads, so
-      // they are all in flight together) and are left out below
-#pragma unroll
-      for (int s = 0; s < kMergeFast; ++s) {
-        const size_t pr = (size_t)(slot0 + min(s, n - 1) * stride) * p.rows_chunk + r;
-        ms[s] = p.part_ml[pr * 2];
-        ls[s] = p.part_ml[pr * 2 + 1];
-        os[s] = reinterpret_cast<const f32x4*>(p.part_o + pr * p.D)[d4];
-      }
-      float M = -INFINITY;
-#pragma unroll
-      for (int s = 0; s < kMergeFast; ++s) M = fmaxf(M, ms[s]);  // the repeats change no maximum
-      float L = 0.f;
-#pragma unroll
-      for (int s = 0; s < kMergeFast; ++s) {
-        ms[s] = s >= n || ms[s] == -INFINITY ? 0.f : exp2f(ms[s] - M);  // the weight, before 1 / L
-        L += ms[s] * ls[s];
-      }
-      const float inv = 1.0f / L;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < kMergeFast; ++s) acc += (ms[s] * inv) * os[s];
-      const int row = w.row0 + r;
-      const int node = w.o0 + row / p.G;
-      const int qh = w.kvh * p.G + row % p.G;
-      reinterpret_cast<f32x4*>(p.out + ((size_t)node * p.Hq + qh) * p.D)[d4] = acc;
-    }
-    return;
-  }
-  for (int r = r0 + tid; r < r1; r += nthr) {
+  const int tid = threadIdx.x;
+  {
+    const int r = r0 + (tid >> 3), j = tid & 7;
+    const bool live = r < r1;
+    constexpr int C = kMaxSplits / 8;
+    float ms[C], ls[C];
     float M = -INFINITY;
-    for (int s = 0; s < n; ++s) M = fmaxf(M, p.part_ml[((size_t)(slot0 + s * stride) * p.rows_chunk + r) * 2]);
-    float L = 0.f;
-    for (int s = 0; s < n; ++s) {
-      const size_t pr = (size_t)(slot0 + s * stride) * p.rows_chunk + r;
-      const float ms = p.part_ml[pr * 2];
-      const float ws = ms == -INFINITY ? 0.f : exp2f(ms - M);
-      wt[(r - r0) * n + s] = ws;
-      L += ws * p.part_ml[pr * 2 + 1];
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int sidx = j + 8 * c;
+      ms[c] = -INFINITY;
+      ls[c] = 0.f;
+      if (live && sidx < n) {
+        const size_t pr = (size_t)(slot0 + sidx * stride) * p.rows_chunk + r;
+        ms[c] = p.part_ml[pr * 2];
+        ls[c] = p.part_ml[pr * 2 + 1];
+      }
+      M = fmaxf(M, ms[c]);
     }
+    M = fmaxf(M, __shfl_xor(M, 1));
+    M = fmaxf(M, __shfl_xor(M, 2));
+    M = fmaxf(M, __shfl_xor(M, 4));
+    float L = 0.f;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      ms[c] = ms[c] == -INFINITY ? 0.f : exp2f(ms[c] - M);  // the weight, before 1 / L
+      L += ms[c] * ls[c];
+    }
+    L += __shfl_xor(L, 1);
+    L += __shfl_xor(L, 2);
+    L += __shfl_xor(L, 4);
     const float inv = 1.0f / L;
-    for (int s = 0; s < n; ++s) wt[(r - r0) * n + s] *= inv;
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+      if (live && j + 8 * c < n) wt[(r - r0) * kMaxSplits + j + 8 * c] = ms[c] * inv;
   }
   __syncthreads();
   const int D4 = p.D / 4;
-  for (int idx = tid; idx < (r1 - r0) * D4; idx += nthr) {
-    const int r = r0 + idx / D4, d4 = idx % D4;
+  for (int idx = tid; idx < (r1 - r0) * D4; idx += kMergeThreads) {
+    const int rl = idx / D4, d4 = idx % D4;
+    const int r = r0 + rl;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < n; ++s)
-      acc += wt[(r - r0) * n + s] *
-             reinterpret_cast<const f32x4*>(p.part_o + ((size_t)(slot0 + s * stride) * p.rows_chunk + r) * p.D)[d4];
+    for (int s0 = 0; s0 < n; s0 += 8) {
+      f32x4 os[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        os[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (s0 + k < n)
+          os[k] = reinterpret_cast<const f32x4*>(p.part_o + ((size_t)(slot0 + (s0 + k) * stride) * p.rows_chunk + r) *
+                                                 p.D)[d4];
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (s0 + k < n) acc += wt[rl * kMaxSplits + s0 + k] * os[k];
+    }
     const int row = w.row0 + r;
     const int node = w.o0 + row / p.G;
     const int qh = w.kvh * p.G + row % p.G;
@@ -241,10 +240,7 @@ __device__ void merge_partials(const AttnParams& p, const Work& w, int slot0, in
 // before these loads; an in-kernel device-scope fence would write back whole
 // L2 caches). per_slot: key splits per stored partial (4 for the MFMA path,
 // whose workgroups fold their 4 splits first; 1 for the VALU path).
-constexpr int kMergeRows = 16;   // rows per merge workgroup (grid y)
-constexpr int kMergeWt = kMergeRows * kMaxSplits;  // weights of one merge workgroup, at most
-static_assert(kMergeWt * sizeof(float) <= 8192, "merge weight table");
-__global__ void __launch_bounds__(256) merge_kernel(const AttnParams p, int per_slot) {
+__global__ void __launch_bounds__(kMergeThreads) merge_kernel(const AttnParams p, int per_slot) {
   __shared__ float wt[kMergeWt];
   const int u = blockIdx.x;
   int lo = 0, hi = p.B;  // unit_off[lo] <= u < unit_off[lo + 1]
@@ -2431,7 +2427,7 @@ static ttv_status run_attention(const ttv_batch* batch, const void* q, int32_t q
   if (s != TTV_OK || !pl.merge) return s;
   hipLaunchKernelGGL(merge_kernel,
                      dim3(static_cast<unsigned>(pl.nunits), static_cast<unsigned>((p.rows_chunk + kMergeRows - 1) / kMergeRows)),
-                     dim3(128), 0, st, p, pl.mfma && !pl.wide ? 4 : 1);
+                     dim3(kMergeThreads), 0, st, p, pl.mfma && !pl.wide ? 4 : 1);
   return check_launch("tree_verify_attention merge");
 }
 
