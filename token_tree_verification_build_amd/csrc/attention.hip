@@ -378,36 +378,25 @@ __device__ __forceinline__ void dma16v(const void* g, const void* lds) { dma16v_
 // of one unit, and the two waves of a pair split the unit's row chunk (RB0
 // row blocks of 16 rows, then RB1) and share one LDS ring, each staging half
 // of every tile. 512 threads at 2 waves per SIMD: 256 registers per wave.
-// WIDE (bf16): the pairs take 4 row chunks of one (kv head, key split)
-// instead and all eight waves share one ring, each staging an eighth of every
-// tile, so a K/V byte is read once for up to 4 * 96 rows.
-template <bool I8, bool WIDE, int RB0, int RB1, int S>
-__global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
-  static_assert(!(I8 && WIDE), "the wide layout is bf16 only");
-  constexpr int NP = 4;                       // wave pairs = consecutive key splits (WIDE: row chunks)
+// (bf16 KV with at most 96 rows per KV head; int8 KV and wider bf16 chunks
+// take the kernels split by phase below.)
+template <int RB0, int RB1, int S>
+__global__ void __launch_bounds__(512) attn_bf16_narrow_kernel(const AttnParams p) {
+  constexpr int NP = 4;                       // wave pairs = consecutive key splits
   constexpr int NW = 2 * NP;                  // waves
   constexpr int RBU = RB0 + RB1;              // row blocks of the unit's row chunk
   constexpr int D = 128;
-  constexpr int RBYTES = I8 ? D : 2 * D;      // bytes of one K (or V) row
+  constexpr int RBYTES = 2 * D;               // bytes of one K (or V) row
   constexpr int CH = RBYTES / 16;             // 16-byte chunks per row
   constexpr int KT = 32;                      // keys per tile
   constexpr int KBYTES = KT * RBYTES;         // one K (or V) tile
   constexpr int NK = KBYTES / 1024;           // DMA instructions per K (or V) tile
-  constexpr int SC_OFF = 2 * KBYTES;          // int8: 32 k-scales then 32 v-scales
-  constexpr int TILE = 2 * KBYTES + (I8 ? 128 : 0);
-  constexpr int NDK = WIDE ? NK / 4 : NK + (I8 ? 1 : 0);  // DMA instructions per tile of the K half (h = 0)
-  constexpr int NDV = WIDE ? NK / 4 : NK;     // ... and of the V half (h = 1), always all issued
-  constexpr int NR = WIDE ? 1 : NP;           // rings
-  constexpr int NQ = WIDE ? NP : 1;           // row chunks with their own Q fragments
-  typedef typename std::conditional<I8, f16x8, bf16x8>::type qk_t;  // QK operand type
+  constexpr int TILE = 2 * KBYTES;            // K tile, then V tile
   // per pair: an S-stage ring of K/V tiles; per workgroup: the unit's Q^T
   // fragments (one conflict-free 16-byte read per use) and ancestor bitsets
-  __shared__ __attribute__((aligned(16))) char ring_all[NR][S][TILE];
-  __shared__ __attribute__((aligned(16))) u32x4 qsh_all[NQ][WIDE ? 1 : RBU * 4 * 64];  // WIDE: Q in registers
-  __shared__ uint64_t tbits_all[NQ][RBU * 16];
-  // WIDE: V^T fragments of a tile as fp16, converted once for all waves
-  // (double-buffered: tile t is converted in step t and used in step t + 1)
-  __shared__ __attribute__((aligned(16))) u32x4 vT[WIDE ? 2 : 1][WIDE ? 8 * 64 : 1];
+  __shared__ __attribute__((aligned(16))) char ring_all[NP][S][TILE];
+  __shared__ __attribute__((aligned(16))) u32x4 qsh[RBU * 4 * 64];
+  __shared__ uint64_t tbits_s[RBU * 16];
   __shared__ int s_nt[NP];
 
   const int wgi = xcd_slot(blockIdx.x, p.nwg / NP);
@@ -421,64 +410,26 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
   const int li = lane & 15;
   const int lg = lane >> 4;
   Work w;
-  decode(p, wgi * NP + pair, w);  // the pairs share (b, kv head, row chunk); WIDE: (b, kv head, split)
-  char (*ring)[TILE] = ring_all[WIDE ? 0 : pair];
-  u32x4* qsh = qsh_all[WIDE ? pair : 0];
-  uint64_t* tbits_s = tbits_all[WIDE ? pair : 0];
+  decode(p, wgi * NP + pair, w);  // the pairs share (b, kv head, row chunk)
+  char (*ring)[TILE] = ring_all[pair];
 
-  // WIDE: the pair's row blocks, the first half (rounded up) on wave 0
-  const int nrb_pair = (w.nrows + 15) / 16;  // <= RB0 + RB1
-  const int nrb_w = h == 0 ? (nrb_pair + 1) / 2 : nrb_pair / 2;
-  const int rb0_w = h == 0 ? 0 : (nrb_pair + 1) / 2;
-  // WIDE: this wave's Q^T fragments in registers (d = 32ks + 8g + e)
-  bf16x8 qreg[WIDE ? RB0 : 1][4];
-  if constexpr (WIDE) {
-    static_assert(RB0 == RB1, "wide: equal halves");
-#pragma unroll
-    for (int rb = 0; rb < RB0; ++rb) {
-      const int rloc = (rb0_w + rb) * 16 + li;
-      const bool ok = rb < nrb_w && rloc < w.nrows;
-      const int row = ok ? w.row0 + rloc : 0;
-      const int node = w.o0 + row / p.G;
-      const int qh = w.kvh * p.G + row % p.G;
-      const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + ((size_t)node * p.Hq + qh) * D;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        u32x4 x = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * lg);
-        if (!ok) x = u32x4{0, 0, 0, 0};
-        qreg[rb][ks] = __builtin_bit_cast(bf16x8, x);
-      }
-    }
-  }
   // Q^T fragments into LDS. k-slot mapping of the QK product (shared by K and
-  // Q): bf16 KV d = 32ks + 8g + e (bf16 operands); int8 KV d = 32g + 8ks + e
-  // (fp16 operands, so a lane's 32 int8 codes are contiguous).
-  for (int f = wave; f < (WIDE ? 0 : RBU * 4); f += NW) {
+  // Q): d = 32ks + 8g + e.
+  for (int f = wave; f < RBU * 4; f += NW) {
     const int rb = f >> 2, ks = f & 3;
     const int rloc = rb * 16 + li;
     const bool ok = rloc < w.nrows;
-    const int row = ok ? w.row0 + rloc : 0;  // a padding chunk (WIDE) reads row 0
+    const int row = ok ? w.row0 + rloc : 0;
     const int node = w.o0 + row / p.G;
     const int qh = w.kvh * p.G + row % p.G;
     const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + ((size_t)node * p.Hq + qh) * D;
-    const int d0 = I8 ? 32 * lg + 8 * ks : 32 * ks + 8 * lg;
-    u32x4 x = *reinterpret_cast<const u32x4*>(qrow + d0);
+    u32x4 x = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * lg);
     if (!ok) x = u32x4{0, 0, 0, 0};
-    if constexpr (I8) {
-      f16x8 hx;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        hx[e] = static_cast<_Float16>(__uint_as_float((e & 1) ? (x[e >> 1] & 0xFFFF0000u) : (x[e >> 1] << 16)));
-      x = __builtin_bit_cast(u32x4, hx);
-    }
     qsh[f * 64 + lane] = x;
   }
   // ancestor bitsets of the unit's rows, needed by block tiles only
-  for (int r = WIDE ? h * 64 + lane : static_cast<int>(threadIdx.x); r < RBU * 16; r += WIDE ? 128 : 64 * NW)
+  for (int r = threadIdx.x; r < RBU * 16; r += 64 * NW)
     tbits_s[r] = r < w.nrows ? row_bits(p, w, w.row0 + r) : 1ull;
-  if constexpr (WIDE) {  // the "previous tile" of step 0 multiplies zeros
-    vT[1][threadIdx.x] = u32x4{0, 0, 0, 0};
-  }
   // every ordinary load has landed before the DMA ring starts, so the waits in
   // the loop count ring traffic only
   wait_vmcnt<0>();
@@ -487,26 +438,17 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
   const size_t head = (size_t)w.b * p.Hkv + w.kvh;
   const char* kbase = static_cast<const char*>(p.k) + head * p.cap * RBYTES;
   const char* vbase = static_cast<const char*>(p.v) + head * p.cap * RBYTES;
-  const uint16_t* ksb = I8 ? p.ks + head * p.cap : nullptr;
-  const uint16_t* vsb = I8 ? p.vs + head * p.cap : nullptr;
 
   // Per-lane DMA geometry: piece j of a K (or V) tile is tile row
   // r = (64 j + lane) / CH, 16-byte chunk (64 j + lane) % CH of that row
   // (swizzled), i.e. byte koff[j] of the tile.
   auto piece_row = [&](int j) { return (64 * j + lane) / CH; };
   auto piece_col = [&](int j) {
-    return 16u * static_cast<uint32_t>(((64 * j + lane) % CH) ^ lds_swz<I8>(piece_row(j)));
+    return 16u * static_cast<uint32_t>(((64 * j + lane) % CH) ^ lds_swz<false>(piece_row(j)));
   };
-  // WIDE: wave (h, pair) stages pieces NDK * pair .. of its half of each tile
-  constexpr int NKW = WIDE ? NK / 4 : NK;
-  const int j0 = WIDE ? NKW * pair : 0;
-  uint32_t koff[NKW];
+  uint32_t koff[NK];
 #pragma unroll
-  for (int j = 0; j < NKW; ++j) koff[j] = static_cast<uint32_t>(piece_row(j0 + j) * RBYTES) + piece_col(j0 + j);
-  // int8 scales: lanes 0-3 stage k-scales of keys t0 + 8 lane .. +8, lanes 4-7
-  // the v-scales
-  const uint16_t* sc_lane = lane < 4 ? ksb : vsb;
-  const int sc_key = 8 * (lane & 3);
+  for (int j = 0; j < NK; ++j) koff[j] = static_cast<uint32_t>(piece_row(j) * RBYTES) + piece_col(j);
 
   // Tile list: prefix tiles over [k_lo, k_hi) (the last may be partial), then
   // on the last split the block tiles over [P, P + T).
@@ -525,8 +467,8 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
     }
   };
 
-  // DMA this wave's half of one tile into ring slot t % S: the K half (with
-  // the int8 scales) or the V half, exactly NDK or NDV instructions. Full
+  // DMA this wave's half of one tile into ring slot t % S: the K half or the
+  // V half, exactly NK instructions. Full
   // tiles use the precomputed offsets; boundary tiles clamp every row into
   // [t0, limit) so they stay in bounds.
   const char* hbase = h == 0 ? kbase : vbase;
@@ -537,25 +479,18 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
     const char* src = hbase + (size_t)t0 * RBYTES;
     if (mode == 0) {
 #pragma unroll
-      for (int j = 0; j < NKW; ++j) dma16(src, koff[j], dst + 1024 * (j0 + j));
+      for (int j = 0; j < NK; ++j) dma16(src, koff[j], dst + 1024 * j);
     } else {
       const int lim = limit - 1 - t0;
 #pragma unroll
-      for (int j = 0; j < NKW; ++j)
-        dma16(src, static_cast<uint32_t>(min(piece_row(j0 + j), lim) * RBYTES) + piece_col(j0 + j),
-              dst + 1024 * (j0 + j));
-    }
-    if constexpr (I8) {
-      // a group reaching past cap is clamped to start at cap - 8 (cap >= 32)
-      if (h == 0 && lane < 8) dma16v(sc_lane + min(t0 + sc_key, p.cap - 8), ring[t % S] + SC_OFF);
+      for (int j = 0; j < NK; ++j)
+        dma16(src, static_cast<uint32_t>(min(piece_row(j), lim) * RBYTES) + piece_col(j), dst + 1024 * j);
     }
   };
   // this wave's half of tile t has landed: at most its halves of the tiles
   // issued after t are still outstanding
   auto wait_tile = [&](int t) {
-    const int ahead = min(S - 2, ntile - 1 - t);
-    if (h == 0) wait_vmcnt_tiles<NDK>(ahead);
-    else wait_vmcnt_tiles<NDV>(ahead);
+    wait_vmcnt_tiles<NK>(min(S - 2, ntile - 1 - t));
   };
 
   // The pair's two waves each stage half of every tile, so a tile is complete
@@ -571,11 +506,10 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
   int nt_wg = 0;
 #pragma unroll
   for (int q = 0; q < NP; ++q) nt_wg = max(nt_wg, s_nt[q]);
-  // the fold (WIDE: each pair's output in turn) goes through LDS: the rings,
-  // or for WIDE the Q fragments' space
+  // the fold goes through LDS, in the rings' space
   float* mo = reinterpret_cast<float*>(&ring_all[0][0][0]);
   float* mml = mo + RBU * 32 * 64;  // mo: [RBU][8][4][64] lane-major o; mml: [RBU * 16][2] (m, l)
-  static_assert(RBU * 32 * 64 * 4 + RBU * 16 * 8 <= NR * S * TILE, "fold area");
+  static_assert(RBU * 32 * 64 * 4 + RBU * 16 * 8 <= NP * S * TILE, "fold area");
   // Row-major stores of rows [0, wq.nrows) of a chunk from mo / mml, four
   // consecutive d per thread (coalesced): the unit's output if one partial
   // covers it, else partial slot `slot`. LDS holds o in the MFMA lane order:
@@ -626,7 +560,6 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
     // running per-row max of t. back(): turn t into fp16 probabilities, add
     // their row sums and P V into the accumulators.
     f32x4 sacc[2][RBA];
-    u32x4 vsc = {0, 0, 0, 0};
     const char* sl = nullptr;
     float negm[RBA];  // -m, or 0 while m is -inf
     float tmax[RBA];  // the lane's largest t = s * kss - m of its row so far
@@ -638,73 +571,26 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
       geom(t, t0, mode, limit);
       sl = ring[t % S];
 
-      // per-key scales (int8): lane holds keys 8g + e, e = 0..7, as fp16
-      u32x4 ksc = {0, 0, 0, 0};
-      vsc = u32x4{0, 0, 0, 0};
-      if constexpr (I8) {
-        if (t0 + KT <= p.cap) {
-          ksc = *reinterpret_cast<const u32x4*>(sl + SC_OFF + 16 * lg);
-          vsc = *reinterpret_cast<const u32x4*>(sl + SC_OFF + 64 + 16 * lg);
-        } else {
-          // the tile reaches past cap: the lane group's scales were staged from
-          // cap - 8 on, so key t0 + 8g + e sits delta places further on
-          const int delta = max(0, t0 + 8 * lg + 8 - p.cap);
-          const uint16_t* ksl = reinterpret_cast<const uint16_t*>(sl + SC_OFF + 16 * lg);
-          const uint16_t* vsl = reinterpret_cast<const uint16_t*>(sl + SC_OFF + 64 + 16 * lg);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int at = min(e + delta, 7);
-            ksc[e >> 1] |= static_cast<uint32_t>(ksl[at]) << (16 * (e & 1));
-            vsc[e >> 1] |= static_cast<uint32_t>(vsl[at]) << (16 * (e & 1));
-          }
-        }
-      }
-      float kss[8];  // score scale of key 8g + e, log2 units
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        kss[e] = I8 ? static_cast<float>(__builtin_bit_cast(f16x8, ksc)[e]) * p.scale_log2 : p.scale_log2;
-
       // S^T = K Q^T: block kb takes tile rows 8(i/4) + 4kb + i%4; k-step outer,
       // so consecutive MFMAs feed independent accumulators
       {
-        u32x4 kraw[2][2];
-        if constexpr (I8) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          bf16x8 kf[2];
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) {
             const int r = 8 * (li >> 2) + 4 * kb + (li & 3);
-            const char* krow = sl + r * RBYTES;
-            const int sw = lds_swz<true>(r);
-            kraw[kb][0] = *reinterpret_cast<const u32x4*>(krow + 16 * ((2 * lg) ^ sw)) ^ 0x80808080u;
-            kraw[kb][1] = *reinterpret_cast<const u32x4*>(krow + 16 * ((2 * lg + 1) ^ sw)) ^ 0x80808080u;
-          }
-        }
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          qk_t kf[2];
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            if constexpr (I8) {
-              const u32x4& src = kraw[kb][ks >> 1];
-              kf[kb] = i8x8_to_f16(src[2 * (ks & 1)], src[2 * (ks & 1) + 1]);
-            } else {
-              const int r = 8 * (li >> 2) + 4 * kb + (li & 3);
-              kf[kb] = __builtin_bit_cast(
-                  bf16x8, *reinterpret_cast<const u32x4*>(sl + r * RBYTES + 16 * ((4 * ks + lg) ^ lds_swz<false>(r))));
-            }
+            kf[kb] = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4*>(sl + r * RBYTES + 16 * ((4 * ks + lg) ^ lds_swz<false>(r))));
           }
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) {
-            qk_t qv;
-            if constexpr (WIDE) qv = __builtin_bit_cast(qk_t, qreg[rb][ks]);
-            else qv = __builtin_bit_cast(qk_t, qsh[((rb0 + rb) * 4 + ks) * 64 + lane]);
+            const bf16x8 qv = __builtin_bit_cast(bf16x8, qsh[((rb0 + rb) * 4 + ks) * 64 + lane]);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
               const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
               const f32x4 acc = ks == 0 ? zero : sacc[kb][rb];
-              if constexpr (I8)
-                sacc[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[kb], qv, acc, 0, 0, 0);
-              else
-                sacc[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb], qv, acc, 0, 0, 0);
+              sacc[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb], qv, acc, 0, 0, 0);
             }
           }
           // keep one k-step of Q fragments in flight at a time (register budget)
@@ -714,7 +600,7 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sacc[e >> 2][rb][e & 3] = fmaf(sacc[e >> 2][rb][e & 3], kss[e], negm[rb]);
+        for (int e = 0; e < 8; ++e) sacc[e >> 2][rb][e & 3] = fmaf(sacc[e >> 2][rb][e & 3], p.scale_log2, negm[rb]);
       }
       if (decltype(masked)::value && mode != 0) {  // boundary tiles: keys past the range, non-ancestors
 #pragma unroll
@@ -739,7 +625,7 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
     };
 
     auto back = [&]() {
-      // P^T fragments (fp16) and their row sums; int8: P' = P * v_scale feeds P V
+      // P^T fragments (fp16) and their row sums
       f16x8 pw[RBA];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
@@ -749,43 +635,10 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
 #pragma unroll
         for (int k = 0; k < 4; ++k)
           l[rb] = __builtin_amdgcn_fdot2(f16x2{pr[2 * k], pr[2 * k + 1]}, f16x2{1, 1}, l[rb], false);
-        if constexpr (I8) pw[rb] = pr * __builtin_bit_cast(f16x8, vsc);
-        else pw[rb] = pr;
+        pw[rb] = pr;
       }
       // O^T += V^T P^T: lane (i, g) reads V rows 8g + e, d = 8i .. 8i+7
-      if constexpr (I8) {
-        uint32_t a[8][2];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int r = 8 * lg + e;
-          const u32x2 v2 = *reinterpret_cast<const u32x2*>(sl + KBYTES + r * RBYTES +
-                                                           16 * ((li >> 1) ^ lds_swz<true>(r)) + 8 * (li & 1));
-          a[e][0] = v2[0] ^ 0x80808080u;
-          a[e][1] = v2[1] ^ 0x80808080u;
-        }
-        // regroup: d-block db = 4hh + j takes byte j of dword hh of keys e = 0..7
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          uint32_t ilo[4], ihi[4];
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            ilo[k] = __builtin_amdgcn_perm(a[2 * k + 1][hh], a[2 * k][hh], 0x05010400u);  // a0 b0 a1 b1
-            ihi[k] = __builtin_amdgcn_perm(a[2 * k + 1][hh], a[2 * k][hh], 0x07030602u);  // a2 b2 a3 b3
-          }
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            u32x4 vf;
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-              vf[k] = f16pair_from_bytes(j < 2 ? ilo[k] : ihi[k], (j & 1) ? 0x04030402u : 0x04010400u);
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-                o[4 * hh + j][rb] =
-                  __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, vf), pw[rb], o[4 * hh + j][rb], 0, 0, 0);
-            }
-          }
-        }
-      } else {
+      {
         u32x4 vr[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -805,44 +658,6 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
             o[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pw[rb], o[db][rb], 0, 0, 0);
           }
         }
-      }
-    };
-
-    // WIDE: P V runs one step behind, from the shared fp16 V^T fragments
-    f16x8 pprev[RBA];
-    auto make_p = [&]() {  // P^T fragments (fp16) of the scored tile and their row sums
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        f16x8 pr;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pr[e] = static_cast<_Float16>(__builtin_amdgcn_exp2f(sacc[e >> 2][rb][e & 3]));
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          l[rb] = __builtin_amdgcn_fdot2(f16x2{pr[2 * k], pr[2 * k + 1]}, f16x2{1, 1}, l[rb], false);
-        pprev[rb] = pr;
-      }
-    };
-    // V^T fragments of V tile t as fp16 into vT[t & 1]: fragment (db, lane
-    // (i, g)) holds V[8g + e][8i + db], e = 0..7; wave w builds d-block
-    // db = w for every lane (eight dword reads, one 16-byte write)
-    auto convert_v = [&](int t) {
-      const char* vt0 = ring[t % S] + KBYTES;
-      f16x8 f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int r = 8 * lg + e;
-        const uint32_t x =
-            *reinterpret_cast<const uint32_t*>(vt0 + r * RBYTES + 16 * (li ^ lds_swz<false>(r)) + 4 * (wave >> 1));
-        f[e] = static_cast<_Float16>(__uint_as_float((wave & 1) ? (x & 0xFFFF0000u) : (x << 16)));
-      }
-      vT[t & 1][wave * 64 + lane] = __builtin_bit_cast(u32x4, f);
-    };
-    auto pv_wide = [&](int t) {  // O^T += V^T P^T for tile t with the P of that tile
-#pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const f16x8 vf = __builtin_bit_cast(f16x8, vT[t & 1][db * 64 + lane]);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) o[db][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pprev[rb], o[db][rb], 0, 0, 0);
       }
     };
 
@@ -899,28 +714,13 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
         wait_tile(t);
         __syncthreads();  // tile t is complete in every pair; slot (t - 1) % S is free
         if (t + S - 1 < ntile) issue(t + S - 1);
-        if constexpr (WIDE) {
-          convert_v(t);
-          scores(t, masked);
-          pv_wide(t - 1);  // (step 0: zero P times the zeroed buffer)
-          make_p();
-        } else {
-          scores(t, masked);
-          back();
-        }
+        scores(t, masked);
+        back();
       };
-      if constexpr (WIDE) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) pprev[rb] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      }
 #pragma nounroll
       for (int t = 0; t < n_full; ++t) step(t, std::false_type{});
 #pragma nounroll
       for (int t = n_full; t < ntile; ++t) step(t, std::true_type{});
-      if constexpr (WIDE) {
-        __syncthreads();  // the last tile's fragments are complete
-        pv_wide(ntile - 1);
-      }
       for (int t = ntile; t < nt_wg; ++t) __syncthreads();
       // every wave has left the loop (its last wait drained its DMAs) before any
       // ring slot is staged again
@@ -944,32 +744,6 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
       l[rb] += __shfl_xor(l[rb], 32);
     }
     __syncthreads();  // every ring is drained
-    if constexpr (WIDE) {
-      // the pairs' chunks are disjoint: each is written out (or stored as
-      // a partial of its own) in turn
-      for (int q = 0; q < NP; ++q) {
-        if (pair == q) {
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) {
-            const int rloc = (rb0 + rb) * 16 + li;
-#pragma unroll
-            for (int db = 0; db < 8; ++db)
-#pragma unroll
-              for (int r = 0; r < 4; ++r) mo[(((rb0 + rb) * 8 + db) * 4 + r) * 64 + lane] = o[db][rb][r];
-            if (lg == 0) {
-              mml[rloc * 2] = m[rb];
-              mml[rloc * 2 + 1] = l[rb];
-            }
-          }
-        }
-        __syncthreads();
-        Work wq;
-        decode(p, wgi * NP + q, wq);
-        store_out(wq, wgi * NP + q, wq.nsplit == 1);
-        __syncthreads();
-      }
-      return;
-    }
     for (int step = 0; step < NP; ++step) {
       if (pair == step) {
 #pragma unroll
@@ -996,20 +770,9 @@ __global__ void __launch_bounds__(512) attn_mfma_kernel(const AttnParams p) {
       __syncthreads();
     }
   };
-  if constexpr (WIDE) {
-    // each wave runs the variant for its own row-block count, so small trees
-    // cost no idle MFMAs
-    static_assert(RB0 == 2 && RB1 == 2, "wide variants");
-    switch (nrb_w) {
-      case 0: per_wave(std::integral_constant<int, 0>{}, rb0_w); break;
-      case 1: per_wave(std::integral_constant<int, 1>{}, rb0_w); break;
-      default: per_wave(std::integral_constant<int, 2>{}, rb0_w); break;
-    }
-  } else {
-    if (h == 0) per_wave(std::integral_constant<int, RB0>{}, 0);
-    else per_wave(std::integral_constant<int, RB1>{}, RB0);
-    store_out(w, wgi, w.nsplit / NP == 1);  // one partial per workgroup
-  }
+  if (h == 0) per_wave(std::integral_constant<int, RB0>{}, 0);
+  else per_wave(std::integral_constant<int, RB1>{}, RB0);
+  store_out(w, wgi, w.nsplit / NP == 1);  // one partial per workgroup
 }
 
 // int8 KV, MFMA path, by phase. A workgroup is NP = 4 wave pairs taking 4
@@ -2383,7 +2146,7 @@ static ttv_status run_attention(const ttv_batch* batch, const void* q, int32_t q
   const bool i8 = layer->dtype == TTV_I8;
   if (pl.mfma) {
 #define TTV_MFMA(I, R0, R1) \
-  hipLaunchKernelGGL((attn_mfma_kernel<I, false, R0, R1, (I) ? 4 : 2>), dim3(mgrid), dim3(512), 0, st, p)
+  hipLaunchKernelGGL((attn_bf16_narrow_kernel<R0, R1, 2>), dim3(mgrid), dim3(512), 0, st, p)
 #define TTV_WIDE(R0, R1) hipLaunchKernelGGL((attn_bf16_split_kernel<kWideMaxRB>), dim3(mgrid), dim3(512), 0, st, p)
 #define TTV_MFMA_RB(R0, R1) TTV_MFMA(false, R0, R1)
 #define TTV_SPLIT(R)                                                                            \
