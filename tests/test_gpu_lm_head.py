@@ -187,7 +187,9 @@ def check_q4(got, hb, wq, sb, rows, block=16384):
 
 
 Q4_SMALL = [(1, 64, 4), (5, 128, 20), (16, 64, 512), (40, 128, 516), (64, 256, 5000), (65, 64, 3000),
-            (130, 128, 1500), (7, 1024, 4100), (20, 320, 1000), (32, 192, 772)]
+            (130, 128, 1500), (7, 1024, 4100), (20, 320, 1000), (32, 192, 772),
+            # 65..128 nodes share one slice (32 vocabulary rows per wave): ragged node and row tails
+            (100, 192, 2048), (128, 64, 3108), (80, 320, 1000), (257, 64, 516)]
 
 
 @pytest.mark.parametrize("N,H,V", Q4_SMALL)

@@ -200,20 +200,23 @@ __global__ void __launch_bounds__(kLmThreads) lm_head_main(const LmParams p) {
 // 8 codes per 32-bit word (hidden element i in bits 4 (i mod 8) of word
 // i / 8), (scale, bias) bf16 pairs stored group-major [H/64][V][2].
 //
-// Same tiling as the bf16 kernel (a wave owns 64 vocabulary rows, the
+// Same tiling as the bf16 kernel (a wave owns VB * 16 vocabulary rows, the
 // hidden states are staged through LDS one 64-element group at a time), but
 // each 32-k MFMA step stays inside one group: lane (i, g) takes hidden
 // elements 64 gi + 8 (2g + h) .. +8 in step h, i.e. code words 8 gi + 2g and
 // 8 gi + 2g + 1 (one 8-byte load). Codes become bf16 small integers exactly,
 // each group's products accumulate from zero on the matrix cores, and the
 // group is folded in as acc += scale * partial + bias * sum(hidden over the
-// group); the group sums come from the staging. At most 64 nodes per slice
-// (the per-group accumulators double the register use).
-constexpr int kLmQ4MaxNB = 4;
+// group); the group sums come from the staging. The per-group accumulators
+// double the register use, so a wave holds VB * 16 vocabulary rows x NB * 16
+// nodes with VB * NB <= 16: VB = 4 (64 rows) up to 64 nodes, VB = 2 (32 rows)
+// beyond, so up to 128 nodes share one slice: every code is converted once
+// for all of them and the head is read once.
+constexpr int kLmQ4MaxNB = 8;
 // up to 32 nodes: 4-wave workgroups (256 vocabulary rows), three per CU, for
-// more loads in flight; more nodes: 8-wave workgroups (512 rows), which halve
-// the hidden-state staging per weight byte
-constexpr int kLmQ4Slab = 4 * kLmRowsPerWave;              // the smaller slab, for the workspace
+// more loads in flight; more nodes: 8-wave workgroups, which halve the
+// hidden-state staging per weight byte
+constexpr int kLmQ4Slab = 4 * kLmRowsPerWave;              // the smallest slab (256 rows), for the workspace
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // byte B of x as a float (v_cvt_f32_ubyte<B>: one instruction, where the
@@ -251,10 +254,11 @@ struct LmQ4Params {
   int n_slabs, n_slices;
 };
 
-template <int NB, int NW>
+template <int NB, int NW, int VB>
 __global__ void __launch_bounds__(NW * kWave) lm_head_q4_main(const LmQ4Params p) {
+  static_assert(VB * NB <= 16 && NW * VB * 16 >= kLmQ4Slab, "accumulators, slab");
   constexpr int kLmQ4Threads = NW * kWave;
-  constexpr int kSlab = NW * kLmRowsPerWave;
+  constexpr int kSlab = NW * VB * 16;
   __shared__ __attribute__((aligned(16))) unsigned char s_x[2][16 * NB * kLmXPitch];
   __shared__ float s_xs[2][16 * NB];  // per staged row: the sum over the group
   __shared__ uint64_t s_best[NW][16 * NB];
@@ -266,23 +270,23 @@ __global__ void __launch_bounds__(NW * kWave) lm_head_q4_main(const LmQ4Params p
   const int lane = threadIdx.x % kWave;
   const int li = lane % 16, lg = lane / 16;
   const int n0 = slice * 16 * kLmQ4MaxNB;
-  const int v_wave = slab * kSlab + wave * kLmRowsPerWave;
+  const int v_wave = slab * kSlab + wave * VB * 16;
   const int G = p.H / 64;
   const int words = p.H / 8;
 
   // code words of this lane's rows (clamped into range; rows past V are ignored)
-  const uint32_t* wrow[4];
-  int vrow[4];
+  const uint32_t* wrow[VB];
+  int vrow[VB];
 #pragma unroll
-  for (int vb = 0; vb < 4; ++vb) {
+  for (int vb = 0; vb < VB; ++vb) {
     vrow[vb] = min(v_wave + 16 * vb + li, p.V - 1);
     wrow[vb] = p.wq + static_cast<int64_t>(vrow[vb]) * words + 2 * lg;
   }
   // (scale, bias) of the lane's output rows 16 vb + 4 lg .. +3 (V % 4 == 0,
   // so the four pairs are one aligned 16-byte load; clamped rows stay in range)
-  int srow[4];
+  int srow[VB];
 #pragma unroll
-  for (int vb = 0; vb < 4; ++vb) srow[vb] = min(v_wave + 16 * vb + 4 * lg, p.V - 4);
+  for (int vb = 0; vb < VB; ++vb) srow[vb] = min(v_wave + 16 * vb + 4 * lg, p.V - 4);
   // hidden-state staging: piece t covers row t / 8, bytes 16 (t % 8) of the
   // group; the 8 pieces of a row sit in 8 consecutive lanes, which also sum it
   constexpr int kPieces = 16 * NB * 8;
@@ -309,9 +313,9 @@ __global__ void __launch_bounds__(NW * kWave) lm_head_q4_main(const LmQ4Params p
     if (t % 8 == 0) s_xs[buf][t / 8] = sum;
   };
 
-  f32x4 acc[4][NB];
+  f32x4 acc[VB][NB];
 #pragma unroll
-  for (int vb = 0; vb < 4; ++vb)
+  for (int vb = 0; vb < VB; ++vb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[vb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -326,16 +330,16 @@ __global__ void __launch_bounds__(NW * kWave) lm_head_q4_main(const LmQ4Params p
   // while c + 1 and c + 2 load. The next group's hidden pieces are issued
   // before group c + 2's words, so waiting for them at the end of the step
   // (the load counter completes in issue order) never waits for c + 2.
-  u32x2 wcur[4], wnext[4];
-  u32x4 sbcur[4], sbnext[4];
+  u32x2 wcur[VB], wnext[VB];
+  u32x4 sbcur[VB], sbnext[VB];
   const int last = G - 1;
 #pragma unroll
-  for (int vb = 0; vb < 4; ++vb) {
+  for (int vb = 0; vb < VB; ++vb) {
     wcur[vb] = *reinterpret_cast<const u32x2*>(wrow[vb]);
     sbcur[vb] = *reinterpret_cast<const u32x4*>(p.sb + 2 * static_cast<int64_t>(srow[vb]));
   }
 #pragma unroll
-  for (int vb = 0; vb < 4; ++vb) {
+  for (int vb = 0; vb < VB; ++vb) {
     wnext[vb] = *reinterpret_cast<const u32x2*>(wrow[vb] + 8 * min(1, last));
     sbnext[vb] = *reinterpret_cast<const u32x4*>(p.sb + 2 * (static_cast<int64_t>(min(1, last)) * p.V + srow[vb]));
   }
@@ -349,18 +353,18 @@ __global__ void __launch_bounds__(NW * kWave) lm_head_q4_main(const LmQ4Params p
       for (int r = 0; r < kPiecesPerThread; ++r)
         if (threadIdx.x + kLmQ4Threads * r < kPieces) xs[r] = x_piece(c + 1, r);
     }
-    u32x2 wn2[4];
-    u32x4 sbn2[4];
+    u32x2 wn2[VB];
+    u32x4 sbn2[VB];
     const int c2 = min(c + 2, last);  // past the end: a re-read of the last group (L2), never used
 #pragma unroll
-    for (int vb = 0; vb < 4; ++vb) {
+    for (int vb = 0; vb < VB; ++vb) {
       wn2[vb] = *reinterpret_cast<const u32x2*>(wrow[vb] + 8 * c2);
       sbn2[vb] = *reinterpret_cast<const u32x4*>(p.sb + 2 * (static_cast<int64_t>(c2) * p.V + srow[vb]));
     }
     // the group's partial sums, from zero
-    f32x4 part[4][NB];
+    f32x4 part[VB][NB];
 #pragma unroll
-    for (int vb = 0; vb < 4; ++vb)
+    for (int vb = 0; vb < VB; ++vb)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) part[vb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -371,7 +375,7 @@ __global__ void __launch_bounds__(NW * kWave) lm_head_q4_main(const LmQ4Params p
         xf[nb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
                                                 &s_x[buf][(16 * nb + li) * kLmXPitch + 32 * lg + 16 * h]));
 #pragma unroll
-      for (int vb = 0; vb < 4; ++vb) {
+      for (int vb = 0; vb < VB; ++vb) {
         const bf16x8 wf = __builtin_bit_cast(bf16x8, q4_to_bf16x8(wcur[vb][h]));
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
@@ -383,7 +387,7 @@ __global__ void __launch_bounds__(NW * kWave) lm_head_q4_main(const LmQ4Params p
     for (int nb = 0; nb < NB; ++nb) {
       const float xsum = s_xs[buf][16 * nb + li];
 #pragma unroll
-      for (int vb = 0; vb < 4; ++vb)
+      for (int vb = 0; vb < VB; ++vb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float sc = __uint_as_float(sbcur[vb][j] << 16);
@@ -397,7 +401,7 @@ __global__ void __launch_bounds__(NW * kWave) lm_head_q4_main(const LmQ4Params p
         if (threadIdx.x + kLmQ4Threads * r < kPieces) x_store(buf ^ 1, r, xs[r]);
     }
 #pragma unroll
-    for (int vb = 0; vb < 4; ++vb) {
+    for (int vb = 0; vb < VB; ++vb) {
       wcur[vb] = wnext[vb];
       sbcur[vb] = sbnext[vb];
       wnext[vb] = wn2[vb];
@@ -411,7 +415,7 @@ __global__ void __launch_bounds__(NW * kWave) lm_head_q4_main(const LmQ4Params p
   for (int nb = 0; nb < NB; ++nb) {
     uint64_t best = 0;
 #pragma unroll
-    for (int vb = 0; vb < 4; ++vb)
+    for (int vb = 0; vb < VB; ++vb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int v = v_wave + 16 * vb + 4 * lg + j;
@@ -557,16 +561,18 @@ extern "C" ttv_status lm_head_q4_argmax(const uint16_t* hidden, int64_t n_rows, 
   const int rows0 = static_cast<int>(n_rows < 16 * kLmQ4MaxNB ? n_rows : 16 * kLmQ4MaxNB);
   const int nb = (rows0 + 15) / 16;
   const int nw = nb <= 2 ? 4 : 8;
-  p.n_slabs = static_cast<int>((vocab + nw * kLmRowsPerWave - 1) / (nw * kLmRowsPerWave));
+  const int vbw = nb <= 4 ? 4 : 2;  // row blocks per wave
+  p.n_slabs = static_cast<int>((vocab + nw * vbw * 16 - 1) / (nw * vbw * 16));
   p.n_slices = static_cast<int>((n_rows + 16 * kLmQ4MaxNB - 1) / (16 * kLmQ4MaxNB));
   const int64_t n_wg = static_cast<int64_t>(p.n_slabs) * p.n_slices;
   TTV_REQUIRE(n_wg <= (1ll << 30), TTV_ERR_INVALID, "lm_head_q4_argmax: too many workgroups");
   const unsigned grid = static_cast<unsigned>((n_wg + kNumXcd - 1) / kNumXcd * kNumXcd);
   hipStream_t s = (hipStream_t)stream;
   switch (nb) {
-#define TTV_LMQ(NB, NW) \
-  case NB: hipLaunchKernelGGL((lm_head_q4_main<NB, NW>), dim3(grid), dim3(NW * kWave), 0, s, p); break;
-    TTV_LMQ(1, 4) TTV_LMQ(2, 4) TTV_LMQ(3, 8) TTV_LMQ(4, 8)
+#define TTV_LMQ(NB, NW, VB) \
+  case NB: hipLaunchKernelGGL((lm_head_q4_main<NB, NW, VB>), dim3(grid), dim3(NW * kWave), 0, s, p); break;
+    TTV_LMQ(1, 4, 4) TTV_LMQ(2, 4, 4) TTV_LMQ(3, 8, 4) TTV_LMQ(4, 8, 4)
+    TTV_LMQ(5, 8, 2) TTV_LMQ(6, 8, 2) TTV_LMQ(7, 8, 2) TTV_LMQ(8, 8, 2)
 #undef TTV_LMQ
     default: return fail(TTV_ERR_INVALID, "lm_head_q4_argmax: internal node-block count");
   }
