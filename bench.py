@@ -48,6 +48,9 @@ def parse():
                          "SQ_VALU_MFMA_COEXEC_CYCLES, SQ_BUSY_CYCLES, SQ_WAIT_INST_ANY, SQ_ACTIVE_INST_LDS, "
                          "SQ_INSTS_VALU, SQ_INSTS_MFMA and GRBM_GUI_ACTIVE into per-kernel MFMA / VALU busy "
                          "fractions, then exit")
+    ap.add_argument("--trace-summary", metavar="KERNEL_STATS_CSV",
+                    help="print the library's kernels from a rocprofv3 --kernel-trace --stats kernel_stats.csv "
+                         "(durations in microseconds), then exit")
     return ap.parse_args()
 
 
@@ -288,8 +291,21 @@ def small_rounds(dev: str, steps: int = 100) -> dict:
 
 
 ATTN_SOURCE = os.path.join(ROOT, "token_tree_verification_build_amd", "csrc", "attention.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "tree_verify_attention_i8_131k_traffic.txt")
+# counter summaries per workload, named for the kernel and the workload they cover
+PROFILE_STEM = {5: "tree_verify_attention_i8_131k", 4: "tree_verify_attention_bf16_ragged_b32"}
 TRAFFIC_TAG = "bench-traffic: "
+# the kernels one tree_verify_attention call launches (main kernels of every
+# path, the exact int8 pass and the split-KV merge)
+ATTN_KERNELS = ("attn_i8_split_kernel", "attn_bf16_split_kernel", "attn_bf16_narrow_kernel", "attn_valu_kernel",
+                "merge_kernel")
+
+
+def is_attention_kernel(name: str) -> bool:
+    return any(k in name for k in ATTN_KERNELS)
+
+
+def profile_file(config: int, what: str) -> str:
+    return os.path.join(ROOT, "profiles", f"{PROFILE_STEM[config]}_{what}.txt")
 
 
 def source_digest(path: str) -> str:
@@ -332,26 +348,26 @@ def pmc_summary(fetch_csv: str, write_csv: str, calib_mib: int) -> None:
     print(f"  {calib_mib} MiB copied; FETCH_SIZE {cf:.0f} KiB -> {f_scale:.4f} B per counted B; "
           f"WRITE_SIZE {cw:.0f} KiB -> {w_scale:.4f} B per counted B")
     print(f"{'kernel':90s} {'n':>4s} {'fetch MB':>10s} {'write MB':>10s} {'scaled MB':>10s}")
-    attn = None   # the attention call = its main kernel + the merge kernel
-    merge = (0.0, 0.0, 0.0)
+    # the attention call = every kernel it launches, each dispatched once per
+    # call (per-dispatch means add up to the call's bytes)
+    main, top, rd, wr = None, -1.0, 0.0, 0.0
     for k in sorted(set(fetch) & set(write)):
+        if "ttv::" not in k and k != ck:   # the library's kernels and the calibration copy
+            continue
         fv, wv = fetch[k], write[k]
         fm, wm = sum(fv) / len(fv) * 1024, sum(wv) / len(wv) * 1024
         tot = fm * f_scale + wm * w_scale
         print(f"{k[:90]:90s} {len(fv):4d} {fm / 1e6:10.2f} {wm / 1e6:10.2f} {tot / 1e6:10.2f}")
-        if ("attn_mfma_kernel" in k or "attn_i8_split_kernel" in k) and (attn is None or tot > attn[1]):
-            attn = (k, tot, fm * f_scale, wm * w_scale)
-        if "merge_kernel" in k:
-            merge = (tot, fm * f_scale, wm * w_scale)
-    if attn is not None:
-        attn = (attn[0], attn[1] + merge[0], attn[2] + merge[1], attn[3] + merge[2])
-    if attn is not None:
-        rec = {"kernel": attn[0], "traffic_bytes": round(attn[1]), "read_bytes": round(attn[2]),
-               "write_bytes": round(attn[3]), "kernel_source_sha256": source_digest(ATTN_SOURCE)}
+        if is_attention_kernel(k):
+            rd, wr = rd + fm * f_scale, wr + wm * w_scale
+            if "merge_kernel" not in k and tot > top:
+                main, top = k, tot
+    if main is not None:
+        rec = {"kernel": main, "traffic_bytes": round(rd + wr), "read_bytes": round(rd),
+               "write_bytes": round(wr), "kernel_source_sha256": source_digest(ATTN_SOURCE)}
         print(TRAFFIC_TAG + json.dumps(rec))
 
 
-MFMA_FILE = os.path.join(ROOT, "profiles", "tree_verify_attention_mfma_busy.txt")
 MFMA_TAG = "bench-mfma: "
 N_CU, N_SIMD, N_XCD = 256, 1024, 8
 
@@ -372,7 +388,8 @@ def sq_summary(csv_path: str) -> None:
         d[r["Counter_Name"]] = float(r["Counter_Value"])
     per: dict = {}
     for (name, _), d in rows.items():
-        per.setdefault(name, []).append(d)
+        if "ttv::" in name:   # the library's kernels only
+            per.setdefault(name, []).append(d)
     print(f"{'kernel':80s} {'n':>3s} {'us':>8s} {'GHz':>5s} {'MFMA%':>6s} {'VALU%':>6s} {'coex%':>6s} "
           f"{'VALU/disp':>10s} {'MFMA/disp':>10s}")
     attn = None
@@ -390,7 +407,7 @@ def sq_summary(csv_path: str) -> None:
         co = 100 * avg("SQ_VALU_MFMA_COEXEC_CYCLES") / (cyc * N_SIMD)
         print(f"{name[:80]:80s} {n:3d} {ns / 1e3:8.1f} {cyc / ns:5.2f} {mf:6.1f} {va:6.1f} {co:6.1f} "
               f"{avg('SQ_INSTS_VALU'):10.3g} {avg('SQ_INSTS_MFMA'):10.3g}")
-        if ("attn_i8_split_kernel" in name or "attn_mfma_kernel" in name) and (attn is None or ns > attn[1]):
+        if is_attention_kernel(name) and "merge_kernel" not in name and (attn is None or ns > attn[1]):
             attn = (name, ns, mf, va, co)
     # every counter of the two busiest kernels, per dispatch
     for name, ds in sorted(per.items(), key=lambda kv: -sum(x["ns"] for x in kv[1]))[:2]:
@@ -402,35 +419,29 @@ def sq_summary(csv_path: str) -> None:
                                      "kernel_source_sha256": source_digest(ATTN_SOURCE)}))
 
 
-def recorded_mfma(workload: str):
-    """MFMA busy fraction of the dominant attention kernel recorded under
-    profiles/ for this workload, or None when the attention source has changed
-    since the counters were taken."""
+def trace_summary(csv_path: str) -> None:
+    """The library's kernels (namespace ttv) of a rocprofv3 kernel_stats.csv,
+    slowest total first."""
+    import csv
+    print(f"{'kernel':82s} {'calls':>6s} {'avg us':>9s} {'min us':>9s} {'max us':>9s} {'total ms':>9s}")
+    rows = [r for r in csv.DictReader(open(csv_path)) if "ttv::" in r["Name"]]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        print(f"{r['Name'][:82]:82s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.1f} "
+              f"{float(r['MinNs']) / 1e3:9.1f} {float(r['MaxNs']) / 1e3:9.1f} "
+              f"{float(r['TotalDurationNs']) / 1e6:9.2f}")
+
+
+def recorded(path: str, tag: str):
+    """The tagged record of a counter summary under profiles/, or None when the
+    file is absent or the attention source has changed since the counters
+    were taken."""
     try:
-        with open(MFMA_FILE) as f:
-            cur = None
+        with open(path) as f:
             for line in f:
-                if line.startswith("workload: "):
-                    cur = line[len("workload: "):].strip()
-                if line.startswith(MFMA_TAG) and cur == workload:
-                    rec = json.loads(line[len(MFMA_TAG):])
+                if line.startswith(tag):
+                    rec = json.loads(line[len(tag):])
                     if rec.get("kernel_source_sha256") == source_digest(ATTN_SOURCE):
                         return rec
-    except OSError:
-        pass
-    return None
-
-
-def recorded_traffic():
-    """Scaled HBM bytes per attention launch recorded under profiles/, or None
-    when the attention source has changed since the counters were taken."""
-    try:
-        with open(TRAFFIC_FILE) as f:
-            for line in f:
-                if line.startswith(TRAFFIC_TAG):
-                    rec = json.loads(line[len(TRAFFIC_TAG):])
-                    if rec.get("kernel_source_sha256") == source_digest(ATTN_SOURCE):
-                        return int(rec["traffic_bytes"])
     except OSError:
         pass
     return None
@@ -448,6 +459,9 @@ def main():
         return
     if args.sq_summary:
         sq_summary(args.sq_summary)
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -808,6 +822,14 @@ def main():
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         cpu = cpu_baseline(spec, caches, qs, logits, min(args.cpu_heads, spec.Hkv), min(args.cpu_seqs, B))
 
+    # counter figures recorded for this workload (None once the attention
+    # source differs from the one they were taken on)
+    traffic = recorded(profile_file(args.config, "traffic"), TRAFFIC_TAG)
+    mfma = recorded(profile_file(args.config, "mfma_busy"), MFMA_TAG)
+    if mfma:
+        kernels["tree_verify_attention"].update(
+            {"mfma_busy": mfma["mfma_busy_pct"] / 100, "valu_busy": mfma["valu_busy_pct"] / 100,
+             "mfma_valu_coexec": mfma["coexec_pct"] / 100, "counted_kernel": mfma["kernel"]})
     res = {
         "metric": "verified tree nodes/sec + achieved HBM GB/s (verify attn, KV gather) on 1 MI355X",
         "value": round(nodes_per_s, 1),
@@ -829,8 +851,9 @@ def main():
                    "step": "mask + L x attention + argmax + walk + in-place rollback gather"},
         "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic() if args.config == 5 else None,
-                     "kernel": "tree_verify_attention"},
+                     "traffic": traffic["traffic_bytes"] if traffic else None,
+                     "kernel": "tree_verify_attention",
+                     "mfma_busy": mfma["mfma_busy_pct"] / 100 if mfma else None},
         "cpu_baseline": cpu,
         "kernels": kernels,
         "other_rounds": small,
