@@ -46,6 +46,7 @@
 // scores, one d per lane for the output, queries and probabilities in LDS.
 #include "common.hpp"
 
+#include <algorithm>
 #include <climits>
 #include <mutex>
 #include <type_traits>
@@ -87,7 +88,14 @@ struct AttnParams {
   int32_t wg_off[TTV_MAX_BATCH + 1];
   int32_t unit_off[TTV_MAX_BATCH + 1];
   int32_t rchunk[TTV_MAX_BATCH];  // rows per chunk of sequence b (<= rows_chunk, the partials' row stride)
+  // wide layout, dispatch order: every workgroup of a full-length split first
+  // (sequence by sequence), then the workgroups of each sequence's last split,
+  // longest first. full_off[b]: full-split workgroups of sequences before b;
+  // last_key[k] = (last-split workgroups of the k longest before k) << 8 | b
+  int32_t full_off[TTV_MAX_BATCH + 1];
+  int32_t last_key[TTV_MAX_BATCH + 1];
 };
+static_assert(sizeof(AttnParams) <= 4096, "kernel arguments");
 
 struct Work {
   int b, kvh, split, rc, nsplit, rc_n, P, T, o0, rows, row0, nrows, unit, slot, k_lo, k_hi;
@@ -99,6 +107,57 @@ struct Work {
 // read by no row and the unit's splits start there.
 __host__ __device__ __forceinline__ int hist_key_start(int P, int window) {
   return (window > 0 && P - window + 1 > 0) ? P - window + 1 : 0;
+}
+
+// Splits of sequence b (the same count decode() derives).
+__host__ __device__ __forceinline__ int seq_splits(const AttnParams& p, int b) {
+  const int P = p.hist_len[b];
+  const int ks = hist_key_start(P, p.window);
+  const int ns = P > ks ? (P - ks + p.split_len - 1) / p.split_len : 1;
+  return (ns + p.split_pad - 1) / p.split_pad * p.split_pad;
+}
+
+// Wide layout: the workgroup that dispatch position g runs. Every workgroup
+// of a full-length split comes first, the short last splits after them,
+// longest first, so the last workgroups to start are the shortest ones.
+// Workgroup index wgi = wg_off[b] / 4 + (kvh * nsplit + split) * grp + group,
+// grp = the sequence's groups of four row chunks.
+__device__ __forceinline__ int wide_order(const AttnParams& p, int g) {
+  int b, kvh, split, grp_i;
+  const int nfull = p.full_off[p.B];
+  auto groups = [&](int bb) {
+    const int rows = (p.node_off[bb + 1] - p.node_off[bb]) * p.G;
+    const int rc = (rows + p.rchunk[bb] - 1) / p.rchunk[bb];
+    return (rc + 3) / 4;
+  };
+  if (g < nfull) {
+    int lo = 0, hi = p.B;  // full_off[lo] <= g < full_off[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (p.full_off[mid] <= g) lo = mid; else hi = mid;
+    }
+    b = lo;
+    const int grp = groups(b), ns = seq_splits(p, b);
+    const int idx = g - p.full_off[b];
+    kvh = idx / ((ns - 1) * grp);
+    const int r = idx % ((ns - 1) * grp);
+    split = r / grp;
+    grp_i = r % grp;
+  } else {
+    const int g2 = g - nfull;
+    int lo = 0, hi = p.B;  // (last_key[lo] >> 8) <= g2 < (last_key[hi] >> 8)
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if ((p.last_key[mid] >> 8) <= g2) lo = mid; else hi = mid;
+    }
+    b = p.last_key[lo] & 255;
+    const int grp = groups(b);
+    const int idx = g2 - (p.last_key[lo] >> 8);
+    kvh = idx / grp;
+    grp_i = idx % grp;
+    split = seq_splits(p, b) - 1;
+  }
+  return p.wg_off[b] / 4 + (kvh * seq_splits(p, b) + split) * groups(b) + grp_i;
 }
 
 __device__ __forceinline__ void decode(const AttnParams& p, int slot, Work& w) {
@@ -1404,9 +1463,10 @@ __global__ void __launch_bounds__(512) attn_bf16_split_kernel(const AttnParams p
 
   // Workgroups are dealt to the XCDs round-robin in launch order: sequences
   // of very different lengths then spread their work over every XCD (no two
-  // workgroups share K/V, so nothing is lost by leaving the XCD-contiguous map)
-  const int wgi = static_cast<int>(blockIdx.x);
-  if (wgi >= p.nwg / NP) return;  // whole workgroup
+  // workgroups share K/V, so nothing is lost by leaving the XCD-contiguous
+  // map); the launch order runs the short last splits at the end
+  if (static_cast<int>(blockIdx.x) >= p.nwg / NP) return;  // whole workgroup
+  const int wgi = wide_order(p, static_cast<int>(blockIdx.x));
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int pair = wave & (NP - 1);  // the pair's two waves sit on one SIMD
   const int h = wave / NP;           // 0: score wave, 1: value wave
@@ -1711,8 +1771,8 @@ __global__ void __launch_bounds__(512) attn_bf16_split_kernel(const AttnParams p
         if (s > 0 && s < ntile) wait_step(s);  // K and V of tile s have landed (step 0 waited above)
         __syncthreads();  // and every pair's P of tile s - 1 is in its buffer
         stage(s);
-        if (s < ntile) convert_v(s);
-        if (s > 0) accumulate(s - 1);
+        if (s > 0) accumulate(s - 1);  // V^T of tile s - 1 and its P: MFMAs issued first
+        if (s < ntile) convert_v(s);    // into the other V^T buffer while they run
       }
       const bool redo = __syncthreads_or(false) && attempt + 1 < kMaxAttempts;
       if (!redo) break;
@@ -2087,6 +2147,37 @@ static ttv_status plan_attention(const ttv_batch* batch, int Hq, const ttv_kv_la
   p.node_off[B] = batch->node_off_h[B];
   p.wg_off[B] = wg;
   p.unit_off[B] = units;
+  if (pl.wide) {
+    // dispatch order (wide_order): full-length splits first, then the last
+    // splits by descending cost (keys times a row-block weight)
+    int32_t order[TTV_MAX_BATCH];
+    int64_t cost[TTV_MAX_BATCH];
+    int nfull = 0;
+    for (int b = 0; b < B; ++b) {
+      const int T = batch->node_off_h[b + 1] - batch->node_off_h[b];
+      const int rc = (T * G + p.rchunk[b] - 1) / p.rchunk[b];
+      const int ns = seq_splits(p, b);
+      const int ks = hist_key_start(p.hist_len[b], window);
+      const int last_keys = p.hist_len[b] - ks - (ns - 1) * p.split_len + T;
+      p.full_off[b] = nfull;
+      nfull += p.Hkv * (ns - 1) * ((rc + 3) / 4);
+      cost[b] = (int64_t)last_keys * (6 + p.rchunk[b] / 16);
+      order[b] = b;
+    }
+    p.full_off[B] = nfull;
+    std::stable_sort(order, order + B, [&](int x, int y) { return cost[x] > cost[y]; });
+    int nlast = 0;
+    for (int k = 0; k < B; ++k) {
+      const int b = order[k];
+      const int T = batch->node_off_h[b + 1] - batch->node_off_h[b];
+      const int rc = (T * G + p.rchunk[b] - 1) / p.rchunk[b];
+      p.last_key[k] = (nlast << 8) | b;
+      nlast += p.Hkv * ((rc + 3) / 4);
+    }
+    p.last_key[B] = nlast << 8;
+    TTV_REQUIRE(nfull + nlast == wg / 4 && nlast < (1 << 22), TTV_ERR_INVALID,
+                "tree_verify_attention: %d workgroups exceed the dispatch-order table", wg / 4);
+  }
   p.nwg = wg;
   pl.nunits = units;
   // partial slots: one per workgroup on the narrow MFMA paths (its four pairs
