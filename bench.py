@@ -675,7 +675,7 @@ def main():
     for n_lm in sorted({int(batch.n_nodes), 16}):
         x_lm = torch.randn(n_lm, H_lm, device=dev, generator=gen_lm).to(torch.bfloat16)
         o_lm = torch.empty(n_lm, dtype=torch.int32, device=dev)
-        ws_lm = torch.empty(ttv.lm_head_q4_argmax_ws(n_lm, V), dtype=torch.uint8, device=dev)
+        ws_lm = torch.empty(ttv.lm_head_q4_argmax_ws(n_lm, V, H_lm), dtype=torch.uint8, device=dev)
         ttv.lm_head_q4_argmax(x_lm, wq_lm, sb_lm, o_lm, ws_lm)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

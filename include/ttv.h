@@ -366,13 +366,17 @@ ttv_status lm_head_argmax(const uint16_t* hidden, int64_t n_rows, int64_t hidden
  *                       group-major, 16-byte aligned
  *   out_idx    (device) int32 [n_rows]: lowest index of the largest logit
  * Each group's products accumulate in fp32 from exact bf16 codes and are
- * folded in as scale * partial + bias * (sum of the group's hidden values).
+ * folded in as scale * partial; the bias term, sum over groups of bias times
+ * the group's sum of hidden values, is a second matrix-core product: the
+ * group sums (fp32, in order) enter it as three exact bf16 terms, its
+ * products accumulate in fp32 and are added once.
  * Limits (TTV_ERR_INVALID): 0 <= n_rows <= 2^24, vocab a multiple of 4,
  * hidden_dim a positive multiple of 64 (<= 2^20), hidden_stride >= hidden_dim
- * and a multiple of 8. ws: >= lm_head_q4_argmax_ws(n_rows, vocab) bytes,
- * contents irrelevant. The codes are read once per 64 nodes.
+ * and a multiple of 8. ws: >= lm_head_q4_argmax_ws(n_rows, vocab, hidden_dim)
+ * bytes, contents irrelevant (0 for hidden_dim < 64). The codes are read once
+ * per 128 nodes.
  */
-size_t lm_head_q4_argmax_ws(int64_t n_rows, int64_t vocab);
+size_t lm_head_q4_argmax_ws(int64_t n_rows, int64_t vocab, int64_t hidden_dim);
 ttv_status lm_head_q4_argmax(const uint16_t* hidden, int64_t n_rows, int64_t hidden_stride, const uint32_t* wq,
                              const uint16_t* scale_bias, int64_t vocab, int64_t hidden_dim, int32_t* out_idx,
                              void* ws, size_t ws_bytes, void* stream);

@@ -388,8 +388,11 @@ def test_lm_head_validation():
 def test_lm_head_q4_validation():
     A = C["lm_head_q4_argmax"]
     V, H = 248320, 5120
-    ws = C["lm_head_q4_argmax_ws"](16, V)
-    assert ws == 16 * ((V + 255) // 256) * 8
+    ws = C["lm_head_q4_argmax_ws"](16, V, H)
+    # best keys per (node, 256-row slab), 256-byte aligned, then the group
+    # sums as three bf16 planes of 16 nodes x (groups rounded up to 32)
+    assert ws == (16 * ((V + 255) // 256) * 8 + 255) // 256 * 256 + 3 * 16 * 96 * 2
+    assert C["lm_head_q4_argmax_ws"](16, V, 32) == 0
 
     def call(n=16, hs=H, v=V, h=H, wq=FAKE, sb=FAKE, x=FAKE, ws_bytes=ws):
         return A(x, n, hs, wq, sb, v, h, FAKE, FAKE, ws_bytes, None)

@@ -86,7 +86,7 @@ _c = {
     "draft_tree_select": _sig("draft_tree_select", _i32, [_i32, _i32, _p, _p, _p, _p, _p, _i32, _p, _p, _p, _p, _p]),
     "lm_head_argmax_ws": _sig("lm_head_argmax_ws", _sz, [_i64, _i64]),
     "lm_head_argmax": _sig("lm_head_argmax", _i32, [_p, _i64, _i64, _p, _i64, _i64, _i64, _p, _p, _sz, _p]),
-    "lm_head_q4_argmax_ws": _sig("lm_head_q4_argmax_ws", _sz, [_i64, _i64]),
+    "lm_head_q4_argmax_ws": _sig("lm_head_q4_argmax_ws", _sz, [_i64, _i64, _i64]),
     "lm_head_q4_argmax": _sig("lm_head_q4_argmax", _i32, [_p, _i64, _i64, _p, _p, _i64, _i64, _p, _p, _sz, _p]),
     "ttv_last_error": _sig("ttv_last_error", ctypes.c_char_p, []),
 }
@@ -510,8 +510,8 @@ def lm_head_argmax(hidden, weight, out_idx, ws, stream=None):
                                 ws.numel() if ws is not None else 0, _stream(stream)), "lm_head_argmax")
 
 
-def lm_head_q4_argmax_ws(n_rows: int, vocab: int) -> int:
-    return int(_c["lm_head_q4_argmax_ws"](n_rows, vocab))
+def lm_head_q4_argmax_ws(n_rows: int, vocab: int, hidden_dim: int) -> int:
+    return int(_c["lm_head_q4_argmax_ws"](n_rows, vocab, hidden_dim))
 
 
 def lm_head_q4_argmax(hidden, wq, scale_bias, out_idx, ws, stream=None):

@@ -200,18 +200,25 @@ __global__ void __launch_bounds__(kLmThreads) lm_head_main(const LmParams p) {
 // 8 codes per 32-bit word (hidden element i in bits 4 (i mod 8) of word
 // i / 8), (scale, bias) bf16 pairs stored group-major [H/64][V][2].
 //
+// logit(v, n) = sum_g scale[g][v] * (sum_{i in g} code[v][i] x[n][i])
+//             + sum_g bias[g][v] * X[n][g],   X[n][g] = sum_{i in g} x[n][i].
+//
 // Same tiling as the bf16 kernel (a wave owns VB * 16 vocabulary rows, the
 // hidden states are staged through LDS one 64-element group at a time), but
 // each 32-k MFMA step stays inside one group: lane (i, g) takes hidden
 // elements 64 gi + 8 (2g + h) .. +8 in step h, i.e. code words 8 gi + 2g and
 // 8 gi + 2g + 1 (one 8-byte load). Codes become bf16 small integers exactly,
-// each group's products accumulate from zero on the matrix cores, and the
-// group is folded in as acc += scale * partial + bias * sum(hidden over the
-// group); the group sums come from the staging. The per-group accumulators
-// double the register use, so a wave holds VB * 16 vocabulary rows x NB * 16
-// nodes with VB * NB <= 16: VB = 4 (64 rows) up to 64 nodes, VB = 2 (32 rows)
-// beyond, so up to 128 nodes share one slice: every code is converted once
-// for all of them and the head is read once.
+// each group's products accumulate from zero on the matrix cores and the
+// group is folded in as acc += scale * partial. The bias term is a small
+// product of its own (vocabulary x groups times groups x nodes) on the matrix
+// cores, 32 groups at a time: a first launch forms X in fp32 and splits it
+// exactly into three bf16 terms (hi + mid + lo), so its products are exact
+// and accumulate in fp32 onto acc. The biases arrive with the scales; each
+// wave keeps its rows' biases of the current and the next 32 groups in LDS.
+// The per-group accumulators double the register use, so a wave holds VB * 16
+// vocabulary rows x NB * 16 nodes with VB * NB <= 16: VB = 4 (64 rows) up to
+// 32 nodes, VB = 2 (32 rows) beyond, so up to 128 nodes share one slice:
+// every code is converted once for all of them and the head is read once.
 constexpr int kLmQ4MaxNB = 8;
 // up to 32 nodes: 4-wave workgroups (256 vocabulary rows), three per CU, for
 // more loads in flight; more nodes: 8-wave workgroups, which halve the
@@ -249,18 +256,53 @@ struct LmQ4Params {
   const uint32_t* wq;   // [V][H/8] packed codes
   const uint16_t* sb;   // [H/64][V][2] bf16 (scale, bias)
   uint64_t* part;       // [N][n_slabs]
+  const uint16_t* xg;   // [3][N][Gp] bf16: the group sums' hi, mid and lo terms (zero for g >= G)
   int64_t x_stride;
   int N, V, H;
+  int Gp;               // groups rounded up to a multiple of 32
   int n_slabs, n_slices;
 };
+
+// X[n][g] in fp32 (the group's 64 values in order), split exactly into
+// hi + mid + lo with each term a bf16 (truncation leaves a remainder of at
+// most 16, then 8 significant bits); padded groups g in [G, Gp) are zero.
+__global__ void __launch_bounds__(256) lm_q4_group_sums(const uint16_t* __restrict__ x, int64_t x_stride, int N,
+                                                       int G, int Gp, uint16_t* __restrict__ xg) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= static_cast<int64_t>(N) * Gp) return;
+  const int n = static_cast<int>(t / Gp), g = static_cast<int>(t % Gp);
+  float s = 0.f;
+  if (g < G) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + n * x_stride + 64 * g);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const u32x4 v = src[q];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s += __uint_as_float(v[e] << 16);
+        s += __uint_as_float(v[e] & 0xFFFF0000u);
+      }
+    }
+  }
+  const uint32_t hi = __float_as_uint(s) & 0xFFFF0000u;
+  const float r1 = s - __uint_as_float(hi);
+  const uint32_t mid = __float_as_uint(r1) & 0xFFFF0000u;
+  const float r2 = r1 - __uint_as_float(mid);
+  const size_t plane = static_cast<size_t>(N) * Gp;
+  xg[t] = static_cast<uint16_t>(hi >> 16);
+  xg[plane + t] = static_cast<uint16_t>(mid >> 16);
+  xg[2 * plane + t] = static_cast<uint16_t>(__float_as_uint(r2) >> 16);
+}
 
 template <int NB, int NW, int VB>
 __global__ void __launch_bounds__(NW * kWave) lm_head_q4_main(const LmQ4Params p) {
   static_assert(VB * NB <= 16 && NW * VB * 16 >= kLmQ4Slab, "accumulators, slab");
   constexpr int kLmQ4Threads = NW * kWave;
   constexpr int kSlab = NW * VB * 16;
+  constexpr int kRows = VB * 16;  // vocabulary rows per wave
   __shared__ __attribute__((aligned(16))) unsigned char s_x[2][16 * NB * kLmXPitch];
-  __shared__ float s_xs[2][16 * NB];  // per staged row: the sum over the group
+  // biases of the wave's rows for groups g (slot g % 64): two chunks of 32
+  __shared__ __attribute__((aligned(16))) uint16_t s_bias[NW][64][kRows];
   __shared__ uint64_t s_best[NW][16 * NB];
   const int slot = xcd_slot(blockIdx.x, p.n_slabs * p.n_slices);
   if (slot < 0) return;  // padding workgroup (whole block, before any barrier)
@@ -270,25 +312,35 @@ __global__ void __launch_bounds__(NW * kWave) lm_head_q4_main(const LmQ4Params p
   const int lane = threadIdx.x % kWave;
   const int li = lane % 16, lg = lane / 16;
   const int n0 = slice * 16 * kLmQ4MaxNB;
-  const int v_wave = slab * kSlab + wave * VB * 16;
+  const int v_wave = slab * kSlab + wave * kRows;
   const int G = p.H / 64;
   const int words = p.H / 8;
 
   // code words of this lane's rows (clamped into range; rows past V are ignored)
   const uint32_t* wrow[VB];
-  int vrow[VB];
 #pragma unroll
-  for (int vb = 0; vb < VB; ++vb) {
-    vrow[vb] = min(v_wave + 16 * vb + li, p.V - 1);
-    wrow[vb] = p.wq + static_cast<int64_t>(vrow[vb]) * words + 2 * lg;
-  }
+  for (int vb = 0; vb < VB; ++vb)
+    wrow[vb] = p.wq + static_cast<int64_t>(min(v_wave + 16 * vb + li, p.V - 1)) * words + 2 * lg;
   // (scale, bias) of the lane's output rows 16 vb + 4 lg .. +3 (V % 4 == 0,
   // so the four pairs are one aligned 16-byte load; clamped rows stay in range)
   int srow[VB];
 #pragma unroll
   for (int vb = 0; vb < VB; ++vb) srow[vb] = min(v_wave + 16 * vb + 4 * lg, p.V - 4);
-  // hidden-state staging: piece t covers row t / 8, bytes 16 (t % 8) of the
-  // group; the 8 pieces of a row sit in 8 consecutive lanes, which also sum it
+  auto sb_load = [&](int vb, int c) {
+    return *reinterpret_cast<const u32x4*>(p.sb + 2 * (static_cast<int64_t>(c) * p.V + srow[vb]));
+  };
+  // the four scales of a (scale, bias) load as two bf16 pairs; its four
+  // biases go to the wave's LDS rows (the 16 lanes of a lane group hold the
+  // same rows: one of them writes)
+  auto scales = [](u32x4 sb) -> u32x2 {
+    return u32x2{__builtin_amdgcn_perm(sb[1], sb[0], 0x05040100u), __builtin_amdgcn_perm(sb[3], sb[2], 0x05040100u)};
+  };
+  auto keep_biases = [&](int vb, u32x4 sb, int g) {
+    if (li == 0)
+      *reinterpret_cast<u32x2*>(&s_bias[wave][g & 63][16 * vb + 4 * lg]) =
+          u32x2{__builtin_amdgcn_perm(sb[1], sb[0], 0x07060302u), __builtin_amdgcn_perm(sb[3], sb[2], 0x07060302u)};
+  };
+  // hidden-state staging: piece t covers row t / 8, bytes 16 (t % 8) of the group
   constexpr int kPieces = 16 * NB * 8;
   constexpr int kPiecesPerThread = (kPieces + kLmQ4Threads - 1) / kLmQ4Threads;
   auto x_piece = [&](int c, int r) -> u32x4 {
@@ -301,16 +353,6 @@ __global__ void __launch_bounds__(NW * kWave) lm_head_q4_main(const LmQ4Params p
   auto x_store = [&](int buf, int r, u32x4 v) {
     const int t = threadIdx.x + kLmQ4Threads * r;
     *reinterpret_cast<u32x4*>(&s_x[buf][(t / 8) * kLmXPitch + 16 * (t % 8)]) = v;
-    float sum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sum += __uint_as_float(v[e] << 16);
-      sum += __uint_as_float(v[e] & 0xFFFF0000u);
-    }
-    sum += __shfl_xor(sum, 1);
-    sum += __shfl_xor(sum, 2);
-    sum += __shfl_xor(sum, 4);
-    if (t % 8 == 0) s_xs[buf][t / 8] = sum;
   };
 
   f32x4 acc[VB][NB];
@@ -318,6 +360,42 @@ __global__ void __launch_bounds__(NW * kWave) lm_head_q4_main(const LmQ4Params p
   for (int vb = 0; vb < VB; ++vb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[vb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // acc += bias (rows x groups) . X (groups x nodes) over groups g0 .. g0 + 31
+  // (those past G are zero): A = the wave's biases (lane (i, g) holds row i,
+  // groups g0 + 8 g .. + 7), B = X as its three bf16 terms (lane (i, g) holds
+  // node i's groups g0 + 8 g .. + 7)
+  auto bias_chunk = [&](int g0) {
+    // the plane geometry re-read here, opaque to the compiler, so that the
+    // 3 x NB fragment addresses are formed in this rare block and not kept
+    // live through the group loop
+    int gp = p.Gp, nn = p.N;
+    asm volatile("" : "+s"(gp), "+s"(nn));
+    const uint16_t* xrow = p.xg + g0 + 8 * lg;
+    bf16x8 bf[VB];
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb) {
+      uint32_t bv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int g = g0 + 8 * lg + e;
+        const uint32_t b = s_bias[wave][g & 63][16 * vb + li];
+        bv[e] = g < G ? b : 0u;
+      }
+      bf[vb] = __builtin_bit_cast(bf16x8, u32x4{bv[0] | (bv[1] << 16), bv[2] | (bv[3] << 16), bv[4] | (bv[5] << 16),
+                                                bv[6] | (bv[7] << 16)});
+    }
+#pragma unroll
+    for (int sp = 0; sp < 3; ++sp)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int n = min(n0 + 16 * nb + li, nn - 1);
+        const bf16x8 xb = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(xrow + (static_cast<size_t>(sp) * nn + n) * gp));
+#pragma unroll
+        for (int vb = 0; vb < VB; ++vb)
+          acc[vb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[vb], xb, acc[vb][nb], 0, 0, 0);
+      }
+  };
 
   u32x4 xs[kPiecesPerThread];
 #pragma unroll
@@ -326,41 +404,46 @@ __global__ void __launch_bounds__(NW * kWave) lm_head_q4_main(const LmQ4Params p
 #pragma unroll
   for (int r = 0; r < kPiecesPerThread; ++r)
     if (threadIdx.x + kLmQ4Threads * r < kPieces) x_store(0, r, xs[r]);
-  // code words and (scale, bias) pairs two groups ahead: group c is used
-  // while c + 1 and c + 2 load. The next group's hidden pieces are issued
-  // before group c + 2's words, so waiting for them at the end of the step
-  // (the load counter completes in issue order) never waits for c + 2.
+  // Code words and (scale, bias) pairs two groups ahead: group c is used
+  // while c + 1 and c + 2 load; a pair load is reduced to its scales (and
+  // its biases put in LDS) one step before its fold. Issue order per step:
+  // the pairs, the next group's hidden pieces, then group c + 2's words, so
+  // waiting for the pieces at the end of the step (the load counter completes
+  // in issue order) covers the pairs and never waits for the words.
   u32x2 wcur[VB], wnext[VB];
-  u32x4 sbcur[VB], sbnext[VB];
+  u32x2 sccur[VB], scnext[VB];
   const int last = G - 1;
 #pragma unroll
   for (int vb = 0; vb < VB; ++vb) {
     wcur[vb] = *reinterpret_cast<const u32x2*>(wrow[vb]);
-    sbcur[vb] = *reinterpret_cast<const u32x4*>(p.sb + 2 * static_cast<int64_t>(srow[vb]));
+    const u32x4 sb0 = sb_load(vb, 0);
+    sccur[vb] = scales(sb0);
+    keep_biases(vb, sb0, 0);
   }
 #pragma unroll
   for (int vb = 0; vb < VB; ++vb) {
     wnext[vb] = *reinterpret_cast<const u32x2*>(wrow[vb] + 8 * min(1, last));
-    sbnext[vb] = *reinterpret_cast<const u32x4*>(p.sb + 2 * (static_cast<int64_t>(min(1, last)) * p.V + srow[vb]));
+    const u32x4 sb1 = sb_load(vb, min(1, last));
+    scnext[vb] = scales(sb1);
+    if (G > 1) keep_biases(vb, sb1, 1);
   }
   __syncthreads();
 
   for (int c = 0; c < G; ++c) {
     const int buf = c & 1;
     const bool more = c + 1 < G;
+    const int c2 = min(c + 2, last);  // past the end: a re-read of the last group (L2), never used
+    u32x4 sbn2[VB];
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb) sbn2[vb] = sb_load(vb, c2);
     if (more) {
 #pragma unroll
       for (int r = 0; r < kPiecesPerThread; ++r)
         if (threadIdx.x + kLmQ4Threads * r < kPieces) xs[r] = x_piece(c + 1, r);
     }
     u32x2 wn2[VB];
-    u32x4 sbn2[VB];
-    const int c2 = min(c + 2, last);  // past the end: a re-read of the last group (L2), never used
 #pragma unroll
-    for (int vb = 0; vb < VB; ++vb) {
-      wn2[vb] = *reinterpret_cast<const u32x2*>(wrow[vb] + 8 * c2);
-      sbn2[vb] = *reinterpret_cast<const u32x4*>(p.sb + 2 * (static_cast<int64_t>(c2) * p.V + srow[vb]));
-    }
+    for (int vb = 0; vb < VB; ++vb) wn2[vb] = *reinterpret_cast<const u32x2*>(wrow[vb] + 8 * c2);
     // the group's partial sums, from zero
     f32x4 part[VB][NB];
 #pragma unroll
@@ -384,17 +467,14 @@ __global__ void __launch_bounds__(NW * kWave) lm_head_q4_main(const LmQ4Params p
     }
     // fold the group in: output (row 16 vb + 4 lg + j, node 16 nb + li)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const float xsum = s_xs[buf][16 * nb + li];
+    for (int vb = 0; vb < VB; ++vb)
 #pragma unroll
-      for (int vb = 0; vb < VB; ++vb)
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w = sccur[vb][j >> 1];
+        const float sc = __uint_as_float((j & 1) ? (w & 0xFFFF0000u) : (w << 16));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float sc = __uint_as_float(sbcur[vb][j] << 16);
-          const float bi = __uint_as_float(sbcur[vb][j] & 0xFFFF0000u);
-          acc[vb][nb][j] = fmaf(sc, part[vb][nb][j], fmaf(bi, xsum, acc[vb][nb][j]));
-        }
-    }
+        for (int nb = 0; nb < NB; ++nb) acc[vb][nb][j] = fmaf(sc, part[vb][nb][j], acc[vb][nb][j]);
+      }
     if (more) {
 #pragma unroll
       for (int r = 0; r < kPiecesPerThread; ++r)
@@ -403,12 +483,17 @@ __global__ void __launch_bounds__(NW * kWave) lm_head_q4_main(const LmQ4Params p
 #pragma unroll
     for (int vb = 0; vb < VB; ++vb) {
       wcur[vb] = wnext[vb];
-      sbcur[vb] = sbnext[vb];
       wnext[vb] = wn2[vb];
-      sbnext[vb] = sbn2[vb];
+      sccur[vb] = scnext[vb];
+      scnext[vb] = scales(sbn2[vb]);
+      if (c + 2 <= last) keep_biases(vb, sbn2[vb], c + 2);
     }
+    // a finished chunk of 32 groups: its bias product (its biases were kept
+    // by this wave; group c + 2 went to the other half of the slots)
+    if ((c & 31) == 31) bias_chunk(c - 31);
     __syncthreads();
   }
+  if (G & 31) bias_chunk(G & ~31);
 
   // epilogue: node 16 nb + li's best over the lane's rows 16 vb + 4 lg + j
 #pragma unroll
@@ -520,9 +605,18 @@ extern "C" ttv_status lm_head_argmax(const uint16_t* hidden, int64_t n_rows, int
   return check_launch("lm_head_argmax reduce");
 }
 
-extern "C" size_t lm_head_q4_argmax_ws(int64_t n_rows, int64_t vocab) {
-  if (n_rows <= 0 || vocab <= 0) return 0;
-  return static_cast<size_t>(n_rows) * static_cast<size_t>((vocab + kLmQ4Slab - 1) / kLmQ4Slab) * sizeof(uint64_t);
+// workspace: the best key per (node, slab), then the group sums' three bf16
+// planes [3][n_rows][Gp] (256-byte aligned)
+static size_t lm_q4_part_bytes(int64_t n_rows, int64_t vocab) {
+  const size_t b = static_cast<size_t>(n_rows) * static_cast<size_t>((vocab + kLmQ4Slab - 1) / kLmQ4Slab) *
+                   sizeof(uint64_t);
+  return (b + 255) / 256 * 256;
+}
+static int lm_q4_gp(int64_t hidden_dim) { return static_cast<int>((hidden_dim / 64 + 31) / 32 * 32); }
+
+extern "C" size_t lm_head_q4_argmax_ws(int64_t n_rows, int64_t vocab, int64_t hidden_dim) {
+  if (n_rows <= 0 || vocab <= 0 || hidden_dim < 64) return 0;
+  return lm_q4_part_bytes(n_rows, vocab) + 3 * static_cast<size_t>(n_rows) * lm_q4_gp(hidden_dim) * sizeof(uint16_t);
 }
 
 extern "C" ttv_status lm_head_q4_argmax(const uint16_t* hidden, int64_t n_rows, int64_t hidden_stride,
@@ -546,7 +640,7 @@ extern "C" ttv_status lm_head_q4_argmax(const uint16_t* hidden, int64_t n_rows, 
                   reinterpret_cast<uintptr_t>(scale_bias) % 16 == 0,
               TTV_ERR_INVALID, "lm_head_q4_argmax: hidden and scale_bias must be 16-byte aligned, wq 8-byte");
   TTV_REQUIRE(vocab * (hidden_dim / 8) <= (int64_t{1} << 40), TTV_ERR_INVALID, "lm_head_q4_argmax: head too large");
-  const size_t need = lm_head_q4_argmax_ws(n_rows, vocab);
+  const size_t need = lm_head_q4_argmax_ws(n_rows, vocab, hidden_dim);
   TTV_REQUIRE(ws && ws_bytes >= need, TTV_ERR_WORKSPACE, "lm_head_q4_argmax: workspace %zu bytes < %zu", ws_bytes,
               need);
   LmQ4Params p;
@@ -554,24 +648,34 @@ extern "C" ttv_status lm_head_q4_argmax(const uint16_t* hidden, int64_t n_rows, 
   p.wq = wq;
   p.sb = scale_bias;
   p.part = static_cast<uint64_t*>(ws);
+  p.xg = reinterpret_cast<const uint16_t*>(static_cast<char*>(ws) + lm_q4_part_bytes(n_rows, vocab));
   p.x_stride = hidden_stride;
   p.N = static_cast<int>(n_rows);
   p.V = static_cast<int>(vocab);
   p.H = static_cast<int>(hidden_dim);
+  p.Gp = lm_q4_gp(hidden_dim);
+  hipStream_t s = (hipStream_t)stream;
+  {
+    const int64_t n_sums = n_rows * p.Gp;
+    TTV_REQUIRE(n_sums <= (int64_t{1} << 36), TTV_ERR_INVALID, "lm_head_q4_argmax: too many group sums");
+    hipLaunchKernelGGL(lm_q4_group_sums, dim3(static_cast<unsigned>((n_sums + 255) / 256)), dim3(256), 0, s, hidden,
+                       hidden_stride, p.N, p.H / 64, p.Gp, const_cast<uint16_t*>(p.xg));
+    ttv_status st = check_launch("lm_head_q4_argmax group sums");
+    if (st != TTV_OK) return st;
+  }
   const int rows0 = static_cast<int>(n_rows < 16 * kLmQ4MaxNB ? n_rows : 16 * kLmQ4MaxNB);
   const int nb = (rows0 + 15) / 16;
   const int nw = nb <= 2 ? 4 : 8;
-  const int vbw = nb <= 4 ? 4 : 2;  // row blocks per wave
+  const int vbw = nb <= 2 ? 4 : 2;  // row blocks per wave
   p.n_slabs = static_cast<int>((vocab + nw * vbw * 16 - 1) / (nw * vbw * 16));
   p.n_slices = static_cast<int>((n_rows + 16 * kLmQ4MaxNB - 1) / (16 * kLmQ4MaxNB));
   const int64_t n_wg = static_cast<int64_t>(p.n_slabs) * p.n_slices;
   TTV_REQUIRE(n_wg <= (1ll << 30), TTV_ERR_INVALID, "lm_head_q4_argmax: too many workgroups");
   const unsigned grid = static_cast<unsigned>((n_wg + kNumXcd - 1) / kNumXcd * kNumXcd);
-  hipStream_t s = (hipStream_t)stream;
   switch (nb) {
 #define TTV_LMQ(NB, NW, VB) \
   case NB: hipLaunchKernelGGL((lm_head_q4_main<NB, NW, VB>), dim3(grid), dim3(NW * kWave), 0, s, p); break;
-    TTV_LMQ(1, 4, 4) TTV_LMQ(2, 4, 4) TTV_LMQ(3, 8, 4) TTV_LMQ(4, 8, 4)
+    TTV_LMQ(1, 4, 4) TTV_LMQ(2, 4, 4) TTV_LMQ(3, 8, 2) TTV_LMQ(4, 8, 2)
     TTV_LMQ(5, 8, 2) TTV_LMQ(6, 8, 2) TTV_LMQ(7, 8, 2) TTV_LMQ(8, 8, 2)
 #undef TTV_LMQ
     default: return fail(TTV_ERR_INVALID, "lm_head_q4_argmax: internal node-block count");
