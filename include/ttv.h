@@ -367,9 +367,9 @@ ttv_status lm_head_argmax(const uint16_t* hidden, int64_t n_rows, int64_t hidden
  *   out_idx    (device) int32 [n_rows]: lowest index of the largest logit
  * Each group's products accumulate in fp32 from exact bf16 codes and are
  * folded in as scale * partial; the bias term, sum over groups of bias times
- * the group's sum of hidden values, is a second matrix-core product: the
- * group sums (fp32, in order) enter it as three exact bf16 terms, its
- * products accumulate in fp32 and are added once.
+ * the group's sum of hidden values, is a second matrix-core product, 32
+ * groups at a time: the group sums (fp32, in order) enter it as three exact
+ * bf16 terms, whose products accumulate in fp32 onto the same logits.
  * Limits (TTV_ERR_INVALID): 0 <= n_rows <= 2^24, vocab a multiple of 4,
  * hidden_dim a positive multiple of 64 (<= 2^20), hidden_stride >= hidden_dim
  * and a multiple of 8. ws: >= lm_head_q4_argmax_ws(n_rows, vocab, hidden_dim)

@@ -158,12 +158,13 @@ def run_q4(ttv, hb, wq, sb):
 def check_q4(got, hb, wq, sb, rows, block=16384):
     """Exact where the top two float64 logits are further apart than twice
     the bound on the kernel's error, and within the bound everywhere. Bound:
-    each group's 64 products accumulate in fp32 and the group is folded with
-    one fma (G roundings over the scaled partials); each group's hidden sum
-    accumulates in fp32 (64 terms), enters the bias product as three exact
-    bf16 terms whose 3 G products accumulate in fp32, and the bias total is
-    added once, so the error is at most
-    2^-24 (64 + 3 G + 8) sum_k |x_k| (s q_k + |b|) (G groups)."""
+    each group's 64 products accumulate in fp32 (64 roundings) and the group
+    is folded into the running logit with one fma (G roundings); each
+    group's hidden sum accumulates in fp32 (63 roundings) and enters the bias
+    product as three exact bf16 terms, whose 3 G exact products accumulate
+    onto the same running logit (3 G roundings). Every rounding is at most
+    2^-24 of a partial sum bounded by sum_k |x_k| (s q_k + |b|), so the error
+    is at most 2^-24 (64 + 4 G + 8) sum_k |x_k| (s q_k + |b|) (G groups)."""
     H = hb.shape[1]
     G = H // 64
     Xa = np.abs(bf16_bits_to_f32(hb[rows]).astype(np.float64))
@@ -179,7 +180,7 @@ def check_q4(got, hb, wq, sb, rows, block=16384):
     want = np.argmax(L, axis=1)
     decided = 0
     for r, n in enumerate(rows):
-        tol = 2.0 ** -24 * (64 + 3 * G + 8) * A[r].max()
+        tol = 2.0 ** -24 * (64 + 4 * G + 8) * A[r].max()
         top = np.sort(L[r])[-2:]
         assert 0 <= got[n] < wq.shape[0]
         assert L[r, got[n]] >= top[-1] - 2 * tol, f"node {n}: {L[r, got[n]]} vs {top[-1]} (tol {tol})"
