@@ -282,7 +282,11 @@ ttv_status tree_verify_attention_static(const ttv_batch* batch, const void* q, i
  * at least P_b + T_b for every b gives the same key sets as
  * tree_verify_attention). Arguments, layouts, limits and accuracy as there;
  * ws >= tree_verify_attention_window_ws(..., window) bytes. The band runs on
- * the VALU path for every dtype.
+ * the matrix cores (the same kernels as tree_verify_attention) when window
+ * >= 64 and, for every sequence whose first in-band history keys are hidden
+ * from some of its nodes, the in-band history holds at least one whole
+ * 32-key tile beyond the tiles of those keys; otherwise, and for f32 queries,
+ * on the VALU path.
  */
 size_t tree_verify_attention_window_ws(const ttv_batch* batch, int32_t Hq, const ttv_kv_layer* layer,
                                        int32_t q_dtype, int32_t window);

@@ -288,3 +288,16 @@ def test_window_attention_causal_block(ttv):
     from workloads import chain_tree
     parents = [chain_tree(33), chain_tree(8)]
     _window_check(ttv, "bf16", parents, [500, 70], 16, 4, [10, 40, 200], seed=5, causal=True)
+
+
+def test_window_attention_small_trees_edge_tiles(ttv):
+    """Trees of at most 19 nodes and a chain (the narrow bf16 kernel, and the
+    int8 one) under windows whose first keys are hidden from some rows: 64
+    and 65 (one hidden-key tile; at history 129 the window of 64 leaves no
+    whole tile behind it, so that call takes the vector path), 96/97/128
+    around the second tile, and windows reaching the start of the history."""
+    from workloads import chain_tree
+    parents = [random_tree(rng_for(1620, s), n) for s, n in enumerate((19, 7, 12))] + [chain_tree(3)]
+    hist = [5000, 2000, 700, 129]
+    _window_check(ttv, "bf16", parents, hist, 40, 8, [64, 65, 96, 97, 128, 500, 1999, 2000, 2020], seed=7)
+    _window_check(ttv, "i8", parents, hist, 40, 8, [64, 65, 100, 1000, 2010], seed=8)

@@ -206,6 +206,50 @@ __device__ __forceinline__ uint64_t row_bits(const AttnParams& p, const Work& w,
   return (2ull << t) - 1ull;  // t = 63 wraps to all ones
 }
 
+// The key tiles of a work item, in processing order: prefix tiles over
+// [k_lo, k_hi) (the last may be partial), then on the last split the block
+// tiles over [P, P + T). Under a sliding window node i keeps keys
+// j >= P - window + 1 + i (key j > P + i - window), so the first keys of the
+// unit's range are seen by some rows and not by others; the tiles holding
+// them ("edge" tiles, at most two: T <= 64) go behind the other prefix tiles
+// and are masked per row, so that the first tile, whose scores set the rows'
+// references, is one that every row sees whole. Tile modes: 0 a full prefix
+// tile, 1 the partial last prefix tile, 2 a block tile (ancestor bits),
+// 3 an edge tile (keys >= edge_lo + the row's node).
+struct TileList {
+  int k_lo, k_hi, P, T, edge_lo, n_edge, n_rest, n_pref, n_full, ntile;
+  __device__ __forceinline__ void init(const AttnParams& p, const Work& w, int kt) {
+    k_lo = w.k_lo;
+    k_hi = w.k_hi;
+    P = w.P;
+    T = w.T;
+    edge_lo = P - p.window + 1;
+    const int edge_end = min(edge_lo + T - 1, k_hi);  // keys below it are hidden from some row
+    n_edge = p.window > 0 && edge_end > k_lo ? (edge_end - k_lo + kt - 1) / kt : 0;
+    const int rest_lo = k_lo + kt * n_edge;
+    n_rest = k_hi > rest_lo ? (k_hi - rest_lo + kt - 1) / kt : 0;
+    n_full = k_hi > rest_lo ? (k_hi - rest_lo) / kt : 0;  // the leading mode-0 tiles
+    n_pref = n_edge + n_rest;
+    ntile = n_pref + (w.last ? (T + kt - 1) / kt : 0);
+  }
+  __device__ __forceinline__ void geom(int t, int kt, int& t0, int& mode, int& limit) const {
+    if (t < n_rest) {
+      t0 = k_lo + kt * (n_edge + t);
+      limit = k_hi;
+      mode = t0 + kt <= k_hi ? 0 : 1;
+    } else if (t < n_pref) {
+      t0 = k_lo + kt * (t - n_rest);
+      limit = k_hi;
+      mode = 3;
+    } else {
+      t0 = P + kt * (t - n_pref);
+      limit = P + T;
+      mode = 2;
+    }
+    t0 = __builtin_amdgcn_readfirstlane(t0);
+  }
+};
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
@@ -509,22 +553,12 @@ __global__ void __launch_bounds__(512) attn_bf16_narrow_kernel(const AttnParams 
 #pragma unroll
   for (int j = 0; j < NK; ++j) koff[j] = static_cast<uint32_t>(piece_row(j) * RBYTES) + piece_col(j);
 
-  // Tile list: prefix tiles over [k_lo, k_hi) (the last may be partial), then
-  // on the last split the block tiles over [P, P + T).
-  const int n_pref = w.k_hi > w.k_lo ? (w.k_hi - w.k_lo + KT - 1) / KT : 0;
-  const int ntile = n_pref + (w.last ? (w.T + KT - 1) / KT : 0);
-  const int n_full = w.k_hi > w.k_lo ? (w.k_hi - w.k_lo) / KT : 0;  // the leading mode-0 tiles
-  auto geom = [&](int t, int& t0, int& mode, int& limit) {
-    if (t < n_pref) {
-      t0 = w.k_lo + KT * t;
-      limit = w.k_hi;
-      mode = t0 + KT <= w.k_hi ? 0 : 1;
-    } else {
-      t0 = w.P + KT * (t - n_pref);
-      limit = w.P + w.T;
-      mode = 2;
-    }
-  };
+  // Tile list (full prefix tiles first, then the partial, edge and block ones)
+  TileList tl;
+  tl.init(p, w, KT);
+  const int ntile = tl.ntile;
+  const int n_full = tl.n_full;
+  auto geom = [&](int t, int& t0, int& mode, int& limit) { tl.geom(t, KT, t0, mode, limit); };
 
   // DMA this wave's half of one tile into ring slot t % S: the K half or the
   // V half, exactly NK instructions. Full
@@ -665,10 +699,12 @@ __global__ void __launch_bounds__(512) attn_bf16_narrow_kernel(const AttnParams 
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           const uint64_t bits = mode == 2 ? tbits_s[(rb0 + rb) * 16 + li] : ~0ull;
+          // an edge tile: the row's node i keeps keys >= edge_lo + i
+          const int lo = mode == 3 ? tl.edge_lo + (w.row0 + (rb0 + rb) * 16 + li) / p.G : INT_MIN;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int key = t0 + 8 * lg + e;
-            const bool keep = key < limit && ((bits >> ((key - w.P) & 63)) & 1ull);
+            const bool keep = key < limit && key >= lo && ((bits >> ((key - w.P) & 63)) & 1ull);
             sacc[e >> 2][rb][e & 3] = keep ? sacc[e >> 2][rb][e & 3] : -INFINITY;
           }
         }
@@ -930,22 +966,12 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
 #pragma unroll
   for (int j = 0; j < NK; ++j) koff[j] = static_cast<uint32_t>(piece_row(j) * RBYTES) + piece_col(j);
 
-  // Tile list: prefix tiles over [k_lo, k_hi) (the last may be partial), then
-  // on the last split the block tiles over [P, P + T).
-  const int n_pref = w.k_hi > w.k_lo ? (w.k_hi - w.k_lo + KT - 1) / KT : 0;
-  const int ntile = n_pref + (w.last ? (w.T + KT - 1) / KT : 0);
-  const int n_full = w.k_hi > w.k_lo ? (w.k_hi - w.k_lo) / KT : 0;  // the leading mode-0 tiles
-  auto geom = [&](int t, int& t0, int& mode, int& limit) {
-    if (t < n_pref) {
-      t0 = w.k_lo + KT * t;
-      limit = w.k_hi;
-      mode = t0 + KT <= w.k_hi ? 0 : 1;
-    } else {
-      t0 = w.P + KT * (t - n_pref);
-      limit = w.P + w.T;
-      mode = 2;
-    }
-  };
+  // Tile list (full prefix tiles first, then the partial, edge and block ones)
+  TileList tl;
+  tl.init(p, w, KT);
+  const int ntile = tl.ntile;
+  const int n_full = tl.n_full;
+  auto geom = [&](int t, int& t0, int& mode, int& limit) { tl.geom(t, KT, t0, mode, limit); };
   // Staging loads, issued by the value wave: K tile t (codes + both scale
   // groups: NDK instructions) or V tile t (NDV) into its ring slot. Boundary
   // tiles clamp every row into [t0, limit); a scale group reaching past cap is
@@ -1164,10 +1190,12 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           const uint64_t bits = mode == 2 ? tbits_s[rb * 16 + li] : ~0ull;
+          // an edge tile: the row's node i keeps keys >= edge_lo + i
+          const int lo = mode == 3 ? tl.edge_lo + (w.row0 + rb * 16 + li) / p.G : INT_MIN;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int key = t0 + 8 * lg + e;
-            const bool keep = key < limit && ((bits >> ((key - w.P) & 63)) & 1ull);
+            const bool keep = key < limit && key >= lo && ((bits >> ((key - w.P) & 63)) & 1ull);
             sacc[e >> 2][rb][e & 3] = keep ? sacc[e >> 2][rb][e & 3] : -INFINITY;
           }
         }
@@ -1500,22 +1528,13 @@ __global__ void __launch_bounds__(512) attn_bf16_split_kernel(const AttnParams p
 #pragma unroll
   for (int j = 0; j < NKW; ++j) koff[j] = static_cast<uint32_t>(piece_row(j0 + j) * RBYTES) + piece_col(j0 + j);
 
-  // Tile list: prefix tiles over [k_lo, k_hi) (the last may be partial), then
-  // on the last split the block tiles over [P, P + T). Every pair has the same.
-  const int n_pref = w.k_hi > w.k_lo ? (w.k_hi - w.k_lo + KT - 1) / KT : 0;
-  const int ntile = n_pref + (w.last ? (w.T + KT - 1) / KT : 0);
-  const int n_full = w.k_hi > w.k_lo ? (w.k_hi - w.k_lo) / KT : 0;
-  auto geom = [&](int t, int& t0, int& mode, int& limit) {
-    if (t < n_pref) {
-      t0 = w.k_lo + KT * t;
-      limit = w.k_hi;
-      mode = t0 + KT <= w.k_hi ? 0 : 1;
-    } else {
-      t0 = w.P + KT * (t - n_pref);
-      limit = w.P + w.T;
-      mode = 2;
-    }
-  };
+  // Tile list (full prefix tiles first, then the partial, edge and block
+  // ones); every pair has the same
+  TileList tl;
+  tl.init(p, w, KT);
+  const int ntile = tl.ntile;
+  const int n_full = tl.n_full;
+  auto geom = [&](int t, int& t0, int& mode, int& limit) { tl.geom(t, KT, t0, mode, limit); };
   // this value wave's pieces of tile t of K (or V) into ring slot t % S;
   // boundary tiles clamp every row into [t0, limit)
   auto issue_tile = [&](const char* base, uint32_t ring_lds, int t) {
@@ -1623,10 +1642,12 @@ __global__ void __launch_bounds__(512) attn_bf16_split_kernel(const AttnParams p
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           const uint64_t bits = mode == 2 ? tbits_s[rb * 16 + li] : ~0ull;
+          // an edge tile: the row's node i keeps keys >= edge_lo + i
+          const int lo = mode == 3 ? tl.edge_lo + (w.row0 + rb * 16 + li) / p.G : INT_MIN;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int key = t0 + 8 * lg + e;
-            const bool keep = key < limit && ((bits >> ((key - w.P) & 63)) & 1ull);
+            const bool keep = key < limit && key >= lo && ((bits >> ((key - w.P) & 63)) & 1ull);
             sacc[e >> 2][rb][e & 3] = keep ? sacc[e >> 2][rb][e & 3] : -INFINITY;
           }
         }
@@ -2042,20 +2063,30 @@ static ttv_status plan_attention(const ttv_batch* batch, int Hq, const ttv_kv_la
   const int B = batch->B;
   const int G = Hq / L->Hkv;
   int max_rows = 0, maxP = 0;
+  // a window on the matrix cores: at least 64 keys (so no block key of a
+  // tree of at most 64 nodes leaves the band), and every sequence whose
+  // first keys are hidden from some rows (at most two 32-key edge tiles)
+  // also has a whole tile past them, which the MFMA kernels score first
+  bool window_mfma = window == 0 || window >= 64;
   for (int b = 0; b < B; ++b) {
     const int T = batch->node_off_h[b + 1] - batch->node_off_h[b];
     const int P = batch->hist_len_h[b];
     TTV_REQUIRE((int64_t)P + T <= L->cap, TTV_ERR_INVALID,
                 "tree_verify_attention: sequence %d needs P + T = %d rows, cache holds %d", b, P + T, L->cap);
     max_rows = T * G > max_rows ? T * G : max_rows;
-    const int ph = P - hist_key_start(P, window);  // history keys the sequence's rows read
+    const int ks = hist_key_start(P, window);
+    const int ph = P - ks;  // history keys the sequence's rows read
     maxP = ph > maxP ? ph : maxP;
+    if (window > 0) {
+      const int edge_end = std::min(P - window + T, P);  // node i keeps keys >= P - window + 1 + i
+      const int n_edge = edge_end > ks ? (edge_end - ks + 31) / 32 : 0;
+      if (n_edge > 0 && ph < 32 * (n_edge + 1)) window_mfma = false;
+    }
   }
-  // the window's band runs on the VALU path (its per-row lower bound is one
-  // compare per key there); fewer than 16 rows still take the matrix cores,
-  // with the block's missing rows as zero queries: the VALU kernel's one wave
-  // per 16 rows and split would leave most of the chip idle
-  pl.mfma = bf && L->D == 128 && max_rows >= 1 && L->cap >= 32 && window == 0;
+  // fewer than 16 rows still take the matrix cores, with the block's missing
+  // rows as zero queries: the VALU kernel's one wave per 16 rows and split
+  // would leave most of the chip idle
+  pl.mfma = bf && L->D == 128 && max_rows >= 1 && L->cap >= 32 && window_mfma;
   pl.wide = pl.mfma && L->dtype != TTV_I8 && max_rows > 16 * kMfmaMaxRB;
   if (pl.wide) {
     // up to four balanced chunks of at most 80 rows side by side (more rows
@@ -2117,7 +2148,10 @@ static ttv_status plan_attention(const ttv_batch* batch, int Hq, const ttv_kv_la
   int64_t sl = (work + (pl.wide ? kWideTargetWG : kTargetWG) - 1) / (pl.wide ? kWideTargetWG : kTargetWG);
   const int64_t min_sl = (maxP + kMaxSplits - 1) / kMaxSplits;
   if (sl < min_sl) sl = min_sl;
-  if (sl < 256) sl = 256;
+  // at least four 32-key tiles: short histories still spread over several
+  // workgroups, and a window's first split holds its (at most two) edge
+  // tiles and a whole tile past them
+  if (sl < 128) sl = 128;
   sl = (sl + 63) / 64 * 64;
   p.split_len = static_cast<int>(sl);
   // MFMA workgroups are 4 wave pairs = 4 consecutive key splits of one unit,
