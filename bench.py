@@ -34,6 +34,9 @@ def parse():
     ap.add_argument("--no-take", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-small", action="store_true", help="skip the tiny, chain and 16-layer int8 round timings")
+    ap.add_argument("--no-window", action="store_true",
+                    help="skip the sliding-window layer timing (its launches share the attention kernels' names, so "
+                         "counter and trace summaries of the full-context call leave it out)")
     ap.add_argument("--cpu-heads", type=int, default=8, help="KV heads per sampled sequence in the CPU oracle sample")
     ap.add_argument("--cpu-seqs", type=int, default=2, help="sequences in the CPU oracle sample")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -576,29 +579,30 @@ def main():
     # node i reads the keys past P + i - 1024, i.e. the last 1,023 history rows
     # of every sequence plus its block; algorithmic bytes count those rows once
     W_SLIDE = 1024
-    wws = torch.zeros(ttv.tree_verify_attention_window_ws(batch, spec.Hq, layers[0], spec.q_dtype, W_SLIDE),
-                      dtype=torch.uint8, device=dev)
-    ttv.tree_verify_attention_window(batch, qs[0], layers[0], anc, scale, W_SLIDE, out, wws)
-    wev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
-    torch.cuda.synchronize()
-    for i, (e0, e1) in enumerate(wev):
-        e0.record()
-        ttv.tree_verify_attention_window(batch, qs[i % L], layers[i % L], anc, scale, W_SLIDE, out, wws)
-        e1.record()
-    torch.cuda.synchronize()
-    win_ms = sorted(e0.elapsed_time(e1) for e0, e1 in wev)[len(wev) // 2]
-    T_b = np.diff(spec.node_off)
-    win_rows = int(np.sum(np.minimum(spec.hist_len, W_SLIDE - 1) + T_b))
-    wbytes = (win_rows * spec.Hkv * kv_row_bytes(spec)
-              + spec.n_nodes * spec.Hq * spec.D * ((2 if spec.q_dtype == "bf16" else 4) + 4))
-    kernels["tree_verify_attention_window1024"] = {
-        "median_us": round(win_ms * 1e3, 2), "bytes": wbytes, "GBps": round(wbytes / (win_ms / 1e3) / 1e9, 1),
-        "frac_hbm": round(wbytes / (win_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
-        "what": f"one layer of the round under a {W_SLIDE}-token sliding window (median of 20 launches)",
-    }
-    print(f"[bench] sliding-window layer (W={W_SLIDE}) {win_ms * 1e3:.1f} us "
-          f"({kernels['tree_verify_attention_window1024']['GBps']} GB/s)", file=sys.stderr, flush=True)
-    del wws
+    if not args.no_window:
+        wws = torch.zeros(ttv.tree_verify_attention_window_ws(batch, spec.Hq, layers[0], spec.q_dtype, W_SLIDE),
+                          dtype=torch.uint8, device=dev)
+        ttv.tree_verify_attention_window(batch, qs[0], layers[0], anc, scale, W_SLIDE, out, wws)
+        wev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+        torch.cuda.synchronize()
+        for i, (e0, e1) in enumerate(wev):
+            e0.record()
+            ttv.tree_verify_attention_window(batch, qs[i % L], layers[i % L], anc, scale, W_SLIDE, out, wws)
+            e1.record()
+        torch.cuda.synchronize()
+        win_ms = sorted(e0.elapsed_time(e1) for e0, e1 in wev)[len(wev) // 2]
+        T_b = np.diff(spec.node_off)
+        win_rows = int(np.sum(np.minimum(spec.hist_len, W_SLIDE - 1) + T_b))
+        wbytes = (win_rows * spec.Hkv * kv_row_bytes(spec)
+                  + spec.n_nodes * spec.Hq * spec.D * ((2 if spec.q_dtype == "bf16" else 4) + 4))
+        kernels["tree_verify_attention_window1024"] = {
+            "median_us": round(win_ms * 1e3, 2), "bytes": wbytes, "GBps": round(wbytes / (win_ms / 1e3) / 1e9, 1),
+            "frac_hbm": round(wbytes / (win_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "what": f"one layer of the round under a {W_SLIDE}-token sliding window (median of 20 launches)",
+        }
+        print(f"[bench] sliding-window layer (W={W_SLIDE}) {win_ms * 1e3:.1f} us "
+              f"({kernels['tree_verify_attention_window1024']['GBps']} GB/s)", file=sys.stderr, flush=True)
+        del wws
 
     # sampled selection (temperature 1, top-k 20, top-p 0.95, one uniform per
     # node): the temperature > 0 form of the argmax step, timed on its own
