@@ -16,34 +16,45 @@
 //           read once for all of its rows (GQA sharing).
 //   split = a range of split_len prefix keys; the last split of a unit also
 //           takes the block keys [P, P + T) under the ancestor bitsets.
-//   Each split keeps an online softmax (reference max m, sum l, unnormalised
-//   output) over its keys. A unit covered by one workgroup is written
+//   Each split keeps its softmax against a per-row reference m (set from its
+//   first tile), the row sums l and the unnormalised output over its keys. A unit covered by one workgroup is written
 //   directly; otherwise every workgroup stores one (m, l, o) partial and a
-//   second launch merges a unit's partials by log-sum-exp. Workgroups are laid
-//   out XCD-contiguously so a unit's splits share one L2.
+//   second launch merges a unit's partials by log-sum-exp.
 //
-// MFMA path (bf16 queries, bf16 or int8 KV, D = 128, >= 16 rows): workgroups
-// of 4 wave pairs; a pair takes one split, its two waves split the unit's
-// rows and share one LDS ring of 32-key K/V tiles streamed from HBM by
-// LDS-DMA (each wave stages half of every tile). With lane = (i = lane % 16,
-// g = lane / 16) and v_mfma_f32_16x16x32_{bf16,f16}:
+// MFMA path (bf16 queries, bf16 or int8 KV, D = 128; a block of fewer than 16
+// rows is padded with zero queries): workgroups of 4 wave pairs, the two
+// waves of a pair on one SIMD, K/V streamed through LDS in 32-key tiles by
+// LDS-DMA. Three kernels:
+//   attn_i8_split_kernel   int8 KV. The pairs take 4 consecutive splits of
+//                          one unit (XCD-contiguous workgroups); a pair's
+//                          score wave forms S and the probabilities, its
+//                          value wave accumulates O and issues every load.
+//   attn_bf16_narrow_kernel bf16 KV, at most 96 rows per KV head. The pairs
+//                          take 4 consecutive splits; the two waves of a pair
+//                          split the rows and stage half of every tile each.
+//   attn_bf16_split_kernel bf16 KV, more rows. The pairs take up to 4 row
+//                          chunks of one (KV head, split) and share one ring;
+//                          split by phase as the int8 kernel. Workgroups are
+//                          dealt round-robin to the XCDs, longest first.
+// With lane = (i = lane % 16, g = lane / 16) and
+// v_mfma_f32_16x16x32_{bf16,f16}:
 //   S^T = K Q^T : A = K (16 keys x 32 d), B = Q^T (32 d x 16 rows). The two
 //       16-key blocks of a tile take keys 8(i/4) + 4kb + i%4, so the output
 //       lane (i, g) receives keys 8g .. 8g+7 of query row i.
 //   O^T = V^T P^T (v_mfma_f32_16x16x32_f16): B = P^T is exactly that lane's
 //       8 probabilities (k-slot group g <-> keys 8g..8g+7), rounded to fp16.
-//       A = V^T with output row m of d-block db standing for d = 8m + db, so
-//       lane (i, g) needs V[8g + e][8i .. 8i+8) for e = 0..7: eight contiguous
-//       16-byte (bf16) or 8-byte (int8) LDS reads, regrouped in registers.
-//   Precision: bf16 values and int8 codes convert to fp16 exactly, so the only
-//       rounding in P V is the fp16 probability (2^-12 relative); a bf16
-//       probability (2^-9) would not hold a 2e-3 bound once a short prefix
-//       makes the softmax peaked. bf16 V must therefore lie in fp16 range.
+//       A = V^T, lane (i, g) holding V[8g + e][d] for e = 0..7 of its d.
+//   Precision: bf16 values (in fp16 range) and int8 codes convert to fp16
+//       exactly, so the only rounding in P V is the fp16 probability (2^-12
+//       relative); a bf16 probability (2^-9) would not hold a 2e-3 bound once
+//       a short prefix makes the softmax peaked. bf16 V must therefore lie in
+//       fp16 range.
 //   int8 KV: codes (|c| <= 127) convert exactly to fp16; the per-token scales
 //       fold into the scores (s = (q . c) * k_scale) and into the
 //       probabilities (p' = p * v_scale), so the matrix cores only see codes.
-// VALU path (fp32 everything, or fewer than 16 rows): one key per lane for
-// scores, one d per lane for the output, queries and probabilities in LDS.
+// VALU path (fp32 queries and KV, D = 64, caches of fewer than 32 rows, and
+// windows the MFMA kernels do not take): one key per lane for scores, one d
+// per lane for the output, queries and probabilities in LDS.
 #include "common.hpp"
 
 #include <algorithm>
