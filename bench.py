@@ -312,9 +312,26 @@ def profile_file(config: int, what: str) -> str:
 
 
 def source_digest(path: str) -> str:
+    """SHA-256 of the source's code: every line with its // comment and
+    surrounding blanks removed, empty lines dropped (a comment edit leaves
+    recorded counters valid; any code change invalidates them)."""
     import hashlib
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    code = []
+    with open(path, encoding="utf-8") as f:
+        for line in f:
+            out, in_str, i = [], False, 0
+            while i < len(line):
+                ch = line[i]
+                if ch == '"' and (i == 0 or line[i - 1] != "\\"):
+                    in_str = not in_str
+                elif not in_str and line.startswith("//", i):
+                    break
+                out.append(ch)
+                i += 1
+            t = "".join(out).strip()
+            if t:
+                code.append(t)
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()
 
 
 def pmc_rows(csv_path: str, counter: str) -> dict:
