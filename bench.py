@@ -877,8 +877,8 @@ def main():
     mfma = recorded(profile_file(args.config, "mfma_busy"), MFMA_TAG)
     if mfma:
         kernels["tree_verify_attention"].update(
-            {"mfma_busy": mfma["mfma_busy_pct"] / 100, "valu_busy": mfma["valu_busy_pct"] / 100,
-             "mfma_valu_coexec": mfma["coexec_pct"] / 100, "counted_kernel": mfma["kernel"]})
+            {"mfma_busy": round(mfma["mfma_busy_pct"] / 100, 4), "valu_busy": round(mfma["valu_busy_pct"] / 100, 4),
+             "mfma_valu_coexec": round(mfma["coexec_pct"] / 100, 4), "counted_kernel": mfma["kernel"]})
     res = {
         "metric": "verified tree nodes/sec + achieved HBM GB/s (verify attn, KV gather) on 1 MI355X",
         "value": round(nodes_per_s, 1),
@@ -902,7 +902,7 @@ def main():
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic["traffic_bytes"] if traffic else None,
                      "kernel": "tree_verify_attention",
-                     "mfma_busy": mfma["mfma_busy_pct"] / 100 if mfma else None},
+                     "mfma_busy": round(mfma["mfma_busy_pct"] / 100, 4) if mfma else None},
         "cpu_baseline": cpu,
         "kernels": kernels,
         "other_rounds": small,
