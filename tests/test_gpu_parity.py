@@ -459,8 +459,10 @@ def test_attention_query_magnitudes(ttv, kv, qscale):
     fp16's normal range) to 300 (scores hundreds of log units apart, row sums
     of |q| past the offset code conversion's bound on the int8 path). The
     int8 path scales each row chunk's queries by a power of two into fp16
-    range and converts codes exactly once the rows' |q| sums grow; both KV
-    dtypes must stay within the tolerance of the float64 oracle."""
+    range (a call this small converts every code exactly, in one launch; the
+    offset form and its flagged second launch are checked at full size
+    below); both KV dtypes must stay within the tolerance of the float64
+    oracle."""
     from workloads.configs import _spec
     from workloads.gen import bf16_bits_to_f32, to_bf16_bits
     r = rng_for(1260, int(qscale * 1000) % 997, 0 if kv == "i8" else 1)
@@ -677,6 +679,45 @@ def test_long_context_full_size_sampled(ttv):
         worst = max(worst, float(np.abs(got - want).max()))
     log(f"full-size sampled rows: max|err| {worst:.3e}")
     assert worst <= TOL_BF16
+    assert np.isfinite(to_host(out)).all()
+
+
+def test_int8_offset_and_flagged_exact_launches(ttv):
+    """An int8 call above the single-launch size (2 sequences x 8 KV heads x
+    140,016 keys x 260 B = 582 MB) with unit-size queries on sequence 0 (the
+    offset code conversion) and queries scaled by 300 on sequence 1 (row sums
+    of |q| past the offset form's bound: those workgroups are flagged by the
+    first launch and run exact in the second). Sampled rows of both sequences
+    against the oracle."""
+    from workloads.device import dev_kv_cache, dev_queries
+    P, T, Hq, Hkv, D = 140000, 16, 40, 8, 128
+    G = Hq // Hkv
+    parents = [random_tree(rng_for(1320, b), T) for b in range(2)]
+    node_off = np.array([0, T, 2 * T], np.int32)
+    batch = ttv.Batch(node_off, np.array([P, P], np.int32))
+    c = dev_kv_cache(1320, 0, 2, Hkv, P + T, D, "i8", "cuda")
+    layer = ttv.KVLayer(c["k"], c["v"], c["k_scale"], c["v_scale"])
+    q = dev_queries(1321, 0, 2 * T, Hq, D, "bf16", "cuda")
+    q[T:] = (q[T:].float() * 300.0).to(torch.bfloat16)
+    anc, _, st = run_mask(ttv, batch, to_dev(np.concatenate(parents)))
+    scale = 1 / math.sqrt(D)
+    out, _ = run_attention(ttv, batch, q, layer, anc, scale)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    r = rng_for(1322)
+    worst = [0.0, 0.0]
+    for b in (0, 1):
+        for _ in range(2):
+            g = int(r.integers(0, Hkv))
+            slab = {n: to_host(c[n][b, g, :P + T]) for n in ("k", "v", "k_scale", "v_scale")}
+            for t in sorted({int(r.integers(0, T)), T - 1}):
+                node = b * T + t
+                qrows = to_host(q[node, g * G:(g + 1) * G])
+                want = _oracle_node_rows(slab, "i8", qrows, P, parents[b], t, scale)
+                got = to_host(out[node, g * G:(g + 1) * G])
+                worst[b] = max(worst[b], float(np.abs(got - want).max()))
+    log(f"int8 two-launch: max|err| offset rows {worst[0]:.3e}, exact rows {worst[1]:.3e}")
+    assert max(worst) <= TOL_BF16
     assert np.isfinite(to_host(out)).all()
 
 

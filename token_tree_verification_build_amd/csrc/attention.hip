@@ -905,11 +905,15 @@ constexpr float kOffsetQ1Max = 128.0f;
 //
 // The choice between the two conversions is made per workgroup from its rows
 // and the kernel is instantiated once per choice (one instantiation holding
-// both schedules the offset loop worse): the EXACT = false launch runs every
-// workgroup whose rows keep the offset form and flags the others in
-// exact_flags; the EXACT = true launch that follows runs the flagged ones.
-template <int RB, bool EXACT>
+// both schedules the offset loop worse): the MODE = kI8Offset launch runs
+// every workgroup whose rows keep the offset form and flags the others in
+// exact_flags; the MODE = kI8Flagged launch that follows runs the flagged
+// ones. A call too small for the offset form's gain to pay for a second
+// launch runs every workgroup exact in one MODE = kI8Exact launch.
+constexpr int kI8Offset = 0, kI8Flagged = 1, kI8Exact = 2;
+template <int RB, int MODE>
 __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) {
+  constexpr bool EXACT = MODE != kI8Offset;
   constexpr int NP = 4;                      // wave pairs = consecutive key splits of one unit
   constexpr int NW = 2 * NP;                 // waves
   constexpr int D = 128;
@@ -938,7 +942,7 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
 
   const int wgi = xcd_slot(blockIdx.x, p.nwg / NP);
   if (wgi < 0) return;  // whole workgroup
-  if constexpr (EXACT) {
+  if constexpr (MODE == kI8Flagged) {
     if (p.exact_flags[wgi] == 0) return;  // the offset launch ran it
   }
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
@@ -2050,6 +2054,7 @@ struct AttnPlan {
   AttnParams prm;  // everything except pointers
   int nunits;
   bool merge;  // some unit has more than one partial
+  bool i8_one_launch;  // int8: every workgroup takes the exact conversion in a single launch
   size_t off_ml, off_o, off_flags, ws_bytes;
 };
 
@@ -2193,6 +2198,17 @@ static ttv_status plan_attention(const ttv_batch* batch, int Hq, const ttv_kv_la
   p.node_off[B] = batch->node_off_h[B];
   p.wg_off[B] = wg;
   p.unit_off[B] = units;
+  // int8: below ~512 MB of K/V a call's kernel runs a few hundred µs or less,
+  // where the offset form's few percent are worth less than the exact
+  // launch that follows it (~5 µs): run everything exact in one launch
+  {
+    int64_t kv_rows = 0;
+    for (int b = 0; b < B; ++b) {
+      const int P = batch->hist_len_h[b];
+      kv_rows += (int64_t)p.Hkv * (P - hist_key_start(P, window) + batch->node_off_h[b + 1] - batch->node_off_h[b]);
+    }
+    pl.i8_one_launch = L->dtype == TTV_I8 && kv_rows * (2 * L->D + 4) < (int64_t{512} << 20);
+  }
   if (pl.wide) {
     // dispatch order (wide_order): full-length splits first, then the last
     // splits by descending cost (keys times a row-block weight)
@@ -2286,10 +2302,14 @@ static ttv_status run_attention(const ttv_batch* batch, const void* q, int32_t q
   hipLaunchKernelGGL((attn_bf16_narrow_kernel<R0, R1, 2>), dim3(mgrid), dim3(512), 0, st, p)
 #define TTV_WIDE(R0, R1) hipLaunchKernelGGL((attn_bf16_split_kernel<kWideMaxRB>), dim3(mgrid), dim3(512), 0, st, p)
 #define TTV_MFMA_RB(R0, R1) TTV_MFMA(false, R0, R1)
-#define TTV_SPLIT(R)                                                                            \
-  do {                                                                                          \
-    hipLaunchKernelGGL((attn_i8_split_kernel<R, false>), dim3(mgrid), dim3(512), 0, st, p);      \
-    hipLaunchKernelGGL((attn_i8_split_kernel<R, true>), dim3(mgrid), dim3(512), 0, st, p);       \
+#define TTV_SPLIT(R)                                                                                  \
+  do {                                                                                                \
+    if (pl.i8_one_launch) {                                                                           \
+      hipLaunchKernelGGL((attn_i8_split_kernel<R, kI8Exact>), dim3(mgrid), dim3(512), 0, st, p);       \
+    } else {                                                                                          \
+      hipLaunchKernelGGL((attn_i8_split_kernel<R, kI8Offset>), dim3(mgrid), dim3(512), 0, st, p);      \
+      hipLaunchKernelGGL((attn_i8_split_kernel<R, kI8Flagged>), dim3(mgrid), dim3(512), 0, st, p);     \
+    }                                                                                                 \
   } while (0)
     if (i8) {
       switch (pl.rb) {
