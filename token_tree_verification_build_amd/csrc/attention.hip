@@ -74,7 +74,7 @@ constexpr int kMfmaMaxRB = 6;   // row blocks of 16 per MFMA row chunk (96 rows,
 constexpr int kI8MaxRB = 5;     // int8: both waves of a pair hold all row blocks (80 rows)
 constexpr int kValuRows = 16;   // rows per VALU workgroup
 constexpr int kTargetWG = 1024;
-constexpr int kWideTargetWG = 768;
+constexpr int kWideTargetWG = 512;
 constexpr int kWideMaxRB = 5;  // bf16 wide layout: row blocks per row chunk (one pair of waves each)
 constexpr int kMaxSplits = 64;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -2159,8 +2159,8 @@ static ttv_status plan_attention(const ttv_batch* batch, int Hq, const ttv_kv_la
     work += (int64_t)p.Hkv * (pl.wide ? (rc + 3) / 4 : rc) * (ph > 0 ? ph : 1);
   }
   // a wide workgroup's partial is up to 320 rows of fp32: its split is kept
-  // long (about three workgroups per compute unit; with the short last
-  // splits dispatched at the end the tail stays small)
+  // long (about two workgroups per compute unit; with the short last splits
+  // dispatched at the end the tail stays small)
   int64_t sl = (work + (pl.wide ? kWideTargetWG : kTargetWG) - 1) / (pl.wide ? kWideTargetWG : kTargetWG);
   const int64_t min_sl = (maxP + kMaxSplits - 1) / kMaxSplits;
   if (sl < min_sl) sl = min_sl;
