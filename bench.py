@@ -190,6 +190,31 @@ def small_rounds(dev: str, steps: int = 100) -> dict:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n * 1e3  # us
 
+    def graph_timed(fn, ncopies, n):
+        """The same steps captured once per rotation copy as HIP graphs
+        (torch.cuda.CUDAGraph over the library's launches), replayed in turn:
+        the per-step launch cost without the host's per-launch overhead."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        graphs = []
+        for i in range(ncopies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                fn(i)
+            graphs.append(g)
+        torch.cuda.current_stream().wait_stream(side)
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n):
+            graphs[i % ncopies].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        del graphs
+        return e0.elapsed_time(e1) / n * 1e3  # us
+
     def round_runner(spec, layer_sets, q_sets, logit_sets):
         """step(i): mask + attention per layer + argmax + walk + in-place
         gather on rotation copy i % len(layer_sets)."""
@@ -238,7 +263,9 @@ def small_rounds(dev: str, steps: int = 100) -> dict:
     step = round_runner(spec, [[ttv.KVLayer(k, v)]], [[torch.from_numpy(L0["q"]).to(dev)]],
                         [torch.from_numpy(tens["logits"]).to(dev)])
     us = timed(step, steps)
+    gus = graph_timed(step, 1, steps)
     res["config1"] = {"us_per_step": round(us, 2), "nodes_per_s": round(spec.n_nodes / us * 1e6, 1),
+                      "us_per_step_graph": round(gus, 2), "nodes_per_s_graph": round(spec.n_nodes / gus * 1e6, 1),
                       "nodes": spec.n_nodes, "rotation_copies": 1,
                       "what": "7-node fp32 tree, 4/2 heads, D 64, prefix 64, vocab 1024"}
     # linear chains over a 2048-token bf16 prefix, and the chain-shape attention cost ratios
@@ -257,7 +284,9 @@ def small_rounds(dev: str, steps: int = 100) -> dict:
         if T > 1:
             step = round_runner(spec, layer_sets, [[q]], logit_sets)
             us = timed(step, max(steps, 2 * nrot))
+            gus = graph_timed(step, nrot, max(steps, 2 * nrot))
             res[f"config2_T{T}"] = {"us_per_step": round(us, 2), "nodes_per_s": round(T / us * 1e6, 1), "nodes": T,
+                                    "us_per_step_graph": round(gus, 2), "nodes_per_s_graph": round(T / gus * 1e6, 1),
                                     "rotation_copies": nrot, "rotated_bytes": nrot * per_copy,
                                     "what": f"chain of {T} nodes, bf16, 40/8 heads, prefix 2048, vocab 248320"}
         batch = ttv.Batch(spec.node_off, spec.hist_len, device=dev)
@@ -285,7 +314,9 @@ def small_rounds(dev: str, steps: int = 100) -> dict:
     logits = dev_planted_logits(spec.seed, spec.flat_targets, spec.vocab, spec.sigma, dev)
     step = round_runner(spec, layer_sets, [qs], [logits.clone() for _ in range(nrot)])
     us = timed(step, max(steps, 2 * nrot))
+    gus = graph_timed(step, nrot, max(steps, 2 * nrot))
     res["config3"] = {"us_per_step": round(us, 2), "nodes_per_s": round(spec.n_nodes / us * 1e6, 1),
+                      "us_per_step_graph": round(gus, 2), "nodes_per_s_graph": round(spec.n_nodes / gus * 1e6, 1),
                       "nodes": spec.n_nodes, "rotation_copies": nrot, "rotated_bytes": nrot * per_copy,
                       "what": "16-node int8 tree, 16 layers, 40/8 heads, prefix 4096, vocab 248320"}
     del copies, layer_sets, base
@@ -853,8 +884,8 @@ def main():
         small = small_rounds(dev)
         for k, r in small.items():
             if "us_per_step" in r:
-                print(f"[bench] {k}: {r['us_per_step']} us/step, {r['nodes_per_s']} nodes/s", file=sys.stderr,
-                      flush=True)
+                print(f"[bench] {k}: {r['us_per_step']} us/step, {r['nodes_per_s']} nodes/s "
+                      f"(graph replay {r['us_per_step_graph']} us/step)", file=sys.stderr, flush=True)
         print(f"[bench] attention T4/T1 {small['verify_cost_ratio']['T4_over_T1']}, "
               f"T8/T1 {small['verify_cost_ratio']['T8_over_T1']}", file=sys.stderr, flush=True)
 
