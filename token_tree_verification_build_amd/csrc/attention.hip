@@ -1761,6 +1761,10 @@ __global__ void __launch_bounds__(512) attn_bf16_split_kernel(const AttnParams p
 
   auto value_wave = [&](auto rb_count) {
     constexpr int RB = decltype(rb_count)::value;
+    // its instructions go first when both waves of the pair are ready: the
+    // score wave's exponentials then run beside these products (-2% against
+    // no priority, -1% against the score wave first)
+    __builtin_amdgcn_s_setprio(3);
     constexpr int RBA = RB > 0 ? RB : 1;
     f32x4 o[8][RBA];
     // V^T fragments of V tile t as fp16 into vT[t & 1]: fragment (db, lane
