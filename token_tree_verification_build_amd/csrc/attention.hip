@@ -425,16 +425,6 @@ __device__ __forceinline__ f16x8 i8x8_to_f16(uint32_t lo, uint32_t hi) {
   return __builtin_bit_cast(f16x8, r);
 }
 
-// Wait until at most N vector-memory operations of this wave are outstanding
-// (they complete in issue order).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-  __asm__ volatile("" ::: "memory");
-}
-
 // Wait until this wave's LDS reads (and scalar loads) have returned.
 __device__ __forceinline__ void wait_lgkmcnt0() {
   __asm__ volatile("" ::: "memory");
@@ -463,26 +453,6 @@ __device__ __forceinline__ int lds_swz(int r) {
   else return ((r >> 3) & 3) | ((r & 3) << 2);                      // 16 chunks per 256-byte row
 }
 
-// Direct global -> LDS loads of 16 bytes per lane; lane i lands at lds + 16 i
-// (lds must be wave-uniform). Issued as inline asm on purpose: the compiler
-// treats its own LDS-DMA builtin as possibly aliasing every later LDS read and
-// would wait for all outstanding DMAs (vmcnt 0) before each tile, which
-// serialises the ring. Completion is tracked explicitly with wait_vmcnt; the
-// memory clobber keeps every other memory access in program order.
-__device__ __forceinline__ uint32_t lds_u32(const void* lds) {
-  return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(lds))));
-}
-// scalar base (wave-uniform) + 32-bit per-lane byte offset; lds: LDS byte
-// address (wave-uniform)
-__device__ __forceinline__ void dma16_at(const void* sbase, uint32_t voff, uint32_t lds) {
-  __asm__ volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
-                   : "memory");
-}
-// per-lane 64-bit address
-__device__ __forceinline__ void dma16v_at(const void* g, uint32_t lds) {
-  __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory");
-}
 __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, const void* lds) {
   dma16_at(sbase, voff, lds_u32(lds));
 }

@@ -214,16 +214,16 @@ __global__ void __launch_bounds__(kLmThreads) lm_head_main(const LmParams p) {
 // cores, 32 groups at a time: a first launch forms X in fp32 and splits it
 // exactly into three bf16 terms (hi + mid + lo), so its products are exact
 // and accumulate in fp32 onto acc. The biases arrive with the scales; each
-// wave keeps its rows' biases of the current and the next 32 groups in LDS.
-// The per-group accumulators double the register use, so a wave holds VB * 16
-// vocabulary rows x NB * 16 nodes with VB * NB <= 16: VB = 4 (64 rows) up to
-// 32 nodes, VB = 2 (32 rows) beyond, so up to 128 nodes share one slice:
-// every code is converted once for all of them and the head is read once.
+// wave keeps its rows' biases of the current and the next 32 groups in LDS,
+// and the group sums of a chunk are staged in LDS with its last group.
+// A wave holds VB * 16 = 32 vocabulary rows x NB * 16 nodes (NB <= 8), so up
+// to 128 nodes share one slice: every code is converted once for all of them
+// and the head is read once. The group's partial sums are formed one node
+// block at a time, the fold of each block issued in the shadow of the next
+// block's MFMAs, so only two blocks of partial sums are live. Workgroups are
+// 8 waves (256 vocabulary rows).
 constexpr int kLmQ4MaxNB = 8;
-// up to 32 nodes: 4-wave workgroups (256 vocabulary rows), three per CU, for
-// more loads in flight; more nodes: 8-wave workgroups, which halve the
-// hidden-state staging per weight byte
-constexpr int kLmQ4Slab = 4 * kLmRowsPerWave;              // the smallest slab (256 rows), for the workspace
+constexpr int kLmQ4Slab = 4 * kLmRowsPerWave;              // vocabulary rows per workgroup (256), for the workspace
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // byte B of x as a float (v_cvt_f32_ubyte<B>: one instruction, where the
@@ -296,13 +296,22 @@ __global__ void __launch_bounds__(256) lm_q4_group_sums(const uint16_t* __restri
 
 template <int NB, int NW, int VB>
 __global__ void __launch_bounds__(NW * kWave) lm_head_q4_main(const LmQ4Params p) {
-  static_assert(VB * NB <= 16 && NW * VB * 16 >= kLmQ4Slab, "accumulators, slab");
+  static_assert(VB * NB <= 16 && NW * VB * 16 == kLmQ4Slab, "accumulators, slab");
   constexpr int kLmQ4Threads = NW * kWave;
   constexpr int kSlab = NW * VB * 16;
   constexpr int kRows = VB * 16;  // vocabulary rows per wave
   __shared__ __attribute__((aligned(16))) unsigned char s_x[2][16 * NB * kLmXPitch];
   // biases of the wave's rows for groups g (slot g % 64): two chunks of 32
   __shared__ __attribute__((aligned(16))) uint16_t s_bias[NW][64][kRows];
+  // the group sums' three bf16 terms of the current chunk of 32 groups:
+  // [term][node row] rows of 64 bytes, padded to kXgPitch (conflict-free
+  // 16-byte reads by 16 consecutive node rows), filled by whole 1 KiB
+  // direct-to-LDS loads
+  constexpr int kXgPitch = 80;
+  constexpr int kXgRows = 3 * 16 * NB;
+  constexpr int kXgSlots = kXgRows * (kXgPitch / 16);  // 16-byte slots
+  constexpr int kXgDma = (kXgSlots + 63) / 64;         // loads of 64 slots
+  __shared__ __attribute__((aligned(16))) unsigned char s_xg[kXgDma * 1024];
   __shared__ uint64_t s_best[NW][16 * NB];
   const int slot = xcd_slot(blockIdx.x, p.n_slabs * p.n_slices);
   if (slot < 0) return;  // padding workgroup (whole block, before any barrier)
@@ -364,13 +373,22 @@ __global__ void __launch_bounds__(NW * kWave) lm_head_q4_main(const LmQ4Params p
   // (those past G are zero): A = the wave's biases (lane (i, g) holds row i,
   // groups g0 + 8 g .. + 7), B = X as its three bf16 terms (lane (i, g) holds
   // node i's groups g0 + 8 g .. + 7)
+  // Stages the group sums of the chunk starting at g0 (groups g0 .. g0 + 31
+  // of the padded planes, in bounds) into s_xg with direct global -> LDS
+  // loads, no registers: load j of the workgroup fills slots 64 j .. +63,
+  // slot q being row q / 5, 16-byte part q % 5. The pad part of a row and any
+  // slot past the rows load a valid address and are never read.
+  auto stage_xg = [&](int g0) {
+    const uint32_t base = lds_u32(s_xg);
+    for (int j = wave; j < kXgDma; j += NW) {
+      const int q = 64 * j + lane;
+      const int row = min(q / (kXgPitch / 16), kXgRows - 1);
+      const int part = min(q % (kXgPitch / 16), 3);
+      const int sp = row / (16 * NB), n = min(n0 + row % (16 * NB), p.N - 1);
+      dma16v_at(p.xg + (static_cast<size_t>(sp) * p.N + n) * p.Gp + g0 + 8 * part, base + 1024 * j);
+    }
+  };
   auto bias_chunk = [&](int g0) {
-    // the plane geometry re-read here, opaque to the compiler, so that the
-    // 3 x NB fragment addresses are formed in this rare block and not kept
-    // live through the group loop
-    int gp = p.Gp, nn = p.N;
-    asm volatile("" : "+s"(gp), "+s"(nn));
-    const uint16_t* xrow = p.xg + g0 + 8 * lg;
     bf16x8 bf[VB];
 #pragma unroll
     for (int vb = 0; vb < VB; ++vb) {
@@ -388,9 +406,8 @@ __global__ void __launch_bounds__(NW * kWave) lm_head_q4_main(const LmQ4Params p
     for (int sp = 0; sp < 3; ++sp)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const int n = min(n0 + 16 * nb + li, nn - 1);
         const bf16x8 xb = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(xrow + (static_cast<size_t>(sp) * nn + n) * gp));
+            bf16x8, *reinterpret_cast<const u32x4*>(&s_xg[(sp * 16 * NB + 16 * nb + li) * kXgPitch + 16 * lg]));
 #pragma unroll
         for (int vb = 0; vb < VB; ++vb)
           acc[vb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[vb], xb, acc[vb][nb], 0, 0, 0);
@@ -404,96 +421,131 @@ __global__ void __launch_bounds__(NW * kWave) lm_head_q4_main(const LmQ4Params p
 #pragma unroll
   for (int r = 0; r < kPiecesPerThread; ++r)
     if (threadIdx.x + kLmQ4Threads * r < kPieces) x_store(0, r, xs[r]);
-  // Code words and (scale, bias) pairs two groups ahead: group c is used
-  // while c + 1 and c + 2 load; a pair load is reduced to its scales (and
-  // its biases put in LDS) one step before its fold. Issue order per step:
-  // the pairs, the next group's hidden pieces, then group c + 2's words, so
-  // waiting for the pieces at the end of the step (the load counter completes
-  // in issue order) covers the pairs and never waits for the words.
-  u32x2 wcur[VB], wnext[VB];
-  u32x2 sccur[VB], scnext[VB];
+  // Code words and (scale, bias) pairs two groups ahead, in a two-slot
+  // register ring: slot c & 1 holds group c's, and is refilled with group
+  // c + 2's right after group c has been converted, so no loaded register is
+  // copied from one step to the next (a copy of a register still loading
+  // would wait for that load, exposing its latency every step). The group
+  // loop is unrolled by two so that the slot index is known at compile time.
+  // Issue order per step: the next group's hidden pieces, then group c + 2's
+  // words and pairs; the step ends waiting for its hidden pieces, which (the
+  // load counter completes in issue order) also covers what the step before
+  // issued, but nothing issued after the pieces.
   const int last = G - 1;
+  u32x2 wr[2][VB];
+  u32x4 sbw[2][VB];
 #pragma unroll
-  for (int vb = 0; vb < VB; ++vb) {
-    wcur[vb] = *reinterpret_cast<const u32x2*>(wrow[vb]);
-    const u32x4 sb0 = sb_load(vb, 0);
-    sccur[vb] = scales(sb0);
-    keep_biases(vb, sb0, 0);
-  }
+  for (int q = 0; q < 2; ++q)
 #pragma unroll
-  for (int vb = 0; vb < VB; ++vb) {
-    wnext[vb] = *reinterpret_cast<const u32x2*>(wrow[vb] + 8 * min(1, last));
-    const u32x4 sb1 = sb_load(vb, min(1, last));
-    scnext[vb] = scales(sb1);
-    if (G > 1) keep_biases(vb, sb1, 1);
-  }
+    for (int vb = 0; vb < VB; ++vb) {
+      wr[q][vb] = *reinterpret_cast<const u32x2*>(wrow[vb] + 8 * min(q, last));
+      sbw[q][vb] = sb_load(vb, min(q, last));
+    }
   __syncthreads();
 
-  for (int c = 0; c < G; ++c) {
-    const int buf = c & 1;
+  auto step = [&](int c, auto slot_tag) __attribute__((always_inline)) {
+    constexpr int Q = decltype(slot_tag)::value;  // == c & 1
+    const int buf = Q;
     const bool more = c + 1 < G;
-    const int c2 = min(c + 2, last);  // past the end: a re-read of the last group (L2), never used
-    u32x4 sbn2[VB];
-#pragma unroll
-    for (int vb = 0; vb < VB; ++vb) sbn2[vb] = sb_load(vb, c2);
+    // the last step of a chunk of 32 groups (or of the row) stages the
+    // chunk's group sums for its bias product, ahead of the step's loads
+    const bool chunk_end = (c & 31) == 31 || c == last;
+    if (chunk_end) stage_xg(c & ~31);
     if (more) {
 #pragma unroll
       for (int r = 0; r < kPiecesPerThread; ++r)
         if (threadIdx.x + kLmQ4Threads * r < kPieces) xs[r] = x_piece(c + 1, r);
     }
-    u32x2 wn2[VB];
+    // the group's codes as bf16 (both 32-element halves), its scales, and
+    // its biases into this wave's LDS rows
+    bf16x8 wf[VB][2];
+    float sc[VB][4];
 #pragma unroll
-    for (int vb = 0; vb < VB; ++vb) wn2[vb] = *reinterpret_cast<const u32x2*>(wrow[vb] + 8 * c2);
-    // the group's partial sums, from zero
-    f32x4 part[VB][NB];
+    for (int vb = 0; vb < VB; ++vb) {
 #pragma unroll
-    for (int vb = 0; vb < VB; ++vb)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) part[vb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      bf16x8 xf[NB];
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        xf[nb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                                &s_x[buf][(16 * nb + li) * kLmXPitch + 32 * lg + 16 * h]));
-#pragma unroll
-      for (int vb = 0; vb < VB; ++vb) {
-        const bf16x8 wf = __builtin_bit_cast(bf16x8, q4_to_bf16x8(wcur[vb][h]));
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          part[vb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xf[nb], part[vb][nb], 0, 0, 0);
-      }
-    }
-    // fold the group in: output (row 16 vb + 4 lg + j, node 16 nb + li)
-#pragma unroll
-    for (int vb = 0; vb < VB; ++vb)
+      for (int h = 0; h < 2; ++h) wf[vb][h] = __builtin_bit_cast(bf16x8, q4_to_bf16x8(wr[Q][vb][h]));
+      const u32x2 scw = scales(sbw[Q][vb]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t w = sccur[vb][j >> 1];
-        const float sc = __uint_as_float((j & 1) ? (w & 0xFFFF0000u) : (w << 16));
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[vb][nb][j] = fmaf(sc, part[vb][nb][j], acc[vb][nb][j]);
+        const uint32_t w = scw[j >> 1];
+        sc[vb][j] = __uint_as_float((j & 1) ? (w & 0xFFFF0000u) : (w << 16));
       }
+      keep_biases(vb, sbw[Q][vb], c);
+    }
+    // refill the slot with group c + 2 (past the end: a re-read of the last
+    // group, never used)
+    const int c2 = min(c + 2, last);
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb) {
+      wr[Q][vb] = *reinterpret_cast<const u32x2*>(wrow[vb] + 8 * c2);
+      sbw[Q][vb] = sb_load(vb, c2);
+    }
+
+    // One node block at a time: the group's partial sums of block nb (two
+    // MFMAs from zero), and in their shadow the fold of block nb - 1 into the
+    // running logits, acc += scale * partial (output row 16 vb + 4 lg + j,
+    // node 16 nb + li). Only two blocks of partial sums are live.
+    auto fold = [&](const f32x4 (&part)[VB], int nb) __attribute__((always_inline)) {
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[vb][nb][j] = fmaf(sc[vb][j], part[vb][j], acc[vb][nb][j]);
+          // ties the fold to this point of the schedule (emits nothing):
+          // otherwise the folds, used only by the next group, sink below the
+          // scheduling barriers to the end of the group
+          asm volatile("" : "+v"(acc[vb][nb][j]));
+        }
+    };
+    // block nb + 1's hidden fragments are read while block nb multiplies; a
+    // scheduling barrier closes each block, so the compiler cannot gather the
+    // MFMAs of all blocks first and leave the folds to the end
+    auto x_frag = [&](int nb, int h) {
+      return __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(&s_x[buf][(16 * nb + li) * kLmXPitch + 32 * lg + 16 * h]));
+    };
+    f32x4 prev[VB];
+    bf16x8 x0 = x_frag(0, 0), x1 = x_frag(0, 1);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      bf16x8 y0 = x0, y1 = x1;
+      if (nb + 1 < NB) {
+        y0 = x_frag(nb + 1, 0);
+        y1 = x_frag(nb + 1, 1);
+      }
+      f32x4 cur[VB];
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) {
+        cur[vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[vb][0], x0, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        cur[vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[vb][1], x1, cur[vb], 0, 0, 0);
+      }
+      if (nb > 0) fold(prev, nb - 1);
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) prev[vb] = cur[vb];
+      x0 = y0;
+      x1 = y1;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    fold(prev, NB - 1);
     if (more) {
 #pragma unroll
       for (int r = 0; r < kPiecesPerThread; ++r)
         if (threadIdx.x + kLmQ4Threads * r < kPieces) x_store(buf ^ 1, r, xs[r]);
     }
-#pragma unroll
-    for (int vb = 0; vb < VB; ++vb) {
-      wcur[vb] = wnext[vb];
-      wnext[vb] = wn2[vb];
-      sccur[vb] = scnext[vb];
-      scnext[vb] = scales(sbn2[vb]);
-      if (c + 2 <= last) keep_biases(vb, sbn2[vb], c + 2);
-    }
-    // a finished chunk of 32 groups: its bias product (its biases were kept
-    // by this wave; group c + 2 went to the other half of the slots)
-    if ((c & 31) == 31) bias_chunk(c - 31);
+    // the staging loads came before the step's 2 VB refill loads: once at
+    // most that many are outstanding, they have landed (in issue order)
+    if (chunk_end) wait_vmcnt<2 * VB>();
     __syncthreads();
+    // a finished chunk: its bias product (its biases were kept by this wave;
+    // its group sums are staged)
+    if (chunk_end) bias_chunk(c & ~31);
+  };
+  int c = 0;
+  for (; c + 1 < G; c += 2) {
+    step(c, std::integral_constant<int, 0>{});
+    step(c + 1, std::integral_constant<int, 1>{});
   }
-  if (G & 31) bias_chunk(G & ~31);
+  if (c < G) step(c, std::integral_constant<int, 0>{});
 
   // epilogue: node 16 nb + li's best over the lane's rows 16 vb + 4 lg + j
 #pragma unroll
@@ -665,9 +717,7 @@ extern "C" ttv_status lm_head_q4_argmax(const uint16_t* hidden, int64_t n_rows, 
   }
   const int rows0 = static_cast<int>(n_rows < 16 * kLmQ4MaxNB ? n_rows : 16 * kLmQ4MaxNB);
   const int nb = (rows0 + 15) / 16;
-  const int nw = nb <= 2 ? 4 : 8;
-  const int vbw = nb <= 2 ? 4 : 2;  // row blocks per wave
-  p.n_slabs = static_cast<int>((vocab + nw * vbw * 16 - 1) / (nw * vbw * 16));
+  p.n_slabs = static_cast<int>((vocab + kLmQ4Slab - 1) / kLmQ4Slab);
   p.n_slices = static_cast<int>((n_rows + 16 * kLmQ4MaxNB - 1) / (16 * kLmQ4MaxNB));
   const int64_t n_wg = static_cast<int64_t>(p.n_slabs) * p.n_slices;
   TTV_REQUIRE(n_wg <= (1ll << 30), TTV_ERR_INVALID, "lm_head_q4_argmax: too many workgroups");
@@ -675,7 +725,7 @@ extern "C" ttv_status lm_head_q4_argmax(const uint16_t* hidden, int64_t n_rows, 
   switch (nb) {
 #define TTV_LMQ(NB, NW, VB) \
   case NB: hipLaunchKernelGGL((lm_head_q4_main<NB, NW, VB>), dim3(grid), dim3(NW * kWave), 0, s, p); break;
-    TTV_LMQ(1, 4, 4) TTV_LMQ(2, 4, 4) TTV_LMQ(3, 8, 2) TTV_LMQ(4, 8, 2)
+    TTV_LMQ(1, 8, 2) TTV_LMQ(2, 8, 2) TTV_LMQ(3, 8, 2) TTV_LMQ(4, 8, 2)
     TTV_LMQ(5, 8, 2) TTV_LMQ(6, 8, 2) TTV_LMQ(7, 8, 2) TTV_LMQ(8, 8, 2)
 #undef TTV_LMQ
     default: return fail(TTV_ERR_INVALID, "lm_head_q4_argmax: internal node-block count");
