@@ -30,8 +30,7 @@ namespace ttv {
 
 constexpr int kLmWaves = 8;
 constexpr int kLmThreads = kLmWaves * kWave;
-constexpr int kLmRowsPerWave = 64;                       // 4 blocks of 16 vocabulary rows
-constexpr int kLmSlab = kLmWaves * kLmRowsPerWave;       // 512 vocabulary rows per workgroup
+constexpr int kLmMaxVB = 4;                              // blocks of 16 vocabulary rows per wave, at most
 constexpr int kLmKc = 64;                                // k elements per LDS slice (two MFMA steps)
 constexpr int kLmXPitch = kLmKc * 2 + 16;                // bytes per staged hidden row (padded)
 constexpr int kLmMaxNB = 8;                              // 16-node blocks per slice (128 nodes)
@@ -62,24 +61,28 @@ struct LmParams {
   int n_slabs, n_slices;
 };
 
-template <int NB>
+// A wave owns VB blocks of 16 vocabulary rows (VB = 4 up to 112 nodes, 3 at
+// 128: its accumulators, both weight slots and the hidden fragments then fit
+// in 256 registers), a workgroup kLmWaves * 16 * VB rows.
+template <int NB, int VB>
 __global__ void __launch_bounds__(kLmThreads) lm_head_main(const LmParams p) {
+  constexpr int kRows = 16 * VB;
   __shared__ __attribute__((aligned(16))) unsigned char s_x[2][16 * NB * kLmXPitch];
   __shared__ uint64_t s_best[kLmWaves][16 * NB];
   const int slot = xcd_slot(blockIdx.x, p.n_slabs * p.n_slices);
   if (slot < 0) return;  // padding workgroup (whole block, before any barrier)
   const int slab = slot / p.n_slices;
   const int slice = slot % p.n_slices;
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave));
   const int lane = threadIdx.x % kWave;
   const int li = lane % 16, lg = lane / 16;
   const int n0 = slice * 16 * kLmMaxNB;
-  const int v_wave = slab * kLmSlab + wave * kLmRowsPerWave;
+  const int v_wave = slab * kLmWaves * kRows + wave * kRows;
 
   // weight rows of this lane (clamped into range; rows past V are ignored)
-  const unsigned char* wrow[4];
+  const unsigned char* wrow[VB];
 #pragma unroll
-  for (int vb = 0; vb < 4; ++vb) {
+  for (int vb = 0; vb < VB; ++vb) {
     const int v = min(v_wave + 16 * vb + li, p.V - 1);
     wrow[vb] = reinterpret_cast<const unsigned char*>(p.w + static_cast<int64_t>(v) * p.w_stride) + 16 * lg;
   }
@@ -99,14 +102,26 @@ __global__ void __launch_bounds__(kLmThreads) lm_head_main(const LmParams p) {
     *reinterpret_cast<u32x4*>(&s_x[buf][(t / 8) * kLmXPitch + 16 * (t % 8)]) = v;
   };
 
-  f32x4 acc[4][NB];
+  f32x4 acc[VB][NB];
 #pragma unroll
-  for (int vb = 0; vb < 4; ++vb)
+  for (int vb = 0; vb < VB; ++vb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[vb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int n_chunks = p.H / kLmKc;
-  // prologue: slice 0 of the hidden states into LDS, weight step 0 in flight
+  const int last = n_chunks - 1;
+  // Weight fragments in a two-slot register ring: slot c & 1 holds slice c's
+  // and is refilled with slice c + 2's as soon as slice c's MFMAs have been
+  // issued, so no loaded register is copied from one slice to the next (a
+  // copy of a register still loading would wait for that load, exposing its
+  // latency every slice). The slice loop is unrolled by two so that the slot
+  // index is known at compile time; past the last slice the refill re-reads
+  // it (in bounds, never used).
+  u32x4 wr[2][2][VB];
+  auto w_load = [&](int c, int h, int vb) {
+    return *reinterpret_cast<const u32x4*>(wrow[vb] + c * (kLmKc * 2) + 64 * h);
+  };
+  // prologue: slice 0 of the hidden states into LDS, weight slices 0 and 1 in flight
   u32x4 xs[kPiecesPerThread];
 #pragma unroll
   for (int r = 0; r < kPiecesPerThread; ++r)
@@ -114,61 +129,72 @@ __global__ void __launch_bounds__(kLmThreads) lm_head_main(const LmParams p) {
 #pragma unroll
   for (int r = 0; r < kPiecesPerThread; ++r)
     if (threadIdx.x + kLmThreads * r < kPieces) x_store(0, r, xs[r]);
-  u32x4 wcur[2][4];
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
+  for (int q = 0; q < 2; ++q)
 #pragma unroll
-    for (int vb = 0; vb < 4; ++vb) wcur[h][vb] = *reinterpret_cast<const u32x4*>(wrow[vb] + 64 * h);
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) wr[q][h][vb] = w_load(min(q, last), h, vb);
   __syncthreads();
 
-  for (int c = 0; c < n_chunks; ++c) {
-    const int buf = c & 1;
+  auto step = [&](int c, auto slot_tag) __attribute__((always_inline)) {
+    constexpr int Q = decltype(slot_tag)::value;  // == c & 1
+    const int buf = Q;
     const bool more = c + 1 < n_chunks;
-    // next slice: hidden pieces and weight fragments in flight
-    u32x4 wnext[2][4];
+    // next slice's hidden pieces in flight
     if (more) {
 #pragma unroll
       for (int r = 0; r < kPiecesPerThread; ++r)
         if (threadIdx.x + kLmThreads * r < kPieces) xs[r] = x_piece(c + 1, r);
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int vb = 0; vb < 4; ++vb)
-          wnext[h][vb] = *reinterpret_cast<const u32x4*>(wrow[vb] + (c + 1) * (kLmKc * 2) + 64 * h);
     }
-    // two 32-k steps on the current slice
+    // two 32-k steps on the current slice, one hidden fragment at a time:
+    // fragment f + 1 is read while fragment f multiplies, and a scheduling
+    // barrier closes each fragment, so the compiler cannot hoist all the
+    // reads (their registers would not fit beside the accumulators and both
+    // weight slots)
+    auto x_frag = [&](int f) {
+      const int h = f / NB, nb = f % NB;
+      return __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(&s_x[buf][(16 * nb + li) * kLmXPitch + 64 * h + 16 * lg]));
+    };
+    bf16x8 xf = x_frag(0);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      bf16x8 xf[NB];
+    for (int f = 0; f < 2 * NB; ++f) {
+      const int h = f / NB, nb = f % NB;
+      const bf16x8 xn = f + 1 < 2 * NB ? x_frag(f + 1) : xf;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        xf[nb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                                &s_x[buf][(16 * nb + li) * kLmXPitch + 64 * h + 16 * lg]));
-#pragma unroll
-      for (int vb = 0; vb < 4; ++vb) {
-        const bf16x8 wf = __builtin_bit_cast(bf16x8, wcur[h][vb]);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[vb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xf[nb], acc[vb][nb], 0, 0, 0);
-      }
+      for (int vb = 0; vb < VB; ++vb)
+        acc[vb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wr[Q][h][vb]), xf,
+                                                              acc[vb][nb], 0, 0, 0);
+      xf = xn;
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // the slot refilled with slice c + 2
+    const int c2 = min(c + 2, last);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) wr[Q][h][vb] = w_load(c2, h, vb);
     if (more) {
 #pragma unroll
       for (int r = 0; r < kPiecesPerThread; ++r)
         if (threadIdx.x + kLmThreads * r < kPieces) x_store(buf ^ 1, r, xs[r]);
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int vb = 0; vb < 4; ++vb) wcur[h][vb] = wnext[h][vb];
     }
     __syncthreads();
+  };
+  int c = 0;
+  for (; c + 1 < n_chunks; c += 2) {
+    step(c, std::integral_constant<int, 0>{});
+    step(c + 1, std::integral_constant<int, 1>{});
   }
+  if (c < n_chunks) step(c, std::integral_constant<int, 0>{});
 
   // epilogue: node 16 nb + li's best over the lane's rows 16 vb + 4 lg + j
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     uint64_t best = 0;
 #pragma unroll
-    for (int vb = 0; vb < 4; ++vb)
+    for (int vb = 0; vb < VB; ++vb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int v = v_wave + 16 * vb + 4 * lg + j;
@@ -223,7 +249,7 @@ __global__ void __launch_bounds__(kLmThreads) lm_head_main(const LmParams p) {
 // block's MFMAs, so only two blocks of partial sums are live. Workgroups are
 // 8 waves (256 vocabulary rows).
 constexpr int kLmQ4MaxNB = 8;
-constexpr int kLmQ4Slab = 4 * kLmRowsPerWave;              // vocabulary rows per workgroup (256), for the workspace
+constexpr int kLmQ4Slab = 256;                             // vocabulary rows per workgroup, for the workspace
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // byte B of x as a float (v_cvt_f32_ubyte<B>: one instruction, where the
@@ -593,7 +619,13 @@ __global__ void __launch_bounds__(kWave) lm_head_reduce(const uint64_t* __restri
   if (threadIdx.x == 0) out_idx[n] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(best));
 }
 
-static int lm_slabs(int64_t vocab) { return static_cast<int>((vocab + kLmSlab - 1) / kLmSlab); }
+// row blocks per wave for a call of n_rows nodes (the node blocks of its
+// first slice decide), and the vocabulary slabs of kLmWaves such waves
+static int lm_vb(int64_t n_rows) { return n_rows > 16 * (kLmMaxNB - 1) ? 3 : kLmMaxVB; }
+static int lm_slabs(int64_t n_rows, int64_t vocab) {
+  const int64_t rows = int64_t{kLmWaves} * 16 * lm_vb(n_rows);
+  return static_cast<int>((vocab + rows - 1) / rows);
+}
 
 }  // namespace ttv
 
@@ -601,7 +633,7 @@ using namespace ttv;
 
 extern "C" size_t lm_head_argmax_ws(int64_t n_rows, int64_t vocab) {
   if (n_rows <= 0 || vocab <= 0) return 0;
-  return static_cast<size_t>(n_rows) * lm_slabs(vocab) * sizeof(uint64_t);
+  return static_cast<size_t>(n_rows) * lm_slabs(n_rows, vocab) * sizeof(uint64_t);
 }
 
 extern "C" ttv_status lm_head_argmax(const uint16_t* hidden, int64_t n_rows, int64_t hidden_stride,
@@ -634,7 +666,7 @@ extern "C" ttv_status lm_head_argmax(const uint16_t* hidden, int64_t n_rows, int
   p.N = static_cast<int>(n_rows);
   p.V = static_cast<int>(vocab);
   p.H = static_cast<int>(hidden_dim);
-  p.n_slabs = lm_slabs(vocab);
+  p.n_slabs = lm_slabs(n_rows, vocab);
   p.n_slices = static_cast<int>((n_rows + 16 * kLmMaxNB - 1) / (16 * kLmMaxNB));
   const int64_t n_wg = static_cast<int64_t>(p.n_slabs) * p.n_slices;
   TTV_REQUIRE(n_wg <= (1ll << 30), TTV_ERR_INVALID, "lm_head_argmax: too many workgroups");
@@ -645,7 +677,7 @@ extern "C" ttv_status lm_head_argmax(const uint16_t* hidden, int64_t n_rows, int
   hipStream_t s = (hipStream_t)stream;
   switch (nb) {
 #define TTV_LM(NB) \
-  case NB: hipLaunchKernelGGL(lm_head_main<NB>, dim3(grid), dim3(kLmThreads), 0, s, p); break;
+  case NB: hipLaunchKernelGGL((lm_head_main<NB, NB == kLmMaxNB ? 3 : kLmMaxVB>), dim3(grid), dim3(kLmThreads), 0, s, p); break;
     TTV_LM(1) TTV_LM(2) TTV_LM(3) TTV_LM(4) TTV_LM(5) TTV_LM(6) TTV_LM(7) TTV_LM(8)
 #undef TTV_LM
     default: return fail(TTV_ERR_INVALID, "lm_head_argmax: internal node-block count");
