@@ -395,10 +395,6 @@ __global__ void __launch_bounds__(NW * kWave) lm_head_q4_main(const LmQ4Params p
   for (int vb = 0; vb < VB; ++vb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[vb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // acc += bias (rows x groups) . X (groups x nodes) over groups g0 .. g0 + 31
-  // (those past G are zero): A = the wave's biases (lane (i, g) holds row i,
-  // groups g0 + 8 g .. + 7), B = X as its three bf16 terms (lane (i, g) holds
-  // node i's groups g0 + 8 g .. + 7)
   // Stages the group sums of the chunk starting at g0 (groups g0 .. g0 + 31
   // of the padded planes, in bounds) into s_xg with direct global -> LDS
   // loads, no registers: load j of the workgroup fills slots 64 j .. +63,
@@ -414,6 +410,10 @@ __global__ void __launch_bounds__(NW * kWave) lm_head_q4_main(const LmQ4Params p
       dma16v_at(p.xg + (static_cast<size_t>(sp) * p.N + n) * p.Gp + g0 + 8 * part, base + 1024 * j);
     }
   };
+  // acc += bias (rows x groups) . X (groups x nodes) over groups g0 .. g0 + 31
+  // (those past G are zero): A = the wave's biases (lane (i, g) holds row i,
+  // groups g0 + 8 g .. + 7), B = X as its three bf16 terms (lane (i, g) holds
+  // node i's groups g0 + 8 g .. + 7)
   auto bias_chunk = [&](int g0) {
     bf16x8 bf[VB];
 #pragma unroll
