@@ -84,6 +84,9 @@ def check(got, hb, wb, rows):
 SMALL = [  # (N, H, V)
     (1, 64, 1), (5, 128, 17), (16, 64, 511), (16, 640, 512), (40, 128, 513), (128, 256, 5000), (130, 64, 3000),
     (300, 128, 1500), (7, 1024, 4096 + 77),
+    # up to 112 nodes a workgroup covers 512 vocabulary rows, above that 384:
+    # both sides of the switch, with vocabularies ending inside a slab
+    (112, 192, 1500), (113, 192, 1500), (127, 128, 385), (97, 64, 513),
 ]
 
 
