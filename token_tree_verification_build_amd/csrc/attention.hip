@@ -69,6 +69,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kMfmaMaxRB = 6;   // row blocks of 16 per MFMA row chunk (96 rows, two waves)
 constexpr int kI8MaxRB = 5;     // int8: both waves of a pair hold all row blocks (80 rows)
@@ -446,11 +447,13 @@ __device__ __forceinline__ void wait_vmcnt_tiles(int ahead) {
 // LDS layout of a staged K or V tile: 32 rows of RBYTES, 16-byte chunks. The
 // logical chunk c of row r sits at physical chunk c ^ swz(r), chosen so that
 // the 16 rows one fragment read touches (rows 8a + 4kb + b) land in 16
-// different bank groups.
+// different bank groups; for int8 tiles also the 8 rows 8g .. 8g + 7 that one
+// transposed V read touches (a 128-byte row is half a bank row, so even and
+// odd rows take the two halves and the swizzle keeps each half's rows apart).
 template <bool I8>
 __device__ __forceinline__ int lds_swz(int r) {
-  if constexpr (I8) return ((r >> 3) & 3) | (((r >> 1) & 1) << 2);  // 8 chunks per 128-byte row
-  else return ((r >> 3) & 3) | ((r & 3) << 2);                      // 16 chunks per 256-byte row
+  if constexpr (I8) return ((r >> 1) & 3) ^ (((r >> 3) & 1) << 1) ^ (((r >> 4) & 1) << 2);  // 8 chunks per row
+  else return ((r >> 3) & 3) | ((r & 3) << 2);                                            // 16 chunks per row
 }
 
 __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, const void* lds) {
@@ -1296,48 +1299,41 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
   } else {
     // ------------------------------------------------------ value wave ----
     f32x4 o[8][RB], osum[RB];
-    // V tile t into registers: lane (i, g) reads V rows 8g + e, d = 8i ..
-    // 8i+7; the slot is free for the next DMA once these reads returned
+    // V tile t into registers, transposed by the read (ds_read_b64_tr_b8): the
+    // 16 lanes of lane group g address both 8-byte halves of chunk db of rows
+    // 8 g .. 8 g + 7 (lane r: row 8 g + r / 2, half r % 2) and lane i receives
+    // byte i % 8 of half i / 8 of each of those rows, so a[db] holds the codes
+    // of keys 8 g + e (byte e) at d = 16 db + i: one d-block of V^T. The slot
+    // is free for the next DMA once these reads returned.
     uint32_t a[8][2];
     auto load_v = [&](int t) {
-      const char* sl = vring_all[pair][t % SV];
+      const int r = 8 * lg + (li >> 1);
+      const char* rowp = vring_all[pair][t % SV] + r * RBYTES + 8 * (li & 1);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int r = 8 * lg + e;
-        const u32x2 v2 = *reinterpret_cast<const u32x2*>(sl + r * RBYTES + 16 * ((li >> 1) ^ lds_swz<true>(r)) +
-                                                         8 * (li & 1));
-        a[e][0] = v2[0] ^ 0x80808080u;
-        a[e][1] = v2[1] ^ 0x80808080u;
+      for (int db = 0; db < 8; ++db) {
+        const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) i32x2*)(rowp + 16 * (db ^ lds_swz<true>(r))));
+        a[db][0] = static_cast<uint32_t>(x[0]) ^ 0x80808080u;
+        a[db][1] = static_cast<uint32_t>(x[1]) ^ 0x80808080u;
       }
       wait_lgkmcnt0();
     };
-    // O^T += V^T P'^T for the loaded tile from P buffer b
+    // O^T += V^T P'^T for the loaded tile from P buffer b: d-block db's V^T
+    // fragment is a[db] as fp16 of c + 1152, four d-blocks at a time
+    // (register budget: o holds 32 RB)
     auto accumulate = [&](int b) {
-      // V^T fragments (codes + 1152) of d-blocks 4hh .. 4hh + 3, half at a
-      // time (register budget: o holds 32 RB): d-block db = 4hh + j takes
-      // byte j of dword hh of keys e = 0..7
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        u32x4 vf[4];
-        uint32_t ilo[4], ihi[4];
+        f16x8 vf[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          ilo[k] = __builtin_amdgcn_perm(a[2 * k + 1][hh], a[2 * k][hh], 0x05010400u);  // a0 b0 a1 b1
-          ihi[k] = __builtin_amdgcn_perm(a[2 * k + 1][hh], a[2 * k][hh], 0x07030602u);  // a2 b2 a3 b3
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int k = 0; k < 4; ++k)
-            vf[j][k] = __builtin_amdgcn_perm(kExp64, j < 2 ? ilo[k] : ihi[k], (j & 1) ? 0x04030402u : 0x04010400u);
+        for (int j = 0; j < 4; ++j) vf[j] = i8x8_to_f16_biased(a[4 * hh + j][0], a[4 * hh + j][1]);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           const f16x8 pw = __builtin_bit_cast(f16x8, pbuf[b][rb * 64 + lane]);
           if (hh == 0) osum[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pw, osum[rb], 0, 0, 0);
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            o[4 * hh + j][rb] =
-                __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, vf[j]), pw, o[4 * hh + j][rb], 0, 0, 0);
+            o[4 * hh + j][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[j], pw, o[4 * hh + j][rb], 0, 0, 0);
         }
       }
     };
@@ -1412,17 +1408,13 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
   // them.
   const int nwg_unit = w.nsplit / NP;
   // Row-major stores, four consecutive d per thread (coalesced); o sits in LDS
-  // in the MFMA lane order: row 16 rb + i, d = 32 g + 8 r + db is element r of
-  // block (rb * 8 + db) * 64 + 16 g + i.
+  // in the MFMA lane order: row 16 rb + i, d = 16 db + 4 g + r is element r of
+  // block (rb * 8 + db) * 64 + 16 g + i, so four consecutive d are one block
+  // entry.
   for (int flat = 4 * threadIdx.x; flat < w.nrows * D; flat += 4 * 64 * NW) {
     const int rloc = flat / D, d0 = flat % D;
     const int rb = rloc >> 4, i = rloc & 15;
-    f32x4 v;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int d = d0 + u;
-      v[u] = mo[(rb * 8 + (d & 7)) * 64 + 16 * (d >> 5) + i][(d >> 3) & 3];
-    }
+    f32x4 v = mo[(rb * 8 + (d0 >> 4)) * 64 + 16 * ((d0 >> 2) & 3) + i];
     if (nwg_unit == 1) {
       const int row = w.row0 + rloc;
       const int node = w.o0 + row / p.G;
