@@ -116,6 +116,26 @@ __device__ __forceinline__ double exp_nonpos_f64(double t) {
   return ldexp(fma(d1, r8, d0), static_cast<int>(n));
 }
 
+// The same exponential with a finer reduction, for the chunk statistics (one
+// per logit): t = (64 q + j) ln2 / 64 + r with |r| <= ln2 / 128 (the same
+// split of ln2, scaled by 1/64, so k * ln2_hi / 64 stays exact for |k| up to
+// 2^21), e^t = 2^q * 2^(j/64) * e^r, e^r by its Taylor series through r^5 in
+// Horner form (the next term is below 4e-17 relative), 2^(j/64) from a
+// 64-entry table the caller fills with exp2_frac64 (a few ulp). About a third
+// of the instructions of exp_nonpos_f64.
+__device__ __forceinline__ double exp2_frac64(int j) {
+  return 2.0 * exp_nonpos_f64(static_cast<double>(j - 64) * (6.93147180559945309417e-01 / 64.0));
+}
+__device__ __forceinline__ double exp_nonpos_tab(double t, const double* __restrict__ tab) {
+  const double k = rint(t * (64.0 * 1.4426950408889634074));
+  const double r = fma(-k, 1.90821492927058770002e-10 / 64.0, fma(-k, 6.93147180369123816490e-01 / 64.0, t));
+  const int ki = static_cast<int>(k);
+  constexpr double f3 = 1.0 / 6, f4 = f3 / 4, f5 = f4 / 5;
+  const double e = fma(fma(fma(fma(fma(f5, r, f4), r, f3), r, 0.5), r, 1.0), r, 1.0);
+  const double v = ldexp(tab[ki & 63] * e, ki >> 6);
+  return t < -745.0 ? 0.0 : v;  // (k, and so ki, is not finite or out of range only here)
+}
+
 // Pass 1: wave w of workgroup (g, row) takes chunk c = 4g + w (of 64 *
 // PER_LANE values) of the row and writes its top k keys (in no particular
 // order; key 0, below every value, fills slots a short chunk cannot) to
@@ -128,11 +148,17 @@ __global__ void __launch_bounds__(kSelLanes * kSelWaves)
   static_assert(PER_LANE % 4 == 0 && PER_LANE <= kSelPerLane, "chunk of 64 * PER_LANE values");
   constexpr int kChunk = kSelLanes * PER_LANE;
   __shared__ uint64_t s_cand[kSelWaves][kSelCap];
+  __shared__ double s_exp_tab[kStats ? kSelWaves : 1][64];  // 2^(j/64), one copy per wave
   const int wave = threadIdx.x / kSelLanes;
   const int lane = threadIdx.x % kSelLanes;
   const int row = blockIdx.y;
   const int c = blockIdx.x * kSelWaves + wave;
   if (c >= n_chunks) return;  // whole wave; pass 1 has no workgroup barrier
+  const double* tab = s_exp_tab[kStats ? wave : 0];
+  if constexpr (kStats) {  // the wave's own table: its LDS writes precede its reads
+    s_exp_tab[wave][lane] = exp2_frac64(lane);
+    __builtin_amdgcn_wave_barrier();
+  }
   const float* __restrict__ x = logits + static_cast<int64_t>(row) * row_stride;
   const int64_t c0 = static_cast<int64_t>(c) * kChunk;
   auto idx_of = [&](int j) -> uint32_t { return static_cast<uint32_t>(c0 + 4 * (64 * (j >> 2) + lane) + (j & 3)); };
@@ -173,7 +199,7 @@ __global__ void __launch_bounds__(kSelLanes * kSelWaves)
       const bool bad = lnan || lmf == INFINITY || lmin == -INFINITY;
       double sum = 0.0;
 #pragma unroll
-      for (int j = 0; j < PER_LANE; ++j) sum += exp_nonpos_f64(static_cast<double>(xf[j]) - m);
+      for (int j = 0; j < PER_LANE; ++j) sum += exp_nonpos_tab(static_cast<double>(xf[j]) - m, tab);
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
       const bool any_bad = __ballot(bad) != 0;
@@ -279,7 +305,7 @@ __global__ void __launch_bounds__(kSelLanes * kSelWaves)
 #pragma unroll
     for (int j = 0; j < PER_LANE; ++j) {
       bad |= ov[j] >= 0xFF800000u || ov[j] == 0x007FFFFFu;
-      if (ov[j]) s += exp_nonpos_f64(static_cast<double>(key_value(static_cast<uint64_t>(ov[j]) << 32)) - m);
+      if (ov[j]) s += exp_nonpos_tab(static_cast<double>(key_value(static_cast<uint64_t>(ov[j]) << 32)) - m, tab);
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
