@@ -476,6 +476,48 @@ def test_attention_query_magnitudes(ttv, kv, qscale):
     _attn_check(ttv, spec, {"layers": [layer]}, TOL_BF16, label=f"qscale {qscale} {kv}")
 
 
+@pytest.mark.parametrize("spread", [2, 4])
+def test_int8_spread_scales_error_relative_to_abs_values(ttv, spread):
+    """int8 KV whose per-token k- and v-scales spread log-uniformly over a
+    factor 2^spread within each head (outputs up to ~15 instead of ~3):
+    P and P' = P * v_scale are rounded to fp16, so the error of an output
+    row is bounded relative to the largest element of sum_j p_j |v_j|, the
+    attention of |V| (the oracle run on the codes' absolute values), not
+    absolutely."""
+    from workloads.configs import _spec
+    r = rng_for(1270, spread)
+    B, Hq, Hkv, D = 6, 40, 8, 128
+    parents = [confidence_tree(rng_for(1271, spread, b), 16, 8, 1000, 4)[0] for b in range(B)]
+    hist = [int(r.integers(0, 1200)) for _ in range(B)]
+    spec = _spec(1270, B, 1, Hq, Hkv, D, 16, 1.0, "i8", "bf16", hist, parents, [np.zeros(16, np.int64)] * B,
+                 [np.zeros(16, np.int64)] * B, [[0]] * B)
+    layer = make_kv_cache(1272, spread, B, Hkv, spec.cap, D, "i8")
+    for n in ("k_scale", "v_scale"):
+        f = np.exp2(r.uniform(-spread / 2, spread / 2, layer[n].shape))
+        layer[n] = (layer[n].astype(np.float64) * f).astype(np.float16)
+    layer["q"] = make_queries(1273, spread, spec.n_nodes, Hq, D, "bf16")
+    batch = spec_batch(ttv, spec)
+    anc, _, st = run_mask(ttv, batch, to_dev(spec.flat("parents")))
+    dev, kvl = layer_to_dev(ttv, layer)
+    out, _ = run_attention(ttv, batch, to_dev(layer["q"], "bf16"), kvl, anc, 1 / math.sqrt(D))
+    torch.cuda.synchronize()
+    kv = {k: v for k, v in layer.items() if k != "q"}
+    want = O.tree_verify_attention(layer["q"], kv, spec.node_off, spec.hist_len, spec.parents, 1 / math.sqrt(D),
+                                   "bf16", "i8")
+    absv = dict(kv, v=np.abs(kv["v"].astype(np.int16)).astype(np.int8))
+    cond = O.tree_verify_attention(layer["q"], absv, spec.node_off, spec.hist_len, spec.parents, 1 / math.sqrt(D),
+                                   "bf16", "i8")
+    g = to_host(out)
+    assert np.isfinite(g).all() and int(st.item()) == 0
+    # per output row: the largest element of the attention of |V| (an element
+    # whose dominant keys hold code 0 is itself near zero, and the keys whose
+    # fp16 P' underflows still leave an error of that row's scale)
+    rel = float((np.abs(g - want) / np.maximum(cond.max(axis=2, keepdims=True), 1e-30)).max())
+    log(f"int8 scales spread 2^{spread}: max|out| {np.abs(want).max():.3e}, max|err| {np.abs(g - want).max():.3e}, "
+        f"max err / (attention of |V|) {rel:.3e}")
+    assert rel <= TOL_BF16
+
+
 def _oracle_node_rows(slab: dict, kv: str, qrows, P: int, parent, t: int, scale: float):
     """The oracle's attention rows of one node and one KV head from that
     head's cache slab ({'k','v'[, scales]} [P + T, D] / [P + T]): the node's
