@@ -245,11 +245,11 @@ ttv_status sliding_mask_from_caller(const float* caller, int32_t T, int32_t S, i
  * (bf16 / int8 KV) and 1e-5 (fp32) on N(0,1) keys and values with queries
  * N(0, s^2), s from 1e-6 to 300 (tested). The probabilities P and, for int8
  * KV, P' = P * v_scale are fp16, so in general the error of an output row
- * scales with sum_j p_j |v_j|: with int8 per-token scales that spread over
- * a factor 16 within a head it stays below 2e-3 of that row's largest
- * element (tested); wider spreads lose more (measured ~3e-3 at 64x, ~2e-2
- * at 65536x), because a pass that raises a row's reference after an fp16
- * overflow shrinks P' of small-v-scale keys toward fp16's subnormal range.
+ * scales with sum_j p_j |v_j|: with int8 per-token k- and v-scales that
+ * spread over a factor up to 2^12 within a head it stays below 2e-3 of that
+ * row's largest element (tested at 2^4, 2^8, 2^12; measured ~6e-4); at
+ * 2^16 it reached 4e-3 (P' overflows then, and the rows lowered to bring it
+ * back into range lose fp16 precision).
  * Concurrent calls on one GPU must not share a workspace.
  */
 size_t tree_verify_attention_ws(const ttv_batch* batch, int32_t Hq, const ttv_kv_layer* layer,

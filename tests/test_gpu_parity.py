@@ -476,10 +476,10 @@ def test_attention_query_magnitudes(ttv, kv, qscale):
     _attn_check(ttv, spec, {"layers": [layer]}, TOL_BF16, label=f"qscale {qscale} {kv}")
 
 
-@pytest.mark.parametrize("spread", [2, 4])
+@pytest.mark.parametrize("spread", [4, 8, 12])
 def test_int8_spread_scales_error_relative_to_abs_values(ttv, spread):
     """int8 KV whose per-token k- and v-scales spread log-uniformly over a
-    factor 2^spread within each head (outputs up to ~15 instead of ~3):
+    factor 2^spread within each head (outputs up to ~200 instead of ~3):
     P and P' = P * v_scale are rounded to fp16, so the error of an output
     row is bounded relative to the largest element of sum_j p_j |v_j|, the
     attention of |V| (the oracle run on the codes' absolute values), not

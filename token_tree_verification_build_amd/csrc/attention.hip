@@ -1272,12 +1272,16 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
       const bool redo = __syncthreads_or(bad || past) && attempt + 1 < kMaxAttempts;
       if (!redo) break;
       if (attempt > 0) {
-        // raise the rows that went past the bound; an overflow with none of
-        // them came from P * v_scale: lower every row of this split
+        // raise the rows that went past the bound to put each row's largest
+        // score at the usual kMargin below its reference (the scores are
+        // recomputed identically, so neither P nor P' can overflow again,
+        // and P' of small-v-scale keys keeps the first pass's distance from
+        // fp16's subnormal range); an overflow with none of them came from
+        // P * v_scale: lower every row of this split by the growing margin
         const bool lower_all = !past && (__ballot(bad) != 0 || s_bad[pair] != 0);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-          if (__ballot(mx[rb] > 6.0f) != 0) negm[rb] -= mx[rb] + margin;
+          if (__ballot(mx[rb] > 6.0f) != 0) negm[rb] -= mx[rb] + kMargin;
           else if (lower_all) negm[rb] -= margin;
         }
       }
