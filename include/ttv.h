@@ -241,8 +241,10 @@ ttv_status sliding_mask_from_caller(const float* caller, int32_t T, int32_t S, i
  * -1152 * sum_d q_d while every row of the chunk has
  * sum_d |q_d| * softmax_scale * log2(e) <= 128; past that they are converted
  * to c exactly and the accumulators start at zero. Requires Hq % Hkv == 0,
- * cap >= P_b + T_b. Accuracy against float64: max-abs error below 2e-3
- * (bf16 / int8 KV) and 1e-5 (fp32) on N(0,1) keys and values with queries
+ * cap >= P_b + T_b; cache rows (and scales) past P_b + T_b are never part of
+ * the result and may hold anything, non-finite values included (tested).
+ * Accuracy against float64: max-abs error below 2e-3 (bf16 / int8 KV) and
+ * 1e-5 (fp32) on N(0,1) keys and values with queries
  * N(0, s^2), s from 1e-6 to 300 (tested). The probabilities P and, for int8
  * KV, P' = P * v_scale are fp16, so in general the error of an output row
  * scales with sum_j p_j |v_j|: with int8 per-token k- and v-scales that

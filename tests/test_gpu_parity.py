@@ -518,6 +518,51 @@ def test_int8_spread_scales_error_relative_to_abs_values(ttv, spread):
     assert rel <= TOL_BF16
 
 
+@pytest.mark.parametrize("kv,D", [("i8", 128), ("bf16", 128), ("i8", 64), ("f32", 64)])
+def test_attention_ignores_cache_rows_past_live_length(ttv, kv, D):
+    """Cache rows past each sequence's P_b + T_b are not part of the call:
+    filled with NaN / infinity (scales, bf16 and fp32 values) or arbitrary
+    codes, they must leave the output finite and equal to the oracle's, which
+    never reads them. Boundary tiles load whole 8-key scale groups and clamp
+    code rows, so those rows do reach the kernels' registers."""
+    from workloads.configs import _spec
+    r = rng_for(1290, D, {"i8": 0, "bf16": 1, "f32": 2}[kv])
+    B, Hq, Hkv = 3, (40 if kv != "f32" else 4), (8 if kv != "f32" else 2)
+    parents = [confidence_tree(rng_for(1291, b), 16, 8, 1000, 4)[0] for b in range(B)]
+    hist = [37, 130, 203]
+    spec = _spec(1290, B, 1, Hq, Hkv, D, 16, 1.0, kv, "f32" if kv == "f32" else "bf16", hist, parents,
+                 [np.zeros(16, np.int64)] * B, [np.zeros(16, np.int64)] * B, [[0]] * B)
+    cap = spec.cap + 45
+    layer = make_kv_cache(1292, D, B, Hkv, cap, D, kv)
+    layer["q"] = make_queries(1293, D, spec.n_nodes, Hq, D, "f32" if kv == "f32" else "bf16")
+    host = {k: v.copy() for k, v in layer.items()}
+    for b in range(B):
+        live = hist[b] + 16
+        for n in ("k", "v"):
+            if kv == "i8":
+                host[n][b, :, live:] = r.integers(-127, 128, host[n][b, :, live:].shape, dtype=np.int8)
+                sc = host[n + "_scale"].view(np.uint16)
+                sc[b, :, live:] = np.where(r.integers(0, 2, sc[b, :, live:].shape) == 0, 0x7C00, 0x7E00)
+            elif kv == "bf16":
+                host[n][b, :, live:] = 0x7FC0
+            else:
+                host[n][b, :, live:] = np.float32(np.nan)
+    batch = spec_batch(ttv, spec)
+    anc, _, st = run_mask(ttv, batch, to_dev(spec.flat("parents")))
+    dev, kvl = layer_to_dev(ttv, host)
+    q = to_dev(host["q"], None if kv == "f32" else "bf16")
+    out, _ = run_attention(ttv, batch, q, kvl, anc, 1 / math.sqrt(D))
+    torch.cuda.synchronize()
+    want = O.tree_verify_attention(layer["q"], {k: v for k, v in layer.items() if k != "q"}, spec.node_off,
+                                   spec.hist_len, spec.parents, 1 / math.sqrt(D), "f32" if kv == "f32" else "bf16",
+                                   kv)
+    g = to_host(out)
+    assert np.isfinite(g).all(), f"{kv}: non-finite output from rows past the live length"
+    err = float(np.abs(g - want).max())
+    log(f"garbage past live length {kv} D={D}: max|err| {err:.3e}")
+    assert err <= (TOL_F32 if kv == "f32" else TOL_BF16)
+
+
 def _oracle_node_rows(slab: dict, kv: str, qrows, P: int, parent, t: int, scale: float):
     """The oracle's attention rows of one node and one KV head from that
     head's cache slab ({'k','v'[, scales]} [P + T, D] / [P + T]): the node's

@@ -1141,6 +1141,16 @@ __global__ void __launch_bounds__(512) attn_i8_split_kernel(const AttnParams p) 
       const char* sl = kring_all[pair][t % SK];
       const u32x4 ksc = scales(sl, t0, 0);
       vsc = scales(sl, t0, 64);
+      if (decltype(masked)::value && mode != 0) {
+        // keys at or past the range end (cache rows past the live length
+        // among them, whose scales may hold anything) take v-scale 0: their
+        // P is 0, and 0 * inf or 0 * NaN would not be
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const int key = t0 + 8 * lg + 2 * h;
+          vsc[h] &= (key < limit ? 0x0000FFFFu : 0u) | (key + 1 < limit ? 0xFFFF0000u : 0u);
+        }
+      }
       float kss[8];  // score scale of key 8g + e, log2 units
 #pragma unroll
       for (int e = 0; e < 8; ++e) kss[e] = static_cast<float>(__builtin_bit_cast(f16x8, ksc)[e]) * sl2;
