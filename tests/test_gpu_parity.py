@@ -518,8 +518,9 @@ def test_int8_spread_scales_error_relative_to_abs_values(ttv, spread):
     assert rel <= TOL_BF16
 
 
-@pytest.mark.parametrize("kv,D", [("i8", 128), ("bf16", 128), ("i8", 64), ("f32", 64)])
-def test_attention_ignores_cache_rows_past_live_length(ttv, kv, D):
+@pytest.mark.parametrize("kv,D,T", [("i8", 128, 16), ("bf16", 128, 16), ("bf16", 128, 40), ("i8", 64, 16),
+                                    ("f32", 64, 16)])
+def test_attention_ignores_cache_rows_past_live_length(ttv, kv, D, T):
     """Cache rows past each sequence's P_b + T_b are not part of the call:
     filled with NaN / infinity (scales, bf16 and fp32 values) or arbitrary
     codes, they must leave the output finite and equal to the oracle's, which
@@ -528,16 +529,16 @@ def test_attention_ignores_cache_rows_past_live_length(ttv, kv, D):
     from workloads.configs import _spec
     r = rng_for(1290, D, {"i8": 0, "bf16": 1, "f32": 2}[kv])
     B, Hq, Hkv = 3, (40 if kv != "f32" else 4), (8 if kv != "f32" else 2)
-    parents = [confidence_tree(rng_for(1291, b), 16, 8, 1000, 4)[0] for b in range(B)]
+    parents = [confidence_tree(rng_for(1291, b), T, 8, 1000, 4)[0] for b in range(B)]
     hist = [37, 130, 203]
     spec = _spec(1290, B, 1, Hq, Hkv, D, 16, 1.0, kv, "f32" if kv == "f32" else "bf16", hist, parents,
-                 [np.zeros(16, np.int64)] * B, [np.zeros(16, np.int64)] * B, [[0]] * B)
+                 [np.zeros(T, np.int64)] * B, [np.zeros(T, np.int64)] * B, [[0]] * B)
     cap = spec.cap + 45
     layer = make_kv_cache(1292, D, B, Hkv, cap, D, kv)
     layer["q"] = make_queries(1293, D, spec.n_nodes, Hq, D, "f32" if kv == "f32" else "bf16")
     host = {k: v.copy() for k, v in layer.items()}
     for b in range(B):
-        live = hist[b] + 16
+        live = hist[b] + T
         for n in ("k", "v"):
             if kv == "i8":
                 host[n][b, :, live:] = r.integers(-127, 128, host[n][b, :, live:].shape, dtype=np.int8)
@@ -559,7 +560,7 @@ def test_attention_ignores_cache_rows_past_live_length(ttv, kv, D):
     g = to_host(out)
     assert np.isfinite(g).all(), f"{kv}: non-finite output from rows past the live length"
     err = float(np.abs(g - want).max())
-    log(f"garbage past live length {kv} D={D}: max|err| {err:.3e}")
+    log(f"garbage past live length {kv} D={D} T={T}: max|err| {err:.3e}")
     assert err <= (TOL_F32 if kv == "f32" else TOL_BF16)
 
 
