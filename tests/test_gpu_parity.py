@@ -286,6 +286,22 @@ def test_gather_matches_oracle(ttv, dtype, D, in_place, kind):
 
 
 @pytest.mark.parametrize("in_place", [True, False])
+def test_gather_more_layers_than_one_launch(ttv, in_place):
+    """37 layers: the copies run as launches of 16 layers each (16, 16, 5)
+    after one validation, every layer gathered as the oracle's take."""
+    rng = rng_for(1185, int(in_place))
+    B, cap, L = 3, 300, 37
+    live = np.array([cap - 3 * b for b in range(B)])
+    sels = _selections(rng, live, "rollback")
+    host, base, got, st, live = _gather_case(ttv, "i8", in_place, sels, B=B, L=L, D=64, cap=cap)
+    assert st == 0
+    for l in range(L):
+        want = O.gather_layer(dict(host[l]), sels, base=base[l])
+        for n in want:
+            np.testing.assert_array_equal(got[l][n], want[n], err_msg=f"layer {l} {n}")
+
+
+@pytest.mark.parametrize("in_place", [True, False])
 def test_gather_bad_selection_writes_nothing(ttv, in_place):
     rng = rng_for(1190)
     live = np.array([700, 697, 694])

@@ -380,6 +380,11 @@ extern "C" ttv_status kv_gather_positions(const ttv_kv_layer* src, const ttv_kv_
   int chunk = (max_n + kMaxSelChunks - 1) / kMaxSelChunks;
   chunk = chunk < kMinSelChunk ? kMinSelChunk : (chunk + 255) / 256 * 256;
   const int nch = max_n == 0 ? 1 : (max_n + chunk - 1) / chunk;
+  // the largest copy grid (a launch of kLayersPerLaunch layers), checked before anything is launched
+  const int take_chunks = (max_live + kTakeRows - 1) / kTakeRows;
+  const int64_t max_grid = static_cast<int64_t>(n_layers < kLayersPerLaunch ? n_layers : kLayersPerLaunch) * B *
+                           L0.Hkv * (in_place ? 1 : take_chunks);
+  TTV_REQUIRE(max_grid <= 0x7FFFFFFF, TTV_ERR_INVALID, "kv_gather_positions: grid too large");
   hipStream_t st = (hipStream_t)stream;
   LiveLens lens{};
   for (int b = 0; b < B; ++b) lens.live[b] = live_len_h[b];
@@ -405,16 +410,14 @@ extern "C" ttv_status kv_gather_positions(const ttv_kv_layer* src, const ttv_kv_
       P.dvs[i] = a.dtype == TTV_I8 ? d.v_scale : nullptr;
     }
     if (in_place) {
-      const int64_t nblk = static_cast<int64_t>(nl) * B * L0.Hkv;
-      TTV_REQUIRE(nblk <= 0x7FFFFFFF, TTV_ERR_INVALID, "kv_gather_positions: grid too large");
+      const int64_t nblk = static_cast<int64_t>(nl) * B * L0.Hkv;  // <= max_grid
       // at most 4 pieces of 16 B per buffer per thread: 1024 rows of int8 D=64 ... 32 rows of f32 D=512
       hipLaunchKernelGGL((compact_kernel<4, false>), dim3(static_cast<unsigned>(nblk)), dim3(kGatherThreads), 0, st, P,
                          B, L0.Hkv, L0.cap, row_bytes, sel, sel_stride, sel_len, j0s, bad, nullptr);
     } else {
-      const int chunks = (max_live + kTakeRows - 1) / kTakeRows;
+      const int chunks = take_chunks;
       if (chunks == 0) continue;
-      const int64_t nblk = static_cast<int64_t>(nl) * B * L0.Hkv * chunks;
-      TTV_REQUIRE(nblk <= 0x7FFFFFFF, TTV_ERR_INVALID, "kv_gather_positions: grid too large");
+      const int64_t nblk = static_cast<int64_t>(nl) * B * L0.Hkv * chunks;  // <= max_grid
       hipLaunchKernelGGL(take_kernel, dim3(static_cast<unsigned>(nblk)), dim3(kGatherThreads), 0, st, P, B, L0.Hkv,
                          L0.cap, row_bytes, chunks, sel, sel_stride, sel_len, bad);
     }
