@@ -486,6 +486,9 @@ extern "C" ttv_status kv_gather_within_tail(const ttv_kv_layer* layers, int32_t 
   int32_t* ends = j0s + B;
   int32_t* starts = ends + B;
   int32_t* bad = starts + B;
+  TTV_REQUIRE(static_cast<int64_t>(n_layers < kLayersPerLaunch ? n_layers : kLayersPerLaunch) * B * L0.Hkv <=
+                  0x7FFFFFFF,
+              TTV_ERR_INVALID, "kv_gather_within_tail: grid too large");
   hipStream_t st = (hipStream_t)stream;
   hipLaunchKernelGGL(tail_validate_kernel, dim3(B), dim3(kWave), 0, st, kept, kept_stride, kept_len, tails, j0s,
                      ends, starts, bad, dev_status);
@@ -505,8 +508,7 @@ extern "C" ttv_status kv_gather_within_tail(const ttv_kv_layer* layers, int32_t 
       P.dks[i] = P.ks[i] ? a.k_scale : nullptr;
       P.dvs[i] = P.vs[i] ? a.v_scale : nullptr;
     }
-    const int64_t nblk = static_cast<int64_t>(nl) * B * L0.Hkv;
-    TTV_REQUIRE(nblk <= 0x7FFFFFFF, TTV_ERR_INVALID, "kv_gather_within_tail: grid too large");
+    const int64_t nblk = static_cast<int64_t>(nl) * B * L0.Hkv;  // checked above
     hipLaunchKernelGGL((compact_kernel<4, true>), dim3(static_cast<unsigned>(nblk)), dim3(kGatherThreads), 0, st, P,
                        B, L0.Hkv, L0.cap, row_bytes, kept, kept_stride, ends, j0s, bad, starts);
     s = check_launch("kv_gather_within_tail copy");

@@ -738,21 +738,21 @@ extern "C" ttv_status lm_head_q4_argmax(const uint16_t* hidden, int64_t n_rows, 
   p.V = static_cast<int>(vocab);
   p.H = static_cast<int>(hidden_dim);
   p.Gp = lm_q4_gp(hidden_dim);
-  hipStream_t s = (hipStream_t)stream;
-  {
-    const int64_t n_sums = n_rows * p.Gp;
-    TTV_REQUIRE(n_sums <= (int64_t{1} << 36), TTV_ERR_INVALID, "lm_head_q4_argmax: too many group sums");
-    hipLaunchKernelGGL(lm_q4_group_sums, dim3(static_cast<unsigned>((n_sums + 255) / 256)), dim3(256), 0, s, hidden,
-                       hidden_stride, p.N, p.H / 64, p.Gp, const_cast<uint16_t*>(p.xg));
-    ttv_status st = check_launch("lm_head_q4_argmax group sums");
-    if (st != TTV_OK) return st;
-  }
   const int rows0 = static_cast<int>(n_rows < 16 * kLmQ4MaxNB ? n_rows : 16 * kLmQ4MaxNB);
   const int nb = (rows0 + 15) / 16;
   p.n_slabs = static_cast<int>((vocab + kLmQ4Slab - 1) / kLmQ4Slab);
   p.n_slices = static_cast<int>((n_rows + 16 * kLmQ4MaxNB - 1) / (16 * kLmQ4MaxNB));
   const int64_t n_wg = static_cast<int64_t>(p.n_slabs) * p.n_slices;
   TTV_REQUIRE(n_wg <= (1ll << 30), TTV_ERR_INVALID, "lm_head_q4_argmax: too many workgroups");
+  const int64_t n_sums = n_rows * p.Gp;
+  TTV_REQUIRE(n_sums <= (int64_t{1} << 36), TTV_ERR_INVALID, "lm_head_q4_argmax: too many group sums");
+  hipStream_t s = (hipStream_t)stream;
+  {
+    hipLaunchKernelGGL(lm_q4_group_sums, dim3(static_cast<unsigned>((n_sums + 255) / 256)), dim3(256), 0, s, hidden,
+                       hidden_stride, p.N, p.H / 64, p.Gp, const_cast<uint16_t*>(p.xg));
+    ttv_status st = check_launch("lm_head_q4_argmax group sums");
+    if (st != TTV_OK) return st;
+  }
   const unsigned grid = static_cast<unsigned>((n_wg + kNumXcd - 1) / kNumXcd * kNumXcd);
   switch (nb) {
 #define TTV_LMQ(NB, NW, VB) \
