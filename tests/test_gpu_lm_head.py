@@ -34,14 +34,14 @@ def ttv():
 def run(ttv, hb, wb, hs_pad=0, ws_pad=0):
     N, H = hb.shape
     V = wb.shape[0]
-    if hs_pad:
-        buf = np.zeros((N, H + hs_pad), np.uint16)
+    if hs_pad:  # the padding holds NaN: no element past H may be read
+        buf = np.full((N, H + hs_pad), 0x7FC0, np.uint16)
         buf[:, :H] = hb
         Xd = to_dev(buf, "bf16")[:, :H]
     else:
         Xd = to_dev(hb, "bf16")
     if ws_pad:
-        buf = np.zeros((V, H + ws_pad), np.uint16)
+        buf = np.full((V, H + ws_pad), 0x7FC0, np.uint16)
         buf[:, :H] = wb
         Wd = to_dev(buf, "bf16")[:, :H]
     else:
@@ -147,14 +147,19 @@ def test_full_size_sampled(ttv, N):
 from workloads import lm_head_q4_inputs, lm_head_q4_random  # noqa: E402
 
 
-def run_q4(ttv, hb, wq, sb):
-    N = hb.shape[0]
+def run_q4(ttv, hb, wq, sb, hs_pad=0):
+    N, H = hb.shape
     V = wq.shape[0]
+    if hs_pad:  # the padding holds NaN: no element past H may be read
+        buf = np.full((N, H + hs_pad), 0x7FC0, np.uint16)
+        buf[:, :H] = hb
+        Xd = to_dev(buf, "bf16")[:, :H]
+    else:
+        Xd = to_dev(hb, "bf16")
     out = torch.full((max(N, 1),), -3, dtype=torch.int32, device="cuda")
-    ws = zeros_ws(ttv.lm_head_q4_argmax_ws(N, V, hb.shape[1]))
+    ws = zeros_ws(ttv.lm_head_q4_argmax_ws(N, V, H))
     ws.fill_(0x5A)
-    ttv.lm_head_q4_argmax(to_dev(hb, "bf16"), torch.from_numpy(wq.view(np.int32)).to("cuda"),
-                          to_dev(sb, "bf16"), out, ws)
+    ttv.lm_head_q4_argmax(Xd, torch.from_numpy(wq.view(np.int32)).to("cuda"), to_dev(sb, "bf16"), out, ws)
     return to_host(out)[:N]
 
 
@@ -204,6 +209,13 @@ def test_q4_small_against_oracle(ttv, N, H, V):
     log(f"lm_head_q4 N={N} H={H} V={V}")
     hb, wq, sb = lm_head_q4_inputs(N * 3 + H + V, N, H, V)
     got = run_q4(ttv, hb, wq, sb)
+    assert check_q4(got, hb, wq, sb, list(range(N))) >= N // 2
+
+
+def test_q4_padded_hidden_stride(ttv):
+    N, H, V = 20, 192, 1000
+    hb, wq, sb = lm_head_q4_inputs(9, N, H, V)
+    got = run_q4(ttv, hb, wq, sb, hs_pad=40)
     assert check_q4(got, hb, wq, sb, list(range(N))) >= N // 2
 
 

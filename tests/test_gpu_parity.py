@@ -200,7 +200,7 @@ def test_argmax_ties_zero_nan_and_tails(ttv):
     _check_argmax(ttv, X, "ties/zero/nan")
     # unaligned row stride forces the scalar path
     Y = np.ascontiguousarray(X[:, :V - 3])
-    Yd = to_dev(np.ascontiguousarray(np.pad(Y, ((0, 0), (0, 1)))))
+    Yd = to_dev(np.ascontiguousarray(np.pad(Y, ((0, 0), (0, 1)), constant_values=np.nan)))  # never read
     out = torch.full((24,), -7, dtype=torch.int32, device="cuda")
     ttv.vocab_argmax(Yd, out, zeros_ws(ttv.vocab_argmax_ws(24, V - 3)), vocab=V - 3)
     np.testing.assert_array_equal(to_host(out), O.vocab_argmax(Y))

@@ -111,7 +111,7 @@ def test_sample_ties_nonfinite_and_unaligned(ttv):
     check(ttv, X, U, 1, 1.0, 20, 0.95, "ties/non-finite")
     check(ttv, X, U, 1, 1.0, 64, 1.0, "ties/non-finite k=64")
     # unaligned rows take the scalar loads
-    Y = np.ascontiguousarray(np.pad(X[:, : V5 - 3], ((0, 0), (0, 1))))
+    Y = np.ascontiguousarray(np.pad(X[:, : V5 - 3], ((0, 0), (0, 1)), constant_values=np.inf))  # never read
     check(ttv, Y, U, 1, 1.0, 20, 0.95, "unaligned", vocab=V5 - 3)
 
 
