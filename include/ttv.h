@@ -34,8 +34,10 @@
  *  - Pointers marked (device) are device memory; (host) are host memory.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL is the default
  *    stream). The library never synchronises, never allocates and holds no
- *    state apart from a thread-local error string. The caller owns every
- *    buffer, including workspaces sized by the *_ws queries.
+ *    state apart from a thread-local error string (and, for
+ *    tree_verify_attention_static, a static device scratch array and its
+ *    per-device address). The caller owns every buffer, including
+ *    workspaces sized by the *_ws queries.
  *  - Return value: TTV_OK, or an error code with a reason in ttv_last_error().
  *    TTV_ERR_INVALID and TTV_ERR_UNSUPPORTED are decided on the host before
  *    anything is launched, so nothing has been written when they return.
