@@ -61,9 +61,10 @@ struct LmParams {
   int n_slabs, n_slices;
 };
 
-// A wave owns VB blocks of 16 vocabulary rows (VB = 4 up to 112 nodes, 3 at
-// 128: its accumulators, both weight slots and the hidden fragments then fit
-// in 256 registers), a workgroup kLmWaves * 16 * VB rows.
+// A wave owns VB blocks of 16 vocabulary rows (VB = 4 up to 112 nodes; at
+// 128 only 3 fit beside the accumulators, both weight slots and the hidden
+// fragments in 256 registers, and 2 run ~1% faster than 3: 970 workgroups
+// fill the last round better than 647), a workgroup kLmWaves * 16 * VB rows.
 template <int NB, int VB>
 __global__ void __launch_bounds__(kLmThreads) lm_head_main(const LmParams p) {
   constexpr int kRows = 16 * VB;
@@ -621,7 +622,7 @@ __global__ void __launch_bounds__(kWave) lm_head_reduce(const uint64_t* __restri
 
 // row blocks per wave for a call of n_rows nodes (the node blocks of its
 // first slice decide), and the vocabulary slabs of kLmWaves such waves
-static int lm_vb(int64_t n_rows) { return n_rows > 16 * (kLmMaxNB - 1) ? 3 : kLmMaxVB; }
+static int lm_vb(int64_t n_rows) { return n_rows > 16 * (kLmMaxNB - 1) ? 2 : kLmMaxVB; }
 static int lm_slabs(int64_t n_rows, int64_t vocab) {
   const int64_t rows = int64_t{kLmWaves} * 16 * lm_vb(n_rows);
   return static_cast<int>((vocab + rows - 1) / rows);
@@ -677,7 +678,7 @@ extern "C" ttv_status lm_head_argmax(const uint16_t* hidden, int64_t n_rows, int
   hipStream_t s = (hipStream_t)stream;
   switch (nb) {
 #define TTV_LM(NB) \
-  case NB: hipLaunchKernelGGL((lm_head_main<NB, NB == kLmMaxNB ? 3 : kLmMaxVB>), dim3(grid), dim3(kLmThreads), 0, s, p); break;
+  case NB: hipLaunchKernelGGL((lm_head_main<NB, NB == kLmMaxNB ? 2 : kLmMaxVB>), dim3(grid), dim3(kLmThreads), 0, s, p); break;
     TTV_LM(1) TTV_LM(2) TTV_LM(3) TTV_LM(4) TTV_LM(5) TTV_LM(6) TTV_LM(7) TTV_LM(8)
 #undef TTV_LM
     default: return fail(TTV_ERR_INVALID, "lm_head_argmax: internal node-block count");
