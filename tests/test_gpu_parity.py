@@ -534,6 +534,44 @@ def test_int8_spread_scales_error_relative_to_abs_values(ttv, spread):
     assert rel <= TOL_BF16
 
 
+@pytest.mark.parametrize("spread,T", [(6, 16), (10, 16), (10, 40)])
+def test_bf16_spread_magnitudes_error_relative_to_abs_values(ttv, spread, T):
+    """bf16 KV whose per-token key and value magnitudes spread log-uniformly
+    over a factor 2^spread within each head: scores then span hundreds of
+    log2 units (references raised by redo passes) and outputs reach ~100.
+    As for int8 KV the error of an output row is bounded relative to the
+    largest element of the attention of |V| (the oracle on |v|)."""
+    from workloads.configs import _spec
+    from workloads.gen import bf16_bits_to_f32, to_bf16_bits
+    r = rng_for(1280, spread, T)
+    B, Hq, Hkv, D = 6, 40, 8, 128
+    parents = [confidence_tree(rng_for(1281, spread, T, b), T, 8, 1000, 4)[0] for b in range(B)]
+    hist = [int(r.integers(0, 3000)) for _ in range(B)]
+    spec = _spec(1280, B, 1, Hq, Hkv, D, 16, 1.0, "bf16", "bf16", hist, parents, [np.zeros(T, np.int64)] * B,
+                 [np.zeros(T, np.int64)] * B, [[0]] * B)
+    layer = make_kv_cache(1282, spread, B, Hkv, spec.cap, D, "bf16")
+    for n in ("k", "v"):
+        f = np.exp2(r.uniform(-spread / 2, spread / 2, layer[n].shape[:3]))[..., None]
+        layer[n] = to_bf16_bits(bf16_bits_to_f32(layer[n]) * f.astype(np.float32))
+    q = make_queries(1283, spread, spec.n_nodes, Hq, D, "bf16")
+    batch = spec_batch(ttv, spec)
+    anc, _, st = run_mask(ttv, batch, to_dev(spec.flat("parents")))
+    dev, kvl = layer_to_dev(ttv, layer)
+    out, _ = run_attention(ttv, batch, to_dev(q, "bf16"), kvl, anc, 1 / math.sqrt(D))
+    torch.cuda.synchronize()
+    want = O.tree_verify_attention(q, layer, spec.node_off, spec.hist_len, spec.parents, 1 / math.sqrt(D), "bf16",
+                                   "bf16")
+    absv = dict(layer, v=layer["v"] & np.uint16(0x7FFF))  # clear the bf16 sign bit
+    cond = O.tree_verify_attention(q, absv, spec.node_off, spec.hist_len, spec.parents, 1 / math.sqrt(D), "bf16",
+                                   "bf16")
+    g = to_host(out)
+    assert np.isfinite(g).all() and int(st.item()) == 0
+    rel = float((np.abs(g - want) / np.maximum(cond.max(axis=2, keepdims=True), 1e-30)).max())
+    log(f"bf16 magnitudes spread 2^{spread}, T={T}: max|out| {np.abs(want).max():.3e}, "
+        f"max|err| {np.abs(g - want).max():.3e}, max err / (attention of |V|) {rel:.3e}")
+    assert rel <= TOL_BF16
+
+
 @pytest.mark.parametrize("kv,D,T", [("i8", 128, 16), ("bf16", 128, 16), ("bf16", 128, 40), ("i8", 64, 16),
                                     ("f32", 64, 16)])
 def test_attention_ignores_cache_rows_past_live_length(ttv, kv, D, T):
