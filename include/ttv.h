@@ -145,7 +145,7 @@ typedef struct ttv_kv_layer {
  * top_k of those F * top_k candidates by score (ties to the lower index).
  * Limits (TTV_ERR_INVALID): 1 <= B <= TTV_MAX_BATCH, 1 <= top_k <= 16,
  * top_k <= vocab <= 2^31 - 1, row_stride >= vocab, top_k <= cand_cap <= 4096,
- * ceil(vocab / 4096) * top_k <= 65536. ws: >= draft_tree_expand_ws(B * F,
+ * ceil(vocab / 2048) * top_k <= 65536. ws: >= draft_tree_expand_ws(B * F,
  * vocab, top_k) bytes, contents irrelevant. Device checks: a row with a NaN
  * or an infinity stores TTV_DEV_BAD_LOGITS; a table without room for the
  * depth (count + F * top_k > cand_cap) or without a frontier stores

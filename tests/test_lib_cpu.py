@@ -336,7 +336,7 @@ def test_draft_validation():
     E, S = C["draft_tree_expand"], C["draft_tree_select"]
     V = 248320
     ws = C["draft_tree_expand_ws"](16, V, 4)
-    nc = (V + 4095) // 4096
+    nc = (V + 2047) // 2048  # 2,048-logit chunks: 4 candidates (8 B) and 16 B of statistics each
     assert ws == 16 * nc * 4 * 8 + 16 * nc * 16
 
     def expand(B=2, depth=1, k=4, vocab=V, stride=V, cap=128, ws_bytes=ws, logits=FAKE):

@@ -24,7 +24,10 @@
 namespace ttv {
 
 constexpr int kDraftMaxK = 16;        // top_k limit: <= 16 frontier rows, <= 256 new candidates a depth
-constexpr int kDraftPerLane = kSelPerLane;  // chunks of 4096 logits, as the sampled selection
+// chunks of 2,048 logits: twice the waves of 4,096-logit chunks, each half as
+// long, which shortens the chunk pass more than the row pass's twice as many
+// candidates lengthen it (1,024, 1,536, 3,072 and 4,096 were slower)
+constexpr int kDraftPerLane = 32;
 constexpr int kDraftChunk = kSelLanes * kDraftPerLane;
 constexpr int kDraftMaxCand = 4096;   // candidate table limit per sequence
 
