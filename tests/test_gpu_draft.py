@@ -124,6 +124,8 @@ CASES = [  # (B, top_k, depths, n_nodes, V, stride_pad)
     (3, 1, 5, 6, 5000, 0),      # no branching: the chain of argmaxes
     (2, 16, 3, 64, 70000, 0),   # widest frontier, largest tree
     (4, 8, 4, 64, 4097 + 13, 0),  # a ragged last chunk
+    (2, 4, 3, 16, 2048 + 5, 0),   # one full 2,048-logit chunk and a 5-logit tail
+    (3, 4, 4, 16, 3 * 2048, 0),   # whole chunks only
     (2, 2, 6, 12, 100, 0),      # a vocabulary smaller than one chunk
     (3, 4, 3, 16, 9001, 3),     # unaligned row stride
     (5, 3, 2, 13, 12288, 0),    # every candidate chosen (1 + 3 + 9)
@@ -191,7 +193,7 @@ def test_ties_across_chunks(ttv):
     r = rng_for(5, 2).standard_normal((1, 1, V)).astype(np.float32)
     for i in (8191, 4096, V - 1):
         r[0, 0, i] = 9.0
-    for i in (12287, 4095, 100):
+    for i in (12287, 4095, 100, 2047, 2048):
         r[0, 0, i] = 8.5
     table = ttv.DraftTable(1, 4, 16)
     assert gpu_expand(ttv, table, 1, r) == 0
